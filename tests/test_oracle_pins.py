@@ -1,0 +1,459 @@
+"""Pins of the CPU oracle against what the pages and the mathematics fix (CPU only).
+
+Each test checks the oracle against something other than itself: values stated on the pages
+(golden fixtures), hand-derived worked examples, exhaustive brute-force searches written
+independently here (argmin over the value grid, exact rational arithmetic), and library routines
+(torch's float8/bfloat16 conversions, torch's tanh-GELU, numpy matmul).
+"""
+import json
+import math
+import os
+from fractions import Fraction
+
+import numpy as np
+import pytest
+import torch
+
+import oracle as O
+from fp4_block_scaled_amd import synth
+
+GOLDEN = os.path.join(os.path.dirname(__file__), "golden")
+
+
+def _golden(name):
+    with open(os.path.join(GOLDEN, name)) as f:
+        return json.load(f)
+
+
+def _bf16_bits_exact(values):
+    """float values -> BF16 bit patterns, asserting each value is exactly representable."""
+    t = torch.tensor(values, dtype=torch.float64)
+    b = t.to(torch.float32).to(torch.bfloat16)
+    assert torch.equal(b.to(torch.float64), t) and torch.equal(torch.signbit(b), torch.signbit(t))
+    return b.view(torch.int16).numpy().view(np.uint16)
+
+
+def _unpack(packed, n):
+    packed = np.asarray(packed, dtype=np.uint8)
+    out = np.empty(packed.shape[:-1] + (n,), dtype=np.uint8)
+    out[..., 0::2] = packed & 0xF
+    out[..., 1::2] = packed >> 4
+    return out
+
+
+E2M1_GRID = np.array(_golden("e2m1_grid.json")["magnitudes"], dtype=np.float64)
+# E4M3 magnitudes 0..126 from torch's float8_e4m3fn decoding (library, independent of the oracle)
+E4M3_GRID = torch.arange(0, 127, dtype=torch.uint8).view(torch.float8_e4m3fn).to(
+    torch.float64).numpy()
+
+
+# ---------------------------------------------------------------------------------------------
+# element formats
+# ---------------------------------------------------------------------------------------------
+def test_e2m1_decode_is_the_stated_grid():
+    g = _golden("e2m1_grid.json")
+    for c in range(8):
+        assert O.e2m1_value(c) == g["magnitudes"][c]
+        neg = O.e2m1_value(c | g["sign_bit"])
+        assert neg == -g["magnitudes"][c] and math.copysign(1.0, neg) == -1.0
+    vals = sorted({O.e2m1_value(c) for c in range(16)})
+    assert len(vals) == 15  # +0 and -0 compare equal: 16 codes, 15 distinct reals
+
+
+def test_e4m3_decode_matches_torch():
+    ref = torch.arange(0, 256, dtype=torch.int32).to(torch.uint8).view(
+        torch.float8_e4m3fn).to(torch.float64).numpy()
+    for b in range(256):
+        v = O.e4m3_value(b)
+        if b in (0x7F, 0xFF):
+            assert math.isnan(v)
+        else:
+            assert v == ref[b], b
+    assert O.e4m3_value(0x7E) == 448.0 and O.e4m3_value(0x01) == 2.0 ** -9
+
+
+def test_e8m0_decode_is_power_of_two():
+    for b in range(255):
+        assert O.e8m0_value(b) == 2.0 ** (b - 127)
+    assert math.isnan(O.e8m0_value(255))
+
+
+def _nearest_even(q, grid):
+    """Independent RNE: argmin distance over the grid, ties to the even index; saturates."""
+    d = np.abs(q[:, None] - grid[None, :])
+    dmin = d.min(axis=1, keepdims=True)
+    cand = d == dmin
+    first = cand.argmax(axis=1)
+    two = cand.sum(axis=1) == 2
+    return np.where(two & (first % 2 == 1), first + 1, first)
+
+
+def test_e2m1_rne_bruteforce_dense():
+    q = np.concatenate([np.arange(0, 8 * 256 + 1) / 256.0,
+                        np.random.default_rng(0).uniform(0, 9, 20000)])
+    ref = _nearest_even(q, E2M1_GRID)
+    got = np.array([O.e2m1_rne_mag(float(v)) for v in q])
+    np.testing.assert_array_equal(got, ref)
+
+
+def test_e4m3_rne_matches_torch_conversion():
+    # all midpoints and representable points below saturation, plus random fp32 values
+    mags = E4M3_GRID
+    mids = (mags[:-1] + mags[1:]) / 2
+    rng = np.random.default_rng(1)
+    rand = np.exp(rng.uniform(np.log(2.0 ** -12), np.log(460.0), 20000)).astype(np.float32)
+    q = np.concatenate([mags, mids, rand.astype(np.float64)])
+    q = q[q < 448.0 + 8.0]          # torch turns >= 464 into NaN; saturation tested below
+    tq = torch.tensor(q, dtype=torch.float32)
+    assert torch.equal(tq.to(torch.float64), torch.tensor(q))  # fp32-exact inputs
+    ref = tq.to(torch.float8_e4m3fn).view(torch.uint8).numpy() & 0x7F
+    got = np.array([O.e4m3_rne_mag(float(v)) for v in q])
+    np.testing.assert_array_equal(got, ref)
+    for v in (464.0, 480.0, 1e6):
+        assert O.e4m3_rne_mag(v) == 0x7E  # saturate, never the NaN code
+
+
+def test_bf16_rne_matches_torch_and_ties():
+    rng = np.random.default_rng(2)
+    f = np.concatenate([rng.standard_normal(5000), rng.standard_normal(500) * 1e-39,
+                        rng.standard_normal(500) * 1e37]).astype(np.float32)
+    ref = torch.from_numpy(f).to(torch.bfloat16).view(torch.int16).numpy().view(np.uint16)
+    got = np.array([O.bf16_rne(float(v)) for v in f], dtype=np.uint16)
+    np.testing.assert_array_equal(got, ref)
+    # exact ties in fp64 beyond fp32 precision: 1 + 2^-8 -> 1 (even), 1 + 3*2^-8 -> 1 + 2^-6
+    assert O.bf16_rne(1.0 + 2.0 ** -8) == 0x3F80
+    assert O.bf16_rne(1.0 + 3 * 2.0 ** -8) == 0x3F82
+    assert O.bf16_rne(1.0 + 2.0 ** -8 + 2.0 ** -40) == 0x3F81  # just above the tie
+    assert O.bf16_rne(-0.0) == 0x8000
+    assert O.bf16_rne(3.5e38) == 0x7F80
+
+
+# ---------------------------------------------------------------------------------------------
+# worked examples
+# ---------------------------------------------------------------------------------------------
+def _block_bits(b):
+    return np.asarray(b["bits"], dtype=np.uint16) if "bits" in b else _bf16_bits_exact(b["x"])
+
+
+@pytest.mark.parametrize("b", _golden("mxfp4_worked_blocks.json")["blocks"], ids=lambda b: b["name"])
+def test_mxfp4_worked_blocks(b):
+    bits = _block_bits(b)[None, :]
+    codes, scales = O.quantize_mx_bf16(bits, O.E2M1)
+    assert int(scales[0, 0]) == b["scale"]
+    np.testing.assert_array_equal(_unpack(codes[0], 32), b["codes"])
+    if "packed" in b:
+        np.testing.assert_array_equal(codes[0], b["packed"])
+    assert codes.shape == (1, 16)  # two codes per byte
+
+
+@pytest.mark.parametrize("b", _golden("mxfp8_worked_blocks.json")["blocks"], ids=lambda b: b["name"])
+def test_mxfp8_worked_blocks(b):
+    bits = _block_bits(b)[None, :]
+    codes, scales = O.quantize_mx_bf16(bits, O.E4M3)
+    assert int(scales[0, 0]) == b["scale"]
+    np.testing.assert_array_equal(codes[0], b["codes"])
+
+
+@pytest.mark.parametrize("b", _golden("nvfp4_worked_blocks.json")["blocks"], ids=lambda b: b["name"])
+def test_nvfp4_worked_blocks(b):
+    bits = _block_bits(b)[None, :]
+    codes, scales = O.quantize_nv_bf16(bits, 1.0)
+    assert int(scales[0, 0]) == b["scale"]
+    np.testing.assert_array_equal(_unpack(codes[0], 16), b["codes"])
+    if "packed" in b:
+        np.testing.assert_array_equal(codes[0], b["packed"])
+
+
+# ---------------------------------------------------------------------------------------------
+# exhaustive brute force over every finite BF16 value
+# ---------------------------------------------------------------------------------------------
+_ALL_BF16 = np.arange(0, 65536, dtype=np.uint32).astype(np.uint16)
+_FINITE_BF16 = _ALL_BF16[(_ALL_BF16 & 0x7F80) != 0x7F80]
+
+
+def _mx_brute(x_f64, anchor, emax, grid, sign_shift):
+    amax = np.maximum(np.abs(x_f64), abs(anchor))
+    _, ex = np.frexp(amax)
+    e = np.where(amax == 0, -127, ex - 1 - emax)
+    e = np.clip(e, -127, 127)
+    q = np.ldexp(np.abs(x_f64), -e)
+    idx = _nearest_even(q, grid)
+    return (idx | (np.signbit(x_f64).astype(np.int64) << sign_shift)).astype(np.uint8), e + 127
+
+
+@pytest.mark.parametrize("anchor", [0.0, 6.0, 1.0, 3.0, 2.0 ** -124, 2.0 ** -126, 1.5 * 2.0 ** 100,
+                                    2.0 ** 127])
+@pytest.mark.parametrize("elem", [O.E2M1, O.E4M3])
+def test_mx_quantize_exhaustive_bf16(anchor, elem):
+    x = O.bf16_values(_FINITE_BF16)
+    n = len(x)
+    abits = _bf16_bits_exact([anchor])[0]
+    block = np.zeros((n, 32), dtype=np.uint16)
+    block[:, 0] = _FINITE_BF16
+    block[:, 1] = abits
+    codes, scales = O.quantize_mx_bf16(block, elem)
+    if elem == O.E2M1:
+        got = _unpack(codes, 32)
+        ref, sref = _mx_brute(x, anchor, 2, E2M1_GRID, 3)
+        ref_a, _ = _mx_brute(np.full(n, anchor), np.abs(x), 2, E2M1_GRID, 3)
+    else:
+        got = codes
+        ref, sref = _mx_brute(x, anchor, 8, E4M3_GRID, 7)
+        ref_a, _ = _mx_brute(np.full(n, anchor), np.abs(x), 8, E4M3_GRID, 7)
+    np.testing.assert_array_equal(scales[:, 0], sref)
+    np.testing.assert_array_equal(got[:, 0], ref)
+    np.testing.assert_array_equal(got[:, 1], ref_a)
+    assert np.all(got[:, 2:] == 0)
+
+
+# ---------------------------------------------------------------------------------------------
+# exact rational brute force for NVFP4 (any global scale) and MX
+# ---------------------------------------------------------------------------------------------
+_E2M1_F = [Fraction(v) for v in E2M1_GRID]
+_E4M3_F = [Fraction(float(v)) for v in E4M3_GRID]
+
+
+def _rne_pick(q, mags):
+    if q >= mags[-1]:
+        return len(mags) - 1
+    for i in range(len(mags) - 1):
+        lo, hi = mags[i], mags[i + 1]
+        if q <= hi:
+            if q - lo < hi - q:
+                return i
+            if q - lo > hi - q:
+                return i + 1
+            return i if i % 2 == 0 else i + 1
+    raise AssertionError
+
+
+def _nv_ref(xs, sg):
+    sgf = Fraction(float(np.float32(sg)))
+    fx = [Fraction(float(v)) for v in xs]
+    amax = max(abs(v) for v in fx)
+    si = _rne_pick(amax / (6 * sgf), _E4M3_F)
+    sb = _E4M3_F[si]
+    codes = []
+    for v, raw in zip(fx, xs):
+        s = 8 if math.copysign(1.0, raw) < 0 else 0
+        codes.append(s | (0 if sb == 0 else _rne_pick(abs(v) / (sb * sgf), _E2M1_F)))
+    return codes, si
+
+
+def _blocks_for_nv(nblk, seed):
+    x = synth.activation_f32(seed, nblk, 16, 1.0, 0.1, 30.0)
+    x[::7] *= 1e-3
+    x[::11] *= 50.0
+    return synth.bits16(synth.to_bf16(x))
+
+
+@pytest.mark.parametrize("sg", [1.0, 40.0 / 2688.0, 0.5, 3.0 / 7.0, 1e-3])
+def test_nvfp4_exact_rational_bruteforce(sg):
+    sg32 = float(np.float32(sg))
+    bits = _blocks_for_nv(64, 77)
+    codes, scales = O.quantize_nv_bf16(bits, sg32)
+    got = _unpack(codes, 16)
+    xs = O.bf16_values(bits)
+    for r in range(bits.shape[0]):
+        ref_codes, ref_s = _nv_ref(xs[r], sg32)
+        assert int(scales[r, 0]) == ref_s, r
+        np.testing.assert_array_equal(got[r], ref_codes)
+
+
+def test_nv_global_scale_is_rounded_quotient():
+    for amax in (40.0, 1.0, 0.046875, 123.5, 2.0 ** -100):
+        exp = Fraction(amax) / 2688
+        got = Fraction(O.nv_global_scale(amax))
+        # binary32 rounding of the exact quotient: nearest among neighbours
+        f = np.float32(float(exp))
+        cands = [np.nextafter(f, np.float32(0)), f, np.nextafter(f, np.float32(np.inf))]
+        best = min(cands, key=lambda c: abs(Fraction(float(c)) - exp))
+        assert got == Fraction(float(best))
+    assert O.nv_global_scale(0.0) == 1.0
+
+
+# ---------------------------------------------------------------------------------------------
+# invariants of the scale rule
+# ---------------------------------------------------------------------------------------------
+def _act_bits(M, K, seed=11):
+    return synth.bits16(synth.to_bf16(synth.activation_f32(seed, M, K, 1.0, 0.01, 20.0)))
+
+
+@pytest.mark.parametrize("elem", [O.E2M1, O.E4M3])
+def test_dequant_requant_is_identity(elem):
+    bits = _act_bits(64, 1024)
+    codes, scales = O.quantize_mx_bf16(bits, elem)
+    deq = O.dequantize_mx(codes, scales, 1024, elem)
+    # MX dequantization is exact in BF16 for quantizer output of BF16 input
+    deq_bits = _bf16_bits_exact(deq.ravel().tolist()).reshape(deq.shape)
+    codes2, scales2 = O.quantize_mx_bf16(deq_bits, elem)
+    np.testing.assert_array_equal(scales2, scales)
+    np.testing.assert_array_equal(codes2, codes)
+
+
+def test_nvfp4_dequant_requant_identity_unit_scale():
+    bits = _act_bits(32, 256, seed=13)
+    codes, scales = O.quantize_nv_bf16(bits, 1.0)
+    deq = O.dequantize_nv(codes, scales, 1.0, 256)
+    deq_bits = _bf16_bits_exact(deq.ravel().tolist()).reshape(deq.shape)
+    codes2, scales2 = O.quantize_nv_bf16(deq_bits, 1.0)
+    np.testing.assert_array_equal(scales2, scales)
+    np.testing.assert_array_equal(codes2, codes)
+
+
+@pytest.mark.parametrize("j", [-5, -1, 1, 7])
+def test_power_of_two_equivariance(j):
+    bits = _act_bits(16, 512, seed=17)
+    x = O.bf16_values(bits)
+    bits_j = _bf16_bits_exact((x * 2.0 ** j).ravel().tolist()).reshape(x.shape)
+    c0, s0 = O.quantize_mx_bf16(bits, O.E2M1)
+    c1, s1 = O.quantize_mx_bf16(bits_j, O.E2M1)
+    np.testing.assert_array_equal(c1, c0)
+    np.testing.assert_array_equal(s1.astype(int), s0.astype(int) + j)
+
+
+def test_scales_are_powers_of_two_and_block_max_is_4_or_6():
+    bits = _act_bits(128, 2048, seed=19)
+    codes, scales = O.quantize_mx_bf16(bits, O.E2M1)
+    assert scales.max() < 255
+    mags = _unpack(codes, 2048) & 7
+    blk_max = mags.reshape(128, 64, 32).max(axis=2)
+    assert set(np.unique(blk_max)) <= {6, 7}
+
+
+def test_row_sharding_is_bit_identical():
+    bits = _act_bits(96, 640, seed=23)
+    c, s = O.quantize_mx_bf16(bits, O.E2M1)
+    for a, b in ((0, 1), (5, 37), (37, 96)):
+        cs, ss = O.quantize_mx_bf16(bits[a:b], O.E2M1)
+        np.testing.assert_array_equal(cs, c[a:b])
+        np.testing.assert_array_equal(ss, s[a:b])
+
+
+def test_quantization_error_sanity_band():
+    """Not a pin: relative RMS error of MXFP4 on Gaussian data is of the order of the ~11.6 %
+    residual error the W4A8 page reports for real weights."""
+    bits = synth.bits16(synth.to_bf16(synth.normal_f32(29, (256, 1024), 0.02)))
+    x = O.bf16_values(bits)
+    codes, scales = O.quantize_mx_bf16(bits, O.E2M1)
+    deq = O.dequantize_mx(codes, scales, 1024)
+    rel = np.linalg.norm(deq - x) / np.linalg.norm(x)
+    assert 0.05 < rel < 0.25
+
+
+# ---------------------------------------------------------------------------------------------
+# storage arithmetic
+# ---------------------------------------------------------------------------------------------
+def test_storage_matches_model_card():
+    g = _golden("storage_wan_a14b.json")
+    h, f = g["hidden"], g["ffn"]
+    codes, scales = O.quantize_mx_bf16(np.zeros((1, h), dtype=np.uint16))
+    per_elem_mx = (codes.nbytes + scales.nbytes) / h
+    assert per_elem_mx == 4.25 / 8
+    codes_nv, scales_nv = O.quantize_nv_bf16(np.zeros((1, h), dtype=np.uint16), 1.0)
+    assert (codes_nv.nbytes + scales_nv.nbytes) / h == 4.5 / 8
+    elems = g["blocks"] * (g["attention_linears_per_block"] * h * h +
+                           g["ffn_linears_per_block"] * h * f)
+    total = elems * per_elem_mx
+    assert abs(total - g["stated_bytes"]) / g["stated_bytes"] < 0.01
+
+
+# ---------------------------------------------------------------------------------------------
+# GEMM, epilogues, low-rank
+# ---------------------------------------------------------------------------------------------
+def _rand_codes(rng, rows, cols, scale_lo=127, scale_hi=128):
+    codes = rng.integers(0, 256, size=(rows, cols // 2), dtype=np.uint8)
+    scales = rng.integers(scale_lo, scale_hi, size=(rows, cols // 32)).astype(np.uint8)
+    return codes, scales
+
+
+def test_gemm_exact_grid_case_matches_numpy():
+    rng = np.random.default_rng(31)
+    M, N, K = 9, 13, 256
+    ac, as_ = _rand_codes(rng, M, K)
+    wc, ws = _rand_codes(rng, N, K)
+    a = O.dequantize_mx(ac, as_, K)
+    w = O.dequantize_mx(wc, ws, K)
+    # values on the E2M1 grid, unit scales: every partial sum is a multiple of 1/4 below 2^20
+    y, t = O.gemm(a, w)
+    np.testing.assert_array_equal(y, a @ w.T)
+    np.testing.assert_array_equal(t, np.abs(a) @ np.abs(w).T)
+
+
+def test_gemm_random_scales_and_bias():
+    rng = np.random.default_rng(37)
+    M, N, K = 7, 11, 320
+    ac, as_ = _rand_codes(rng, M, K, 110, 140)
+    wc, ws = _rand_codes(rng, N, K, 110, 140)
+    bias_bits = synth.bits16(synth.to_f16(synth.normal_f32(5, (N,), 0.01)))
+    y, t = O.linear_ref_mx(ac, as_, O.E2M1, wc, ws, K, bias_bits)
+    a = O.dequantize_mx(ac, as_, K)
+    w = O.dequantize_mx(wc, ws, K)
+    b = torch.from_numpy(bias_bits.view(np.int16)).view(torch.float16).to(torch.float64).numpy()
+    ref = a @ w.T + b
+    np.testing.assert_allclose(y, ref, rtol=1e-12, atol=1e-300 + 1e-12 * np.abs(t).max())
+
+
+def test_gemm_one_hot_weight_and_zero_activation():
+    rng = np.random.default_rng(41)
+    M, N, K = 5, 8, 64
+    ac, as_ = _rand_codes(rng, M, K, 120, 135)
+    a = O.dequantize_mx(ac, as_, K)
+    w = np.zeros((N, K))
+    for n in range(N):
+        w[n, 3 * n] = 1.0
+    bias = np.arange(N) * 0.125
+    y, _ = O.gemm(a, w, bias)
+    np.testing.assert_array_equal(y, a[:, 0:3 * N:3] + bias)
+    y0, t0 = O.gemm(np.zeros((M, K)), w, bias)
+    np.testing.assert_array_equal(y0, np.broadcast_to(bias, (M, N)))
+    assert np.all(t0 == 0)
+
+
+def test_gelu_matches_torch_and_identities():
+    y = np.concatenate([np.linspace(-12, 12, 4001), [0.0, -0.0, 1e-30, -1e-30]])
+    g = O.gelu_tanh(y)
+    ref = torch.nn.functional.gelu(torch.from_numpy(y), approximate="tanh").numpy()
+    # the formula cancels in 1 + tanh(.) for large negative y: compare against |y| there
+    assert np.all(np.abs(g - ref) <= 1e-14 * np.abs(ref) + 4e-16 * np.abs(y))
+    assert O.gelu_tanh(np.array([0.0]))[0] == 0.0
+    np.testing.assert_allclose(O.gelu_tanh(y) - O.gelu_tanh(-y), y, rtol=1e-13, atol=1e-15)
+
+
+def test_lowrank_branch():
+    M, K, R, N = 6, 96, 32, 40
+    x = _act_bits(M, K, seed=43)
+    down = synth.bits16(synth.to_bf16(synth.normal_f32(44, (K, R), 0.02)))
+    up = synth.bits16(synth.to_bf16(synth.normal_f32(45, (R, N), 0.02)))
+    ub, lr, la = O.lowrank(x, down, up)
+    s = O.bf16_values(x) @ O.bf16_values(down)
+    u = O.bf16_values(ub)
+    # u is a BF16 neighbour of the exact sum, within half an ulp (round to nearest)
+    _, ex = np.frexp(np.abs(u))
+    ulp = np.ldexp(1.0, ex - 8)
+    assert np.all(np.abs(u - s) <= 0.5 * ulp + 1e-12 * np.abs(s))
+    upv = O.bf16_values(up)
+    np.testing.assert_allclose(lr, u @ upv, rtol=1e-12, atol=1e-15)
+    np.testing.assert_allclose(la, np.abs(u) @ np.abs(upv), rtol=1e-12, atol=1e-15)
+    _, lr0, _ = O.lowrank(x, np.zeros_like(down), up)
+    assert np.all(lr0 == 0)
+
+
+# ---------------------------------------------------------------------------------------------
+# the seeded generator
+# ---------------------------------------------------------------------------------------------
+def test_generator_is_deterministic_and_normal():
+    a = synth.normal_f32(1001, (100000,), 1.0)
+    b = synth.normal_f32(1001, (100000,), 1.0)
+    c = synth.normal_f32(1002, (100000,), 1.0)
+    assert np.array_equal(a, b) and not np.array_equal(a, c)
+    assert abs(a.mean()) < 0.02 and abs(a.std() - 1.0) < 0.02
+    # prefix property of a counter-based stream
+    np.testing.assert_array_equal(synth.normal_f32(1001, (1000,), 1.0), a[:1000])
+    idx = synth.outlier_channels(1004, 512, 5)
+    assert len(set(idx.tolist())) == 5 and idx.min() >= 0 and idx.max() < 512
+    x = synth.activation_f32(1000, 4, 512, 1.0, 0.01, 20.0)
+    plain = synth.normal_f32(1001, (4, 512), 1.0)
+    ratio = np.abs(x / np.where(plain == 0, 1, plain))
+    cols = np.where(np.all(np.isclose(ratio, 20.0), axis=0))[0]
+    assert sorted(cols.tolist()) == sorted(idx.tolist())
