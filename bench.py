@@ -1,0 +1,274 @@
+"""Benchmark of the W4A4 MXFP4 linear layer (dynamic activation quantization + block-scaled GEMM
++ bias, BF16 output) at the Wan2.2-A14B attention-projection shape M=75600, K=N=5120.
+
+One step = one call of the library's ``mx_linear``: the activation quantizer kernel followed by
+the GEMM kernel, on inputs already resident in HBM.  ``value`` is whole-step throughput in
+TFLOP/s (2*M*N*K per step).  The roofline object describes the dominant kernel (the GEMM),
+timed alone with HIP events on the stream it is launched on; the quantizer is timed the same
+way and reported beside it.  The CPU baseline times the oracle on a bounded row sample.
+
+  python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME] [--no-cpu]
+
+Other workloads (``--workload``) bench the variant paths: the FFN pair, W4A8 SVDQuant, NVFP4.
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import platform
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+METRIC = "W4A4 MXFP4 linear TFLOPS (quant+GEMM) at Wan-A14B shapes; % MXFP4 MFMA peak"
+PEAK_TFLOPS = {"mxfp4": 10100.0, "mxfp8": 5000.0, "bf16": 2500.0}
+HBM_GBPS = 8000.0
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic.json")
+KERNEL_SOURCES = [os.path.join(ROOT, "fp4_block_scaled_amd", "csrc", f)
+                  for f in ("mx_gemm.hip", "mx_quant.hip", "mx_common.h")]
+
+
+def kernel_source_hash() -> str:
+    h = hashlib.sha256()
+    for f in KERNEL_SOURCES:
+        with open(f, "rb") as fh:
+            h.update(fh.read())
+    return h.hexdigest()[:16]
+
+
+def measured_traffic(workload: str, kernel: str):
+    """HBM bytes per launch from the committed rocprofv3 counter runs, if they were taken on
+    the current kernel sources; else None."""
+    try:
+        with open(TRAFFIC_FILE) as f:
+            t = json.load(f)
+    except (OSError, ValueError):
+        return None
+    e = t.get(workload, {}).get(kernel)
+    if not e or e.get("source_hash") != kernel_source_hash():
+        return None
+    return e.get("bytes_per_launch")
+
+
+def cpu_info():
+    model = platform.processor() or ""
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    model = line.split(":", 1)[1].strip()
+                    break
+    except OSError:
+        pass
+    return model
+
+
+def time_events(fn, iters: int, torch):
+    """Average milliseconds of fn() over iters launches, HIP events on the current stream."""
+    s = torch.cuda.current_stream()
+    start, end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    start.record(s)
+    for _ in range(iters):
+        fn()
+    end.record(s)
+    torch.cuda.synchronize()
+    return start.elapsed_time(end) / iters
+
+
+def cpu_baseline_mx(wl, a_bits, w_codes, w_scales, b_bits, rows: int):
+    """The oracle (as it stands) on a sample of rows: quantize + dequantize + fp64 GEMM."""
+    import numpy as np
+    import oracle as O
+    idx = np.concatenate([np.arange(rows // 2), np.arange(wl.M - rows // 2, wl.M)])
+    sample = np.ascontiguousarray(a_bits[idx])
+    wdeq = O.dequantize_mx(w_codes, w_scales, wl.K)     # weight preparation: not timed
+    bias = O.f16_values(b_bits) if b_bits is not None else None
+    t0 = time.perf_counter()
+    ac, as_ = O.quantize_mx_bf16(sample, O.E2M1)
+    adeq = O.dequantize_mx(ac, as_, wl.K, O.E2M1)
+    O.gemm(adeq, wdeq, bias)
+    dt = time.perf_counter() - t0
+    flops = 2.0 * rows * wl.K * wl.N
+    threads = int(os.environ.get("OMP_NUM_THREADS", os.cpu_count() or 1))
+    return {"value": flops / dt / 1e12, "unit": "TFLOP/s", "cores": threads, "kind": "oracle",
+            "sample": f"{rows} rows (first and last {rows // 2}) of the {wl.M}x{wl.K}x{wl.N} linear: "
+                      f"oracle MXFP4 quantization + dequantization + fp64 GEMM, {dt:.2f} s; "
+                      f"CPU: {cpu_info()}"}
+
+
+def bench_mx_linear(args, torch, mx, synth):
+    import numpy as np
+    wl = synth.WORKLOADS[args.workload]
+    M, K, N = wl.M, wl.K, wl.N
+    t0 = time.perf_counter()
+    a_bits = synth.bits16(synth.to_bf16(wl.activation()))
+    w_bf = synth.to_bf16(wl.weight())
+    b = wl.bias()
+    b_bits = synth.bits16(synth.to_f16(b)) if b is not None else None
+    a = torch.from_numpy(a_bits.view(np.int16)).view(torch.bfloat16).cuda()
+    bias = torch.from_numpy(b_bits.view(np.int16)).view(torch.float16).cuda() if b is not None else None
+    wq = mx.quantize(w_bf.cuda(), "mxfp4")                # offline weight preparation
+    out = torch.empty((M, N), dtype=torch.bfloat16, device="cuda")
+    ws = torch.empty(mx.linear_workspace_bytes(M, K, "mxfp4"), dtype=torch.uint8, device="cuda")
+    aq = mx.empty_qmatrix(M, K, "mxfp4")
+    torch.cuda.synchronize()
+    setup_s = time.perf_counter() - t0
+
+    step = lambda: mx.linear(a, wq, bias, out=out, workspace=ws)
+    quant = lambda: mx.quantize(a, "mxfp4", out=aq)
+    gemm = lambda: mx.linear_q(aq, wq, bias, out=out)
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    t_start = time.perf_counter()
+    ms_step = time_events(step, args.steps, torch)
+    wall_ms = (time.perf_counter() - t_start) * 1e3 / args.steps
+    quant()
+    ms_quant = time_events(quant, args.steps, torch)
+    ms_gemm = time_events(gemm, args.steps, torch)
+
+    flops = 2.0 * M * N * K
+    quant_bytes = M * K * 2 + M * K // 2 + M * K // 32
+    gemm_bytes = M * K // 2 + M * K // 32 + N * K // 2 + N * K // 32 + M * N * 2 + (N * 2 if b is not None else 0)
+    achieved = flops / (ms_gemm * 1e-3) / 1e12
+    traffic = measured_traffic(args.workload, "gemm")
+    res = {
+        "metric": METRIC,
+        "value": flops / (ms_step * 1e-3) / 1e12,
+        "unit": "TFLOP/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": ms_step,
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "mxfp4",
+        "data": "synthetic",
+        "config": {"workload": wl.name, "M": M, "K": K, "N": N,
+                   "activation": f"N(0,1), {int(round(wl.outlier_frac * K))} outlier channels x{wl.outlier_factor:g}",
+                   "weight": f"N(0,{wl.w_sigma}) MXFP4", "bias": "fp16", "output": "bf16"},
+        "roofline": {"bound": "mfma", "achieved": achieved, "peak": PEAK_TFLOPS["mxfp4"],
+                     "unit": "TFLOP/s", "frac": achieved / PEAK_TFLOPS["mxfp4"],
+                     "traffic": traffic, "kernel": "gemm_mx_kernel (MXFP4 x MXFP4, bias, BF16 out)",
+                     "algorithmic_flops_per_launch": flops, "ms_per_launch": ms_gemm},
+        "kernels": {
+            "quantizer": {"ms": ms_quant, "GB/s": quant_bytes / (ms_quant * 1e-3) / 1e9,
+                          "frac_hbm": quant_bytes / (ms_quant * 1e-3) / 1e9 / HBM_GBPS,
+                          "algorithmic_bytes": quant_bytes,
+                          "traffic": measured_traffic(args.workload, "quant")},
+            "gemm": {"ms": ms_gemm, "TFLOP/s": achieved, "algorithmic_bytes": gemm_bytes},
+            "step_frac_of_mxfp4_peak": flops / (ms_step * 1e-3) / 1e12 / PEAK_TFLOPS["mxfp4"],
+            "wall_ms_per_step": wall_ms,
+        },
+        "setup_s": setup_s,
+    }
+    if not args.no_cpu:
+        res["cpu_baseline"] = cpu_baseline_mx(wl, a_bits, wq.codes.cpu().numpy(),
+                                              wq.scales.cpu().numpy(), b_bits, args.cpu_rows)
+    else:
+        res["cpu_baseline"] = None
+    return res
+
+
+def bench_variant(args, torch, mx, synth):
+    """Variant workloads (not the headline metric): FFN pair, W4A8 SVDQuant, NVFP4."""
+    import numpy as np
+    wl = synth.WORKLOADS[args.workload]
+    M, K, N = wl.M, wl.K, wl.N
+    to_dev = lambda bits, dt: torch.from_numpy(bits.view(np.int16)).view(dt).cuda()
+    a = to_dev(synth.bits16(synth.to_bf16(wl.activation())), torch.bfloat16)
+    w_dev = to_dev(synth.bits16(synth.to_bf16(wl.weight())), torch.bfloat16)
+    b = wl.bias()
+    bias = to_dev(synth.bits16(synth.to_f16(b)), torch.float16) if b is not None else None
+    kernels = {}
+    if wl.N2:  # FFN pair
+        wq = mx.quantize(w_dev, "mxfp4")
+        w2q = mx.quantize(to_dev(synth.bits16(synth.to_bf16(wl.weight2())), torch.bfloat16), "mxfp4")
+        b2 = to_dev(synth.bits16(synth.to_f16(wl.bias2())), torch.float16)
+        h = mx.empty_qmatrix(M, N, "mxfp4")
+        out = torch.empty((M, wl.N2), dtype=torch.bfloat16, device="cuda")
+        ws = torch.empty(mx.linear_workspace_bytes(M, K, "mxfp4"), dtype=torch.uint8, device="cuda")
+        step = lambda: (mx.linear(a, wq, bias, epilogue="bias_gelu_quant_mxfp4", out=h, workspace=ws),
+                        mx.linear_q(h, w2q, b2, out=out))
+        flops = 2.0 * M * K * N + 2.0 * M * N * wl.N2
+        dtype, peak = "mxfp4", PEAK_TFLOPS["mxfp4"]
+        aq = mx.quantize(a, "mxfp4")
+        kernels["ffn0_gemm_gelu_requant_ms"] = time_events(
+            lambda: mx.linear_q(aq, wq, bias, epilogue="bias_gelu_quant_mxfp4", out=h), args.steps, torch)
+        kernels["ffn2_gemm_ms"] = time_events(lambda: mx.linear_q(h, w2q, b2, out=out), args.steps, torch)
+    elif wl.fmt == "w4a8":
+        wq = mx.quantize(w_dev, "mxfp4")
+        down = to_dev(synth.bits16(synth.to_bf16(np.ascontiguousarray(wl.lora_down().T))), torch.bfloat16)
+        up = to_dev(synth.bits16(synth.to_bf16(np.ascontiguousarray(wl.lora_up().T))), torch.bfloat16)
+        lr = mx.LowRank(down, up)
+        out = torch.empty((M, N), dtype=torch.bfloat16, device="cuda")
+        ws = torch.empty(mx.linear_workspace_bytes(M, K, "mxfp8", wl.rank), dtype=torch.uint8, device="cuda")
+        step = lambda: mx.linear(a, wq, bias, act_fmt="mxfp8", lowrank=lr, out=out, workspace=ws)
+        flops = 2.0 * M * N * K
+        dtype, peak = "mxfp8xmxfp4", PEAK_TFLOPS["mxfp8"]
+        aq = mx.quantize(a, "mxfp8")
+        kernels["gemm_no_lowrank_ms"] = time_events(lambda: mx.linear_q(aq, wq, bias, out=out), args.steps, torch)
+        kernels["quant_mxfp8_ms"] = time_events(lambda: mx.quantize(a, "mxfp8", out=aq), args.steps, torch)
+    elif wl.fmt == "nvfp4":
+        wq = mx.quantize_weight_nvfp4(w_dev)
+        sg_a = mx.nvfp4_global_scale(wl.act_amax_static)
+        out = torch.empty((M, N), dtype=torch.bfloat16, device="cuda")
+        ws = torch.empty(mx.linear_workspace_bytes(M, K, "nvfp4"), dtype=torch.uint8, device="cuda")
+        step = lambda: mx.linear(a, wq, bias, act_fmt="nvfp4", act_global_scale=sg_a, out=out, workspace=ws)
+        flops = 2.0 * M * N * K
+        dtype, peak = "nvfp4->bf16", PEAK_TFLOPS["bf16"]
+        aq = mx.quantize(a, "nvfp4", sg_a)
+        kernels["gemm_ms"] = time_events(lambda: mx.linear_q(aq, wq, bias, out=out), args.steps, torch)
+        kernels["quant_nvfp4_ms"] = time_events(lambda: mx.quantize(a, "nvfp4", sg_a, out=aq), args.steps, torch)
+    else:
+        raise SystemExit(f"unknown variant workload {args.workload}")
+    for _ in range(args.warmup):
+        step()
+    ms = time_events(step, args.steps, torch)
+    v = flops / (ms * 1e-3) / 1e12
+    return {"metric": f"{wl.name} TFLOPS (quant+GEMM)", "value": v, "unit": "TFLOP/s", "n_gpus": 1,
+            "steps": args.steps, "warmup": args.warmup, "ms_per_step": ms, "higher_is_better": True,
+            "scaling": "weak", "vs_baseline": None, "dtype": dtype, "data": "synthetic",
+            "config": {"workload": wl.name, "M": M, "K": K, "N": N},
+            "frac_of_peak": v / peak, "peak_tflops": peak, "kernels": kernels}
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--workload", default="wan_a14b_attn_75600x5120x5120")
+    ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
+    ap.add_argument("--cpu-rows", type=int, default=64)
+    args = ap.parse_args()
+    world = int(os.environ.get("WORLD_SIZE", "1"))
+    if args.gpus != 1 or world != 1:
+        print(json.dumps({"error": "this build runs on one GPU only; the linear shards along M "
+                                   "with no exchange (see DESIGN.md), so run --gpus 1"}), flush=True)
+        raise SystemExit(2)
+
+    import torch
+    import fp4_block_scaled_amd as mx
+    from fp4_block_scaled_amd import synth
+
+    if not torch.cuda.is_available():
+        raise SystemExit("bench.py needs a GPU")
+    mx.lib()
+    if args.workload == "wan_a14b_attn_75600x5120x5120" or synth.WORKLOADS[args.workload].fmt == "mxfp4" \
+            and not synth.WORKLOADS[args.workload].N2:
+        res = bench_mx_linear(args, torch, mx, synth)
+    else:
+        res = bench_variant(args, torch, mx, synth)
+    print(json.dumps(res), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -1,0 +1,252 @@
+"""MI355X-native microscaled-FP4 linear layer: thin Python binding over ``libmxfp.so``.
+
+Every step runs in the library's gfx950 kernels; this module only marshals arguments (torch
+supplies device memory and the current HIP stream).  There is no CPU fallback: if the native
+library is missing or no GPU is present the calls raise.
+
+The C ABI is declared in ``include/mxfp.h``; the functions here carry the same names:
+``quantize``, ``dequantize``, ``absmax``, ``nvfp4_global_scale``, ``linear`` (dynamic
+activation quantization + block-scaled GEMM + epilogue), ``linear_q`` (pre-quantized
+activation) and ``linear_workspace_bytes``.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+from dataclasses import dataclass
+from typing import Optional
+
+import torch  # loaded first: its HIP runtime is the one the native library binds to
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_HERE, "libmxfp.so")
+
+MXFP4, MXFP8, NVFP4 = 0, 1, 2
+EPI_BIAS, EPI_BIAS_GELU, EPI_BIAS_GELU_QUANT_MXFP4 = 0, 1, 2
+OUT_BF16, OUT_F32 = 0, 1
+_GROUP = {MXFP4: 32, MXFP8: 32, NVFP4: 16}
+_FMT_NAMES = {"mxfp4": MXFP4, "mxfp8": MXFP8, "nvfp4": NVFP4}
+_EPI_NAMES = {"bias": EPI_BIAS, "bias_gelu": EPI_BIAS_GELU,
+              "bias_gelu_quant_mxfp4": EPI_BIAS_GELU_QUANT_MXFP4}
+
+
+class MxError(RuntimeError):
+    pass
+
+
+class _QMatrix(ctypes.Structure):
+    _fields_ = [("codes", ctypes.c_void_p), ("scales", ctypes.c_void_p),
+                ("global_scale", ctypes.c_float), ("fmt", ctypes.c_int32),
+                ("rows", ctypes.c_int64), ("cols", ctypes.c_int64)]
+
+
+class _LowRank(ctypes.Structure):
+    _fields_ = [("down", ctypes.c_void_p), ("up", ctypes.c_void_p), ("rank", ctypes.c_int32)]
+
+
+_lib = None
+
+
+def lib():
+    """The loaded native library (raises if it is not built)."""
+    global _lib
+    if _lib is None:
+        if not os.path.exists(LIB_PATH):
+            raise MxError(f"native library {LIB_PATH} is missing: run __graft_entry__.build()")
+        L = ctypes.CDLL(LIB_PATH)
+        P, I64, I32 = ctypes.c_void_p, ctypes.c_int64, ctypes.c_int32
+        L.mx_abi_version.restype = ctypes.c_int
+        L.mx_status_string.argtypes = [ctypes.c_int]
+        L.mx_status_string.restype = ctypes.c_char_p
+        L.mx_last_error.restype = ctypes.c_char_p
+        L.mx_quantize.argtypes = [P, I64, I64, I64, I32, ctypes.c_float, P, P, P]
+        L.mx_dequantize.argtypes = [ctypes.POINTER(_QMatrix), P, I64, P]
+        L.mx_absmax.argtypes = [P, I64, I64, I64, P, P]
+        L.mx_nvfp4_global_scale.argtypes = [ctypes.c_float]
+        L.mx_nvfp4_global_scale.restype = ctypes.c_float
+        L.mx_linear_workspace_bytes.argtypes = [I64, I64, I32, I32]
+        L.mx_linear_workspace_bytes.restype = ctypes.c_size_t
+        L.mx_linear.argtypes = [P, I64, I64, I64, I32, ctypes.c_float, ctypes.POINTER(_QMatrix), P,
+                                ctypes.POINTER(_LowRank), I32, I32, P, I64, P, P, ctypes.c_size_t, P]
+        L.mx_linear_q.argtypes = [ctypes.POINTER(_QMatrix), ctypes.POINTER(_QMatrix), P, I32, I32,
+                                  P, I64, P, P]
+        for f in ("mx_quantize", "mx_dequantize", "mx_absmax", "mx_linear", "mx_linear_q"):
+            getattr(L, f).restype = ctypes.c_int
+        if L.mx_abi_version() != 1:
+            raise MxError("libmxfp.so ABI version mismatch")
+        _lib = L
+    return _lib
+
+
+def _check(status: int):
+    if status != 0:
+        L = lib()
+        raise MxError(f"{L.mx_status_string(status).decode()}: {L.mx_last_error().decode()}")
+
+
+def _stream():
+    return ctypes.c_void_p(torch.cuda.current_stream().cuda_stream)
+
+
+def _fmt(fmt) -> int:
+    return _FMT_NAMES[fmt] if isinstance(fmt, str) else int(fmt)
+
+
+def _ptr(t: Optional[torch.Tensor]):
+    return None if t is None else ctypes.c_void_p(t.data_ptr())
+
+
+def _ld(t: torch.Tensor) -> int:
+    """Row stride in elements (a single-row tensor may carry any stride for its first dim)."""
+    return t.stride(0) if t.shape[0] > 1 else t.shape[1]
+
+
+def _need_cuda(t: torch.Tensor, name: str, dtype=None):
+    if not t.is_cuda:
+        raise MxError(f"{name} must be a GPU tensor")
+    if dtype is not None and t.dtype != dtype:
+        raise MxError(f"{name} must be {dtype}, got {t.dtype}")
+
+
+@dataclass
+class QMatrix:
+    """A quantized matrix: codes [rows, cols/2] (FP4) or [rows, cols] (FP8) uint8, scales
+    [rows, cols/G] uint8, an NVFP4 global scale (decode direction), the format id."""
+    codes: torch.Tensor
+    scales: torch.Tensor
+    fmt: int
+    rows: int
+    cols: int
+    global_scale: float = 1.0
+
+    def _c(self) -> _QMatrix:
+        return _QMatrix(self.codes.data_ptr(), self.scales.data_ptr(), self.global_scale,
+                        self.fmt, self.rows, self.cols)
+
+
+@dataclass
+class LowRank:
+    """SVDQuant low-rank branch: down_t BF16 [rank, K] (the K x rank down factor stored
+    transposed, K contiguous) and up_t BF16 [N, rank] (the rank x N up factor transposed)."""
+    down_t: torch.Tensor
+    up_t: torch.Tensor
+
+    @property
+    def rank(self) -> int:
+        return self.down_t.shape[0]
+
+
+def empty_qmatrix(rows: int, cols: int, fmt, device="cuda", global_scale: float = 1.0) -> QMatrix:
+    fmt = _fmt(fmt)
+    code_cols = cols if fmt == MXFP8 else cols // 2
+    codes = torch.empty((rows, code_cols), dtype=torch.uint8, device=device)
+    scales = torch.empty((rows, cols // _GROUP[fmt]), dtype=torch.uint8, device=device)
+    return QMatrix(codes, scales, fmt, rows, cols, global_scale)
+
+
+def quantize(x: torch.Tensor, fmt="mxfp4", global_scale: float = 1.0,
+             out: Optional[QMatrix] = None) -> QMatrix:
+    """Dynamic quantization of a 2-D BF16 GPU tensor (row stride may exceed its width)."""
+    fmt = _fmt(fmt)
+    _need_cuda(x, "x", torch.bfloat16)
+    if x.dim() != 2 or x.stride(1) != 1:
+        raise MxError("x must be 2-D with unit column stride")
+    rows, cols = x.shape
+    q = out if out is not None else empty_qmatrix(rows, cols, fmt, x.device, global_scale)
+    q.global_scale = global_scale
+    _check(lib().mx_quantize(_ptr(x), rows, cols, _ld(x), fmt, global_scale,
+                             _ptr(q.codes), _ptr(q.scales), _stream()))
+    return q
+
+
+def dequantize(q: QMatrix) -> torch.Tensor:
+    y = torch.empty((q.rows, q.cols), dtype=torch.bfloat16, device=q.codes.device)
+    qc = q._c()
+    _check(lib().mx_dequantize(ctypes.byref(qc), _ptr(y), q.cols, _stream()))
+    return y
+
+
+def absmax(x: torch.Tensor) -> torch.Tensor:
+    """Largest |x| of a BF16 GPU matrix, as a one-element float32 GPU tensor."""
+    _need_cuda(x, "x", torch.bfloat16)
+    out = torch.empty(1, dtype=torch.float32, device=x.device)
+    rows, cols = x.shape
+    _check(lib().mx_absmax(_ptr(x), rows, cols, _ld(x), _ptr(out), _stream()))
+    return out
+
+
+def nvfp4_global_scale(amax: float) -> float:
+    return float(lib().mx_nvfp4_global_scale(float(amax)))
+
+
+def quantize_weight_nvfp4(w: torch.Tensor) -> QMatrix:
+    """NVFP4 weight preparation: the tensor's global scale from its absmax, then quantization."""
+    sg = nvfp4_global_scale(absmax(w).item())
+    return quantize(w, NVFP4, sg)
+
+
+def linear_workspace_bytes(M: int, K: int, act_fmt="mxfp4", rank: int = 0) -> int:
+    return int(lib().mx_linear_workspace_bytes(M, K, _fmt(act_fmt), rank))
+
+
+def _epi(e) -> int:
+    return _EPI_NAMES[e] if isinstance(e, str) else int(e)
+
+
+def _alloc_out(M: int, N: int, epi: int, out_dtype, device):
+    if epi == EPI_BIAS_GELU_QUANT_MXFP4:
+        return empty_qmatrix(M, N, MXFP4, device)
+    return torch.empty((M, N), dtype=out_dtype, device=device)
+
+
+def _out_args(out, epi, out_dtype):
+    if epi == EPI_BIAS_GELU_QUANT_MXFP4:
+        return _ptr(out.codes), out.cols, _ptr(out.scales), OUT_BF16
+    od = OUT_F32 if out_dtype == torch.float32 else OUT_BF16
+    return _ptr(out), (_ld(out) if out.shape[0] else out.shape[1]), None, od
+
+
+def linear(a: torch.Tensor, w: QMatrix, bias: Optional[torch.Tensor] = None, act_fmt="mxfp4",
+           act_global_scale: float = 1.0, lowrank: Optional[LowRank] = None, epilogue="bias",
+           out_dtype=torch.bfloat16, out=None, workspace: Optional[torch.Tensor] = None):
+    """y = epilogue(Q(a) . W^T + bias) with a dynamically quantized to ``act_fmt``.
+
+    a: BF16 [M, K] GPU tensor; w: QMatrix [N, K]; bias: FP16 [N] or None.  Returns a BF16/F32
+    [M, N] tensor, or a MXFP4 QMatrix [M, N] for the re-quantizing epilogue."""
+    act_fmt, epi = _fmt(act_fmt), _epi(epilogue)
+    _need_cuda(a, "a", torch.bfloat16)
+    if a.dim() != 2 or a.stride(1) != 1:
+        raise MxError("a must be 2-D with unit column stride")
+    if bias is not None:
+        _need_cuda(bias, "bias", torch.float16)
+    M, K = a.shape
+    if out is None:
+        out = _alloc_out(M, w.rows, epi, out_dtype, a.device)
+    rank = lowrank.rank if lowrank is not None else 0
+    need = linear_workspace_bytes(M, K, act_fmt, rank) if M else 0
+    if workspace is None:
+        workspace = torch.empty(max(need, 1), dtype=torch.uint8, device=a.device)
+    wc = w._c()
+    lr = None
+    if lowrank is not None:
+        lr = ctypes.byref(_LowRank(lowrank.down_t.data_ptr(), lowrank.up_t.data_ptr(), rank))
+    optr, ld, sptr, od = _out_args(out, epi, out_dtype)
+    _check(lib().mx_linear(_ptr(a), M, K, _ld(a) if M else K, act_fmt, act_global_scale, ctypes.byref(wc),
+                           _ptr(bias), lr, epi, od, optr, ld, sptr, _ptr(workspace),
+                           workspace.numel(), _stream()))
+    return out
+
+
+def linear_q(a: QMatrix, w: QMatrix, bias: Optional[torch.Tensor] = None, epilogue="bias",
+             out_dtype=torch.bfloat16, out=None):
+    """The same GEMM and epilogues on a pre-quantized activation QMatrix [M, K]."""
+    epi = _epi(epilogue)
+    if bias is not None:
+        _need_cuda(bias, "bias", torch.float16)
+    if out is None:
+        out = _alloc_out(a.rows, w.rows, epi, out_dtype, a.codes.device)
+    ac, wc = a._c(), w._c()
+    optr, ld, sptr, od = _out_args(out, epi, out_dtype)
+    _check(lib().mx_linear_q(ctypes.byref(ac), ctypes.byref(wc), _ptr(bias), epi, od, optr, ld,
+                             sptr, _stream()))
+    return out

@@ -1,0 +1,274 @@
+// C ABI of the library (declared in include/mxfp.h): argument validation, workspace layout and
+// dispatch to the gfx950 kernels.  Nothing is launched unless every check passes.
+#include <math.h>
+#include <stdarg.h>
+#include <stdio.h>
+#include <string.h>
+
+#include "mx_internal.h"
+#include "mxfp.h"
+
+namespace {
+
+thread_local char g_err[512];
+
+mx_status fail(mx_status st, const char* fmt, ...) {
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(g_err, sizeof g_err, fmt, ap);
+  va_end(ap);
+  return st;
+}
+
+mx_status hip_status(hipError_t e, const char* what) {
+  if (e == hipSuccess) return MX_OK;
+  return fail(MX_ERR_HIP, "%s: %s", what, hipGetErrorString(e));
+}
+
+bool aligned(const void* p, uintptr_t a) { return ((uintptr_t)p % a) == 0; }
+
+int group_of(int32_t fmt) { return fmt == MX_FMT_NVFP4 ? 16 : 32; }
+bool fmt_ok(int32_t fmt) { return fmt == MX_FMT_MXFP4 || fmt == MX_FMT_MXFP8 || fmt == MX_FMT_NVFP4; }
+int64_t code_bytes(int64_t rows, int64_t cols, int32_t fmt) {
+  return fmt == MX_FMT_MXFP8 ? rows * cols : rows * (cols / 2);
+}
+size_t round_up(size_t v, size_t a) { return (v + a - 1) / a * a; }
+
+struct Workspace {
+  uint8_t* codes;
+  uint8_t* scales;
+  uint16_t* u;
+};
+
+Workspace carve(void* ws, int64_t M, int64_t K, int32_t act_fmt, int32_t rank) {
+  Workspace w;
+  uint8_t* p = (uint8_t*)ws;
+  w.codes = p;
+  p += round_up((size_t)code_bytes(M, K, act_fmt), 256);
+  w.scales = p;
+  p += round_up((size_t)(M * (K / group_of(act_fmt))), 256);
+  w.u = rank > 0 ? (uint16_t*)p : nullptr;
+  return w;
+}
+
+bool finite_pos(float v) { return isfinite(v) && v > 0.0f; }
+
+// Validation shared by mx_linear and mx_linear_q (everything after the activation).
+mx_status check_gemm_tail(int32_t act_fmt, int64_t M, int64_t K, const mx_qmatrix* w,
+                          const uint16_t* bias, int32_t epilogue, int32_t out_dtype, void* out,
+                          int64_t ld_out, uint8_t* out_scales) {
+  if (!w) return fail(MX_ERR_NULL, "w is NULL");
+  if (!w->codes || !w->scales) return fail(MX_ERR_NULL, "w->codes / w->scales is NULL");
+  if (!out && M != 0) return fail(MX_ERR_NULL, "out is NULL");
+  if (!fmt_ok(act_fmt) || !fmt_ok(w->fmt)) return fail(MX_ERR_UNSUPPORTED, "unknown format");
+  const bool mx_pair = w->fmt == MX_FMT_MXFP4 && (act_fmt == MX_FMT_MXFP4 || act_fmt == MX_FMT_MXFP8);
+  const bool nv_pair = w->fmt == MX_FMT_NVFP4 && act_fmt == MX_FMT_NVFP4;
+  if (!mx_pair && !nv_pair)
+    return fail(MX_ERR_UNSUPPORTED, "format pair (act %d, weight %d) not provided", act_fmt, w->fmt);
+  if (M < 0 || K <= 0) return fail(MX_ERR_SHAPE, "M must be >= 0 and K > 0");
+  if (w->cols != K) return fail(MX_ERR_SHAPE, "w->cols (%lld) != K (%lld)", (long long)w->cols, (long long)K);
+  if (w->rows < 1) return fail(MX_ERR_SHAPE, "w->rows must be >= 1");
+  if (K % 32) return fail(MX_ERR_SHAPE, "K (%lld) must be a multiple of 32", (long long)K);
+  if (M > INT32_MAX || w->rows > INT32_MAX || K > INT32_MAX)
+    return fail(MX_ERR_SHAPE, "M, N and K must fit in 31 bits");
+  if (nv_pair && !finite_pos(w->global_scale))
+    return fail(MX_ERR_SHAPE, "NVFP4 weight global scale must be finite and > 0");
+  if (!aligned(w->codes, 16) || !aligned(w->scales, 8))
+    return fail(MX_ERR_ALIGN, "weight codes need 16-byte and scales 8-byte alignment");
+  if (bias && !aligned(bias, 8)) return fail(MX_ERR_ALIGN, "bias needs 8-byte alignment");
+  const int64_t N = w->rows;
+  if (epilogue == MX_EPI_BIAS || epilogue == MX_EPI_BIAS_GELU) {
+    if (out_dtype != MX_OUT_BF16 && out_dtype != MX_OUT_F32)
+      return fail(MX_ERR_UNSUPPORTED, "unknown output dtype %d", out_dtype);
+    if (ld_out < N) return fail(MX_ERR_SHAPE, "ld_out (%lld) < N (%lld)", (long long)ld_out, (long long)N);
+    if (ld_out % 4) return fail(MX_ERR_ALIGN, "ld_out must be a multiple of 4");
+    if (M != 0 && !aligned(out, out_dtype == MX_OUT_F32 ? 16 : 8))
+      return fail(MX_ERR_ALIGN, "out is not aligned for vector stores");
+  } else if (epilogue == MX_EPI_BIAS_GELU_QUANT_MXFP4) {
+    if (!out_scales && M != 0) return fail(MX_ERR_NULL, "out_scales is NULL");
+    if (N % 32) return fail(MX_ERR_SHAPE, "re-quantizing epilogue needs N %% 32 == 0");
+    if (ld_out != N) return fail(MX_ERR_SHAPE, "re-quantizing epilogue needs ld_out == N");
+    if (M != 0 && !aligned(out, 8)) return fail(MX_ERR_ALIGN, "out codes need 8-byte alignment");
+  } else {
+    return fail(MX_ERR_UNSUPPORTED, "unknown epilogue %d", epilogue);
+  }
+  return MX_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+int mx_abi_version(void) { return MX_ABI_VERSION; }
+
+const char* mx_status_string(int status) {
+  switch (status) {
+    case MX_OK: return "MX_OK";
+    case MX_ERR_NULL: return "MX_ERR_NULL";
+    case MX_ERR_SHAPE: return "MX_ERR_SHAPE";
+    case MX_ERR_ALIGN: return "MX_ERR_ALIGN";
+    case MX_ERR_UNSUPPORTED: return "MX_ERR_UNSUPPORTED";
+    case MX_ERR_WORKSPACE: return "MX_ERR_WORKSPACE";
+    case MX_ERR_HIP: return "MX_ERR_HIP";
+    default: return "MX_UNKNOWN_STATUS";
+  }
+}
+
+const char* mx_last_error(void) { return g_err; }
+
+float mx_nvfp4_global_scale(float amax) {
+  if (!(amax > 0.0f) || !isfinite(amax)) return 1.0f;
+  volatile float num = amax, den = 2688.0f;  // 6 (max E2M1) * 448 (max E4M3)
+  return num / den;
+}
+
+mx_status mx_quantize(const uint16_t* x, int64_t rows, int64_t cols, int64_t ld_x, int32_t fmt,
+                      float global_scale, void* codes, uint8_t* scales, void* stream) {
+  g_err[0] = 0;
+  if (!fmt_ok(fmt)) return fail(MX_ERR_UNSUPPORTED, "unknown format %d", fmt);
+  const int G = group_of(fmt);
+  if (rows < 0 || cols <= 0) return fail(MX_ERR_SHAPE, "rows must be >= 0 and cols > 0");
+  if (cols % G) return fail(MX_ERR_SHAPE, "cols (%lld) must be a multiple of %d", (long long)cols, G);
+  if (ld_x < cols) return fail(MX_ERR_SHAPE, "ld_x < cols");
+  if (fmt == MX_FMT_NVFP4 && !finite_pos(global_scale))
+    return fail(MX_ERR_SHAPE, "NVFP4 global scale must be finite and > 0");
+  if (rows == 0) return MX_OK;
+  if (!x || !codes || !scales) return fail(MX_ERR_NULL, "x, codes and scales must be non-NULL");
+  if (!aligned(x, 16) || ld_x % 8) return fail(MX_ERR_ALIGN, "x needs 16-byte alignment and ld_x %% 8 == 0");
+  if (!aligned(codes, fmt == MX_FMT_MXFP8 ? 8 : 4)) return fail(MX_ERR_ALIGN, "codes misaligned");
+  hipStream_t s = (hipStream_t)stream;
+  hipError_t e = fmt == MX_FMT_NVFP4
+                     ? mxk::launch_quant_nv(x, rows, cols, ld_x, global_scale, (uint8_t*)codes, scales, s)
+                     : mxk::launch_quant_mx(x, rows, cols, ld_x, fmt == MX_FMT_MXFP8 ? 1 : 0,
+                                            (uint8_t*)codes, scales, s);
+  return hip_status(e, "mx_quantize launch");
+}
+
+mx_status mx_dequantize(const mx_qmatrix* q, uint16_t* y, int64_t ld_y, void* stream) {
+  g_err[0] = 0;
+  if (!q) return fail(MX_ERR_NULL, "q is NULL");
+  if (!fmt_ok(q->fmt)) return fail(MX_ERR_UNSUPPORTED, "unknown format %d", q->fmt);
+  const int G = group_of(q->fmt);
+  if (q->rows < 0 || q->cols <= 0 || q->cols % G) return fail(MX_ERR_SHAPE, "bad rows/cols");
+  if (ld_y < q->cols) return fail(MX_ERR_SHAPE, "ld_y < cols");
+  if (q->fmt == MX_FMT_NVFP4 && !finite_pos(q->global_scale))
+    return fail(MX_ERR_SHAPE, "NVFP4 global scale must be finite and > 0");
+  if (q->rows == 0) return MX_OK;
+  if (!q->codes || !q->scales || !y) return fail(MX_ERR_NULL, "codes, scales and y must be non-NULL");
+  if (!aligned(y, 16) || ld_y % 8) return fail(MX_ERR_ALIGN, "y needs 16-byte alignment and ld_y %% 8 == 0");
+  if (!aligned(q->codes, q->fmt == MX_FMT_MXFP8 ? 8 : 4)) return fail(MX_ERR_ALIGN, "codes misaligned");
+  hipError_t e = mxk::launch_dequant((const uint8_t*)q->codes, q->scales, q->rows, q->cols, q->fmt,
+                                     q->global_scale, y, ld_y, (hipStream_t)stream);
+  return hip_status(e, "mx_dequantize launch");
+}
+
+mx_status mx_absmax(const uint16_t* x, int64_t rows, int64_t cols, int64_t ld_x, float* amax,
+                    void* stream) {
+  g_err[0] = 0;
+  if (!x || !amax) return fail(MX_ERR_NULL, "x and amax must be non-NULL");
+  if (rows < 0 || cols < 0 || ld_x < cols) return fail(MX_ERR_SHAPE, "bad rows/cols/ld_x");
+  if (!aligned(amax, 4)) return fail(MX_ERR_ALIGN, "amax misaligned");
+  return hip_status(mxk::launch_absmax(x, rows, cols, ld_x, amax, (hipStream_t)stream),
+                    "mx_absmax launch");
+}
+
+size_t mx_linear_workspace_bytes(int64_t M, int64_t K, int32_t act_fmt, int32_t rank) {
+  if (M <= 0 || K <= 0 || !fmt_ok(act_fmt)) return 0;
+  size_t b = round_up((size_t)code_bytes(M, K, act_fmt), 256) +
+             round_up((size_t)(M * (K / group_of(act_fmt))), 256);
+  if (rank > 0) b += round_up((size_t)M * (size_t)rank * 2, 256);
+  return b;
+}
+
+static mx_status run_gemm(const uint8_t* a_codes, const uint8_t* a_scales, float a_gscale,
+                          int32_t act_fmt, int64_t M, int64_t K, const mx_qmatrix* w,
+                          const uint16_t* bias, const uint16_t* lr_u, const mx_lowrank* lr,
+                          int32_t epilogue, int32_t out_dtype, void* out, int64_t ld_out,
+                          uint8_t* out_scales, hipStream_t s) {
+  mxk::GemmParams p;
+  p.a_codes = a_codes;
+  p.a_scales = a_scales;
+  p.w_codes = (const uint8_t*)w->codes;
+  p.w_scales = w->scales;
+  p.bias = bias;
+  p.lr_u = lr_u;
+  p.lr_up = lr ? lr->up : nullptr;
+  p.R = lr ? lr->rank : 0;
+  p.out = out;
+  p.out_scales = out_scales;
+  p.ld_out = ld_out;
+  p.out_scale = w->fmt == MX_FMT_NVFP4 ? a_gscale * w->global_scale : 1.0f;
+  p.M = (int)M;
+  p.N = (int)w->rows;
+  p.K = (int)K;
+  p.epi = epilogue == MX_EPI_BIAS ? mxk::EPI_BIAS
+                                  : epilogue == MX_EPI_BIAS_GELU ? mxk::EPI_GELU : mxk::EPI_GELU_QUANT;
+  p.out_f32 = out_dtype == MX_OUT_F32 ? 1 : 0;
+  hipError_t e = w->fmt == MX_FMT_NVFP4 ? mxk::launch_gemm_nv(p, s)
+                                         : mxk::launch_gemm_mx(p, act_fmt == MX_FMT_MXFP8, s);
+  return hip_status(e, "GEMM launch");
+}
+
+mx_status mx_linear(const uint16_t* a, int64_t M, int64_t K, int64_t ld_a, int32_t act_fmt,
+                    float act_global_scale, const mx_qmatrix* w, const uint16_t* bias,
+                    const mx_lowrank* lr, int32_t epilogue, int32_t out_dtype, void* out,
+                    int64_t ld_out, uint8_t* out_scales, void* workspace, size_t workspace_bytes,
+                    void* stream) {
+  g_err[0] = 0;
+  mx_status st = check_gemm_tail(act_fmt, M, K, w, bias, epilogue, out_dtype, out, ld_out, out_scales);
+  if (st != MX_OK) return st;
+  if (!a && M != 0) return fail(MX_ERR_NULL, "a is NULL");
+  if (ld_a < K) return fail(MX_ERR_SHAPE, "ld_a < K");
+  if ((M != 0 && !aligned(a, 16)) || ld_a % 8)
+    return fail(MX_ERR_ALIGN, "a needs 16-byte alignment and ld_a %% 8 == 0");
+  if (act_fmt == MX_FMT_NVFP4 && !finite_pos(act_global_scale))
+    return fail(MX_ERR_SHAPE, "NVFP4 activation global scale must be finite and > 0");
+  const int32_t rank = lr ? lr->rank : 0;
+  if (lr) {
+    if (act_fmt == MX_FMT_NVFP4) return fail(MX_ERR_UNSUPPORTED, "low-rank branch needs an MX format");
+    if (!lr->down || !lr->up) return fail(MX_ERR_NULL, "lr->down / lr->up is NULL");
+    if (rank < 1 || rank > 64 || rank % 16) return fail(MX_ERR_SHAPE, "rank must be 16, 32, 48 or 64");
+    if (!aligned(lr->down, 16) || !aligned(lr->up, 16)) return fail(MX_ERR_ALIGN, "low-rank factors need 16-byte alignment");
+  }
+  if (M == 0) return MX_OK;
+  const size_t need = mx_linear_workspace_bytes(M, K, act_fmt, rank);
+  if (!workspace || workspace_bytes < need)
+    return fail(MX_ERR_WORKSPACE, "workspace of %zu bytes needed, %zu given", need, workspace_bytes);
+  if (!aligned(workspace, 256)) return fail(MX_ERR_ALIGN, "workspace needs 256-byte alignment");
+
+  hipStream_t s = (hipStream_t)stream;
+  Workspace ws = carve(workspace, M, K, act_fmt, rank);
+  hipError_t e;
+  if (act_fmt == MX_FMT_NVFP4)
+    e = mxk::launch_quant_nv(a, M, K, ld_a, act_global_scale, ws.codes, ws.scales, s);
+  else
+    e = mxk::launch_quant_mx(a, M, K, ld_a, act_fmt == MX_FMT_MXFP8 ? 1 : 0, ws.codes, ws.scales, s);
+  if (e != hipSuccess) return hip_status(e, "activation quantizer launch");
+  if (rank > 0) {
+    e = mxk::launch_lowrank_down(a, ld_a, lr->down, (int)M, (int)K, rank, ws.u, s);
+    if (e != hipSuccess) return hip_status(e, "low-rank launch");
+  }
+  return run_gemm(ws.codes, ws.scales, act_global_scale, act_fmt, M, K, w, bias, ws.u, lr,
+                  epilogue, out_dtype, out, ld_out, out_scales, s);
+}
+
+mx_status mx_linear_q(const mx_qmatrix* a, const mx_qmatrix* w, const uint16_t* bias,
+                      int32_t epilogue, int32_t out_dtype, void* out, int64_t ld_out,
+                      uint8_t* out_scales, void* stream) {
+  g_err[0] = 0;
+  if (!a) return fail(MX_ERR_NULL, "a is NULL");
+  mx_status st = check_gemm_tail(a->fmt, a->rows, a->cols, w, bias, epilogue, out_dtype, out,
+                                 ld_out, out_scales);
+  if (st != MX_OK) return st;
+  if (a->rows == 0) return MX_OK;
+  if (!a->codes || !a->scales) return fail(MX_ERR_NULL, "a->codes / a->scales is NULL");
+  if (!aligned(a->codes, 16) || !aligned(a->scales, 8))
+    return fail(MX_ERR_ALIGN, "activation codes need 16-byte and scales 8-byte alignment");
+  if (a->fmt == MX_FMT_NVFP4 && !finite_pos(a->global_scale))
+    return fail(MX_ERR_SHAPE, "NVFP4 activation global scale must be finite and > 0");
+  return run_gemm((const uint8_t*)a->codes, a->scales, a->global_scale, a->fmt, a->rows, a->cols,
+                  w, bias, nullptr, nullptr, epilogue, out_dtype, out, ld_out, out_scales,
+                  (hipStream_t)stream);
+}
+
+}  // extern "C"

@@ -1,0 +1,156 @@
+// Device-side helpers shared by the gfx950 kernels of this library (internal header).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include <type_traits>
+
+namespace mxk {
+
+typedef int v4i __attribute__((ext_vector_type(4)));
+typedef int v8i __attribute__((ext_vector_type(8)));
+typedef float v4f __attribute__((ext_vector_type(4)));
+typedef float v16f __attribute__((ext_vector_type(16)));
+typedef __bf16 v8bf __attribute__((ext_vector_type(8)));
+
+// ---------------------------------------------------------------------------------------------
+// storage conversions
+// ---------------------------------------------------------------------------------------------
+__device__ __forceinline__ float bf16_to_f32(uint32_t b16) { return __uint_as_float(b16 << 16); }
+
+// fp32 -> bf16, round to nearest even (NaN -> quiet NaN, overflow -> inf).
+__device__ __forceinline__ uint32_t f32_to_bf16_rne(float f) {
+  uint32_t u = __float_as_uint(f);
+  if ((u & 0x7FFFFFFFu) > 0x7F800000u) return 0x7FC0u;
+  u += 0x7FFFu + ((u >> 16) & 1u);
+  return u >> 16;
+}
+
+// fp64 -> bf16 with one rounding (nearest even) of the exact double value.
+__device__ __forceinline__ uint32_t f64_to_bf16_rne(double v) {
+  uint64_t u = (uint64_t)__double_as_longlong(v);
+  uint32_t sign = (uint32_t)(u >> 48) & 0x8000u;
+  uint64_t ua = u & 0x7FFFFFFFFFFFFFFFull;
+  if (ua > 0x7FF0000000000000ull) return 0x7FC0u;  // NaN
+  double a = __longlong_as_double((long long)ua);
+  if (a < 0x1p-126) {  // BF16 subnormal range: quantum 2^-133 (result 128 = smallest normal)
+    double m = __builtin_rint(a * 0x1p133);
+    return sign | (uint32_t)m;
+  }
+  // keep 7 of the 52 stored mantissa bits, ties to even
+  uint64_t r = (ua + 0xFFFFFFFFFFFull + ((ua >> 45) & 1ull)) >> 45;
+  int64_t e = (int64_t)(r >> 7) - 1023 + 127;
+  if (e >= 255) return sign | 0x7F80u;
+  return sign | (uint32_t)((e << 7) | (int64_t)(r & 0x7F));
+}
+
+__device__ __forceinline__ float f16_to_f32(uint32_t h) {
+  const unsigned short hs = (unsigned short)h;
+  _Float16 hv;
+  __builtin_memcpy(&hv, &hs, 2);
+  return (float)hv;
+}
+
+typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
+
+// 16-byte streaming load (read once, do not keep in cache)
+__device__ __forceinline__ uint4 load_stream16(const void* p) {
+  const u32x4 v = __builtin_nontemporal_load((const u32x4*)p);
+  return make_uint4(v.x, v.y, v.z, v.w);
+}
+
+// Raw buffer loads (gfx9 descriptor: no stride, bounds checked against num_records; an access
+// past the end reads zero).
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* base, uint32_t bytes) {
+  return __builtin_amdgcn_make_buffer_rsrc((void*)base, (short)0, (int)bytes, 0x00020000);
+}
+__device__ __forceinline__ uint4 load16(__amdgpu_buffer_rsrc_t r, uint32_t off) {
+  const auto v = __builtin_amdgcn_raw_buffer_load_b128(r, (int)off, 0, 0);
+  return make_uint4(v[0], v[1], v[2], v[3]);
+}
+__device__ __forceinline__ uint2 load8(__amdgpu_buffer_rsrc_t r, uint32_t off) {
+  const auto v = __builtin_amdgcn_raw_buffer_load_b64(r, (int)off, 0, 0);
+  return make_uint2(v[0], v[1]);
+}
+__device__ __forceinline__ uint32_t load4(__amdgpu_buffer_rsrc_t r, uint32_t off) {
+  return (uint32_t)__builtin_amdgcn_raw_buffer_load_b32(r, (int)off, 0, 0);
+}
+__device__ __forceinline__ uint32_t load1(__amdgpu_buffer_rsrc_t r, uint32_t off) {
+  return (uint32_t)__builtin_amdgcn_raw_buffer_load_b8(r, (int)off, 0, 0);
+}
+
+// ---------------------------------------------------------------------------------------------
+// element encodings (OCP MX v1.0).  Inputs are exact non-negative magnitudes.
+// ---------------------------------------------------------------------------------------------
+// E2M1 magnitude code of q, round to nearest even, saturating at 6.
+//  q < 1: the grid is 0, 0.5 (step 0.5): code = rne(2q) in {0, 1, 2}.
+//  q >= 1: one mantissa bit: round the binary32 pattern at bit 22, then the exponent and the
+//  kept bit give the code directly (1.0 -> 2 ... 6.0 -> 7, 8.0 and above saturate to 7).
+__device__ __forceinline__ uint32_t e2m1_code(float q) {
+  if (q < 1.0f) return (uint32_t)__builtin_rintf(q * 2.0f);
+  uint32_t u = __float_as_uint(q);
+  uint32_t r = (u + 0x1FFFFFu + ((u >> 22) & 1u)) >> 22;
+  uint32_t c = r - 252u;
+  return c > 7u ? 7u : c;
+}
+
+// E4M3 magnitude code of q, round to nearest even, subnormal step 2^-9, saturating at 448.
+__device__ __forceinline__ uint32_t e4m3_code(float q) {
+  if (q < 0.015625f) return (uint32_t)__builtin_rintf(q * 512.0f);
+  uint32_t u = __float_as_uint(q);
+  uint32_t r = (u + 0x7FFFFu + ((u >> 20) & 1u)) >> 20;
+  uint32_t c = r - (120u << 3);
+  return c > 126u ? 126u : c;
+}
+
+// Same from an fp64 magnitude (one rounding of the double value).
+__device__ __forceinline__ uint32_t e4m3_code_f64(double q) {
+  if (q < 0.015625) return (uint32_t)__builtin_rint(q * 512.0);
+  uint64_t u = (uint64_t)__double_as_longlong(q);
+  uint64_t r = (u + 0xFFFFFFFFFFFFull + ((u >> 49) & 1ull)) >> 49;
+  int64_t c = (int64_t)r - ((1023 - 7) << 3);
+  return c > 126 ? 126u : (uint32_t)c;
+}
+
+// Decoded magnitudes.
+__device__ __forceinline__ float e2m1_value(uint32_t code) {
+  // 0, 0.5, 1, 1.5, 2, 3, 4, 6 as binary32 exponent/mantissa, sign from bit 3
+  uint32_t m = code & 7u;
+  uint32_t bits = m == 0 ? 0u : m == 1 ? 0x3F000000u : ((126u + (m >> 1)) << 23) | ((m & 1u) << 22);
+  return __uint_as_float(bits | ((code & 8u) << 28));
+}
+
+__device__ __forceinline__ float e4m3_value(uint32_t b) {
+  uint32_t e = (b >> 3) & 0xFu, m = b & 7u;
+  float v;
+  if (e == 0xF && m == 7) return __uint_as_float(0x7FC00000u);
+  if (e == 0) v = (float)m * 0x1p-9f;
+  else v = __uint_as_float(((e + 120u) << 23) | (m << 20));
+  return (b & 0x80u) ? -v : v;
+}
+
+// ---------------------------------------------------------------------------------------------
+// cross-lane helpers
+// ---------------------------------------------------------------------------------------------
+// max with the lane xor 1 / xor 2 inside each quad (DPP quad_perm)
+__device__ __forceinline__ uint32_t quad_xor1(uint32_t v) {
+  return (uint32_t)__builtin_amdgcn_mov_dpp((int)v, 0xB1, 0xF, 0xF, false);  // [1,0,3,2]
+}
+__device__ __forceinline__ uint32_t quad_xor2(uint32_t v) {
+  return (uint32_t)__builtin_amdgcn_mov_dpp((int)v, 0x4E, 0xF, 0xF, false);  // [2,3,0,1]
+}
+
+__device__ __forceinline__ int lane_id() { return (int)__lane_id(); }
+
+// Compile-time loop: f(std::integral_constant<int, I>) for I = 0 .. N-1.  Register arrays indexed
+// through it always see constant indices, whatever the unroller decides for large bodies.
+template <int N, int I = 0, typename F>
+__device__ __forceinline__ void static_for(F&& f) {
+  if constexpr (I < N) {
+    f(std::integral_constant<int, I>{});
+    static_for<N, I + 1>(f);
+  }
+}
+
+}  // namespace mxk

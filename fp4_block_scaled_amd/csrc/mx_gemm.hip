@@ -1,0 +1,575 @@
+// Block-scaled GEMMs for gfx950 with fused epilogues.
+//
+// MXFP4 W4A4 (MXFP4 model cards, Quantization Details) and MXFP8 x MXFP4 W4A8 (W4A8 SVDQuant
+// page) run on the CDNA4 scaled MFMA V_MFMA_SCALE_F32_32X32X64_F8F6F4: its K of 64 is two
+// 32-element scale blocks, each lane supplies one E8M0 byte per operand and the bytes of the
+// lanes of half b scale block b, so the per-32 MX scales cost nothing.  The MFMA "A" operand is
+// the weight tile (n rows), the "B" operand the activation tile (m rows), which puts 16 values
+// of one output row m, 4 consecutive n at a time, in each lane: the epilogue can store them as
+// vectors and reduce a 32-wide re-quantization group with a single cross-lane exchange.
+//
+// K ordering inside a 256-element K chunk: the sum over k is order-free, so MFMA step s (0..3)
+// takes the chunk's 32-element blocks s and 4 + s as its two scale blocks.  The scale of block
+// b comes from the lanes of half b (lane / 32), so a lane of half h needs the E8M0 bytes of
+// blocks 4h + s, s = 0..3: the contiguous dword [4h, 4h+4) of the row's 8 chunk scales, op_sel
+// s picking the byte.  FP4 lanes of half h hold their block whole (64 contiguous bytes per row
+// and chunk); FP8 lanes split theirs (see mx_step).  Both operands pair the same k.
+//
+// Staging: a 256 x 256 output tile per workgroup (4 waves, 128 x 128 each, 4 x 4 MFMA blocks),
+// K chunks of 256 double-buffered in LDS.  LDS rows hold 16-byte chunks XOR-swizzled by the
+// row index so that the 16-byte fragment reads of 8 consecutive rows hit distinct banks.
+//
+// NVFP4 (NVFP4 model card, Model Details) has E4M3 scales per 16 elements that the scaled MFMA
+// cannot apply, and code * scale needs up to 6 significant bits, more than FP8 holds; it is
+// dequantized exactly to BF16 after staging and run on V_MFMA_F32_32X32X16_BF16, with the
+// product of the two FP32 global scales applied in the epilogue.
+#include "mx_common.h"
+#include "mx_internal.h"
+
+namespace mxk {
+
+constexpr int KC = 256;  // K elements per staged chunk
+
+__device__ __forceinline__ float gelu_tanh_f32(float y) {
+  const float c = 0.7978845608028654f;  // sqrt(2/pi)
+  return 0.5f * y * (1.0f + tanhf(c * (y + 0.044715f * y * y * y)));
+}
+
+// byte offset of 16-byte chunk c of LDS row `row` (rows of `rowb` bytes)
+__device__ __forceinline__ int swz(int row, int c, int rowb) {
+  return row * rowb + ((c ^ (row & 7)) << 4);
+}
+
+// ---------------------------------------------------------------------------------------------
+// epilogue: one 32 (n) x 32 (m) accumulator block
+// ---------------------------------------------------------------------------------------------
+// lane l holds m = mb + (l & 31) and n = nb + 8a + 4h + i for a, i in 0..3 (h = l >> 5):
+// acc[4a + i].
+__device__ __forceinline__ void epilogue_block(const GemmParams& p, v16f acc, int nb, int mb) {
+  const int lane = lane_id();
+  const int h = lane >> 5;
+  const int m = mb + (lane & 31);
+  float v[16];
+#pragma unroll
+  for (int e = 0; e < 16; ++e) v[e] = acc[e] * p.out_scale;
+  // bias (FP16, added in fp32 after accumulation)
+  if (p.bias) {
+#pragma unroll
+    for (int a = 0; a < 4; ++a) {
+      const int n = nb + 8 * a + 4 * h;
+      if (n + 3 < p.N) {
+        const uint2 b = *(const uint2*)(p.bias + n);
+        v[4 * a + 0] += f16_to_f32(b.x & 0xFFFFu);
+        v[4 * a + 1] += f16_to_f32(b.x >> 16);
+        v[4 * a + 2] += f16_to_f32(b.y & 0xFFFFu);
+        v[4 * a + 3] += f16_to_f32(b.y >> 16);
+      } else {
+#pragma unroll
+        for (int i = 0; i < 4; ++i)
+          if (n + i < p.N) v[4 * a + i] += f16_to_f32(p.bias[n + i]);
+      }
+    }
+  }
+  if (p.epi != EPI_BIAS) {
+#pragma unroll
+    for (int e = 0; e < 16; ++e) v[e] = gelu_tanh_f32(v[e]);
+  }
+  if (p.epi == EPI_GELU_QUANT) {
+    // MXFP4 re-quantization of h along n: the 32 values of this block for row m live in lanes
+    // l and l ^ 32.  Same rule as the activation quantizer, on binary32 values.
+    uint32_t amax = 0;
+#pragma unroll
+    for (int e = 0; e < 16; ++e) amax = max(amax, __float_as_uint(v[e]) & 0x7FFFFFFFu);
+    amax = max(amax, (uint32_t)__shfl_xor((int)amax, 32));
+    const bool bad = amax >= 0x7F800000u;
+    int ex = (int)(amax >> 23) - 129;  // floor(log2 amax) - 2, clamped below
+    if (ex < -127) ex = -127;
+    const float inv = __uint_as_float((uint32_t)(127 - ex) << 23);
+    uint32_t run[4];
+#pragma unroll
+    for (int a = 0; a < 4; ++a) {
+      uint32_t r = 0;
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const uint32_t u = __float_as_uint(v[4 * a + i]);
+        const float q = __uint_as_float(u & 0x7FFFFFFFu) * inv;
+        r |= (e2m1_code(q) | ((u >> 28) & 8u)) << (4 * i);
+      }
+      run[a] = bad ? 0u : r;  // 4 codes = 2 bytes at byte offset 4a + 2h of the block
+    }
+    const uint32_t X = run[0] | (run[1] << 16), Y = run[2] | (run[3] << 16);
+    const uint32_t recv = (uint32_t)__shfl_xor((int)(h ? X : Y), 32);
+    uint32_t d0, d1;
+    if (h == 0) {  // bytes 0..7: own runs 0,1 (low halves) and the partner's runs 0,1
+      d0 = (X & 0xFFFFu) | (recv << 16);
+      d1 = (X >> 16) | (recv & 0xFFFF0000u);
+    } else {       // bytes 8..15: partner's runs 2,3 and own runs 2,3 (high halves)
+      d0 = (recv & 0xFFFFu) | (Y << 16);
+      d1 = (recv >> 16) | (Y & 0xFFFF0000u);
+    }
+    if (m < p.M && nb < p.N) {
+      uint8_t* codes = (uint8_t*)p.out;
+      *(uint2*)(codes + (int64_t)m * (p.N >> 1) + (nb >> 1) + 8 * h) = make_uint2(d0, d1);
+      if (h == 0)
+        p.out_scales[(int64_t)m * (p.N >> 5) + (nb >> 5)] = bad ? (uint8_t)0xFF : (uint8_t)(ex + 127);
+    }
+    return;
+  }
+  if (m >= p.M) return;
+#pragma unroll
+  for (int a = 0; a < 4; ++a) {
+    const int n = nb + 8 * a + 4 * h;
+    if (p.out_f32) {
+      float* o = (float*)p.out + (int64_t)m * p.ld_out + n;
+      if (n + 3 < p.N) {
+        *(float4*)o = make_float4(v[4 * a], v[4 * a + 1], v[4 * a + 2], v[4 * a + 3]);
+      } else {
+#pragma unroll
+        for (int i = 0; i < 4; ++i)
+          if (n + i < p.N) o[i] = v[4 * a + i];
+      }
+    } else {
+      uint16_t* o = (uint16_t*)p.out + (int64_t)m * p.ld_out + n;
+      const uint32_t b0 = f32_to_bf16_rne(v[4 * a]), b1 = f32_to_bf16_rne(v[4 * a + 1]);
+      const uint32_t b2 = f32_to_bf16_rne(v[4 * a + 2]), b3 = f32_to_bf16_rne(v[4 * a + 3]);
+      if (n + 3 < p.N) {
+        *(uint2*)o = make_uint2(b0 | (b1 << 16), b2 | (b3 << 16));
+      } else {
+        const uint32_t bb[4] = {b0, b1, b2, b3};
+#pragma unroll
+        for (int i = 0; i < 4; ++i)
+          if (n + i < p.N) o[i] = (uint16_t)bb[i];
+      }
+    }
+  }
+}
+
+// low-rank term: acc += up_t[n, :] . u[m, :] over rank R (BF16 MFMA 32x32x16)
+__device__ __forceinline__ v16f lowrank_block(const GemmParams& p, v16f acc, int nb, int mb) {
+  const int lane = lane_id();
+  const int h = lane >> 5;
+  const int n = min(nb + (lane & 31), p.N - 1);
+  const int m = min(mb + (lane & 31), p.M - 1);
+  for (int r0 = 0; r0 < p.R; r0 += 16) {
+    const uint4 wa = *(const uint4*)(p.lr_up + (int64_t)n * p.R + r0 + 8 * h);
+    const uint4 ub = *(const uint4*)(p.lr_u + (int64_t)m * p.R + r0 + 8 * h);
+    v8bf fa, fb;
+    __builtin_memcpy(&fa, &wa, 16);
+    __builtin_memcpy(&fb, &ub, 16);
+    acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fa, fb, acc, 0, 0, 0);
+  }
+  return acc;
+}
+
+// ---------------------------------------------------------------------------------------------
+// MX GEMM (W: E2M1, A: E2M1 or E4M3)
+// ---------------------------------------------------------------------------------------------
+template <int BM, int BN, bool AFP8>
+struct MxTile {
+  static_assert((BM == 128 || BM == 256) && (BN == 128 || BN == 256), "tile sizes");
+  static constexpr int ACH = AFP8 ? 16 : 8;          // 16-byte chunks per A row per K chunk
+  static constexpr int WROWB = 128, AROWB = ACH * 16;
+  static constexpr int W_BYTES = BN * WROWB, A_BYTES = BM * AROWB;
+  static constexpr int WS_BYTES = BN * 8, AS_BYTES = BM * 8;
+  static constexpr int STAGE = W_BYTES + A_BYTES + WS_BYTES + AS_BYTES;
+  static constexpr int FN = BN / 64, FM = BM / 64;    // 32x32 blocks per wave (2 x 2 waves)
+  static constexpr int WLD = BN * 8 / 256, ALD = BM * ACH / 256;
+};
+
+template <int BM, int BN, bool AFP8, int S>
+__device__ __forceinline__ void mx_step(const uint8_t* sW, const uint8_t* sA, int wn0, int wm0,
+                                        const uint32_t (&wsc)[BN / 64],
+                                        const uint32_t (&asc)[BM / 64],
+                                        v16f (&acc)[BN / 64][BM / 64]) {
+  using T = MxTile<BM, BN, AFP8>;
+  const int lane = lane_id();
+  const int r32 = lane & 31, h = lane >> 5;
+  v8i wf[T::FN], af[T::FM];
+#pragma unroll
+  for (int i = 0; i < T::FN; ++i) {
+    const int row = wn0 + 32 * i + r32;
+    const uint4 d = *(const uint4*)(sW + swz(row, 4 * h + S, T::WROWB));
+    wf[i] = v8i{(int)d.x, (int)d.y, (int)d.z, (int)d.w, 0, 0, 0, 0};
+  }
+#pragma unroll
+  for (int j = 0; j < T::FM; ++j) {
+    const int row = wm0 + 32 * j + r32;
+    if (AFP8) {
+      // An FP8 operand lane of half h carries, in bytes 0-15, elements 16h..16h+15 of the
+      // MFMA's first 32-element block and, in bytes 16-31, the same elements of its second
+      // block (an FP4 lane carries its own block whole).  With block 0 = K block S and block 1
+      // = K block 4 + S of the chunk, that is 16-byte chunk 2S + h and chunk 8 + 2S + h.
+      const uint4 d0 = *(const uint4*)(sA + swz(row, 2 * S + h, T::AROWB));
+      const uint4 d1 = *(const uint4*)(sA + swz(row, 8 + 2 * S + h, T::AROWB));
+      af[j] = v8i{(int)d0.x, (int)d0.y, (int)d0.z, (int)d0.w,
+                  (int)d1.x, (int)d1.y, (int)d1.z, (int)d1.w};
+    } else {
+      const uint4 d = *(const uint4*)(sA + swz(row, 4 * h + S, T::AROWB));
+      af[j] = v8i{(int)d.x, (int)d.y, (int)d.z, (int)d.w, 0, 0, 0, 0};
+    }
+  }
+  static_for<T::FN>([&](auto i) {
+    static_for<T::FM>([&](auto j) {
+      acc[i][j] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(
+          wf[i], af[j], acc[i][j], 4, AFP8 ? 0 : 4, S, (int)wsc[i], S, (int)asc[j]);
+    });
+  });
+}
+
+// Global -> register staging of one K chunk.  Buffer loads: the descriptor of each operand
+// starts at the tile's first row and ends at the matrix end, so rows past M or N read as zero
+// without clamping, and every load of a thread shares one VGPR offset pattern.
+template <int BM, int BN, bool AFP8, bool KAL>
+struct MxStage {
+  using T = MxTile<BM, BN, AFP8>;
+  uint4 w[T::WLD], a[T::ALD];
+  uint2 ws, as;  // this thread's share of the chunk's scale bytes (8 or 4 bytes each)
+};
+
+template <int BM, int BN, bool AFP8, bool KAL>
+__global__ void __launch_bounds__(256, 1) gemm_mx_kernel(GemmParams p) {
+  using T = MxTile<BM, BN, AFP8>;
+  __shared__ __attribute__((aligned(16))) uint8_t smem[2 * T::STAGE];
+
+  const int tid = threadIdx.x;
+  const int lane = tid & 63, wave = tid >> 6;
+  const int wn0 = (wave >> 1) * (BN / 2), wm0 = (wave & 1) * (BM / 2);
+  const int tiles_n = (p.N + BN - 1) / BN;
+  const int tm = blockIdx.x / tiles_n, tn = blockIdx.x - tm * tiles_n;
+  const int m0 = tm * BM, n0 = tn * BN;
+  const int nkc = (p.K + KC - 1) / KC;
+  const int kblocks = p.K >> 5;
+  const uint32_t w_row = (uint32_t)p.K >> 1, a_row = AFP8 ? (uint32_t)p.K : ((uint32_t)p.K >> 1);
+  const uint32_t s_row = (uint32_t)kblocks;
+
+  auto clamp32 = [](uint64_t v) -> uint32_t { return v > 0xFFFFFFFFull ? 0xFFFFFFFFu : (uint32_t)v; };
+  const __amdgpu_buffer_rsrc_t rw = make_rsrc(p.w_codes + (int64_t)n0 * w_row, clamp32((uint64_t)(p.N - n0) * w_row));
+  const __amdgpu_buffer_rsrc_t ra = make_rsrc(p.a_codes + (int64_t)m0 * a_row, clamp32((uint64_t)(p.M - m0) * a_row));
+  const __amdgpu_buffer_rsrc_t rws = make_rsrc(p.w_scales + (int64_t)n0 * s_row, clamp32((uint64_t)(p.N - n0) * s_row));
+  const __amdgpu_buffer_rsrc_t ras = make_rsrc(p.a_scales + (int64_t)m0 * s_row, clamp32((uint64_t)(p.M - m0) * s_row));
+
+  // per-thread offsets of load i: row = i * (256 / CH) + tid / CH, chunk c = tid % CH
+  const uint32_t voff_w = (uint32_t)(tid >> 3) * w_row + (uint32_t)(tid & 7) * 16u;
+  const uint32_t voff_a = (uint32_t)(tid / T::ACH) * a_row + (uint32_t)(tid % T::ACH) * 16u;
+  constexpr int W_ROWS_PER_LD = 256 / 8, A_ROWS_PER_LD = 256 / T::ACH;
+
+  MxStage<BM, BN, AFP8, KAL> st;
+  auto gload = [&](int kc) {
+#pragma unroll
+    for (int i = 0; i < T::WLD; ++i)
+      st.w[i] = load16(rw, voff_w + (uint32_t)(i * W_ROWS_PER_LD) * w_row + (uint32_t)kc * 128u);
+#pragma unroll
+    for (int i = 0; i < T::ALD; ++i)
+      st.a[i] = load16(ra, voff_a + (uint32_t)(i * A_ROWS_PER_LD) * a_row + (uint32_t)kc * T::AROWB);
+    if (KAL) {
+      // the tile's BN (BM) rows of 8 scale bytes are spread over all 256 threads
+      if (BN == 256) st.ws = load8(rws, (uint32_t)tid * s_row + (uint32_t)kc * 8u);
+      else st.ws = make_uint2(load4(rws, (uint32_t)(tid >> 1) * s_row + (uint32_t)kc * 8u + (tid & 1) * 4u), 0u);
+      if (BM == 256) st.as = load8(ras, (uint32_t)tid * s_row + (uint32_t)kc * 8u);
+      else st.as = make_uint2(load4(ras, (uint32_t)(tid >> 1) * s_row + (uint32_t)kc * 8u + (tid & 1) * 4u), 0u);
+    } else {
+      // K not a multiple of the chunk: the last chunk is partial.  Codes past the row end are
+      // zeroed (reading them is in bounds: the next row, or past the buffer end, which reads 0)
+      // and scale bytes are read one by one.
+      const int kb0 = kc * 8;
+#pragma unroll
+      for (int i = 0; i < T::WLD; ++i)
+        if (kb0 + (tid & 7) >= kblocks) st.w[i] = make_uint4(0, 0, 0, 0);
+#pragma unroll
+      for (int i = 0; i < T::ALD; ++i)
+        if (kb0 + (AFP8 ? (tid % T::ACH) >> 1 : tid % T::ACH) >= kblocks) st.a[i] = make_uint4(0, 0, 0, 0);
+      uint32_t wlo = 0, whi = 0, alo = 0, ahi = 0;
+      for (int b = 0; b < 8; ++b) {
+        if (kb0 + b < kblocks) {
+          const uint32_t vw = tid < BN ? load1(rws, (uint32_t)tid * s_row + (uint32_t)(kb0 + b)) : 0u;
+          const uint32_t va = tid < BM ? load1(ras, (uint32_t)tid * s_row + (uint32_t)(kb0 + b)) : 0u;
+          if (b < 4) { wlo |= vw << (8 * b); alo |= va << (8 * b); }
+          else { whi |= vw << (8 * (b - 4)); ahi |= va << (8 * (b - 4)); }
+        }
+      }
+      st.ws = make_uint2(wlo, whi);
+      st.as = make_uint2(alo, ahi);
+    }
+  };
+  // LDS row of load i is i * ROWS_PER_LD + tid / CH, so its XOR swizzle (row & 7) is the
+  // thread's own (tid / CH) & 7 for every i.
+  const int lds_w = (tid >> 3) * T::WROWB + (((tid & 7) ^ ((tid >> 3) & 7)) << 4);
+  const int lds_a = (tid / T::ACH) * T::AROWB + (((tid % T::ACH) ^ ((tid / T::ACH) & 7)) << 4);
+  auto sstore = [&](int buf) {
+    uint8_t* sW = smem + buf * T::STAGE;
+    uint8_t* sA = sW + T::W_BYTES;
+    uint8_t* sWS = sA + T::A_BYTES;
+    uint8_t* sAS = sWS + T::WS_BYTES;
+#pragma unroll
+    for (int i = 0; i < T::WLD; ++i) *(uint4*)(sW + lds_w + i * W_ROWS_PER_LD * T::WROWB) = st.w[i];
+#pragma unroll
+    for (int i = 0; i < T::ALD; ++i) *(uint4*)(sA + lds_a + i * A_ROWS_PER_LD * T::AROWB) = st.a[i];
+    if (KAL) {
+      if (BN == 256) *(uint2*)(sWS + tid * 8) = st.ws;
+      else *(uint32_t*)(sWS + tid * 4) = st.ws.x;
+      if (BM == 256) *(uint2*)(sAS + tid * 8) = st.as;
+      else *(uint32_t*)(sAS + tid * 4) = st.as.x;
+    } else {
+      if (tid < BN) *(uint2*)(sWS + tid * 8) = st.ws;
+      if (tid < BM) *(uint2*)(sAS + tid * 8) = st.as;
+    }
+  };
+
+  v16f acc[T::FN][T::FM];
+  static_for<T::FN>([&](auto i) { static_for<T::FM>([&](auto j) { acc[i][j] = v16f{}; }); });
+
+  gload(0);
+  sstore(0);
+  __syncthreads();
+  const int r32 = lane & 31, h = lane >> 5;
+  for (int kc = 0; kc < nkc; ++kc) {
+    const int buf = kc & 1;
+    // The loop body has no branch, so nothing can be sunk past the MFMAs: the chunk after the
+    // last one is loaded and stored too (its buffer loads are bounds-checked, and that LDS
+    // buffer is never read again).
+    gload(kc + 1);
+    __builtin_amdgcn_sched_barrier(0);  // issue the loads before this chunk's MFMAs
+    {
+      const uint8_t* sW = smem + buf * T::STAGE;
+      const uint8_t* sA = sW + T::W_BYTES;
+      const uint8_t* sWS = sA + T::A_BYTES;
+      const uint8_t* sAS = sWS + T::WS_BYTES;
+      uint32_t wsc[T::FN], asc[T::FM];
+#pragma unroll
+      for (int i = 0; i < T::FN; ++i) wsc[i] = *(const uint32_t*)(sWS + (wn0 + 32 * i + r32) * 8 + 4 * h);
+#pragma unroll
+      for (int j = 0; j < T::FM; ++j) asc[j] = *(const uint32_t*)(sAS + (wm0 + 32 * j + r32) * 8 + 4 * h);
+      mx_step<BM, BN, AFP8, 0>(sW, sA, wn0, wm0, wsc, asc, acc);
+      mx_step<BM, BN, AFP8, 1>(sW, sA, wn0, wm0, wsc, asc, acc);
+      mx_step<BM, BN, AFP8, 2>(sW, sA, wn0, wm0, wsc, asc, acc);
+      mx_step<BM, BN, AFP8, 3>(sW, sA, wn0, wm0, wsc, asc, acc);
+    }
+    // Keep the LDS stores of the next chunk (and their wait on its global loads) behind this
+    // chunk's MFMAs: issuing the MFMAs takes as long as they run, so the loads issued above are
+    // in flight for the whole MFMA block.
+    __builtin_amdgcn_sched_barrier(0);
+    sstore(buf ^ 1);
+    __syncthreads();
+  }
+
+  static_for<T::FN>([&](auto i) {
+    static_for<T::FM>([&](auto j) {
+      const int nb = n0 + wn0 + 32 * i, mb = m0 + wm0 + 32 * j;
+      v16f a = acc[i][j];
+      if (p.R > 0) a = lowrank_block(p, a, nb, mb);
+      if (nb < p.N && mb < p.M) epilogue_block(p, a, nb, mb);
+    });
+  });
+}
+
+// ---------------------------------------------------------------------------------------------
+// NVFP4 GEMM: E2M1 codes with per-16 E4M3 scales, exact dequant to BF16, BF16 MFMA
+// ---------------------------------------------------------------------------------------------
+template <int BM, int BN>
+struct NvTile {
+  static constexpr int ROWB = 128;                   // 256 FP4 codes per row per K chunk
+  static constexpr int W_BYTES = BN * ROWB, A_BYTES = BM * ROWB;
+  static constexpr int WS_BYTES = BN * 16, AS_BYTES = BM * 16;  // 16 E4M3 scales per row
+  static constexpr int STAGE = W_BYTES + A_BYTES + WS_BYTES + AS_BYTES;
+  static constexpr int FN = BN / 64, FM = BM / 64;
+  static constexpr int WLD = BN * 8 / 256, ALD = BM * 8 / 256;
+};
+
+// 8 E2M1 codes (one dword) times an E4M3 block scale, as 8 exact BF16 values
+__device__ __forceinline__ v8bf nv_dequant8(uint32_t codes, float sb) {
+  uint32_t out[4];
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const float lo = e2m1_value((codes >> (8 * i)) & 0xFu) * sb;
+    const float hi = e2m1_value((codes >> (8 * i + 4)) & 0xFu) * sb;
+    out[i] = (__float_as_uint(lo) >> 16) | (__float_as_uint(hi) & 0xFFFF0000u);
+  }
+  v8bf r;
+  __builtin_memcpy(&r, out, 16);
+  return r;
+}
+
+template <int BM, int BN>
+__global__ void __launch_bounds__(256, 1) gemm_nv_kernel(GemmParams p) {
+  using T = NvTile<BM, BN>;
+  __shared__ __attribute__((aligned(16))) uint8_t smem[2 * T::STAGE];
+
+  const int tid = threadIdx.x;
+  const int lane = tid & 63, wave = tid >> 6;
+  const int wn0 = (wave >> 1) * (BN / 2), wm0 = (wave & 1) * (BM / 2);
+  const int tiles_n = (p.N + BN - 1) / BN;
+  const int tm = blockIdx.x / tiles_n, tn = blockIdx.x - tm * tiles_n;
+  const int m0 = tm * BM, n0 = tn * BN;
+  const int nkc = (p.K + KC - 1) / KC;
+  const int kgroups = p.K >> 4;
+  const int64_t row_b = p.K >> 1, s_row = kgroups;
+
+  uint4 wreg[T::WLD], areg[T::ALD];
+  uint4 wsreg = make_uint4(0, 0, 0, 0), asreg = make_uint4(0, 0, 0, 0);
+
+  auto load_sc = [&](const uint8_t* src, int kc) -> uint4 {
+    uint32_t w[4] = {0, 0, 0, 0};
+    for (int b = 0; b < 16; ++b) {
+      const uint32_t v = (kc * 16 + b < kgroups) ? src[b] : 0u;
+      w[b >> 2] |= v << (8 * (b & 3));
+    }
+    return make_uint4(w[0], w[1], w[2], w[3]);
+  };
+  auto gload = [&](int kc) {
+#pragma unroll
+    for (int i = 0; i < T::WLD; ++i) {
+      const int q = i * 256 + tid, row = q >> 3, c = q & 7;
+      const int n = min(n0 + row, p.N - 1);
+      const int kg = kc * 16 + 2 * c;  // a 16-byte chunk holds two 16-element groups
+      wreg[i] = kg < kgroups
+                    ? *(const uint4*)(p.w_codes + (int64_t)n * row_b + (int64_t)kc * 128 + c * 16)
+                    : make_uint4(0, 0, 0, 0);
+    }
+#pragma unroll
+    for (int i = 0; i < T::ALD; ++i) {
+      const int q = i * 256 + tid, row = q >> 3, c = q & 7;
+      const int m = min(m0 + row, p.M - 1);
+      const int kg = kc * 16 + 2 * c;
+      areg[i] = kg < kgroups
+                    ? *(const uint4*)(p.a_codes + (int64_t)m * row_b + (int64_t)kc * 128 + c * 16)
+                    : make_uint4(0, 0, 0, 0);
+    }
+    if (tid < BN) wsreg = load_sc(p.w_scales + (int64_t)min(n0 + tid, p.N - 1) * s_row + kc * 16, kc);
+    if (tid < BM) asreg = load_sc(p.a_scales + (int64_t)min(m0 + tid, p.M - 1) * s_row + kc * 16, kc);
+  };
+  auto sstore = [&](int buf) {
+    uint8_t* sW = smem + buf * T::STAGE;
+    uint8_t* sA = sW + T::W_BYTES;
+    uint8_t* sWS = sA + T::A_BYTES;
+    uint8_t* sAS = sWS + T::WS_BYTES;
+#pragma unroll
+    for (int i = 0; i < T::WLD; ++i) {
+      const int q = i * 256 + tid, row = q >> 3, c = q & 7;
+      *(uint4*)(sW + swz(row, c, T::ROWB)) = wreg[i];
+    }
+#pragma unroll
+    for (int i = 0; i < T::ALD; ++i) {
+      const int q = i * 256 + tid, row = q >> 3, c = q & 7;
+      *(uint4*)(sA + swz(row, c, T::ROWB)) = areg[i];
+    }
+    if (tid < BN) *(uint4*)(sWS + tid * 16) = wsreg;
+    if (tid < BM) *(uint4*)(sAS + tid * 16) = asreg;
+  };
+
+  v16f acc[T::FN][T::FM];
+#pragma unroll
+  for (int i = 0; i < T::FN; ++i)
+#pragma unroll
+    for (int j = 0; j < T::FM; ++j) acc[i][j] = v16f{};
+
+  gload(0);
+  sstore(0);
+  __syncthreads();
+  const int r32 = lane & 31, h = lane >> 5;
+  for (int kc = 0; kc < nkc; ++kc) {
+    const int buf = kc & 1;
+    if (kc + 1 < nkc) gload(kc + 1);
+    const uint8_t* sW = smem + buf * T::STAGE;
+    const uint8_t* sA = sW + T::W_BYTES;
+    const uint8_t* sWS = sA + T::A_BYTES;
+    const uint8_t* sAS = sWS + T::WS_BYTES;
+    // group g covers K [16g, 16g+16) of the chunk: 8 bytes at row offset 8g; lane half h takes
+    // elements 8h..8h+7, i.e. the dword at byte 8g + 4h (inside 16-byte chunk g/2).
+    for (int g = 0; g < 16; ++g) {
+      v8bf wf[T::FN], af[T::FM];
+#pragma unroll
+      for (int i = 0; i < T::FN; ++i) {
+        const int row = wn0 + 32 * i + r32;
+        const uint32_t c = *(const uint32_t*)(sW + swz(row, g >> 1, T::ROWB) + 8 * (g & 1) + 4 * h);
+        wf[i] = nv_dequant8(c, e4m3_value(sWS[row * 16 + g]));
+      }
+#pragma unroll
+      for (int j = 0; j < T::FM; ++j) {
+        const int row = wm0 + 32 * j + r32;
+        const uint32_t c = *(const uint32_t*)(sA + swz(row, g >> 1, T::ROWB) + 8 * (g & 1) + 4 * h);
+        af[j] = nv_dequant8(c, e4m3_value(sAS[row * 16 + g]));
+      }
+      static_for<T::FN>([&](auto i) {
+        static_for<T::FM>([&](auto j) {
+          acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(wf[i], af[j], acc[i][j], 0, 0, 0);
+        });
+      });
+    }
+    if (kc + 1 < nkc) sstore(buf ^ 1);
+    __syncthreads();
+  }
+
+  static_for<T::FN>([&](auto i) {
+    static_for<T::FM>([&](auto j) {
+      const int nb = n0 + wn0 + 32 * i, mb = m0 + wm0 + 32 * j;
+      if (nb < p.N && mb < p.M) epilogue_block(p, acc[i][j], nb, mb);
+    });
+  });
+}
+
+// ---------------------------------------------------------------------------------------------
+// low-rank down projection u = bf16(x . down_t^T): one wave per 32 (r) x 32 (m) block
+// ---------------------------------------------------------------------------------------------
+__global__ void __launch_bounds__(64) lowrank_down_kernel(const uint16_t* __restrict__ x,
+                                                           int64_t ld_x,
+                                                           const uint16_t* __restrict__ down_t,
+                                                           int M, int K, int R,
+                                                           uint16_t* __restrict__ u) {
+  const int lane = threadIdx.x;
+  const int h = lane >> 5;
+  const int rb = blockIdx.y * 32, mb = blockIdx.x * 32;
+  const int r = min(rb + (lane & 31), R - 1);
+  const int m = min(mb + (lane & 31), M - 1);
+  v16f acc = v16f{};
+  for (int k = 0; k < K; k += 16) {
+    const uint4 da = *(const uint4*)(down_t + (int64_t)r * K + k + 8 * h);
+    const uint4 xb = *(const uint4*)(x + (int64_t)m * ld_x + k + 8 * h);
+    v8bf fa, fb;
+    __builtin_memcpy(&fa, &da, 16);
+    __builtin_memcpy(&fb, &xb, 16);
+    acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fa, fb, acc, 0, 0, 0);
+  }
+  const int mo = mb + (lane & 31);
+  if (mo >= M) return;
+#pragma unroll
+  for (int e = 0; e < 16; ++e) {
+    const int ro = rb + 8 * (e >> 2) + 4 * h + (e & 3);
+    if (ro < R) u[(int64_t)mo * R + ro] = (uint16_t)f32_to_bf16_rne(acc[e]);
+  }
+}
+
+// ---------------------------------------------------------------------------------------------
+// launchers
+// ---------------------------------------------------------------------------------------------
+template <int BM, int BN, bool AFP8>
+static hipError_t run_mx(const GemmParams& p, hipStream_t s) {
+  const int tiles = ((p.M + BM - 1) / BM) * ((p.N + BN - 1) / BN);
+  if (p.K % KC == 0)
+    gemm_mx_kernel<BM, BN, AFP8, true><<<tiles, 256, 0, s>>>(p);
+  else
+    gemm_mx_kernel<BM, BN, AFP8, false><<<tiles, 256, 0, s>>>(p);
+  return hipGetLastError();
+}
+
+hipError_t launch_gemm_mx(const GemmParams& p, bool act_fp8, hipStream_t s) {
+  if (p.M == 0) return hipSuccess;
+  if (act_fp8) return run_mx<128, 256, true>(p, s);
+  return run_mx<256, 256, false>(p, s);
+}
+
+hipError_t launch_gemm_nv(const GemmParams& p, hipStream_t s) {
+  if (p.M == 0) return hipSuccess;
+  const int tiles = ((p.M + 255) / 256) * ((p.N + 255) / 256);
+  gemm_nv_kernel<256, 256><<<tiles, 256, 0, s>>>(p);
+  return hipGetLastError();
+}
+
+hipError_t launch_lowrank_down(const uint16_t* x, int64_t ld_x, const uint16_t* down_t, int M,
+                               int K, int R, uint16_t* u, hipStream_t s) {
+  if (M == 0) return hipSuccess;
+  dim3 grid((M + 31) / 32, (R + 31) / 32);
+  lowrank_down_kernel<<<grid, 64, 0, s>>>(x, ld_x, down_t, M, K, R, u);
+  return hipGetLastError();
+}
+
+}  // namespace mxk

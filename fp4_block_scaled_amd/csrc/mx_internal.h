@@ -1,0 +1,46 @@
+// Internal launcher interface between the C ABI (mx_capi.hip) and the kernels (internal header).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace mxk {
+
+// Quantizers / dequantizer / absmax (mx_quant.hip)
+hipError_t launch_quant_mx(const uint16_t* x, int64_t rows, int64_t cols, int64_t ld, int elem,
+                           uint8_t* codes, uint8_t* scales, hipStream_t s);
+hipError_t launch_quant_nv(const uint16_t* x, int64_t rows, int64_t cols, int64_t ld, float sg,
+                           uint8_t* codes, uint8_t* scales, hipStream_t s);
+hipError_t launch_dequant(const uint8_t* codes, const uint8_t* scales, int64_t rows, int64_t cols,
+                          int fmt, float sg, uint16_t* y, int64_t ld, hipStream_t s);
+hipError_t launch_absmax(const uint16_t* x, int64_t rows, int64_t cols, int64_t ld, float* out,
+                         hipStream_t s);
+
+// GEMMs (mx_gemm.hip)
+enum { EPI_BIAS = 0, EPI_GELU = 1, EPI_GELU_QUANT = 2 };
+
+struct GemmParams {
+  const uint8_t* a_codes;   // [M, K/2] (FP4) or [M, K] (FP8)
+  const uint8_t* a_scales;  // [M, K/32] E8M0, or [M, K/16] E4M3 (NVFP4)
+  const uint8_t* w_codes;   // [N, K/2]
+  const uint8_t* w_scales;  // [N, K/32] or [N, K/16]
+  const uint16_t* bias;     // FP16 [N] or nullptr
+  const uint16_t* lr_u;     // BF16 [M, R] or nullptr (low-rank intermediate)
+  const uint16_t* lr_up;    // BF16 [N, R]
+  void* out;                // BF16 / FP32 [M, ld_out], or FP4 codes [M, N/2]
+  uint8_t* out_scales;      // [M, N/32] for the re-quantizing epilogue
+  int64_t ld_out;
+  float out_scale;          // NVFP4: product of the two global scales, else 1
+  int M, N, K, R;
+  int epi;
+  int out_f32;
+};
+
+// act_fp8: activation codes are E4M3 (W4A8); otherwise E2M1.
+hipError_t launch_gemm_mx(const GemmParams& p, bool act_fp8, hipStream_t s);
+hipError_t launch_gemm_nv(const GemmParams& p, hipStream_t s);
+// u[m, r] = bf16_rne(sum_k x[m, k] * down_t[r, k])
+hipError_t launch_lowrank_down(const uint16_t* x, int64_t ld_x, const uint16_t* down_t, int M,
+                               int K, int R, uint16_t* u, hipStream_t s);
+
+}  // namespace mxk

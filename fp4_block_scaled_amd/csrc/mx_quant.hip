@@ -1,0 +1,284 @@
+// Quantizer, dequantizer and absmax kernels for gfx950.
+//
+// MX quantization (MXFP4 model cards, Quantization Details: per-32 E8M0 scales, activations
+// quantized dynamically; W4A8 SVDQuant page: dynamic MXFP8 activations), bit-level rules of OCP
+// MX v1.0: shared exponent floor(log2 amax) - emax, RNE onto the element grid with saturation,
+// sign kept.  NVFP4 (NVFP4 model card, Model Details): per-16 E4M3 block scales under an FP32
+// global scale.
+//
+// The quantizers are HBM-bound (2 bytes read, 0.53 / 1.03 bytes written per element): every
+// thread moves one 16-byte vector of 8 BF16 values, four (MX) or two (NVFP4) neighbouring lanes
+// own one scale group and reduce its amax with DPP quad permutes, and the code bytes of a wave
+// land in one contiguous span.  All arithmetic that decides a code is exact: BF16 magnitudes
+// are ordered like their bit patterns (so amax is an integer max), the scale is an exponent
+// field subtraction, q = |x| * 2^-e is an exact binary32 product (fp32 denormals are enabled),
+// and the NVFP4 thresholds are exact fp64 products compared against binary32 values.
+#include "mx_common.h"
+#include "mx_internal.h"
+
+namespace mxk {
+
+// ---------------------------------------------------------------------------------------------
+// MXFP4 / MXFP8
+// ---------------------------------------------------------------------------------------------
+template <int ELEM>  // 0: E2M1 (emax 2), 1: E4M3 (emax 8)
+__global__ void __launch_bounds__(256) quant_mx_kernel(const uint16_t* __restrict__ x,
+                                                        int64_t rows, int64_t cols, int64_t ld,
+                                                        uint8_t* __restrict__ codes,
+                                                        uint8_t* __restrict__ scales) {
+  const int64_t gpr = cols >> 5;       // groups per row
+  const int64_t total = rows * gpr * 4;  // four threads per group
+  const int64_t stride = (int64_t)gridDim.x * 256;
+  for (int64_t t = (int64_t)blockIdx.x * 256 + threadIdx.x; t < total; t += stride) {
+    const int64_t g = t >> 2;
+    const int part = (int)(t & 3);
+    const int64_t r = g / gpr;
+    const int64_t gc = g - r * gpr;
+    const uint4 v = load_stream16(x + r * ld + gc * 32 + part * 8);
+    uint32_t w[4] = {v.x, v.y, v.z, v.w};
+    uint32_t amax = 0;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      uint32_t lo = w[i] & 0x7FFFu, hi = (w[i] >> 16) & 0x7FFFu;
+      amax = max(amax, max(lo, hi));
+    }
+    amax = max(amax, quad_xor1(amax));
+    amax = max(amax, quad_xor2(amax));
+    const bool bad = amax >= 0x7F80u;  // NaN or Inf in the group
+    const int E = (int)(amax >> 7);    // BF16 exponent field of amax
+    const int emax = ELEM == 0 ? 2 : 8;
+    int e = E - 127 - emax;            // floor(log2 amax) - emax (subnormal/zero: clamped below)
+    if (e < -127) e = -127;
+    const float inv = __uint_as_float((uint32_t)(127 - e) << 23);  // 2^-e, a normal binary32
+    if (ELEM == 0) {
+      uint32_t packed = 0;
+#pragma unroll
+      for (int i = 0; i < 8; ++i) {
+        uint32_t b = (w[i >> 1] >> ((i & 1) * 16)) & 0xFFFFu;
+        float q = bf16_to_f32(b & 0x7FFFu) * inv;
+        uint32_t c = e2m1_code(q) | ((b >> 12) & 8u);
+        packed |= c << (4 * i);
+      }
+      if (bad) packed = 0;
+      *(uint32_t*)(codes + r * (cols >> 1) + gc * 16 + part * 4) = packed;
+    } else {
+      uint32_t p0 = 0, p1 = 0;
+#pragma unroll
+      for (int i = 0; i < 8; ++i) {
+        uint32_t b = (w[i >> 1] >> ((i & 1) * 16)) & 0xFFFFu;
+        float q = bf16_to_f32(b & 0x7FFFu) * inv;
+        uint32_t c = e4m3_code(q) | ((b >> 8) & 0x80u);
+        if (i < 4) p0 |= c << (8 * i);
+        else p1 |= c << (8 * (i - 4));
+      }
+      if (bad) p0 = p1 = 0;
+      *(uint2*)(codes + r * cols + gc * 32 + part * 8) = make_uint2(p0, p1);
+    }
+    if (part == 0) scales[r * gpr + gc] = bad ? (uint8_t)0xFF : (uint8_t)(e + 127);
+  }
+}
+
+// ---------------------------------------------------------------------------------------------
+// NVFP4
+// ---------------------------------------------------------------------------------------------
+// binary32 value just below a positive finite one
+__device__ __forceinline__ float prev_float(float f) { return __uint_as_float(__float_as_uint(f) - 1u); }
+
+// Largest binary32 value <= t (t > 0 exact double).
+__device__ __forceinline__ float f64_round_down(double t) {
+  float f = (float)t;
+  if ((double)f > t) f = prev_float(f);
+  return f;
+}
+
+// Thresholds of the E2M1 rounding for block scale D = sb * sg, as binary32 values such that
+// for a binary32 magnitude a:  code = sum_j [a > T_j].  The midpoints are 0.25, 0.75, 1.25,
+// 1.75, 2.5, 3.5, 5; ties at 0.25, 1.25, 2.5, 5 round down (to the even code) and ties at 0.75,
+// 1.75, 3.5 round up.  For a strict ">" against the exact t*D, any binary32 a satisfies
+// a > t*D <=> a > RD(t*D).  For ">=", a >= t*D <=> a > prev(t*D) when t*D is a binary32 value,
+// else <=> a > RD(t*D).
+struct NvThresholds {
+  float t[7];
+};
+
+__device__ __forceinline__ NvThresholds nv_thresholds(double D, bool zero) {
+  NvThresholds th;
+  const double mids[7] = {0.25, 0.75, 1.25, 1.75, 2.5, 3.5, 5.0};
+  const bool ge[7] = {false, true, false, true, false, true, false};
+#pragma unroll
+  for (int j = 0; j < 7; ++j) {
+    if (zero) {
+      th.t[j] = __uint_as_float(0x7F800000u);  // +inf: every magnitude rounds to 0
+      continue;
+    }
+    double T = mids[j] * D;  // exact: <= 3 + 28 significant bits
+    float f = f64_round_down(T);
+    if (ge[j] && (double)f == T) f = prev_float(f);
+    th.t[j] = f;
+  }
+  return th;
+}
+
+__global__ void __launch_bounds__(256) quant_nv_kernel(const uint16_t* __restrict__ x,
+                                                        int64_t rows, int64_t cols, int64_t ld,
+                                                        float sg, uint8_t* __restrict__ codes,
+                                                        uint8_t* __restrict__ scales) {
+  const int64_t gpr = cols >> 4;       // 16-element groups per row
+  const int64_t total = rows * gpr * 2;  // two threads per group
+  const int64_t stride = (int64_t)gridDim.x * 256;
+  const double six_sg = 6.0 * (double)sg;
+  for (int64_t t = (int64_t)blockIdx.x * 256 + threadIdx.x; t < total; t += stride) {
+    const int64_t g = t >> 1;
+    const int part = (int)(t & 1);
+    const int64_t r = g / gpr;
+    const int64_t gc = g - r * gpr;
+    const uint4 v = load_stream16(x + r * ld + gc * 16 + part * 8);
+    uint32_t w[4] = {v.x, v.y, v.z, v.w};
+    uint32_t amax = 0;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      uint32_t lo = w[i] & 0x7FFFu, hi = (w[i] >> 16) & 0x7FFFu;
+      amax = max(amax, max(lo, hi));
+    }
+    amax = max(amax, quad_xor1(amax));
+    const bool bad = amax >= 0x7F80u;
+    // sb = E4M3_rne_sat(amax / (6 sg)): the fp64 quotient of an 8-bit by a 26-bit significand
+    // is never rounded onto a false E4M3 midpoint, so rounding it again is a single rounding.
+    const double qd = (double)bf16_to_f32(amax) / six_sg;
+    const uint32_t sbyte = e4m3_code_f64(qd);
+    const float sb = e4m3_value(sbyte);
+    const NvThresholds th = nv_thresholds((double)sb * (double)sg, sbyte == 0);
+    uint32_t packed = 0;
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+      uint32_t b = (w[i >> 1] >> ((i & 1) * 16)) & 0xFFFFu;
+      float a = bf16_to_f32(b & 0x7FFFu);
+      uint32_t c = 0;
+#pragma unroll
+      for (int j = 0; j < 7; ++j) c += a > th.t[j] ? 1u : 0u;
+      packed |= (c | ((b >> 12) & 8u)) << (4 * i);
+    }
+    if (bad) packed = 0;
+    *(uint32_t*)(codes + r * (cols >> 1) + gc * 8 + part * 4) = packed;
+    if (part == 0) scales[r * gpr + gc] = bad ? (uint8_t)0x7F : (uint8_t)sbyte;
+  }
+}
+
+// ---------------------------------------------------------------------------------------------
+// dequantization (one thread per 8 elements)
+// ---------------------------------------------------------------------------------------------
+__global__ void __launch_bounds__(256) dequant_kernel(const uint8_t* __restrict__ codes,
+                                                       const uint8_t* __restrict__ scales,
+                                                       int64_t rows, int64_t cols, int fmt,
+                                                       float sg, uint16_t* __restrict__ y,
+                                                       int64_t ld) {
+  const int64_t per_row = cols >> 3;
+  const int64_t total = rows * per_row;
+  const int64_t stride = (int64_t)gridDim.x * 256;
+  for (int64_t t = (int64_t)blockIdx.x * 256 + threadIdx.x; t < total; t += stride) {
+    const int64_t r = t / per_row;
+    const int64_t c0 = (t - r * per_row) * 8;
+    uint32_t out[4];
+    if (fmt == 1) {  // MXFP8
+      const uint2 cb = *(const uint2*)(codes + r * cols + c0);
+      const uint32_t s = scales[r * (cols >> 5) + (c0 >> 5)];
+#pragma unroll
+      for (int i = 0; i < 8; ++i) {
+        uint32_t code = ((i < 4 ? cb.x : cb.y) >> (8 * (i & 3))) & 0xFFu;
+        float v = s == 0xFF ? __uint_as_float(0x7FC00000u)
+                            : __builtin_amdgcn_ldexpf(e4m3_value(code), (int)s - 127);
+        uint32_t h = f32_to_bf16_rne(v);
+        out[i >> 1] = (i & 1) ? (out[i >> 1] | (h << 16)) : h;
+      }
+    } else {
+      const uint32_t cb = *(const uint32_t*)(codes + r * (cols >> 1) + (c0 >> 1));
+      if (fmt == 0) {  // MXFP4: exact
+        const uint32_t s = scales[r * (cols >> 5) + (c0 >> 5)];
+#pragma unroll
+        for (int i = 0; i < 8; ++i) {
+          uint32_t code = (cb >> (4 * i)) & 0xFu;
+          float v = s == 0xFF ? __uint_as_float(0x7FC00000u)
+                              : __builtin_amdgcn_ldexpf(e2m1_value(code), (int)s - 127);
+          uint32_t h = f32_to_bf16_rne(v);
+          out[i >> 1] = (i & 1) ? (out[i >> 1] | (h << 16)) : h;
+        }
+      } else {  // NVFP4: one rounding of code * sb * sg
+        const uint32_t sbyte = scales[r * (cols >> 4) + (c0 >> 4)];
+        const double sbg = (double)e4m3_value(sbyte) * (double)sg;
+#pragma unroll
+        for (int i = 0; i < 8; ++i) {
+          uint32_t code = (cb >> (4 * i)) & 0xFu;
+          uint32_t h = f64_to_bf16_rne((double)e2m1_value(code) * sbg);
+          out[i >> 1] = (i & 1) ? (out[i >> 1] | (h << 16)) : h;
+        }
+      }
+    }
+    *(uint4*)(y + r * ld + c0) = make_uint4(out[0], out[1], out[2], out[3]);
+  }
+}
+
+// ---------------------------------------------------------------------------------------------
+// absmax: one workgroup, deterministic (max is order independent)
+// ---------------------------------------------------------------------------------------------
+__global__ void __launch_bounds__(1024) absmax_kernel(const uint16_t* __restrict__ x, int64_t rows,
+                                                       int64_t cols, int64_t ld,
+                                                       float* __restrict__ out) {
+  __shared__ uint32_t red[1024];
+  uint32_t m = 0;
+  const int64_t total = rows * cols;
+  for (int64_t i = threadIdx.x; i < total; i += 1024) {
+    const int64_t r = i / cols;
+    m = max(m, (uint32_t)(x[r * ld + (i - r * cols)] & 0x7FFFu));
+  }
+  red[threadIdx.x] = m;
+  __syncthreads();
+  for (int s = 512; s > 0; s >>= 1) {
+    if ((int)threadIdx.x < s) red[threadIdx.x] = max(red[threadIdx.x], red[threadIdx.x + s]);
+    __syncthreads();
+  }
+  if (threadIdx.x == 0) *out = bf16_to_f32(red[0]);
+}
+
+// ---------------------------------------------------------------------------------------------
+// launchers
+// ---------------------------------------------------------------------------------------------
+static int grid_for(int64_t threads) {
+  int64_t blocks = (threads + 255) / 256;
+  const int64_t cap = 256 * 64;  // enough resident waves to cover HBM latency
+  return (int)(blocks < cap ? (blocks > 0 ? blocks : 1) : cap);
+}
+
+hipError_t launch_quant_mx(const uint16_t* x, int64_t rows, int64_t cols, int64_t ld, int elem,
+                           uint8_t* codes, uint8_t* scales, hipStream_t s) {
+  const int64_t threads = rows * (cols / 32) * 4;
+  if (threads == 0) return hipSuccess;
+  if (elem == 0)
+    quant_mx_kernel<0><<<grid_for(threads), 256, 0, s>>>(x, rows, cols, ld, codes, scales);
+  else
+    quant_mx_kernel<1><<<grid_for(threads), 256, 0, s>>>(x, rows, cols, ld, codes, scales);
+  return hipGetLastError();
+}
+
+hipError_t launch_quant_nv(const uint16_t* x, int64_t rows, int64_t cols, int64_t ld, float sg,
+                           uint8_t* codes, uint8_t* scales, hipStream_t s) {
+  const int64_t threads = rows * (cols / 16) * 2;
+  if (threads == 0) return hipSuccess;
+  quant_nv_kernel<<<grid_for(threads), 256, 0, s>>>(x, rows, cols, ld, sg, codes, scales);
+  return hipGetLastError();
+}
+
+hipError_t launch_dequant(const uint8_t* codes, const uint8_t* scales, int64_t rows, int64_t cols,
+                          int fmt, float sg, uint16_t* y, int64_t ld, hipStream_t s) {
+  const int64_t threads = rows * (cols / 8);
+  if (threads == 0) return hipSuccess;
+  dequant_kernel<<<grid_for(threads), 256, 0, s>>>(codes, scales, rows, cols, fmt, sg, y, ld);
+  return hipGetLastError();
+}
+
+hipError_t launch_absmax(const uint16_t* x, int64_t rows, int64_t cols, int64_t ld, float* out,
+                         hipStream_t s) {
+  absmax_kernel<<<1, 1024, 0, s>>>(x, rows, cols, ld, out);
+  return hipGetLastError();
+}
+
+}  // namespace mxk

@@ -1,0 +1,176 @@
+/*
+ * mxfp.h - C ABI of the MI355X (gfx950) microscaled-FP4 linear layer.
+ *
+ * What it computes (model cards of quantized Wan2.2 transformers):
+ *  - "Wan2.2-I2V-A14B-Lightning-Diffusers-MXFP4-AutoRound", Quantization Details, and
+ *    "Wan2.2-Animate-14B-Diffusers-MXFP4-AutoRound", Quantization Details: W4A4 MXFP4 linear
+ *    layers; weights are FP4 E2M1 codes packed two per byte with one E8M0 scale per 32
+ *    consecutive input channels; activations are quantized to MXFP4 dynamically at run time;
+ *    biases are F16.
+ *  - "Wan2.2-T2V-A14B-Diffusers-NVFP4-AutoRound", Model Details: NVFP4 variant, E2M1 codes with
+ *    one FP8 E4M3 scale per 16 and one FP32 global scale per tensor; activation block scales
+ *    dynamic, activation global scale static.
+ *  - "Wan2.2 W4A8 SVDQuant - NVIDIA (CUDA) artifacts": W4A8 variant, MXFP4 weights times
+ *    dynamically quantized MXFP8 (E4M3, per-32 E8M0) activations plus a rank-32 low-rank branch
+ *    with BF16 factors.
+ * The bit-level encodings follow OCP Microscaling (MX) v1.0: the shared exponent of a block is
+ * floor(log2(max|x|)) - emax(element) (emax 2 for E2M1, 8 for E4M3), elements are rounded to
+ * nearest-even with saturation, signs are kept.  NVFP4 stores its global scale in the decode
+ * direction: value = code * block_scale * global_scale.
+ *
+ * Conventions for every call:
+ *  - Pointers marked "device" are HIP device (or host-coherent) addresses owned by the caller;
+ *    the library allocates nothing, frees nothing and keeps no pointer after the call returns.
+ *  - BF16 and FP16 values are passed as uint16_t bit patterns.
+ *  - Layouts are row-major and unshuffled.  FP4 codes: [rows, cols/2] bytes, element 2j in the
+ *    low nibble of byte j.  FP8 codes: [rows, cols] bytes.  Scales: [rows, cols/G] bytes with
+ *    G = 32 (E8M0, MX formats) or G = 16 (E4M3, NVFP4); groups start at column 0.
+ *  - A linear layer computes y[m, n] = sum_k a[m, k] * w[n, k] + bias[n]: the weight is N x K
+ *    with K contiguous ("TN"); the output is M x N.
+ *  - `stream` is a hipStream_t (NULL = the default stream).  Calls are asynchronous on that
+ *    stream; results are valid once the caller synchronises it.
+ *  - Errors: every argument is validated before anything is launched, so on an error nothing is
+ *    written.  MX_ERR_HIP reports a launch failure.  mx_last_error() gives a message for the
+ *    calling thread's last failing call.  M = 0 (rows = 0) is a valid no-op.
+ *  - Results are deterministic: no atomics, no split-K; the same inputs give the same bytes.
+ *  - Calls are thread-safe; the library holds no state besides the per-thread error message.
+ */
+#ifndef MXFP_H
+#define MXFP_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define MX_ABI_VERSION 1
+
+typedef enum mx_status {
+    MX_OK = 0,
+    MX_ERR_NULL = 1,        /* a required pointer is NULL */
+    MX_ERR_SHAPE = 2,       /* sizes inconsistent or not a multiple of the group size */
+    MX_ERR_ALIGN = 3,       /* a pointer or leading dimension breaks the alignment rule */
+    MX_ERR_UNSUPPORTED = 4, /* format / epilogue / output combination not provided */
+    MX_ERR_WORKSPACE = 5,   /* workspace missing or smaller than mx_linear_workspace_bytes */
+    MX_ERR_HIP = 6          /* a HIP launch failed */
+} mx_status;
+
+typedef enum mx_format {
+    MX_FMT_MXFP4 = 0, /* E2M1 codes, E8M0 scale per 32 */
+    MX_FMT_MXFP8 = 1, /* E4M3 codes, E8M0 scale per 32 */
+    MX_FMT_NVFP4 = 2  /* E2M1 codes, E4M3 scale per 16, FP32 global scale */
+} mx_format;
+
+typedef enum mx_epilogue {
+    MX_EPI_BIAS = 0,                 /* y = acc + bias */
+    MX_EPI_BIAS_GELU = 1,            /* y = gelu_tanh(acc + bias) */
+    MX_EPI_BIAS_GELU_QUANT_MXFP4 = 2 /* h = gelu_tanh(acc + bias), re-quantized to MXFP4 along N */
+} mx_epilogue;
+
+typedef enum mx_out_dtype { MX_OUT_BF16 = 0, MX_OUT_F32 = 1 } mx_out_dtype;
+
+/* A quantized matrix (rows x cols logical elements) in the layouts above. */
+typedef struct mx_qmatrix {
+    const void* codes;     /* device */
+    const uint8_t* scales; /* device */
+    float global_scale;    /* NVFP4 only: decode-direction FP32 global scale; ignored for MX */
+    int32_t fmt;           /* mx_format */
+    int64_t rows;
+    int64_t cols;
+} mx_qmatrix;
+
+/* Low-rank branch of SVDQuant ("Wan2.2 W4A8 SVDQuant", Contents/Accuracy: rank-32 BF16
+ * factors).  y += bf16(x . down) . up, x being the unquantized BF16 activation. */
+typedef struct mx_lowrank {
+    const uint16_t* down; /* device BF16 [K, rank], row-major */
+    const uint16_t* up;   /* device BF16 [rank, N], row-major */
+    int32_t rank;         /* 1..64, a multiple of 16 */
+} mx_lowrank;
+
+/* Version of this ABI (MX_ABI_VERSION). */
+int mx_abi_version(void);
+
+/* Human-readable name of a status code (static storage). */
+const char* mx_status_string(int status);
+
+/* Message describing the calling thread's last failing call ("" if none). */
+const char* mx_last_error(void);
+
+/*
+ * mx_quantize - dynamic quantization of a BF16 matrix (rows x cols, leading dimension ld_x
+ * elements) to `fmt`.
+ *  MXFP4 / MXFP8: per 32 consecutive columns, scale byte = clamp(floor(log2 amax) - emax,
+ *    -127, 127) + 127 (all-zero block: 0; a NaN/Inf in the block: 0xFF with codes 0); codes are
+ *    RNE(|x| * 2^-exponent) on the element grid, saturating, with the sign of x.
+ *  NVFP4: per 16 columns, block scale sb = E4M3_rne_sat(amax / (6 * global_scale)) and codes
+ *    E2M1_rne_sat(|x| / (sb * global_scale)), each the exact real rounded once; sb = 0 gives
+ *    zero magnitudes; a NaN/Inf in the block gives scale 0x7F (E4M3 NaN) and codes 0.
+ *    global_scale (> 0, finite) is ignored for the MX formats.
+ * codes: device, [rows, cols/2] (FP4) or [rows, cols] (FP8) bytes.  scales: device,
+ * [rows, cols/G] bytes.  Requires cols % G == 0, ld_x >= cols, x 16-byte aligned, ld_x % 8 == 0.
+ */
+mx_status mx_quantize(const uint16_t* x, int64_t rows, int64_t cols, int64_t ld_x, int32_t fmt,
+                      float global_scale, void* codes, uint8_t* scales, void* stream);
+
+/*
+ * mx_dequantize - BF16 values of a quantized matrix: y = code * 2^(scale - 127) for MX (exact),
+ * y = bf16_rne(code * sb * global_scale) for NVFP4 (one rounding of the exact product).  A NaN
+ * scale byte gives NaN.  y: device BF16, rows x cols with leading dimension ld_y >= cols.
+ */
+mx_status mx_dequantize(const mx_qmatrix* q, uint16_t* y, int64_t ld_y, void* stream);
+
+/*
+ * mx_absmax - largest |x| of a BF16 matrix, written as one float to device memory *amax
+ * (NaN-free input expected).  Used to derive an NVFP4 tensor's global scale.
+ */
+mx_status mx_absmax(const uint16_t* x, int64_t rows, int64_t cols, int64_t ld_x, float* amax,
+                    void* stream);
+
+/* NVFP4 global scale of a tensor with largest magnitude amax: fp32(amax / (6 * 448)), 1 for
+ * amax = 0.  Host-side arithmetic only. */
+float mx_nvfp4_global_scale(float amax);
+
+/* Bytes of workspace mx_linear needs for an M x K activation in act_fmt (codes + scales of the
+ * quantized activation, plus the low-rank intermediate when rank > 0). */
+size_t mx_linear_workspace_bytes(int64_t M, int64_t K, int32_t act_fmt, int32_t rank);
+
+/*
+ * mx_linear - the quantized linear layer on a BF16 activation a (M x K, leading dimension ld_a):
+ * quantize a dynamically to act_fmt (act_global_scale is the static NVFP4 activation global
+ * scale), then y = dequant(a) . dequant(w)^T in fp32 accumulation, then the epilogue.
+ * Supported (act_fmt, w->fmt): (MXFP4, MXFP4) W4A4; (MXFP8, MXFP4) W4A8; (NVFP4, NVFP4).
+ *  bias: device FP16 [N] or NULL.
+ *  lr:   low-rank branch or NULL (MX formats only); y += bf16_rne(a . lr->down) . lr->up,
+ *        added before the bias.
+ *  epilogue MX_EPI_BIAS / MX_EPI_BIAS_GELU: out is BF16 (out_dtype MX_OUT_BF16) or FP32
+ *        (MX_OUT_F32), M x N with leading dimension ld_out elements.  The BF16 result is the
+ *        RNE of the FP32 result.
+ *  epilogue MX_EPI_BIAS_GELU_QUANT_MXFP4: h = gelu_tanh(acc + bias) in fp32 is quantized to
+ *        MXFP4 with groups of 32 along N: out receives codes [M, N/2] and out_scales [M, N/32]
+ *        (contiguous; ld_out must be N; out_dtype ignored).  Requires N % 32 == 0.
+ *  workspace: device, >= mx_linear_workspace_bytes(M, K, act_fmt, rank) bytes, 256-byte
+ *        aligned; its contents on return are unspecified.
+ * Requires K % 32 == 0 (K % 16 == 0 for NVFP4), w->cols == K, N = w->rows >= 1.
+ */
+mx_status mx_linear(const uint16_t* a, int64_t M, int64_t K, int64_t ld_a, int32_t act_fmt,
+                    float act_global_scale, const mx_qmatrix* w, const uint16_t* bias,
+                    const mx_lowrank* lr, int32_t epilogue, int32_t out_dtype, void* out,
+                    int64_t ld_out, uint8_t* out_scales, void* workspace, size_t workspace_bytes,
+                    void* stream);
+
+/*
+ * mx_linear_q - the same GEMM and epilogues on an already quantized activation a (M x K), e.g.
+ * the MXFP4 output of a MX_EPI_BIAS_GELU_QUANT_MXFP4 call feeding the next linear.  No
+ * workspace and no low-rank branch.
+ */
+mx_status mx_linear_q(const mx_qmatrix* a, const mx_qmatrix* w, const uint16_t* bias,
+                      int32_t epilogue, int32_t out_dtype, void* out, int64_t ld_out,
+                      uint8_t* out_scales, void* stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* MXFP_H */

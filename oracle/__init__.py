@@ -64,6 +64,8 @@ def lib():
         L.mxr_gelu_tanh_array.restype = None
         L.mxr_lowrank.argtypes = [_P, _I, _I, _I, _P, _I, _P, _I, _P, _P, _P]
         L.mxr_lowrank.restype = None
+        L.mxr_bf16_rne_array.argtypes = [_P, _I, _P]
+        L.mxr_bf16_rne_array.restype = None
         L.mxr_absmax_bf16.argtypes = [_P, _I, _I, _I]
         L.mxr_absmax_bf16.restype = ctypes.c_double
         _lib = L
@@ -102,6 +104,14 @@ def bf16_value(bits: int) -> float:
 
 def bf16_rne(v: float) -> int:
     return lib().mxr_bf16_rne(v)
+
+
+def bf16_rne_array(v: np.ndarray) -> np.ndarray:
+    """BF16 bit patterns of exact fp64 values (one rounding each)."""
+    v, pv = _c(v, np.float64)
+    out = np.empty(v.shape, dtype=np.uint16)
+    lib().mxr_bf16_rne_array(pv, v.size, out.ctypes.data)
+    return out
 
 
 def f16_values(bits: np.ndarray) -> np.ndarray:

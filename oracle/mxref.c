@@ -438,3 +438,9 @@ double mxr_absmax_bf16(const uint16_t* x, int64_t rows, int64_t cols, int64_t ld
         }
     return amax;
 }
+
+/* Element-wise BF16 rounding of an array of exact reals (see mxr_bf16_rne). */
+void mxr_bf16_rne_array(const double* v, int64_t n, uint16_t* out) {
+#pragma omp parallel for schedule(static)
+    for (int64_t i = 0; i < n; ++i) out[i] = mxr_bf16_rne(v[i]);
+}

@@ -1,0 +1,163 @@
+"""The C ABI library: it loads, exports exactly what include/mxfp.h declares, and its host-side
+logic (validation, workspace arithmetic, global-scale arithmetic) behaves as documented.  CPU
+only: no call here reaches a kernel launch (every one fails validation first or is host-only).
+"""
+import ctypes
+import os
+import re
+import subprocess
+
+import numpy as np
+import pytest
+
+import oracle as O
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "mxfp.h")
+
+
+@pytest.fixture(scope="module")
+def mx():
+    import fp4_block_scaled_amd as m
+    return m
+
+
+def _declared():
+    txt = open(HEADER).read()
+    txt = re.sub(r"/\*.*?\*/", "", txt, flags=re.S)
+    return sorted(set(re.findall(r"\b(mx_[a-z0-9_]+)\s*\(", txt)))
+
+
+def test_header_declares_the_boundary():
+    names = _declared()
+    for required in ("mx_quantize", "mx_dequantize", "mx_linear", "mx_linear_q", "mx_absmax",
+                     "mx_linear_workspace_bytes", "mx_nvfp4_global_scale", "mx_status_string",
+                     "mx_last_error", "mx_abi_version"):
+        assert required in names
+
+
+def test_library_exports_every_declared_symbol(mx):
+    L = mx.lib()
+    for name in _declared():
+        assert hasattr(L, name), name
+    out = subprocess.run(["nm", "-D", "--defined-only", mx.LIB_PATH], capture_output=True,
+                         text=True, check=True).stdout
+    exported = sorted({l.split()[-1] for l in out.splitlines() if re.search(r" T mx_", l)})
+    assert exported == _declared()
+
+
+def test_status_strings(mx):
+    L = mx.lib()
+    for code, name in enumerate(["MX_OK", "MX_ERR_NULL", "MX_ERR_SHAPE", "MX_ERR_ALIGN",
+                                 "MX_ERR_UNSUPPORTED", "MX_ERR_WORKSPACE", "MX_ERR_HIP"]):
+        assert L.mx_status_string(code).decode() == name
+    assert L.mx_abi_version() == 1
+
+
+def test_nvfp4_global_scale_host_arithmetic_matches_oracle(mx):
+    for amax in (40.0, 1.0, 0.0078125, 3.140625, 30.0 * 4.5, 1e-30):
+        assert mx.nvfp4_global_scale(amax) == O.nv_global_scale(amax)
+    assert mx.nvfp4_global_scale(0.0) == 1.0
+
+
+def test_workspace_bytes(mx):
+    ws = mx.linear_workspace_bytes
+    r = lambda v: (v + 255) // 256 * 256
+    assert ws(75600, 5120, "mxfp4") == r(75600 * 2560) + r(75600 * 160)
+    assert ws(4290, 3072, "mxfp8", 32) == r(4290 * 3072) + r(4290 * 96) + r(4290 * 32 * 2)
+    assert ws(75600, 5120, "nvfp4") == r(75600 * 2560) + r(75600 * 320)
+    assert ws(0, 5120, "mxfp4") == 0
+
+
+FAKE = 0x10000  # an aligned, never dereferenced address
+
+
+def _rc(st):
+    return st
+
+
+def test_quantize_validation(mx):
+    L = mx.lib()
+    P = ctypes.c_void_p
+    # unknown format
+    assert L.mx_quantize(P(FAKE), 4, 64, 64, 7, 1.0, P(FAKE), P(FAKE), None) == 4
+    # cols not a multiple of the group
+    assert L.mx_quantize(P(FAKE), 4, 48, 48, mx.MXFP4, 1.0, P(FAKE), P(FAKE), None) == 2
+    assert L.mx_quantize(P(FAKE), 4, 24, 24, mx.NVFP4, 1.0, P(FAKE), P(FAKE), None) == 2
+    # ld < cols
+    assert L.mx_quantize(P(FAKE), 4, 64, 32, mx.MXFP4, 1.0, P(FAKE), P(FAKE), None) == 2
+    # NVFP4 needs a positive finite global scale
+    assert L.mx_quantize(P(FAKE), 4, 64, 64, mx.NVFP4, 0.0, P(FAKE), P(FAKE), None) == 2
+    assert L.mx_quantize(P(FAKE), 4, 64, 64, mx.NVFP4, float("inf"), P(FAKE), P(FAKE), None) == 2
+    # NULL pointers
+    assert L.mx_quantize(None, 4, 64, 64, mx.MXFP4, 1.0, P(FAKE), P(FAKE), None) == 1
+    # misaligned input / leading dimension
+    assert L.mx_quantize(P(FAKE + 2), 4, 64, 64, mx.MXFP4, 1.0, P(FAKE), P(FAKE), None) == 3
+    assert L.mx_quantize(P(FAKE), 4, 64, 68, mx.MXFP4, 1.0, P(FAKE), P(FAKE), None) == 3
+    assert "alignment" in L.mx_last_error().decode()
+    # zero rows is a no-op even with NULL pointers
+    assert L.mx_quantize(None, 0, 64, 64, mx.MXFP4, 1.0, None, None, None) == 0
+
+
+def _qm(mx, rows, cols, fmt, gs=1.0, codes=FAKE, scales=FAKE):
+    return mx._QMatrix(codes, scales, gs, fmt, rows, cols)
+
+
+def test_linear_validation(mx):
+    L = mx.lib()
+    P = ctypes.c_void_p
+    byref = ctypes.byref
+    w = _qm(mx, 64, 128, mx.MXFP4)
+
+    def call(a=FAKE, M=16, K=128, lda=128, act=mx.MXFP4, ags=1.0, w_=w, bias=None, lr=None,
+             epi=0, od=0, out=FAKE, ldo=64, osc=None, ws=FAKE, wsb=1 << 20):
+        return L.mx_linear(P(a) if a else None, M, K, lda, act, ags, byref(w_) if w_ else None,
+                           P(bias) if bias else None, lr, epi, od, P(out) if out else None, ldo,
+                           P(osc) if osc else None, P(ws) if ws else None, wsb, None)
+
+    assert call(w_=None) == 1
+    assert call(a=0) == 1
+    assert call(out=0) == 1
+    assert call(act=mx.NVFP4) == 4                   # NVFP4 activation with an MXFP4 weight
+    assert call(w_=_qm(mx, 64, 128, mx.MXFP8)) == 4  # FP8 weights are not provided
+    assert call(K=96) == 2                           # w->cols != K
+    assert call(K=100, w_=_qm(mx, 64, 100, mx.MXFP4), lda=104) == 2  # K % 32
+    assert call(ldo=32) == 2                         # ld_out < N
+    assert call(epi=2) == 1                          # re-quant epilogue without out_scales
+    assert call(epi=2, osc=FAKE, w_=_qm(mx, 48, 128, mx.MXFP4), ldo=48) == 2  # N % 32
+    assert call(epi=2, osc=FAKE, ldo=128) == 2      # ld_out must be N
+    assert call(epi=9) == 4
+    assert call(od=5) == 4
+    assert call(ws=0) == 5
+    assert call(wsb=100) == 5
+    assert call(ws=FAKE + 16) == 3                   # workspace alignment
+    assert call(a=FAKE + 8) == 3
+    assert call(bias=FAKE + 2) == 3
+    assert call(act=mx.NVFP4, w_=_qm(mx, 64, 128, mx.NVFP4, gs=0.0)) == 2
+    assert call(act=mx.NVFP4, ags=-1.0, w_=_qm(mx, 64, 128, mx.NVFP4, gs=1.0)) == 2
+    lr_bad = mx._LowRank(FAKE, FAKE, 24)
+    assert call(lr=byref(lr_bad)) == 2
+    lr_nv = mx._LowRank(FAKE, FAKE, 32)
+    assert call(act=mx.NVFP4, w_=_qm(mx, 64, 128, mx.NVFP4), lr=byref(lr_nv)) == 4
+    assert call(M=0, ws=0) == 0                      # empty activation: no-op
+
+
+def test_linear_q_validation(mx):
+    L = mx.lib()
+    P = ctypes.c_void_p
+    a = _qm(mx, 16, 128, mx.MXFP4)
+    w = _qm(mx, 64, 128, mx.MXFP4)
+    assert L.mx_linear_q(None, ctypes.byref(w), None, 0, 0, P(FAKE), 64, None, None) == 1
+    a_bad = _qm(mx, 16, 96, mx.MXFP4)
+    assert L.mx_linear_q(ctypes.byref(a_bad), ctypes.byref(w), None, 0, 0, P(FAKE), 64, None, None) == 2
+    a_mis = _qm(mx, 16, 128, mx.MXFP4, codes=FAKE + 4)
+    assert L.mx_linear_q(ctypes.byref(a_mis), ctypes.byref(w), None, 0, 0, P(FAKE), 64, None, None) == 3
+    a0 = _qm(mx, 0, 128, mx.MXFP4)
+    assert L.mx_linear_q(ctypes.byref(a0), ctypes.byref(w), None, 0, 0, P(FAKE), 64, None, None) == 0
+
+
+def test_binding_fails_loudly_without_native_library(mx, monkeypatch, tmp_path):
+    monkeypatch.setattr(mx, "_lib", None)
+    monkeypatch.setattr(mx, "LIB_PATH", str(tmp_path / "missing.so"))
+    with pytest.raises(mx.MxError):
+        mx.lib()

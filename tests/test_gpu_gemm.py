@@ -1,0 +1,308 @@
+"""GPU parity of the block-scaled linear layer against the CPU oracle.
+
+Tolerance (from the task's contract): |y_gpu - y_ref| <= 2e-3 * sum_k |a_k w_k| per element,
+before the final BF16 rounding (checked on the FP32 output), plus one binary32 rounding of the
+result; the BF16 output must be the RNE of the FP32 output.  Exact special cases are compared
+bit for bit.
+"""
+import numpy as np
+import pytest
+import torch
+
+import oracle as O
+from fp4_block_scaled_amd import synth
+from _util import (activation_bits, assert_within, bf16_rne_of_f32, dev_bits16, f16_bits,
+                   sample_rows, to_dev_bf16, to_dev_f16, unpack_fp4, weight_bits)
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(scope="module")
+def mx():
+    import fp4_block_scaled_amd as m
+    assert torch.cuda.is_available()
+    m.lib()
+    return m
+
+
+def _quant_w(mx, w_bits):
+    q = mx.quantize(to_dev_bf16(w_bits), "mxfp4")
+    return q
+
+
+def _mx_case(mx, M, K, N, seed=0, bias=True, act="mxfp4", out_dtype=torch.float32, epi="bias"):
+    a_bits = activation_bits(M, K, seed_base=11000 + seed)
+    w_bits = weight_bits(N, K, seed=11100 + seed)
+    b_bits = f16_bits(synth.normal_f32(11200 + seed, (N,), 0.01)) if bias else None
+    wq = _quant_w(mx, w_bits)
+    y = mx.linear(to_dev_bf16(a_bits), wq, to_dev_f16(b_bits) if bias else None, act_fmt=act,
+                  out_dtype=out_dtype, epilogue=epi)
+    torch.cuda.synchronize()
+    elem = O.E4M3 if act == "mxfp8" else O.E2M1
+    ac, as_ = O.quantize_mx_bf16(a_bits, elem)
+    wc, ws = O.quantize_mx_bf16(w_bits, O.E2M1)
+    assert np.array_equal(wq.codes.cpu().numpy(), wc) and np.array_equal(wq.scales.cpu().numpy(), ws)
+    y_ref, abs_sum = O.linear_ref_mx(ac, as_, elem, wc, ws, K, b_bits)
+    return y, y_ref, abs_sum, (a_bits, wq, b_bits)
+
+
+@pytest.mark.parametrize("M,K,N", [(256, 512, 512), (300, 1024, 640), (1, 256, 256), (37, 288, 96),
+                                   (64, 32, 32), (513, 768, 1024)])
+def test_mxfp4_linear_f32_vs_oracle(mx, M, K, N):
+    y, y_ref, abs_sum, _ = _mx_case(mx, M, K, N, seed=M + K + N)
+    assert_within(y.cpu().numpy(), y_ref, abs_sum)
+
+
+def test_bf16_output_is_rne_of_f32_output(mx):
+    M, K, N = 300, 1024, 640
+    a_bits = activation_bits(M, K, seed_base=12000)
+    wq = _quant_w(mx, weight_bits(N, K, seed=12100))
+    b = to_dev_f16(f16_bits(synth.normal_f32(12200, (N,), 0.01)))
+    a = to_dev_bf16(a_bits)
+    y32 = mx.linear(a, wq, b, out_dtype=torch.float32)
+    y16 = mx.linear(a, wq, b, out_dtype=torch.bfloat16)
+    torch.cuda.synchronize()
+    np.testing.assert_array_equal(dev_bits16(y16), bf16_rne_of_f32(y32.cpu().numpy()))
+
+
+def test_exact_grid_case_is_bit_exact(mx):
+    """Grid-valued operands with unit scales: every partial sum is a multiple of 1/4 below 2^24,
+    so any fp32 summation order gives the exact result."""
+    rng = np.random.default_rng(3)
+    M, K, N = 96, 2048, 160
+    grid = np.array([0, 0.5, 1, 1.5, 2, 3, 4, 6], dtype=np.float32)
+    a = rng.choice(grid, size=(M, K)) * rng.choice([-1, 1], size=(M, K))
+    w = rng.choice(grid, size=(N, K)) * rng.choice([-1, 1], size=(N, K))
+    a[:, ::32] = 6.0  # every block max is 6 -> unit scale
+    w[:, ::32] = 4.0
+    a_bits = synth.bits16(synth.to_bf16(a.astype(np.float32)))
+    w_bits = synth.bits16(synth.to_bf16(w.astype(np.float32)))
+    wq = _quant_w(mx, w_bits)
+    y = mx.linear(to_dev_bf16(a_bits), wq, None, out_dtype=torch.float32)
+    torch.cuda.synchronize()
+    ref = a.astype(np.float64) @ w.astype(np.float64).T
+    np.testing.assert_array_equal(y.cpu().numpy().astype(np.float64), ref)
+
+
+def test_one_hot_weight_and_zero_activation(mx):
+    M, K, N = 130, 512, 64
+    a_bits = activation_bits(M, K, seed_base=12300)
+    w = np.zeros((N, K), dtype=np.float32)
+    for n in range(N):
+        w[n, 7 * n] = 1.0
+    wq = _quant_w(mx, synth.bits16(synth.to_bf16(w)))
+    b_bits = f16_bits(synth.normal_f32(12400, (N,), 0.01))
+    bias = O.f16_values(b_bits)
+    y = mx.linear(to_dev_bf16(a_bits), wq, to_dev_f16(b_bits), out_dtype=torch.float32)
+    torch.cuda.synchronize()
+    ac, as_ = O.quantize_mx_bf16(a_bits)
+    adeq = O.dequantize_mx(ac, as_, K)
+    ref = (adeq[:, 0:7 * N:7] + bias).astype(np.float32)  # one fp32 rounding of â + b
+    np.testing.assert_array_equal(y.cpu().numpy(), ref)
+    y0 = mx.linear(torch.zeros((M, K), dtype=torch.bfloat16, device="cuda"), wq,
+                   to_dev_f16(b_bits), out_dtype=torch.float32)
+    torch.cuda.synchronize()
+    np.testing.assert_array_equal(y0.cpu().numpy(), np.broadcast_to(bias.astype(np.float32), (M, N)))
+
+
+def test_linear_deterministic_and_no_writes_past_output(mx):
+    M, K, N = 200, 1024, 384
+    a = to_dev_bf16(activation_bits(M, K, seed_base=12500))
+    wq = _quant_w(mx, weight_bits(N, K, seed=12600))
+    buf = torch.full((M * N + 8192,), -7.0, dtype=torch.float32, device="cuda")
+    out = buf[: M * N].view(M, N)
+    mx.linear(a, wq, None, out_dtype=torch.float32, out=out)
+    first = out.clone()
+    mx.linear(a, wq, None, out_dtype=torch.float32, out=out)
+    torch.cuda.synchronize()
+    assert torch.equal(first, out)
+    assert torch.all(buf[M * N:] == -7.0)
+
+
+def test_empty_activation_is_noop(mx):
+    wq = _quant_w(mx, weight_bits(64, 256, seed=12700))
+    y = mx.linear(torch.zeros((0, 256), dtype=torch.bfloat16, device="cuda"), wq)
+    torch.cuda.synchronize()
+    assert y.shape == (0, 64)
+
+
+def test_validation_failure_writes_nothing(mx):
+    M, K, N = 64, 256, 64
+    a = to_dev_bf16(activation_bits(M, K, seed_base=12800))
+    wq = _quant_w(mx, weight_bits(N, K, seed=12900))
+    out = torch.full((M, N), 3.0, dtype=torch.float32, device="cuda")
+    small_ws = torch.empty(16, dtype=torch.uint8, device="cuda")
+    with pytest.raises(mx.MxError, match="WORKSPACE"):
+        mx.linear(a, wq, None, out_dtype=torch.float32, out=out, workspace=small_ws)
+    torch.cuda.synchronize()
+    assert torch.all(out == 3.0)
+
+
+# ---------------------------------------------------------------------------------------------
+# W4A8 (MXFP8 activations) and the low-rank branch
+# ---------------------------------------------------------------------------------------------
+@pytest.mark.parametrize("M,K,N", [(130, 512, 256), (300, 3072, 384)])
+def test_w4a8_linear_vs_oracle(mx, M, K, N):
+    y, y_ref, abs_sum, _ = _mx_case(mx, M, K, N, seed=7 * M, act="mxfp8")
+    assert_within(y.cpu().numpy(), y_ref, abs_sum)
+
+
+def _lowrank_case(mx, M, K, N, R, act, bias):
+    a_bits = activation_bits(M, K, seed_base=13000, factor=25.0)
+    w_bits = weight_bits(N, K, seed=13100)
+    down = synth.bits16(synth.to_bf16(synth.normal_f32(13200, (K, R), 0.02)))
+    up = synth.bits16(synth.to_bf16(synth.normal_f32(13300, (R, N), 0.02)))
+    b_bits = f16_bits(synth.normal_f32(13400, (N,), 0.01)) if bias else None
+    wq = _quant_w(mx, w_bits)
+    lr = mx.LowRank(to_dev_bf16(np.ascontiguousarray(down.T)), to_dev_bf16(np.ascontiguousarray(up.T)))
+    y = mx.linear(to_dev_bf16(a_bits), wq, to_dev_f16(b_bits) if bias else None, act_fmt=act,
+                  lowrank=lr, out_dtype=torch.float32)
+    torch.cuda.synchronize()
+    elem = O.E4M3 if act == "mxfp8" else O.E2M1
+    ac, as_ = O.quantize_mx_bf16(a_bits, elem)
+    wc, ws = O.quantize_mx_bf16(w_bits)
+    y_ref, abs_sum = O.linear_ref_mx(ac, as_, elem, wc, ws, K, b_bits)
+    u_bits, lr_ref, lr_abs = O.lowrank(a_bits, down, up)
+    # u is rounded to BF16 from an fp32 (GPU) or exact (oracle) sum: near a rounding midpoint
+    # the two may pick neighbouring BF16 values, a change of up to 2^-8 |u_r| per term.
+    u = O.bf16_values(u_bits)
+    flip = (2.0 ** -8) * (np.abs(u) @ np.abs(O.bf16_values(up)))
+    return y, y_ref + lr_ref, abs_sum, 2e-3 * lr_abs + flip
+
+
+@pytest.mark.parametrize("act", ["mxfp8", "mxfp4"])
+@pytest.mark.parametrize("R", [32, 16, 64])
+def test_lowrank_branch_vs_oracle(mx, act, R):
+    y, y_ref, abs_sum, extra = _lowrank_case(mx, 200, 768, 320, R, act, bias=(R == 32))
+    assert_within(y.cpu().numpy(), y_ref, abs_sum, extra, what=f"low-rank {act} R={R}")
+
+
+def test_lowrank_zero_down_is_plain_w4a8(mx):
+    M, K, N, R = 96, 512, 256, 32
+    a = to_dev_bf16(activation_bits(M, K, seed_base=13500))
+    wq = _quant_w(mx, weight_bits(N, K, seed=13600))
+    lr = mx.LowRank(torch.zeros((R, K), dtype=torch.bfloat16, device="cuda"),
+                    to_dev_bf16(synth.bits16(synth.to_bf16(synth.normal_f32(13700, (N, R), 0.02)))))
+    y1 = mx.linear(a, wq, None, act_fmt="mxfp8", lowrank=lr, out_dtype=torch.float32)
+    y0 = mx.linear(a, wq, None, act_fmt="mxfp8", out_dtype=torch.float32)
+    torch.cuda.synchronize()
+    assert torch.equal(y1, y0)
+
+
+# ---------------------------------------------------------------------------------------------
+# FFN epilogues: GELU and GELU + MXFP4 re-quantization, then the second linear on the codes
+# ---------------------------------------------------------------------------------------------
+def _ffn_inputs(M, K, N):
+    a_bits = activation_bits(M, K, seed_base=14000, factor=30.0)
+    w_bits = weight_bits(N, K, seed=14100, sigma=0.01)
+    b_bits = f16_bits(synth.normal_f32(14200, (N,), 0.01))
+    return a_bits, w_bits, b_bits
+
+
+def test_gelu_epilogue_vs_oracle(mx):
+    M, K, N = 300, 1024, 640
+    a_bits, w_bits, b_bits = _ffn_inputs(M, K, N)
+    wq = _quant_w(mx, w_bits)
+    h = mx.linear(to_dev_bf16(a_bits), wq, to_dev_f16(b_bits), epilogue="bias_gelu",
+                  out_dtype=torch.float32)
+    torch.cuda.synchronize()
+    ac, as_ = O.quantize_mx_bf16(a_bits)
+    wc, ws = O.quantize_mx_bf16(w_bits)
+    y_ref, abs_sum = O.linear_ref_mx(ac, as_, O.E2M1, wc, ws, K, b_bits)
+    h_ref = O.gelu_tanh(y_ref)
+    # |gelu'| <= 1.13: the GEMM tolerance propagates scaled by 1.13; plus fp32 tanh error
+    tol_y = 2e-3 * abs_sum + 2.0 ** -23 * np.abs(y_ref)
+    err = np.abs(h.cpu().numpy().astype(np.float64) - h_ref)
+    assert np.all(err <= 1.13 * tol_y + 4e-6 * np.abs(h_ref) + 1e-7)
+
+
+def test_gelu_requant_epilogue_self_consistent_and_close_to_oracle(mx):
+    M, K, N = 300, 1024, 640
+    a_bits, w_bits, b_bits = _ffn_inputs(M, K, N)
+    wq = _quant_w(mx, w_bits)
+    a, b = to_dev_bf16(a_bits), to_dev_f16(b_bits)
+    hq = mx.linear(a, wq, b, epilogue="bias_gelu_quant_mxfp4")
+    h32 = mx.linear(a, wq, b, epilogue="bias_gelu", out_dtype=torch.float32)
+    torch.cuda.synchronize()
+    # the codes are exactly Q_MX of the GPU's own fp32 h (same kernel, same accumulation order)
+    c_self, s_self = O.quantize_mx_f32(h32.cpu().numpy())
+    np.testing.assert_array_equal(hq.scales.cpu().numpy(), s_self)
+    np.testing.assert_array_equal(hq.codes.cpu().numpy(), c_self)
+    # against the oracle's h: codes may flip only where h sits near a rounding midpoint
+    ac, as_ = O.quantize_mx_bf16(a_bits)
+    wc, ws = O.quantize_mx_bf16(w_bits)
+    y_ref, _ = O.linear_ref_mx(ac, as_, O.E2M1, wc, ws, K, b_bits)
+    c_ref, s_ref = O.quantize_mx_f64(O.gelu_tanh(y_ref))
+    mism = np.mean(unpack_fp4(c_ref, N) != unpack_fp4(hq.codes.cpu().numpy(), N))
+    print(f"re-quantized H code mismatch rate vs oracle: {mism:.2e}")
+    assert mism < 1e-2
+
+
+def test_ffn_pair_second_linear_on_gpu_codes(mx):
+    M, K, N = 300, 512, 1024
+    a_bits, w_bits, b_bits = _ffn_inputs(M, K, N)
+    w2_bits = weight_bits(K, N, seed=14300, sigma=0.01)
+    b2_bits = f16_bits(synth.normal_f32(14400, (K,), 0.01))
+    wq = _quant_w(mx, w_bits)
+    w2q = _quant_w(mx, w2_bits)
+    hq = mx.linear(to_dev_bf16(a_bits), wq, to_dev_f16(b_bits), epilogue="bias_gelu_quant_mxfp4")
+    y = mx.linear_q(hq, w2q, to_dev_f16(b2_bits), out_dtype=torch.float32)
+    torch.cuda.synchronize()
+    y_ref, abs_sum = O.linear_ref_mx(hq.codes.cpu().numpy(), hq.scales.cpu().numpy(), O.E2M1,
+                                     w2q.codes.cpu().numpy(), w2q.scales.cpu().numpy(), N, b2_bits)
+    assert_within(y.cpu().numpy(), y_ref, abs_sum, what="FFN2 on GPU H codes")
+
+
+# ---------------------------------------------------------------------------------------------
+# NVFP4
+# ---------------------------------------------------------------------------------------------
+@pytest.mark.parametrize("M,K,N", [(300, 1024, 640), (64, 512, 256), (257, 288, 96)])
+def test_nvfp4_linear_vs_oracle(mx, M, K, N):
+    a_bits = activation_bits(M, K, seed_base=15000, factor=30.0)
+    w_bits = weight_bits(N, K, seed=15100, sigma=0.01)
+    b_bits = f16_bits(synth.normal_f32(15200, (N,), 0.01))
+    sg_a = O.nv_global_scale(40.0)
+    wq = mx.quantize_weight_nvfp4(to_dev_bf16(w_bits))
+    sg_w = wq.global_scale
+    assert sg_w == O.nv_global_scale(O.absmax_bf16(w_bits))
+    y = mx.linear(to_dev_bf16(a_bits), wq, to_dev_f16(b_bits), act_fmt="nvfp4",
+                  act_global_scale=sg_a, out_dtype=torch.float32)
+    torch.cuda.synchronize()
+    ac, as_ = O.quantize_nv_bf16(a_bits, sg_a)
+    wc, ws = O.quantize_nv_bf16(w_bits, sg_w)
+    assert np.array_equal(wq.codes.cpu().numpy(), wc) and np.array_equal(wq.scales.cpu().numpy(), ws)
+    y_ref, abs_sum = O.linear_ref_nv(ac, as_, sg_a, wc, ws, sg_w, K, b_bits)
+    assert_within(y.cpu().numpy(), y_ref, abs_sum, what="NVFP4 linear")
+
+
+# ---------------------------------------------------------------------------------------------
+# full workload sizes, in the launch configuration the benchmark times (sampled rows)
+# ---------------------------------------------------------------------------------------------
+def _full_mx(mx, wl_name, act, nsample=192):
+    wl = synth.WORKLOADS[wl_name]
+    a_bits = synth.bits16(synth.to_bf16(wl.activation()))
+    w_bits = synth.bits16(synth.to_bf16(wl.weight()))
+    b = wl.bias()
+    b_bits = f16_bits(b) if b is not None else None
+    wq = _quant_w(mx, w_bits)
+    a = to_dev_bf16(a_bits)
+    rows = sample_rows(wl.M, nsample)
+    y = mx.linear(a, wq, to_dev_f16(b_bits) if b is not None else None, act_fmt=act,
+                  out_dtype=torch.float32)
+    torch.cuda.synchronize()
+    ys = y[torch.from_numpy(rows).cuda()].cpu().numpy()
+    del y
+    elem = O.E4M3 if act == "mxfp8" else O.E2M1
+    ac, as_ = O.quantize_mx_bf16(a_bits[rows], elem)
+    wc, ws = O.quantize_mx_bf16(w_bits)
+    y_ref, abs_sum = O.linear_ref_mx(ac, as_, elem, wc, ws, wl.K, b_bits)
+    return assert_within(ys, y_ref, abs_sum, what=wl_name)
+
+
+def test_full_size_wan_a14b_attention_projection(mx):
+    r = _full_mx(mx, "wan_a14b_attn_75600x5120x5120", "mxfp4")
+    print(f"max err/tol {r:.3f}")
+
+
+def test_full_size_w4a8(mx):
+    _full_mx(mx, "wan_ti2v5b_w4a8_4290x3072x14336", "mxfp8")

@@ -1,0 +1,193 @@
+"""GPU parity of the quantizers and the dequantizer against the CPU oracle (bit-exact)."""
+import json
+import os
+
+import numpy as np
+import pytest
+import torch
+
+import oracle as O
+from fp4_block_scaled_amd import synth
+from _util import (activation_bits, dev_bits16, to_dev_bf16, unpack_fp4)
+
+pytestmark = pytest.mark.gpu
+
+GOLDEN = os.path.join(os.path.dirname(__file__), "golden")
+
+
+@pytest.fixture(scope="module")
+def mx():
+    import fp4_block_scaled_amd as m
+    assert torch.cuda.is_available()
+    m.lib()
+    return m
+
+
+def _gpu_quant(mx, bits, fmt, sg=1.0):
+    q = mx.quantize(to_dev_bf16(bits), fmt, sg)
+    torch.cuda.synchronize()
+    return q.codes.cpu().numpy(), q.scales.cpu().numpy()
+
+
+ALL = np.arange(0, 65536, dtype=np.uint32).astype(np.uint16)
+
+
+@pytest.mark.parametrize("fmt,elem", [("mxfp4", O.E2M1), ("mxfp8", O.E4M3)])
+def test_mx_quantizer_exhaustive_bf16(mx, fmt, elem):
+    """Every BF16 pattern (NaN and Inf included) under several block maxima."""
+    anchors = [0x0000, 0x40C0, 0x3F80, 0x4040, 0x0180, 0x0080, 0x7F7F, 0x43E0, 0x0001]
+    for a in anchors:
+        block = np.zeros((len(ALL), 32), dtype=np.uint16)
+        block[:, 0] = ALL
+        block[:, 1] = a
+        block[:, 5] = ALL[::-1]
+        ref_c, ref_s = O.quantize_mx_bf16(block, elem)
+        c, s = _gpu_quant(mx, block, fmt)
+        np.testing.assert_array_equal(s, ref_s, err_msg=f"scales, anchor {a:#06x}")
+        np.testing.assert_array_equal(c, ref_c, err_msg=f"codes, anchor {a:#06x}")
+
+
+@pytest.mark.parametrize("name,fmt,elem", [("mxfp4_worked_blocks.json", "mxfp4", O.E2M1),
+                                           ("mxfp8_worked_blocks.json", "mxfp8", O.E4M3)])
+def test_mx_worked_blocks_on_gpu(mx, name, fmt, elem):
+    blocks = json.load(open(os.path.join(GOLDEN, name)))["blocks"]
+    for b in blocks:
+        if "bits" in b:
+            bits = np.asarray(b["bits"], dtype=np.uint16)
+        else:
+            bits = synth.bits16(torch.tensor(b["x"], dtype=torch.float64).to(torch.float32)
+                                .to(torch.bfloat16))
+        c, s = _gpu_quant(mx, bits[None, :], fmt)
+        assert int(s[0, 0]) == b["scale"], b["name"]
+        codes = unpack_fp4(c[0], 32) if elem == O.E2M1 else c[0]
+        np.testing.assert_array_equal(codes, b["codes"], err_msg=b["name"])
+
+
+def test_nv_worked_blocks_on_gpu(mx):
+    for b in json.load(open(os.path.join(GOLDEN, "nvfp4_worked_blocks.json")))["blocks"]:
+        bits = synth.bits16(torch.tensor(b["x"], dtype=torch.float64).to(torch.float32)
+                            .to(torch.bfloat16))
+        c, s = _gpu_quant(mx, bits[None, :], "nvfp4", 1.0)
+        assert int(s[0, 0]) == b["scale"], b["name"]
+        np.testing.assert_array_equal(unpack_fp4(c[0], 16), b["codes"], err_msg=b["name"])
+
+
+@pytest.mark.parametrize("sg", [1.0, 40.0 / 2688.0, 0.5, 3.0 / 7.0, 1e-3, 0.0625 / 2688.0])
+def test_nv_quantizer_vs_oracle(mx, sg):
+    sg = float(np.float32(sg))
+    x = synth.activation_f32(4321, 512, 1024, 1.0, 0.01, 30.0)
+    x[::5] *= 1e-3
+    x[1::7] *= 40.0
+    bits = synth.bits16(synth.to_bf16(x))
+    ref_c, ref_s = O.quantize_nv_bf16(bits, sg)
+    c, s = _gpu_quant(mx, bits, "nvfp4", sg)
+    np.testing.assert_array_equal(s, ref_s)
+    np.testing.assert_array_equal(c, ref_c)
+
+
+def test_nv_quantizer_exhaustive_bf16(mx):
+    sg = float(np.float32(40.0 / 2688.0))
+    for a in (0x0000, 0x4220, 0x3F80, 0x4300):
+        block = np.zeros((len(ALL), 16), dtype=np.uint16)
+        block[:, 0] = ALL
+        block[:, 1] = a
+        block[:, 9] = ALL[::-1]
+        ref_c, ref_s = O.quantize_nv_bf16(block, sg)
+        c, s = _gpu_quant(mx, block, "nvfp4", sg)
+        np.testing.assert_array_equal(s, ref_s, err_msg=f"anchor {a:#06x}")
+        np.testing.assert_array_equal(c, ref_c, err_msg=f"anchor {a:#06x}")
+
+
+@pytest.mark.parametrize("rows,cols,ld", [(1, 32, 32), (3, 96, 104), (257, 512, 512),
+                                          (1000, 3072, 3072)])
+@pytest.mark.parametrize("fmt,elem", [("mxfp4", O.E2M1), ("mxfp8", O.E4M3)])
+def test_mx_quantizer_shapes_and_strides(mx, rows, cols, ld, fmt, elem):
+    full = activation_bits(rows, ld, seed_base=7000 + cols)
+    x = to_dev_bf16(full)[:, :cols]
+    q = mx.quantize(x, fmt)
+    torch.cuda.synchronize()
+    ref_c, ref_s = O.quantize_mx_bf16(np.ascontiguousarray(full[:, :cols]), elem)
+    np.testing.assert_array_equal(q.scales.cpu().numpy(), ref_s)
+    np.testing.assert_array_equal(q.codes.cpu().numpy(), ref_c)
+
+
+def test_quantizer_writes_nothing_past_its_outputs_and_is_deterministic(mx):
+    rows, cols = 77, 640
+    bits = activation_bits(rows, cols, seed_base=7100)
+    x = to_dev_bf16(bits)
+    codes = torch.full((rows * cols // 2 + 4096,), 0xAB, dtype=torch.uint8, device="cuda")
+    scales = torch.full((rows * cols // 32 + 4096,), 0xCD, dtype=torch.uint8, device="cuda")
+    out = mx.QMatrix(codes[: rows * cols // 2].view(rows, cols // 2),
+                     scales[: rows * cols // 32].view(rows, cols // 32), mx.MXFP4, rows, cols)
+    mx.quantize(x, "mxfp4", out=out)
+    first = (codes.clone(), scales.clone())
+    mx.quantize(x, "mxfp4", out=out)
+    torch.cuda.synchronize()
+    assert torch.all(codes[rows * cols // 2:] == 0xAB)
+    assert torch.all(scales[rows * cols // 32:] == 0xCD)
+    assert torch.equal(first[0], codes) and torch.equal(first[1], scales)
+
+
+def test_row_shards_quantize_identically(mx):
+    bits = activation_bits(300, 1024, seed_base=7200)
+    x = to_dev_bf16(bits)
+    whole = mx.quantize(x, "mxfp4")
+    for a, b in ((0, 1), (1, 129), (129, 300)):
+        part = mx.quantize(x[a:b], "mxfp4")
+        torch.cuda.synchronize()
+        assert torch.equal(part.codes, whole.codes[a:b])
+        assert torch.equal(part.scales, whole.scales[a:b])
+
+
+@pytest.mark.parametrize("fmt,elem", [("mxfp4", O.E2M1), ("mxfp8", O.E4M3)])
+def test_dequantize_mx_exact(mx, fmt, elem):
+    bits = activation_bits(64, 1024, seed_base=7300)
+    q = mx.quantize(to_dev_bf16(bits), fmt)
+    y = mx.dequantize(q)
+    torch.cuda.synchronize()
+    ref = O.dequantize_mx(q.codes.cpu().numpy(), q.scales.cpu().numpy(), 1024, elem)
+    np.testing.assert_array_equal(dev_bits16(y), O.bf16_rne_array(ref))
+    # requantizing the dequantized tensor is the identity
+    q2 = mx.quantize(y, fmt)
+    torch.cuda.synchronize()
+    assert torch.equal(q2.codes, q.codes) and torch.equal(q2.scales, q.scales)
+
+
+def test_dequantize_nv(mx):
+    sg = float(np.float32(40.0 / 2688.0))
+    bits = activation_bits(64, 1024, seed_base=7400, factor=30.0)
+    q = mx.quantize(to_dev_bf16(bits), "nvfp4", sg)
+    y = mx.dequantize(q)
+    torch.cuda.synchronize()
+    ref = O.dequantize_nv(q.codes.cpu().numpy(), q.scales.cpu().numpy(), sg, 1024)
+    np.testing.assert_array_equal(dev_bits16(y), O.bf16_rne_array(ref))
+
+
+def test_absmax_and_global_scale(mx):
+    bits = activation_bits(333, 640, seed_base=7500, factor=30.0)
+    a = mx.absmax(to_dev_bf16(bits)).item()
+    assert a == O.absmax_bf16(bits)
+    assert mx.nvfp4_global_scale(a) == O.nv_global_scale(a)
+
+
+@pytest.mark.parametrize("wl_name", ["wan_a14b_attn_75600x5120x5120",
+                                     "wan_ti2v5b_w4a8_4290x3072x3072"])
+def test_full_size_activation_quantizer(mx, wl_name):
+    """The activation quantizer at the full workload size, every element against the oracle."""
+    wl = synth.WORKLOADS[wl_name]
+    bits = synth.bits16(synth.to_bf16(wl.activation()))
+    fmt, elem = ("mxfp8", O.E4M3) if wl.fmt == "w4a8" else ("mxfp4", O.E2M1)
+    c, s = _gpu_quant(mx, bits, fmt)
+    ref_c, ref_s = O.quantize_mx_bf16(bits, elem)
+    assert np.array_equal(s, ref_s)
+    assert np.array_equal(c, ref_c)
+
+
+def test_full_size_nvfp4_activation_quantizer(mx):
+    wl = synth.WORKLOADS["wan_a14b_nvfp4_75600x5120x13824"]
+    sg = O.nv_global_scale(wl.act_amax_static)
+    bits = synth.bits16(synth.to_bf16(wl.activation()))
+    c, s = _gpu_quant(mx, bits, "nvfp4", sg)
+    ref_c, ref_s = O.quantize_nv_bf16(bits, sg)
+    assert np.array_equal(s, ref_s)
+    assert np.array_equal(c, ref_c)
