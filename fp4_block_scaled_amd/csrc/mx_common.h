@@ -73,6 +73,40 @@ __device__ __forceinline__ uint2 load8(__amdgpu_buffer_rsrc_t r, uint32_t off) {
   const auto v = __builtin_amdgcn_raw_buffer_load_b64(r, (int)off, 0, 0);
   return make_uint2(v[0], v[1]);
 }
+// Direct-to-LDS buffer loads (CDNA4 "buffer_load_dword{,x4} ... lds"): lane i of the wave writes
+// its 4 or 16 bytes at LDS address m0 + 4i / 16i.  Written as inline asm so that the compiler
+// does not wait on them before unrelated LDS reads: the caller waits explicitly (vmcnt) before
+// the barrier that publishes the chunk.  The asm has no register outputs; its VGPR/SGPR inputs
+// are consumed at issue.  The descriptor is an SGPR quad (gfx9 raw buffer, num_records bounds
+// check: accesses past the end read zero).
+__device__ __forceinline__ v4i make_rsrc_sgpr(const void* base, uint32_t bytes) {
+  const uint64_t a = (uint64_t)base;
+  v4i r;
+  r[0] = __builtin_amdgcn_readfirstlane((int)(uint32_t)a);
+  r[1] = __builtin_amdgcn_readfirstlane((int)((uint32_t)(a >> 32) & 0xFFFFu));
+  r[2] = __builtin_amdgcn_readfirstlane((int)bytes);
+  r[3] = 0x00020000;
+  return r;
+}
+__device__ __forceinline__ void dma_lds16(v4i rs, uint32_t lds_addr, uint32_t voff, uint32_t soff) {
+  asm volatile("s_mov_b32 m0, %0\n\tbuffer_load_dwordx4 %1, %2, %3 offen lds"
+               :: "s"(lds_addr), "v"(voff), "s"(rs), "s"(soff) : "memory", "m0");
+}
+__device__ __forceinline__ void dma_lds4(v4i rs, uint32_t lds_addr, uint32_t voff, uint32_t soff) {
+  asm volatile("s_mov_b32 m0, %0\n\tbuffer_load_dword %1, %2, %3 offen lds"
+               :: "s"(lds_addr), "v"(voff), "s"(rs), "s"(soff) : "memory", "m0");
+}
+// Wait for all vector-memory operations / all LDS operations of the wave.  Builtins, not asm,
+// so that the compiler's own wait-count bookkeeping sees them (after vmcnt(0) it knows nothing
+// of its own is in flight and inserts no further waits that would also stall on the DMA).
+// Encodings (gfx9 s_waitcnt): vmcnt [3:0]+[15:14], expcnt [6:4], lgkmcnt [11:8].
+__device__ __forceinline__ void wait_vmem_all() { __builtin_amdgcn_s_waitcnt(0x0F70); }
+__device__ __forceinline__ void wait_lds_all() { __builtin_amdgcn_s_waitcnt(0xC07F); }
+template <typename T>
+__device__ __forceinline__ uint32_t lds_addr_of(T* p) {
+  return (uint32_t)(uintptr_t)(__attribute__((address_space(3))) uint8_t*)p;
+}
+
 __device__ __forceinline__ uint32_t load4(__amdgpu_buffer_rsrc_t r, uint32_t off) {
   return (uint32_t)__builtin_amdgcn_raw_buffer_load_b32(r, (int)off, 0, 0);
 }
@@ -129,6 +163,19 @@ __device__ __forceinline__ float e4m3_value(uint32_t b) {
   else v = __uint_as_float(((e + 120u) << 23) | (m << 20));
   return (b & 0x80u) ? -v : v;
 }
+
+// ---------------------------------------------------------------------------------------------
+// V_MFMA_SCALE_F32_32X32X64_F8F6F4 with operand vectors sized by format (the intrinsic is
+// overloaded on them; the clang builtin only exposes the 8-dword form, which would keep four
+// zero registers per FP4 operand).  The format, op_sel and scale-select arguments must be
+// compile-time constants at the call site.
+// ---------------------------------------------------------------------------------------------
+__device__ v16f mfma_scale_32x32x64_f4f4(v4i a, v4i b, v16f c, int fmt_a, int fmt_b, int opsel_a,
+                                         int scale_a, int opsel_b, int scale_b)
+    __asm("llvm.amdgcn.mfma.scale.f32.32x32x64.f8f6f4.v4i32.v4i32");
+__device__ v16f mfma_scale_32x32x64_f4f8(v4i a, v8i b, v16f c, int fmt_a, int fmt_b, int opsel_a,
+                                         int scale_a, int opsel_b, int scale_b)
+    __asm("llvm.amdgcn.mfma.scale.f32.32x32x64.f8f6f4.v4i32.v8i32");
 
 // ---------------------------------------------------------------------------------------------
 // cross-lane helpers
