@@ -112,10 +112,10 @@ def bench_mx_linear(args, torch, mx, synth):
     b_bits = synth.bits16(synth.to_f16(b)) if b is not None else None
     a = torch.from_numpy(a_bits.view(np.int16)).view(torch.bfloat16).cuda()
     bias = torch.from_numpy(b_bits.view(np.int16)).view(torch.float16).cuda() if b is not None else None
-    wq = mx.quantize(w_bf.cuda(), "mxfp4")                # offline weight preparation
+    wq = mx.quantize(w_bf.cuda(), "mxfp4", layout="tiled")  # offline weight preparation
     out = torch.empty((M, N), dtype=torch.bfloat16, device="cuda")
     ws = torch.empty(mx.linear_workspace_bytes(M, K, "mxfp4"), dtype=torch.uint8, device="cuda")
-    aq = mx.empty_qmatrix(M, K, "mxfp4")
+    aq = mx.empty_qmatrix(M, K, "mxfp4", layout="tiled")  # what mx_linear stages internally
     torch.cuda.synchronize()
     setup_s = time.perf_counter() - t0
 
@@ -156,7 +156,8 @@ def bench_mx_linear(args, torch, mx, synth):
                    "weight": f"N(0,{wl.w_sigma}) MXFP4", "bias": "fp16", "output": "bf16"},
         "roofline": {"bound": "mfma", "achieved": achieved, "peak": PEAK_TFLOPS["mxfp4"],
                      "unit": "TFLOP/s", "frac": achieved / PEAK_TFLOPS["mxfp4"],
-                     "traffic": traffic, "kernel": "gemm_mx_kernel (MXFP4 x MXFP4, bias, BF16 out)",
+                     "traffic": traffic,
+                     "kernel": "gemm_mx_ring_kernel<256,128> (MXFP4 x MXFP4, tiled operands, bias, BF16 out)",
                      "algorithmic_flops_per_launch": flops, "ms_per_launch": ms_gemm},
         "kernels": {
             "quantizer": {"ms": ms_quant, "GB/s": quant_bytes / (ms_quant * 1e-3) / 1e9,
@@ -170,8 +171,9 @@ def bench_mx_linear(args, torch, mx, synth):
         "setup_s": setup_s,
     }
     if not args.no_cpu:
-        res["cpu_baseline"] = cpu_baseline_mx(wl, a_bits, wq.codes.cpu().numpy(),
-                                              wq.scales.cpu().numpy(), b_bits, args.cpu_rows)
+        wrm = mx.relayout(wq)  # the oracle reads the canonical layout
+        res["cpu_baseline"] = cpu_baseline_mx(wl, a_bits, wrm.codes.cpu().numpy(),
+                                              wrm.scales.cpu().numpy(), b_bits, args.cpu_rows)
     else:
         res["cpu_baseline"] = None
     return res
@@ -189,8 +191,9 @@ def bench_variant(args, torch, mx, synth):
     bias = to_dev(synth.bits16(synth.to_f16(b)), torch.float16) if b is not None else None
     kernels = {}
     if wl.N2:  # FFN pair
-        wq = mx.quantize(w_dev, "mxfp4")
-        w2q = mx.quantize(to_dev(synth.bits16(synth.to_bf16(wl.weight2())), torch.bfloat16), "mxfp4")
+        wq = mx.quantize(w_dev, "mxfp4", layout="tiled")
+        w2q = mx.quantize(to_dev(synth.bits16(synth.to_bf16(wl.weight2())), torch.bfloat16), "mxfp4",
+                          layout="tiled")
         b2 = to_dev(synth.bits16(synth.to_f16(wl.bias2())), torch.float16)
         h = mx.empty_qmatrix(M, N, "mxfp4")
         out = torch.empty((M, wl.N2), dtype=torch.bfloat16, device="cuda")
@@ -199,12 +202,12 @@ def bench_variant(args, torch, mx, synth):
                         mx.linear_q(h, w2q, b2, out=out))
         flops = 2.0 * M * K * N + 2.0 * M * N * wl.N2
         dtype, peak = "mxfp4", PEAK_TFLOPS["mxfp4"]
-        aq = mx.quantize(a, "mxfp4")
+        aq = mx.quantize(a, "mxfp4", layout="tiled")
         kernels["ffn0_gemm_gelu_requant_ms"] = time_events(
             lambda: mx.linear_q(aq, wq, bias, epilogue="bias_gelu_quant_mxfp4", out=h), args.steps, torch)
         kernels["ffn2_gemm_ms"] = time_events(lambda: mx.linear_q(h, w2q, b2, out=out), args.steps, torch)
     elif wl.fmt == "w4a8":
-        wq = mx.quantize(w_dev, "mxfp4")
+        wq = mx.quantize(w_dev, "mxfp4", layout="tiled")
         down = to_dev(synth.bits16(synth.to_bf16(np.ascontiguousarray(wl.lora_down().T))), torch.bfloat16)
         up = to_dev(synth.bits16(synth.to_bf16(np.ascontiguousarray(wl.lora_up().T))), torch.bfloat16)
         lr = mx.LowRank(down, up)
@@ -213,7 +216,7 @@ def bench_variant(args, torch, mx, synth):
         step = lambda: mx.linear(a, wq, bias, act_fmt="mxfp8", lowrank=lr, out=out, workspace=ws)
         flops = 2.0 * M * N * K
         dtype, peak = "mxfp8xmxfp4", PEAK_TFLOPS["mxfp8"]
-        aq = mx.quantize(a, "mxfp8")
+        aq = mx.quantize(a, "mxfp8", layout="tiled")
         kernels["gemm_no_lowrank_ms"] = time_events(lambda: mx.linear_q(aq, wq, bias, out=out), args.steps, torch)
         kernels["quant_mxfp8_ms"] = time_events(lambda: mx.quantize(a, "mxfp8", out=aq), args.steps, torch)
     elif wl.fmt == "nvfp4":
@@ -240,6 +243,79 @@ def bench_variant(args, torch, mx, synth):
             "frac_of_peak": v / peak, "peak_tflops": peak, "kernels": kernels}
 
 
+COPY_BYTES = 1 << 30
+COPY_KERNEL_HINT = "copy"  # substring of the device copy kernel's name in the counter CSV
+
+
+def copy_calibration(torch):
+    """A plain copy of COPY_BYTES (read once, written once): the counters' bytes for it give the
+    scale factor from FETCH_SIZE / WRITE_SIZE to HBM bytes."""
+    src = torch.empty(COPY_BYTES // 2, dtype=torch.bfloat16, device="cuda").fill_(1.0)
+    dst = torch.empty_like(src)
+    torch.cuda.synchronize()
+    for _ in range(3):
+        dst.copy_(src)
+    torch.cuda.synchronize()
+    print(json.dumps({"copy_calibration_bytes": COPY_BYTES}), flush=True)
+
+
+def _counter_means(csv_path: str, counter: str):
+    """Counter value per dispatch (KiB), by kernel name, from a rocprofv3 counter CSV: the mean
+    over the dispatches within a factor 2 of the kernel's largest (the full-size launches; the
+    same kernel also runs on the small weight matrix at set-up)."""
+    import csv
+    vals = {}
+    with open(csv_path, newline="") as f:
+        for row in csv.DictReader(f):
+            if row.get("Counter_Name") == counter:
+                vals.setdefault(row["Kernel_Name"], []).append(float(row["Counter_Value"]))
+    out = {}
+    for k, v in vals.items():
+        big = [x for x in v if x >= 0.5 * max(v)]
+        out[k] = (sum(big) / len(big), len(big))
+    return out
+
+
+def ingest_counters(args, fetch_csv: str, write_csv: str, out_md: str):
+    fetch = _counter_means(fetch_csv, "FETCH_SIZE")
+    write = _counter_means(write_csv, "WRITE_SIZE")
+
+    def find(d, *subs):
+        hits = [k for k in d if all(s in k for s in subs)]
+        if not hits:
+            raise SystemExit(f"no kernel matching {subs} in counters")
+        return max(hits, key=lambda k: d[k][0])
+
+    kc_f, kc_w = find(fetch, COPY_KERNEL_HINT), find(write, COPY_KERNEL_HINT)
+    f_scale = COPY_BYTES / (fetch[kc_f][0] * 1024.0)
+    w_scale = COPY_BYTES / (write[kc_w][0] * 1024.0)
+    entries = {"gemm": ("gemm_mx_ring_kernel",), "quant": ("quant_mx_tiled_kernel",)}
+    try:
+        with open(TRAFFIC_FILE) as f:
+            table = json.load(f)
+    except (OSError, ValueError):
+        table = {}
+    wl = table.setdefault(args.workload, {})
+    lines = [f"# HBM traffic per launch, workload {args.workload}", "",
+             f"Copy calibration: {kc_f}: FETCH_SIZE {fetch[kc_f][0]:.0f} KiB, "
+             f"WRITE_SIZE {write[kc_w][0]:.0f} KiB per launch for a {COPY_BYTES} B copy; "
+             f"scale factors {f_scale:.4f} (fetch), {w_scale:.4f} (write).", "",
+             "| kernel | dispatches | FETCH_SIZE KiB | WRITE_SIZE KiB | HBM read B | HBM write B |",
+             "|---|---|---|---|---|---|"]
+    for key, subs in entries.items():
+        kf, kw = find(fetch, *subs), find(write, *subs)
+        rd, wr = fetch[kf][0] * 1024.0 * f_scale, write[kw][0] * 1024.0 * w_scale
+        wl[key] = {"bytes_per_launch": rd + wr, "read_bytes": rd, "write_bytes": wr,
+                   "source_hash": kernel_source_hash(), "kernel": kf}
+        lines.append(f"| {kf[:90]} | {fetch[kf][1]} | {fetch[kf][0]:.0f} | {write[kw][0]:.0f} | "
+                     f"{rd:.4g} | {wr:.4g} |")
+    with open(TRAFFIC_FILE, "w") as f:
+        json.dump(table, f, indent=1, sort_keys=True)
+    with open(out_md, "a") as f:
+        f.write("\n".join(lines) + "\n")
+    print("\n".join(lines))
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -247,8 +323,17 @@ def main():
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--workload", default="wan_a14b_attn_75600x5120x5120")
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
-    ap.add_argument("--cpu-rows", type=int, default=64)
+    ap.add_argument("--cpu-rows", type=int, default=16384,
+                    help="rows of the CPU oracle sample (about 10-30 s on 8-16 cores)")
+    ap.add_argument("--copy-calibration", action="store_true",
+                    help="first run a plain device copy of COPY_BYTES, for HBM counter calibration")
+    ap.add_argument("--ingest-counters", nargs=3, metavar=("FETCH_CSV", "WRITE_CSV", "OUT_MD"),
+                    help="turn two rocprofv3 --pmc runs (FETCH_SIZE, WRITE_SIZE; each holding the "
+                         "copy calibration and a bench run) into profiles/traffic.json and a summary")
     args = ap.parse_args()
+    if args.ingest_counters:
+        ingest_counters(args, *args.ingest_counters)
+        return
     world = int(os.environ.get("WORLD_SIZE", "1"))
     if args.gpus != 1 or world != 1:
         print(json.dumps({"error": "this build runs on one GPU only; the linear shards along M "
@@ -262,6 +347,8 @@ def main():
     if not torch.cuda.is_available():
         raise SystemExit("bench.py needs a GPU")
     mx.lib()
+    if args.copy_calibration:
+        copy_calibration(torch)
     if args.workload == "wan_a14b_attn_75600x5120x5120" or synth.WORKLOADS[args.workload].fmt == "mxfp4" \
             and not synth.WORKLOADS[args.workload].N2:
         res = bench_mx_linear(args, torch, mx, synth)

@@ -5,7 +5,8 @@ supplies device memory and the current HIP stream).  There is no CPU fallback: i
 library is missing or no GPU is present the calls raise.
 
 The C ABI is declared in ``include/mxfp.h``; the functions here carry the same names:
-``quantize``, ``dequantize``, ``absmax``, ``nvfp4_global_scale``, ``linear`` (dynamic
+``quantize``, ``dequantize``, ``absmax``, ``nvfp4_global_scale``, ``relayout``, ``tiled_bytes``,
+``linear`` (dynamic
 activation quantization + block-scaled GEMM + epilogue), ``linear_q`` (pre-quantized
 activation) and ``linear_workspace_bytes``.
 """
@@ -22,12 +23,14 @@ _HERE = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(_HERE, "libmxfp.so")
 
 MXFP4, MXFP8, NVFP4 = 0, 1, 2
+ROW_MAJOR, TILED = 0, 1
 EPI_BIAS, EPI_BIAS_GELU, EPI_BIAS_GELU_QUANT_MXFP4 = 0, 1, 2
 OUT_BF16, OUT_F32 = 0, 1
 _GROUP = {MXFP4: 32, MXFP8: 32, NVFP4: 16}
 _FMT_NAMES = {"mxfp4": MXFP4, "mxfp8": MXFP8, "nvfp4": NVFP4}
 _EPI_NAMES = {"bias": EPI_BIAS, "bias_gelu": EPI_BIAS_GELU,
               "bias_gelu_quant_mxfp4": EPI_BIAS_GELU_QUANT_MXFP4}
+_LAYOUT_NAMES = {"row_major": ROW_MAJOR, "tiled": TILED}
 
 
 class MxError(RuntimeError):
@@ -37,7 +40,7 @@ class MxError(RuntimeError):
 class _QMatrix(ctypes.Structure):
     _fields_ = [("codes", ctypes.c_void_p), ("scales", ctypes.c_void_p),
                 ("global_scale", ctypes.c_float), ("fmt", ctypes.c_int32),
-                ("rows", ctypes.c_int64), ("cols", ctypes.c_int64)]
+                ("rows", ctypes.c_int64), ("cols", ctypes.c_int64), ("layout", ctypes.c_int32)]
 
 
 class _LowRank(ctypes.Structure):
@@ -59,7 +62,10 @@ def lib():
         L.mx_status_string.argtypes = [ctypes.c_int]
         L.mx_status_string.restype = ctypes.c_char_p
         L.mx_last_error.restype = ctypes.c_char_p
-        L.mx_quantize.argtypes = [P, I64, I64, I64, I32, ctypes.c_float, P, P, P]
+        L.mx_quantize.argtypes = [P, I64, I64, I64, I32, I32, ctypes.c_float, P, P, P]
+        SZ = ctypes.POINTER(ctypes.c_size_t)
+        L.mx_tiled_bytes.argtypes = [I64, I64, I32, SZ, SZ]
+        L.mx_relayout.argtypes = [ctypes.POINTER(_QMatrix), ctypes.POINTER(_QMatrix), P]
         L.mx_dequantize.argtypes = [ctypes.POINTER(_QMatrix), P, I64, P]
         L.mx_absmax.argtypes = [P, I64, I64, I64, P, P]
         L.mx_nvfp4_global_scale.argtypes = [ctypes.c_float]
@@ -70,9 +76,10 @@ def lib():
                                 ctypes.POINTER(_LowRank), I32, I32, P, I64, P, P, ctypes.c_size_t, P]
         L.mx_linear_q.argtypes = [ctypes.POINTER(_QMatrix), ctypes.POINTER(_QMatrix), P, I32, I32,
                                   P, I64, P, P]
-        for f in ("mx_quantize", "mx_dequantize", "mx_absmax", "mx_linear", "mx_linear_q"):
+        for f in ("mx_quantize", "mx_dequantize", "mx_absmax", "mx_linear", "mx_linear_q",
+                  "mx_tiled_bytes", "mx_relayout"):
             getattr(L, f).restype = ctypes.c_int
-        if L.mx_abi_version() != 1:
+        if L.mx_abi_version() != 2:
             raise MxError("libmxfp.so ABI version mismatch")
         _lib = L
     return _lib
@@ -90,6 +97,10 @@ def _stream():
 
 def _fmt(fmt) -> int:
     return _FMT_NAMES[fmt] if isinstance(fmt, str) else int(fmt)
+
+
+def _layout(layout) -> int:
+    return _LAYOUT_NAMES[layout] if isinstance(layout, str) else int(layout)
 
 
 def _ptr(t: Optional[torch.Tensor]):
@@ -110,18 +121,21 @@ def _need_cuda(t: torch.Tensor, name: str, dtype=None):
 
 @dataclass
 class QMatrix:
-    """A quantized matrix: codes [rows, cols/2] (FP4) or [rows, cols] (FP8) uint8, scales
-    [rows, cols/G] uint8, an NVFP4 global scale (decode direction), the format id."""
+    """A quantized matrix: uint8 codes and scales, an NVFP4 global scale (decode direction),
+    the format id and the layout.  Row-major: codes [rows, cols/2] (FP4) or [rows, cols] (FP8),
+    scales [rows, cols/G].  Tiled (MX formats): flat byte tensors in the GEMM operand layout of
+    ``include/mxfp.h``."""
     codes: torch.Tensor
     scales: torch.Tensor
     fmt: int
     rows: int
     cols: int
     global_scale: float = 1.0
+    layout: int = ROW_MAJOR
 
     def _c(self) -> _QMatrix:
         return _QMatrix(self.codes.data_ptr(), self.scales.data_ptr(), self.global_scale,
-                        self.fmt, self.rows, self.cols)
+                        self.fmt, self.rows, self.cols, self.layout)
 
 
 @dataclass
@@ -136,8 +150,21 @@ class LowRank:
         return self.down_t.shape[0]
 
 
-def empty_qmatrix(rows: int, cols: int, fmt, device="cuda", global_scale: float = 1.0) -> QMatrix:
-    fmt = _fmt(fmt)
+def tiled_bytes(rows: int, cols: int, fmt="mxfp4"):
+    """(code bytes, scale bytes) of a rows x cols matrix in the tiled layout."""
+    cb, sb = ctypes.c_size_t(), ctypes.c_size_t()
+    _check(lib().mx_tiled_bytes(rows, cols, _fmt(fmt), ctypes.byref(cb), ctypes.byref(sb)))
+    return cb.value, sb.value
+
+
+def empty_qmatrix(rows: int, cols: int, fmt, device="cuda", global_scale: float = 1.0,
+                  layout="row_major") -> QMatrix:
+    fmt, layout = _fmt(fmt), _layout(layout)
+    if layout == TILED:
+        cb, sb = tiled_bytes(rows, cols, fmt)
+        codes = torch.empty(cb, dtype=torch.uint8, device=device)
+        scales = torch.empty(sb, dtype=torch.uint8, device=device)
+        return QMatrix(codes, scales, fmt, rows, cols, global_scale, TILED)
     code_cols = cols if fmt == MXFP8 else cols // 2
     codes = torch.empty((rows, code_cols), dtype=torch.uint8, device=device)
     scales = torch.empty((rows, cols // _GROUP[fmt]), dtype=torch.uint8, device=device)
@@ -145,18 +172,29 @@ def empty_qmatrix(rows: int, cols: int, fmt, device="cuda", global_scale: float 
 
 
 def quantize(x: torch.Tensor, fmt="mxfp4", global_scale: float = 1.0,
-             out: Optional[QMatrix] = None) -> QMatrix:
-    """Dynamic quantization of a 2-D BF16 GPU tensor (row stride may exceed its width)."""
+             out: Optional[QMatrix] = None, layout="row_major") -> QMatrix:
+    """Dynamic quantization of a 2-D BF16 GPU tensor (row stride may exceed its width), into
+    the row-major or (MX formats) the tiled layout; ``out`` fixes the layout when given."""
     fmt = _fmt(fmt)
     _need_cuda(x, "x", torch.bfloat16)
     if x.dim() != 2 or x.stride(1) != 1:
         raise MxError("x must be 2-D with unit column stride")
     rows, cols = x.shape
-    q = out if out is not None else empty_qmatrix(rows, cols, fmt, x.device, global_scale)
+    q = out if out is not None else empty_qmatrix(rows, cols, fmt, x.device, global_scale, layout)
     q.global_scale = global_scale
-    _check(lib().mx_quantize(_ptr(x), rows, cols, _ld(x), fmt, global_scale,
+    _check(lib().mx_quantize(_ptr(x), rows, cols, _ld(x), fmt, q.layout, global_scale,
                              _ptr(q.codes), _ptr(q.scales), _stream()))
     return q
+
+
+def relayout(q: QMatrix, layout=None) -> QMatrix:
+    """A copy of q in the other layout (or the one named): tiled for the GEMM, row-major to
+    read it."""
+    target = (TILED if q.layout == ROW_MAJOR else ROW_MAJOR) if layout is None else _layout(layout)
+    out = empty_qmatrix(q.rows, q.cols, q.fmt, q.codes.device, q.global_scale, target)
+    src, dst = q._c(), out._c()
+    _check(lib().mx_relayout(ctypes.byref(src), ctypes.byref(dst), _stream()))
+    return out
 
 
 def dequantize(q: QMatrix) -> torch.Tensor:

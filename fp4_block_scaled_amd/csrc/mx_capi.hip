@@ -33,6 +33,20 @@ int64_t code_bytes(int64_t rows, int64_t cols, int32_t fmt) {
   return fmt == MX_FMT_MXFP8 ? rows * cols : rows * (cols / 2);
 }
 size_t round_up(size_t v, size_t a) { return (v + a - 1) / a * a; }
+bool is_mx(int32_t fmt) { return fmt == MX_FMT_MXFP4 || fmt == MX_FMT_MXFP8; }
+int64_t padded_rows(int64_t rows) { return (rows + 255) / 256 * 256; }
+// tiled sizes (MX formats, cols % 128 == 0)
+size_t tiled_code_bytes(int64_t rows, int64_t cols, int32_t fmt) { return (size_t)code_bytes(padded_rows(rows), cols, fmt); }
+size_t tiled_scale_bytes(int64_t rows, int64_t cols) { return (size_t)(padded_rows(rows) * (cols / 32)); }
+// The activation of mx_linear is staged in the tiled layout when the GEMM can use it.
+bool act_tiled(int32_t act_fmt, int64_t K) { return is_mx(act_fmt) && K % 128 == 0; }
+mx_status check_layout(const mx_qmatrix* q, const char* name) {
+  if (q->layout == MX_LAYOUT_ROW_MAJOR) return MX_OK;
+  if (q->layout != MX_LAYOUT_TILED) return fail(MX_ERR_UNSUPPORTED, "%s: unknown layout %d", name, q->layout);
+  if (!is_mx(q->fmt)) return fail(MX_ERR_UNSUPPORTED, "%s: the tiled layout holds MX formats only", name);
+  if (q->cols % 128) return fail(MX_ERR_SHAPE, "%s: the tiled layout needs cols %% 128 == 0", name);
+  return MX_OK;
+}
 
 struct Workspace {
   uint8_t* codes;
@@ -40,13 +54,20 @@ struct Workspace {
   uint16_t* u;
 };
 
+size_t ws_code_bytes(int64_t M, int64_t K, int32_t act_fmt) {
+  return act_tiled(act_fmt, K) ? tiled_code_bytes(M, K, act_fmt) : (size_t)code_bytes(M, K, act_fmt);
+}
+size_t ws_scale_bytes(int64_t M, int64_t K, int32_t act_fmt) {
+  return act_tiled(act_fmt, K) ? tiled_scale_bytes(M, K) : (size_t)(M * (K / group_of(act_fmt)));
+}
+
 Workspace carve(void* ws, int64_t M, int64_t K, int32_t act_fmt, int32_t rank) {
   Workspace w;
   uint8_t* p = (uint8_t*)ws;
   w.codes = p;
-  p += round_up((size_t)code_bytes(M, K, act_fmt), 256);
+  p += round_up(ws_code_bytes(M, K, act_fmt), 256);
   w.scales = p;
-  p += round_up((size_t)(M * (K / group_of(act_fmt))), 256);
+  p += round_up(ws_scale_bytes(M, K, act_fmt), 256);
   w.u = rank > 0 ? (uint16_t*)p : nullptr;
   return w;
 }
@@ -68,6 +89,10 @@ mx_status check_gemm_tail(int32_t act_fmt, int64_t M, int64_t K, const mx_qmatri
   if (M < 0 || K <= 0) return fail(MX_ERR_SHAPE, "M must be >= 0 and K > 0");
   if (w->cols != K) return fail(MX_ERR_SHAPE, "w->cols (%lld) != K (%lld)", (long long)w->cols, (long long)K);
   if (w->rows < 1) return fail(MX_ERR_SHAPE, "w->rows must be >= 1");
+  {
+    mx_status ls = check_layout(w, "w");
+    if (ls != MX_OK) return ls;
+  }
   if (K % 32) return fail(MX_ERR_SHAPE, "K (%lld) must be a multiple of 32", (long long)K);
   if (M > INT32_MAX || w->rows > INT32_MAX || K > INT32_MAX)
     return fail(MX_ERR_SHAPE, "M, N and K must fit in 31 bits");
@@ -123,9 +148,15 @@ float mx_nvfp4_global_scale(float amax) {
 }
 
 mx_status mx_quantize(const uint16_t* x, int64_t rows, int64_t cols, int64_t ld_x, int32_t fmt,
-                      float global_scale, void* codes, uint8_t* scales, void* stream) {
+                      int32_t layout, float global_scale, void* codes, uint8_t* scales,
+                      void* stream) {
   g_err[0] = 0;
   if (!fmt_ok(fmt)) return fail(MX_ERR_UNSUPPORTED, "unknown format %d", fmt);
+  if (layout != MX_LAYOUT_ROW_MAJOR && layout != MX_LAYOUT_TILED)
+    return fail(MX_ERR_UNSUPPORTED, "unknown layout %d", layout);
+  const bool tiled = layout == MX_LAYOUT_TILED;
+  if (tiled && !is_mx(fmt)) return fail(MX_ERR_UNSUPPORTED, "the tiled layout holds MX formats only");
+  if (tiled && cols % 128) return fail(MX_ERR_SHAPE, "the tiled layout needs cols %% 128 == 0");
   const int G = group_of(fmt);
   if (rows < 0 || cols <= 0) return fail(MX_ERR_SHAPE, "rows must be >= 0 and cols > 0");
   if (cols % G) return fail(MX_ERR_SHAPE, "cols (%lld) must be a multiple of %d", (long long)cols, G);
@@ -137,6 +168,11 @@ mx_status mx_quantize(const uint16_t* x, int64_t rows, int64_t cols, int64_t ld_
   if (!aligned(x, 16) || ld_x % 8) return fail(MX_ERR_ALIGN, "x needs 16-byte alignment and ld_x %% 8 == 0");
   if (!aligned(codes, fmt == MX_FMT_MXFP8 ? 8 : 4)) return fail(MX_ERR_ALIGN, "codes misaligned");
   hipStream_t s = (hipStream_t)stream;
+  if (tiled) {
+    if (!aligned(codes, 16) || !aligned(scales, 16)) return fail(MX_ERR_ALIGN, "tiled codes and scales need 16-byte alignment");
+    return hip_status(mxk::launch_quant_mx_tiled(x, rows, cols, ld_x, fmt == MX_FMT_MXFP8 ? 1 : 0,
+                                                 (uint8_t*)codes, scales, s), "mx_quantize launch");
+  }
   hipError_t e = fmt == MX_FMT_NVFP4
                      ? mxk::launch_quant_nv(x, rows, cols, ld_x, global_scale, (uint8_t*)codes, scales, s)
                      : mxk::launch_quant_mx(x, rows, cols, ld_x, fmt == MX_FMT_MXFP8 ? 1 : 0,
@@ -144,10 +180,46 @@ mx_status mx_quantize(const uint16_t* x, int64_t rows, int64_t cols, int64_t ld_
   return hip_status(e, "mx_quantize launch");
 }
 
+mx_status mx_tiled_bytes(int64_t rows, int64_t cols, int32_t fmt, size_t* code_bytes_out,
+                         size_t* scale_bytes_out) {
+  g_err[0] = 0;
+  if (!code_bytes_out || !scale_bytes_out) return fail(MX_ERR_NULL, "output pointers must be non-NULL");
+  if (!is_mx(fmt)) return fail(MX_ERR_UNSUPPORTED, "the tiled layout holds MX formats only");
+  if (rows < 0 || cols <= 0 || cols % 128) return fail(MX_ERR_SHAPE, "rows >= 0 and cols %% 128 == 0 needed");
+  *code_bytes_out = tiled_code_bytes(rows, cols, fmt);
+  *scale_bytes_out = tiled_scale_bytes(rows, cols);
+  return MX_OK;
+}
+
+mx_status mx_relayout(const mx_qmatrix* src, const mx_qmatrix* dst, void* stream) {
+  g_err[0] = 0;
+  if (!src || !dst) return fail(MX_ERR_NULL, "src and dst must be non-NULL");
+  if (src->fmt != dst->fmt || src->rows != dst->rows || src->cols != dst->cols)
+    return fail(MX_ERR_SHAPE, "src and dst differ in format or shape");
+  if (!is_mx(src->fmt)) return fail(MX_ERR_UNSUPPORTED, "the tiled layout holds MX formats only");
+  mx_status ls = check_layout(src, "src");
+  if (ls == MX_OK) ls = check_layout(dst, "dst");
+  if (ls != MX_OK) return ls;
+  if (src->layout == dst->layout) return fail(MX_ERR_UNSUPPORTED, "src and dst have the same layout");
+  if (src->rows < 0 || src->cols <= 0) return fail(MX_ERR_SHAPE, "bad rows/cols");
+  if (src->rows == 0) return MX_OK;
+  if (!src->codes || !src->scales || !dst->codes || !dst->scales)
+    return fail(MX_ERR_NULL, "codes and scales must be non-NULL");
+  if (!aligned(src->codes, 16) || !aligned(dst->codes, 16) || !aligned(src->scales, 4) || !aligned(dst->scales, 4))
+    return fail(MX_ERR_ALIGN, "codes need 16-byte and scales 4-byte alignment");
+  return hip_status(mxk::launch_relayout((const uint8_t*)src->codes, src->scales, (uint8_t*)dst->codes,
+                                         (uint8_t*)dst->scales, src->rows, src->cols,
+                                         src->fmt == MX_FMT_MXFP8 ? 1 : 0,
+                                         dst->layout == MX_LAYOUT_TILED, (hipStream_t)stream),
+                    "mx_relayout launch");
+}
+
 mx_status mx_dequantize(const mx_qmatrix* q, uint16_t* y, int64_t ld_y, void* stream) {
   g_err[0] = 0;
   if (!q) return fail(MX_ERR_NULL, "q is NULL");
   if (!fmt_ok(q->fmt)) return fail(MX_ERR_UNSUPPORTED, "unknown format %d", q->fmt);
+  if (q->layout != MX_LAYOUT_ROW_MAJOR)
+    return fail(MX_ERR_UNSUPPORTED, "mx_dequantize reads row-major matrices (see mx_relayout)");
   const int G = group_of(q->fmt);
   if (q->rows < 0 || q->cols <= 0 || q->cols % G) return fail(MX_ERR_SHAPE, "bad rows/cols");
   if (ld_y < q->cols) return fail(MX_ERR_SHAPE, "ld_y < cols");
@@ -174,14 +246,13 @@ mx_status mx_absmax(const uint16_t* x, int64_t rows, int64_t cols, int64_t ld_x,
 
 size_t mx_linear_workspace_bytes(int64_t M, int64_t K, int32_t act_fmt, int32_t rank) {
   if (M <= 0 || K <= 0 || !fmt_ok(act_fmt)) return 0;
-  size_t b = round_up((size_t)code_bytes(M, K, act_fmt), 256) +
-             round_up((size_t)(M * (K / group_of(act_fmt))), 256);
+  size_t b = round_up(ws_code_bytes(M, K, act_fmt), 256) + round_up(ws_scale_bytes(M, K, act_fmt), 256);
   if (rank > 0) b += round_up((size_t)M * (size_t)rank * 2, 256);
   return b;
 }
 
 static mx_status run_gemm(const uint8_t* a_codes, const uint8_t* a_scales, float a_gscale,
-                          int32_t act_fmt, int64_t M, int64_t K, const mx_qmatrix* w,
+                          int32_t act_fmt, bool a_is_tiled, int64_t M, int64_t K, const mx_qmatrix* w,
                           const uint16_t* bias, const uint16_t* lr_u, const mx_lowrank* lr,
                           int32_t epilogue, int32_t out_dtype, void* out, int64_t ld_out,
                           uint8_t* out_scales, hipStream_t s) {
@@ -204,6 +275,8 @@ static mx_status run_gemm(const uint8_t* a_codes, const uint8_t* a_scales, float
   p.epi = epilogue == MX_EPI_BIAS ? mxk::EPI_BIAS
                                   : epilogue == MX_EPI_BIAS_GELU ? mxk::EPI_GELU : mxk::EPI_GELU_QUANT;
   p.out_f32 = out_dtype == MX_OUT_F32 ? 1 : 0;
+  p.a_tiled = a_is_tiled ? 1 : 0;
+  p.w_tiled = w->layout == MX_LAYOUT_TILED ? 1 : 0;
   hipError_t e = w->fmt == MX_FMT_NVFP4 ? mxk::launch_gemm_nv(p, s)
                                          : mxk::launch_gemm_mx(p, act_fmt == MX_FMT_MXFP8, s);
   return hip_status(e, "GEMM launch");
@@ -239,8 +312,11 @@ mx_status mx_linear(const uint16_t* a, int64_t M, int64_t K, int64_t ld_a, int32
   hipStream_t s = (hipStream_t)stream;
   Workspace ws = carve(workspace, M, K, act_fmt, rank);
   hipError_t e;
+  const bool tiled = act_tiled(act_fmt, K);
   if (act_fmt == MX_FMT_NVFP4)
     e = mxk::launch_quant_nv(a, M, K, ld_a, act_global_scale, ws.codes, ws.scales, s);
+  else if (tiled)
+    e = mxk::launch_quant_mx_tiled(a, M, K, ld_a, act_fmt == MX_FMT_MXFP8 ? 1 : 0, ws.codes, ws.scales, s);
   else
     e = mxk::launch_quant_mx(a, M, K, ld_a, act_fmt == MX_FMT_MXFP8 ? 1 : 0, ws.codes, ws.scales, s);
   if (e != hipSuccess) return hip_status(e, "activation quantizer launch");
@@ -248,7 +324,7 @@ mx_status mx_linear(const uint16_t* a, int64_t M, int64_t K, int64_t ld_a, int32
     e = mxk::launch_lowrank_down(a, ld_a, lr->down, (int)M, (int)K, rank, ws.u, s);
     if (e != hipSuccess) return hip_status(e, "low-rank launch");
   }
-  return run_gemm(ws.codes, ws.scales, act_global_scale, act_fmt, M, K, w, bias, ws.u, lr,
+  return run_gemm(ws.codes, ws.scales, act_global_scale, act_fmt, tiled, M, K, w, bias, ws.u, lr,
                   epilogue, out_dtype, out, ld_out, out_scales, s);
 }
 
@@ -260,13 +336,16 @@ mx_status mx_linear_q(const mx_qmatrix* a, const mx_qmatrix* w, const uint16_t* 
   mx_status st = check_gemm_tail(a->fmt, a->rows, a->cols, w, bias, epilogue, out_dtype, out,
                                  ld_out, out_scales);
   if (st != MX_OK) return st;
+  st = check_layout(a, "a");
+  if (st != MX_OK) return st;
   if (a->rows == 0) return MX_OK;
   if (!a->codes || !a->scales) return fail(MX_ERR_NULL, "a->codes / a->scales is NULL");
   if (!aligned(a->codes, 16) || !aligned(a->scales, 8))
     return fail(MX_ERR_ALIGN, "activation codes need 16-byte and scales 8-byte alignment");
   if (a->fmt == MX_FMT_NVFP4 && !finite_pos(a->global_scale))
     return fail(MX_ERR_SHAPE, "NVFP4 activation global scale must be finite and > 0");
-  return run_gemm((const uint8_t*)a->codes, a->scales, a->global_scale, a->fmt, a->rows, a->cols,
+  return run_gemm((const uint8_t*)a->codes, a->scales, a->global_scale, a->fmt,
+                  a->layout == MX_LAYOUT_TILED, a->rows, a->cols,
                   w, bias, nullptr, nullptr, epilogue, out_dtype, out, ld_out, out_scales,
                   (hipStream_t)stream);
 }

@@ -200,4 +200,21 @@ __device__ __forceinline__ void static_for(F&& f) {
   }
 }
 
+// Tiled GEMM operand layout (MX formats, columns a multiple of 128, rows padded to 256): the
+// byte offsets of one 16-byte code piece and of one row's 4 scale bytes of a 128-column chunk.
+constexpr int TILE_ROWS = 256;
+__host__ __device__ inline int64_t tiled_rows(int64_t rows) { return (rows + TILE_ROWS - 1) / TILE_ROWS * TILE_ROWS; }
+// FP4: 1 KB tile = 16 rows x 128 columns; piece g (0..3) of row r in chunk kb
+__device__ __forceinline__ int64_t tiled_fp4_off(int64_t r, int64_t kb, int g, int64_t nkc) {
+  return ((r >> 4) * nkc + kb) * 1024 + (r & 15) * 64 + ((g ^ (int)((r >> 2) & 3)) << 4);
+}
+// FP8: 1 KB tile = 8 rows x 128 columns; piece g (0..7) of row r in chunk kb
+__device__ __forceinline__ int64_t tiled_fp8_off(int64_t r, int64_t kb, int g, int64_t nkc) {
+  return ((r >> 3) * nkc + kb) * 1024 + (r & 7) * 128 + ((g ^ (int)((r >> 1) & 7)) << 4);
+}
+// scales: 256-byte tile = 64 rows x 4 bytes
+__device__ __forceinline__ int64_t tiled_scale_off(int64_t r, int64_t kb, int64_t nkc) {
+  return ((r >> 6) * nkc + kb) * 256 + (r & 63) * 4;
+}
+
 }  // namespace mxk

@@ -8,16 +8,15 @@
 // of one output row m, 4 consecutive n at a time, in each lane: the epilogue can store them as
 // vectors and reduce a 32-wide re-quantization group with a single cross-lane exchange.
 //
-// K ordering inside a 256-element K chunk: the sum over k is order-free, so MFMA step s (0..3)
-// takes the chunk's 32-element blocks s and 4 + s as its two scale blocks.  The scale of block
-// b comes from the lanes of half b (lane / 32), so a lane of half h needs the E8M0 bytes of
-// blocks 4h + s, s = 0..3: the contiguous dword [4h, 4h+4) of the row's 8 chunk scales, op_sel
-// s picking the byte.  FP4 lanes of half h hold their block whole (64 contiguous bytes per row
-// and chunk); FP8 lanes split theirs (see mx_step).  Both operands pair the same k.
-//
-// Staging: a 256 x 256 output tile per workgroup (4 waves, 128 x 128 each, 4 x 4 MFMA blocks),
-// K chunks of 256 double-buffered in LDS.  LDS rows hold 16-byte chunks XOR-swizzled by the
-// row index so that the 16-byte fragment reads of 8 consecutive rows hit distinct banks.
+// Two MX kernels share those conventions:
+//  - the ring kernel (K % 128 == 0, every configuration of the model): 256 x 128 (W4A4) or
+//    128 x 128 (W4A8) output tiles, two workgroups per compute unit, a 3-deep LDS ring of
+//    128-element K chunks filled by direct-to-LDS buffer loads, operands row-major or in the
+//    tiled layout whose 1 KB / 256 B tiles are exactly the LDS images the ring holds;
+//  - the register-staged kernel for any other K (a multiple of 32): 256-element chunks
+//    double-buffered through registers, partial last chunk zero-filled.
+// Sums over k are order-free, so each kernel pairs K blocks into MFMA steps in whatever order
+// makes the per-lane scale bytes one shifted or op_sel-selected dword (see each kernel).
 //
 // NVFP4 (NVFP4 model card, Model Details) has E4M3 scales per 16 elements that the scaled MFMA
 // cannot apply, and code * scale needs up to 6 significant bits, more than FP8 holds; it is
@@ -201,58 +200,6 @@ __device__ __forceinline__ void epilogue_block(const GemmParams& p, v16f acc, in
   }
 }
 
-// Output of one wave's sub-tile through LDS, for the BF16 / FP32 epilogues when N, ld_out and out
-// are 16-byte granular.  The 16 values a lane holds per 32 x 32 block are 4 runs of 4 consecutive
-// n in one row, so direct stores put 16-byte pieces of 32 rows in each instruction.  Instead the
-// values go to a (32 FM)-row x 128-byte LDS buffer (64 BF16 / 32 FP32 columns, 16-byte chunks
-// XOR-swizzled by row), and each store instruction writes 8 whole 128-byte row segments.
-// `stage` is this wave's (32 FM) x 128 bytes; only this wave touches it.
-template <int FN, int FM, int EPI, bool OUTF32>
-__device__ __forceinline__ void epilogue_staged(const GemmParams& p, v16f (&acc)[FN][FM], int n_base,
-                                                int m_base, uint8_t* stage) {
-  const int lane = lane_id();
-  const int r32 = lane & 31, h = lane >> 5;
-  auto sw = [](int row, int c) { return row * 128 + ((c ^ ((row ^ (row >> 3)) & 7)) << 4); };
-  constexpr int PER_PASS = OUTF32 ? 1 : 2;  // n-blocks per 128-byte row segment
-  static_for<FN / PER_PASS>([&](auto pass) {
-    static_for<PER_PASS>([&](auto ii) {
-      constexpr int I = decltype(pass)::value * PER_PASS + decltype(ii)::value;
-      const int col0 = decltype(ii)::value * 32;
-      float b[16];
-      load_bias16(p, n_base + 32 * I, b);
-      static_for<FM>([&](auto j) {
-        __builtin_amdgcn_sched_barrier(0);  // one block at a time: keep register use small
-        float v[16];
-        finish16<EPI>(p, acc[I][j], b, v);
-        const int row = 32 * j + r32;
-#pragma unroll
-        for (int a = 0; a < 4; ++a) {
-          const int col = col0 + 8 * a + 4 * h;  // first of 4 consecutive columns
-          if (OUTF32) {
-            *(float4*)(stage + sw(row, col >> 2)) = make_float4(v[4 * a], v[4 * a + 1], v[4 * a + 2], v[4 * a + 3]);
-          } else {
-            const uint32_t b0 = f32_to_bf16_rne(v[4 * a]) | (f32_to_bf16_rne(v[4 * a + 1]) << 16);
-            const uint32_t b1 = f32_to_bf16_rne(v[4 * a + 2]) | (f32_to_bf16_rne(v[4 * a + 3]) << 16);
-            *(uint2*)(stage + sw(row, col >> 3) + ((col & 4) << 1)) = make_uint2(b0, b1);
-          }
-        }
-      });
-    });
-    wait_lds_all();  // the wave's own LDS writes are done
-    constexpr int ESZ = OUTF32 ? 4 : 2;
-    const int ncol0 = n_base + decltype(pass)::value * (OUTF32 ? 32 : 64);
-#pragma unroll
-    for (int t = 0; t < FM * 4; ++t) {
-      const int row = t * 8 + (lane >> 3), c = lane & 7;
-      const uint4 d = *(const uint4*)(stage + sw(row, c));
-      const int m = m_base + row;
-      const int n = ncol0 + c * (16 / ESZ);
-      if (m < p.M && n < p.N) *(uint4*)((uint8_t*)p.out + ((int64_t)m * p.ld_out + n) * ESZ) = d;
-    }
-    wait_lds_all();  // reads done before the next pass writes
-  });
-}
-
 // Direct epilogue of a wave's sub-tile (re-quantizing epilogue, or unaligned outputs).
 template <int FN, int FM, int EPI, bool OUTF32>
 __device__ __forceinline__ void epilogue_direct(const GemmParams& p, v16f (&acc)[FN][FM], int n_base,
@@ -303,6 +250,11 @@ struct MxTile {
   static constexpr int WLD = BN * 8 / 256, ALD = BM * ACH / 256;
 };
 
+// Register-staged kernel, K ordering inside a 256-element chunk: MFMA step s (0..3) takes the
+// chunk's 32-element blocks s and 4 + s as its two scale blocks.  The scale of block b comes
+// from the lanes of half b, so a lane of half h needs the E8M0 bytes of blocks 4h + s: the
+// dword [4h, 4h+4) of the row's 8 chunk scales, op_sel s picking the byte.  FP4 lanes of half h
+// hold their block whole; FP8 lanes split theirs (below).  LDS rows of 128 or 256 bytes.
 template <int BM, int BN, bool AFP8, int S>
 __device__ __forceinline__ void mx_step(const uint8_t* sW, const uint8_t* sA, int wn0, int wm0,
                                         const uint32_t (&wsc)[BN / 64],
@@ -340,69 +292,6 @@ __device__ __forceinline__ void mx_step(const uint8_t* sW, const uint8_t* sA, in
       acc[i][j] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(
           wf[i], af[j], acc[i][j], 4, AFP8 ? 0 : 4, S, (int)wsc[i], S, (int)asc[j]);
     });
-  });
-}
-
-// Global -> register staging of one K chunk.  Buffer loads: the descriptor of each operand
-// starts at the tile's first row and ends at the matrix end, so rows past M or N read as zero
-// without clamping, and every load of a thread shares one VGPR offset pattern.
-// Fragments of one MFMA step (see mx_step), split into an LDS load and the MFMAs so that the
-// loads of step s+1 can be in flight while the MFMAs of step s issue.
-template <int BM, int BN, bool AFP8>
-struct MxFrags {
-  typedef typename std::conditional<AFP8, v8i, v4i>::type AV;
-  v4i w[BN / 64];
-  AV a[BM / 64];
-};
-
-// One scaled MFMA: weight fragment (FP4) x activation fragment (FP4 or FP8).
-template <bool AFP8, int S>
-__device__ __forceinline__ v16f mx_mfma(const v4i& w, const typename MxFrags<256, 256, AFP8>::AV& a,
-                                        const v16f& c, uint32_t ws, uint32_t as) {
-  if constexpr (AFP8) return mfma_scale_32x32x64_f4f8(w, a, c, 4, 0, S, (int)ws, S, (int)as);
-  else return mfma_scale_32x32x64_f4f4(w, a, c, 4, 4, S, (int)ws, S, (int)as);
-}
-
-template <int BM, int BN, bool AFP8, int S>
-__device__ __forceinline__ void mx_load(const uint8_t* sW, const uint8_t* sA, int wn0, int wm0,
-                                        MxFrags<BM, BN, AFP8>& f) {
-  using T = MxTile<BM, BN, AFP8>;
-  const int lane = lane_id();
-  const int r32 = lane & 31, h = lane >> 5;
-#pragma unroll
-  for (int i = 0; i < T::FN; ++i) {
-    const int row = wn0 + 32 * i + r32;
-    f.w[i] = *(const v4i*)(sW + swz(row, 4 * h + S, T::WROWB));
-  }
-#pragma unroll
-  for (int j = 0; j < T::FM; ++j) {
-    const int row = wm0 + 32 * j + r32;
-    if constexpr (AFP8) {
-      const v4i d0 = *(const v4i*)(sA + swz(row, 2 * S + h, T::AROWB));
-      const v4i d1 = *(const v4i*)(sA + swz(row, 8 + 2 * S + h, T::AROWB));
-      f.a[j] = v8i{d0[0], d0[1], d0[2], d0[3], d1[0], d1[1], d1[2], d1[3]};
-    } else {
-      f.a[j] = *(const v4i*)(sA + swz(row, 4 * h + S, T::AROWB));
-    }
-  }
-}
-
-// The MFMAs of step S for weight row-block I only (FM instructions).
-template <int BM, int BN, bool AFP8, int S, int I>
-__device__ __forceinline__ void mx_mma_row(const MxFrags<BM, BN, AFP8>& f, const uint32_t (&wsc)[BN / 64],
-                                           const uint32_t (&asc)[BM / 64],
-                                           v16f (&acc)[BN / 64][BM / 64]) {
-  using T = MxTile<BM, BN, AFP8>;
-  static_for<T::FM>([&](auto j) { acc[I][j] = mx_mfma<AFP8, S>(f.w[I], f.a[j], acc[I][j], wsc[I], asc[j]); });
-}
-
-template <int BM, int BN, bool AFP8, int S>
-__device__ __forceinline__ void mx_mma(const MxFrags<BM, BN, AFP8>& f, const uint32_t (&wsc)[BN / 64],
-                                       const uint32_t (&asc)[BM / 64],
-                                       v16f (&acc)[BN / 64][BM / 64]) {
-  using T = MxTile<BM, BN, AFP8>;
-  static_for<T::FN>([&](auto i) {
-    static_for<T::FM>([&](auto j) { acc[i][j] = mx_mfma<AFP8, S>(f.w[i], f.a[j], acc[i][j], wsc[i], asc[j]); });
   });
 }
 
@@ -548,23 +437,58 @@ __global__ void __launch_bounds__(256, 1) gemm_mx_kernel(GemmParams p) {
   });
 }
 
-// Persistent schedule: workgroup b stays on XCD b % 8 and walks that XCD's contiguous range of
-// tiles (see tile_coords) with a stride of the XCD's workgroup count.
-struct XcdSchedule {
-  int start, count, stride, first;
+// ---------------------------------------------------------------------------------------------
+// MX GEMM, ring-staged (K a multiple of 128)
+// ---------------------------------------------------------------------------------------------
+// Two workgroups per compute unit, each with a BM x BN output tile (4 waves, 2 x 2, BM/2 x BN/2
+// each) and a 3-deep LDS ring of 128-element K chunks.  Chunk kc + 2 is fetched by direct-to-LDS
+// buffer loads while chunk kc is multiplied, so two chunks of load latency are hidden; the second
+// workgroup on the CU fills the MFMA pipe while one waits at its barrier or runs its epilogue.
+//
+// K ordering inside a 128-element chunk (four 32-element blocks): MFMA step s (0, 1) takes blocks
+// s and 2 + s as its scale blocks 0 and 1.  An FP4 lane of half h holds block 2h + s whole (16
+// bytes); an FP8 lane of half h holds elements 16h..16h+15 of both blocks.  The E8M0 bytes of a
+// row's chunk are one dword (blocks 0..3); shifted right by 16h, op_sel s picks block 2h + s.
+//
+// LDS rows (64 bytes for FP4 codes, 128 for FP8) hold 16-byte pieces XOR-swizzled by the row so
+// that a quarter wave of 16-byte fragment reads (16 consecutive rows, one piece index) covers
+// all 64 banks: piece ^ ((row >> 2) & 3) for 64-byte rows, piece ^ ((row >> 1) & 7) for 128-byte
+// rows.  A load instruction fills 1 KB of consecutive LDS (16 or 8 rows), lane i slot i, so each
+// lane fetches the global piece that the swizzle puts in its slot.
+template <int BM, int BN, bool AFP8>
+struct RingTile {
+  static_assert((BM == 128 || BM == 256) && BN == 128, "tile sizes");
+  static constexpr int KCR = 128;
+  static constexpr int WROWB = 64, AROWB = AFP8 ? 128 : 64;  // bytes per row and chunk
+  static constexpr int W_BYTES = BN * WROWB, A_BYTES = BM * AROWB;
+  static constexpr int WS_BYTES = BN * 4, AS_BYTES = BM * 4;
+  static constexpr int STAGE = W_BYTES + A_BYTES + WS_BYTES + AS_BYTES;
+  static constexpr int NSTAGE = 3;
+  static constexpr int FN = BN / 64, FM = BM / 64;
+  static constexpr int NW = W_BYTES / 4096, NA = A_BYTES / 4096;  // 1 KB loads per wave
+  static constexpr int TA = BM / 64, TW = BN / 64;                  // 256-byte scale loads
+  static constexpr int NS = (TA + TW + 3) / 4;                      // scale loads per wave
+  static constexpr int NDMA = NW + NA + NS;
+  static_assert(NSTAGE * STAGE <= 80 * 1024, "two workgroups per compute unit");
 };
-__device__ __forceinline__ XcdSchedule xcd_schedule(int total) {
-  const int x = blockIdx.x & 7, slot = blockIdx.x >> 3;
-  const int q = total >> 3, r = total & 7;
-  XcdSchedule s;
-  s.start = x * q + min(x, r);
-  s.count = q + (x < r ? 1 : 0);
-  s.stride = ((int)gridDim.x - x + 7) >> 3;  // workgroups on this XCD
-  s.first = slot;
-  return s;
+
+template <int N>
+__device__ __forceinline__ void wait_vmcnt() {
+  static_assert(N >= 0 && N < 64, "vmcnt range");
+  __builtin_amdgcn_s_waitcnt((N & 15) | (7 << 4) | (15 << 8) | ((N >> 4) << 14));
 }
-__device__ __forceinline__ void band_coords(int t, int tiles_m, int tiles_n, int& tm, int& tn) {
-  constexpr int GM = 4;
+// Workgroup barrier without the release fence of __syncthreads (which would wait for every load
+// in flight, the prefetched chunks included); the memory clobber keeps LDS accesses on their side.
+__device__ __forceinline__ void barrier_only() { asm volatile("s_barrier" ::: "memory"); }
+
+// Tile order for a grid of one tile per workgroup: XCD x = b % 8 gets a contiguous range of tile
+// indices, walked in bands of GM tile rows (m), column by column.
+template <int GM>
+__device__ __forceinline__ void tile_coords_gm(int b, int tiles_m, int tiles_n, int& tm, int& tn) {
+  const int total = tiles_m * tiles_n;
+  const int q = total >> 3, r = total & 7;
+  const int x = b & 7, j = b >> 3;
+  const int t = x * q + min(x, r) + j;
   const int band = t / (GM * tiles_n);
   const int in = t - band * GM * tiles_n;
   const int rows = min(GM, tiles_m - band * GM);
@@ -572,210 +496,210 @@ __device__ __forceinline__ void band_coords(int t, int tiles_m, int tiles_n, int
   tn = in / rows;
 }
 
-// The MX GEMM with chunks staged by direct-to-LDS buffer loads (K a multiple of the chunk).  Each
-// load instruction of a wave writes 64 consecutive 16-byte LDS slots, so a lane fetches the
-// global chunk that belongs in its slot under the row swizzle: no VGPR staging, no LDS store
-// instructions.  One workgroup per CU runs persistently over its tiles; the loads of the next
-// chunk -- the next tile's first chunk at the end of a tile -- fly while the current chunk is
-// multiplied, so a tile's start costs no load latency.
 template <int BM, int BN, bool AFP8, int EPI, bool OUTF32, bool LR>
-__global__ void __launch_bounds__(256, 1) gemm_mx_dma_kernel(GemmParams p) {
-  using T = MxTile<BM, BN, AFP8>;
-  __shared__ __attribute__((aligned(16))) uint8_t smem[2 * T::STAGE];
+__global__ void __launch_bounds__(256, 2) gemm_mx_ring_kernel(GemmParams p) {
+  using T = RingTile<BM, BN, AFP8>;
+  typedef typename std::conditional<AFP8, v8i, v4i>::type AV;
+  __shared__ __attribute__((aligned(16))) uint8_t smem[T::NSTAGE * T::STAGE];
 
-  const int tid = threadIdx.x;
-  const int lane = tid & 63;
-  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int lane = threadIdx.x & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int r32 = lane & 31, h = lane >> 5;
   const int wn0 = (wave >> 1) * (BN / 2), wm0 = (wave & 1) * (BM / 2);
   const int tiles_n = (p.N + BN - 1) / BN, tiles_m = (p.M + BM - 1) / BM;
-  const XcdSchedule sched = xcd_schedule(tiles_m * tiles_n);
-  if (sched.first >= sched.count) return;
-  const int nkc = p.K / KC;
+  int tm, tn;
+  tile_coords_gm<8>(blockIdx.x, tiles_m, tiles_n, tm, tn);
+  const int m0 = tm * BM, n0 = tn * BN;
+  const int nkc = p.K / T::KCR;
   const uint32_t w_row = (uint32_t)p.K >> 1, a_row = AFP8 ? (uint32_t)p.K : ((uint32_t)p.K >> 1);
   const uint32_t s_row = (uint32_t)p.K >> 5;
-  // staged output: 16-byte pieces of whole rows ((BM / 2) rows x 128 bytes per wave fit the free
-  // chunk buffer)
-  constexpr int ESZ = OUTF32 ? 4 : 2;
-  const bool staged_out = EPI != EPI_GELU_QUANT && (p.N % (16 / ESZ)) == 0 &&
-                          (p.ld_out % (16 / ESZ)) == 0 && (((uintptr_t)p.out) & 15) == 0;
-  static_assert(4 * (BM / 2) * 128 <= T::STAGE, "staging area fits a chunk buffer");
 
-  // buffer descriptors of one tile: they start at the tile's first row and end at the matrix
-  // end, so rows past M or N read as zero; an absent tile gets empty descriptors
-  struct TileDesc {
-    v4i w, a, ws, as;
-    int m0, n0;
-  };
+  // Operand addressing.  Every load is descriptor + per-lane VGPR offset (range-checked) + chunk
+  // offset kc * step in the scalar offset.
+  //  Row-major operands: the descriptor starts at the tile's first row and ends at the matrix
+  //  end, so rows past M or N read as zero; the VGPR offset holds row * row_bytes + piece.
+  //  Tiled operands: the tile's rows are all present (rows are padded to 256); each 1 KB (256 B)
+  //  load is one contiguous tile of the layout, the VGPR offset is tile row * chunk count * 1 KB
+  //  (256 B) + lane * 16 (4).
   auto clamp32 = [](uint64_t v) -> uint32_t { return v > 0xFFFFFFFFull ? 0xFFFFFFFFu : (uint32_t)v; };
-  auto describe = [&](int j, bool present) {
-    int tm, tn;
-    band_coords(sched.start + j, tiles_m, tiles_n, tm, tn);
-    TileDesc d;
-    d.m0 = tm * BM;
-    d.n0 = tn * BN;
-    const uint64_t wn = present ? (uint64_t)(p.N - d.n0) : 0, am = present ? (uint64_t)(p.M - d.m0) : 0;
-    d.w = make_rsrc_sgpr(p.w_codes + (int64_t)d.n0 * w_row, clamp32(wn * w_row));
-    d.a = make_rsrc_sgpr(p.a_codes + (int64_t)d.m0 * a_row, clamp32(am * a_row));
-    d.ws = make_rsrc_sgpr(p.w_scales + (int64_t)d.n0 * s_row, clamp32(wn * s_row));
-    d.as = make_rsrc_sgpr(p.a_scales + (int64_t)d.m0 * s_row, clamp32(am * s_row));
-    return d;
-  };
+  const uint64_t wn = (uint64_t)(p.N - n0), am = (uint64_t)(p.M - m0);
+  const bool wt = p.w_tiled != 0, at = p.a_tiled != 0;
+  constexpr int A_TROWS = AFP8 ? 8 : 16;  // rows per 1 KB code tile
+  const uint64_t kb1k = (uint64_t)nkc * 1024u, kb256 = (uint64_t)nkc * 256u;
+  const v4i rw = wt ? make_rsrc_sgpr(p.w_codes + (int64_t)(n0 / 16) * kb1k, clamp32((uint64_t)(BN / 16) * kb1k))
+                    : make_rsrc_sgpr(p.w_codes + (int64_t)n0 * w_row, clamp32(wn * w_row));
+  const v4i ra = at ? make_rsrc_sgpr(p.a_codes + (int64_t)(m0 / A_TROWS) * kb1k, clamp32((uint64_t)(BM / A_TROWS) * kb1k))
+                    : make_rsrc_sgpr(p.a_codes + (int64_t)m0 * a_row, clamp32(am * a_row));
+  const v4i rws = wt ? make_rsrc_sgpr(p.w_scales + (int64_t)(n0 / 64) * kb256, clamp32((uint64_t)(BN / 64) * kb256))
+                     : make_rsrc_sgpr(p.w_scales + (int64_t)n0 * s_row, clamp32(wn * s_row));
+  const v4i ras = at ? make_rsrc_sgpr(p.a_scales + (int64_t)(m0 / 64) * kb256, clamp32((uint64_t)(BM / 64) * kb256))
+                     : make_rsrc_sgpr(p.a_scales + (int64_t)m0 * s_row, clamp32(am * s_row));
+  const uint32_t w_step = wt ? 1024u : 64u, a_step = at ? 1024u : (uint32_t)T::AROWB;
+  const uint32_t ws_step = wt ? 256u : 4u, as_step = at ? 256u : 4u;
 
-  // Load instructions per wave and chunk: W codes BN/32 (1 KB each), A codes BM*ACH/256,
-  // W / A scales BN/128, BM/128 (4-byte loads, 256 B each).  Lane offsets are recomputed at
-  // each load (a few integer ops) rather than held in registers across the tile.
-  constexpr int NW = BN / 32, NA = BM * T::ACH / 256, NWS = BN / 128, NAS = BM / 128;
-  constexpr int A_RPI = 64 / T::ACH;  // A rows per load instruction
-  auto off_w = [&](int i) {
-    const int row = (wave * NW + i) * 8 + (lane >> 3);
-    const int c = (lane & 7) ^ ((row ^ (row >> 3)) & 7);
-    return (uint32_t)row * w_row + (uint32_t)c * 16u;
+  // lane offsets of the row-major code loads: 64-byte rows, 16 per load; 128-byte rows, 8 per load
+  const uint32_t pc64 = (uint32_t)((lane & 3) ^ ((lane >> 4) & 3)) * 16u;
+  const uint32_t lt16 = (uint32_t)lane * 16u;
+  auto off_w = [&](int q) {
+    const int tr = wave * T::NW + q;  // 16-row group of the tile
+    return wt ? (uint32_t)tr * (uint32_t)kb1k + lt16 : (uint32_t)(16 * tr + (lane >> 2)) * w_row + pc64;
   };
-  auto off_a = [&](int i) {
-    const int row = (wave * NA + i) * A_RPI + lane / T::ACH;
-    const int c = (lane % T::ACH) ^ (T::ACH == 8 ? ((row ^ (row >> 3)) & 7) : (row & 15));
-    return (uint32_t)row * a_row + (uint32_t)c * 16u;
-  };
-  auto off_s = [&](int base_row) { return (uint32_t)(base_row + (lane >> 1)) * s_row + (uint32_t)(lane & 1) * 4u; };
-
-  const uint32_t lds0 = lds_addr_of(smem);
-  // Load instruction q of a chunk (0 <= q < NDMA), in the order W codes, A codes, W scales,
-  // A scales; issued in small groups between the MFMAs so that the vector-memory queue never
-  // backs up into the MFMA issue.
-  constexpr int NDMA = NW + NA + NWS + NAS;
-  auto dma_one = [&](auto qc, const TileDesc& d, int kc, int buf) {
-    constexpr int q = decltype(qc)::value;
-    const uint32_t sW = lds0 + (uint32_t)(buf * T::STAGE);
-    const uint32_t sA = sW + T::W_BYTES, sWS = sA + T::A_BYTES, sAS = sWS + T::WS_BYTES;
-    if constexpr (q < NW) {
-      dma_lds16(d.w, sW + (uint32_t)((wave * NW + q) * 1024), off_w(q), (uint32_t)kc * 128u);
-    } else if constexpr (q < NW + NA) {
-      constexpr int i = q - NW;
-      dma_lds16(d.a, sA + (uint32_t)((wave * NA + i) * 1024), off_a(i), (uint32_t)(kc * T::AROWB));
-    } else if constexpr (q < NW + NA + NWS) {
-      constexpr int i = q - NW - NA;
-      dma_lds4(d.ws, sWS + (uint32_t)((wave * NWS + i) * 256), off_s((wave * NWS + i) * 32), (uint32_t)kc * 8u);
+  auto off_a = [&](int q) {
+    const int tr = wave * T::NA + q;  // A_TROWS-row group of the tile
+    if (at) return (uint32_t)tr * (uint32_t)kb1k + lt16;
+    if constexpr (AFP8) {
+      const int row = 8 * tr + (lane >> 3);
+      return (uint32_t)row * a_row + (uint32_t)((lane & 7) ^ ((row >> 1) & 7)) * 16u;
     } else {
-      constexpr int i = q - NW - NA - NWS;
-      dma_lds4(d.as, sAS + (uint32_t)((wave * NAS + i) * 256), off_s((wave * NAS + i) * 32), (uint32_t)kc * 8u);
+      return (uint32_t)(16 * tr + (lane >> 2)) * a_row + pc64;
     }
   };
-  auto dma = [&](const TileDesc& d, int kc, int buf) {
-    static_for<NDMA>([&](auto q) { dma_one(q, d, kc, buf); });
+  // scale load k of this wave: 64 rows of A scales (u < TA) or of W scales; surplus slots repeat
+  // the last W load (the same bytes to the same place)
+  auto scale_slot = [&](int k, int& urow, bool& is_a) {
+    const int u = wave + 4 * k;
+    is_a = u < T::TA;
+    urow = is_a ? u : min(u - T::TA, T::TW - 1);
   };
-  // instructions [LO, HI) of the chunk
-  auto dma_range = [&](auto lo, auto hi, const TileDesc& d, int kc, int buf) {
-    static_for<decltype(hi)::value - decltype(lo)::value>([&](auto q) {
-      dma_one(std::integral_constant<int, decltype(lo)::value + decltype(q)::value>{}, d, kc, buf);
+  auto off_s = [&](int urow, bool tiled) {
+    return tiled ? (uint32_t)urow * (uint32_t)kb256 + (uint32_t)lane * 4u : (uint32_t)(64 * urow + lane) * s_row;
+  };
+
+  const uint32_t lds0 = lds_addr_of(smem);
+  auto issue = [&](int kc, int st) {
+    const bool live = kc < nkc;  // past the last chunk: empty descriptors, no memory traffic
+    v4i dw = rw, da = ra, dws = rws, das = ras;
+    dw[2] = live ? dw[2] : 0;
+    da[2] = live ? da[2] : 0;
+    dws[2] = live ? dws[2] : 0;
+    das[2] = live ? das[2] : 0;
+    const uint32_t sW = lds0 + (uint32_t)(st * T::STAGE);
+    const uint32_t sA = sW + T::W_BYTES, sWS = sA + T::A_BYTES, sAS = sWS + T::WS_BYTES;
+    static_for<T::NW>([&](auto q) {
+      dma_lds16(dw, sW + (uint32_t)((wave * T::NW + q) * 1024), off_w(q), (uint32_t)kc * w_step);
+    });
+    static_for<T::NA>([&](auto q) {
+      dma_lds16(da, sA + (uint32_t)((wave * T::NA + q) * 1024), off_a(q), (uint32_t)kc * a_step);
+    });
+    static_for<T::NS>([&](auto k) {
+      int urow;
+      bool is_a;
+      scale_slot(k, urow, is_a);
+      dma_lds4(is_a ? das : dws, (is_a ? sAS : sWS) + (uint32_t)(urow * 256), off_s(urow, is_a ? at : wt),
+               (uint32_t)kc * (is_a ? as_step : ws_step));
     });
   };
 
-  const int r32 = lane & 31, h = lane >> 5;
-  auto load_scales = [&](int buf, uint32_t (&wsc)[T::FN], uint32_t (&asc)[T::FM]) {
-    const uint8_t* sWS = smem + buf * T::STAGE + T::W_BYTES + T::A_BYTES;
-    const uint8_t* sAS = sWS + T::WS_BYTES;
-#pragma unroll
-    for (int i = 0; i < T::FN; ++i) wsc[i] = *(const uint32_t*)(sWS + (wn0 + 32 * i + r32) * 8 + 4 * h);
-#pragma unroll
-    for (int j = 0; j < T::FM; ++j) asc[j] = *(const uint32_t*)(sAS + (wm0 + 32 * j + r32) * 8 + 4 * h);
-  };
-  auto sw_of = [&](int buf) { return (const uint8_t*)smem + buf * T::STAGE; };
-  auto sa_of = [&](int buf) { return (const uint8_t*)smem + buf * T::STAGE + T::W_BYTES; };
-
-  // Software pipeline: the LDS loads of MFMA step s+1 are issued before the MFMAs of step s, and
-  // the barrier that publishes chunk kc+1 sits between the loads and the MFMAs of step 3 of
-  // chunk kc, so the barrier and the first loads of kc+1 overlap those MFMAs.  The chunk loop
-  // body is one basic block, so nothing moves across its scheduling barriers: each tile's first
-  // pass multiplies zero fragments for the (absent) step 3 of chunk -1.
   v16f acc[T::FN][T::FM];
-  MxFrags<BM, BN, AFP8> f0, f1;
-  uint32_t wsc[T::FN], asc[T::FM], wsc3[T::FN], asc3[T::FM];
+  static_for<T::FN>([&](auto i) { static_for<T::FM>([&](auto j) { acc[i][j] = v16f{}; }); });
 
-  int j = sched.first;
-  TileDesc cur = describe(j, true);
-  int gc = 0;  // chunks staged so far (LDS buffer parity)
-  dma(cur, 0, 0);
-  wait_vmem_all();
-  __syncthreads();
-  load_scales(0, wsc, asc);
-  mx_load<BM, BN, AFP8, 0>(sw_of(0), sa_of(0), wn0, wm0, f0);
-  while (true) {
-    const int jn = j + sched.stride;
-    const bool has_next = jn < sched.count;
-    const TileDesc nxt = describe(has_next ? jn : j, has_next);
-    static_for<T::FN>([&](auto i) { static_for<T::FM>([&](auto jj) { acc[i][jj] = v16f{}; }); });
+  // fragment addresses inside a stage (step 0; step 1 is piece ^ 1)
+  const int wrow = wn0 + r32, arow = wm0 + r32;  // + 32 i: the XOR term is unchanged
+  const uint32_t shift = 16u * (uint32_t)h;
+
+  issue(0, 0);
+  issue(1, 1);
+  int st = 0;
+  for (int kc = 0; kc < nkc; ++kc) {
+    wait_vmcnt<T::NDMA>();  // this wave's loads of chunk kc landed (chunk kc + 1 may be in flight)
+    wait_lds_all();
+    barrier_only();         // every wave's loads of chunk kc landed; stage kc - 1 is free
+    const int st2 = st == 0 ? 2 : st - 1;
+    const uint8_t* sW = smem + st * T::STAGE;
+    const uint8_t* sA = sW + T::W_BYTES;
+    const uint8_t* sWS = sA + T::A_BYTES;
+    const uint8_t* sAS = sWS + T::WS_BYTES;
+    uint32_t wsc[T::FN], asc[T::FM];
+    v4i wf[2][T::FN];
+    AV af[2][T::FM];
 #pragma unroll
-    for (int i = 0; i < T::FN; ++i) { f1.w[i] = v4i{}; wsc3[i] = 0; }
+    for (int i = 0; i < T::FN; ++i) wsc[i] = *(const uint32_t*)(sWS + (wrow + 32 * i) * 4) >> shift;
 #pragma unroll
-    for (int jj = 0; jj < T::FM; ++jj) { f1.a[jj] = typename MxFrags<BM, BN, AFP8>::AV{}; asc3[jj] = 0; }
-    // nothing of the compiler's own may be in flight inside the chunk loop: a wait it would
-    // insert there for, say, a register reload would also wait for the chunk loads
-    wait_vmem_all();
-    for (int kc = 0; kc < nkc; ++kc, ++gc) {
-      const int buf = gc & 1;
-      // the next chunk: this tile's kc + 1, or the next tile's chunk 0 (empty descriptors past
-      // the last tile).  Its buffer held chunk gc - 1, which every wave finished reading before
-      // the last barrier.
-      const bool last = kc + 1 == nkc;
-      const TileDesc& dd = last ? nxt : cur;
-      const int dkc = last ? 0 : kc + 1;
-      // The loads of the next chunk are spread over the first three MFMA steps of this pass
-      // (one group after each weight row-block), the fourth step covers their latency.
-      constexpr int NPART = 3 * T::FN;
-      auto mma_dma = [&](auto sc, auto part0, const MxFrags<BM, BN, AFP8>& f, const uint32_t (&ws_)[T::FN],
-                         const uint32_t (&as_)[T::FM]) {
-        static_for<T::FN>([&](auto i) {
-          mx_mma_row<BM, BN, AFP8, decltype(sc)::value, decltype(i)::value>(f, ws_, as_, acc);
-          __builtin_amdgcn_sched_barrier(0);
-          constexpr int P = decltype(part0)::value + decltype(i)::value;
-          dma_range(std::integral_constant<int, P * NDMA / NPART>{},
-                    std::integral_constant<int, (P + 1) * NDMA / NPART>{}, dd, dkc, buf ^ 1);
-          __builtin_amdgcn_sched_barrier(0);
-        });
-      };
-      mma_dma(std::integral_constant<int, 3>{}, std::integral_constant<int, 0>{}, f1, wsc3, asc3);
-      mx_load<BM, BN, AFP8, 1>(sw_of(buf), sa_of(buf), wn0, wm0, f1);
-      __builtin_amdgcn_sched_barrier(0);
-      mma_dma(std::integral_constant<int, 0>{}, std::integral_constant<int, T::FN>{}, f0, wsc, asc);
-      mx_load<BM, BN, AFP8, 2>(sw_of(buf), sa_of(buf), wn0, wm0, f0);
-      __builtin_amdgcn_sched_barrier(0);
-      mma_dma(std::integral_constant<int, 1>{}, std::integral_constant<int, 2 * T::FN>{}, f1, wsc, asc);
-      mx_load<BM, BN, AFP8, 3>(sw_of(buf), sa_of(buf), wn0, wm0, f1);
-      __builtin_amdgcn_sched_barrier(0);
-      mx_mma<BM, BN, AFP8, 2>(f0, wsc, asc, acc);
-      __builtin_amdgcn_sched_barrier(0);
+    for (int j = 0; j < T::FM; ++j) asc[j] = *(const uint32_t*)(sAS + (arow + 32 * j) * 4) >> shift;
 #pragma unroll
-      for (int i = 0; i < T::FN; ++i) wsc3[i] = wsc[i];
+    for (int s = 0; s < 2; ++s) {
 #pragma unroll
-      for (int jj = 0; jj < T::FM; ++jj) asc3[jj] = asc[jj];
-      wait_lds_all();  // step-3 fragments are in registers
-      wait_vmem_all();  // this wave's part of the next chunk landed
-      __syncthreads();
-      load_scales(buf ^ 1, wsc, asc);
-      mx_load<BM, BN, AFP8, 0>(sw_of(buf ^ 1), sa_of(buf ^ 1), wn0, wm0, f0);
-      __builtin_amdgcn_sched_barrier(0);
+      for (int i = 0; i < T::FN; ++i) {
+        const int row = wrow + 32 * i;
+        wf[s][i] = *(const v4i*)(sW + row * 64 + (((2 * h + s) ^ ((row >> 2) & 3)) << 4));
+      }
+#pragma unroll
+      for (int j = 0; j < T::FM; ++j) {
+        const int row = arow + 32 * j;
+        if constexpr (AFP8) {
+          const int g = (row >> 1) & 7;
+          const v4i d0 = *(const v4i*)(sA + row * 128 + (((2 * s + h) ^ g) << 4));
+          const v4i d1 = *(const v4i*)(sA + row * 128 + (((4 + 2 * s + h) ^ g) << 4));
+          af[s][j] = v8i{d0[0], d0[1], d0[2], d0[3], d1[0], d1[1], d1[2], d1[3]};
+        } else {
+          af[s][j] = *(const v4i*)(sA + row * 64 + (((2 * h + s) ^ ((row >> 2) & 3)) << 4));
+        }
+      }
     }
-    mx_mma<BM, BN, AFP8, 3>(f1, wsc3, asc3, acc);
-
-    if (LR) {
+    __builtin_amdgcn_sched_barrier(0);
+    issue(kc + 2, st2);
+    __builtin_amdgcn_sched_barrier(0);
+    static_for<2>([&](auto sc) {
+      constexpr int S = decltype(sc)::value;
       static_for<T::FN>([&](auto i) {
-        static_for<T::FM>([&](auto jj) {
-          acc[i][jj] = lowrank_block(p, acc[i][jj], cur.n0 + wn0 + 32 * i, cur.m0 + wm0 + 32 * jj);
+        static_for<T::FM>([&](auto j) {
+          if constexpr (AFP8)
+            acc[i][j] = mfma_scale_32x32x64_f4f8(wf[S][i], af[S][j], acc[i][j], 4, 0, S, (int)wsc[i], S, (int)asc[j]);
+          else
+            acc[i][j] = mfma_scale_32x32x64_f4f4(wf[S][i], af[S][j], acc[i][j], 4, 4, S, (int)wsc[i], S, (int)asc[j]);
         });
       });
-    }
-    if (staged_out) {
-      // the buffer of the tile's last chunk is free: every wave read its step-3 fragments before
-      // the last barrier, and the next tile's first load into it waits for the barrier below
-      uint8_t* stage = smem + ((gc - 1) & 1) * T::STAGE + wave * (BM / 2) * 128;
-      epilogue_staged<T::FN, T::FM, EPI, OUTF32>(p, acc, cur.n0 + wn0, cur.m0 + wm0, stage);
-      __syncthreads();
-    } else {
-      epilogue_direct<T::FN, T::FM, EPI, OUTF32>(p, acc, cur.n0 + wn0, cur.m0 + wm0);
-    }
-    if (!has_next) break;
-    j = jn;
-    cur = nxt;
+    });
+    __builtin_amdgcn_sched_barrier(0);
+    st = st == 2 ? 0 : st + 1;
+  }
+
+  if (LR) {
+    static_for<T::FN>([&](auto i) {
+      static_for<T::FM>([&](auto j) {
+        acc[i][j] = lowrank_block(p, acc[i][j], n0 + wn0 + 32 * i, m0 + wm0 + 32 * j);
+      });
+    });
+  }
+  // BF16 output through LDS: the tile is written to the (now idle) ring as BM rows of 256 bytes
+  // (16-byte chunks XOR-swizzled by the row), then stored as whole 256-byte row segments, four
+  // rows per instruction, instead of 8-byte pieces of 32 rows.
+  const bool staged = EPI != EPI_GELU_QUANT && !OUTF32 && (p.N % 8) == 0 && (p.ld_out % 8) == 0 &&
+                      (((uintptr_t)p.out) & 15) == 0;
+  if (!staged) {
+    epilogue_direct<T::FN, T::FM, EPI, OUTF32>(p, acc, n0 + wn0, m0 + wm0);
+    return;
+  }
+  static_assert(BM * BN * 2 <= T::NSTAGE * T::STAGE, "output tile fits the ring");
+  wait_vmem_all();  // the (empty) loads issued for the chunks past the end have landed
+  barrier_only();   // every wave is done with the ring
+  static_for<T::FN>([&](auto i) {
+    float b[16];
+    load_bias16(p, n0 + wn0 + 32 * i, b);
+    static_for<T::FM>([&](auto j) {
+      __builtin_amdgcn_sched_barrier(0);
+      float v[16];
+      finish16<EPI>(p, acc[i][j], b, v);
+      const int row = wm0 + 32 * j + r32;
+#pragma unroll
+      for (int g = 0; g < 4; ++g) {
+        const int c = (wn0 + 32 * i) / 8 + g;  // 16-byte chunk of the row (8 BF16)
+        const uint32_t lo = f32_to_bf16_rne(v[4 * g]) | (f32_to_bf16_rne(v[4 * g + 1]) << 16);
+        const uint32_t hi = f32_to_bf16_rne(v[4 * g + 2]) | (f32_to_bf16_rne(v[4 * g + 3]) << 16);
+        *(uint2*)(smem + row * 256 + ((c ^ (row & 15)) << 4) + 8 * h) = make_uint2(lo, hi);
+      }
+    });
+  });
+  wait_lds_all();
+  barrier_only();
+  const int c = lane & 15;
+  const int n = n0 + 8 * c;
+#pragma unroll 4
+  for (int it = 0; it < BM / 16; ++it) {
+    const int row = wave * (BM / 4) + 4 * it + (lane >> 4);
+    const uint4 d = *(const uint4*)(smem + row * 256 + ((c ^ (row & 15)) << 4));
+    const int m = m0 + row;
+    if (m < p.M && n < p.N) *(uint4*)((uint16_t*)p.out + (int64_t)m * p.ld_out + n) = d;
   }
 }
 
@@ -958,59 +882,36 @@ __global__ void __launch_bounds__(64) lowrank_down_kernel(const uint16_t* __rest
 // ---------------------------------------------------------------------------------------------
 // launchers
 // ---------------------------------------------------------------------------------------------
-// Workgroups of the persistent GEMM launch: one per compute unit of the current device.
-static int persistent_grid() {
-  static int cus[64] = {};
-  int dev = 0;
-  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 256;
-  if (cus[dev] == 0) {
-    int n = 0;
-    if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || n <= 0) n = 256;
-    cus[dev] = n;
-  }
-  return cus[dev];
-}
-
 template <int BM, int BN, bool AFP8, int EPI, bool OUTF32, bool LR>
-static void run_mx_dma(const GemmParams& p, int grid, hipStream_t s) {
-  gemm_mx_dma_kernel<BM, BN, AFP8, EPI, OUTF32, LR><<<grid, 256, 0, s>>>(p);
+static void run_ring(const GemmParams& p, int grid, hipStream_t s) {
+  gemm_mx_ring_kernel<BM, BN, AFP8, EPI, OUTF32, LR><<<grid, 256, 0, s>>>(p);
 }
 
-// The specialised instantiations: every epilogue for W4A4, the plain one (with and without the
-// low-rank branch) for W4A8 and for W4A4 SVDQuant.  Other combinations take the generic kernel.
-template <int BM, int BN, bool AFP8>
-static bool run_mx_dma_epi(const GemmParams& p, int grid, hipStream_t s) {
-  const bool lr = p.R > 0;
-  if (p.epi == EPI_BIAS) {
-    if (lr) {
-      if (p.out_f32) run_mx_dma<BM, BN, AFP8, EPI_BIAS, true, true>(p, grid, s);
-      else run_mx_dma<BM, BN, AFP8, EPI_BIAS, false, true>(p, grid, s);
-    } else {
-      if (p.out_f32) run_mx_dma<BM, BN, AFP8, EPI_BIAS, true, false>(p, grid, s);
-      else run_mx_dma<BM, BN, AFP8, EPI_BIAS, false, false>(p, grid, s);
-    }
-    return true;
-  }
-  if constexpr (!AFP8) {
-    if (lr) return false;
-    if (p.epi == EPI_GELU_QUANT) run_mx_dma<BM, BN, AFP8, EPI_GELU_QUANT, false, false>(p, grid, s);
-    else if (p.out_f32) run_mx_dma<BM, BN, AFP8, EPI_GELU, true, false>(p, grid, s);
-    else run_mx_dma<BM, BN, AFP8, EPI_GELU, false, false>(p, grid, s);
-    return true;
-  }
-  return false;
+// Every (epilogue, output type, low-rank) combination of the ring kernel.
+template <int BM, int BN, bool AFP8, int EPI, bool LR>
+static void run_ring_o(const GemmParams& p, int grid, hipStream_t s) {
+  if (EPI != EPI_GELU_QUANT && p.out_f32) run_ring<BM, BN, AFP8, EPI, true, LR>(p, grid, s);
+  else run_ring<BM, BN, AFP8, EPI, false, LR>(p, grid, s);
+}
+template <int BM, int BN, bool AFP8, bool LR>
+static void run_ring_e(const GemmParams& p, int grid, hipStream_t s) {
+  if (p.epi == EPI_GELU_QUANT) run_ring_o<BM, BN, AFP8, EPI_GELU_QUANT, LR>(p, grid, s);
+  else if (p.epi == EPI_GELU) run_ring_o<BM, BN, AFP8, EPI_GELU, LR>(p, grid, s);
+  else run_ring_o<BM, BN, AFP8, EPI_BIAS, LR>(p, grid, s);
 }
 
+// K % 128 == 0: the ring kernel (row-major or tiled operands); otherwise the register-staged
+// kernel, which reads row-major operands (the tiled layout implies K % 128 == 0).
 template <int BM, int BN, bool AFP8>
 static hipError_t run_mx(const GemmParams& p, hipStream_t s) {
-  const int tiles = ((p.M + BM - 1) / BM) * ((p.N + BN - 1) / BN);
-  bool done = false;
-  if (p.K % KC == 0) {
-    const int cap = persistent_grid();
-    const int grid = tiles < cap ? tiles : cap;
-    done = run_mx_dma_epi<BM, BN, AFP8>(p, grid, s);
+  if (p.K % 128 == 0) {
+    const int tiles = ((p.M + BM - 1) / BM) * ((p.N + 127) / 128);
+    if (p.R > 0) run_ring_e<BM, 128, AFP8, true>(p, tiles, s);
+    else run_ring_e<BM, 128, AFP8, false>(p, tiles, s);
+  } else {
+    const int tiles = ((p.M + BM - 1) / BM) * ((p.N + BN - 1) / BN);
+    gemm_mx_kernel<BM, BN, AFP8, false><<<tiles, 256, 0, s>>>(p);
   }
-  if (!done) gemm_mx_kernel<BM, BN, AFP8, false><<<tiles, 256, 0, s>>>(p);
   return hipGetLastError();
 }
 

@@ -9,6 +9,14 @@ namespace mxk {
 // Quantizers / dequantizer / absmax (mx_quant.hip)
 hipError_t launch_quant_mx(const uint16_t* x, int64_t rows, int64_t cols, int64_t ld, int elem,
                            uint8_t* codes, uint8_t* scales, hipStream_t s);
+// MX quantization into the tiled GEMM layout (cols % 128 == 0); rows up to the padded count are
+// written, the padding with zeros.
+hipError_t launch_quant_mx_tiled(const uint16_t* x, int64_t rows, int64_t cols, int64_t ld, int elem,
+                                 uint8_t* codes, uint8_t* scales, hipStream_t s);
+// Row-major <-> tiled copy of MX codes and scales (to_tiled: direction).
+hipError_t launch_relayout(const uint8_t* src_codes, const uint8_t* src_scales, uint8_t* dst_codes,
+                           uint8_t* dst_scales, int64_t rows, int64_t cols, int elem, bool to_tiled,
+                           hipStream_t s);
 hipError_t launch_quant_nv(const uint16_t* x, int64_t rows, int64_t cols, int64_t ld, float sg,
                            uint8_t* codes, uint8_t* scales, hipStream_t s);
 hipError_t launch_dequant(const uint8_t* codes, const uint8_t* scales, int64_t rows, int64_t cols,
@@ -34,6 +42,7 @@ struct GemmParams {
   int M, N, K, R;
   int epi;
   int out_f32;
+  int a_tiled, w_tiled;     // operand layouts: 0 row-major, 1 tiled (MX formats)
 };
 
 // act_fp8: activation codes are E4M3 (W4A8); otherwise E2M1.

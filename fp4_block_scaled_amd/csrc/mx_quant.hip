@@ -21,7 +21,48 @@ namespace mxk {
 // ---------------------------------------------------------------------------------------------
 // MXFP4 / MXFP8
 // ---------------------------------------------------------------------------------------------
+// One thread's 8 elements of a 32-element group (the group's four threads are one DPP quad):
+// the group's scale byte and the thread's codes, 4 bytes (E2M1, lo) or 8 bytes (E4M3, lo, hi).
 template <int ELEM>  // 0: E2M1 (emax 2), 1: E4M3 (emax 8)
+__device__ __forceinline__ void quant_mx8(const uint4 v, uint32_t& lo, uint32_t& hi, uint32_t& sbyte) {
+  uint32_t w[4] = {v.x, v.y, v.z, v.w};
+  uint32_t amax = 0;
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    uint32_t l = w[i] & 0x7FFFu, h = (w[i] >> 16) & 0x7FFFu;
+    amax = max(amax, max(l, h));
+  }
+  amax = max(amax, quad_xor1(amax));
+  amax = max(amax, quad_xor2(amax));
+  const bool bad = amax >= 0x7F80u;  // NaN or Inf in the group
+  const int E = (int)(amax >> 7);    // BF16 exponent field of amax
+  const int emax = ELEM == 0 ? 2 : 8;
+  int e = E - 127 - emax;            // floor(log2 amax) - emax (subnormal/zero: clamped below)
+  if (e < -127) e = -127;
+  const float inv = __uint_as_float((uint32_t)(127 - e) << 23);  // 2^-e, a normal binary32
+  lo = hi = 0;
+  if (ELEM == 0) {
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+      uint32_t b = (w[i >> 1] >> ((i & 1) * 16)) & 0xFFFFu;
+      float q = bf16_to_f32(b & 0x7FFFu) * inv;
+      lo |= (e2m1_code(q) | ((b >> 12) & 8u)) << (4 * i);
+    }
+  } else {
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+      uint32_t b = (w[i >> 1] >> ((i & 1) * 16)) & 0xFFFFu;
+      float q = bf16_to_f32(b & 0x7FFFu) * inv;
+      uint32_t c = e4m3_code(q) | ((b >> 8) & 0x80u);
+      if (i < 4) lo |= c << (8 * i);
+      else hi |= c << (8 * (i - 4));
+    }
+  }
+  if (bad) lo = hi = 0;
+  sbyte = bad ? 0xFFu : (uint32_t)(e + 127);
+}
+
+template <int ELEM>
 __global__ void __launch_bounds__(256) quant_mx_kernel(const uint16_t* __restrict__ x,
                                                         int64_t rows, int64_t cols, int64_t ld,
                                                         uint8_t* __restrict__ codes,
@@ -34,47 +75,71 @@ __global__ void __launch_bounds__(256) quant_mx_kernel(const uint16_t* __restric
     const int part = (int)(t & 3);
     const int64_t r = g / gpr;
     const int64_t gc = g - r * gpr;
-    const uint4 v = load_stream16(x + r * ld + gc * 32 + part * 8);
-    uint32_t w[4] = {v.x, v.y, v.z, v.w};
-    uint32_t amax = 0;
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      uint32_t lo = w[i] & 0x7FFFu, hi = (w[i] >> 16) & 0x7FFFu;
-      amax = max(amax, max(lo, hi));
-    }
-    amax = max(amax, quad_xor1(amax));
-    amax = max(amax, quad_xor2(amax));
-    const bool bad = amax >= 0x7F80u;  // NaN or Inf in the group
-    const int E = (int)(amax >> 7);    // BF16 exponent field of amax
-    const int emax = ELEM == 0 ? 2 : 8;
-    int e = E - 127 - emax;            // floor(log2 amax) - emax (subnormal/zero: clamped below)
-    if (e < -127) e = -127;
-    const float inv = __uint_as_float((uint32_t)(127 - e) << 23);  // 2^-e, a normal binary32
+    uint32_t lo, hi, sbyte;
+    quant_mx8<ELEM>(load_stream16(x + r * ld + gc * 32 + part * 8), lo, hi, sbyte);
+    if (ELEM == 0) *(uint32_t*)(codes + r * (cols >> 1) + gc * 16 + part * 4) = lo;
+    else *(uint2*)(codes + r * cols + gc * 32 + part * 8) = make_uint2(lo, hi);
+    if (part == 0) scales[r * gpr + gc] = (uint8_t)sbyte;
+  }
+}
+
+// Tiled output: a workgroup quantizes 16 rows x 128 columns per step (16 threads per row, 8
+// elements each), which is one 1 KB FP4 code tile (two FP8 tiles) and a quarter of a scale tile.
+// Rows from `rows` to the padded count quantize zeros (zero codes, scale byte 0).
+template <int ELEM>
+__global__ void __launch_bounds__(256) quant_mx_tiled_kernel(const uint16_t* __restrict__ x,
+                                                              int64_t rows, int64_t cols, int64_t ld,
+                                                              uint8_t* __restrict__ codes,
+                                                              uint8_t* __restrict__ scales) {
+  const int64_t nkc = cols >> 7;
+  const int64_t items = (tiled_rows(rows) >> 4) * nkc;
+  const int rl = threadIdx.x >> 4, c8 = threadIdx.x & 15;
+  const int g4 = c8 >> 2, part = c8 & 3;
+  for (int64_t it = blockIdx.x; it < items; it += gridDim.x) {
+    const int64_t rb = it / nkc, kb = it - rb * nkc;
+    const int64_t r = rb * 16 + rl;
+    const uint4 v = r < rows ? load_stream16(x + r * ld + kb * 128 + c8 * 8) : make_uint4(0, 0, 0, 0);
+    uint32_t lo, hi, sbyte;
+    quant_mx8<ELEM>(v, lo, hi, sbyte);
     if (ELEM == 0) {
-      uint32_t packed = 0;
-#pragma unroll
-      for (int i = 0; i < 8; ++i) {
-        uint32_t b = (w[i >> 1] >> ((i & 1) * 16)) & 0xFFFFu;
-        float q = bf16_to_f32(b & 0x7FFFu) * inv;
-        uint32_t c = e2m1_code(q) | ((b >> 12) & 8u);
-        packed |= c << (4 * i);
-      }
-      if (bad) packed = 0;
-      *(uint32_t*)(codes + r * (cols >> 1) + gc * 16 + part * 4) = packed;
+      *(uint32_t*)(codes + tiled_fp4_off(r, kb, g4, nkc) + part * 4) = lo;
     } else {
-      uint32_t p0 = 0, p1 = 0;
-#pragma unroll
-      for (int i = 0; i < 8; ++i) {
-        uint32_t b = (w[i >> 1] >> ((i & 1) * 16)) & 0xFFFFu;
-        float q = bf16_to_f32(b & 0x7FFFu) * inv;
-        uint32_t c = e4m3_code(q) | ((b >> 8) & 0x80u);
-        if (i < 4) p0 |= c << (8 * i);
-        else p1 |= c << (8 * (i - 4));
-      }
-      if (bad) p0 = p1 = 0;
-      *(uint2*)(codes + r * cols + gc * 32 + part * 8) = make_uint2(p0, p1);
+      // the group's 32 bytes are pieces 2 g4 and 2 g4 + 1; this thread's 8 bytes are half a piece
+      *(uint2*)(codes + tiled_fp8_off(r, kb, 2 * g4 + (part >> 1), nkc) + (part & 1) * 8) = make_uint2(lo, hi);
     }
-    if (part == 0) scales[r * gpr + gc] = bad ? (uint8_t)0xFF : (uint8_t)(e + 127);
+    if (part == 0) scales[tiled_scale_off(r, kb, nkc) + g4] = (uint8_t)sbyte;
+  }
+}
+
+// Row-major <-> tiled copy: one thread per 16-byte code piece (and, for the first piece of each
+// 128-column chunk, the row's 4 scale bytes of that chunk).  Padding rows of a tiled destination
+// are zero-filled.
+template <int ELEM, bool TO_TILED>
+__global__ void __launch_bounds__(256) relayout_kernel(const uint8_t* __restrict__ sc, const uint8_t* __restrict__ ss,
+                                                        uint8_t* __restrict__ dc, uint8_t* __restrict__ ds,
+                                                        int64_t rows, int64_t cols) {
+  const int64_t nkc = cols >> 7;
+  constexpr int PPC = ELEM == 0 ? 4 : 8;  // 16-byte pieces per row and chunk
+  const int64_t row_bytes = ELEM == 0 ? cols >> 1 : cols;
+  const int64_t nrows = TO_TILED ? tiled_rows(rows) : rows;
+  const int64_t total = nrows * nkc * PPC;
+  const int64_t stride = (int64_t)gridDim.x * 256;
+  for (int64_t t = (int64_t)blockIdx.x * 256 + threadIdx.x; t < total; t += stride) {
+    const int64_t r = t / (nkc * PPC);
+    const int64_t j = t - r * (nkc * PPC);  // piece index within the row
+    const int64_t kb = j / PPC;
+    const int g = (int)(j - kb * PPC);
+    const int64_t rm = r * row_bytes + j * 16;
+    const int64_t ti = ELEM == 0 ? tiled_fp4_off(r, kb, g, nkc) : tiled_fp8_off(r, kb, g, nkc);
+    const int64_t rs = r * (cols >> 5) + kb * 4, ts = tiled_scale_off(r, kb, nkc);
+    if (TO_TILED) {
+      const bool in = r < rows;
+      *(uint4*)(dc + ti) = in ? *(const uint4*)(sc + rm) : make_uint4(0, 0, 0, 0);
+      if (g == 0) *(uint32_t*)(ds + ts) = in ? *(const uint32_t*)(ss + rs) : 0u;
+    } else {
+      *(uint4*)(dc + rm) = *(const uint4*)(sc + ti);
+      if (g == 0) *(uint32_t*)(ds + rs) = *(const uint32_t*)(ss + ts);
+    }
   }
 }
 
@@ -256,6 +321,35 @@ hipError_t launch_quant_mx(const uint16_t* x, int64_t rows, int64_t cols, int64_
     quant_mx_kernel<0><<<grid_for(threads), 256, 0, s>>>(x, rows, cols, ld, codes, scales);
   else
     quant_mx_kernel<1><<<grid_for(threads), 256, 0, s>>>(x, rows, cols, ld, codes, scales);
+  return hipGetLastError();
+}
+
+hipError_t launch_quant_mx_tiled(const uint16_t* x, int64_t rows, int64_t cols, int64_t ld, int elem,
+                                 uint8_t* codes, uint8_t* scales, hipStream_t s) {
+  const int64_t items = (tiled_rows(rows) / 16) * (cols / 128);
+  if (items == 0) return hipSuccess;
+  const int grid = (int)(items < 256 * 64 ? items : 256 * 64);
+  if (elem == 0)
+    quant_mx_tiled_kernel<0><<<grid, 256, 0, s>>>(x, rows, cols, ld, codes, scales);
+  else
+    quant_mx_tiled_kernel<1><<<grid, 256, 0, s>>>(x, rows, cols, ld, codes, scales);
+  return hipGetLastError();
+}
+
+hipError_t launch_relayout(const uint8_t* src_codes, const uint8_t* src_scales, uint8_t* dst_codes,
+                           uint8_t* dst_scales, int64_t rows, int64_t cols, int elem, bool to_tiled,
+                           hipStream_t s) {
+  const int64_t nrows = to_tiled ? tiled_rows(rows) : rows;
+  const int64_t threads = nrows * (cols / 128) * (elem == 0 ? 4 : 8);
+  if (threads == 0) return hipSuccess;
+  const int grid = grid_for(threads);
+  if (elem == 0) {
+    if (to_tiled) relayout_kernel<0, true><<<grid, 256, 0, s>>>(src_codes, src_scales, dst_codes, dst_scales, rows, cols);
+    else relayout_kernel<0, false><<<grid, 256, 0, s>>>(src_codes, src_scales, dst_codes, dst_scales, rows, cols);
+  } else {
+    if (to_tiled) relayout_kernel<1, true><<<grid, 256, 0, s>>>(src_codes, src_scales, dst_codes, dst_scales, rows, cols);
+    else relayout_kernel<1, false><<<grid, 256, 0, s>>>(src_codes, src_scales, dst_codes, dst_scales, rows, cols);
+  }
   return hipGetLastError();
 }
 

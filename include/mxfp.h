@@ -22,9 +22,23 @@
  *  - Pointers marked "device" are HIP device (or host-coherent) addresses owned by the caller;
  *    the library allocates nothing, frees nothing and keeps no pointer after the call returns.
  *  - BF16 and FP16 values are passed as uint16_t bit patterns.
- *  - Layouts are row-major and unshuffled.  FP4 codes: [rows, cols/2] bytes, element 2j in the
- *    low nibble of byte j.  FP8 codes: [rows, cols] bytes.  Scales: [rows, cols/G] bytes with
- *    G = 32 (E8M0, MX formats) or G = 16 (E4M3, NVFP4); groups start at column 0.
+ *  - The canonical layout (MX_LAYOUT_ROW_MAJOR) is row-major and unshuffled.  FP4 codes:
+ *    [rows, cols/2] bytes, element 2j in the low nibble of byte j.  FP8 codes: [rows, cols]
+ *    bytes.  Scales: [rows, cols/G] bytes with G = 32 (E8M0, MX formats) or G = 16 (E4M3,
+ *    NVFP4); groups start at column 0.
+ *  - MX_LAYOUT_TILED (MXFP4 / MXFP8 only, cols % 128 == 0) is the GEMM operand layout: the
+ *    same bytes regrouped so that every 1 KB of codes and every 256 bytes of scales that the
+ *    GEMM stages together are contiguous.  Rows are padded to Rp = rows rounded up to 256; the
+ *    padding rows hold zero codes and zero scale bytes.  With nkc = cols / 128:
+ *      FP4 codes: 1 KB tile (rb, kb) = rows 16rb..16rb+15, columns 128kb..128kb+127, at byte
+ *        (rb * nkc + kb) * 1024; row r of the tile at 64r; its 16-byte column group g (32
+ *        elements, nibbles packed as above) at 16 * (g ^ ((r >> 2) & 3)).
+ *      FP8 codes: 1 KB tile (rb, kb) = rows 8rb..8rb+7, at byte (rb * nkc + kb) * 1024; row r
+ *        of the tile at 128r; its 16-byte column group g (16 elements) at 16 * (g ^ (((8rb +
+ *        r) >> 1) & 7)).
+ *      Scales: 256-byte tile (sb, kb) = rows 64sb..64sb+63 at byte (sb * nkc + kb) * 256; row
+ *        r of the tile at 4r: the four scale bytes of columns 128kb..128kb+127 in order.
+ *    Sizes: codes Rp * cols / 2 (FP4) or Rp * cols (FP8) bytes, scales Rp * cols / 32 bytes.
  *  - A linear layer computes y[m, n] = sum_k a[m, k] * w[n, k] + bias[n]: the weight is N x K
  *    with K contiguous ("TN"); the output is M x N.
  *  - `stream` is a hipStream_t (NULL = the default stream).  Calls are asynchronous on that
@@ -45,7 +59,7 @@
 extern "C" {
 #endif
 
-#define MX_ABI_VERSION 1
+#define MX_ABI_VERSION 2
 
 typedef enum mx_status {
     MX_OK = 0,
@@ -71,7 +85,12 @@ typedef enum mx_epilogue {
 
 typedef enum mx_out_dtype { MX_OUT_BF16 = 0, MX_OUT_F32 = 1 } mx_out_dtype;
 
-/* A quantized matrix (rows x cols logical elements) in the layouts above. */
+typedef enum mx_layout {
+    MX_LAYOUT_ROW_MAJOR = 0, /* canonical */
+    MX_LAYOUT_TILED = 1      /* GEMM operand layout (see above) */
+} mx_layout;
+
+/* A quantized matrix (rows x cols logical elements) in one of the layouts above. */
 typedef struct mx_qmatrix {
     const void* codes;     /* device */
     const uint8_t* scales; /* device */
@@ -79,14 +98,17 @@ typedef struct mx_qmatrix {
     int32_t fmt;           /* mx_format */
     int64_t rows;
     int64_t cols;
+    int32_t layout;        /* mx_layout */
 } mx_qmatrix;
 
 /* Low-rank branch of SVDQuant ("Wan2.2 W4A8 SVDQuant", Contents/Accuracy: rank-32 BF16
- * factors).  y += bf16(x . down) . up, x being the unquantized BF16 activation. */
+ * factors).  y += bf16(x . L_down) . L_up, x being the unquantized BF16 activation, L_down the
+ * K x rank and L_up the rank x N factor; both are passed transposed so that the summed index is
+ * contiguous. */
 typedef struct mx_lowrank {
-    const uint16_t* down; /* device BF16 [K, rank], row-major */
-    const uint16_t* up;   /* device BF16 [rank, N], row-major */
-    int32_t rank;         /* 1..64, a multiple of 16 */
+    const uint16_t* down; /* device BF16 [rank, K]: L_down transposed (row r = column r of L_down) */
+    const uint16_t* up;   /* device BF16 [N, rank]: L_up transposed */
+    int32_t rank;         /* 16, 32, 48 or 64 */
 } mx_lowrank;
 
 /* Version of this ABI (MX_ABI_VERSION). */
@@ -108,16 +130,34 @@ const char* mx_last_error(void);
  *    E2M1_rne_sat(|x| / (sb * global_scale)), each the exact real rounded once; sb = 0 gives
  *    zero magnitudes; a NaN/Inf in the block gives scale 0x7F (E4M3 NaN) and codes 0.
  *    global_scale (> 0, finite) is ignored for the MX formats.
- * codes: device, [rows, cols/2] (FP4) or [rows, cols] (FP8) bytes.  scales: device,
- * [rows, cols/G] bytes.  Requires cols % G == 0, ld_x >= cols, x 16-byte aligned, ld_x % 8 == 0.
+ * layout MX_LAYOUT_ROW_MAJOR: codes device [rows, cols/2] (FP4) or [rows, cols] (FP8) bytes,
+ *   scales device [rows, cols/G] bytes.
+ * layout MX_LAYOUT_TILED (MX formats, cols % 128 == 0): codes and scales in the tiled layout,
+ *   of mx_tiled_bytes sizes, 16-byte aligned; the padding rows are written with zeros.
+ * Requires cols % G == 0, ld_x >= cols, x 16-byte aligned, ld_x % 8 == 0.
  */
 mx_status mx_quantize(const uint16_t* x, int64_t rows, int64_t cols, int64_t ld_x, int32_t fmt,
-                      float global_scale, void* codes, uint8_t* scales, void* stream);
+                      int32_t layout, float global_scale, void* codes, uint8_t* scales,
+                      void* stream);
+
+/* Byte sizes of the codes and the scales of a rows x cols matrix of format fmt in the tiled
+ * layout (MX formats, cols % 128 == 0).  Host-side arithmetic only. */
+mx_status mx_tiled_bytes(int64_t rows, int64_t cols, int32_t fmt, size_t* code_bytes,
+                         size_t* scale_bytes);
+
+/*
+ * mx_relayout - copy a quantized matrix into the other layout: src and dst have the same fmt
+ * (MXFP4 or MXFP8), rows and cols (cols % 128 == 0) and different layouts.  The bytes are only
+ * moved, never re-encoded; a tiled destination gets zero padding rows.  Used to prepare a
+ * weight once for the GEMM, or to read a tiled matrix back in the canonical layout.
+ */
+mx_status mx_relayout(const mx_qmatrix* src, const mx_qmatrix* dst, void* stream);
 
 /*
  * mx_dequantize - BF16 values of a quantized matrix: y = code * 2^(scale - 127) for MX (exact),
  * y = bf16_rne(code * sb * global_scale) for NVFP4 (one rounding of the exact product).  A NaN
  * scale byte gives NaN.  y: device BF16, rows x cols with leading dimension ld_y >= cols.
+ * Row-major matrices only (mx_relayout converts a tiled one).
  */
 mx_status mx_dequantize(const mx_qmatrix* q, uint16_t* y, int64_t ld_y, void* stream);
 
@@ -133,7 +173,8 @@ mx_status mx_absmax(const uint16_t* x, int64_t rows, int64_t cols, int64_t ld_x,
 float mx_nvfp4_global_scale(float amax);
 
 /* Bytes of workspace mx_linear needs for an M x K activation in act_fmt (codes + scales of the
- * quantized activation, plus the low-rank intermediate when rank > 0). */
+ * quantized activation -- in the tiled layout for the MX formats when K % 128 == 0 -- plus the
+ * low-rank intermediate when rank > 0). */
 size_t mx_linear_workspace_bytes(int64_t M, int64_t K, int32_t act_fmt, int32_t rank);
 
 /*
@@ -152,6 +193,8 @@ size_t mx_linear_workspace_bytes(int64_t M, int64_t K, int32_t act_fmt, int32_t 
  *        (contiguous; ld_out must be N; out_dtype ignored).  Requires N % 32 == 0.
  *  workspace: device, >= mx_linear_workspace_bytes(M, K, act_fmt, rank) bytes, 256-byte
  *        aligned; its contents on return are unspecified.
+ * w: row-major, or tiled (MX formats): a weight prepared once with mx_relayout or quantized
+ *        directly into the tiled layout is the fast GEMM operand.
  * Requires K % 32 == 0 (K % 16 == 0 for NVFP4), w->cols == K, N = w->rows >= 1.
  */
 mx_status mx_linear(const uint16_t* a, int64_t M, int64_t K, int64_t ld_a, int32_t act_fmt,
@@ -163,7 +206,7 @@ mx_status mx_linear(const uint16_t* a, int64_t M, int64_t K, int64_t ld_a, int32
 /*
  * mx_linear_q - the same GEMM and epilogues on an already quantized activation a (M x K), e.g.
  * the MXFP4 output of a MX_EPI_BIAS_GELU_QUANT_MXFP4 call feeding the next linear.  No
- * workspace and no low-rank branch.
+ * workspace and no low-rank branch.  a and w may each be row-major or tiled (MX formats).
  */
 mx_status mx_linear_q(const mx_qmatrix* a, const mx_qmatrix* w, const uint16_t* bias,
                       int32_t epilogue, int32_t out_dtype, void* out, int64_t ld_out,

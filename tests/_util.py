@@ -74,3 +74,30 @@ def sample_rows(M: int, count: int, seed: int = 5) -> np.ndarray:
     tail = np.arange(max(0, M - 96), M)
     mid = rng.choice(M, size=min(M, count), replace=False)
     return np.unique(np.concatenate([head, mid, tail]))
+
+
+def tile_mx(codes: np.ndarray, scales: np.ndarray, rows: int, cols: int, fp8: bool):
+    """The tiled GEMM operand layout of include/mxfp.h, built from row-major codes [rows, cols/2]
+    (FP4) or [rows, cols] (FP8) and scales [rows, cols/32] by plain index arithmetic: rows padded
+    to a multiple of 256 with zeros; 1 KB code tiles of 16 (FP4) or 8 (FP8) rows x 128 columns,
+    16-byte pieces XOR-placed by the row; 256-byte scale tiles of 64 rows x 4 bytes."""
+    rp = (rows + 255) // 256 * 256
+    nkc = cols // 128
+    row_bytes = cols if fp8 else cols // 2
+    c = np.zeros((rp, row_bytes), dtype=np.uint8)
+    c[:rows] = codes.reshape(rows, row_bytes)
+    s = np.zeros((rp, cols // 32), dtype=np.uint8)
+    s[:rows] = scales.reshape(rows, cols // 32)
+    out_c = np.zeros(rp * row_bytes, dtype=np.uint8)
+    out_s = np.zeros(rp * (cols // 32), dtype=np.uint8)
+    trows, pieces = (8, 8) if fp8 else (16, 4)
+    for r in range(rp):
+        for kb in range(nkc):
+            base = ((r // trows) * nkc + kb) * 1024 + (r % trows) * (1024 // trows)
+            for g in range(pieces):
+                slot = g ^ (((r >> 1) & 7) if fp8 else ((r >> 2) & 3))
+                src = c[r, kb * 16 * pieces + 16 * g: kb * 16 * pieces + 16 * g + 16]
+                out_c[base + 16 * slot: base + 16 * slot + 16] = src
+            sb = ((r // 64) * nkc + kb) * 256 + (r % 64) * 4
+            out_s[sb: sb + 4] = s[r, 4 * kb: 4 * kb + 4]
+    return out_c, out_s

@@ -51,7 +51,7 @@ def test_status_strings(mx):
     for code, name in enumerate(["MX_OK", "MX_ERR_NULL", "MX_ERR_SHAPE", "MX_ERR_ALIGN",
                                  "MX_ERR_UNSUPPORTED", "MX_ERR_WORKSPACE", "MX_ERR_HIP"]):
         assert L.mx_status_string(code).decode() == name
-    assert L.mx_abi_version() == 1
+    assert L.mx_abi_version() == 2
 
 
 def test_nvfp4_global_scale_host_arithmetic_matches_oracle(mx):
@@ -63,10 +63,22 @@ def test_nvfp4_global_scale_host_arithmetic_matches_oracle(mx):
 def test_workspace_bytes(mx):
     ws = mx.linear_workspace_bytes
     r = lambda v: (v + 255) // 256 * 256
-    assert ws(75600, 5120, "mxfp4") == r(75600 * 2560) + r(75600 * 160)
-    assert ws(4290, 3072, "mxfp8", 32) == r(4290 * 3072) + r(4290 * 96) + r(4290 * 32 * 2)
+    # MX activations with K % 128 == 0 are staged tiled: rows padded to a multiple of 256
+    assert ws(75600, 5120, "mxfp4") == r(75776 * 2560) + r(75776 * 160)
+    assert ws(4290, 3072, "mxfp8", 32) == r(4352 * 3072) + r(4352 * 96) + r(4290 * 32 * 2)
+    assert ws(300, 160, "mxfp4") == r(300 * 80) + r(300 * 5)  # row-major: K % 128 != 0
     assert ws(75600, 5120, "nvfp4") == r(75600 * 2560) + r(75600 * 320)
     assert ws(0, 5120, "mxfp4") == 0
+
+
+def test_tiled_bytes(mx):
+    assert mx.tiled_bytes(75600, 5120, "mxfp4") == (75776 * 2560, 75776 * 160)
+    assert mx.tiled_bytes(1, 128, "mxfp8") == (256 * 128, 256 * 4)
+    assert mx.tiled_bytes(0, 256, "mxfp4") == (0, 0)
+    with pytest.raises(mx.MxError):
+        mx.tiled_bytes(16, 160, "mxfp4")   # cols % 128
+    with pytest.raises(mx.MxError):
+        mx.tiled_bytes(16, 128, "nvfp4")   # MX formats only
 
 
 FAKE = 0x10000  # an aligned, never dereferenced address
@@ -80,27 +92,32 @@ def test_quantize_validation(mx):
     L = mx.lib()
     P = ctypes.c_void_p
     # unknown format
-    assert L.mx_quantize(P(FAKE), 4, 64, 64, 7, 1.0, P(FAKE), P(FAKE), None) == 4
+    assert L.mx_quantize(P(FAKE), 4, 64, 64, 7, 0, 1.0, P(FAKE), P(FAKE), None) == 4
     # cols not a multiple of the group
-    assert L.mx_quantize(P(FAKE), 4, 48, 48, mx.MXFP4, 1.0, P(FAKE), P(FAKE), None) == 2
-    assert L.mx_quantize(P(FAKE), 4, 24, 24, mx.NVFP4, 1.0, P(FAKE), P(FAKE), None) == 2
+    assert L.mx_quantize(P(FAKE), 4, 48, 48, mx.MXFP4, 0, 1.0, P(FAKE), P(FAKE), None) == 2
+    assert L.mx_quantize(P(FAKE), 4, 24, 24, mx.NVFP4, 0, 1.0, P(FAKE), P(FAKE), None) == 2
     # ld < cols
-    assert L.mx_quantize(P(FAKE), 4, 64, 32, mx.MXFP4, 1.0, P(FAKE), P(FAKE), None) == 2
+    assert L.mx_quantize(P(FAKE), 4, 64, 32, mx.MXFP4, 0, 1.0, P(FAKE), P(FAKE), None) == 2
     # NVFP4 needs a positive finite global scale
-    assert L.mx_quantize(P(FAKE), 4, 64, 64, mx.NVFP4, 0.0, P(FAKE), P(FAKE), None) == 2
-    assert L.mx_quantize(P(FAKE), 4, 64, 64, mx.NVFP4, float("inf"), P(FAKE), P(FAKE), None) == 2
+    assert L.mx_quantize(P(FAKE), 4, 64, 64, mx.NVFP4, 0, 0.0, P(FAKE), P(FAKE), None) == 2
+    assert L.mx_quantize(P(FAKE), 4, 64, 64, mx.NVFP4, 0, float("inf"), P(FAKE), P(FAKE), None) == 2
     # NULL pointers
-    assert L.mx_quantize(None, 4, 64, 64, mx.MXFP4, 1.0, P(FAKE), P(FAKE), None) == 1
+    assert L.mx_quantize(None, 4, 64, 64, mx.MXFP4, 0, 1.0, P(FAKE), P(FAKE), None) == 1
     # misaligned input / leading dimension
-    assert L.mx_quantize(P(FAKE + 2), 4, 64, 64, mx.MXFP4, 1.0, P(FAKE), P(FAKE), None) == 3
-    assert L.mx_quantize(P(FAKE), 4, 64, 68, mx.MXFP4, 1.0, P(FAKE), P(FAKE), None) == 3
+    assert L.mx_quantize(P(FAKE + 2), 4, 64, 64, mx.MXFP4, 0, 1.0, P(FAKE), P(FAKE), None) == 3
+    assert L.mx_quantize(P(FAKE), 4, 64, 68, mx.MXFP4, 0, 1.0, P(FAKE), P(FAKE), None) == 3
     assert "alignment" in L.mx_last_error().decode()
+    # tiled layout: MX formats with cols % 128 == 0, 16-byte aligned outputs; unknown layouts
+    assert L.mx_quantize(P(FAKE), 4, 96, 96, mx.MXFP4, 1, 1.0, P(FAKE), P(FAKE), None) == 2
+    assert L.mx_quantize(P(FAKE), 4, 128, 128, mx.NVFP4, 1, 1.0, P(FAKE), P(FAKE), None) == 4
+    assert L.mx_quantize(P(FAKE), 4, 128, 128, mx.MXFP4, 1, 1.0, P(FAKE + 4), P(FAKE), None) == 3
+    assert L.mx_quantize(P(FAKE), 4, 128, 128, mx.MXFP4, 5, 1.0, P(FAKE), P(FAKE), None) == 4
     # zero rows is a no-op even with NULL pointers
-    assert L.mx_quantize(None, 0, 64, 64, mx.MXFP4, 1.0, None, None, None) == 0
+    assert L.mx_quantize(None, 0, 64, 64, mx.MXFP4, 0, 1.0, None, None, None) == 0
 
 
-def _qm(mx, rows, cols, fmt, gs=1.0, codes=FAKE, scales=FAKE):
-    return mx._QMatrix(codes, scales, gs, fmt, rows, cols)
+def _qm(mx, rows, cols, fmt, gs=1.0, codes=FAKE, scales=FAKE, layout=0):
+    return mx._QMatrix(codes, scales, gs, fmt, rows, cols, layout)
 
 
 def test_linear_validation(mx):
@@ -139,6 +156,9 @@ def test_linear_validation(mx):
     assert call(lr=byref(lr_bad)) == 2
     lr_nv = mx._LowRank(FAKE, FAKE, 32)
     assert call(act=mx.NVFP4, w_=_qm(mx, 64, 128, mx.NVFP4), lr=byref(lr_nv)) == 4
+    assert call(K=160, lda=160, w_=_qm(mx, 64, 160, mx.MXFP4, layout=1)) == 2  # tiled needs K % 128
+    assert call(act=mx.NVFP4, w_=_qm(mx, 64, 128, mx.NVFP4, layout=1)) == 4     # tiled NVFP4
+    assert call(w_=_qm(mx, 64, 128, mx.MXFP4, layout=3)) == 4                   # unknown layout
     assert call(M=0, ws=0) == 0                      # empty activation: no-op
 
 
@@ -154,6 +174,21 @@ def test_linear_q_validation(mx):
     assert L.mx_linear_q(ctypes.byref(a_mis), ctypes.byref(w), None, 0, 0, P(FAKE), 64, None, None) == 3
     a0 = _qm(mx, 0, 128, mx.MXFP4)
     assert L.mx_linear_q(ctypes.byref(a0), ctypes.byref(w), None, 0, 0, P(FAKE), 64, None, None) == 0
+
+
+def test_relayout_validation(mx):
+    L = mx.lib()
+    rm, ti = _qm(mx, 16, 128, mx.MXFP4), _qm(mx, 16, 128, mx.MXFP4, layout=1)
+    assert L.mx_relayout(None, ctypes.byref(ti), None) == 1
+    assert L.mx_relayout(ctypes.byref(rm), ctypes.byref(rm), None) == 4        # same layout
+    assert L.mx_relayout(ctypes.byref(rm), ctypes.byref(_qm(mx, 8, 128, mx.MXFP4, layout=1)), None) == 2
+    assert L.mx_relayout(ctypes.byref(_qm(mx, 16, 96, mx.MXFP4)),
+                         ctypes.byref(_qm(mx, 16, 96, mx.MXFP4, layout=1)), None) == 2  # cols % 128
+    assert L.mx_relayout(ctypes.byref(_qm(mx, 16, 128, mx.NVFP4)),
+                         ctypes.byref(_qm(mx, 16, 128, mx.NVFP4, layout=1)), None) == 4
+    assert L.mx_relayout(ctypes.byref(_qm(mx, 16, 128, mx.MXFP4, codes=FAKE + 4)), ctypes.byref(ti), None) == 3
+    assert L.mx_relayout(ctypes.byref(_qm(mx, 0, 128, mx.MXFP4)),
+                         ctypes.byref(_qm(mx, 0, 128, mx.MXFP4, layout=1)), None) == 0
 
 
 def test_binding_fails_loudly_without_native_library(mx, monkeypatch, tmp_path):

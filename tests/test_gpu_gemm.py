@@ -47,14 +47,16 @@ def _mx_case(mx, M, K, N, seed=0, bias=True, act="mxfp4", out_dtype=torch.float3
 
 
 @pytest.mark.parametrize("M,K,N", [(256, 512, 512), (300, 1024, 640), (1, 256, 256), (37, 288, 96),
-                                   (64, 32, 32), (513, 768, 1024)])
+                                   (64, 32, 32), (513, 768, 1024), (260, 384, 200), (300, 640, 160),
+                                   (700, 1280, 96)])
 def test_mxfp4_linear_f32_vs_oracle(mx, M, K, N):
     y, y_ref, abs_sum, _ = _mx_case(mx, M, K, N, seed=M + K + N)
     assert_within(y.cpu().numpy(), y_ref, abs_sum)
 
 
-def test_bf16_output_is_rne_of_f32_output(mx):
-    M, K, N = 300, 1024, 640
+@pytest.mark.parametrize("M,K,N", [(300, 1024, 640), (77, 256, 100), (260, 384, 200)])
+def test_bf16_output_is_rne_of_f32_output(mx, M, K, N):
+    """Both BF16 store paths: staged through LDS (N % 8 == 0) and direct (N = 100)."""
     a_bits = activation_bits(M, K, seed_base=12000)
     wq = _quant_w(mx, weight_bits(N, K, seed=12100))
     b = to_dev_f16(f16_bits(synth.normal_f32(12200, (N,), 0.01)))
@@ -138,10 +140,27 @@ def test_validation_failure_writes_nothing(mx):
     assert torch.all(out == 3.0)
 
 
+@pytest.mark.parametrize("act", ["mxfp4", "mxfp8"])
+@pytest.mark.parametrize("M,K,N", [(300, 1024, 640), (260, 384, 200), (513, 768, 1024)])
+def test_tiled_operands_give_identical_results(mx, M, K, N, act):
+    """The tiled layout only moves bytes: every layout pairing gives the same output bits."""
+    a = to_dev_bf16(activation_bits(M, K, seed_base=16000 + M))
+    w_rm = _quant_w(mx, weight_bits(N, K, seed=16100 + N))
+    w_t = mx.relayout(w_rm)
+    bias = to_dev_f16(f16_bits(synth.normal_f32(16200, (N,), 0.01)))
+    a_rm = mx.quantize(a, act)
+    a_t = mx.quantize(a, act, layout="tiled")
+    ref = mx.linear_q(a_rm, w_rm, bias, out_dtype=torch.float32)
+    for aa, ww in ((a_t, w_t), (a_rm, w_t), (a_t, w_rm)):
+        assert torch.equal(mx.linear_q(aa, ww, bias, out_dtype=torch.float32), ref)
+    assert torch.equal(mx.linear(a, w_t, bias, act_fmt=act, out_dtype=torch.float32), ref)
+    assert torch.equal(mx.linear(a, w_rm, bias, act_fmt=act, out_dtype=torch.float32), ref)
+
+
 # ---------------------------------------------------------------------------------------------
 # W4A8 (MXFP8 activations) and the low-rank branch
 # ---------------------------------------------------------------------------------------------
-@pytest.mark.parametrize("M,K,N", [(130, 512, 256), (300, 3072, 384)])
+@pytest.mark.parametrize("M,K,N", [(130, 512, 256), (300, 3072, 384), (77, 384, 200)])
 def test_w4a8_linear_vs_oracle(mx, M, K, N):
     y, y_ref, abs_sum, _ = _mx_case(mx, M, K, N, seed=7 * M, act="mxfp8")
     assert_within(y.cpu().numpy(), y_ref, abs_sum)
@@ -284,14 +303,17 @@ def _full_mx(mx, wl_name, act, nsample=192):
     w_bits = synth.bits16(synth.to_bf16(wl.weight()))
     b = wl.bias()
     b_bits = f16_bits(b) if b is not None else None
-    wq = _quant_w(mx, w_bits)
+    wq = mx.relayout(_quant_w(mx, w_bits))  # the benchmark's prepared (tiled) weight
     a = to_dev_bf16(a_bits)
     rows = sample_rows(wl.M, nsample)
-    y = mx.linear(a, wq, to_dev_f16(b_bits) if b is not None else None, act_fmt=act,
-                  out_dtype=torch.float32)
+    bias = to_dev_f16(b_bits) if b is not None else None
+    y = mx.linear(a, wq, bias, act_fmt=act, out_dtype=torch.float32)
+    y16 = mx.linear(a, wq, bias, act_fmt=act, out_dtype=torch.bfloat16)
     torch.cuda.synchronize()
-    ys = y[torch.from_numpy(rows).cuda()].cpu().numpy()
-    del y
+    idx = torch.from_numpy(rows).cuda()
+    ys = y[idx].cpu().numpy()
+    np.testing.assert_array_equal(dev_bits16(y16[idx]), bf16_rne_of_f32(ys))
+    del y, y16
     elem = O.E4M3 if act == "mxfp8" else O.E2M1
     ac, as_ = O.quantize_mx_bf16(a_bits[rows], elem)
     wc, ws = O.quantize_mx_bf16(w_bits)

@@ -8,7 +8,7 @@ import torch
 
 import oracle as O
 from fp4_block_scaled_amd import synth
-from _util import (activation_bits, dev_bits16, to_dev_bf16, unpack_fp4)
+from _util import (activation_bits, dev_bits16, tile_mx, to_dev_bf16, unpack_fp4)
 
 pytestmark = pytest.mark.gpu
 
@@ -191,3 +191,55 @@ def test_full_size_nvfp4_activation_quantizer(mx):
     ref_c, ref_s = O.quantize_nv_bf16(bits, sg)
     assert np.array_equal(s, ref_s)
     assert np.array_equal(c, ref_c)
+
+
+# ---------------------------------------------------------------------------------------------
+# tiled GEMM operand layout
+# ---------------------------------------------------------------------------------------------
+@pytest.mark.parametrize("rows,cols", [(300, 640), (1, 128), (256, 1024), (70, 384)])
+@pytest.mark.parametrize("fmt,elem", [("mxfp4", O.E2M1), ("mxfp8", O.E4M3)])
+def test_tiled_quantizer_is_the_tiled_oracle(mx, rows, cols, fmt, elem):
+    bits = activation_bits(rows, cols, seed_base=15000 + rows + cols)
+    ref_c, ref_s = O.quantize_mx_bf16(bits, elem)
+    tc, ts = tile_mx(ref_c, ref_s, rows, cols, fp8=(fmt == "mxfp8"))
+    x = to_dev_bf16(bits)
+    q = mx.quantize(x, fmt, layout="tiled")
+    torch.cuda.synchronize()
+    np.testing.assert_array_equal(q.scales.cpu().numpy(), ts)
+    np.testing.assert_array_equal(q.codes.cpu().numpy(), tc)
+    # relayout both ways moves the same bytes
+    back = mx.relayout(q)
+    fwd = mx.relayout(mx.quantize(x, fmt))
+    torch.cuda.synchronize()
+    np.testing.assert_array_equal(back.codes.cpu().numpy(), ref_c)
+    np.testing.assert_array_equal(back.scales.cpu().numpy(), ref_s)
+    np.testing.assert_array_equal(fwd.codes.cpu().numpy(), tc)
+    np.testing.assert_array_equal(fwd.scales.cpu().numpy(), ts)
+
+
+@pytest.mark.parametrize("fmt,elem", [("mxfp4", O.E2M1), ("mxfp8", O.E4M3)])
+def test_tiled_quantizer_exhaustive_bf16(mx, fmt, elem):
+    """Every BF16 pattern, four 32-element groups per row, through the tiled quantizer."""
+    block = np.zeros((len(ALL), 32), dtype=np.uint16)
+    block[:, 0] = ALL
+    block[:, 1] = 0x40C0
+    block[:, 7] = ALL[::-1]
+    bits = block.reshape(len(ALL) // 4, 128)
+    ref_c, ref_s = O.quantize_mx_bf16(bits, elem)
+    tc, ts = tile_mx(ref_c, ref_s, bits.shape[0], 128, fp8=(fmt == "mxfp8"))
+    q = mx.quantize(to_dev_bf16(bits), fmt, layout="tiled")
+    torch.cuda.synchronize()
+    np.testing.assert_array_equal(q.scales.cpu().numpy(), ts)
+    np.testing.assert_array_equal(q.codes.cpu().numpy(), tc)
+
+
+def test_tiled_outputs_write_nothing_past_their_buffers(mx):
+    rows, cols = 37, 256
+    x = to_dev_bf16(activation_bits(rows, cols, seed_base=15500))
+    cb, sb = mx.tiled_bytes(rows, cols, "mxfp4")
+    codes = torch.full((cb + 4096,), 0xA5, dtype=torch.uint8, device="cuda")
+    scales = torch.full((sb + 4096,), 0x5A, dtype=torch.uint8, device="cuda")
+    q = mx.QMatrix(codes[:cb], scales[:sb], mx.MXFP4, rows, cols, layout=mx.TILED)
+    mx.quantize(x, out=q)
+    torch.cuda.synchronize()
+    assert torch.all(codes[cb:] == 0xA5) and torch.all(scales[sb:] == 0x5A)
