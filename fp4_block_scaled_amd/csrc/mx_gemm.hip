@@ -566,29 +566,28 @@ __global__ void __launch_bounds__(256, 2) gemm_mx_ring_kernel(GemmParams p) {
   };
 
   const uint32_t lds0 = lds_addr_of(smem);
-  auto issue = [&](int kc, int st) {
-    const bool live = kc < nkc;  // past the last chunk: empty descriptors, no memory traffic
-    v4i dw = rw, da = ra, dws = rws, das = ras;
-    dw[2] = live ? dw[2] : 0;
-    da[2] = live ? da[2] : 0;
-    dws[2] = live ? dws[2] : 0;
-    das[2] = live ? das[2] : 0;
+  auto issue_one = [&](auto qc, int kc, int st) {
+    constexpr int Q = decltype(qc)::value;
+    const bool live = kc < nkc;
     const uint32_t sW = lds0 + (uint32_t)(st * T::STAGE);
     const uint32_t sA = sW + T::W_BYTES, sWS = sA + T::A_BYTES, sAS = sWS + T::WS_BYTES;
-    static_for<T::NW>([&](auto q) {
-      dma_lds16(dw, sW + (uint32_t)((wave * T::NW + q) * 1024), off_w(q), (uint32_t)kc * w_step);
-    });
-    static_for<T::NA>([&](auto q) {
+    if constexpr (Q < T::NW) {
+      v4i dw = rw; dw[2] = live ? dw[2] : 0;
+      dma_lds16(dw, sW + (uint32_t)((wave * T::NW + Q) * 1024), off_w(Q), (uint32_t)kc * w_step);
+    } else if constexpr (Q < T::NW + T::NA) {
+      constexpr int q = Q - T::NW;
+      v4i da = ra; da[2] = live ? da[2] : 0;
       dma_lds16(da, sA + (uint32_t)((wave * T::NA + q) * 1024), off_a(q), (uint32_t)kc * a_step);
-    });
-    static_for<T::NS>([&](auto k) {
-      int urow;
-      bool is_a;
+    } else {
+      constexpr int k = Q - T::NW - T::NA;
+      int urow; bool is_a;
       scale_slot(k, urow, is_a);
+      v4i dws = rws, das = ras; dws[2] = live ? dws[2] : 0; das[2] = live ? das[2] : 0;
       dma_lds4(is_a ? das : dws, (is_a ? sAS : sWS) + (uint32_t)(urow * 256), off_s(urow, is_a ? at : wt),
                (uint32_t)kc * (is_a ? as_step : ws_step));
-    });
+    }
   };
+  auto issue = [&](int kc, int st) { static_for<T::NDMA>([&](auto q) { issue_one(q, kc, st); }); };
 
   v16f acc[T::FN][T::FM];
   static_for<T::FN>([&](auto i) { static_for<T::FM>([&](auto j) { acc[i][j] = v16f{}; }); });
@@ -637,8 +636,8 @@ __global__ void __launch_bounds__(256, 2) gemm_mx_ring_kernel(GemmParams p) {
       }
     }
     __builtin_amdgcn_sched_barrier(0);
-    issue(kc + 2, st2);
-    __builtin_amdgcn_sched_barrier(0);
+    // the next chunk's loads, one after every two MFMAs: a burst of them would fill the
+    // vector-memory queue and hold up the MFMA issue behind it
     static_for<2>([&](auto sc) {
       constexpr int S = decltype(sc)::value;
       static_for<T::FN>([&](auto i) {
@@ -647,6 +646,18 @@ __global__ void __launch_bounds__(256, 2) gemm_mx_ring_kernel(GemmParams p) {
             acc[i][j] = mfma_scale_32x32x64_f4f8(wf[S][i], af[S][j], acc[i][j], 4, 0, S, (int)wsc[i], S, (int)asc[j]);
           else
             acc[i][j] = mfma_scale_32x32x64_f4f4(wf[S][i], af[S][j], acc[i][j], 4, 4, S, (int)wsc[i], S, (int)asc[j]);
+          constexpr int M = S * T::FN * T::FM + decltype(i)::value * T::FM + decltype(j)::value;
+          constexpr int TOTAL = 2 * T::FN * T::FM;
+          static_assert(TOTAL >= T::NDMA, "one load slot per MFMA at most");
+          // load q goes after MFMA (q + 1) * TOTAL / NDMA - 1 (distinct slots, the last MFMA last)
+          static_for<T::NDMA>([&](auto qc) {
+            constexpr int Q = decltype(qc)::value;
+            if constexpr ((Q + 1) * TOTAL / T::NDMA - 1 == M) {
+              __builtin_amdgcn_sched_barrier(0);
+              issue_one(qc, kc + 2, st2);
+              __builtin_amdgcn_sched_barrier(0);
+            }
+          });
         });
       });
     });
@@ -890,7 +901,8 @@ static void run_ring(const GemmParams& p, int grid, hipStream_t s) {
 // Every (epilogue, output type, low-rank) combination of the ring kernel.
 template <int BM, int BN, bool AFP8, int EPI, bool LR>
 static void run_ring_o(const GemmParams& p, int grid, hipStream_t s) {
-  if (EPI != EPI_GELU_QUANT && p.out_f32) run_ring<BM, BN, AFP8, EPI, true, LR>(p, grid, s);
+  if constexpr (EPI == EPI_GELU_QUANT) run_ring<BM, BN, AFP8, EPI, false, LR>(p, grid, s);
+  else if (p.out_f32) run_ring<BM, BN, AFP8, EPI, true, LR>(p, grid, s);
   else run_ring<BM, BN, AFP8, EPI, false, LR>(p, grid, s);
 }
 template <int BM, int BN, bool AFP8, bool LR>
