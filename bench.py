@@ -226,7 +226,7 @@ def bench_variant(args, torch, mx, synth):
         ws = torch.empty(mx.linear_workspace_bytes(M, K, "nvfp4"), dtype=torch.uint8, device="cuda")
         step = lambda: mx.linear(a, wq, bias, act_fmt="nvfp4", act_global_scale=sg_a, out=out, workspace=ws)
         flops = 2.0 * M * N * K
-        dtype, peak = "nvfp4->bf16", PEAK_TFLOPS["bf16"]
+        dtype, peak = "nvfp4->f16", PEAK_TFLOPS["bf16"]  # FP16 and BF16 MFMA share the 2.5 PF peak
         aq = mx.quantize(a, "nvfp4", sg_a)
         kernels["gemm_ms"] = time_events(lambda: mx.linear_q(aq, wq, bias, out=out), args.steps, torch)
         kernels["quant_nvfp4_ms"] = time_events(lambda: mx.quantize(a, "nvfp4", sg_a, out=aq), args.steps, torch)

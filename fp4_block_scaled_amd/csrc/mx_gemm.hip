@@ -496,6 +496,50 @@ __device__ __forceinline__ void tile_coords_gm(int b, int tiles_m, int tiles_n, 
   tn = in / rows;
 }
 
+// BF16 output of a BM x 128 ring-kernel tile through LDS (the ring is idle once the K loop is
+// done): the tile is written as BM rows of 256 bytes, 16-byte chunks XOR-swizzled by the row,
+// then stored as whole 256-byte row segments, four rows per instruction, instead of 8-byte
+// pieces of 32 rows.  Waves hold (BM/2) x 64 sub-tiles (2 x 2 waves).
+template <int EPI, bool OUTF32>
+__device__ __forceinline__ bool ring_staged_ok(const GemmParams& p) {
+  return EPI != EPI_GELU_QUANT && !OUTF32 && (p.N % 8) == 0 && (p.ld_out % 8) == 0 &&
+         (((uintptr_t)p.out) & 15) == 0;
+}
+template <int BM, int FN, int FM, int EPI>
+__device__ __forceinline__ void epilogue_ring_staged(const GemmParams& p, v16f (&acc)[FN][FM], uint8_t* smem,
+                                                     int n0, int m0, int wn0, int wm0, int wave) {
+  const int lane = lane_id();
+  const int r32 = lane & 31, h = lane >> 5;
+  static_for<FN>([&](auto i) {
+    float b[16];
+    load_bias16(p, n0 + wn0 + 32 * i, b);
+    static_for<FM>([&](auto j) {
+      __builtin_amdgcn_sched_barrier(0);
+      float v[16];
+      finish16<EPI>(p, acc[i][j], b, v);
+      const int row = wm0 + 32 * j + r32;
+#pragma unroll
+      for (int g = 0; g < 4; ++g) {
+        const int c = (wn0 + 32 * i) / 8 + g;  // 16-byte chunk of the row (8 BF16)
+        const uint32_t lo = f32_to_bf16_rne(v[4 * g]) | (f32_to_bf16_rne(v[4 * g + 1]) << 16);
+        const uint32_t hi = f32_to_bf16_rne(v[4 * g + 2]) | (f32_to_bf16_rne(v[4 * g + 3]) << 16);
+        *(uint2*)(smem + row * 256 + ((c ^ (row & 15)) << 4) + 8 * h) = make_uint2(lo, hi);
+      }
+    });
+  });
+  wait_lds_all();
+  barrier_only();
+  const int c = lane & 15;
+  const int n = n0 + 8 * c;
+#pragma unroll 4
+  for (int it = 0; it < BM / 16; ++it) {
+    const int row = wave * (BM / 4) + 4 * it + (lane >> 4);
+    const uint4 d = *(const uint4*)(smem + row * 256 + ((c ^ (row & 15)) << 4));
+    const int m = m0 + row;
+    if (m < p.M && n < p.N) *(uint4*)((uint16_t*)p.out + (int64_t)m * p.ld_out + n) = d;
+  }
+}
+
 template <int BM, int BN, bool AFP8, int EPI, bool OUTF32, bool LR>
 __global__ void __launch_bounds__(256, 2) gemm_mx_ring_kernel(GemmParams p) {
   using T = RingTile<BM, BN, AFP8>;
@@ -672,45 +716,13 @@ __global__ void __launch_bounds__(256, 2) gemm_mx_ring_kernel(GemmParams p) {
       });
     });
   }
-  // BF16 output through LDS: the tile is written to the (now idle) ring as BM rows of 256 bytes
-  // (16-byte chunks XOR-swizzled by the row), then stored as whole 256-byte row segments, four
-  // rows per instruction, instead of 8-byte pieces of 32 rows.
-  const bool staged = EPI != EPI_GELU_QUANT && !OUTF32 && (p.N % 8) == 0 && (p.ld_out % 8) == 0 &&
-                      (((uintptr_t)p.out) & 15) == 0;
-  if (!staged) {
+  if (ring_staged_ok<EPI, OUTF32>(p)) {
+    static_assert(BM * BN * 2 <= T::NSTAGE * T::STAGE, "output tile fits the ring");
+    wait_vmem_all();  // the (empty) loads issued for the chunks past the end have landed
+    barrier_only();   // every wave is done with the ring
+    epilogue_ring_staged<BM, T::FN, T::FM, EPI>(p, acc, smem, n0, m0, wn0, wm0, wave);
+  } else {
     epilogue_direct<T::FN, T::FM, EPI, OUTF32>(p, acc, n0 + wn0, m0 + wm0);
-    return;
-  }
-  static_assert(BM * BN * 2 <= T::NSTAGE * T::STAGE, "output tile fits the ring");
-  wait_vmem_all();  // the (empty) loads issued for the chunks past the end have landed
-  barrier_only();   // every wave is done with the ring
-  static_for<T::FN>([&](auto i) {
-    float b[16];
-    load_bias16(p, n0 + wn0 + 32 * i, b);
-    static_for<T::FM>([&](auto j) {
-      __builtin_amdgcn_sched_barrier(0);
-      float v[16];
-      finish16<EPI>(p, acc[i][j], b, v);
-      const int row = wm0 + 32 * j + r32;
-#pragma unroll
-      for (int g = 0; g < 4; ++g) {
-        const int c = (wn0 + 32 * i) / 8 + g;  // 16-byte chunk of the row (8 BF16)
-        const uint32_t lo = f32_to_bf16_rne(v[4 * g]) | (f32_to_bf16_rne(v[4 * g + 1]) << 16);
-        const uint32_t hi = f32_to_bf16_rne(v[4 * g + 2]) | (f32_to_bf16_rne(v[4 * g + 3]) << 16);
-        *(uint2*)(smem + row * 256 + ((c ^ (row & 15)) << 4) + 8 * h) = make_uint2(lo, hi);
-      }
-    });
-  });
-  wait_lds_all();
-  barrier_only();
-  const int c = lane & 15;
-  const int n = n0 + 8 * c;
-#pragma unroll 4
-  for (int it = 0; it < BM / 16; ++it) {
-    const int row = wave * (BM / 4) + 4 * it + (lane >> 4);
-    const uint4 d = *(const uint4*)(smem + row * 256 + ((c ^ (row & 15)) << 4));
-    const int m = m0 + row;
-    if (m < p.M && n < p.N) *(uint4*)((uint16_t*)p.out + (int64_t)m * p.ld_out + n) = d;
   }
 }
 
@@ -860,6 +872,181 @@ __global__ void __launch_bounds__(256, 1) gemm_nv_kernel(GemmParams p) {
 }
 
 // ---------------------------------------------------------------------------------------------
+// NVFP4 GEMM, ring-staged (K a multiple of 64)
+// ---------------------------------------------------------------------------------------------
+// The E4M3 per-16 block scales cannot ride in the scaled MFMA (E8M0 per 32 only), and code x
+// block scale needs up to 6 significant bits.  Both are exact in FP16 (11 bits; magnitudes
+// 2^-10 .. 2688), so each lane dequantizes its own fragments in registers with the gfx950
+// conversions (two E2M1 codes -> two FP16, exact; two E4M3 scales -> two FP16, exact) and one
+// packed FP16 multiply, and the product runs on V_MFMA_F32_32X32X16_F16.  The two FP32 global
+// scales multiply the accumulator in the epilogue.
+// Tile and waves as the MX ring kernel (256 x 128, 2 x 2 waves of 128 x 64, two workgroups per
+// compute unit); K chunks of 64 (32 code bytes and 4 scale bytes per row) in a 4-deep LDS ring.
+// K order inside a chunk: lane half h holds chunk elements 32h..32h+31 (16 contiguous bytes);
+// MFMA step t (0..3) takes elements 32h + 8t .. 32h + 8t + 7, which lie in scale block 2h + t/2.
+// LDS code rows are 32 bytes, the two 16-byte halves swapped on rows with bit 3 set, so that a
+// quarter wave (16 consecutive rows, one half each) reads 16 distinct bank groups.
+template <int BM, int BN>
+struct NvRingTile {
+  static_assert(BM == 256 && BN == 128, "tile sizes");
+  static constexpr int KCN = 64, ROWB = 32;
+  static constexpr int W_BYTES = BN * ROWB, A_BYTES = BM * ROWB;
+  static constexpr int WS_BYTES = BN * 4, AS_BYTES = BM * 4;
+  static constexpr int STAGE = W_BYTES + A_BYTES + WS_BYTES + AS_BYTES;
+  static constexpr int NSTAGE = 4;
+  static constexpr int LDS = NSTAGE * STAGE > BM * BN * 2 ? NSTAGE * STAGE : BM * BN * 2;
+  static constexpr int FN = BN / 64, FM = BM / 64;
+  static constexpr int NW = W_BYTES / 4096, NA = A_BYTES / 4096;  // 1 KB loads per wave
+  static constexpr int TA = BM / 64, TW = BN / 64;                 // 256-byte scale loads
+  static constexpr int NS = (TA + TW + 3) / 4;
+  static constexpr int NDMA = NW + NA + NS;
+  static_assert(LDS <= 80 * 1024, "two workgroups per compute unit");
+};
+
+// 8 E2M1 codes (one dword, element 2j in the low nibble of byte j) times a block scale, as 8
+// exact FP16 values.  The conversion's scale operand only contributes its exponent, so it is 1
+// and the block scale is a packed FP16 multiply (exact: at most 6 significant bits).
+__device__ __forceinline__ v8h nv_dequant8_f16(uint32_t codes, v2h sb) {
+  const v2h p0 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(codes, 1.0f, 0) * sb;
+  const v2h p1 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(codes, 1.0f, 1) * sb;
+  const v2h p2 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(codes, 1.0f, 2) * sb;
+  const v2h p3 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(codes, 1.0f, 3) * sb;
+  return v8h{p0[0], p0[1], p1[0], p1[1], p2[0], p2[1], p3[0], p3[1]};
+}
+
+template <int BM, int BN, int EPI, bool OUTF32>
+__global__ void __launch_bounds__(256, 2) gemm_nv_ring_kernel(GemmParams p) {
+  using T = NvRingTile<BM, BN>;
+  __shared__ __attribute__((aligned(16))) uint8_t smem[T::LDS];
+
+  const int lane = threadIdx.x & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int r32 = lane & 31, h = lane >> 5;
+  const int wn0 = (wave >> 1) * (BN / 2), wm0 = (wave & 1) * (BM / 2);
+  const int tiles_n = (p.N + BN - 1) / BN, tiles_m = (p.M + BM - 1) / BM;
+  int tm, tn;
+  tile_coords_gm<8>(blockIdx.x, tiles_m, tiles_n, tm, tn);
+  const int m0 = tm * BM, n0 = tn * BN;
+  const int nkc = p.K / T::KCN;
+  const uint32_t row_b = (uint32_t)p.K >> 1, s_row = (uint32_t)p.K >> 4;
+
+  // descriptors from the tile's first row to the matrix end (rows past M or N read as zero)
+  auto clamp32 = [](uint64_t v) -> uint32_t { return v > 0xFFFFFFFFull ? 0xFFFFFFFFu : (uint32_t)v; };
+  const uint64_t wn = (uint64_t)(p.N - n0), am = (uint64_t)(p.M - m0);
+  const v4i rw = make_rsrc_sgpr(p.w_codes + (int64_t)n0 * row_b, clamp32(wn * row_b));
+  const v4i ra = make_rsrc_sgpr(p.a_codes + (int64_t)m0 * row_b, clamp32(am * row_b));
+  const v4i rws = make_rsrc_sgpr(p.w_scales + (int64_t)n0 * s_row, clamp32(wn * s_row));
+  const v4i ras = make_rsrc_sgpr(p.a_scales + (int64_t)m0 * s_row, clamp32(am * s_row));
+  // code loads: 32 rows of 32 bytes per 1 KB load, lane i -> row i/2, LDS half i&1
+  const uint32_t half_lane = (uint32_t)((lane & 1) ^ ((lane >> 4) & 1)) * 16u;
+  auto off_c = [&](int grp) { return (uint32_t)(32 * grp + (lane >> 1)) * row_b + half_lane; };
+  auto scale_slot = [&](int k, int& urow, bool& is_a) {
+    const int u = wave + 4 * k;
+    is_a = u < T::TA;
+    urow = is_a ? u : min(u - T::TA, T::TW - 1);
+  };
+  const uint32_t lds0 = lds_addr_of(smem);
+  auto issue_one = [&](auto qc, int kc, int st) {
+    constexpr int Q = decltype(qc)::value;
+    const bool live = kc < nkc;
+    const uint32_t sW = lds0 + (uint32_t)(st * T::STAGE);
+    const uint32_t sA = sW + T::W_BYTES, sWS = sA + T::A_BYTES, sAS = sWS + T::WS_BYTES;
+    if constexpr (Q < T::NW) {
+      v4i d = rw;
+      d[2] = live ? d[2] : 0;
+      dma_lds16(d, sW + (uint32_t)((wave * T::NW + Q) * 1024), off_c(wave * T::NW + Q), (uint32_t)kc * 32u);
+    } else if constexpr (Q < T::NW + T::NA) {
+      constexpr int q = Q - T::NW;
+      v4i d = ra;
+      d[2] = live ? d[2] : 0;
+      dma_lds16(d, sA + (uint32_t)((wave * T::NA + q) * 1024), off_c(wave * T::NA + q), (uint32_t)kc * 32u);
+    } else {
+      constexpr int k = Q - T::NW - T::NA;
+      int urow;
+      bool is_a;
+      scale_slot(k, urow, is_a);
+      v4i d = is_a ? ras : rws;
+      d[2] = live ? d[2] : 0;
+      dma_lds4(d, (is_a ? sAS : sWS) + (uint32_t)(urow * 256), (uint32_t)(64 * urow + lane) * s_row,
+               (uint32_t)kc * 4u);
+    }
+  };
+
+  v16f acc[T::FN][T::FM];
+  static_for<T::FN>([&](auto i) { static_for<T::FM>([&](auto j) { acc[i][j] = v16f{}; }); });
+  const int wrow = wn0 + r32, arow = wm0 + r32;  // + 32 i: the half swap (bit 3) is unchanged
+  const uint32_t cpos_w = (uint32_t)(wrow * 32 + ((h ^ ((wrow >> 3) & 1)) << 4));
+  const uint32_t cpos_a = (uint32_t)(arow * 32 + ((h ^ ((arow >> 3) & 1)) << 4));
+  const uint32_t shift = 16u * (uint32_t)h;
+
+  static_for<T::NSTAGE - 1>([&](auto i) {
+    static_for<T::NDMA>([&](auto q) { issue_one(q, (int)decltype(i)::value, (int)decltype(i)::value); });
+  });
+  int st = 0;
+  for (int kc = 0; kc < nkc; ++kc) {
+    wait_vmcnt<(T::NSTAGE - 2) * T::NDMA>();  // chunk kc landed (later ones may be in flight)
+    wait_lds_all();
+    barrier_only();
+    const int stn = st == 0 ? T::NSTAGE - 1 : st - 1;  // the stage of chunk kc - 1, now free
+    const uint8_t* sW = smem + st * T::STAGE;
+    const uint8_t* sA = sW + T::W_BYTES;
+    const uint8_t* sWS = sA + T::A_BYTES;
+    const uint8_t* sAS = sWS + T::WS_BYTES;
+    v4i wc[T::FN], ac[T::FM];
+    v2h wsl[T::FN], wsh[T::FN], asl[T::FM], ash[T::FM];
+#pragma unroll
+    for (int i = 0; i < T::FN; ++i) {
+      wc[i] = *(const v4i*)(sW + cpos_w + i * 32 * 32);
+      const uint32_t sb = *(const uint32_t*)(sWS + (wrow + 32 * i) * 4) >> shift;
+      const v2h s2 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(sb, 1.0f, false);
+      wsl[i] = v2h{s2[0], s2[0]};
+      wsh[i] = v2h{s2[1], s2[1]};
+    }
+#pragma unroll
+    for (int j = 0; j < T::FM; ++j) {
+      ac[j] = *(const v4i*)(sA + cpos_a + j * 32 * 32);
+      const uint32_t sb = *(const uint32_t*)(sAS + (arow + 32 * j) * 4) >> shift;
+      const v2h s2 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(sb, 1.0f, false);
+      asl[j] = v2h{s2[0], s2[0]};
+      ash[j] = v2h{s2[1], s2[1]};
+    }
+    __builtin_amdgcn_sched_barrier(0);
+    static_for<4>([&](auto tc) {
+      constexpr int t = decltype(tc)::value;
+      v8h wf[T::FN], af[T::FM];
+#pragma unroll
+      for (int i = 0; i < T::FN; ++i) wf[i] = nv_dequant8_f16((uint32_t)wc[i][t], t < 2 ? wsl[i] : wsh[i]);
+#pragma unroll
+      for (int j = 0; j < T::FM; ++j) af[j] = nv_dequant8_f16((uint32_t)ac[j][t], t < 2 ? asl[j] : ash[j]);
+      static_for<T::FN>([&](auto i) {
+        static_for<T::FM>([&](auto j) {
+          acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_f16(wf[i], af[j], acc[i][j], 0, 0, 0);
+          constexpr int M = t * T::FN * T::FM + decltype(i)::value * T::FM + decltype(j)::value;
+          constexpr int TOTAL = 4 * T::FN * T::FM;
+          static_for<T::NDMA>([&](auto qc) {
+            if constexpr ((decltype(qc)::value + 1) * TOTAL / T::NDMA - 1 == M) {
+              __builtin_amdgcn_sched_barrier(0);
+              issue_one(qc, kc + T::NSTAGE - 1, stn);
+              __builtin_amdgcn_sched_barrier(0);
+            }
+          });
+        });
+      });
+    });
+    __builtin_amdgcn_sched_barrier(0);
+    st = st == T::NSTAGE - 1 ? 0 : st + 1;
+  }
+
+  if (ring_staged_ok<EPI, OUTF32>(p)) {
+    wait_vmem_all();
+    barrier_only();
+    epilogue_ring_staged<BM, T::FN, T::FM, EPI>(p, acc, smem, n0, m0, wn0, wm0, wave);
+  } else {
+    epilogue_direct<T::FN, T::FM, EPI, OUTF32>(p, acc, n0 + wn0, m0 + wm0);
+  }
+}
+
+// ---------------------------------------------------------------------------------------------
 // low-rank down projection u = bf16(x . down_t^T): one wave per 32 (r) x 32 (m) block
 // ---------------------------------------------------------------------------------------------
 __global__ void __launch_bounds__(64) lowrank_down_kernel(const uint16_t* __restrict__ x,
@@ -933,10 +1120,25 @@ hipError_t launch_gemm_mx(const GemmParams& p, bool act_fp8, hipStream_t s) {
   return run_mx<256, 256, false>(p, s);
 }
 
+template <int EPI>
+static void run_nv_ring(const GemmParams& p, int grid, hipStream_t s) {
+  if constexpr (EPI == EPI_GELU_QUANT) gemm_nv_ring_kernel<256, 128, EPI, false><<<grid, 256, 0, s>>>(p);
+  else if (p.out_f32) gemm_nv_ring_kernel<256, 128, EPI, true><<<grid, 256, 0, s>>>(p);
+  else gemm_nv_ring_kernel<256, 128, EPI, false><<<grid, 256, 0, s>>>(p);
+}
+
+// K % 64 == 0: the ring kernel; otherwise the register-staged kernel (K a multiple of 16).
 hipError_t launch_gemm_nv(const GemmParams& p, hipStream_t s) {
   if (p.M == 0) return hipSuccess;
-  const int tiles = ((p.M + 255) / 256) * ((p.N + 255) / 256);
-  gemm_nv_kernel<256, 256><<<tiles, 256, 0, s>>>(p);
+  if (p.K % 64 == 0) {
+    const int tiles = ((p.M + 255) / 256) * ((p.N + 127) / 128);
+    if (p.epi == EPI_GELU_QUANT) run_nv_ring<EPI_GELU_QUANT>(p, tiles, s);
+    else if (p.epi == EPI_GELU) run_nv_ring<EPI_GELU>(p, tiles, s);
+    else run_nv_ring<EPI_BIAS>(p, tiles, s);
+  } else {
+    const int tiles = ((p.M + 255) / 256) * ((p.N + 255) / 256);
+    gemm_nv_kernel<256, 256><<<tiles, 256, 0, s>>>(p);
+  }
   return hipGetLastError();
 }
 
