@@ -457,19 +457,22 @@ __global__ void __launch_bounds__(256, 1) gemm_mx_kernel(GemmParams p) {
 // lane fetches the global piece that the swizzle puts in its slot.
 template <int BM, int BN, bool AFP8>
 struct RingTile {
-  static_assert((BM == 128 || BM == 256) && BN == 128, "tile sizes");
+  static_assert((BM == 128 || BM == 256) && (BN == 128 || BN == 256), "tile sizes");
+  static constexpr int NWAVES = BN / 32;                 // 2 (m) x BN/64 (n) waves
+  static constexpr int WGS = 256 / BN;                   // workgroups per compute unit
   static constexpr int KCR = 128;
   static constexpr int WROWB = 64, AROWB = AFP8 ? 128 : 64;  // bytes per row and chunk
   static constexpr int W_BYTES = BN * WROWB, A_BYTES = BM * AROWB;
   static constexpr int WS_BYTES = BN * 4, AS_BYTES = BM * 4;
   static constexpr int STAGE = W_BYTES + A_BYTES + WS_BYTES + AS_BYTES;
   static constexpr int NSTAGE = 3;
-  static constexpr int FN = BN / 64, FM = BM / 64;
-  static constexpr int NW = W_BYTES / 4096, NA = A_BYTES / 4096;  // 1 KB loads per wave
+  static constexpr int LDS = NSTAGE * STAGE > BM * BN * 2 ? NSTAGE * STAGE : BM * BN * 2;
+  static constexpr int FN = 2, FM = BM / 64;                       // 32x32 blocks per wave
+  static constexpr int NW = W_BYTES / 1024 / NWAVES, NA = A_BYTES / 1024 / NWAVES;  // 1 KB loads
   static constexpr int TA = BM / 64, TW = BN / 64;                  // 256-byte scale loads
-  static constexpr int NS = (TA + TW + 3) / 4;                      // scale loads per wave
+  static constexpr int NS = (TA + TW + NWAVES - 1) / NWAVES;        // scale loads per wave
   static constexpr int NDMA = NW + NA + NS;
-  static_assert(NSTAGE * STAGE <= 80 * 1024, "two workgroups per compute unit");
+  static_assert(LDS * WGS <= 160 * 1024, "LDS of the workgroups of a compute unit");
 };
 
 template <int N>
@@ -496,18 +499,20 @@ __device__ __forceinline__ void tile_coords_gm(int b, int tiles_m, int tiles_n, 
   tn = in / rows;
 }
 
-// BF16 output of a BM x 128 ring-kernel tile through LDS (the ring is idle once the K loop is
-// done): the tile is written as BM rows of 256 bytes, 16-byte chunks XOR-swizzled by the row,
-// then stored as whole 256-byte row segments, four rows per instruction, instead of 8-byte
-// pieces of 32 rows.  Waves hold (BM/2) x 64 sub-tiles (2 x 2 waves).
+// BF16 output of a BM x BN ring-kernel tile through LDS (the ring is idle once the K loop is
+// done): the tile is written as BM rows of 2 BN bytes, 16-byte chunks XOR-swizzled by the row,
+// then stored as whole row segments (four 256-byte or two 512-byte rows per instruction)
+// instead of 8-byte pieces of 32 rows.  Waves hold (BM/2) x 64 sub-tiles (2 x BN/64 waves).
 template <int EPI, bool OUTF32>
 __device__ __forceinline__ bool ring_staged_ok(const GemmParams& p) {
   return EPI != EPI_GELU_QUANT && !OUTF32 && (p.N % 8) == 0 && (p.ld_out % 8) == 0 &&
          (((uintptr_t)p.out) & 15) == 0;
 }
-template <int BM, int FN, int FM, int EPI>
+template <int BM, int BN, int FN, int FM, int EPI>
 __device__ __forceinline__ void epilogue_ring_staged(const GemmParams& p, v16f (&acc)[FN][FM], uint8_t* smem,
                                                      int n0, int m0, int wn0, int wm0, int wave) {
+  constexpr int RB = BN * 2, NCH = RB / 16;  // bytes and 16-byte chunks per staged row
+  constexpr int NWAVES = BN / 32, RPI = 64 / NCH;  // waves; rows per store instruction
   const int lane = lane_id();
   const int r32 = lane & 31, h = lane >> 5;
   static_for<FN>([&](auto i) {
@@ -523,33 +528,33 @@ __device__ __forceinline__ void epilogue_ring_staged(const GemmParams& p, v16f (
         const int c = (wn0 + 32 * i) / 8 + g;  // 16-byte chunk of the row (8 BF16)
         const uint32_t lo = f32_to_bf16_rne(v[4 * g]) | (f32_to_bf16_rne(v[4 * g + 1]) << 16);
         const uint32_t hi = f32_to_bf16_rne(v[4 * g + 2]) | (f32_to_bf16_rne(v[4 * g + 3]) << 16);
-        *(uint2*)(smem + row * 256 + ((c ^ (row & 15)) << 4) + 8 * h) = make_uint2(lo, hi);
+        *(uint2*)(smem + row * RB + ((c ^ (row & (NCH - 1))) << 4) + 8 * h) = make_uint2(lo, hi);
       }
     });
   });
   wait_lds_all();
   barrier_only();
-  const int c = lane & 15;
+  const int c = lane % NCH;
   const int n = n0 + 8 * c;
 #pragma unroll 4
-  for (int it = 0; it < BM / 16; ++it) {
-    const int row = wave * (BM / 4) + 4 * it + (lane >> 4);
-    const uint4 d = *(const uint4*)(smem + row * 256 + ((c ^ (row & 15)) << 4));
+  for (int it = 0; it < BM / NWAVES / RPI; ++it) {
+    const int row = wave * (BM / NWAVES) + RPI * it + lane / NCH;
+    const uint4 d = *(const uint4*)(smem + row * RB + ((c ^ (row & (NCH - 1))) << 4));
     const int m = m0 + row;
     if (m < p.M && n < p.N) *(uint4*)((uint16_t*)p.out + (int64_t)m * p.ld_out + n) = d;
   }
 }
 
 template <int BM, int BN, bool AFP8, int EPI, bool OUTF32, bool LR>
-__global__ void __launch_bounds__(256, 2) gemm_mx_ring_kernel(GemmParams p) {
+__global__ void __launch_bounds__(BN * 2, 256 / BN) gemm_mx_ring_kernel(GemmParams p) {
   using T = RingTile<BM, BN, AFP8>;
   typedef typename std::conditional<AFP8, v8i, v4i>::type AV;
-  __shared__ __attribute__((aligned(16))) uint8_t smem[T::NSTAGE * T::STAGE];
+  __shared__ __attribute__((aligned(16))) uint8_t smem[T::LDS];
 
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int r32 = lane & 31, h = lane >> 5;
-  const int wn0 = (wave >> 1) * (BN / 2), wm0 = (wave & 1) * (BM / 2);
+  const int wn0 = (wave >> 1) * 64, wm0 = (wave & 1) * (BM / 2);
   const int tiles_n = (p.N + BN - 1) / BN, tiles_m = (p.M + BM - 1) / BM;
   int tm, tn;
   tile_coords_gm<8>(blockIdx.x, tiles_m, tiles_n, tm, tn);
@@ -601,7 +606,7 @@ __global__ void __launch_bounds__(256, 2) gemm_mx_ring_kernel(GemmParams p) {
   // scale load k of this wave: 64 rows of A scales (u < TA) or of W scales; surplus slots repeat
   // the last W load (the same bytes to the same place)
   auto scale_slot = [&](int k, int& urow, bool& is_a) {
-    const int u = wave + 4 * k;
+    const int u = wave + T::NWAVES * k;
     is_a = u < T::TA;
     urow = is_a ? u : min(u - T::TA, T::TW - 1);
   };
@@ -640,31 +645,27 @@ __global__ void __launch_bounds__(256, 2) gemm_mx_ring_kernel(GemmParams p) {
   const int wrow = wn0 + r32, arow = wm0 + r32;  // + 32 i: the XOR term is unchanged
   const uint32_t shift = 16u * (uint32_t)h;
 
-  issue(0, 0);
-  issue(1, 1);
-  int st = 0;
-  for (int kc = 0; kc < nkc; ++kc) {
-    wait_vmcnt<T::NDMA>();  // this wave's loads of chunk kc landed (chunk kc + 1 may be in flight)
-    wait_lds_all();
-    barrier_only();         // every wave's loads of chunk kc landed; stage kc - 1 is free
-    const int st2 = st == 0 ? 2 : st - 1;
-    const uint8_t* sW = smem + st * T::STAGE;
-    const uint8_t* sA = sW + T::W_BYTES;
-    const uint8_t* sWS = sA + T::A_BYTES;
-    const uint8_t* sAS = sWS + T::WS_BYTES;
+  // The fragments of a chunk (both MFMA steps) and its scale dwords, read from stage `stg`.
+  struct Frags {
     uint32_t wsc[T::FN], asc[T::FM];
     v4i wf[2][T::FN];
     AV af[2][T::FM];
+  };
+  auto read_chunk = [&](int stg, Frags& f) {
+    const uint8_t* sW = smem + stg * T::STAGE;
+    const uint8_t* sA = sW + T::W_BYTES;
+    const uint8_t* sWS = sA + T::A_BYTES;
+    const uint8_t* sAS = sWS + T::WS_BYTES;
 #pragma unroll
-    for (int i = 0; i < T::FN; ++i) wsc[i] = *(const uint32_t*)(sWS + (wrow + 32 * i) * 4) >> shift;
+    for (int i = 0; i < T::FN; ++i) f.wsc[i] = *(const uint32_t*)(sWS + (wrow + 32 * i) * 4) >> shift;
 #pragma unroll
-    for (int j = 0; j < T::FM; ++j) asc[j] = *(const uint32_t*)(sAS + (arow + 32 * j) * 4) >> shift;
+    for (int j = 0; j < T::FM; ++j) f.asc[j] = *(const uint32_t*)(sAS + (arow + 32 * j) * 4) >> shift;
 #pragma unroll
     for (int s = 0; s < 2; ++s) {
 #pragma unroll
       for (int i = 0; i < T::FN; ++i) {
         const int row = wrow + 32 * i;
-        wf[s][i] = *(const v4i*)(sW + row * 64 + (((2 * h + s) ^ ((row >> 2) & 3)) << 4));
+        f.wf[s][i] = *(const v4i*)(sW + row * 64 + (((2 * h + s) ^ ((row >> 2) & 3)) << 4));
       }
 #pragma unroll
       for (int j = 0; j < T::FM; ++j) {
@@ -673,40 +674,73 @@ __global__ void __launch_bounds__(256, 2) gemm_mx_ring_kernel(GemmParams p) {
           const int g = (row >> 1) & 7;
           const v4i d0 = *(const v4i*)(sA + row * 128 + (((2 * s + h) ^ g) << 4));
           const v4i d1 = *(const v4i*)(sA + row * 128 + (((4 + 2 * s + h) ^ g) << 4));
-          af[s][j] = v8i{d0[0], d0[1], d0[2], d0[3], d1[0], d1[1], d1[2], d1[3]};
+          f.af[s][j] = v8i{d0[0], d0[1], d0[2], d0[3], d1[0], d1[1], d1[2], d1[3]};
         } else {
-          af[s][j] = *(const v4i*)(sA + row * 64 + (((2 * h + s) ^ ((row >> 2) & 3)) << 4));
+          f.af[s][j] = *(const v4i*)(sA + row * 64 + (((2 * h + s) ^ ((row >> 2) & 3)) << 4));
         }
       }
     }
-    __builtin_amdgcn_sched_barrier(0);
-    // the next chunk's loads, one after every two MFMAs: a burst of them would fill the
-    // vector-memory queue and hold up the MFMA issue behind it
-    static_for<2>([&](auto sc) {
-      constexpr int S = decltype(sc)::value;
-      static_for<T::FN>([&](auto i) {
-        static_for<T::FM>([&](auto j) {
-          if constexpr (AFP8)
-            acc[i][j] = mfma_scale_32x32x64_f4f8(wf[S][i], af[S][j], acc[i][j], 4, 0, S, (int)wsc[i], S, (int)asc[j]);
-          else
-            acc[i][j] = mfma_scale_32x32x64_f4f4(wf[S][i], af[S][j], acc[i][j], 4, 4, S, (int)wsc[i], S, (int)asc[j]);
-          constexpr int M = S * T::FN * T::FM + decltype(i)::value * T::FM + decltype(j)::value;
-          constexpr int TOTAL = 2 * T::FN * T::FM;
-          static_assert(TOTAL >= T::NDMA, "one load slot per MFMA at most");
-          // load q goes after MFMA (q + 1) * TOTAL / NDMA - 1 (distinct slots, the last MFMA last)
-          static_for<T::NDMA>([&](auto qc) {
-            constexpr int Q = decltype(qc)::value;
-            if constexpr ((Q + 1) * TOTAL / T::NDMA - 1 == M) {
-              __builtin_amdgcn_sched_barrier(0);
-              issue_one(qc, kc + 2, st2);
-              __builtin_amdgcn_sched_barrier(0);
-            }
-          });
+  };
+  // The MFMAs of step S, with the loads of chunk `dkc` into stage `dst` that fall in this step:
+  // load q goes after MFMA (q + 1) * TOTAL / NDMA - 1 of the chunk's TOTAL (distinct slots; a
+  // burst of loads would fill the vector-memory queue and hold up the MFMA issue behind it).
+  constexpr int TOTAL = 2 * T::FN * T::FM;
+  static_assert(TOTAL >= T::NDMA, "one load slot per MFMA at most");
+  auto mma_step = [&](auto sc, const Frags& f, int dkc, int dst) {
+    constexpr int S = decltype(sc)::value;
+    static_for<T::FN>([&](auto i) {
+      static_for<T::FM>([&](auto j) {
+        if constexpr (AFP8)
+          acc[i][j] = mfma_scale_32x32x64_f4f8(f.wf[S][i], f.af[S][j], acc[i][j], 4, 0, S, (int)f.wsc[i], S, (int)f.asc[j]);
+        else
+          acc[i][j] = mfma_scale_32x32x64_f4f4(f.wf[S][i], f.af[S][j], acc[i][j], 4, 4, S, (int)f.wsc[i], S, (int)f.asc[j]);
+        constexpr int M = S * T::FN * T::FM + decltype(i)::value * T::FM + decltype(j)::value;
+        static_for<T::NDMA>([&](auto qc) {
+          if constexpr ((decltype(qc)::value + 1) * TOTAL / T::NDMA - 1 == M) {
+            __builtin_amdgcn_sched_barrier(0);
+            issue_one(qc, dkc, dst);
+            __builtin_amdgcn_sched_barrier(0);
+          }
         });
       });
     });
+  };
+  // loads issued during step 0 (those of a chunk that precede its step-1 MFMAs)
+  constexpr int LOADS_S0 = [] {
+    int n = 0;
+    for (int q = 0; q < T::NDMA; ++q) n += (q + 1) * TOTAL / T::NDMA - 1 < TOTAL / 2 ? 1 : 0;
+    return n;
+  }();
+
+  // Software pipeline over chunks.  Iteration kc: step-0 MFMAs of chunk kc (its fragments were
+  // read last iteration) while chunk kc + 2 starts loading into the stage of chunk kc - 1; then
+  // the barrier that publishes chunk kc + 1 -- its wait overlaps the MFMAs already in the pipe --
+  // and the reads of chunk kc + 1 under the step-1 MFMAs of chunk kc.  A stage is refilled only
+  // after the barrier that follows every wave's last read of it (each wave drains its LDS reads
+  // before each barrier).
+  issue(0, 0);
+  issue(1, 1);
+  wait_vmcnt<T::NDMA>();
+  barrier_only();
+  Frags cur;
+  read_chunk(0, cur);
+  int st = 0;  // stage of chunk kc
+  for (int kc = 0; kc < nkc; ++kc) {
+    const int st1 = st == 2 ? 0 : st + 1;  // chunk kc + 1
+    const int st2 = st == 0 ? 2 : st - 1;  // chunk kc + 2 (the stage of chunk kc - 1)
     __builtin_amdgcn_sched_barrier(0);
-    st = st == 2 ? 0 : st + 1;
+    mma_step(std::integral_constant<int, 0>{}, cur, kc + 2, st2);
+    __builtin_amdgcn_sched_barrier(0);
+    wait_vmcnt<LOADS_S0>();  // chunk kc + 1 landed (only chunk kc + 2's first loads may fly)
+    wait_lds_all();          // this wave's reads of chunk kc are done
+    barrier_only();
+    Frags nxt;
+    read_chunk(st1, nxt);    // past the last chunk this reads a stale stage: unused
+    __builtin_amdgcn_sched_barrier(0);
+    mma_step(std::integral_constant<int, 1>{}, cur, kc + 2, st2);
+    __builtin_amdgcn_sched_barrier(0);
+    cur = nxt;
+    st = st1;
   }
 
   if (LR) {
@@ -717,10 +751,10 @@ __global__ void __launch_bounds__(256, 2) gemm_mx_ring_kernel(GemmParams p) {
     });
   }
   if (ring_staged_ok<EPI, OUTF32>(p)) {
-    static_assert(BM * BN * 2 <= T::NSTAGE * T::STAGE, "output tile fits the ring");
+    static_assert(BM * BN * 2 <= T::LDS, "output tile fits the ring");
     wait_vmem_all();  // the (empty) loads issued for the chunks past the end have landed
     barrier_only();   // every wave is done with the ring
-    epilogue_ring_staged<BM, T::FN, T::FM, EPI>(p, acc, smem, n0, m0, wn0, wm0, wave);
+    epilogue_ring_staged<BM, BN, T::FN, T::FM, EPI>(p, acc, smem, n0, m0, wn0, wm0, wave);
   } else {
     epilogue_direct<T::FN, T::FM, EPI, OUTF32>(p, acc, n0 + wn0, m0 + wm0);
   }
@@ -1040,7 +1074,7 @@ __global__ void __launch_bounds__(256, 2) gemm_nv_ring_kernel(GemmParams p) {
   if (ring_staged_ok<EPI, OUTF32>(p)) {
     wait_vmem_all();
     barrier_only();
-    epilogue_ring_staged<BM, T::FN, T::FM, EPI>(p, acc, smem, n0, m0, wn0, wm0, wave);
+    epilogue_ring_staged<BM, BN, T::FN, T::FM, EPI>(p, acc, smem, n0, m0, wn0, wm0, wave);
   } else {
     epilogue_direct<T::FN, T::FM, EPI, OUTF32>(p, acc, n0 + wn0, m0 + wm0);
   }
@@ -1082,7 +1116,7 @@ __global__ void __launch_bounds__(64) lowrank_down_kernel(const uint16_t* __rest
 // ---------------------------------------------------------------------------------------------
 template <int BM, int BN, bool AFP8, int EPI, bool OUTF32, bool LR>
 static void run_ring(const GemmParams& p, int grid, hipStream_t s) {
-  gemm_mx_ring_kernel<BM, BN, AFP8, EPI, OUTF32, LR><<<grid, 256, 0, s>>>(p);
+  gemm_mx_ring_kernel<BM, BN, AFP8, EPI, OUTF32, LR><<<grid, BN * 2, 0, s>>>(p);
 }
 
 // Every (epilogue, output type, low-rank) combination of the ring kernel.
@@ -1104,9 +1138,13 @@ static void run_ring_e(const GemmParams& p, int grid, hipStream_t s) {
 template <int BM, int BN, bool AFP8>
 static hipError_t run_mx(const GemmParams& p, hipStream_t s) {
   if (p.K % 128 == 0) {
-    const int tiles = ((p.M + BM - 1) / BM) * ((p.N + 127) / 128);
-    if (p.R > 0) run_ring_e<BM, 128, AFP8, true>(p, tiles, s);
-    else run_ring_e<BM, 128, AFP8, false>(p, tiles, s);
+#ifndef MX_RING_BN
+#define MX_RING_BN 128
+#endif
+    constexpr int RBN = AFP8 ? 128 : MX_RING_BN;
+    const int tiles = ((p.M + BM - 1) / BM) * ((p.N + RBN - 1) / RBN);
+    if (p.R > 0) run_ring_e<BM, RBN, AFP8, true>(p, tiles, s);
+    else run_ring_e<BM, RBN, AFP8, false>(p, tiles, s);
   } else {
     const int tiles = ((p.M + BM - 1) / BM) * ((p.N + BN - 1) / BN);
     gemm_mx_kernel<BM, BN, AFP8, false><<<tiles, 256, 0, s>>>(p);

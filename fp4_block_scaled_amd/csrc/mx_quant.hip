@@ -18,11 +18,22 @@
 
 namespace mxk {
 
+typedef __bf16 bf2v __attribute__((ext_vector_type(2)));
+typedef uint16_t u16x2 __attribute__((ext_vector_type(2)));
+typedef short i16x2 __attribute__((ext_vector_type(2)));
+
 // ---------------------------------------------------------------------------------------------
 // MXFP4 / MXFP8
 // ---------------------------------------------------------------------------------------------
 // One thread's 8 elements of a 32-element group (the group's four threads are one DPP quad):
 // the group's scale byte and the thread's codes, 4 bytes (E2M1, lo) or 8 bytes (E4M3, lo, hi).
+// The element rounding is the gfx950 scaled conversion (V_CVT_SCALEF32_PK_FP4_BF16 /
+// _PK_FP8_BF16), which rounds |x| / 2^e to nearest-even on the element grid and keeps the sign;
+// it was checked exhaustively against that rule on every BF16 value and scale exponent
+// (subnormals included).  Two differences from the rule are handled here: E4M3 overflow gives
+// the NaN code instead of saturating, so magnitudes are first clamped to 448 * 2^e (they can
+// exceed it only by less than one binade, q < 512); and a NaN/Inf in the group gives all-zero
+// codes with scale 0xFF.
 template <int ELEM>  // 0: E2M1 (emax 2), 1: E4M3 (emax 8)
 __device__ __forceinline__ void quant_mx8(const uint4 v, uint32_t& lo, uint32_t& hi, uint32_t& sbyte) {
   uint32_t w[4] = {v.x, v.y, v.z, v.w};
@@ -39,24 +50,39 @@ __device__ __forceinline__ void quant_mx8(const uint4 v, uint32_t& lo, uint32_t&
   const int emax = ELEM == 0 ? 2 : 8;
   int e = E - 127 - emax;            // floor(log2 amax) - emax (subnormal/zero: clamped below)
   if (e < -127) e = -127;
-  const float inv = __uint_as_float((uint32_t)(127 - e) << 23);  // 2^-e, a normal binary32
-  lo = hi = 0;
+  // 2^e as a binary32 (2^-127 is subnormal)
+  const float scale = __uint_as_float(e >= -126 ? (uint32_t)(127 + e) << 23 : 0x00400000u);
+  bf2v b[4];
+  if (ELEM == 1) {
+    const uint32_t lim = (uint32_t)((e + 135) << 7 | 0x60);  // BF16 bits of 448 * 2^e
+    const u16x2 lim2 = {(uint16_t)lim, (uint16_t)lim};
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      u16x2 mag;
+      const uint32_t m = w[i] & 0x7FFF7FFFu;
+      __builtin_memcpy(&mag, &m, 4);
+      mag = __builtin_elementwise_min(mag, lim2);
+      uint32_t c;
+      __builtin_memcpy(&c, &mag, 4);
+      w[i] = c | (w[i] & 0x80008000u);
+    }
+  }
+#pragma unroll
+  for (int i = 0; i < 4; ++i) __builtin_memcpy(&b[i], &w[i], 4);
   if (ELEM == 0) {
-#pragma unroll
-    for (int i = 0; i < 8; ++i) {
-      uint32_t b = (w[i >> 1] >> ((i & 1) * 16)) & 0xFFFFu;
-      float q = bf16_to_f32(b & 0x7FFFu) * inv;
-      lo |= (e2m1_code(q) | ((b >> 12) & 8u)) << (4 * i);
-    }
+    uint32_t r = __builtin_amdgcn_cvt_scalef32_pk_fp4_bf16(0u, b[0], scale, 0);
+    r = __builtin_amdgcn_cvt_scalef32_pk_fp4_bf16(r, b[1], scale, 1);
+    r = __builtin_amdgcn_cvt_scalef32_pk_fp4_bf16(r, b[2], scale, 2);
+    r = __builtin_amdgcn_cvt_scalef32_pk_fp4_bf16(r, b[3], scale, 3);
+    lo = r;
+    hi = 0;
   } else {
-#pragma unroll
-    for (int i = 0; i < 8; ++i) {
-      uint32_t b = (w[i >> 1] >> ((i & 1) * 16)) & 0xFFFFu;
-      float q = bf16_to_f32(b & 0x7FFFu) * inv;
-      uint32_t c = e4m3_code(q) | ((b >> 8) & 0x80u);
-      if (i < 4) lo |= c << (8 * i);
-      else hi |= c << (8 * (i - 4));
-    }
+    i16x2 r0 = __builtin_amdgcn_cvt_scalef32_pk_fp8_bf16(i16x2{0, 0}, b[0], scale, false);
+    r0 = __builtin_amdgcn_cvt_scalef32_pk_fp8_bf16(r0, b[1], scale, true);
+    i16x2 r1 = __builtin_amdgcn_cvt_scalef32_pk_fp8_bf16(i16x2{0, 0}, b[2], scale, false);
+    r1 = __builtin_amdgcn_cvt_scalef32_pk_fp8_bf16(r1, b[3], scale, true);
+    __builtin_memcpy(&lo, &r0, 4);
+    __builtin_memcpy(&hi, &r1, 4);
   }
   if (bad) lo = hi = 0;
   sbyte = bad ? 0xFFu : (uint32_t)(e + 127);
@@ -83,31 +109,45 @@ __global__ void __launch_bounds__(256) quant_mx_kernel(const uint16_t* __restric
   }
 }
 
-// Tiled output: a workgroup quantizes 16 rows x 128 columns per step (16 threads per row, 8
-// elements each), which is one 1 KB FP4 code tile (two FP8 tiles) and a quarter of a scale tile.
-// Rows from `rows` to the padded count quantize zeros (zero codes, scale byte 0).
+// Tiled output: a workgroup quantizes 16 rows x 512 columns per step (16 threads per row, four
+// 128-column chunks of 8 elements each), so each row is read as 1 KB contiguous and each chunk
+// is written as one 1 KB FP4 code tile (two FP8 tiles) and a quarter of a scale tile.  The four
+// loads of a thread are issued before any is used.  Rows from `rows` to the padded count
+// quantize zeros (zero codes, scale byte 0).
 template <int ELEM>
 __global__ void __launch_bounds__(256) quant_mx_tiled_kernel(const uint16_t* __restrict__ x,
                                                               int64_t rows, int64_t cols, int64_t ld,
                                                               uint8_t* __restrict__ codes,
                                                               uint8_t* __restrict__ scales) {
+  constexpr int IT = 4;
   const int64_t nkc = cols >> 7;
-  const int64_t items = (tiled_rows(rows) >> 4) * nkc;
+  const int64_t nkg = (nkc + IT - 1) / IT;  // groups of IT chunks per row block
+  const int64_t items = (tiled_rows(rows) >> 4) * nkg;
   const int rl = threadIdx.x >> 4, c8 = threadIdx.x & 15;
   const int g4 = c8 >> 2, part = c8 & 3;
   for (int64_t it = blockIdx.x; it < items; it += gridDim.x) {
-    const int64_t rb = it / nkc, kb = it - rb * nkc;
+    const int64_t rb = it / nkg, kg = it - rb * nkg;
     const int64_t r = rb * 16 + rl;
-    const uint4 v = r < rows ? load_stream16(x + r * ld + kb * 128 + c8 * 8) : make_uint4(0, 0, 0, 0);
-    uint32_t lo, hi, sbyte;
-    quant_mx8<ELEM>(v, lo, hi, sbyte);
-    if (ELEM == 0) {
-      *(uint32_t*)(codes + tiled_fp4_off(r, kb, g4, nkc) + part * 4) = lo;
-    } else {
-      // the group's 32 bytes are pieces 2 g4 and 2 g4 + 1; this thread's 8 bytes are half a piece
-      *(uint2*)(codes + tiled_fp8_off(r, kb, 2 * g4 + (part >> 1), nkc) + (part & 1) * 8) = make_uint2(lo, hi);
+    uint4 v[IT];
+#pragma unroll
+    for (int u = 0; u < IT; ++u) {
+      const int64_t kb = kg * IT + u;
+      v[u] = r < rows && kb < nkc ? load_stream16(x + r * ld + kb * 128 + c8 * 8) : make_uint4(0, 0, 0, 0);
     }
-    if (part == 0) scales[tiled_scale_off(r, kb, nkc) + g4] = (uint8_t)sbyte;
+#pragma unroll
+    for (int u = 0; u < IT; ++u) {
+      const int64_t kb = kg * IT + u;
+      if (kb >= nkc) break;  // uniform: the last group of a row block may be partial
+      uint32_t lo, hi, sbyte;
+      quant_mx8<ELEM>(v[u], lo, hi, sbyte);
+      if (ELEM == 0) {
+        *(uint32_t*)(codes + tiled_fp4_off(r, kb, g4, nkc) + part * 4) = lo;
+      } else {
+        // the group's 32 bytes are pieces 2 g4 and 2 g4 + 1; this thread's 8 bytes are half a piece
+        *(uint2*)(codes + tiled_fp8_off(r, kb, 2 * g4 + (part >> 1), nkc) + (part & 1) * 8) = make_uint2(lo, hi);
+      }
+      if (part == 0) scales[tiled_scale_off(r, kb, nkc) + g4] = (uint8_t)sbyte;
+    }
   }
 }
 
@@ -326,9 +366,9 @@ hipError_t launch_quant_mx(const uint16_t* x, int64_t rows, int64_t cols, int64_
 
 hipError_t launch_quant_mx_tiled(const uint16_t* x, int64_t rows, int64_t cols, int64_t ld, int elem,
                                  uint8_t* codes, uint8_t* scales, hipStream_t s) {
-  const int64_t items = (tiled_rows(rows) / 16) * (cols / 128);
+  const int64_t items = (tiled_rows(rows) / 16) * ((cols / 128 + 3) / 4);
   if (items == 0) return hipSuccess;
-  const int grid = (int)(items < 256 * 64 ? items : 256 * 64);
+  const int grid = (int)(items < 256 * 32 ? items : 256 * 32);
   if (elem == 0)
     quant_mx_tiled_kernel<0><<<grid, 256, 0, s>>>(x, rows, cols, ld, codes, scales);
   else

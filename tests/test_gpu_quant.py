@@ -47,6 +47,22 @@ def test_mx_quantizer_exhaustive_bf16(mx, fmt, elem):
         np.testing.assert_array_equal(c, ref_c, err_msg=f"codes, anchor {a:#06x}")
 
 
+@pytest.mark.parametrize("fmt,elem", [("mxfp4", O.E2M1), ("mxfp8", O.E4M3)])
+def test_mx_quantizer_exhaustive_over_scale_exponents(mx, fmt, elem):
+    """Every BF16 pattern under block maxima 1.5 * 2^k swept across the exponent range: the
+    element rounding runs on the hardware scaled conversion, so every scale exponent it can be
+    given is checked against the oracle (q = |x| 2^-e covers [0, 8) / [0, 512) in each case)."""
+    for E in range(1, 255, 6):
+        block = np.zeros((len(ALL), 32), dtype=np.uint16)
+        block[:, 0] = ALL
+        block[:, 1] = (E << 7) | 0x40
+        block[:, 9] = ALL[::-1] ^ 0x8000
+        ref_c, ref_s = O.quantize_mx_bf16(block, elem)
+        c, s = _gpu_quant(mx, block, fmt)
+        np.testing.assert_array_equal(s, ref_s, err_msg=f"scales, anchor exponent {E}")
+        np.testing.assert_array_equal(c, ref_c, err_msg=f"codes, anchor exponent {E}")
+
+
 @pytest.mark.parametrize("name,fmt,elem", [("mxfp4_worked_blocks.json", "mxfp4", O.E2M1),
                                            ("mxfp8_worked_blocks.json", "mxfp8", O.E4M3)])
 def test_mx_worked_blocks_on_gpu(mx, name, fmt, elem):
