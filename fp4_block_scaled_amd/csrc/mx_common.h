@@ -22,6 +22,17 @@ typedef _Float16 v8h __attribute__((ext_vector_type(8)));
 __device__ __forceinline__ float bf16_to_f32(uint32_t b16) { return __uint_as_float(b16 << 16); }
 
 // fp32 -> bf16, round to nearest even (NaN -> quiet NaN, overflow -> inf).
+// Two binary32 values rounded to nearest-even BF16, packed lo | hi << 16: gfx950's
+// V_CVT_PK_BF16_F32 (probed against the RNE rule on 8.4M values incl. ties, subnormals and
+// overflow; a NaN stays a NaN).
+typedef float v2f32 __attribute__((ext_vector_type(2)));
+typedef __bf16 v2bf16 __attribute__((ext_vector_type(2)));
+__device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
+  const v2bf16 r = __builtin_convertvector(v2f32{lo, hi}, v2bf16);
+  uint32_t u;
+  __builtin_memcpy(&u, &r, 4);
+  return u;
+}
 __device__ __forceinline__ uint32_t f32_to_bf16_rne(float f) {
   uint32_t u = __float_as_uint(f);
   if ((u & 0x7FFFFFFFu) > 0x7F800000u) return 0x7FC0u;
@@ -111,6 +122,9 @@ __device__ __forceinline__ uint32_t lds_addr_of(T* p) {
 
 __device__ __forceinline__ uint32_t load4(__amdgpu_buffer_rsrc_t r, uint32_t off) {
   return (uint32_t)__builtin_amdgcn_raw_buffer_load_b32(r, (int)off, 0, 0);
+}
+__device__ __forceinline__ uint32_t load2(__amdgpu_buffer_rsrc_t r, uint32_t off) {
+  return (uint32_t)__builtin_amdgcn_raw_buffer_load_b16(r, (int)off, 0, 0);
 }
 __device__ __forceinline__ uint32_t load1(__amdgpu_buffer_rsrc_t r, uint32_t off) {
   return (uint32_t)__builtin_amdgcn_raw_buffer_load_b8(r, (int)off, 0, 0);

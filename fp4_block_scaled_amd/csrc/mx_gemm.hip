@@ -70,18 +70,20 @@ __device__ __forceinline__ void tile_coords(int b, int tiles_m, int tiles_n, int
 // Bias of one 32-column block: the 16 values at this lane's n positions (zero without bias).
 __device__ __forceinline__ void load_bias16(const GemmParams& p, int nb, float (&b)[16]) {
   const int h = lane_id() >> 5;
+  // buffer loads: columns past N (and a missing bias) read as zero, without branches
+  const __amdgpu_buffer_rsrc_t rb = make_rsrc(p.bias, p.bias ? (uint32_t)p.N * 2u : 0u);
 #pragma unroll
   for (int a = 0; a < 4; ++a) {
-    const int n = nb + 8 * a + 4 * h;
-    if (p.bias && n + 3 < p.N) {
-      const uint2 u = *(const uint2*)(p.bias + n);
+    const uint32_t off = (uint32_t)(nb + 8 * a + 4 * h) * 2u;
+    if ((p.N & 3) == 0) {  // whole runs of 4 in or out of range
+      const uint2 u = load8(rb, off);
       b[4 * a + 0] = f16_to_f32(u.x & 0xFFFFu);
       b[4 * a + 1] = f16_to_f32(u.x >> 16);
       b[4 * a + 2] = f16_to_f32(u.y & 0xFFFFu);
       b[4 * a + 3] = f16_to_f32(u.y >> 16);
     } else {
 #pragma unroll
-      for (int i = 0; i < 4; ++i) b[4 * a + i] = (p.bias && n + i < p.N) ? f16_to_f32(p.bias[n + i]) : 0.0f;
+      for (int i = 0; i < 4; ++i) b[4 * a + i] = f16_to_f32(load2(rb, off + 2u * i));
     }
   }
 }
@@ -118,12 +120,11 @@ __device__ __forceinline__ void store_block(const GemmParams& p, const float (&v
       }
     } else {
       uint16_t* o = (uint16_t*)p.out + (int64_t)m * p.ld_out + n;
-      const uint32_t b0 = f32_to_bf16_rne(v[4 * a]), b1 = f32_to_bf16_rne(v[4 * a + 1]);
-      const uint32_t b2 = f32_to_bf16_rne(v[4 * a + 2]), b3 = f32_to_bf16_rne(v[4 * a + 3]);
+      const uint32_t p01 = pack_bf16x2(v[4 * a], v[4 * a + 1]), p23 = pack_bf16x2(v[4 * a + 2], v[4 * a + 3]);
       if (n + 3 < p.N) {
-        *(uint2*)o = make_uint2(b0 | (b1 << 16), b2 | (b3 << 16));
+        *(uint2*)o = make_uint2(p01, p23);
       } else {
-        const uint32_t bb[4] = {b0, b1, b2, b3};
+        const uint32_t bb[4] = {p01 & 0xFFFFu, p01 >> 16, p23 & 0xFFFFu, p23 >> 16};
 #pragma unroll
         for (int i = 0; i < 4; ++i)
           if (n + i < p.N) o[i] = (uint16_t)bb[i];
@@ -526,8 +527,8 @@ __device__ __forceinline__ void epilogue_ring_staged(const GemmParams& p, v16f (
 #pragma unroll
       for (int g = 0; g < 4; ++g) {
         const int c = (wn0 + 32 * i) / 8 + g;  // 16-byte chunk of the row (8 BF16)
-        const uint32_t lo = f32_to_bf16_rne(v[4 * g]) | (f32_to_bf16_rne(v[4 * g + 1]) << 16);
-        const uint32_t hi = f32_to_bf16_rne(v[4 * g + 2]) | (f32_to_bf16_rne(v[4 * g + 3]) << 16);
+        const uint32_t lo = pack_bf16x2(v[4 * g], v[4 * g + 1]);
+        const uint32_t hi = pack_bf16x2(v[4 * g + 2], v[4 * g + 3]);
         *(uint2*)(smem + row * RB + ((c ^ (row & (NCH - 1))) << 4) + 8 * h) = make_uint2(lo, hi);
       }
     });
