@@ -195,16 +195,16 @@ def bench_variant(args, torch, mx, synth):
         w2q = mx.quantize(to_dev(synth.bits16(synth.to_bf16(wl.weight2())), torch.bfloat16), "mxfp4",
                           layout="tiled")
         b2 = to_dev(synth.bits16(synth.to_f16(wl.bias2())), torch.float16)
-        h = mx.empty_qmatrix(M, N, "mxfp4")
+        h = mx.empty_qmatrix(M, N, "mxfp4", layout="tiled")  # FFN0 writes H in the GEMM layout
         out = torch.empty((M, wl.N2), dtype=torch.bfloat16, device="cuda")
         ws = torch.empty(mx.linear_workspace_bytes(M, K, "mxfp4"), dtype=torch.uint8, device="cuda")
-        step = lambda: (mx.linear(a, wq, bias, epilogue="bias_gelu_quant_mxfp4", out=h, workspace=ws),
+        step = lambda: (mx.linear(a, wq, bias, epilogue="bias_gelu_quant_mxfp4_tiled", out=h, workspace=ws),
                         mx.linear_q(h, w2q, b2, out=out))
         flops = 2.0 * M * K * N + 2.0 * M * N * wl.N2
         dtype, peak = "mxfp4", PEAK_TFLOPS["mxfp4"]
         aq = mx.quantize(a, "mxfp4", layout="tiled")
         kernels["ffn0_gemm_gelu_requant_ms"] = time_events(
-            lambda: mx.linear_q(aq, wq, bias, epilogue="bias_gelu_quant_mxfp4", out=h), args.steps, torch)
+            lambda: mx.linear_q(aq, wq, bias, epilogue="bias_gelu_quant_mxfp4_tiled", out=h), args.steps, torch)
         kernels["ffn2_gemm_ms"] = time_events(lambda: mx.linear_q(h, w2q, b2, out=out), args.steps, torch)
     elif wl.fmt == "w4a8":
         wq = mx.quantize(w_dev, "mxfp4", layout="tiled")

@@ -24,12 +24,13 @@ LIB_PATH = os.path.join(_HERE, "libmxfp.so")
 
 MXFP4, MXFP8, NVFP4 = 0, 1, 2
 ROW_MAJOR, TILED = 0, 1
-EPI_BIAS, EPI_BIAS_GELU, EPI_BIAS_GELU_QUANT_MXFP4 = 0, 1, 2
+EPI_BIAS, EPI_BIAS_GELU, EPI_BIAS_GELU_QUANT_MXFP4, EPI_BIAS_GELU_QUANT_MXFP4_TILED = 0, 1, 2, 3
 OUT_BF16, OUT_F32 = 0, 1
 _GROUP = {MXFP4: 32, MXFP8: 32, NVFP4: 16}
 _FMT_NAMES = {"mxfp4": MXFP4, "mxfp8": MXFP8, "nvfp4": NVFP4}
 _EPI_NAMES = {"bias": EPI_BIAS, "bias_gelu": EPI_BIAS_GELU,
-              "bias_gelu_quant_mxfp4": EPI_BIAS_GELU_QUANT_MXFP4}
+              "bias_gelu_quant_mxfp4": EPI_BIAS_GELU_QUANT_MXFP4,
+              "bias_gelu_quant_mxfp4_tiled": EPI_BIAS_GELU_QUANT_MXFP4_TILED}
 _LAYOUT_NAMES = {"row_major": ROW_MAJOR, "tiled": TILED}
 
 
@@ -234,11 +235,13 @@ def _epi(e) -> int:
 def _alloc_out(M: int, N: int, epi: int, out_dtype, device):
     if epi == EPI_BIAS_GELU_QUANT_MXFP4:
         return empty_qmatrix(M, N, MXFP4, device)
+    if epi == EPI_BIAS_GELU_QUANT_MXFP4_TILED:
+        return empty_qmatrix(M, N, MXFP4, device, layout=TILED)
     return torch.empty((M, N), dtype=out_dtype, device=device)
 
 
 def _out_args(out, epi, out_dtype):
-    if epi == EPI_BIAS_GELU_QUANT_MXFP4:
+    if epi in (EPI_BIAS_GELU_QUANT_MXFP4, EPI_BIAS_GELU_QUANT_MXFP4_TILED):
         return _ptr(out.codes), out.cols, _ptr(out.scales), OUT_BF16
     od = OUT_F32 if out_dtype == torch.float32 else OUT_BF16
     return _ptr(out), (_ld(out) if out.shape[0] else out.shape[1]), None, od
@@ -250,7 +253,8 @@ def linear(a: torch.Tensor, w: QMatrix, bias: Optional[torch.Tensor] = None, act
     """y = epilogue(Q(a) . W^T + bias) with a dynamically quantized to ``act_fmt``.
 
     a: BF16 [M, K] GPU tensor; w: QMatrix [N, K]; bias: FP16 [N] or None.  Returns a BF16/F32
-    [M, N] tensor, or a MXFP4 QMatrix [M, N] for the re-quantizing epilogue."""
+    [M, N] tensor, or a MXFP4 QMatrix [M, N] (row-major or tiled) for the re-quantizing
+    epilogues."""
     act_fmt, epi = _fmt(act_fmt), _epi(epilogue)
     _need_cuda(a, "a", torch.bfloat16)
     if a.dim() != 2 or a.stride(1) != 1:

@@ -114,6 +114,13 @@ mx_status check_gemm_tail(int32_t act_fmt, int64_t M, int64_t K, const mx_qmatri
     if (N % 32) return fail(MX_ERR_SHAPE, "re-quantizing epilogue needs N %% 32 == 0");
     if (ld_out != N) return fail(MX_ERR_SHAPE, "re-quantizing epilogue needs ld_out == N");
     if (M != 0 && !aligned(out, 8)) return fail(MX_ERR_ALIGN, "out codes need 8-byte alignment");
+  } else if (epilogue == MX_EPI_BIAS_GELU_QUANT_MXFP4_TILED) {
+    if (act_fmt != MX_FMT_MXFP4) return fail(MX_ERR_UNSUPPORTED, "tiled re-quantized output needs MXFP4 activations");
+    if (!out_scales && M != 0) return fail(MX_ERR_NULL, "out_scales is NULL");
+    if (N % 128 || K % 128) return fail(MX_ERR_SHAPE, "tiled re-quantized output needs N %% 128 == 0 and K %% 128 == 0");
+    if (ld_out != N) return fail(MX_ERR_SHAPE, "re-quantizing epilogue needs ld_out == N");
+    if (M != 0 && (!aligned(out, 16) || !aligned(out_scales, 16)))
+      return fail(MX_ERR_ALIGN, "tiled output codes and scales need 16-byte alignment");
   } else {
     return fail(MX_ERR_UNSUPPORTED, "unknown epilogue %d", epilogue);
   }
@@ -273,7 +280,8 @@ static mx_status run_gemm(const uint8_t* a_codes, const uint8_t* a_scales, float
   p.N = (int)w->rows;
   p.K = (int)K;
   p.epi = epilogue == MX_EPI_BIAS ? mxk::EPI_BIAS
-                                  : epilogue == MX_EPI_BIAS_GELU ? mxk::EPI_GELU : mxk::EPI_GELU_QUANT;
+          : epilogue == MX_EPI_BIAS_GELU ? mxk::EPI_GELU
+          : epilogue == MX_EPI_BIAS_GELU_QUANT_MXFP4 ? mxk::EPI_GELU_QUANT : mxk::EPI_GELU_QUANT_T;
   p.out_f32 = out_dtype == MX_OUT_F32 ? 1 : 0;
   p.a_tiled = a_is_tiled ? 1 : 0;
   p.w_tiled = w->layout == MX_LAYOUT_TILED ? 1 : 0;

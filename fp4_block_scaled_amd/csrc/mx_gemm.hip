@@ -31,9 +31,14 @@ namespace mxk {
 
 constexpr int KC = 256;  // K elements per staged chunk
 
+// tanh-form GELU, 0.5 y (1 + tanh(u)) with u = sqrt(2/pi) (y + 0.044715 y^3), evaluated as the
+// equal y / (1 + exp(-2u)): no cancellation for large negative y, and one hardware exp2 and one
+// reciprocal (about 1 ulp each, a few 1e-7 relative overall; exp2 overflow gives the limit 0).
 __device__ __forceinline__ float gelu_tanh_f32(float y) {
   const float c = 0.7978845608028654f;  // sqrt(2/pi)
-  return 0.5f * y * (1.0f + tanhf(c * (y + 0.044715f * y * y * y)));
+  const float u = c * (y + 0.044715f * y * y * y);
+  const float e = __builtin_amdgcn_exp2f(u * -2.8853900817779268f);  // exp(-2u) = 2^(-2u log2 e)
+  return y * __builtin_amdgcn_rcpf(1.0f + e);
 }
 
 // Byte offset of 16-byte chunk c of LDS row `row` (rows of `rowb` = 128 or 256 bytes).  The
@@ -134,7 +139,12 @@ __device__ __forceinline__ void store_block(const GemmParams& p, const float (&v
 }
 
 // MXFP4 re-quantization of h along n: the 32 values of a block for row m live in lanes l and
-// l ^ 32.  Same rule as the activation quantizer, on binary32 values.  Requires N % 32 == 0.
+// l ^ 32.  Same rule as the activation quantizer, on binary32 values: the element rounding is
+// gfx950's V_CVT_SCALEF32_PK_FP4_F32 (|h| / 2^e to nearest-even on the E2M1 grid, sign kept;
+// probed against that rule on 8.4M values incl. ties, their neighbours and subnormals).
+// Requires N % 32 == 0.  TILED: codes and scales go to the tiled layout, and rows past M (up to
+// the 256-row padding, which the tile covers) are written as zeros.
+template <bool TILED>
 __device__ __forceinline__ void requant_block(const GemmParams& p, const float (&v)[16], int nb, int mb) {
   const int lane = lane_id();
   const int h = lane >> 5;
@@ -146,18 +156,13 @@ __device__ __forceinline__ void requant_block(const GemmParams& p, const float (
   const bool bad = amax >= 0x7F800000u;
   int ex = (int)(amax >> 23) - 129;  // floor(log2 amax) - 2, clamped below
   if (ex < -127) ex = -127;
-  const float inv = __uint_as_float((uint32_t)(127 - ex) << 23);
+  const float scale = __uint_as_float(ex >= -126 ? (uint32_t)(127 + ex) << 23 : 0x00400000u);  // 2^ex
   uint32_t run[4];
 #pragma unroll
   for (int a = 0; a < 4; ++a) {
-    uint32_t r = 0;
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const uint32_t u = __float_as_uint(v[4 * a + i]);
-      const float q = __uint_as_float(u & 0x7FFFFFFFu) * inv;
-      r |= (e2m1_code(q) | ((u >> 28) & 8u)) << (4 * i);
-    }
-    run[a] = bad ? 0u : r;  // 4 codes = 2 bytes at byte offset 4a + 2h of the block
+    uint32_t r = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(0u, v[4 * a], v[4 * a + 1], scale, 0);
+    r = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(r, v[4 * a + 2], v[4 * a + 3], scale, 1);
+    run[a] = bad ? 0u : (r & 0xFFFFu);  // 4 codes = 2 bytes at byte offset 4a + 2h of the block
   }
   const uint32_t X = run[0] | (run[1] << 16), Y = run[2] | (run[3] << 16);
   const uint32_t recv = (uint32_t)__shfl_xor((int)(h ? X : Y), 32);
@@ -169,11 +174,19 @@ __device__ __forceinline__ void requant_block(const GemmParams& p, const float (
     d0 = (recv & 0xFFFFu) | (Y << 16);
     d1 = (recv >> 16) | (Y & 0xFFFF0000u);
   }
-  if (m < p.M && nb < p.N) {
-    uint8_t* codes = (uint8_t*)p.out;
+  uint8_t sbyte = bad ? (uint8_t)0xFF : (uint8_t)(ex + 127);
+  uint8_t* codes = (uint8_t*)p.out;
+  if (TILED) {
+    if (nb < p.N) {
+      if (m >= p.M) d0 = d1 = 0, sbyte = 0;  // padding rows
+      const int64_t nkc = p.N >> 7, kb = nb >> 7;
+      const int g = (nb & 127) >> 5;
+      *(uint2*)(codes + tiled_fp4_off(m, kb, g, nkc) + 8 * h) = make_uint2(d0, d1);
+      if (h == 0) p.out_scales[tiled_scale_off(m, kb, nkc) + g] = sbyte;
+    }
+  } else if (m < p.M && nb < p.N) {
     *(uint2*)(codes + (int64_t)m * (p.N >> 1) + (nb >> 1) + 8 * h) = make_uint2(d0, d1);
-    if (h == 0)
-      p.out_scales[(int64_t)m * (p.N >> 5) + (nb >> 5)] = bad ? (uint8_t)0xFF : (uint8_t)(ex + 127);
+    if (h == 0) p.out_scales[(int64_t)m * (p.N >> 5) + (nb >> 5)] = sbyte;
   }
 }
 
@@ -183,7 +196,7 @@ __device__ __forceinline__ void epilogue_block_t(const GemmParams& p, const v16f
                                                  int nb, int mb) {
   float v[16];
   finish16<EPI>(p, acc, b, v);
-  if (EPI == EPI_GELU_QUANT) requant_block(p, v, nb, mb);
+  if (EPI == EPI_GELU_QUANT || EPI == EPI_GELU_QUANT_T) requant_block<EPI == EPI_GELU_QUANT_T>(p, v, nb, mb);
   else store_block<OUTF32>(p, v, nb, mb);
 }
 
@@ -213,7 +226,7 @@ __device__ __forceinline__ void epilogue_direct(const GemmParams& p, v16f (&acc)
       static_for<FM>([&](auto j) {
         __builtin_amdgcn_sched_barrier(0);  // one block at a time: keep register use small
         const int mb = m_base + 32 * j;
-        if (mb < p.M) epilogue_block_t<EPI, OUTF32>(p, acc[i][j], b, nb, mb);
+        if (mb < p.M || EPI == EPI_GELU_QUANT_T) epilogue_block_t<EPI, OUTF32>(p, acc[i][j], b, nb, mb);
       });
     }
   });
@@ -506,7 +519,7 @@ __device__ __forceinline__ void tile_coords_gm(int b, int tiles_m, int tiles_n, 
 // instead of 8-byte pieces of 32 rows.  Waves hold (BM/2) x 64 sub-tiles (2 x BN/64 waves).
 template <int EPI, bool OUTF32>
 __device__ __forceinline__ bool ring_staged_ok(const GemmParams& p) {
-  return EPI != EPI_GELU_QUANT && !OUTF32 && (p.N % 8) == 0 && (p.ld_out % 8) == 0 &&
+  return (EPI == EPI_BIAS || EPI == EPI_GELU) && !OUTF32 && (p.N % 8) == 0 && (p.ld_out % 8) == 0 &&
          (((uintptr_t)p.out) & 15) == 0;
 }
 template <int BM, int BN, int FN, int FM, int EPI>
@@ -1123,12 +1136,18 @@ static void run_ring(const GemmParams& p, int grid, hipStream_t s) {
 // Every (epilogue, output type, low-rank) combination of the ring kernel.
 template <int BM, int BN, bool AFP8, int EPI, bool LR>
 static void run_ring_o(const GemmParams& p, int grid, hipStream_t s) {
-  if constexpr (EPI == EPI_GELU_QUANT) run_ring<BM, BN, AFP8, EPI, false, LR>(p, grid, s);
+  if constexpr (EPI == EPI_GELU_QUANT || EPI == EPI_GELU_QUANT_T) run_ring<BM, BN, AFP8, EPI, false, LR>(p, grid, s);
   else if (p.out_f32) run_ring<BM, BN, AFP8, EPI, true, LR>(p, grid, s);
   else run_ring<BM, BN, AFP8, EPI, false, LR>(p, grid, s);
 }
 template <int BM, int BN, bool AFP8, bool LR>
 static void run_ring_e(const GemmParams& p, int grid, hipStream_t s) {
+  if constexpr (!AFP8) {  // the tiled re-quantized output needs the 256-row tiles of W4A4
+    if (p.epi == EPI_GELU_QUANT_T) {
+      run_ring_o<BM, BN, AFP8, EPI_GELU_QUANT_T, LR>(p, grid, s);
+      return;
+    }
+  }
   if (p.epi == EPI_GELU_QUANT) run_ring_o<BM, BN, AFP8, EPI_GELU_QUANT, LR>(p, grid, s);
   else if (p.epi == EPI_GELU) run_ring_o<BM, BN, AFP8, EPI_GELU, LR>(p, grid, s);
   else run_ring_o<BM, BN, AFP8, EPI_BIAS, LR>(p, grid, s);

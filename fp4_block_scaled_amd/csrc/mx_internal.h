@@ -25,7 +25,8 @@ hipError_t launch_absmax(const uint16_t* x, int64_t rows, int64_t cols, int64_t 
                          hipStream_t s);
 
 // GEMMs (mx_gemm.hip)
-enum { EPI_BIAS = 0, EPI_GELU = 1, EPI_GELU_QUANT = 2 };
+// EPI_GELU_QUANT_T: the re-quantized output in the tiled layout (rows padded with zeros)
+enum { EPI_BIAS = 0, EPI_GELU = 1, EPI_GELU_QUANT = 2, EPI_GELU_QUANT_T = 3 };
 
 struct GemmParams {
   const uint8_t* a_codes;   // [M, K/2] (FP4) or [M, K] (FP8)

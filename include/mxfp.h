@@ -80,7 +80,8 @@ typedef enum mx_format {
 typedef enum mx_epilogue {
     MX_EPI_BIAS = 0,                 /* y = acc + bias */
     MX_EPI_BIAS_GELU = 1,            /* y = gelu_tanh(acc + bias) */
-    MX_EPI_BIAS_GELU_QUANT_MXFP4 = 2 /* h = gelu_tanh(acc + bias), re-quantized to MXFP4 along N */
+    MX_EPI_BIAS_GELU_QUANT_MXFP4 = 2, /* h = gelu_tanh(acc + bias), re-quantized to MXFP4 along N */
+    MX_EPI_BIAS_GELU_QUANT_MXFP4_TILED = 3 /* the same, written in the tiled layout */
 } mx_epilogue;
 
 typedef enum mx_out_dtype { MX_OUT_BF16 = 0, MX_OUT_F32 = 1 } mx_out_dtype;
@@ -191,6 +192,10 @@ size_t mx_linear_workspace_bytes(int64_t M, int64_t K, int32_t act_fmt, int32_t 
  *  epilogue MX_EPI_BIAS_GELU_QUANT_MXFP4: h = gelu_tanh(acc + bias) in fp32 is quantized to
  *        MXFP4 with groups of 32 along N: out receives codes [M, N/2] and out_scales [M, N/32]
  *        (contiguous; ld_out must be N; out_dtype ignored).  Requires N % 32 == 0.
+ *  epilogue MX_EPI_BIAS_GELU_QUANT_MXFP4_TILED: the same codes and scales as an M x N MXFP4
+ *        matrix in the tiled layout (mx_tiled_bytes(M, N) sizes, padding rows zero), ready to be
+ *        the activation of the next linear.  Requires MXFP4 activations, K % 128 == 0,
+ *        N % 128 == 0, ld_out == N, out and out_scales 16-byte aligned.
  *  workspace: device, >= mx_linear_workspace_bytes(M, K, act_fmt, rank) bytes, 256-byte
  *        aligned; its contents on return are unspecified.
  * w: row-major, or tiled (MX formats): a weight prepared once with mx_relayout or quantized

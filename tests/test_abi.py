@@ -143,6 +143,10 @@ def test_linear_validation(mx):
     assert call(epi=2) == 1                          # re-quant epilogue without out_scales
     assert call(epi=2, osc=FAKE, w_=_qm(mx, 48, 128, mx.MXFP4), ldo=48) == 2  # N % 32
     assert call(epi=2, osc=FAKE, ldo=128) == 2      # ld_out must be N
+    assert call(epi=3, osc=FAKE, act=mx.MXFP8) == 4  # tiled re-quantized output: MXFP4 activations only
+    assert call(epi=3, osc=FAKE, w_=_qm(mx, 96, 128, mx.MXFP4), ldo=96) == 2   # N % 128
+    assert call(epi=3, osc=FAKE, K=160, lda=160, w_=_qm(mx, 128, 160, mx.MXFP4), ldo=128) == 2  # K % 128
+    assert call(epi=3, osc=FAKE + 8, w_=_qm(mx, 128, 128, mx.MXFP4), ldo=128) == 3  # alignment
     assert call(epi=9) == 4
     assert call(od=5) == 4
     assert call(ws=0) == 5

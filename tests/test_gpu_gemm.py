@@ -12,7 +12,7 @@ import torch
 import oracle as O
 from fp4_block_scaled_amd import synth
 from _util import (activation_bits, assert_within, bf16_rne_of_f32, dev_bits16, f16_bits,
-                   sample_rows, to_dev_bf16, to_dev_f16, unpack_fp4, weight_bits)
+                   sample_rows, tile_mx, to_dev_bf16, to_dev_f16, unpack_fp4, weight_bits)
 
 pytestmark = pytest.mark.gpu
 
@@ -270,6 +270,29 @@ def test_ffn_pair_second_linear_on_gpu_codes(mx):
     y_ref, abs_sum = O.linear_ref_mx(hq.codes.cpu().numpy(), hq.scales.cpu().numpy(), O.E2M1,
                                      w2q.codes.cpu().numpy(), w2q.scales.cpu().numpy(), N, b2_bits)
     assert_within(y.cpu().numpy(), y_ref, abs_sum, what="FFN2 on GPU H codes")
+
+
+def test_tiled_requant_output_feeds_the_next_linear(mx):
+    """The tiled re-quantizing epilogue writes exactly the row-major epilogue's codes and scales,
+    regrouped (padding rows zero), and FFN2 on them gives the same output bits."""
+    M, K, N = 300, 512, 1024
+    a_bits, w_bits, b_bits = _ffn_inputs(M, K, N)
+    w2_bits = weight_bits(K, N, seed=14300, sigma=0.01)
+    b2 = to_dev_f16(f16_bits(synth.normal_f32(14400, (K,), 0.01)))
+    a, b = to_dev_bf16(a_bits), to_dev_f16(b_bits)
+    wq = mx.relayout(_quant_w(mx, w_bits))
+    w2q = mx.relayout(_quant_w(mx, w2_bits))
+    h_rm = mx.linear(a, wq, b, epilogue="bias_gelu_quant_mxfp4")
+    h_t = mx.linear(a, wq, b, epilogue="bias_gelu_quant_mxfp4_tiled")
+    torch.cuda.synchronize()
+    assert h_t.layout == mx.TILED
+    tc, ts = tile_mx(h_rm.codes.cpu().numpy(), h_rm.scales.cpu().numpy(), M, N, fp8=False)
+    np.testing.assert_array_equal(h_t.codes.cpu().numpy(), tc)
+    np.testing.assert_array_equal(h_t.scales.cpu().numpy(), ts)
+    y_rm = mx.linear_q(h_rm, w2q, b2, out_dtype=torch.float32)
+    y_t = mx.linear_q(h_t, w2q, b2, out_dtype=torch.float32)
+    torch.cuda.synchronize()
+    assert torch.equal(y_rm, y_t)
 
 
 # ---------------------------------------------------------------------------------------------
