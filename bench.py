@@ -67,9 +67,12 @@ def cpu_info():
     return model
 
 
-def time_events(fn, iters: int, torch):
-    """Average milliseconds of fn() over iters launches, HIP events on the current stream."""
+def time_events(fn, iters: int, torch, warmup: int = 3):
+    """Average milliseconds of fn() over iters launches, HIP events on the current stream, after
+    `warmup` untimed launches."""
     s = torch.cuda.current_stream()
+    for _ in range(warmup):
+        fn()
     start, end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     torch.cuda.synchronize()
     start.record(s)

@@ -249,6 +249,42 @@ __device__ __forceinline__ v16f lowrank_block(const GemmParams& p, v16f acc, int
   return acc;
 }
 
+// The low-rank term of a wave's FN x FM blocks: every fragment of up_t and u (rank <= 64) is
+// loaded first, so the loads of the whole sub-tile are in flight together, then the MFMAs.
+template <int FN, int FM>
+__device__ __forceinline__ void lowrank_tile(const GemmParams& p, v16f (&acc)[FN][FM], int n_base, int m_base) {
+  constexpr int RQ = 4;  // rank / 16 at most
+  const int lane = lane_id();
+  const int h = lane >> 5;
+  uint4 wa[FN][RQ], ub[FM][RQ];
+#pragma unroll
+  for (int i = 0; i < FN; ++i) {
+    const int n = min(n_base + 32 * i + (lane & 31), p.N - 1);
+#pragma unroll
+    for (int q = 0; q < RQ; ++q)
+      wa[i][q] = 16 * q < p.R ? *(const uint4*)(p.lr_up + (int64_t)n * p.R + 16 * q + 8 * h) : make_uint4(0, 0, 0, 0);
+  }
+#pragma unroll
+  for (int j = 0; j < FM; ++j) {
+    const int m = min(m_base + 32 * j + (lane & 31), p.M - 1);
+#pragma unroll
+    for (int q = 0; q < RQ; ++q)
+      ub[j][q] = 16 * q < p.R ? *(const uint4*)(p.lr_u + (int64_t)m * p.R + 16 * q + 8 * h) : make_uint4(0, 0, 0, 0);
+  }
+#pragma unroll
+  for (int q = 0; q < RQ; ++q) {
+    if (16 * q >= p.R) break;
+    static_for<FN>([&](auto i) {
+      static_for<FM>([&](auto j) {
+        v8bf fa, fb;
+        __builtin_memcpy(&fa, &wa[i][q], 16);
+        __builtin_memcpy(&fb, &ub[j][q], 16);
+        acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fa, fb, acc[i][j], 0, 0, 0);
+      });
+    });
+  }
+}
+
 // ---------------------------------------------------------------------------------------------
 // MX GEMM (W: E2M1, A: E2M1 or E4M3)
 // ---------------------------------------------------------------------------------------------
@@ -472,7 +508,11 @@ __global__ void __launch_bounds__(256, 1) gemm_mx_kernel(GemmParams p) {
 template <int BM, int BN, bool AFP8>
 struct RingTile {
   static_assert((BM == 128 || BM == 256) && (BN == 128 || BN == 256), "tile sizes");
-  static constexpr int NWAVES = BN / 32;                 // 2 (m) x BN/64 (n) waves
+#ifndef MX_RING_W256
+#define MX_RING_W256 8
+#endif
+  // 2 (m) x NWAVES/2 (n) waves; a 256-wide tile has 8 waves of 128 x 64 or 4 of 128 x 128
+  static constexpr int NWAVES = BN == 256 ? MX_RING_W256 : 4;
   static constexpr int WGS = 256 / BN;                   // workgroups per compute unit
   static constexpr int KCR = 128;
   static constexpr int WROWB = 64, AROWB = AFP8 ? 128 : 64;  // bytes per row and chunk
@@ -481,7 +521,7 @@ struct RingTile {
   static constexpr int STAGE = W_BYTES + A_BYTES + WS_BYTES + AS_BYTES;
   static constexpr int NSTAGE = 3;
   static constexpr int LDS = NSTAGE * STAGE > BM * BN * 2 ? NSTAGE * STAGE : BM * BN * 2;
-  static constexpr int FN = 2, FM = BM / 64;                       // 32x32 blocks per wave
+  static constexpr int FN = BN / (NWAVES / 2) / 32, FM = BM / 64;  // 32x32 blocks per wave
   static constexpr int NW = W_BYTES / 1024 / NWAVES, NA = A_BYTES / 1024 / NWAVES;  // 1 KB loads
   static constexpr int TA = BM / 64, TW = BN / 64;                  // 256-byte scale loads
   static constexpr int NS = (TA + TW + NWAVES - 1) / NWAVES;        // scale loads per wave
@@ -522,11 +562,11 @@ __device__ __forceinline__ bool ring_staged_ok(const GemmParams& p) {
   return (EPI == EPI_BIAS || EPI == EPI_GELU) && !OUTF32 && (p.N % 8) == 0 && (p.ld_out % 8) == 0 &&
          (((uintptr_t)p.out) & 15) == 0;
 }
-template <int BM, int BN, int FN, int FM, int EPI>
+template <int BM, int BN, int FN, int FM, int EPI, int NWAVES = BN / 32>
 __device__ __forceinline__ void epilogue_ring_staged(const GemmParams& p, v16f (&acc)[FN][FM], uint8_t* smem,
                                                      int n0, int m0, int wn0, int wm0, int wave) {
   constexpr int RB = BN * 2, NCH = RB / 16;  // bytes and 16-byte chunks per staged row
-  constexpr int NWAVES = BN / 32, RPI = 64 / NCH;  // waves; rows per store instruction
+  constexpr int RPI = 64 / NCH;              // rows per store instruction
   const int lane = lane_id();
   const int r32 = lane & 31, h = lane >> 5;
   static_for<FN>([&](auto i) {
@@ -560,7 +600,7 @@ __device__ __forceinline__ void epilogue_ring_staged(const GemmParams& p, v16f (
 }
 
 template <int BM, int BN, bool AFP8, int EPI, bool OUTF32, bool LR>
-__global__ void __launch_bounds__(BN * 2, 256 / BN) gemm_mx_ring_kernel(GemmParams p) {
+__global__ void __launch_bounds__((RingTile<BM, BN, AFP8>::NWAVES * 64), 256 / BN) gemm_mx_ring_kernel(GemmParams p) {
   using T = RingTile<BM, BN, AFP8>;
   typedef typename std::conditional<AFP8, v8i, v4i>::type AV;
   __shared__ __attribute__((aligned(16))) uint8_t smem[T::LDS];
@@ -568,7 +608,7 @@ __global__ void __launch_bounds__(BN * 2, 256 / BN) gemm_mx_ring_kernel(GemmPara
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int r32 = lane & 31, h = lane >> 5;
-  const int wn0 = (wave >> 1) * 64, wm0 = (wave & 1) * (BM / 2);
+  const int wn0 = (wave >> 1) * (32 * T::FN), wm0 = (wave & 1) * (BM / 2);
   const int tiles_n = (p.N + BN - 1) / BN, tiles_m = (p.M + BM - 1) / BM;
   int tm, tn;
   tile_coords_gm<8>(blockIdx.x, tiles_m, tiles_n, tm, tn);
@@ -757,18 +797,12 @@ __global__ void __launch_bounds__(BN * 2, 256 / BN) gemm_mx_ring_kernel(GemmPara
     st = st1;
   }
 
-  if (LR) {
-    static_for<T::FN>([&](auto i) {
-      static_for<T::FM>([&](auto j) {
-        acc[i][j] = lowrank_block(p, acc[i][j], n0 + wn0 + 32 * i, m0 + wm0 + 32 * j);
-      });
-    });
-  }
+  if (LR) lowrank_tile<T::FN, T::FM>(p, acc, n0 + wn0, m0 + wm0);
   if (ring_staged_ok<EPI, OUTF32>(p)) {
     static_assert(BM * BN * 2 <= T::LDS, "output tile fits the ring");
     wait_vmem_all();  // the (empty) loads issued for the chunks past the end have landed
     barrier_only();   // every wave is done with the ring
-    epilogue_ring_staged<BM, BN, T::FN, T::FM, EPI>(p, acc, smem, n0, m0, wn0, wm0, wave);
+    epilogue_ring_staged<BM, BN, T::FN, T::FM, EPI, T::NWAVES>(p, acc, smem, n0, m0, wn0, wm0, wave);
   } else {
     epilogue_direct<T::FN, T::FM, EPI, OUTF32>(p, acc, n0 + wn0, m0 + wm0);
   }
@@ -936,19 +970,20 @@ __global__ void __launch_bounds__(256, 1) gemm_nv_kernel(GemmParams p) {
 // quarter wave (16 consecutive rows, one half each) reads 16 distinct bank groups.
 template <int BM, int BN>
 struct NvRingTile {
-  static_assert(BM == 256 && BN == 128, "tile sizes");
+  static_assert(BM == 256 && (BN == 128 || BN == 256), "tile sizes");
+  static constexpr int WGS = 256 / BN;  // workgroups per compute unit (4 waves each)
   static constexpr int KCN = 64, ROWB = 32;
   static constexpr int W_BYTES = BN * ROWB, A_BYTES = BM * ROWB;
   static constexpr int WS_BYTES = BN * 4, AS_BYTES = BM * 4;
   static constexpr int STAGE = W_BYTES + A_BYTES + WS_BYTES + AS_BYTES;
   static constexpr int NSTAGE = 4;
   static constexpr int LDS = NSTAGE * STAGE > BM * BN * 2 ? NSTAGE * STAGE : BM * BN * 2;
-  static constexpr int FN = BN / 64, FM = BM / 64;
+  static constexpr int FN = BN / 64, FM = BM / 64;                 // 2 x 2 waves
   static constexpr int NW = W_BYTES / 4096, NA = A_BYTES / 4096;  // 1 KB loads per wave
   static constexpr int TA = BM / 64, TW = BN / 64;                 // 256-byte scale loads
   static constexpr int NS = (TA + TW + 3) / 4;
   static constexpr int NDMA = NW + NA + NS;
-  static_assert(LDS <= 80 * 1024, "two workgroups per compute unit");
+  static_assert(LDS * WGS <= 160 * 1024, "LDS of the workgroups of a compute unit");
 };
 
 // 8 E2M1 codes (one dword, element 2j in the low nibble of byte j) times a block scale, as 8
@@ -963,7 +998,7 @@ __device__ __forceinline__ v8h nv_dequant8_f16(uint32_t codes, v2h sb) {
 }
 
 template <int BM, int BN, int EPI, bool OUTF32>
-__global__ void __launch_bounds__(256, 2) gemm_nv_ring_kernel(GemmParams p) {
+__global__ void __launch_bounds__(256, 256 / BN) gemm_nv_ring_kernel(GemmParams p) {
   using T = NvRingTile<BM, BN>;
   __shared__ __attribute__((aligned(16))) uint8_t smem[T::LDS];
 
@@ -1088,34 +1123,57 @@ __global__ void __launch_bounds__(256, 2) gemm_nv_ring_kernel(GemmParams p) {
   if (ring_staged_ok<EPI, OUTF32>(p)) {
     wait_vmem_all();
     barrier_only();
-    epilogue_ring_staged<BM, BN, T::FN, T::FM, EPI>(p, acc, smem, n0, m0, wn0, wm0, wave);
+    epilogue_ring_staged<BM, BN, T::FN, T::FM, EPI, 4>(p, acc, smem, n0, m0, wn0, wm0, wave);
   } else {
     epilogue_direct<T::FN, T::FM, EPI, OUTF32>(p, acc, n0 + wn0, m0 + wm0);
   }
 }
 
 // ---------------------------------------------------------------------------------------------
-// low-rank down projection u = bf16(x . down_t^T): one wave per 32 (r) x 32 (m) block
+// low-rank down projection u = bf16(x . down_t^T): a workgroup of 4 waves per 32 (r) x 32 (m)
+// block; wave w sums the 16-element K steps w, w + 4, ... with 4 steps' loads in flight, and the
+// four partial sums are added in the fixed order w = 0..3 (deterministic).
 // ---------------------------------------------------------------------------------------------
-__global__ void __launch_bounds__(64) lowrank_down_kernel(const uint16_t* __restrict__ x,
-                                                           int64_t ld_x,
-                                                           const uint16_t* __restrict__ down_t,
-                                                           int M, int K, int R,
-                                                           uint16_t* __restrict__ u) {
-  const int lane = threadIdx.x;
+__global__ void __launch_bounds__(256) lowrank_down_kernel(const uint16_t* __restrict__ x,
+                                                            int64_t ld_x,
+                                                            const uint16_t* __restrict__ down_t,
+                                                            int M, int K, int R,
+                                                            uint16_t* __restrict__ u) {
+  __shared__ float part[3][16][64];
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int h = lane >> 5;
   const int rb = blockIdx.y * 32, mb = blockIdx.x * 32;
   const int r = min(rb + (lane & 31), R - 1);
   const int m = min(mb + (lane & 31), M - 1);
+  const uint16_t* dr = down_t + (int64_t)r * K + 8 * h;
+  const uint16_t* xr = x + (int64_t)m * ld_x + 8 * h;
   v16f acc = v16f{};
-  for (int k = 0; k < K; k += 16) {
-    const uint4 da = *(const uint4*)(down_t + (int64_t)r * K + k + 8 * h);
-    const uint4 xb = *(const uint4*)(x + (int64_t)m * ld_x + k + 8 * h);
-    v8bf fa, fb;
-    __builtin_memcpy(&fa, &da, 16);
-    __builtin_memcpy(&fb, &xb, 16);
-    acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fa, fb, acc, 0, 0, 0);
+  for (int k0 = 16 * wave; k0 < K; k0 += 4 * 64) {
+    uint4 da[4], xb[4];
+#pragma unroll
+    for (int t = 0; t < 4; ++t) {
+      const int k = k0 + 64 * t;
+      da[t] = k < K ? *(const uint4*)(dr + k) : make_uint4(0, 0, 0, 0);
+      xb[t] = k < K ? *(const uint4*)(xr + k) : make_uint4(0, 0, 0, 0);
+    }
+#pragma unroll
+    for (int t = 0; t < 4; ++t) {
+      v8bf fa, fb;
+      __builtin_memcpy(&fa, &da[t], 16);
+      __builtin_memcpy(&fb, &xb[t], 16);
+      acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fa, fb, acc, 0, 0, 0);
+    }
   }
+  if (wave > 0) {
+#pragma unroll
+    for (int e = 0; e < 16; ++e) part[wave - 1][e][lane] = acc[e];
+  }
+  __syncthreads();
+  if (wave > 0) return;
+#pragma unroll
+  for (int w = 0; w < 3; ++w)
+#pragma unroll
+    for (int e = 0; e < 16; ++e) acc[e] += part[w][e][lane];
   const int mo = mb + (lane & 31);
   if (mo >= M) return;
 #pragma unroll
@@ -1130,7 +1188,7 @@ __global__ void __launch_bounds__(64) lowrank_down_kernel(const uint16_t* __rest
 // ---------------------------------------------------------------------------------------------
 template <int BM, int BN, bool AFP8, int EPI, bool OUTF32, bool LR>
 static void run_ring(const GemmParams& p, int grid, hipStream_t s) {
-  gemm_mx_ring_kernel<BM, BN, AFP8, EPI, OUTF32, LR><<<grid, BN * 2, 0, s>>>(p);
+  gemm_mx_ring_kernel<BM, BN, AFP8, EPI, OUTF32, LR><<<grid, RingTile<BM, BN, AFP8>::NWAVES * 64, 0, s>>>(p);
 }
 
 // Every (epilogue, output type, low-rank) combination of the ring kernel.
@@ -1178,18 +1236,22 @@ hipError_t launch_gemm_mx(const GemmParams& p, bool act_fp8, hipStream_t s) {
   return run_mx<256, 256, false>(p, s);
 }
 
+#ifndef NV_RING_BN
+#define NV_RING_BN 256
+#endif
 template <int EPI>
 static void run_nv_ring(const GemmParams& p, int grid, hipStream_t s) {
-  if constexpr (EPI == EPI_GELU_QUANT) gemm_nv_ring_kernel<256, 128, EPI, false><<<grid, 256, 0, s>>>(p);
-  else if (p.out_f32) gemm_nv_ring_kernel<256, 128, EPI, true><<<grid, 256, 0, s>>>(p);
-  else gemm_nv_ring_kernel<256, 128, EPI, false><<<grid, 256, 0, s>>>(p);
+  constexpr int BN = NV_RING_BN;
+  if constexpr (EPI == EPI_GELU_QUANT) gemm_nv_ring_kernel<256, BN, EPI, false><<<grid, 256, 0, s>>>(p);
+  else if (p.out_f32) gemm_nv_ring_kernel<256, BN, EPI, true><<<grid, 256, 0, s>>>(p);
+  else gemm_nv_ring_kernel<256, BN, EPI, false><<<grid, 256, 0, s>>>(p);
 }
 
 // K % 64 == 0: the ring kernel; otherwise the register-staged kernel (K a multiple of 16).
 hipError_t launch_gemm_nv(const GemmParams& p, hipStream_t s) {
   if (p.M == 0) return hipSuccess;
   if (p.K % 64 == 0) {
-    const int tiles = ((p.M + 255) / 256) * ((p.N + 127) / 128);
+    const int tiles = ((p.M + 255) / 256) * ((p.N + NV_RING_BN - 1) / NV_RING_BN);
     if (p.epi == EPI_GELU_QUANT) run_nv_ring<EPI_GELU_QUANT>(p, tiles, s);
     else if (p.epi == EPI_GELU) run_nv_ring<EPI_GELU>(p, tiles, s);
     else run_nv_ring<EPI_BIAS>(p, tiles, s);
@@ -1204,7 +1266,7 @@ hipError_t launch_lowrank_down(const uint16_t* x, int64_t ld_x, const uint16_t* 
                                int K, int R, uint16_t* u, hipStream_t s) {
   if (M == 0) return hipSuccess;
   dim3 grid((M + 31) / 32, (R + 31) / 32);
-  lowrank_down_kernel<<<grid, 64, 0, s>>>(x, ld_x, down_t, M, K, R, u);
+  lowrank_down_kernel<<<grid, 256, 0, s>>>(x, ld_x, down_t, M, K, R, u);
   return hipGetLastError();
 }
 
