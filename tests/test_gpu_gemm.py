@@ -351,3 +351,92 @@ def test_full_size_wan_a14b_attention_projection(mx):
 
 def test_full_size_w4a8(mx):
     _full_mx(mx, "wan_ti2v5b_w4a8_4290x3072x14336", "mxfp8")
+
+
+def test_full_size_w4a8_with_lowrank_branch(mx):
+    """The W4A8 SVDQuant workload as the benchmark runs it: MXFP8 activations, prepared MXFP4
+    weight, rank-32 low-rank branch (no bias), sampled rows against the oracle."""
+    wl = synth.WORKLOADS["wan_ti2v5b_w4a8_4290x3072x3072"]
+    a_bits = synth.bits16(synth.to_bf16(wl.activation()))
+    w_bits = synth.bits16(synth.to_bf16(wl.weight()))
+    down = synth.bits16(synth.to_bf16(wl.lora_down()))
+    up = synth.bits16(synth.to_bf16(wl.lora_up()))
+    wq = mx.relayout(_quant_w(mx, w_bits))
+    lr = mx.LowRank(to_dev_bf16(np.ascontiguousarray(down.T)), to_dev_bf16(np.ascontiguousarray(up.T)))
+    y = mx.linear(to_dev_bf16(a_bits), wq, None, act_fmt="mxfp8", lowrank=lr, out_dtype=torch.float32)
+    torch.cuda.synchronize()
+    rows = sample_rows(wl.M, 256)
+    ys = y[torch.from_numpy(rows).cuda()].cpu().numpy()
+    ac, as_ = O.quantize_mx_bf16(a_bits[rows], O.E4M3)
+    wc, ws = O.quantize_mx_bf16(w_bits)
+    y_ref, abs_sum = O.linear_ref_mx(ac, as_, O.E4M3, wc, ws, wl.K, None)
+    u_bits, lr_ref, lr_abs = O.lowrank(np.ascontiguousarray(a_bits[rows]), down, up)
+    flip = (2.0 ** -8) * (np.abs(O.bf16_values(u_bits)) @ np.abs(O.bf16_values(up)))
+    assert_within(ys, y_ref + lr_ref, abs_sum, 2e-3 * lr_abs + flip, what="W4A8 + low-rank, full size")
+
+
+def test_full_size_ffn_pair(mx):
+    """The FFN pair at 75600 x 5120 -> 13824 -> 5120 as the benchmark runs it (FFN0 writes H
+    tiled, FFN2 reads it), on sampled rows: FFN0's fp32 h against the oracle, the H codes
+    against Q_MX of the GPU's own h, and FFN2 against the oracle on the GPU's H codes."""
+    wl = synth.WORKLOADS["wan_a14b_ffn_75600x5120x13824"]
+    a_bits = synth.bits16(synth.to_bf16(wl.activation()))
+    w_bits = synth.bits16(synth.to_bf16(wl.weight()))
+    w2_bits = synth.bits16(synth.to_bf16(wl.weight2()))
+    b_bits, b2_bits = f16_bits(wl.bias()), f16_bits(wl.bias2())
+    a = to_dev_bf16(a_bits)
+    wq, w2q = mx.relayout(_quant_w(mx, w_bits)), mx.relayout(_quant_w(mx, w2_bits))
+    rows = sample_rows(wl.M, 96)
+    idx = torch.from_numpy(rows).cuda()
+    h32 = mx.linear(a, wq, to_dev_f16(b_bits), epilogue="bias_gelu", out_dtype=torch.float32)
+    torch.cuda.synchronize()
+    h32s = h32[idx].cpu().numpy()
+    del h32
+    hq = mx.linear(a, wq, to_dev_f16(b_bits), epilogue="bias_gelu_quant_mxfp4_tiled")
+    y = mx.linear_q(hq, w2q, to_dev_f16(b2_bits), out_dtype=torch.float32)
+    torch.cuda.synchronize()
+    ys = y[idx].cpu().numpy()
+    del y
+    h_rm = mx.relayout(hq)
+    torch.cuda.synchronize()
+    hc, hs = h_rm.codes[idx].cpu().numpy(), h_rm.scales[idx].cpu().numpy()
+    # FFN0 h against the oracle (GELU-propagated GEMM tolerance, as in the small-shape test)
+    ac, as_ = O.quantize_mx_bf16(a_bits[rows])
+    wc, ws = O.quantize_mx_bf16(w_bits)
+    y0_ref, abs0 = O.linear_ref_mx(ac, as_, O.E2M1, wc, ws, wl.K, b_bits)
+    h_ref = O.gelu_tanh(y0_ref)
+    err = np.abs(h32s.astype(np.float64) - h_ref)
+    tol_y = 2e-3 * abs0 + 2.0 ** -23 * np.abs(y0_ref)
+    assert np.all(err <= 1.13 * tol_y + 4e-6 * np.abs(h_ref) + 1e-7)
+    # H codes are exactly Q_MX of the GPU's own h
+    c_self, s_self = O.quantize_mx_f32(h32s)
+    np.testing.assert_array_equal(hs, s_self)
+    np.testing.assert_array_equal(hc, c_self)
+    # FFN2 on the GPU's H codes
+    w2c, w2s = O.quantize_mx_bf16(w2_bits)
+    y_ref, abs2 = O.linear_ref_mx(hc, hs, O.E2M1, w2c, w2s, wl.N, b2_bits)
+    assert_within(ys, y_ref, abs2, what="FFN2, full size")
+
+
+def test_full_size_nvfp4(mx):
+    """The NVFP4 workload (static activation global scale from amax 40, weight global scale from
+    its absmax), sampled rows against the oracle."""
+    wl = synth.WORKLOADS["wan_a14b_nvfp4_75600x5120x13824"]
+    a_bits = synth.bits16(synth.to_bf16(wl.activation()))
+    w_bits = synth.bits16(synth.to_bf16(wl.weight()))
+    b_bits = f16_bits(wl.bias())
+    wq = mx.quantize_weight_nvfp4(to_dev_bf16(w_bits))
+    sg_a = mx.nvfp4_global_scale(wl.act_amax_static)
+    y = mx.linear(to_dev_bf16(a_bits), wq, to_dev_f16(b_bits), act_fmt="nvfp4",
+                  act_global_scale=sg_a, out_dtype=torch.float32)
+    torch.cuda.synchronize()
+    rows = sample_rows(wl.M, 96)
+    ys = y[torch.from_numpy(rows).cuda()].cpu().numpy()
+    del y
+    assert sg_a == O.nv_global_scale(wl.act_amax_static)
+    sg_w = O.nv_global_scale(float(np.max(np.abs(O.bf16_values(w_bits)))))
+    assert wq.global_scale == sg_w
+    ac, as_ = O.quantize_nv_bf16(a_bits[rows], sg_a)
+    wc, ws = O.quantize_nv_bf16(w_bits, sg_w)
+    y_ref, abs_sum = O.linear_ref_nv(ac, as_, sg_a, wc, ws, sg_w, wl.K, b_bits)
+    assert_within(ys, y_ref, abs_sum, what="NVFP4, full size")
