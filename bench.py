@@ -9,7 +9,8 @@ way and reported beside it.  The CPU baseline times the oracle on a bounded row 
 
   python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME] [--no-cpu]
 
-Other workloads (``--workload``) bench the variant paths: the FFN pair, W4A8 SVDQuant, NVFP4.
+Other workloads (``--workload``) bench the variant paths: the FFN pair, W4A8 SVDQuant, the MXFP8
+W8A8 reference layer, NVFP4.
 """
 from __future__ import annotations
 
@@ -183,7 +184,7 @@ def bench_mx_linear(args, torch, mx, synth):
 
 
 def bench_variant(args, torch, mx, synth):
-    """Variant workloads (not the headline metric): FFN pair, W4A8 SVDQuant, NVFP4."""
+    """Variant workloads (not the headline metric): FFN pair, W4A8 SVDQuant, MXFP8 W8A8, NVFP4."""
     import numpy as np
     wl = synth.WORKLOADS[args.workload]
     M, K, N = wl.M, wl.K, wl.N
@@ -221,6 +222,17 @@ def bench_variant(args, torch, mx, synth):
         dtype, peak = "mxfp8xmxfp4", PEAK_TFLOPS["mxfp8"]
         aq = mx.quantize(a, "mxfp8", layout="tiled")
         kernels["gemm_no_lowrank_ms"] = time_events(lambda: mx.linear_q(aq, wq, bias, out=out), args.steps, torch)
+        kernels["quant_mxfp8_ms"] = time_events(lambda: mx.quantize(a, "mxfp8", out=aq), args.steps, torch)
+    elif wl.fmt == "w8a8":
+        wq = mx.quantize(w_dev, "mxfp8", layout="tiled")
+        out = torch.empty((M, N), dtype=torch.bfloat16, device="cuda")
+        ws = torch.empty(mx.linear_workspace_bytes(M, K, "mxfp8"), dtype=torch.uint8, device="cuda")
+        step = lambda: mx.linear(a, wq, bias, act_fmt="mxfp8", out=out, workspace=ws)
+        flops = 2.0 * M * N * K
+        dtype, peak = "mxfp8", PEAK_TFLOPS["mxfp8"]
+        aq = mx.quantize(a, "mxfp8", layout="tiled")
+        kernels["gemm_ms"] = time_events(lambda: mx.linear_q(aq, wq, bias, out=out), args.steps, torch)
+        kernels["gemm_tflops"] = flops / (kernels["gemm_ms"] * 1e-3) / 1e12
         kernels["quant_mxfp8_ms"] = time_events(lambda: mx.quantize(a, "mxfp8", out=aq), args.steps, torch)
     elif wl.fmt == "nvfp4":
         wq = mx.quantize_weight_nvfp4(w_dev)

@@ -82,9 +82,10 @@ mx_status check_gemm_tail(int32_t act_fmt, int64_t M, int64_t K, const mx_qmatri
   if (!w->codes || !w->scales) return fail(MX_ERR_NULL, "w->codes / w->scales is NULL");
   if (!out && M != 0) return fail(MX_ERR_NULL, "out is NULL");
   if (!fmt_ok(act_fmt) || !fmt_ok(w->fmt)) return fail(MX_ERR_UNSUPPORTED, "unknown format");
-  const bool mx_pair = w->fmt == MX_FMT_MXFP4 && (act_fmt == MX_FMT_MXFP4 || act_fmt == MX_FMT_MXFP8);
+  const bool w4_pair = w->fmt == MX_FMT_MXFP4 && (act_fmt == MX_FMT_MXFP4 || act_fmt == MX_FMT_MXFP8);
+  const bool w8_pair = w->fmt == MX_FMT_MXFP8 && act_fmt == MX_FMT_MXFP8;
   const bool nv_pair = w->fmt == MX_FMT_NVFP4 && act_fmt == MX_FMT_NVFP4;
-  if (!mx_pair && !nv_pair)
+  if (!w4_pair && !w8_pair && !nv_pair)
     return fail(MX_ERR_UNSUPPORTED, "format pair (act %d, weight %d) not provided", act_fmt, w->fmt);
   if (M < 0 || K <= 0) return fail(MX_ERR_SHAPE, "M must be >= 0 and K > 0");
   if (w->cols != K) return fail(MX_ERR_SHAPE, "w->cols (%lld) != K (%lld)", (long long)w->cols, (long long)K);
@@ -94,6 +95,8 @@ mx_status check_gemm_tail(int32_t act_fmt, int64_t M, int64_t K, const mx_qmatri
     if (ls != MX_OK) return ls;
   }
   if (K % 32) return fail(MX_ERR_SHAPE, "K (%lld) must be a multiple of 32", (long long)K);
+  if (w8_pair && K % 128)
+    return fail(MX_ERR_SHAPE, "MXFP8 weights need K %% 128 == 0 (K = %lld)", (long long)K);
   if (M > INT32_MAX || w->rows > INT32_MAX || K > INT32_MAX)
     return fail(MX_ERR_SHAPE, "M, N and K must fit in 31 bits");
   if (nv_pair && !finite_pos(w->global_scale))
@@ -286,7 +289,7 @@ static mx_status run_gemm(const uint8_t* a_codes, const uint8_t* a_scales, float
   p.a_tiled = a_is_tiled ? 1 : 0;
   p.w_tiled = w->layout == MX_LAYOUT_TILED ? 1 : 0;
   hipError_t e = w->fmt == MX_FMT_NVFP4 ? mxk::launch_gemm_nv(p, s)
-                                         : mxk::launch_gemm_mx(p, act_fmt == MX_FMT_MXFP8, s);
+                                         : mxk::launch_gemm_mx(p, act_fmt == MX_FMT_MXFP8, w->fmt == MX_FMT_MXFP8, s);
   return hip_status(e, "GEMM launch");
 }
 

@@ -505,22 +505,23 @@ __global__ void __launch_bounds__(256, 1) gemm_mx_kernel(GemmParams p) {
 // all 64 banks: piece ^ ((row >> 2) & 3) for 64-byte rows, piece ^ ((row >> 1) & 7) for 128-byte
 // rows.  A load instruction fills 1 KB of consecutive LDS (16 or 8 rows), lane i slot i, so each
 // lane fetches the global piece that the swizzle puts in its slot.
-template <int BM, int BN, bool AFP8>
+template <int BM, int BN, bool AFP8, bool WFP8 = false>
 struct RingTile {
   static_assert((BM == 128 || BM == 256) && (BN == 128 || BN == 256), "tile sizes");
+  static_assert(!WFP8 || AFP8, "E4M3 weights are paired with E4M3 activations");
 #ifndef MX_RING_W256
 #define MX_RING_W256 8
 #endif
   // 2 (m) x NWAVES/2 (n) waves; a 256-wide tile has 8 waves of 128 x 64 or 4 of 128 x 128
   static constexpr int NWAVES = BN == 256 ? MX_RING_W256 : 4;
-  static constexpr int WGS = 256 / BN;                   // workgroups per compute unit
   static constexpr int KCR = 128;
-  static constexpr int WROWB = 64, AROWB = AFP8 ? 128 : 64;  // bytes per row and chunk
+  static constexpr int WROWB = WFP8 ? 128 : 64, AROWB = AFP8 ? 128 : 64;  // bytes per row and chunk
   static constexpr int W_BYTES = BN * WROWB, A_BYTES = BM * AROWB;
   static constexpr int WS_BYTES = BN * 4, AS_BYTES = BM * 4;
   static constexpr int STAGE = W_BYTES + A_BYTES + WS_BYTES + AS_BYTES;
   static constexpr int NSTAGE = 3;
   static constexpr int LDS = NSTAGE * STAGE > BM * BN * 2 ? NSTAGE * STAGE : BM * BN * 2;
+  static constexpr int WGS = 2 * LDS <= 160 * 1024 ? 2 : 1;  // workgroups per compute unit
   static constexpr int FN = BN / (NWAVES / 2) / 32, FM = BM / 64;  // 32x32 blocks per wave
   static constexpr int NW = W_BYTES / 1024 / NWAVES, NA = A_BYTES / 1024 / NWAVES;  // 1 KB loads
   static constexpr int TA = BM / 64, TW = BN / 64;                  // 256-byte scale loads
@@ -602,10 +603,12 @@ __device__ __forceinline__ void epilogue_ring_staged(const GemmParams& p, v16f (
   }
 }
 
-template <int BM, int BN, bool AFP8, int EPI, bool OUTF32, bool LR>
-__global__ void __launch_bounds__((RingTile<BM, BN, AFP8>::NWAVES * 64), 256 / BN) gemm_mx_ring_kernel(GemmParams p) {
-  using T = RingTile<BM, BN, AFP8>;
+template <int BM, int BN, bool AFP8, bool WFP8, int EPI, bool OUTF32, bool LR>
+__global__ void __launch_bounds__((RingTile<BM, BN, AFP8, WFP8>::NWAVES * 64), (RingTile<BM, BN, AFP8, WFP8>::WGS))
+gemm_mx_ring_kernel(GemmParams p) {
+  using T = RingTile<BM, BN, AFP8, WFP8>;
   typedef typename std::conditional<AFP8, v8i, v4i>::type AV;
+  typedef typename std::conditional<WFP8, v8i, v4i>::type WV;
   __shared__ __attribute__((aligned(16))) uint8_t smem[T::LDS];
 
   const int lane = threadIdx.x & 63;
@@ -617,7 +620,7 @@ __global__ void __launch_bounds__((RingTile<BM, BN, AFP8>::NWAVES * 64), 256 / B
   tile_coords_gm<8>(blockIdx.x, tiles_m, tiles_n, tm, tn);
   const int m0 = tm * BM, n0 = tn * BN;
   const int nkc = p.K / T::KCR;
-  const uint32_t w_row = (uint32_t)p.K >> 1, a_row = AFP8 ? (uint32_t)p.K : ((uint32_t)p.K >> 1);
+  const uint32_t w_row = WFP8 ? (uint32_t)p.K : ((uint32_t)p.K >> 1), a_row = AFP8 ? (uint32_t)p.K : ((uint32_t)p.K >> 1);
   const uint32_t s_row = (uint32_t)p.K >> 5;
 
   // Operand addressing.  Every load is descriptor + per-lane VGPR offset (range-checked) + chunk
@@ -630,9 +633,9 @@ __global__ void __launch_bounds__((RingTile<BM, BN, AFP8>::NWAVES * 64), 256 / B
   auto clamp32 = [](uint64_t v) -> uint32_t { return v > 0xFFFFFFFFull ? 0xFFFFFFFFu : (uint32_t)v; };
   const uint64_t wn = (uint64_t)(p.N - n0), am = (uint64_t)(p.M - m0);
   const bool wt = p.w_tiled != 0, at = p.a_tiled != 0;
-  constexpr int A_TROWS = AFP8 ? 8 : 16;  // rows per 1 KB code tile
+  constexpr int A_TROWS = AFP8 ? 8 : 16, W_TROWS = WFP8 ? 8 : 16;  // rows per 1 KB code tile
   const uint64_t kb1k = (uint64_t)nkc * 1024u, kb256 = (uint64_t)nkc * 256u;
-  const v4i rw = wt ? make_rsrc_sgpr(p.w_codes + (int64_t)(n0 / 16) * kb1k, clamp32((uint64_t)(BN / 16) * kb1k))
+  const v4i rw = wt ? make_rsrc_sgpr(p.w_codes + (int64_t)(n0 / W_TROWS) * kb1k, clamp32((uint64_t)(BN / W_TROWS) * kb1k))
                     : make_rsrc_sgpr(p.w_codes + (int64_t)n0 * w_row, clamp32(wn * w_row));
   const v4i ra = at ? make_rsrc_sgpr(p.a_codes + (int64_t)(m0 / A_TROWS) * kb1k, clamp32((uint64_t)(BM / A_TROWS) * kb1k))
                     : make_rsrc_sgpr(p.a_codes + (int64_t)m0 * a_row, clamp32(am * a_row));
@@ -640,26 +643,24 @@ __global__ void __launch_bounds__((RingTile<BM, BN, AFP8>::NWAVES * 64), 256 / B
                      : make_rsrc_sgpr(p.w_scales + (int64_t)n0 * s_row, clamp32(wn * s_row));
   const v4i ras = at ? make_rsrc_sgpr(p.a_scales + (int64_t)(m0 / 64) * kb256, clamp32((uint64_t)(BM / 64) * kb256))
                      : make_rsrc_sgpr(p.a_scales + (int64_t)m0 * s_row, clamp32(am * s_row));
-  const uint32_t w_step = wt ? 1024u : 64u, a_step = at ? 1024u : (uint32_t)T::AROWB;
+  const uint32_t w_step = wt ? 1024u : (uint32_t)T::WROWB, a_step = at ? 1024u : (uint32_t)T::AROWB;
   const uint32_t ws_step = wt ? 256u : 4u, as_step = at ? 256u : 4u;
 
   // lane offsets of the row-major code loads: 64-byte rows, 16 per load; 128-byte rows, 8 per load
   const uint32_t pc64 = (uint32_t)((lane & 3) ^ ((lane >> 4) & 3)) * 16u;
   const uint32_t lt16 = (uint32_t)lane * 16u;
-  auto off_w = [&](int q) {
-    const int tr = wave * T::NW + q;  // 16-row group of the tile
-    return wt ? (uint32_t)tr * (uint32_t)kb1k + lt16 : (uint32_t)(16 * tr + (lane >> 2)) * w_row + pc64;
-  };
-  auto off_a = [&](int q) {
-    const int tr = wave * T::NA + q;  // A_TROWS-row group of the tile
-    if (at) return (uint32_t)tr * (uint32_t)kb1k + lt16;
-    if constexpr (AFP8) {
+  auto off_code = [&](auto fp8, int tr, bool tiled, uint32_t row_bytes) -> uint32_t {
+    if (tiled) return (uint32_t)tr * (uint32_t)kb1k + lt16;
+    if constexpr (decltype(fp8)::value) {
       const int row = 8 * tr + (lane >> 3);
-      return (uint32_t)row * a_row + (uint32_t)((lane & 7) ^ ((row >> 1) & 7)) * 16u;
+      return (uint32_t)row * row_bytes + (uint32_t)((lane & 7) ^ ((row >> 1) & 7)) * 16u;
     } else {
-      return (uint32_t)(16 * tr + (lane >> 2)) * a_row + pc64;
+      return (uint32_t)(16 * tr + (lane >> 2)) * row_bytes + pc64;
     }
   };
+  // load q of this wave covers W_TROWS (A_TROWS) rows of the tile
+  auto off_w = [&](int q) { return off_code(std::integral_constant<bool, WFP8>{}, wave * T::NW + q, wt, w_row); };
+  auto off_a = [&](int q) { return off_code(std::integral_constant<bool, AFP8>{}, wave * T::NA + q, at, a_row); };
   // scale load k of this wave: 64 rows of A scales (u < TA) or of W scales; surplus slots repeat
   // the last W load (the same bytes to the same place)
   auto scale_slot = [&](int k, int& urow, bool& is_a) {
@@ -705,8 +706,20 @@ __global__ void __launch_bounds__((RingTile<BM, BN, AFP8>::NWAVES * 64), 256 / B
   // The fragments of a chunk (both MFMA steps) and its scale dwords, read from stage `stg`.
   struct Frags {
     uint32_t wsc[T::FN], asc[T::FM];
-    v4i wf[2][T::FN];
+    WV wf[2][T::FN];
     AV af[2][T::FM];
+  };
+  // 16-byte pieces of a lane's fragment: E2M1 rows (64 bytes) hold the lane's 32-element block
+  // whole in piece 2h + s; E4M3 rows (128 bytes) hold elements 16h..16h+15 of both blocks, in
+  // pieces 2s + h and 4 + 2s + h.
+  auto frag4 = [&](const uint8_t* base, int row, int s) -> v4i {
+    return *(const v4i*)(base + row * 64 + (((2 * h + s) ^ ((row >> 2) & 3)) << 4));
+  };
+  auto frag8 = [&](const uint8_t* base, int row, int s) -> v8i {
+    const int g = (row >> 1) & 7;
+    const v4i d0 = *(const v4i*)(base + row * 128 + (((2 * s + h) ^ g) << 4));
+    const v4i d1 = *(const v4i*)(base + row * 128 + (((4 + 2 * s + h) ^ g) << 4));
+    return v8i{d0[0], d0[1], d0[2], d0[3], d1[0], d1[1], d1[2], d1[3]};
   };
   auto read_chunk = [&](int stg, Frags& f) {
     const uint8_t* sW = smem + stg * T::STAGE;
@@ -721,39 +734,40 @@ __global__ void __launch_bounds__((RingTile<BM, BN, AFP8>::NWAVES * 64), 256 / B
     for (int s = 0; s < 2; ++s) {
 #pragma unroll
       for (int i = 0; i < T::FN; ++i) {
-        const int row = wrow + 32 * i;
-        f.wf[s][i] = *(const v4i*)(sW + row * 64 + (((2 * h + s) ^ ((row >> 2) & 3)) << 4));
+        if constexpr (WFP8) f.wf[s][i] = frag8(sW, wrow + 32 * i, s);
+        else f.wf[s][i] = frag4(sW, wrow + 32 * i, s);
       }
 #pragma unroll
       for (int j = 0; j < T::FM; ++j) {
-        const int row = arow + 32 * j;
-        if constexpr (AFP8) {
-          const int g = (row >> 1) & 7;
-          const v4i d0 = *(const v4i*)(sA + row * 128 + (((2 * s + h) ^ g) << 4));
-          const v4i d1 = *(const v4i*)(sA + row * 128 + (((4 + 2 * s + h) ^ g) << 4));
-          f.af[s][j] = v8i{d0[0], d0[1], d0[2], d0[3], d1[0], d1[1], d1[2], d1[3]};
-        } else {
-          f.af[s][j] = *(const v4i*)(sA + row * 64 + (((2 * h + s) ^ ((row >> 2) & 3)) << 4));
-        }
+        if constexpr (AFP8) f.af[s][j] = frag8(sA, arow + 32 * j, s);
+        else f.af[s][j] = frag4(sA, arow + 32 * j, s);
       }
     }
   };
   // The MFMAs of step S, with the loads of chunk `dkc` into stage `dst` that fall in this step:
-  // load q goes after MFMA (q + 1) * TOTAL / NDMA - 1 of the chunk's TOTAL (distinct slots; a
-  // burst of loads would fill the vector-memory queue and hold up the MFMA issue behind it).
+  // load q goes after MFMA (q + 1) * TOTAL / NDMA - 1 of the chunk's TOTAL (spread out; a burst
+  // of loads would fill the vector-memory queue and hold up the MFMA issue behind it).  With
+  // more loads than MFMAs the first slot takes two.
   constexpr int TOTAL = 2 * T::FN * T::FM;
-  static_assert(TOTAL >= T::NDMA, "one load slot per MFMA at most");
+  static_assert(2 * TOTAL >= T::NDMA, "two load slots per MFMA at most");
+  constexpr auto dma_slot = [](int q) {
+    const int m = (q + 1) * TOTAL / T::NDMA - 1;
+    return m < 0 ? 0 : m;
+  };
   auto mma_step = [&](auto sc, const Frags& f, int dkc, int dst) {
     constexpr int S = decltype(sc)::value;
     static_for<T::FN>([&](auto i) {
       static_for<T::FM>([&](auto j) {
-        if constexpr (AFP8)
+        if constexpr (WFP8)
+          acc[i][j] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(f.wf[S][i], f.af[S][j], acc[i][j], 0, 0, S,
+                                                                      (int)f.wsc[i], S, (int)f.asc[j]);
+        else if constexpr (AFP8)
           acc[i][j] = mfma_scale_32x32x64_f4f8(f.wf[S][i], f.af[S][j], acc[i][j], 4, 0, S, (int)f.wsc[i], S, (int)f.asc[j]);
         else
           acc[i][j] = mfma_scale_32x32x64_f4f4(f.wf[S][i], f.af[S][j], acc[i][j], 4, 4, S, (int)f.wsc[i], S, (int)f.asc[j]);
         constexpr int M = S * T::FN * T::FM + decltype(i)::value * T::FM + decltype(j)::value;
         static_for<T::NDMA>([&](auto qc) {
-          if constexpr ((decltype(qc)::value + 1) * TOTAL / T::NDMA - 1 == M) {
+          if constexpr (dma_slot(decltype(qc)::value) == M) {
             __builtin_amdgcn_sched_barrier(0);
             issue_one(qc, dkc, dst);
             __builtin_amdgcn_sched_barrier(0);
@@ -763,11 +777,16 @@ __global__ void __launch_bounds__((RingTile<BM, BN, AFP8>::NWAVES * 64), 256 / B
     });
   };
   // loads issued during step 0 (those of a chunk that precede its step-1 MFMAs)
-  constexpr int LOADS_S0 = [] {
+  constexpr int LOADS_S0 = [&] {
     int n = 0;
-    for (int q = 0; q < T::NDMA; ++q) n += (q + 1) * TOTAL / T::NDMA - 1 < TOTAL / 2 ? 1 : 0;
+    for (int q = 0; q < T::NDMA; ++q) n += dma_slot(q) < TOTAL / 2 ? 1 : 0;
     return n;
   }();
+  static_assert([&] {
+    for (int q = 0; q < T::NDMA; ++q)
+      if (dma_slot(q) >= TOTAL) return false;
+    return true;
+  }(), "every load has an MFMA slot");
 
   // Software pipeline over chunks.  Iteration kc: step-0 MFMAs of chunk kc (its fragments were
   // read last iteration) while chunk kc + 2 starts loading into the stage of chunk kc - 1; then
@@ -1189,29 +1208,29 @@ __global__ void __launch_bounds__(256) lowrank_down_kernel(const uint16_t* __res
 // ---------------------------------------------------------------------------------------------
 // launchers
 // ---------------------------------------------------------------------------------------------
-template <int BM, int BN, bool AFP8, int EPI, bool OUTF32, bool LR>
+template <int BM, int BN, bool AFP8, bool WFP8, int EPI, bool OUTF32, bool LR>
 static void run_ring(const GemmParams& p, int grid, hipStream_t s) {
-  gemm_mx_ring_kernel<BM, BN, AFP8, EPI, OUTF32, LR><<<grid, RingTile<BM, BN, AFP8>::NWAVES * 64, 0, s>>>(p);
+  gemm_mx_ring_kernel<BM, BN, AFP8, WFP8, EPI, OUTF32, LR><<<grid, RingTile<BM, BN, AFP8, WFP8>::NWAVES * 64, 0, s>>>(p);
 }
 
 // Every (epilogue, output type, low-rank) combination of the ring kernel.
-template <int BM, int BN, bool AFP8, int EPI, bool LR>
+template <int BM, int BN, bool AFP8, bool WFP8, int EPI, bool LR>
 static void run_ring_o(const GemmParams& p, int grid, hipStream_t s) {
-  if constexpr (EPI == EPI_GELU_QUANT || EPI == EPI_GELU_QUANT_T) run_ring<BM, BN, AFP8, EPI, false, LR>(p, grid, s);
-  else if (p.out_f32) run_ring<BM, BN, AFP8, EPI, true, LR>(p, grid, s);
-  else run_ring<BM, BN, AFP8, EPI, false, LR>(p, grid, s);
+  if constexpr (EPI == EPI_GELU_QUANT || EPI == EPI_GELU_QUANT_T) run_ring<BM, BN, AFP8, WFP8, EPI, false, LR>(p, grid, s);
+  else if (p.out_f32) run_ring<BM, BN, AFP8, WFP8, EPI, true, LR>(p, grid, s);
+  else run_ring<BM, BN, AFP8, WFP8, EPI, false, LR>(p, grid, s);
 }
-template <int BM, int BN, bool AFP8, bool LR>
+template <int BM, int BN, bool AFP8, bool WFP8, bool LR>
 static void run_ring_e(const GemmParams& p, int grid, hipStream_t s) {
   if constexpr (!AFP8) {  // the tiled re-quantized output needs the 256-row tiles of W4A4
     if (p.epi == EPI_GELU_QUANT_T) {
-      run_ring_o<BM, BN, AFP8, EPI_GELU_QUANT_T, LR>(p, grid, s);
+      run_ring_o<BM, BN, AFP8, WFP8, EPI_GELU_QUANT_T, LR>(p, grid, s);
       return;
     }
   }
-  if (p.epi == EPI_GELU_QUANT) run_ring_o<BM, BN, AFP8, EPI_GELU_QUANT, LR>(p, grid, s);
-  else if (p.epi == EPI_GELU) run_ring_o<BM, BN, AFP8, EPI_GELU, LR>(p, grid, s);
-  else run_ring_o<BM, BN, AFP8, EPI_BIAS, LR>(p, grid, s);
+  if (p.epi == EPI_GELU_QUANT) run_ring_o<BM, BN, AFP8, WFP8, EPI_GELU_QUANT, LR>(p, grid, s);
+  else if (p.epi == EPI_GELU) run_ring_o<BM, BN, AFP8, WFP8, EPI_GELU, LR>(p, grid, s);
+  else run_ring_o<BM, BN, AFP8, WFP8, EPI_BIAS, LR>(p, grid, s);
 }
 
 // K % 128 == 0: the ring kernel (row-major or tiled operands); otherwise the register-staged
@@ -1224,8 +1243,8 @@ static hipError_t run_mx(const GemmParams& p, hipStream_t s) {
 #endif
     constexpr int RBN = AFP8 ? 128 : MX_RING_BN;
     const int tiles = ((p.M + BM - 1) / BM) * ((p.N + RBN - 1) / RBN);
-    if (p.R > 0) run_ring_e<BM, RBN, AFP8, true>(p, tiles, s);
-    else run_ring_e<BM, RBN, AFP8, false>(p, tiles, s);
+    if (p.R > 0) run_ring_e<BM, RBN, AFP8, false, true>(p, tiles, s);
+    else run_ring_e<BM, RBN, AFP8, false, false>(p, tiles, s);
   } else {
     const int tiles = ((p.M + BM - 1) / BM) * ((p.N + BN - 1) / BN);
     gemm_mx_kernel<BM, BN, AFP8, false><<<tiles, 256, 0, s>>>(p);
@@ -1233,8 +1252,26 @@ static hipError_t run_mx(const GemmParams& p, hipStream_t s) {
   return hipGetLastError();
 }
 
-hipError_t launch_gemm_mx(const GemmParams& p, bool act_fp8, hipStream_t s) {
+// MXFP8 x MXFP8 (W8A8): the ring kernel only; the caller checks K % 128 == 0.  A 128 x 256 tile
+// with 8 waves (one workgroup per compute unit, 148.5 KB of LDS): 12 % faster than 256 x 128
+// and 30 % faster than 128 x 128 at 75600 x 5120 x 5120.
+#ifndef MX_W8_BM
+#define MX_W8_BM 128
+#endif
+#ifndef MX_W8_BN
+#define MX_W8_BN 256
+#endif
+static hipError_t run_w8a8(const GemmParams& p, hipStream_t s) {
+  constexpr int BM = MX_W8_BM, BN = MX_W8_BN;
+  const int tiles = ((p.M + BM - 1) / BM) * ((p.N + BN - 1) / BN);
+  if (p.R > 0) run_ring_e<BM, BN, true, true, true>(p, tiles, s);
+  else run_ring_e<BM, BN, true, true, false>(p, tiles, s);
+  return hipGetLastError();
+}
+
+hipError_t launch_gemm_mx(const GemmParams& p, bool act_fp8, bool w_fp8, hipStream_t s) {
   if (p.M == 0) return hipSuccess;
+  if (w_fp8) return p.K % 128 == 0 && act_fp8 ? run_w8a8(p, s) : hipErrorInvalidValue;
   if (act_fp8) return run_mx<128, 256, true>(p, s);
   return run_mx<256, 256, false>(p, s);
 }

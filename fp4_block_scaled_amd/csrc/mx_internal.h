@@ -31,7 +31,7 @@ enum { EPI_BIAS = 0, EPI_GELU = 1, EPI_GELU_QUANT = 2, EPI_GELU_QUANT_T = 3 };
 struct GemmParams {
   const uint8_t* a_codes;   // [M, K/2] (FP4) or [M, K] (FP8)
   const uint8_t* a_scales;  // [M, K/32] E8M0, or [M, K/16] E4M3 (NVFP4)
-  const uint8_t* w_codes;   // [N, K/2]
+  const uint8_t* w_codes;   // [N, K/2] (FP4) or [N, K] (FP8)
   const uint8_t* w_scales;  // [N, K/32] or [N, K/16]
   const uint16_t* bias;     // FP16 [N] or nullptr
   const uint16_t* lr_u;     // BF16 [M, R] or nullptr (low-rank intermediate)
@@ -46,8 +46,9 @@ struct GemmParams {
   int a_tiled, w_tiled;     // operand layouts: 0 row-major, 1 tiled (MX formats)
 };
 
-// act_fp8: activation codes are E4M3 (W4A8); otherwise E2M1.
-hipError_t launch_gemm_mx(const GemmParams& p, bool act_fp8, hipStream_t s);
+// act_fp8: activation codes are E4M3 (W4A8); otherwise E2M1.  w_fp8: weight codes are E4M3
+// (W8A8, with act_fp8 and K % 128 == 0 only); otherwise E2M1.
+hipError_t launch_gemm_mx(const GemmParams& p, bool act_fp8, bool w_fp8, hipStream_t s);
 hipError_t launch_gemm_nv(const GemmParams& p, hipStream_t s);
 // u[m, r] = bf16_rne(sum_k x[m, k] * down_t[r, k])
 hipError_t launch_lowrank_down(const uint16_t* x, int64_t ld_x, const uint16_t* down_t, int M,

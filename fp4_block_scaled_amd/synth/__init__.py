@@ -106,7 +106,7 @@ class Workload:
     M: int
     K: int
     N: int
-    fmt: str = "mxfp4"     # weight/activation format: mxfp4 | w4a8 | nvfp4
+    fmt: str = "mxfp4"     # weight/activation format: mxfp4 | w4a8 | w8a8 | nvfp4
     a_sigma: float = 1.0
     outlier_frac: float = 0.01
     outlier_factor: float = 20.0
@@ -166,6 +166,11 @@ WORKLOADS = {
     "wan_ti2v5b_w4a8_4290x3072x14336": Workload(
         "wan_ti2v5b_w4a8_4290x3072x14336", 4, 4290, 3072, 14336, "w4a8",
         outlier_frac=0.01, outlier_factor=25.0, w_sigma=0.02, bias_sigma=None, rank=32),
+    # MXFP8 W8A8 reference layer at the attention-projection shape; the same seeds (config 2),
+    # so the same BF16 operands, as the W4A4 workload
+    "wan_a14b_w8a8_75600x5120x5120": Workload(
+        "wan_a14b_w8a8_75600x5120x5120", 2, 75600, 5120, 5120, "w8a8",
+        outlier_frac=0.005, outlier_factor=30.0, w_sigma=0.015),
     # NVFP4 at the A14B FFN shape with a static activation global scale (amax 40)
     "wan_a14b_nvfp4_75600x5120x13824": Workload(
         "wan_a14b_nvfp4_75600x5120x13824", 5, 75600, 5120, 13824, "nvfp4",

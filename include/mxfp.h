@@ -13,6 +13,9 @@
  *  - "Wan2.2 W4A8 SVDQuant - NVIDIA (CUDA) artifacts": W4A8 variant, MXFP4 weights times
  *    dynamically quantized MXFP8 (E4M3, per-32 E8M0) activations plus a rank-32 low-rank branch
  *    with BF16 factors.
+ *  - "Wan2.2-I2V-A14B-Lightning-Diffusers-MXFP4-AutoRound", VBench-I2V results and Performance
+ *    Profile: MXFP8 linear layers (E4M3 weights and activations, per-32 E8M0 scales) are the
+ *    quality and speed reference the MXFP4 layers are compared with (W8A8).
  * The bit-level encodings follow OCP Microscaling (MX) v1.0: the shared exponent of a block is
  * floor(log2(max|x|)) - emax(element) (emax 2 for E2M1, 8 for E4M3), elements are rounded to
  * nearest-even with saturation, signs are kept.  NVFP4 stores its global scale in the decode
@@ -182,7 +185,8 @@ size_t mx_linear_workspace_bytes(int64_t M, int64_t K, int32_t act_fmt, int32_t 
  * mx_linear - the quantized linear layer on a BF16 activation a (M x K, leading dimension ld_a):
  * quantize a dynamically to act_fmt (act_global_scale is the static NVFP4 activation global
  * scale), then y = dequant(a) . dequant(w)^T in fp32 accumulation, then the epilogue.
- * Supported (act_fmt, w->fmt): (MXFP4, MXFP4) W4A4; (MXFP8, MXFP4) W4A8; (NVFP4, NVFP4).
+ * Supported (act_fmt, w->fmt): (MXFP4, MXFP4) W4A4; (MXFP8, MXFP4) W4A8; (MXFP8, MXFP8) W8A8
+ * (K % 128 == 0); (NVFP4, NVFP4).
  *  bias: device FP16 [N] or NULL.
  *  lr:   low-rank branch or NULL (MX formats only); y += bf16_rne(a . lr->down) . lr->up,
  *        added before the bias.
@@ -200,7 +204,8 @@ size_t mx_linear_workspace_bytes(int64_t M, int64_t K, int32_t act_fmt, int32_t 
  *        aligned; its contents on return are unspecified.
  * w: row-major, or tiled (MX formats): a weight prepared once with mx_relayout or quantized
  *        directly into the tiled layout is the fast GEMM operand.
- * Requires K % 32 == 0 (K % 16 == 0 for NVFP4), w->cols == K, N = w->rows >= 1.
+ * Requires K % 32 == 0 (K % 16 == 0 for NVFP4, K % 128 == 0 for MXFP8 weights), w->cols == K,
+ * N = w->rows >= 1.
  */
 mx_status mx_linear(const uint16_t* a, int64_t M, int64_t K, int64_t ld_a, int32_t act_fmt,
                     float act_global_scale, const mx_qmatrix* w, const uint16_t* bias,

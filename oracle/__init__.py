@@ -263,10 +263,11 @@ def absmax_bf16(x_bits) -> float:
 
 
 # ---- composite references -----------------------------------------------------------------
-def linear_ref_mx(a_codes, a_scales, a_elem, w_codes, w_scales, K, bias_f16_bits=None):
-    """Reference MX linear on quantized operands: (y, abs_sum) in fp64."""
+def linear_ref_mx(a_codes, a_scales, a_elem, w_codes, w_scales, K, bias_f16_bits=None, w_elem=E2M1):
+    """Reference MX linear on quantized operands: (y, abs_sum) in fp64.  w_elem is E2M1 for the
+    MXFP4 weights of W4A4 / W4A8, E4M3 for the MXFP8 weights of the W8A8 reference layer."""
     a = dequantize_mx(a_codes, a_scales, K, a_elem)
-    w = dequantize_mx(w_codes, w_scales, K, E2M1)
+    w = dequantize_mx(w_codes, w_scales, K, w_elem)
     bias = None if bias_f16_bits is None else f16_values(bias_f16_bits)
     return gemm(a, w, bias)
 

@@ -136,7 +136,9 @@ def test_linear_validation(mx):
     assert call(a=0) == 1
     assert call(out=0) == 1
     assert call(act=mx.NVFP4) == 4                   # NVFP4 activation with an MXFP4 weight
-    assert call(w_=_qm(mx, 64, 128, mx.MXFP8)) == 4  # FP8 weights are not provided
+    assert call(w_=_qm(mx, 64, 128, mx.MXFP8)) == 4  # FP8 weights pair with FP8 activations only
+    assert call(act=mx.MXFP8, K=160, lda=160, w_=_qm(mx, 64, 160, mx.MXFP8)) == 2  # W8A8 needs K % 128
+    assert call(act=mx.MXFP8, M=0, ws=0, w_=_qm(mx, 64, 128, mx.MXFP8)) == 0      # W8A8 accepted
     assert call(K=96) == 2                           # w->cols != K
     assert call(K=100, w_=_qm(mx, 64, 100, mx.MXFP4), lda=104) == 2  # K % 32
     assert call(ldo=32) == 2                         # ld_out < N

@@ -30,19 +30,21 @@ def _quant_w(mx, w_bits):
     return q
 
 
-def _mx_case(mx, M, K, N, seed=0, bias=True, act="mxfp4", out_dtype=torch.float32, epi="bias"):
+def _mx_case(mx, M, K, N, seed=0, bias=True, act="mxfp4", out_dtype=torch.float32, epi="bias",
+             w_fmt="mxfp4"):
     a_bits = activation_bits(M, K, seed_base=11000 + seed)
     w_bits = weight_bits(N, K, seed=11100 + seed)
     b_bits = f16_bits(synth.normal_f32(11200 + seed, (N,), 0.01)) if bias else None
-    wq = _quant_w(mx, w_bits)
+    wq = mx.quantize(to_dev_bf16(w_bits), w_fmt)
     y = mx.linear(to_dev_bf16(a_bits), wq, to_dev_f16(b_bits) if bias else None, act_fmt=act,
                   out_dtype=out_dtype, epilogue=epi)
     torch.cuda.synchronize()
     elem = O.E4M3 if act == "mxfp8" else O.E2M1
+    w_elem = O.E4M3 if w_fmt == "mxfp8" else O.E2M1
     ac, as_ = O.quantize_mx_bf16(a_bits, elem)
-    wc, ws = O.quantize_mx_bf16(w_bits, O.E2M1)
+    wc, ws = O.quantize_mx_bf16(w_bits, w_elem)
     assert np.array_equal(wq.codes.cpu().numpy(), wc) and np.array_equal(wq.scales.cpu().numpy(), ws)
-    y_ref, abs_sum = O.linear_ref_mx(ac, as_, elem, wc, ws, K, b_bits)
+    y_ref, abs_sum = O.linear_ref_mx(ac, as_, elem, wc, ws, K, b_bits, w_elem=w_elem)
     return y, y_ref, abs_sum, (a_bits, wq, b_bits)
 
 
@@ -166,21 +168,22 @@ def test_w4a8_linear_vs_oracle(mx, M, K, N):
     assert_within(y.cpu().numpy(), y_ref, abs_sum)
 
 
-def _lowrank_case(mx, M, K, N, R, act, bias):
+def _lowrank_case(mx, M, K, N, R, act, bias, w_fmt="mxfp4"):
     a_bits = activation_bits(M, K, seed_base=13000, factor=25.0)
     w_bits = weight_bits(N, K, seed=13100)
     down = synth.bits16(synth.to_bf16(synth.normal_f32(13200, (K, R), 0.02)))
     up = synth.bits16(synth.to_bf16(synth.normal_f32(13300, (R, N), 0.02)))
     b_bits = f16_bits(synth.normal_f32(13400, (N,), 0.01)) if bias else None
-    wq = _quant_w(mx, w_bits)
+    wq = mx.quantize(to_dev_bf16(w_bits), w_fmt)
+    w_elem = O.E4M3 if w_fmt == "mxfp8" else O.E2M1
     lr = mx.LowRank(to_dev_bf16(np.ascontiguousarray(down.T)), to_dev_bf16(np.ascontiguousarray(up.T)))
     y = mx.linear(to_dev_bf16(a_bits), wq, to_dev_f16(b_bits) if bias else None, act_fmt=act,
                   lowrank=lr, out_dtype=torch.float32)
     torch.cuda.synchronize()
     elem = O.E4M3 if act == "mxfp8" else O.E2M1
     ac, as_ = O.quantize_mx_bf16(a_bits, elem)
-    wc, ws = O.quantize_mx_bf16(w_bits)
-    y_ref, abs_sum = O.linear_ref_mx(ac, as_, elem, wc, ws, K, b_bits)
+    wc, ws = O.quantize_mx_bf16(w_bits, w_elem)
+    y_ref, abs_sum = O.linear_ref_mx(ac, as_, elem, wc, ws, K, b_bits, w_elem=w_elem)
     u_bits, lr_ref, lr_abs = O.lowrank(a_bits, down, up)
     # u is rounded to BF16 from an fp32 (GPU) or exact (oracle) sum: near a rounding midpoint
     # the two may pick neighbouring BF16 values, a change of up to 2^-8 |u_r| per term.
@@ -194,6 +197,53 @@ def _lowrank_case(mx, M, K, N, R, act, bias):
 def test_lowrank_branch_vs_oracle(mx, act, R):
     y, y_ref, abs_sum, extra = _lowrank_case(mx, 200, 768, 320, R, act, bias=(R == 32))
     assert_within(y.cpu().numpy(), y_ref, abs_sum, extra, what=f"low-rank {act} R={R}")
+
+
+# ---------------------------------------------------------------------------------------------
+# W8A8 (MXFP8 weights and activations), the MXFP8 reference layer
+# ---------------------------------------------------------------------------------------------
+@pytest.mark.parametrize("M,K,N", [(130, 512, 256), (300, 1024, 640), (77, 384, 200), (1, 128, 128),
+                                   (513, 768, 1024), (260, 3072, 96)])
+def test_w8a8_linear_vs_oracle(mx, M, K, N):
+    y, y_ref, abs_sum, _ = _mx_case(mx, M, K, N, seed=5 * M, act="mxfp8", w_fmt="mxfp8")
+    assert_within(y.cpu().numpy(), y_ref, abs_sum, what=f"W8A8 {M}x{K}x{N}")
+
+
+@pytest.mark.parametrize("M,K,N", [(300, 1024, 640), (260, 384, 200)])
+def test_w8a8_tiled_operands_and_bf16_output(mx, M, K, N):
+    """Every layout pairing gives the same bits, and the BF16 output is the RNE of the FP32 one
+    (both store paths: staged for N % 8 == 0 and direct otherwise)."""
+    a = to_dev_bf16(activation_bits(M, K, seed_base=16500 + M))
+    w_rm = mx.quantize(to_dev_bf16(weight_bits(N, K, seed=16600 + N)), "mxfp8")
+    w_t = mx.relayout(w_rm)
+    bias = to_dev_f16(f16_bits(synth.normal_f32(16700, (N,), 0.01)))
+    a_rm = mx.quantize(a, "mxfp8")
+    a_t = mx.quantize(a, "mxfp8", layout="tiled")
+    ref = mx.linear_q(a_rm, w_rm, bias, out_dtype=torch.float32)
+    for aa, ww in ((a_t, w_t), (a_rm, w_t), (a_t, w_rm)):
+        assert torch.equal(mx.linear_q(aa, ww, bias, out_dtype=torch.float32), ref)
+    assert torch.equal(mx.linear(a, w_t, bias, act_fmt="mxfp8", out_dtype=torch.float32), ref)
+    y16 = mx.linear(a, w_t, bias, act_fmt="mxfp8", out_dtype=torch.bfloat16)
+    torch.cuda.synchronize()
+    np.testing.assert_array_equal(dev_bits16(y16), bf16_rne_of_f32(ref.cpu().numpy()))
+
+
+def test_w8a8_lowrank_and_gelu_epilogue(mx):
+    y, y_ref, abs_sum, extra = _lowrank_case(mx, 200, 768, 320, 32, "mxfp8", bias=True, w_fmt="mxfp8")
+    assert_within(y.cpu().numpy(), y_ref, abs_sum, extra, what="W8A8 low-rank")
+    M, K, N = 300, 1024, 640
+    a_bits, w_bits, b_bits = _ffn_inputs(M, K, N)
+    wq = mx.quantize(to_dev_bf16(w_bits), "mxfp8")
+    h = mx.linear(to_dev_bf16(a_bits), wq, to_dev_f16(b_bits), act_fmt="mxfp8", epilogue="bias_gelu",
+                  out_dtype=torch.float32)
+    torch.cuda.synchronize()
+    ac, as_ = O.quantize_mx_bf16(a_bits, O.E4M3)
+    wc, ws = O.quantize_mx_bf16(w_bits, O.E4M3)
+    y_ref, abs_sum = O.linear_ref_mx(ac, as_, O.E4M3, wc, ws, K, b_bits, w_elem=O.E4M3)
+    h_ref = O.gelu_tanh(y_ref)
+    tol_y = 2e-3 * abs_sum + 2.0 ** -23 * np.abs(y_ref)
+    err = np.abs(h.cpu().numpy().astype(np.float64) - h_ref)
+    assert np.all(err <= 1.13 * tol_y + 4e-6 * np.abs(h_ref) + 1e-7)
 
 
 def test_lowrank_zero_down_is_plain_w4a8(mx):
@@ -320,13 +370,13 @@ def test_nvfp4_linear_vs_oracle(mx, M, K, N):
 # ---------------------------------------------------------------------------------------------
 # full workload sizes, in the launch configuration the benchmark times (sampled rows)
 # ---------------------------------------------------------------------------------------------
-def _full_mx(mx, wl_name, act, nsample=192):
+def _full_mx(mx, wl_name, act, nsample=192, w_fmt="mxfp4"):
     wl = synth.WORKLOADS[wl_name]
     a_bits = synth.bits16(synth.to_bf16(wl.activation()))
     w_bits = synth.bits16(synth.to_bf16(wl.weight()))
     b = wl.bias()
     b_bits = f16_bits(b) if b is not None else None
-    wq = mx.relayout(_quant_w(mx, w_bits))  # the benchmark's prepared (tiled) weight
+    wq = mx.relayout(mx.quantize(to_dev_bf16(w_bits), w_fmt))  # the benchmark's prepared (tiled) weight
     a = to_dev_bf16(a_bits)
     rows = sample_rows(wl.M, nsample)
     bias = to_dev_f16(b_bits) if b is not None else None
@@ -338,9 +388,10 @@ def _full_mx(mx, wl_name, act, nsample=192):
     np.testing.assert_array_equal(dev_bits16(y16[idx]), bf16_rne_of_f32(ys))
     del y, y16
     elem = O.E4M3 if act == "mxfp8" else O.E2M1
+    w_elem = O.E4M3 if w_fmt == "mxfp8" else O.E2M1
     ac, as_ = O.quantize_mx_bf16(a_bits[rows], elem)
-    wc, ws = O.quantize_mx_bf16(w_bits)
-    y_ref, abs_sum = O.linear_ref_mx(ac, as_, elem, wc, ws, wl.K, b_bits)
+    wc, ws = O.quantize_mx_bf16(w_bits, w_elem)
+    y_ref, abs_sum = O.linear_ref_mx(ac, as_, elem, wc, ws, wl.K, b_bits, w_elem=w_elem)
     return assert_within(ys, y_ref, abs_sum, what=wl_name)
 
 
@@ -351,6 +402,11 @@ def test_full_size_wan_a14b_attention_projection(mx):
 
 def test_full_size_w4a8(mx):
     _full_mx(mx, "wan_ti2v5b_w4a8_4290x3072x14336", "mxfp8")
+
+
+def test_full_size_w8a8(mx):
+    r = _full_mx(mx, "wan_a14b_w8a8_75600x5120x5120", "mxfp8", w_fmt="mxfp8")
+    print(f"max err/tol {r:.3f}")
 
 
 def test_full_size_w4a8_with_lowrank_branch(mx):

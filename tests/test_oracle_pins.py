@@ -410,6 +410,34 @@ def test_gemm_one_hot_weight_and_zero_activation():
     assert np.all(t0 == 0)
 
 
+def test_w8a8_reference_exact_and_one_hot():
+    """MXFP8 weights (E4M3 codes): with unit scales every product and partial sum is exact in
+    fp64, so the reference equals numpy's product of the decoded grids; a one-hot weight (code
+    0x38 = 1.0) selects activation columns exactly."""
+    rng = np.random.default_rng(43)
+    M, N, K = 6, 10, 256
+    def e4m3_codes(rows):
+        c = rng.integers(0, 256, size=(rows, K), dtype=np.uint8)
+        c[(c & 0x7F) == 0x7F] = 0x38  # no NaN codes
+        return c
+    ac, wc = e4m3_codes(M), e4m3_codes(N)
+    as_ = np.full((M, K // 32), 127, dtype=np.uint8)
+    ws = np.full((N, K // 32), 127, dtype=np.uint8)
+    grid = np.array([O.e4m3_value(c) for c in range(256)])
+    a, w = grid[ac], grid[wc]
+    y, t = O.linear_ref_mx(ac, as_, O.E4M3, wc, ws, K, None, w_elem=O.E4M3)
+    np.testing.assert_array_equal(y, a @ w.T)
+    np.testing.assert_array_equal(t, np.abs(a) @ np.abs(w).T)
+    oh = np.zeros((N, K), dtype=np.uint8)
+    for n in range(N):
+        oh[n, 5 * n + 1] = 0x38
+    y1, _ = O.linear_ref_mx(ac, as_, O.E4M3, oh, ws, K, None, w_elem=O.E4M3)
+    np.testing.assert_array_equal(y1, a[:, 1:5 * N + 1:5])
+    # the same bytes read as E2M1 weights give a different matrix: the element type is honoured
+    y2, _ = O.linear_ref_mx(ac, as_, O.E4M3, np.ascontiguousarray(oh[:, : K // 2]), ws, K, None)
+    assert not np.array_equal(y2, y1)
+
+
 def test_gelu_matches_torch_and_identities():
     y = np.concatenate([np.linspace(-12, 12, 4001), [0.0, -0.0, 1e-30, -1e-30]])
     g = O.gelu_tanh(y)
