@@ -1152,51 +1152,106 @@ __global__ void __launch_bounds__(256, 256 / BN) gemm_nv_ring_kernel(GemmParams 
 }
 
 // ---------------------------------------------------------------------------------------------
-// low-rank down projection u = bf16(x . down_t^T): a workgroup of 4 waves per 32 (r) x 32 (m)
-// block; wave w sums the 16-element K steps w, w + 4, ... with 4 steps' loads in flight, and the
-// four partial sums are added in the fixed order w = 0..3 (deterministic).
+// low-rank down projection u = bf16(x . down_t^T): one workgroup of 4 waves per 32 (m) x 32 (r)
+// block, wave w summing its own contiguous quarter of K.  A wave streams its 32 rows of x and of
+// down_t through a private 4-stage LDS ring of 64-element K chunks with direct-to-LDS loads: one
+// 1 KB load is 8 rows x 128 bytes, so every cache line is fetched whole by one instruction, and
+// three chunks (24 KB per wave) stay in flight.  One 32x32x16 BF16 MFMA
+// per 16 elements; the four partial sums are added in the fixed order w = 0..3 (deterministic).
+// LDS rows of 128 bytes hold their 16-byte pieces XOR-swizzled by ((row >> 1) & 7).
 // ---------------------------------------------------------------------------------------------
-__global__ void __launch_bounds__(256) lowrank_down_kernel(const uint16_t* __restrict__ x,
-                                                            int64_t ld_x,
-                                                            const uint16_t* __restrict__ down_t,
-                                                            int M, int K, int R,
-                                                            uint16_t* __restrict__ u) {
-  __shared__ float part[3][16][64];
-  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-  const int h = lane >> 5;
+constexpr int LR_WAVES = 4, LR_STG = 4, LR_KC = 64;
+constexpr int LR_HALF = 32 * LR_KC * 2;  // 32 rows x 128 bytes: one operand of a stage
+constexpr int LR_STAGE = 2 * LR_HALF;
+
+__global__ void __launch_bounds__(LR_WAVES * 64) lowrank_down_kernel(const uint16_t* __restrict__ x,
+                                                                     int64_t ld_x,
+                                                                     const uint16_t* __restrict__ down_t,
+                                                                     int M, int K, int R,
+                                                                     uint16_t* __restrict__ u) {
+  __shared__ __attribute__((aligned(16))) uint8_t smem[LR_WAVES * LR_STG * LR_STAGE];
+  const int lane = threadIdx.x & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int h = lane >> 5, r32 = lane & 31;
   const int rb = blockIdx.y * 32, mb = blockIdx.x * 32;
-  const int r = min(rb + (lane & 31), R - 1);
-  const int m = min(mb + (lane & 31), M - 1);
-  const uint16_t* dr = down_t + (int64_t)r * K + 8 * h;
-  const uint16_t* xr = x + (int64_t)m * ld_x + 8 * h;
+  auto clamp32 = [](uint64_t v) -> uint32_t { return v > 0xFFFFFFFFull ? 0xFFFFFFFFu : (uint32_t)v; };
+  // descriptors end at the last element of the block's last row: rows past M (R) and the
+  // elements past K of that row read as zero
+  const int xrows = min(32, M - mb), drows = min(32, R - rb);
+  const uint64_t xrow = (uint64_t)ld_x * 2, drow = (uint64_t)K * 2;
+  const v4i rx = make_rsrc_sgpr(x + (int64_t)mb * ld_x, clamp32((uint64_t)(xrows - 1) * xrow + drow));
+  const v4i rd = make_rsrc_sgpr(down_t + (int64_t)rb * K, clamp32((uint64_t)drows * drow));
+
+  const int nchunks = (K + LR_KC - 1) / LR_KC;
+  const int per = (nchunks + LR_WAVES - 1) / LR_WAVES;
+  const int cbeg = min(nchunks, wave * per), nc = min(nchunks, cbeg + per) - cbeg;
+
+  // load i of a chunk: rows 8i + lane / 8, LDS slot lane % 8 <- global piece slot ^ swizzle
+  uint32_t vx[4], vd[4];
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const int row = 8 * i + (lane >> 3);
+    const uint32_t piece = (uint32_t)((lane & 7) ^ ((row >> 1) & 7));
+    vx[i] = (uint32_t)row * (uint32_t)xrow + piece * 16u;
+    vd[i] = (uint32_t)row * (uint32_t)drow + piece * 16u;
+  }
+  const uint32_t lds_w = lds_addr_of(smem) + (uint32_t)(wave * LR_STG * LR_STAGE);
+  auto issue = [&](int c, int stg) {
+    v4i ax = rx, ad = rd;
+    if (c >= nc) { ax[2] = 0; ad[2] = 0; }  // past this wave's range: zero-filling empty loads
+    const uint32_t soff = (uint32_t)((cbeg + c) * LR_KC * 2);
+    const uint32_t sx = lds_w + (uint32_t)(stg * LR_STAGE);
+#pragma unroll
+    for (int i = 0; i < 4; ++i) dma_lds16(ax, sx + (uint32_t)(i * 1024), vx[i], soff);
+#pragma unroll
+    for (int i = 0; i < 4; ++i) dma_lds16(ad, sx + (uint32_t)(LR_HALF + i * 1024), vd[i], soff);
+  };
+
   v16f acc = v16f{};
-  for (int k0 = 16 * wave; k0 < K; k0 += 4 * 64) {
-    uint4 da[4], xb[4];
+  issue(0, 0);
+  issue(1, 1);
+  issue(2, 2);
+  const int swz = (r32 >> 1) & 7;
+  for (int c = 0; c < nc; ++c) {
+    wait_vmcnt<16>();  // chunk c landed; chunks c + 1 and c + 2 (8 loads each) may still fly
+    asm volatile("" ::: "memory");
+    const uint8_t* sx = smem + (wave * LR_STG + (c & 3)) * LR_STAGE;
+    const uint8_t* sd = sx + LR_HALF;
+    const int k0 = (cbeg + c) * LR_KC;
+    v4i fx[4], fd[4];
 #pragma unroll
-    for (int t = 0; t < 4; ++t) {
-      const int k = k0 + 64 * t;
-      da[t] = k < K ? *(const uint4*)(dr + k) : make_uint4(0, 0, 0, 0);
-      xb[t] = k < K ? *(const uint4*)(xr + k) : make_uint4(0, 0, 0, 0);
+    for (int j = 0; j < 4; ++j) {
+      const int off = r32 * 128 + (((2 * j + h) ^ swz) << 4);
+      fx[j] = *(const v4i*)(sx + off);
+      fd[j] = *(const v4i*)(sd + off);
+      if (k0 + 16 * j + 8 * h >= K) {  // past K (K % 32 == 0, so only whole pieces)
+        fx[j] = v4i{0, 0, 0, 0};
+        fd[j] = v4i{0, 0, 0, 0};
+      }
     }
+    issue(c + 3, (c + 3) & 3);  // into the stage of chunk c - 1, read last iteration
 #pragma unroll
-    for (int t = 0; t < 4; ++t) {
+    for (int j = 0; j < 4; ++j) {
       v8bf fa, fb;
-      __builtin_memcpy(&fa, &da[t], 16);
-      __builtin_memcpy(&fb, &xb[t], 16);
+      __builtin_memcpy(&fa, &fd[j], 16);
+      __builtin_memcpy(&fb, &fx[j], 16);
       acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fa, fb, acc, 0, 0, 0);
     }
   }
+  wait_vmem_all();
+  __syncthreads();  // every wave's loads and reads of the ring are done
+  float* part = (float*)smem;  // [LR_WAVES - 1][16][64]
   if (wave > 0) {
 #pragma unroll
-    for (int e = 0; e < 16; ++e) part[wave - 1][e][lane] = acc[e];
+    for (int e = 0; e < 16; ++e) part[((wave - 1) * 16 + e) * 64 + lane] = acc[e];
   }
   __syncthreads();
   if (wave > 0) return;
 #pragma unroll
-  for (int w = 0; w < 3; ++w)
+  for (int w = 0; w < LR_WAVES - 1; ++w)
 #pragma unroll
-    for (int e = 0; e < 16; ++e) acc[e] += part[w][e][lane];
-  const int mo = mb + (lane & 31);
+    for (int e = 0; e < 16; ++e) acc[e] += part[(w * 16 + e) * 64 + lane];
+  const int mo = mb + r32;
   if (mo >= M) return;
 #pragma unroll
   for (int e = 0; e < 16; ++e) {
@@ -1306,7 +1361,7 @@ hipError_t launch_lowrank_down(const uint16_t* x, int64_t ld_x, const uint16_t* 
                                int K, int R, uint16_t* u, hipStream_t s) {
   if (M == 0) return hipSuccess;
   dim3 grid((M + 31) / 32, (R + 31) / 32);
-  lowrank_down_kernel<<<grid, 256, 0, s>>>(x, ld_x, down_t, M, K, R, u);
+  lowrank_down_kernel<<<grid, LR_WAVES * 64, 0, s>>>(x, ld_x, down_t, M, K, R, u);
   return hipGetLastError();
 }
 
