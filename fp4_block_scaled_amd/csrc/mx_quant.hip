@@ -224,48 +224,105 @@ __device__ __forceinline__ NvThresholds nv_thresholds(double D, bool zero) {
   return th;
 }
 
+// One thread per 16-element group (two 16-byte loads), NV_U groups per thread and step, all
+// loaded before any is coded.  Every rounding below is exact; the fast paths are binary32
+// brackets:
+//  - Block scale sb = E4M3_rne_sat(amax / (6 sg)).  amax * (1/(6 sg)) in binary32 (product and
+//    reciprocal each within an ulp) is within 2^-22 of the exact quotient, so nudging it by 2^-20
+//    down and up brackets the quotient strictly; since RNE is monotone, equal E4M3 codes for the
+//    two ends are the exact code.  Otherwise the fp64 quotient decides (one rounding: an 8-bit by
+//    26-bit quotient never lands on a false E4M3 midpoint).
+//  - Elements: code = RNE(x / D), D = sb * sg, by the hardware FP32 -> E2M1 conversion of the two
+//    nudged products x * (1/D) * (1 -+ 2^-20).  Equal codes are the exact code; a group where any
+//    element's codes differ (within about 2^-20 of a midpoint, exact ties included), or where D
+//    or 6 sg is outside the normal binary32 range, is coded against exact thresholds instead.
+constexpr int NV_U = 2;
+
+// IDX: the group-index type, 32-bit when the group count allows (cheaper division)
+template <typename IDX>
 __global__ void __launch_bounds__(256) quant_nv_kernel(const uint16_t* __restrict__ x,
                                                         int64_t rows, int64_t cols, int64_t ld,
                                                         float sg, uint8_t* __restrict__ codes,
                                                         uint8_t* __restrict__ scales) {
-  const int64_t gpr = cols >> 4;       // 16-element groups per row
-  const int64_t total = rows * gpr * 2;  // two threads per group
-  const int64_t stride = (int64_t)gridDim.x * 256;
+  const IDX gpr = (IDX)(cols >> 4);  // 16-element groups per row
+  const IDX total = (IDX)rows * gpr;
   const double six_sg = 6.0 * (double)sg;
-  for (int64_t t = (int64_t)blockIdx.x * 256 + threadIdx.x; t < total; t += stride) {
-    const int64_t g = t >> 1;
-    const int part = (int)(t & 1);
-    const int64_t r = g / gpr;
-    const int64_t gc = g - r * gpr;
-    const uint4 v = load_stream16(x + r * ld + gc * 16 + part * 8);
-    uint32_t w[4] = {v.x, v.y, v.z, v.w};
-    uint32_t amax = 0;
+  constexpr float kLo = 1.0f - 0x1p-20f, kHi = 1.0f + 0x1p-20f;
+  const float c6 = 6.0f * sg;
+  const bool scale_fast = c6 >= 0x1p-125f && c6 <= 0x1p125f;
+  const float inv6 = __builtin_amdgcn_rcpf(c6);
+  const float inv6_lo = inv6 * kLo, inv6_hi = inv6 * kHi;
+  for (IDX base = (IDX)blockIdx.x * 256 * NV_U; base < total; base += (IDX)gridDim.x * 256 * NV_U) {
+    uint4 v[NV_U][2];
+    IDX rr[NV_U], gc[NV_U];
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      uint32_t lo = w[i] & 0x7FFFu, hi = (w[i] >> 16) & 0x7FFFu;
-      amax = max(amax, max(lo, hi));
+    for (int u = 0; u < NV_U; ++u) {
+      const IDX g = base + u * 256 + threadIdx.x;
+      rr[u] = g / gpr;
+      gc[u] = g - rr[u] * gpr;
+      const uint16_t* src = x + (int64_t)rr[u] * ld + (int64_t)gc[u] * 16;
+      v[u][0] = g < total ? load_stream16(src) : make_uint4(0, 0, 0, 0);
+      v[u][1] = g < total ? load_stream16(src + 8) : make_uint4(0, 0, 0, 0);
     }
-    amax = max(amax, quad_xor1(amax));
-    const bool bad = amax >= 0x7F80u;
-    // sb = E4M3_rne_sat(amax / (6 sg)): the fp64 quotient of an 8-bit by a 26-bit significand
-    // is never rounded onto a false E4M3 midpoint, so rounding it again is a single rounding.
-    const double qd = (double)bf16_to_f32(amax) / six_sg;
-    const uint32_t sbyte = e4m3_code_f64(qd);
-    const float sb = e4m3_value(sbyte);
-    const NvThresholds th = nv_thresholds((double)sb * (double)sg, sbyte == 0);
-    uint32_t packed = 0;
 #pragma unroll
-    for (int i = 0; i < 8; ++i) {
-      uint32_t b = (w[i >> 1] >> ((i & 1) * 16)) & 0xFFFFu;
-      float a = bf16_to_f32(b & 0x7FFFu);
-      uint32_t c = 0;
+    for (int u = 0; u < NV_U; ++u) {
+      const IDX g = base + u * 256 + threadIdx.x;
+      if (g >= total) continue;
+      const uint32_t w[8] = {v[u][0].x, v[u][0].y, v[u][0].z, v[u][0].w,
+                             v[u][1].x, v[u][1].y, v[u][1].z, v[u][1].w};
+      u16x2 m2 = {0, 0};  // per-half maxima of the magnitudes (packed 16-bit max)
 #pragma unroll
-      for (int j = 0; j < 7; ++j) c += a > th.t[j] ? 1u : 0u;
-      packed |= (c | ((b >> 12) & 8u)) << (4 * i);
+      for (int i = 0; i < 8; ++i) {
+        u16x2 mag;
+        const uint32_t wm = w[i] & 0x7FFF7FFFu;
+        __builtin_memcpy(&mag, &wm, 4);
+        m2 = __builtin_elementwise_max(m2, mag);
+      }
+      const uint32_t amax = max((uint32_t)m2.x, (uint32_t)m2.y);
+      const bool bad = amax >= 0x7F80u;
+      const float af = bf16_to_f32(amax);
+      uint32_t sbyte = e4m3_code(af * inv6_lo);
+      if (!scale_fast || sbyte != e4m3_code(af * inv6_hi)) sbyte = e4m3_code_f64((double)af / six_sg);
+      const float sb = e4m3_value(sbyte);
+      const float d32 = sb * sg;
+      uint32_t out0 = 0, out1 = 0;
+      bool exact = !(d32 >= 0x1p-125f && d32 <= 0x1p125f);
+      if (!exact) {
+        const float inv = __builtin_amdgcn_rcpf(d32);
+        const float il = inv * kLo, ih = inv * kHi;
+        uint32_t lo0 = 0, hi0 = 0, lo1 = 0, hi1 = 0;
+        static_for<4>([&](auto q) {
+          constexpr int Q = decltype(q)::value;
+          const float a0 = bf16_to_f32(w[Q] & 0xFFFFu), a1 = __uint_as_float(w[Q] & 0xFFFF0000u);
+          const float b0 = bf16_to_f32(w[4 + Q] & 0xFFFFu), b1 = __uint_as_float(w[4 + Q] & 0xFFFF0000u);
+          lo0 = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(lo0, a0 * il, a1 * il, 1.0f, Q);
+          hi0 = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(hi0, a0 * ih, a1 * ih, 1.0f, Q);
+          lo1 = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(lo1, b0 * il, b1 * il, 1.0f, Q);
+          hi1 = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(hi1, b0 * ih, b1 * ih, 1.0f, Q);
+        });
+        exact = (lo0 != hi0) | (lo1 != hi1);
+        out0 = lo0;
+        out1 = lo1;
+      }
+      if (exact) {
+        const NvThresholds th = nv_thresholds((double)sb * (double)sg, sbyte == 0);
+        out0 = out1 = 0;
+#pragma unroll
+        for (int i = 0; i < 16; ++i) {
+          const uint32_t b = (w[i >> 1] >> ((i & 1) * 16)) & 0xFFFFu;
+          const float a = bf16_to_f32(b & 0x7FFFu);
+          uint32_t c = 0;
+#pragma unroll
+          for (int j = 0; j < 7; ++j) c += a > th.t[j] ? 1u : 0u;
+          c |= (b >> 12) & 8u;
+          if (i < 8) out0 |= c << (4 * i);
+          else out1 |= c << (4 * (i - 8));
+        }
+      }
+      if (bad) out0 = out1 = 0;
+      *(uint2*)(codes + (int64_t)rr[u] * (cols >> 1) + (int64_t)gc[u] * 8) = make_uint2(out0, out1);
+      scales[(int64_t)rr[u] * gpr + (int64_t)gc[u]] = bad ? (uint8_t)0x7F : (uint8_t)sbyte;
     }
-    if (bad) packed = 0;
-    *(uint32_t*)(codes + r * (cols >> 1) + gc * 8 + part * 4) = packed;
-    if (part == 0) scales[r * gpr + gc] = bad ? (uint8_t)0x7F : (uint8_t)sbyte;
   }
 }
 
@@ -395,9 +452,14 @@ hipError_t launch_relayout(const uint8_t* src_codes, const uint8_t* src_scales, 
 
 hipError_t launch_quant_nv(const uint16_t* x, int64_t rows, int64_t cols, int64_t ld, float sg,
                            uint8_t* codes, uint8_t* scales, hipStream_t s) {
-  const int64_t threads = rows * (cols / 16) * 2;
-  if (threads == 0) return hipSuccess;
-  quant_nv_kernel<<<grid_for(threads), 256, 0, s>>>(x, rows, cols, ld, sg, codes, scales);
+  const int64_t groups = rows * (cols / 16);
+  if (groups == 0) return hipSuccess;
+  const int grid = grid_for((groups + NV_U - 1) / NV_U);
+  // the 32-bit index must also hold the last step's base + the step without wrapping
+  if (groups + (int64_t)grid * 256 * NV_U < ((int64_t)1 << 32))
+    quant_nv_kernel<uint32_t><<<grid, 256, 0, s>>>(x, rows, cols, ld, sg, codes, scales);
+  else
+    quant_nv_kernel<int64_t><<<grid, 256, 0, s>>>(x, rows, cols, ld, sg, codes, scales);
   return hipGetLastError();
 }
 

@@ -114,6 +114,18 @@ def test_nv_quantizer_exhaustive_bf16(mx):
         np.testing.assert_array_equal(c, ref_c, err_msg=f"anchor {a:#06x}")
 
 
+@pytest.mark.parametrize("rows,cols,ld", [(1, 16, 16), (3, 96, 104), (257, 528, 536), (1000, 3072, 3072)])
+def test_nv_quantizer_shapes_and_strides(mx, rows, cols, ld):
+    sg = float(np.float32(40.0 / 2688.0))
+    full = activation_bits(rows, ld, seed_base=7500 + cols, factor=30.0)
+    x = to_dev_bf16(full)[:, :cols]
+    q = mx.quantize(x, "nvfp4", sg)
+    torch.cuda.synchronize()
+    ref_c, ref_s = O.quantize_nv_bf16(np.ascontiguousarray(full[:, :cols]), sg)
+    np.testing.assert_array_equal(q.scales.cpu().numpy(), ref_s)
+    np.testing.assert_array_equal(q.codes.cpu().numpy(), ref_c)
+
+
 @pytest.mark.parametrize("rows,cols,ld", [(1, 32, 32), (3, 96, 104), (257, 512, 512),
                                           (1000, 3072, 3072)])
 @pytest.mark.parametrize("fmt,elem", [("mxfp4", O.E2M1), ("mxfp8", O.E4M3)])
