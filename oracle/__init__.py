@@ -68,6 +68,8 @@ def lib():
         L.mxr_bf16_rne_array.restype = None
         L.mxr_absmax_bf16.argtypes = [_P, _I, _I, _I]
         L.mxr_absmax_bf16.restype = ctypes.c_double
+        L.mxr_norm_modulate.argtypes = [_P, _I, _I, _I, ctypes.c_double, _P, _P, _P, _P, _P]
+        L.mxr_norm_modulate.restype = None
         _lib = L
     return _lib
 
@@ -277,3 +279,22 @@ def linear_ref_nv(a_codes, a_scales, sg_a, w_codes, w_scales, sg_w, K, bias_f16_
     w = dequantize_nv(w_codes, w_scales, sg_w, K)
     bias = None if bias_f16_bits is None else f16_values(bias_f16_bits)
     return gemm(a, w, bias)
+
+
+# ---- the producer of a quantized linear's input --------------------------------------------
+def norm_modulate(x_bits, eps: float, gamma=None, beta=None, scale=None, shift=None) -> np.ndarray:
+    """fp64 h = LayerNorm(x) [* gamma + beta] [* (1 + scale) + shift] per row (see
+    mxr_norm_modulate); the vectors are F32 [cols] or None."""
+    x, px = _c(x_bits, np.uint16)
+    rows, cols = x.shape
+    vecs = []
+    for v in (gamma, beta, scale, shift):
+        if v is None:
+            vecs.append((None, None))
+        else:
+            a, pa = _c(v, np.float32)
+            assert a.shape == (cols,)
+            vecs.append((a, pa))
+    h = np.empty((rows, cols), dtype=np.float64)
+    lib().mxr_norm_modulate(px, rows, cols, cols, float(eps), *[p for _, p in vecs], h.ctypes.data)
+    return h

@@ -16,6 +16,9 @@
  *    scale static (calibrated).
  *  - "Wan2.2 W4A8 SVDQuant - NVIDIA (CUDA) artifacts": MXFP4 weights x dynamic MXFP8
  *    activations + a rank-32 low-rank correction with BF16 factors.
+ *  - "Wan2.2-I2V-A14B-Lightning-Diffusers-MXFP4-AutoRound", Quantization Details, list of layers
+ *    kept at higher precision (norm, modulation table): the LayerNorm + modulation that produces
+ *    a quantized linear's input (mxr_norm_modulate).
  * The pages name these formats but do not define them bit by bit; the element and scale
  * encodings follow the OCP Microscaling (MX) v1.0 specification that the "MX" names refer to.
  * Every reading taken where the pages are silent is listed in the design notes; each function
@@ -443,4 +446,39 @@ double mxr_absmax_bf16(const uint16_t* x, int64_t rows, int64_t cols, int64_t ld
 void mxr_bf16_rne_array(const double* v, int64_t n, uint16_t* out) {
 #pragma omp parallel for schedule(static)
     for (int64_t i = 0; i < n; ++i) out[i] = mxr_bf16_rne(v[i]);
+}
+
+/* ------------------------------------------------------------------------------------------ */
+/* The layer in front of a quantized linear: LayerNorm and modulation                         */
+/* ------------------------------------------------------------------------------------------ */
+/* "Wan2.2-I2V-A14B-Lightning-Diffusers-MXFP4-AutoRound", Quantization Details: the quantized
+ * linears quantize their activations dynamically, and the layers kept at higher precision in
+ * front of them include the norm and the modulation table (F32).  The pages do not write these
+ * layers out.  This is the textbook LayerNorm of a row (mean, biased variance, eps inside the
+ * square root), an optional per-column affine y * gamma + beta, then the optional per-column
+ * modulation y * (1 + scale) + shift.  fp64 throughout, from the exact BF16 / F32 inputs; a NULL
+ * vector is the identity (gamma 1, beta 0, scale 0, shift 0).  h is [rows, cols], contiguous. */
+void mxr_norm_modulate(const uint16_t* x, int64_t rows, int64_t cols, int64_t ld, double eps,
+                       const float* gamma, const float* beta, const float* scale,
+                       const float* shift, double* h) {
+#pragma omp parallel for schedule(static)
+    for (int64_t r = 0; r < rows; ++r) {
+        const uint16_t* xr = x + r * ld;
+        double mean = 0.0;
+        for (int64_t k = 0; k < cols; ++k) mean += mxr_bf16_value(xr[k]);
+        mean /= (double)cols;
+        double var = 0.0;
+        for (int64_t k = 0; k < cols; ++k) {
+            double d = mxr_bf16_value(xr[k]) - mean;
+            var += d * d;
+        }
+        var /= (double)cols;
+        double rstd = 1.0 / sqrt(var + eps);
+        for (int64_t k = 0; k < cols; ++k) {
+            double y = (mxr_bf16_value(xr[k]) - mean) * rstd;
+            y = y * (gamma ? (double)gamma[k] : 1.0) + (beta ? (double)beta[k] : 0.0);
+            y = y * (1.0 + (scale ? (double)scale[k] : 0.0)) + (shift ? (double)shift[k] : 0.0);
+            h[r * cols + k] = y;
+        }
+    }
 }

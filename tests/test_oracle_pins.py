@@ -485,3 +485,49 @@ def test_generator_is_deterministic_and_normal():
     ratio = np.abs(x / np.where(plain == 0, 1, plain))
     cols = np.where(np.all(np.isclose(ratio, 20.0), axis=0))[0]
     assert sorted(cols.tolist()) == sorted(idx.tolist())
+
+
+# ---------------------------------------------------------------------------------------------
+# the producer in front of a quantized linear: LayerNorm + modulation
+# ---------------------------------------------------------------------------------------------
+def _f32(seed, n, sigma, mean=0.0):
+    return (synth.normal_f32(seed, (n,), sigma) + np.float32(mean)).astype(np.float32)
+
+
+def test_norm_modulate_matches_torch_layer_norm():
+    """torch's float64 layer_norm is an independent implementation of the normalization."""
+    rows, cols = 7, 320
+    x_bits = synth.bits16(synth.to_bf16(synth.activation_f32(61, rows, cols, 1.0, 0.02, 30.0)))
+    x = O.bf16_values(x_bits)
+    g, b = _f32(62, cols, 0.1, 1.0), _f32(63, cols, 0.1)
+    for eps in (1e-6, 1e-2):
+        ref = torch.nn.functional.layer_norm(torch.from_numpy(x), (cols,), eps=eps).numpy()
+        np.testing.assert_allclose(O.norm_modulate(x_bits, eps), ref, rtol=1e-12, atol=1e-12)
+        ref_aff = torch.nn.functional.layer_norm(torch.from_numpy(x), (cols,),
+                                                 torch.from_numpy(g.astype(np.float64)),
+                                                 torch.from_numpy(b.astype(np.float64)), eps).numpy()
+        np.testing.assert_allclose(O.norm_modulate(x_bits, eps, gamma=g, beta=b), ref_aff,
+                                   rtol=1e-12, atol=1e-12)
+
+
+def test_norm_modulate_identities():
+    rows, cols = 5, 256
+    x_bits = synth.bits16(synth.to_bf16(synth.activation_f32(64, rows, cols, 1.0, 0.0, 1.0)))
+    s, t = _f32(65, cols, 0.2), _f32(66, cols, 0.3)
+    h = O.norm_modulate(x_bits, 0.0)
+    # eps = 0: zero mean and unit (biased) variance per row
+    np.testing.assert_allclose(h.mean(axis=1), 0.0, atol=1e-14)
+    np.testing.assert_allclose((h * h).mean(axis=1), 1.0, rtol=1e-13)
+    # eps = 0: invariant under x -> 2x (exact in both BF16 and fp64)
+    x2 = O.bf16_rne_array(2.0 * O.bf16_values(x_bits))
+    np.testing.assert_array_equal(O.norm_modulate(x2, 0.0), h)
+    # modulation is applied after the normalization, per column
+    hm = O.norm_modulate(x_bits, 0.0, scale=s, shift=t)
+    np.testing.assert_allclose(hm, h * (1.0 + s.astype(np.float64)) + t.astype(np.float64),
+                               rtol=1e-15, atol=1e-15)
+    # a constant row (exact sums) normalizes to 0, so the output is beta * (1 + scale) + shift
+    const = np.full((1, cols), 0x3FC0, dtype=np.uint16)  # 1.5
+    b = _f32(67, cols, 0.5)
+    hc = O.norm_modulate(const, 1e-6, beta=b, scale=s, shift=t)
+    np.testing.assert_array_equal(hc[0], b.astype(np.float64) * (1.0 + s.astype(np.float64))
+                                  + t.astype(np.float64))
