@@ -184,7 +184,8 @@ def bench_mx_linear(args, torch, mx, synth):
 
 
 def bench_variant(args, torch, mx, synth):
-    """Variant workloads (not the headline metric): FFN pair, W4A8 SVDQuant, MXFP8 W8A8, NVFP4."""
+    """Variant workloads (not the headline metric): FFN pair, W4A8 SVDQuant, MXFP8 W8A8, NVFP4,
+    and the producer-fused quantizer."""
     import numpy as np
     wl = synth.WORKLOADS[args.workload]
     M, K, N = wl.M, wl.K, wl.N
@@ -245,6 +246,29 @@ def bench_variant(args, torch, mx, synth):
         aq = mx.quantize(a, "nvfp4", sg_a)
         kernels["gemm_ms"] = time_events(lambda: mx.linear_q(aq, wq, bias, out=out), args.steps, torch)
         kernels["quant_nvfp4_ms"] = time_events(lambda: mx.quantize(a, "nvfp4", sg_a, out=aq), args.steps, torch)
+    elif wl.fmt == "norm":
+        # the producer in front of the linear, fused with its quantizer, against the unfused pair
+        sc, sh = wl.modulation()
+        mod = {"scale": torch.from_numpy(sc).cuda(), "shift": torch.from_numpy(sh).cuda()}
+        q = mx.norm_quantize(a, 1e-6, fmt="mxfp4", layout="tiled", **mod)
+        h = mx.norm(a, 1e-6, **mod)
+        aq = mx.empty_qmatrix(M, K, "mxfp4", layout="tiled")
+        step = lambda: mx.norm_quantize(a, 1e-6, fmt="mxfp4", layout="tiled", out=q, **mod)
+        kernels["norm_bf16_ms"] = time_events(lambda: mx.norm(a, 1e-6, out=h, **mod), args.steps, torch)
+        kernels["quantize_ms"] = time_events(lambda: mx.quantize(h, "mxfp4", out=aq), args.steps, torch)
+        kernels["unfused_ms"] = kernels["norm_bf16_ms"] + kernels["quantize_ms"]
+        for _ in range(args.warmup):
+            step()
+        ms = time_events(step, args.steps, torch)
+        byts = M * K * 2 + M * K // 2 + M * K // 32 + 2 * K * 4
+        v = byts / (ms * 1e-3) / 1e9
+        kernels["speedup_vs_unfused"] = kernels["unfused_ms"] / ms
+        return {"metric": f"{wl.name} GB/s (LayerNorm + modulation + MXFP4 quantization, fused)",
+                "value": v, "unit": "GB/s", "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,
+                "ms_per_step": ms, "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
+                "dtype": "bf16->mxfp4", "data": "synthetic",
+                "config": {"workload": wl.name, "M": M, "K": K, "algorithmic_bytes": byts},
+                "frac_of_peak": v / HBM_GBPS, "peak_gbps": HBM_GBPS, "kernels": kernels}
     else:
         raise SystemExit(f"unknown variant workload {args.workload}")
     for _ in range(args.warmup):

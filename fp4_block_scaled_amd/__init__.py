@@ -77,8 +77,11 @@ def lib():
                                 ctypes.POINTER(_LowRank), I32, I32, P, I64, P, P, ctypes.c_size_t, P]
         L.mx_linear_q.argtypes = [ctypes.POINTER(_QMatrix), ctypes.POINTER(_QMatrix), P, I32, I32,
                                   P, I64, P, P]
+        F = ctypes.c_float
+        L.mx_norm.argtypes = [P, I64, I64, I64, F, P, P, P, P, P, I64, P]
+        L.mx_norm_quantize.argtypes = [P, I64, I64, I64, F, P, P, P, P, I32, I32, P, P, P]
         for f in ("mx_quantize", "mx_dequantize", "mx_absmax", "mx_linear", "mx_linear_q",
-                  "mx_tiled_bytes", "mx_relayout"):
+                  "mx_tiled_bytes", "mx_relayout", "mx_norm", "mx_norm_quantize"):
             getattr(L, f).restype = ctypes.c_int
         if L.mx_abi_version() != 2:
             raise MxError("libmxfp.so ABI version mismatch")
@@ -185,6 +188,45 @@ def quantize(x: torch.Tensor, fmt="mxfp4", global_scale: float = 1.0,
     q.global_scale = global_scale
     _check(lib().mx_quantize(_ptr(x), rows, cols, _ld(x), fmt, q.layout, global_scale,
                              _ptr(q.codes), _ptr(q.scales), _stream()))
+    return q
+
+
+def _vec(v, cols, name):
+    if v is None:
+        return None
+    _need_cuda(v, name, torch.float32)
+    if v.dim() != 1 or v.shape[0] != cols or not v.is_contiguous():
+        raise MxError(f"{name} must be a contiguous float32 vector of length {cols}")
+    return _ptr(v)
+
+
+def norm(x: torch.Tensor, eps: float = 1e-6, gamma=None, beta=None, scale=None, shift=None,
+         out: Optional[torch.Tensor] = None) -> torch.Tensor:
+    """BF16 h = LayerNorm(x) [* gamma + beta] [* (1 + scale) + shift] (the unfused producer)."""
+    _need_cuda(x, "x", torch.bfloat16)
+    if x.dim() != 2 or x.stride(1) != 1:
+        raise MxError("x must be 2-D with unit column stride")
+    rows, cols = x.shape
+    y = out if out is not None else torch.empty((rows, cols), dtype=torch.bfloat16, device=x.device)
+    _check(lib().mx_norm(_ptr(x), rows, cols, _ld(x), float(eps), _vec(gamma, cols, "gamma"),
+                         _vec(beta, cols, "beta"), _vec(scale, cols, "scale"),
+                         _vec(shift, cols, "shift"), _ptr(y), _ld(y), _stream()))
+    return y
+
+
+def norm_quantize(x: torch.Tensor, eps: float = 1e-6, gamma=None, beta=None, scale=None, shift=None,
+                  fmt="mxfp4", layout="tiled", out: Optional[QMatrix] = None) -> QMatrix:
+    """The producer fused with the quantizer: Q(bf16(h)) with h as in norm(), in `layout`."""
+    fmt = _fmt(fmt)
+    _need_cuda(x, "x", torch.bfloat16)
+    if x.dim() != 2 or x.stride(1) != 1:
+        raise MxError("x must be 2-D with unit column stride")
+    rows, cols = x.shape
+    q = out if out is not None else empty_qmatrix(rows, cols, fmt, x.device, 1.0, layout)
+    _check(lib().mx_norm_quantize(_ptr(x), rows, cols, _ld(x), float(eps), _vec(gamma, cols, "gamma"),
+                                  _vec(beta, cols, "beta"), _vec(scale, cols, "scale"),
+                                  _vec(shift, cols, "shift"), fmt, q.layout, _ptr(q.codes),
+                                  _ptr(q.scales), _stream()))
     return q
 
 

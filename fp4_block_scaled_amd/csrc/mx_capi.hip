@@ -190,6 +190,60 @@ mx_status mx_quantize(const uint16_t* x, int64_t rows, int64_t cols, int64_t ld_
   return hip_status(e, "mx_quantize launch");
 }
 
+// Checks shared by mx_norm and mx_norm_quantize (the input side).
+static mx_status check_norm_in(const uint16_t* x, int64_t rows, int64_t cols, int64_t ld_x, float eps,
+                               const float* gamma, const float* beta, const float* scale,
+                               const float* shift) {
+  if (rows < 0 || cols <= 0 || cols % 32) return fail(MX_ERR_SHAPE, "rows >= 0 and cols %% 32 == 0 (cols > 0) needed");
+  if (cols > MX_NORM_MAX_COLS) return fail(MX_ERR_SHAPE, "cols (%lld) > %d", (long long)cols, MX_NORM_MAX_COLS);
+  if (ld_x < cols) return fail(MX_ERR_SHAPE, "ld_x < cols");
+  if (!(eps > 0.0f) || !isfinite(eps)) return fail(MX_ERR_SHAPE, "eps must be finite and > 0");
+  const float* vecs[4] = {gamma, beta, scale, shift};
+  for (const float* v : vecs)
+    if (v && !aligned(v, 4)) return fail(MX_ERR_ALIGN, "gamma / beta / scale / shift need 4-byte alignment");
+  if (rows != 0 && !x) return fail(MX_ERR_NULL, "x is NULL");
+  if (rows != 0 && (!aligned(x, 16) || ld_x % 8)) return fail(MX_ERR_ALIGN, "x needs 16-byte alignment and ld_x %% 8 == 0");
+  return MX_OK;
+}
+
+mx_status mx_norm(const uint16_t* x, int64_t rows, int64_t cols, int64_t ld_x, float eps,
+                  const float* gamma, const float* beta, const float* scale, const float* shift,
+                  uint16_t* y, int64_t ld_y, void* stream) {
+  g_err[0] = 0;
+  mx_status st = check_norm_in(x, rows, cols, ld_x, eps, gamma, beta, scale, shift);
+  if (st != MX_OK) return st;
+  if (ld_y < cols) return fail(MX_ERR_SHAPE, "ld_y < cols");
+  if (rows == 0) return MX_OK;
+  if (!y) return fail(MX_ERR_NULL, "y is NULL");
+  if (!aligned(y, 16) || ld_y % 8) return fail(MX_ERR_ALIGN, "y needs 16-byte alignment and ld_y %% 8 == 0");
+  return hip_status(mxk::launch_norm_quant(x, rows, cols, ld_x, eps, gamma, beta, scale, shift, 0, 0, y,
+                                           ld_y, nullptr, nullptr, (hipStream_t)stream),
+                    "mx_norm launch");
+}
+
+mx_status mx_norm_quantize(const uint16_t* x, int64_t rows, int64_t cols, int64_t ld_x, float eps,
+                           const float* gamma, const float* beta, const float* scale,
+                           const float* shift, int32_t fmt, int32_t layout, void* codes,
+                           uint8_t* scales, void* stream) {
+  g_err[0] = 0;
+  if (fmt != MX_FMT_MXFP4 && fmt != MX_FMT_MXFP8)
+    return fail(MX_ERR_UNSUPPORTED, "mx_norm_quantize writes MXFP4 or MXFP8 (format %d)", fmt);
+  if (layout != MX_LAYOUT_ROW_MAJOR && layout != MX_LAYOUT_TILED)
+    return fail(MX_ERR_UNSUPPORTED, "unknown layout %d", layout);
+  const bool tiled = layout == MX_LAYOUT_TILED;
+  mx_status st = check_norm_in(x, rows, cols, ld_x, eps, gamma, beta, scale, shift);
+  if (st != MX_OK) return st;
+  if (tiled && cols % 128) return fail(MX_ERR_SHAPE, "the tiled layout needs cols %% 128 == 0");
+  if (rows == 0) return MX_OK;
+  if (!codes || !scales) return fail(MX_ERR_NULL, "codes and scales must be non-NULL");
+  if (tiled ? !aligned(codes, 16) || !aligned(scales, 16) : !aligned(codes, fmt == MX_FMT_MXFP8 ? 8 : 4))
+    return fail(MX_ERR_ALIGN, tiled ? "tiled codes and scales need 16-byte alignment" : "codes misaligned");
+  return hip_status(mxk::launch_norm_quant(x, rows, cols, ld_x, eps, gamma, beta, scale, shift,
+                                           tiled ? 2 : 1, fmt == MX_FMT_MXFP8 ? 1 : 0, nullptr, 0,
+                                           (uint8_t*)codes, scales, (hipStream_t)stream),
+                    "mx_norm_quantize launch");
+}
+
 mx_status mx_tiled_bytes(int64_t rows, int64_t cols, int32_t fmt, size_t* code_bytes_out,
                          size_t* scale_bytes_out) {
   g_err[0] = 0;

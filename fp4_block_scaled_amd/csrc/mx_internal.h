@@ -17,6 +17,12 @@ hipError_t launch_quant_mx_tiled(const uint16_t* x, int64_t rows, int64_t cols, 
 hipError_t launch_relayout(const uint8_t* src_codes, const uint8_t* src_scales, uint8_t* dst_codes,
                            uint8_t* dst_scales, int64_t rows, int64_t cols, int elem, bool to_tiled,
                            hipStream_t s);
+// LayerNorm (+ affine) + modulation of a BF16 [rows, cols] matrix, then: out_kind 0 BF16 y,
+// 1 MX codes row-major, 2 MX codes tiled (elem 0 E2M1, 1 E4M3).  cols <= 7680.
+hipError_t launch_norm_quant(const uint16_t* x, int64_t rows, int64_t cols, int64_t ld, float eps,
+                             const float* gamma, const float* beta, const float* scale,
+                             const float* shift, int out_kind, int elem, uint16_t* y, int64_t ld_y,
+                             uint8_t* codes, uint8_t* scales, hipStream_t s);
 hipError_t launch_quant_nv(const uint16_t* x, int64_t rows, int64_t cols, int64_t ld, float sg,
                            uint8_t* codes, uint8_t* scales, hipStream_t s);
 hipError_t launch_dequant(const uint8_t* codes, const uint8_t* scales, int64_t rows, int64_t cols,

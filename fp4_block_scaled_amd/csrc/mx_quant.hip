@@ -151,6 +151,186 @@ __global__ void __launch_bounds__(256) quant_mx_tiled_kernel(const uint16_t* __r
   }
 }
 
+// ---------------------------------------------------------------------------------------------
+// Producer-fused quantizer: LayerNorm (+ affine) and modulation, then the MX group quantizer
+// ---------------------------------------------------------------------------------------------
+// A workgroup of NW <= 8 waves handles 4 rows per step (two workgroups per compute unit overlap
+// each other's loads and barriers).  Wave w owns CPW consecutive 128-column chunks; a lane holds
+// 8 columns (8 (lane & 15) ..) of each chunk in row lane >> 4.
+// Row sums, then sums of squared deviations (two passes over the registers), are reduced across
+// the 16 lanes of a row and then across the waves through LDS in a fixed order, so every wave
+// sees the same mean and rstd.  h = (x - mean) * rstd * A[c] + B[c], with A = gamma (1 + scale)
+// and B = beta (1 + scale) + shift built once per workgroup in LDS, is rounded to BF16; the MX
+// quantizer then codes that BF16 tensor exactly as the standalone quantizer would (same group
+// routine).  OUT 0 writes the BF16 h instead (the unfused producer).  Padding rows of a tiled
+// output get zero codes and zero scale bytes.
+constexpr int NORM_ROWS = 4, NORM_WAVES = 8, NORM_RPL = NORM_ROWS / 4;  // rows per lane
+
+template <int ELEM, int OUT, int CPW>  // OUT 0: BF16 h, 1: codes row-major, 2: codes tiled
+__global__ void __launch_bounds__(NORM_WAVES * 64, 2) norm_quant_kernel(const uint16_t* __restrict__ x, int64_t rows,
+                                                          int64_t cols, int64_t ld, float eps,
+                                                          const float* __restrict__ gamma,
+                                                          const float* __restrict__ beta,
+                                                          const float* __restrict__ scale,
+                                                          const float* __restrict__ shift,
+                                                          uint16_t* __restrict__ y, int64_t ld_y,
+                                                          uint8_t* __restrict__ codes,
+                                                          uint8_t* __restrict__ scales) {
+  extern __shared__ float norm_lds[];  // A[cols], B[cols], psum[waves][16 rows], psq[waves][16 rows]
+  const int nw = (int)(blockDim.x >> 6);
+  const int lane = threadIdx.x & 63;
+  const int wave = __builtin_amdgcn_readfirstlane((int)(threadIdx.x >> 6));
+  float* A = norm_lds;
+  float* B = A + cols;
+  float* psum = B + cols;
+  float* psq = psum + NORM_WAVES * NORM_ROWS;
+  for (int64_t c = threadIdx.x; c < cols; c += blockDim.x) {
+    const float s1 = 1.0f + (scale ? scale[c] : 0.0f);
+    A[c] = (gamma ? gamma[c] : 1.0f) * s1;
+    B[c] = (beta ? beta[c] : 0.0f) * s1 + (shift ? shift[c] : 0.0f);
+  }
+  __syncthreads();
+
+  const int64_t nkc = (cols + 127) >> 7;
+  const int rsub = lane >> 4, cs = lane & 15;
+  const int g4 = cs >> 2, part = cs & 3;
+  const float inv_n = 1.0f / (float)cols;
+  const int64_t nrb = (OUT == 2 ? tiled_rows(rows) : rows + NORM_ROWS - 1) / NORM_ROWS;
+  // the rows of step rb (zero past the matrix); the next step's are loaded before this one is
+  // reduced, so their latency overlaps this step's work
+  auto fetch = [&](int64_t rb, uint4 (&dst)[CPW][NORM_RPL]) {
+#pragma unroll
+    for (int c = 0; c < CPW; ++c) {
+      const int64_t col = (int64_t)(wave * CPW + c) * 128 + cs * 8;
+#pragma unroll
+      for (int i = 0; i < NORM_RPL; ++i) {
+        const int64_t r = rb * NORM_ROWS + rsub + 4 * i;
+        dst[c][i] = rb < nrb && r < rows && col < cols ? load_stream16(x + r * ld + col) : make_uint4(0, 0, 0, 0);
+      }
+    }
+  };
+  uint4 vn[CPW][NORM_RPL];
+  fetch(blockIdx.x, vn);
+  for (int64_t rb = blockIdx.x; rb < nrb; rb += gridDim.x) {
+    const int64_t r0 = rb * NORM_ROWS;
+    uint4 v[CPW][NORM_RPL];
+#pragma unroll
+    for (int c = 0; c < CPW; ++c)
+#pragma unroll
+      for (int i = 0; i < NORM_RPL; ++i) v[c][i] = vn[c][i];
+    fetch(rb + gridDim.x, vn);
+    // pass 1: row sums (columns past cols read as zero)
+    float acc[NORM_RPL];
+#pragma unroll
+    for (int i = 0; i < NORM_RPL; ++i) acc[i] = 0.0f;
+#pragma unroll
+    for (int c = 0; c < CPW; ++c)
+#pragma unroll
+      for (int i = 0; i < NORM_RPL; ++i) {
+        const uint32_t w[4] = {v[c][i].x, v[c][i].y, v[c][i].z, v[c][i].w};
+#pragma unroll
+        for (int e = 0; e < 4; ++e) acc[i] += bf16_to_f32(w[e] & 0xFFFFu) + __uint_as_float(w[e] & 0xFFFF0000u);
+      }
+#pragma unroll
+    for (int i = 0; i < NORM_RPL; ++i)
+#pragma unroll
+      for (int m = 1; m < 16; m <<= 1) acc[i] += __shfl_xor(acc[i], m);
+    if (cs == 0)
+#pragma unroll
+      for (int i = 0; i < NORM_RPL; ++i) psum[wave * NORM_ROWS + rsub + 4 * i] = acc[i];
+    __syncthreads();
+    float mean[NORM_RPL];
+#pragma unroll
+    for (int i = 0; i < NORM_RPL; ++i) {
+      float t = 0.0f;
+      for (int w = 0; w < nw; ++w) t += psum[w * NORM_ROWS + rsub + 4 * i];
+      mean[i] = t * inv_n;
+    }
+    // pass 2: sums of squared deviations over the valid columns
+#pragma unroll
+    for (int i = 0; i < NORM_RPL; ++i) acc[i] = 0.0f;
+#pragma unroll
+    for (int c = 0; c < CPW; ++c) {
+      const bool valid = (int64_t)(wave * CPW + c) * 128 + cs * 8 < cols;
+#pragma unroll
+      for (int i = 0; i < NORM_RPL; ++i) {
+        const uint32_t w[4] = {v[c][i].x, v[c][i].y, v[c][i].z, v[c][i].w};
+        float q = 0.0f;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          const float d0 = bf16_to_f32(w[e] & 0xFFFFu) - mean[i];
+          const float d1 = __uint_as_float(w[e] & 0xFFFF0000u) - mean[i];
+          q += d0 * d0 + d1 * d1;
+        }
+        acc[i] += valid ? q : 0.0f;
+      }
+    }
+#pragma unroll
+    for (int i = 0; i < NORM_RPL; ++i)
+#pragma unroll
+      for (int m = 1; m < 16; m <<= 1) acc[i] += __shfl_xor(acc[i], m);
+    if (cs == 0)
+#pragma unroll
+      for (int i = 0; i < NORM_RPL; ++i) psq[wave * NORM_ROWS + rsub + 4 * i] = acc[i];
+    __syncthreads();
+    float rstd[NORM_RPL];
+#pragma unroll
+    for (int i = 0; i < NORM_RPL; ++i) {
+      float t = 0.0f;
+      for (int w = 0; w < nw; ++w) t += psq[w * NORM_ROWS + rsub + 4 * i];
+      rstd[i] = __builtin_amdgcn_rsqf(t * inv_n + eps);
+    }
+    // pass 3: h, BF16, then the output
+#pragma unroll
+    for (int c = 0; c < CPW; ++c) {
+      const int64_t kb = wave * CPW + c;
+      if (kb >= nkc) break;  // uniform across the wave
+      const int64_t col = kb * 128 + cs * 8;
+      const bool valid = col < cols;
+      float a[8], b[8];
+      if (valid) {
+        *(float4*)&a[0] = *(const float4*)&A[col];
+        *(float4*)&a[4] = *(const float4*)&A[col + 4];
+        *(float4*)&b[0] = *(const float4*)&B[col];
+        *(float4*)&b[4] = *(const float4*)&B[col + 4];
+      } else {
+#pragma unroll
+        for (int e = 0; e < 8; ++e) a[e] = b[e] = 0.0f;
+      }
+#pragma unroll
+      for (int i = 0; i < NORM_RPL; ++i) {
+        const int64_t r = r0 + rsub + 4 * i;
+        const uint32_t w[4] = {v[c][i].x, v[c][i].y, v[c][i].z, v[c][i].w};
+        uint32_t hb[4];
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          const float h0 = (bf16_to_f32(w[e] & 0xFFFFu) - mean[i]) * rstd[i] * a[2 * e] + b[2 * e];
+          const float h1 = (__uint_as_float(w[e] & 0xFFFF0000u) - mean[i]) * rstd[i] * a[2 * e + 1] + b[2 * e + 1];
+          hb[e] = pack_bf16x2(h0, h1);
+        }
+        if constexpr (OUT == 0) {
+          if (r < rows && valid) *(uint4*)(y + r * ld_y + col) = make_uint4(hb[0], hb[1], hb[2], hb[3]);
+        } else {
+          uint32_t lo, hi, sbyte;
+          quant_mx8<ELEM>(make_uint4(hb[0], hb[1], hb[2], hb[3]), lo, hi, sbyte);
+          if constexpr (OUT == 2) {
+            if (r >= rows) lo = hi = sbyte = 0;  // padding rows of the tiled layout
+            if (ELEM == 0) *(uint32_t*)(codes + tiled_fp4_off(r, kb, g4, nkc) + part * 4) = lo;
+            else *(uint2*)(codes + tiled_fp8_off(r, kb, 2 * g4 + (part >> 1), nkc) + (part & 1) * 8) = make_uint2(lo, hi);
+            if (part == 0) scales[tiled_scale_off(r, kb, nkc) + g4] = (uint8_t)sbyte;
+          } else {
+            if (r < rows && valid) {
+              if (ELEM == 0) *(uint32_t*)(codes + r * (cols >> 1) + (col >> 1)) = lo;
+              else *(uint2*)(codes + r * cols + col) = make_uint2(lo, hi);
+              if (part == 0) scales[r * (cols >> 5) + (col >> 5)] = (uint8_t)sbyte;
+            }
+          }
+        }
+      }
+    }
+  }
+}
+
 // Row-major <-> tiled copy: one thread per 16-byte code piece (and, for the first piece of each
 // 128-column chunk, the row's 4 scale bytes of that chunk).  Padding rows of a tiled destination
 // are zero-filled.
@@ -447,6 +627,54 @@ hipError_t launch_relayout(const uint8_t* src_codes, const uint8_t* src_scales, 
     if (to_tiled) relayout_kernel<1, true><<<grid, 256, 0, s>>>(src_codes, src_scales, dst_codes, dst_scales, rows, cols);
     else relayout_kernel<1, false><<<grid, 256, 0, s>>>(src_codes, src_scales, dst_codes, dst_scales, rows, cols);
   }
+  return hipGetLastError();
+}
+
+template <int ELEM, int OUT, int CPW>
+static void run_norm(int grid, int threads, size_t lds, hipStream_t s, const uint16_t* x, int64_t rows,
+                     int64_t cols, int64_t ld, float eps, const float* gamma, const float* beta,
+                     const float* scale, const float* shift, uint16_t* y, int64_t ld_y,
+                     uint8_t* codes, uint8_t* scales) {
+  norm_quant_kernel<ELEM, OUT, CPW><<<grid, threads, lds, s>>>(x, rows, cols, ld, eps, gamma, beta, scale,
+                                                               shift, y, ld_y, codes, scales);
+}
+template <int ELEM, int OUT>
+static void run_norm_c(int cpw, int grid, int threads, size_t lds, hipStream_t s, const uint16_t* x,
+                       int64_t rows, int64_t cols, int64_t ld, float eps, const float* gamma,
+                       const float* beta, const float* scale, const float* shift, uint16_t* y,
+                       int64_t ld_y, uint8_t* codes, uint8_t* scales) {
+#define MX_NORM_CASE(C) \
+  case C: run_norm<ELEM, OUT, C>(grid, threads, lds, s, x, rows, cols, ld, eps, gamma, beta, scale, shift, y, ld_y, codes, scales); break;
+  switch (cpw) {
+    MX_NORM_CASE(1) MX_NORM_CASE(2) MX_NORM_CASE(3) MX_NORM_CASE(4)
+    MX_NORM_CASE(5) MX_NORM_CASE(6) MX_NORM_CASE(7) MX_NORM_CASE(8)
+    default: break;
+  }
+#undef MX_NORM_CASE
+}
+
+hipError_t launch_norm_quant(const uint16_t* x, int64_t rows, int64_t cols, int64_t ld, float eps,
+                             const float* gamma, const float* beta, const float* scale,
+                             const float* shift, int out_kind, int elem, uint16_t* y, int64_t ld_y,
+                             uint8_t* codes, uint8_t* scales, hipStream_t s) {
+  if (rows == 0) return hipSuccess;
+  const int64_t nkc = (cols + 127) / 128;
+  if (nkc > NORM_WAVES * 8) return hipErrorInvalidValue;
+  const int cpw = (int)((nkc + NORM_WAVES - 1) / NORM_WAVES);
+  const int nw = (int)((nkc + cpw - 1) / cpw);
+  const int threads = nw * 64;
+  const size_t lds = (size_t)(2 * cols + 2 * NORM_WAVES * NORM_ROWS) * sizeof(float);
+  const int64_t nrb = (out_kind == 2 ? tiled_rows(rows) : rows + NORM_ROWS - 1) / NORM_ROWS;
+#ifndef MX_NORM_GRID
+#define MX_NORM_GRID 512
+#endif
+  // persistent workgroups (two per compute unit): the A/B vectors are built once per workgroup
+  const int grid = (int)(nrb < MX_NORM_GRID ? nrb : MX_NORM_GRID);
+  if (out_kind == 0) run_norm_c<0, 0>(cpw, grid, threads, lds, s, x, rows, cols, ld, eps, gamma, beta, scale, shift, y, ld_y, codes, scales);
+  else if (out_kind == 1 && elem == 0) run_norm_c<0, 1>(cpw, grid, threads, lds, s, x, rows, cols, ld, eps, gamma, beta, scale, shift, y, ld_y, codes, scales);
+  else if (out_kind == 1) run_norm_c<1, 1>(cpw, grid, threads, lds, s, x, rows, cols, ld, eps, gamma, beta, scale, shift, y, ld_y, codes, scales);
+  else if (elem == 0) run_norm_c<0, 2>(cpw, grid, threads, lds, s, x, rows, cols, ld, eps, gamma, beta, scale, shift, y, ld_y, codes, scales);
+  else run_norm_c<1, 2>(cpw, grid, threads, lds, s, x, rows, cols, ld, eps, gamma, beta, scale, shift, y, ld_y, codes, scales);
   return hipGetLastError();
 }
 

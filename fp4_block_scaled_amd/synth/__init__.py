@@ -24,6 +24,7 @@ _lib = None
 
 # tensor ids inside a config's seed space
 T_A, T_W, T_BIAS, T_OUTLIER, T_LDOWN, T_LUP, T_W2, T_B2 = 1, 2, 3, 4, 5, 6, 7, 8
+T_MSCALE, T_MSHIFT = 9, 10  # modulation vectors of the norm in front of a linear
 
 
 def _load():
@@ -106,7 +107,7 @@ class Workload:
     M: int
     K: int
     N: int
-    fmt: str = "mxfp4"     # weight/activation format: mxfp4 | w4a8 | w8a8 | nvfp4
+    fmt: str = "mxfp4"     # weight/activation format: mxfp4 | w4a8 | w8a8 | nvfp4 | norm
     a_sigma: float = 1.0
     outlier_frac: float = 0.01
     outlier_factor: float = 20.0
@@ -146,6 +147,11 @@ class Workload:
     def lora_up(self) -> np.ndarray:
         return normal_f32(self.seed_base + T_LUP, (self.rank, self.N), self.lr_sigma)
 
+    def modulation(self):
+        """F32 (scale, shift) [K] of the modulation in front of the linear (N(0, 0.1) each)."""
+        return (normal_f32(self.seed_base + T_MSCALE, (self.K,), 0.1),
+                normal_f32(self.seed_base + T_MSHIFT, (self.K,), 0.1))
+
 
 WORKLOADS = {
     # smallest MXFP4 W4A4 instance
@@ -171,6 +177,11 @@ WORKLOADS = {
     "wan_a14b_w8a8_75600x5120x5120": Workload(
         "wan_a14b_w8a8_75600x5120x5120", 2, 75600, 5120, 5120, "w8a8",
         outlier_frac=0.005, outlier_factor=30.0, w_sigma=0.015),
+    # the LayerNorm + modulation in front of the attention projection, fused with its MXFP4
+    # quantizer (same activation seeds as the W4A4 workload; N is unused)
+    "wan_a14b_norm_quant_75600x5120": Workload(
+        "wan_a14b_norm_quant_75600x5120", 2, 75600, 5120, 5120, "norm",
+        outlier_frac=0.005, outlier_factor=30.0),
     # NVFP4 at the A14B FFN shape with a static activation global scale (amax 40)
     "wan_a14b_nvfp4_75600x5120x13824": Workload(
         "wan_a14b_nvfp4_75600x5120x13824", 5, 75600, 5120, 13824, "nvfp4",

@@ -176,6 +176,35 @@ mx_status mx_absmax(const uint16_t* x, int64_t rows, int64_t cols, int64_t ld_x,
  * amax = 0.  Host-side arithmetic only. */
 float mx_nvfp4_global_scale(float amax);
 
+/* Largest cols of mx_norm / mx_norm_quantize. */
+#define MX_NORM_MAX_COLS 7680
+
+/*
+ * mx_norm_quantize - the producer of a quantized linear's input, fused with its quantizer.  The
+ * MXFP4 model card ("intel-ai/Wan2.2-I2V-A14B-Lightning-Diffusers-MXFP4-AutoRound", Quantization
+ * Details) keeps the norm and the modulation table in front of the quantized linears at higher
+ * precision and quantizes the linears' activations dynamically.  Per row of the BF16 matrix x
+ * (rows x cols, leading dimension ld_x), in fp32:
+ *    h = LayerNorm(x) * gamma + beta,  then  h = h * (1 + scale) + shift
+ * (LayerNorm: mean, biased variance, 1/sqrt(var + eps); gamma, beta, scale, shift are device
+ * F32 [cols] vectors, each optional: NULL is the identity).  h is rounded to BF16 and that BF16
+ * matrix is quantized to fmt (MXFP4 or MXFP8) exactly as mx_quantize would: codes and scales in
+ * `layout` (row-major, or tiled with padding rows zero), ready for mx_linear_q.
+ * Requires cols % 32 == 0 (cols % 128 for tiled), cols <= MX_NORM_MAX_COLS, eps finite > 0,
+ * x 16-byte aligned with ld_x % 8 == 0, the vectors 4-byte aligned, codes aligned as for
+ * mx_quantize.  Buffers are sized as for mx_quantize (mx_tiled_bytes for the tiled layout).
+ */
+mx_status mx_norm_quantize(const uint16_t* x, int64_t rows, int64_t cols, int64_t ld_x, float eps,
+                           const float* gamma, const float* beta, const float* scale,
+                           const float* shift, int32_t fmt, int32_t layout, void* codes,
+                           uint8_t* scales, void* stream);
+
+/* mx_norm - the same producer unfused: writes the BF16 h (rows x cols, leading dimension ld_y,
+ * 16-byte aligned, ld_y % 8 == 0) that mx_norm_quantize quantizes. */
+mx_status mx_norm(const uint16_t* x, int64_t rows, int64_t cols, int64_t ld_x, float eps,
+                  const float* gamma, const float* beta, const float* scale, const float* shift,
+                  uint16_t* y, int64_t ld_y, void* stream);
+
 /* Bytes of workspace mx_linear needs for an M x K activation in act_fmt (codes + scales of the
  * quantized activation -- in the tiled layout for the MX formats when K % 128 == 0 -- plus the
  * low-rank intermediate when rank > 0). */

@@ -182,6 +182,39 @@ def test_linear_q_validation(mx):
     assert L.mx_linear_q(ctypes.byref(a0), ctypes.byref(w), None, 0, 0, P(FAKE), 64, None, None) == 0
 
 
+def test_norm_validation(mx):
+    L = mx.lib()
+    P = ctypes.c_void_p
+
+    def nq(x=FAKE, rows=16, cols=256, ld=256, eps=1e-6, g=None, b=None, sc=None, sh=None, fmt=0,
+           layout=1, codes=FAKE, scales=FAKE):
+        return L.mx_norm_quantize(P(x) if x else None, rows, cols, ld, eps, P(g) if g else None,
+                                  P(b) if b else None, P(sc) if sc else None, P(sh) if sh else None,
+                                  fmt, layout, P(codes) if codes else None,
+                                  P(scales) if scales else None, None)
+
+    def nn(x=FAKE, rows=16, cols=256, ld=256, eps=1e-6, y=FAKE, ldy=256):
+        return L.mx_norm(P(x) if x else None, rows, cols, ld, eps, None, None, None, None,
+                         P(y) if y else None, ldy, None)
+
+    assert nq(fmt=2) == 4                        # NVFP4 output is not provided
+    assert nq(layout=5) == 4
+    assert nq(cols=96, ld=96) == 2               # tiled needs cols % 128
+    assert nq(cols=100, ld=104, layout=0) == 2   # cols % 32
+    assert nq(cols=7808, ld=7808) == 2           # beyond MX_NORM_MAX_COLS
+    assert nq(ld=128) == 2                       # ld_x < cols
+    assert nq(eps=0.0) == 2 and nq(eps=float("inf")) == 2
+    assert nq(x=0) == 1 and nq(codes=0) == 1 and nq(scales=0) == 1
+    assert nq(x=FAKE + 8) == 3 and nq(ld=260) == 3
+    assert nq(sc=FAKE + 2) == 3                  # vectors need 4-byte alignment
+    assert nq(codes=FAKE + 8) == 3               # tiled codes need 16-byte alignment
+    assert nq(rows=0, x=0, codes=0, scales=0) == 0
+    assert nn(y=0) == 1
+    assert nn(ldy=128) == 2
+    assert nn(y=FAKE + 8) == 3
+    assert nn(rows=0, x=0, y=0) == 0
+
+
 def test_relayout_validation(mx):
     L = mx.lib()
     rm, ti = _qm(mx, 16, 128, mx.MXFP4), _qm(mx, 16, 128, mx.MXFP4, layout=1)

@@ -1,0 +1,139 @@
+"""GPU parity of the producer-fused quantizer (LayerNorm + modulation, then the MX quantizer).
+
+The GPU computes the row statistics and h in fp32, the oracle in fp64, so the BF16 h the two
+round to may differ by one BF16 step where h lies within fp32 noise of a rounding midpoint: h is
+compared within that bound and its mismatch rate is reported.  The fused codes must equal, bit
+for bit, the standalone quantizer applied to the GPU's own BF16 h (same statistics, same group
+routine), and their mismatch rate against the oracle's codes is reported and bounded.  A
+constant row, whose statistics are exact in fp32, is compared with the oracle bit for bit.
+"""
+import numpy as np
+import pytest
+import torch
+
+import oracle as O
+from fp4_block_scaled_amd import synth
+from _util import activation_bits, dev_bits16, sample_rows, tile_mx, to_dev_bf16
+
+pytestmark = pytest.mark.gpu
+
+EPS = 1e-6
+
+
+@pytest.fixture(scope="module")
+def mx():
+    import fp4_block_scaled_amd as m
+    assert torch.cuda.is_available()
+    m.lib()
+    return m
+
+
+def _vecs(cols, seed, which):
+    """F32 gamma, beta, scale, shift (None where not in `which`), host and device."""
+    host = {}
+    for j, name in enumerate(("gamma", "beta", "scale", "shift")):
+        if name in which:
+            mean = 1.0 if name == "gamma" else 0.0
+            host[name] = (synth.normal_f32(seed + j, (cols,), 0.1) + np.float32(mean)).astype(np.float32)
+        else:
+            host[name] = None
+    dev = {k: (torch.from_numpy(v).cuda() if v is not None else None) for k, v in host.items()}
+    return host, dev
+
+
+def _check_h(h_gpu_bits, h_ref, what):
+    """|h_gpu - h_ref| within one BF16 step of h_ref (plus fp32 noise near zero); returns the
+    rate of elements whose BF16 differs from bf16_rne(h_ref)."""
+    h_gpu = O.bf16_values(h_gpu_bits)
+    err = np.abs(h_gpu - h_ref)
+    tol = 2.0 ** -8 * np.abs(h_ref) + 1e-5
+    bad = err > tol
+    assert not bad.any(), f"{what}: {bad.sum()} elements beyond one BF16 step, max err/tol {np.max(err / tol):.3g}"
+    return float(np.mean(h_gpu_bits != O.bf16_rne_array(h_ref)))
+
+
+@pytest.mark.parametrize("rows,cols,ld,which", [
+    (300, 1024, 1024, ("scale", "shift")),
+    (37, 5120, 5128, ("scale", "shift")),
+    (8, 3072, 3072, ("gamma", "beta")),
+    (1, 32, 32, ()),
+    (129, 7680, 7680, ("gamma", "beta", "scale", "shift")),
+    (64, 96, 104, ("shift",)),
+])
+def test_norm_vs_oracle(mx, rows, cols, ld, which):
+    full = activation_bits(rows, ld, seed_base=21000 + cols, factor=30.0)
+    x_bits = np.ascontiguousarray(full[:, :cols])
+    host, dev = _vecs(cols, 21100 + cols, which)
+    y = mx.norm(to_dev_bf16(full)[:, :cols], EPS, **dev)
+    torch.cuda.synchronize()
+    h_ref = O.norm_modulate(x_bits, EPS, **host)
+    rate = _check_h(dev_bits16(y), h_ref, f"norm {rows}x{cols}")
+    print(f"BF16 h mismatch rate vs oracle: {rate:.2e}")
+    assert rate < 1e-2
+
+
+@pytest.mark.parametrize("fmt", ["mxfp4", "mxfp8"])
+@pytest.mark.parametrize("layout", ["row_major", "tiled"])
+@pytest.mark.parametrize("rows,cols", [(300, 1024), (37, 5120), (1, 128), (515, 3072)])
+def test_norm_quantize_equals_quantize_of_norm(mx, fmt, layout, rows, cols):
+    """The fused kernel's codes are exactly the quantizer's codes of the unfused BF16 h."""
+    x = to_dev_bf16(activation_bits(rows, cols, seed_base=22000 + rows, factor=30.0))
+    _, dev = _vecs(cols, 22100, ("scale", "shift"))
+    q = mx.norm_quantize(x, EPS, fmt=fmt, layout=layout, **dev)
+    ref = mx.quantize(mx.norm(x, EPS, **dev), fmt, layout=layout)
+    torch.cuda.synchronize()
+    assert torch.equal(q.scales, ref.scales)
+    assert torch.equal(q.codes, ref.codes)
+
+
+@pytest.mark.parametrize("fmt,elem", [("mxfp4", O.E2M1), ("mxfp8", O.E4M3)])
+def test_norm_quantize_vs_oracle(mx, fmt, elem):
+    rows, cols = 200, 5120
+    x_bits = activation_bits(rows, cols, seed_base=23000, factor=30.0)
+    host, dev = _vecs(cols, 23100, ("scale", "shift"))
+    q = mx.norm_quantize(to_dev_bf16(x_bits), EPS, fmt=fmt, layout="row_major", **dev)
+    torch.cuda.synchronize()
+    rc, rs = O.quantize_mx_bf16(O.bf16_rne_array(O.norm_modulate(x_bits, EPS, **host)), elem)
+    srate = float(np.mean(q.scales.cpu().numpy() != rs))
+    crate = float(np.mean(q.codes.cpu().numpy() != rc))
+    print(f"{fmt}: scale-byte mismatch rate {srate:.2e}, code-byte mismatch rate {crate:.2e}")
+    assert srate < 1e-3 and crate < 1e-2
+
+
+def test_constant_rows_are_bit_exact_and_tiled_padding_is_zero(mx):
+    """Rows of one value (exact fp32 statistics) normalize to 0, so h = beta (1 + scale) +
+    shift; the codes then match the oracle bit for bit.  Tiled padding rows are zero."""
+    rows, cols = 19, 1024
+    x_bits = np.full((rows, cols), 0x3FC0, dtype=np.uint16)  # 1.5
+    x_bits[5] = 0xBF00  # -0.5
+    host, dev = _vecs(cols, 24000, ("gamma", "beta", "scale", "shift"))
+    y = mx.norm(to_dev_bf16(x_bits), EPS, **dev)
+    q = mx.norm_quantize(to_dev_bf16(x_bits), EPS, fmt="mxfp4", layout="tiled", **dev)
+    torch.cuda.synchronize()
+    h_ref = O.norm_modulate(x_bits, EPS, **host)
+    np.testing.assert_array_equal(dev_bits16(y), O.bf16_rne_array(h_ref))
+    rc, rs = O.quantize_mx_bf16(O.bf16_rne_array(h_ref), O.E2M1)
+    tc, ts = tile_mx(rc, rs, rows, cols, fp8=False)
+    np.testing.assert_array_equal(q.codes.cpu().numpy().ravel(), tc.ravel())
+    np.testing.assert_array_equal(q.scales.cpu().numpy().ravel(), ts.ravel())
+
+
+def test_full_size_wan_a14b_norm_quantize(mx):
+    """75600 x 5120 with modulation, as the benchmark runs it (tiled MXFP4): the fused codes
+    equal the quantizer's codes of the unfused h everywhere, and sampled rows of h are within
+    one BF16 step of the oracle."""
+    wl = synth.WORKLOADS["wan_a14b_norm_quant_75600x5120"]
+    x_bits = synth.bits16(synth.to_bf16(wl.activation()))
+    sc, sh = wl.modulation()
+    dev = {"scale": torch.from_numpy(sc).cuda(), "shift": torch.from_numpy(sh).cuda()}
+    x = to_dev_bf16(x_bits)
+    q = mx.norm_quantize(x, EPS, fmt="mxfp4", layout="tiled", **dev)
+    y = mx.norm(x, EPS, **dev)
+    ref = mx.quantize(y, "mxfp4", layout="tiled")
+    torch.cuda.synchronize()
+    assert torch.equal(q.codes, ref.codes) and torch.equal(q.scales, ref.scales)
+    rows = sample_rows(wl.M, 128)
+    h_ref = O.norm_modulate(np.ascontiguousarray(x_bits[rows]), EPS, scale=sc, shift=sh)
+    rate = _check_h(dev_bits16(y[torch.from_numpy(rows).cuda()]), h_ref, "full-size norm")
+    print(f"BF16 h mismatch rate vs oracle (sampled rows): {rate:.2e}")
+    assert rate < 1e-2
