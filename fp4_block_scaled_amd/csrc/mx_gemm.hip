@@ -249,40 +249,53 @@ __device__ __forceinline__ v16f lowrank_block(const GemmParams& p, v16f acc, int
   return acc;
 }
 
-// The low-rank term of a wave's FN x FM blocks: every fragment of up_t and u (rank <= 64) is
-// loaded first, so the loads of the whole sub-tile are in flight together, then the MFMAs.
-template <int FN, int FM>
-__device__ __forceinline__ void lowrank_tile(const GemmParams& p, v16f (&acc)[FN][FM], int n_base, int m_base) {
-  constexpr int RQ = 4;  // rank / 16 at most
+// The low-rank term of a wave's FN x FM blocks, in 16-rank slices [Q0, Q1): the fragments of
+// up_t and u are loaded (lowrank_load, all in flight together), then the MFMAs (lowrank_mma).
+// A kernel may load the first slices before its K loop, so that their latency is hidden.
+template <int FN, int FM, int NQ>
+struct LrFrags {
+  uint4 wa[FN][NQ], ub[FM][NQ];
+};
+template <int FN, int FM, int Q0, int Q1>
+__device__ __forceinline__ void lowrank_load(const GemmParams& p, LrFrags<FN, FM, Q1 - Q0>& f, int n_base, int m_base) {
   const int lane = lane_id();
   const int h = lane >> 5;
-  uint4 wa[FN][RQ], ub[FM][RQ];
 #pragma unroll
   for (int i = 0; i < FN; ++i) {
     const int n = min(n_base + 32 * i + (lane & 31), p.N - 1);
 #pragma unroll
-    for (int q = 0; q < RQ; ++q)
-      wa[i][q] = 16 * q < p.R ? *(const uint4*)(p.lr_up + (int64_t)n * p.R + 16 * q + 8 * h) : make_uint4(0, 0, 0, 0);
+    for (int q = Q0; q < Q1; ++q)
+      f.wa[i][q - Q0] = 16 * q < p.R ? *(const uint4*)(p.lr_up + (int64_t)n * p.R + 16 * q + 8 * h) : make_uint4(0, 0, 0, 0);
   }
 #pragma unroll
   for (int j = 0; j < FM; ++j) {
     const int m = min(m_base + 32 * j + (lane & 31), p.M - 1);
 #pragma unroll
-    for (int q = 0; q < RQ; ++q)
-      ub[j][q] = 16 * q < p.R ? *(const uint4*)(p.lr_u + (int64_t)m * p.R + 16 * q + 8 * h) : make_uint4(0, 0, 0, 0);
+    for (int q = Q0; q < Q1; ++q)
+      f.ub[j][q - Q0] = 16 * q < p.R ? *(const uint4*)(p.lr_u + (int64_t)m * p.R + 16 * q + 8 * h) : make_uint4(0, 0, 0, 0);
   }
+}
+template <int FN, int FM, int Q0, int Q1>
+__device__ __forceinline__ void lowrank_mma(const GemmParams& p, v16f (&acc)[FN][FM], const LrFrags<FN, FM, Q1 - Q0>& f) {
 #pragma unroll
-  for (int q = 0; q < RQ; ++q) {
+  for (int q = Q0; q < Q1; ++q) {
     if (16 * q >= p.R) break;
     static_for<FN>([&](auto i) {
       static_for<FM>([&](auto j) {
         v8bf fa, fb;
-        __builtin_memcpy(&fa, &wa[i][q], 16);
-        __builtin_memcpy(&fb, &ub[j][q], 16);
+        __builtin_memcpy(&fa, &f.wa[i][q - Q0], 16);
+        __builtin_memcpy(&fb, &f.ub[j][q - Q0], 16);
         acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fa, fb, acc[i][j], 0, 0, 0);
       });
     });
   }
+}
+// rank <= 64: every slice loaded, then the MFMAs
+template <int FN, int FM>
+__device__ __forceinline__ void lowrank_tile(const GemmParams& p, v16f (&acc)[FN][FM], int n_base, int m_base) {
+  LrFrags<FN, FM, 4> f;
+  lowrank_load<FN, FM, 0, 4>(p, f, n_base, m_base);
+  lowrank_mma<FN, FM, 0, 4>(p, acc, f);
 }
 
 // ---------------------------------------------------------------------------------------------
@@ -698,6 +711,11 @@ gemm_mx_ring_kernel(GemmParams p) {
 
   v16f acc[T::FN][T::FM];
   static_for<T::FN>([&](auto i) { static_for<T::FM>([&](auto j) { acc[i][j] = v16f{}; }); });
+  // E4M3-activation tiles (W4A8, few K chunks per tile): the first 32 ranks of the low-rank
+  // branch are loaded before the K loop, so their latency is hidden behind it
+  constexpr bool LR_EARLY = LR && AFP8;
+  LrFrags<T::FN, T::FM, 2> lr_early;
+  if constexpr (LR_EARLY) lowrank_load<T::FN, T::FM, 0, 2>(p, lr_early, n0 + wn0, m0 + wm0);
 
   // fragment addresses inside a stage (step 0; step 1 is piece ^ 1)
   const int wrow = wn0 + r32, arow = wm0 + r32;  // + 32 i: the XOR term is unchanged
@@ -819,7 +837,16 @@ gemm_mx_ring_kernel(GemmParams p) {
     st = st1;
   }
 
-  if (LR) lowrank_tile<T::FN, T::FM>(p, acc, n0 + wn0, m0 + wm0);
+  if constexpr (LR && LR_EARLY) {  // slices 0-1 (rank 32) were loaded before the loop
+    lowrank_mma<T::FN, T::FM, 0, 2>(p, acc, lr_early);
+    if (p.R > 32) {
+      LrFrags<T::FN, T::FM, 2> f;
+      lowrank_load<T::FN, T::FM, 2, 4>(p, f, n0 + wn0, m0 + wm0);
+      lowrank_mma<T::FN, T::FM, 2, 4>(p, acc, f);
+    }
+  } else if constexpr (LR) {
+    lowrank_tile<T::FN, T::FM>(p, acc, n0 + wn0, m0 + wm0);
+  }
   if (ring_staged_ok<EPI, OUTF32>(p)) {
     static_assert(BM * BN * 2 <= T::LDS, "output tile fits the ring");
     wait_vmem_all();  // the (empty) loads issued for the chunks past the end have landed
