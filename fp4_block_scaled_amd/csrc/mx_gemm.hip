@@ -1114,59 +1114,112 @@ __global__ void __launch_bounds__(256, 256 / BN) gemm_nv_ring_kernel(GemmParams 
   static_for<T::NSTAGE - 1>([&](auto i) {
     static_for<T::NDMA>([&](auto q) { issue_one(q, (int)decltype(i)::value, (int)decltype(i)::value); });
   });
-  int st = 0;
-  for (int kc = 0; kc < nkc; ++kc) {
-    wait_vmcnt<(T::NSTAGE - 2) * T::NDMA>();  // chunk kc landed (later ones may be in flight)
-    wait_lds_all();
-    barrier_only();
-    const int stn = st == 0 ? T::NSTAGE - 1 : st - 1;  // the stage of chunk kc - 1, now free
-    const uint8_t* sW = smem + st * T::STAGE;
+  // The codes and scale pairs of a chunk, read from LDS stage `stg`.
+  struct NvFrags {
+    v4i wc[T::FN], ac[T::FM];
+    v2h ws2[T::FN], as2[T::FM];  // the lane's two E4M3 block scales (elements 0-7, 8-15) as FP16
+  };
+  auto read_chunk = [&](int stg, NvFrags& f) {
+    const uint8_t* sW = smem + stg * T::STAGE;
     const uint8_t* sA = sW + T::W_BYTES;
     const uint8_t* sWS = sA + T::A_BYTES;
     const uint8_t* sAS = sWS + T::WS_BYTES;
-    v4i wc[T::FN], ac[T::FM];
-    v2h wsl[T::FN], wsh[T::FN], asl[T::FM], ash[T::FM];
 #pragma unroll
     for (int i = 0; i < T::FN; ++i) {
-      wc[i] = *(const v4i*)(sW + cpos_w + i * 32 * 32);
+      f.wc[i] = *(const v4i*)(sW + cpos_w + i * 32 * 32);
       const uint32_t sb = *(const uint32_t*)(sWS + (wrow + 32 * i) * 4) >> shift;
-      const v2h s2 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(sb, 1.0f, false);
-      wsl[i] = v2h{s2[0], s2[0]};
-      wsh[i] = v2h{s2[1], s2[1]};
+      f.ws2[i] = __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(sb, 1.0f, false);
     }
 #pragma unroll
     for (int j = 0; j < T::FM; ++j) {
-      ac[j] = *(const v4i*)(sA + cpos_a + j * 32 * 32);
+      f.ac[j] = *(const v4i*)(sA + cpos_a + j * 32 * 32);
       const uint32_t sb = *(const uint32_t*)(sAS + (arow + 32 * j) * 4) >> shift;
-      const v2h s2 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(sb, 1.0f, false);
-      asl[j] = v2h{s2[0], s2[0]};
-      ash[j] = v2h{s2[1], s2[1]};
+      f.as2[j] = __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(sb, 1.0f, false);
     }
-    __builtin_amdgcn_sched_barrier(0);
-    static_for<4>([&](auto tc) {
-      constexpr int t = decltype(tc)::value;
-      v8h wf[T::FN], af[T::FM];
-#pragma unroll
-      for (int i = 0; i < T::FN; ++i) wf[i] = nv_dequant8_f16((uint32_t)wc[i][t], t < 2 ? wsl[i] : wsh[i]);
-#pragma unroll
-      for (int j = 0; j < T::FM; ++j) af[j] = nv_dequant8_f16((uint32_t)ac[j][t], t < 2 ? asl[j] : ash[j]);
-      static_for<T::FN>([&](auto i) {
-        static_for<T::FM>([&](auto j) {
-          acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_f16(wf[i], af[j], acc[i][j], 0, 0, 0);
-          constexpr int M = t * T::FN * T::FM + decltype(i)::value * T::FM + decltype(j)::value;
-          constexpr int TOTAL = 4 * T::FN * T::FM;
-          static_for<T::NDMA>([&](auto qc) {
-            if constexpr ((decltype(qc)::value + 1) * TOTAL / T::NDMA - 1 == M) {
-              __builtin_amdgcn_sched_barrier(0);
-              issue_one(qc, kc + T::NSTAGE - 1, stn);
-              __builtin_amdgcn_sched_barrier(0);
-            }
-          });
+  };
+  // Dequantized fragments, double-buffered over the four 16-element steps of a chunk: step
+  // t + 1's fragments are dequantized between step t's MFMAs (one fragment after every
+  // FN * FM / (FN + FM) MFMAs), so the conversions run while the matrix core is busy.
+  v8h wf[2][T::FN], af[2][T::FM];
+  auto dequant_frag = [&](const NvFrags& f, auto tq, auto kq, auto bq) {
+    constexpr int t = decltype(tq)::value, k = decltype(kq)::value, b = decltype(bq)::value;
+    // steps 0-1 (elements 0-7 of the lane's 16) take the first block scale, steps 2-3 the second
+    if constexpr (k < T::FN) {
+      const v2h sc = t < 2 ? __builtin_shufflevector(f.ws2[k], f.ws2[k], 0, 0) : __builtin_shufflevector(f.ws2[k], f.ws2[k], 1, 1);
+      wf[b][k] = nv_dequant8_f16((uint32_t)f.wc[k][t], sc);
+    } else {
+      const v2h sc = t < 2 ? __builtin_shufflevector(f.as2[k - T::FN], f.as2[k - T::FN], 0, 0)
+                           : __builtin_shufflevector(f.as2[k - T::FN], f.as2[k - T::FN], 1, 1);
+      af[b][k - T::FN] = nv_dequant8_f16((uint32_t)f.ac[k - T::FN][t], sc);
+    }
+  };
+  constexpr int TOTAL = 4 * T::FN * T::FM;
+  // The MFMAs of step t of a chunk, with the dequantization of the next step (step 0 of the next
+  // chunk, from fn, after step 3) and the loads of chunk `dkc` into stage `dst` that fall in this
+  // step (load q after MFMA (q + 1) * TOTAL / NDMA - 1).
+  auto mma_step = [&](auto tc, const NvFrags& f, const NvFrags& fn, int dkc, int dst) {
+    constexpr int t = decltype(tc)::value;
+    constexpr int cb = t & 1;
+    static_for<T::FN>([&](auto i) {
+      static_for<T::FM>([&](auto j) {
+        acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_f16(wf[cb][i], af[cb][j], acc[i][j], 0, 0, 0);
+        constexpr int Mi = decltype(i)::value * T::FM + decltype(j)::value;  // MFMA index in the step
+        constexpr int M = t * T::FN * T::FM + Mi;
+        constexpr int PER = T::FN * T::FM / (T::FN + T::FM);  // MFMAs per dequantized fragment
+        if constexpr ((Mi + 1) % PER == 0 && (Mi + 1) / PER <= T::FN + T::FM) {
+          __builtin_amdgcn_sched_barrier(0);
+          dequant_frag(t < 3 ? f : fn, std::integral_constant<int, (t + 1) & 3>{},
+                       std::integral_constant<int, (Mi + 1) / PER - 1>{}, std::integral_constant<int, cb ^ 1>{});
+          __builtin_amdgcn_sched_barrier(0);
+        }
+        static_for<T::NDMA>([&](auto qc) {
+          if constexpr ((decltype(qc)::value + 1) * TOTAL / T::NDMA - 1 == M) {
+            __builtin_amdgcn_sched_barrier(0);
+            issue_one(qc, dkc, dst);
+            __builtin_amdgcn_sched_barrier(0);
+          }
         });
       });
     });
+  };
+  // loads of a chunk issued during steps 0 and 1
+  constexpr int LOADS_H0 = [] {
+    int n = 0;
+    for (int q = 0; q < T::NDMA; ++q) n += (q + 1) * TOTAL / T::NDMA - 1 < TOTAL / 2 ? 1 : 0;
+    return n;
+  }();
+
+  // Software pipeline over chunks.  Iteration kc: steps 0-1 of chunk kc (its codes were read
+  // last iteration) while chunk kc + 3 starts loading into the stage of chunk kc - 1; then the
+  // barrier that publishes chunk kc + 1 (its wait overlaps the MFMAs in flight) and the reads of
+  // chunk kc + 1 under steps 2-3 of chunk kc.  A stage is refilled only after the barrier that
+  // follows every wave's last read of it.
+  NvFrags cur;
+  wait_vmcnt<(T::NSTAGE - 2) * T::NDMA>();  // chunk 0 landed
+  barrier_only();
+  read_chunk(0, cur);
+  static_for<T::FN + T::FM>([&](auto kq) {  // step 0 of chunk 0 (later chunks: under step 3)
+    dequant_frag(cur, std::integral_constant<int, 0>{}, kq, std::integral_constant<int, 0>{});
+  });
+  int st = 0;  // stage of chunk kc
+  for (int kc = 0; kc < nkc; ++kc) {
+    const int stn = st == 0 ? T::NSTAGE - 1 : st - 1;  // the stage of chunk kc - 1: chunk kc + 3
+    const int st1 = st == T::NSTAGE - 1 ? 0 : st + 1;  // chunk kc + 1
     __builtin_amdgcn_sched_barrier(0);
-    st = st == T::NSTAGE - 1 ? 0 : st + 1;
+    mma_step(std::integral_constant<int, 0>{}, cur, cur, kc + T::NSTAGE - 1, stn);
+    mma_step(std::integral_constant<int, 1>{}, cur, cur, kc + T::NSTAGE - 1, stn);
+    __builtin_amdgcn_sched_barrier(0);
+    wait_vmcnt<(T::NSTAGE - 3) * T::NDMA + LOADS_H0>();  // chunk kc + 1 landed
+    wait_lds_all();  // this wave's reads of chunk kc are done
+    barrier_only();
+    NvFrags nxt;
+    read_chunk(st1, nxt);  // past the last chunk this reads a stage never written: unused
+    __builtin_amdgcn_sched_barrier(0);
+    mma_step(std::integral_constant<int, 2>{}, cur, nxt, kc + T::NSTAGE - 1, stn);
+    mma_step(std::integral_constant<int, 3>{}, cur, nxt, kc + T::NSTAGE - 1, stn);
+    __builtin_amdgcn_sched_barrier(0);
+    cur = nxt;
+    st = st1;
   }
 
   if (ring_staged_ok<EPI, OUTF32>(p)) {
