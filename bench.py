@@ -375,8 +375,9 @@ def main():
         return
     world = int(os.environ.get("WORLD_SIZE", "1"))
     if args.gpus != 1 or world != 1:
-        print(json.dumps({"error": "this build runs on one GPU only; the linear shards along M "
-                                   "with no exchange (see DESIGN.md), so run --gpus 1"}), flush=True)
+        print(json.dumps({"error": "the benchmark runs on one GPU only: the linear shards along M "
+                                   "(tokens) with no exchange between GPUs, so one GPU's share is the "
+                                   "measured unit; run --gpus 1"}), flush=True)
         raise SystemExit(2)
 
     import torch
