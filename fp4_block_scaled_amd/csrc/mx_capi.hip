@@ -378,16 +378,24 @@ mx_status mx_linear(const uint16_t* a, int64_t M, int64_t K, int64_t ld_a, int32
   Workspace ws = carve(workspace, M, K, act_fmt, rank);
   hipError_t e;
   const bool tiled = act_tiled(act_fmt, K);
-  if (act_fmt == MX_FMT_NVFP4)
-    e = mxk::launch_quant_nv(a, M, K, ld_a, act_global_scale, ws.codes, ws.scales, s);
-  else if (tiled)
-    e = mxk::launch_quant_mx_tiled(a, M, K, ld_a, act_fmt == MX_FMT_MXFP8 ? 1 : 0, ws.codes, ws.scales, s);
-  else
-    e = mxk::launch_quant_mx(a, M, K, ld_a, act_fmt == MX_FMT_MXFP8 ? 1 : 0, ws.codes, ws.scales, s);
-  if (e != hipSuccess) return hip_status(e, "activation quantizer launch");
-  if (rank > 0) {
-    e = mxk::launch_lowrank_down(a, ld_a, lr->down, (int)M, (int)K, rank, ws.u, s);
-    if (e != hipSuccess) return hip_status(e, "low-rank launch");
+  if (rank > 0 && tiled && act_fmt == MX_FMT_MXFP8) {
+    // W4A8 SVDQuant: one pass over a quantizes it and computes the low-rank input u.  Tiled
+    // padding rows past the last 32-row block stay unwritten in the workspace: they only feed
+    // output rows >= M, which are never stored.
+    e = mxk::launch_quant8_lowrank_down(a, ld_a, lr->down, (int)M, (int)K, rank, ws.u, ws.codes, ws.scales, s);
+    if (e != hipSuccess) return hip_status(e, "quantizer + low-rank launch");
+  } else {
+    if (act_fmt == MX_FMT_NVFP4)
+      e = mxk::launch_quant_nv(a, M, K, ld_a, act_global_scale, ws.codes, ws.scales, s);
+    else if (tiled)
+      e = mxk::launch_quant_mx_tiled(a, M, K, ld_a, act_fmt == MX_FMT_MXFP8 ? 1 : 0, ws.codes, ws.scales, s);
+    else
+      e = mxk::launch_quant_mx(a, M, K, ld_a, act_fmt == MX_FMT_MXFP8 ? 1 : 0, ws.codes, ws.scales, s);
+    if (e != hipSuccess) return hip_status(e, "activation quantizer launch");
+    if (rank > 0) {
+      e = mxk::launch_lowrank_down(a, ld_a, lr->down, (int)M, (int)K, rank, ws.u, s);
+      if (e != hipSuccess) return hip_status(e, "low-rank launch");
+    }
   }
   return run_gemm(ws.codes, ws.scales, act_global_scale, act_fmt, tiled, M, K, w, bias, ws.u, lr,
                   epilogue, out_dtype, out, ld_out, out_scales, s);

@@ -1244,11 +1244,53 @@ constexpr int LR_WAVES = 4, LR_STG = 4, LR_KC = 64;
 constexpr int LR_HALF = 32 * LR_KC * 2;  // 32 rows x 128 bytes: one operand of a stage
 constexpr int LR_STAGE = 2 * LR_HALF;
 
+typedef __bf16 lr_bf2 __attribute__((ext_vector_type(2)));
+typedef short lr_i16x2 __attribute__((ext_vector_type(2)));
+
+// One lane's 32-element MXFP8 group (16 BF16 pairs): the same rule and instruction sequence as
+// the standalone MX quantizer (amax, scale byte floor(log2 amax) - 8 clamped to [-127, 127],
+// magnitudes clamped to 448 * 2^e because the conversion overflows to NaN instead of saturating,
+// then V_CVT_SCALEF32_PK_FP8_BF16), with the amax taken within the lane.  NaN/Inf in the group:
+// codes 0, scale byte 0xFF.
+__device__ __forceinline__ void quant_fp8_group32(const uint32_t (&w)[16], uint32_t (&out)[8], uint32_t& sbyte) {
+  uint32_t amax = 0;
+#pragma unroll
+  for (int i = 0; i < 16; ++i) amax = max(amax, max(w[i] & 0x7FFFu, (w[i] >> 16) & 0x7FFFu));
+  const bool bad = amax >= 0x7F80u;
+  int e = (int)(amax >> 7) - 127 - 8;
+  if (e < -127) e = -127;
+  const float scale = __uint_as_float(e >= -126 ? (uint32_t)(127 + e) << 23 : 0x00400000u);
+  const uint32_t lim = (uint32_t)((e + 135) << 7 | 0x60);  // BF16 bits of 448 * 2^e
+#pragma unroll
+  for (int q = 0; q < 8; ++q) {
+    lr_bf2 b[2];
+#pragma unroll
+    for (int k = 0; k < 2; ++k) {
+      const uint32_t v = w[2 * q + k];
+      const uint32_t lo = min(v & 0x7FFFu, lim), hi = min((v >> 16) & 0x7FFFu, lim);
+      const uint32_t c = lo | (hi << 16) | (v & 0x80008000u);
+      __builtin_memcpy(&b[k], &c, 4);
+    }
+    lr_i16x2 r = __builtin_amdgcn_cvt_scalef32_pk_fp8_bf16(lr_i16x2{0, 0}, b[0], scale, false);
+    r = __builtin_amdgcn_cvt_scalef32_pk_fp8_bf16(r, b[1], scale, true);
+    uint32_t d;
+    __builtin_memcpy(&d, &r, 4);
+    out[q] = bad ? 0u : d;
+  }
+  sbyte = bad ? 0xFFu : (uint32_t)(e + 127);
+}
+
+// QUANT: the same pass also quantizes x to MXFP8 in the tiled layout (codes, scales; rows of the
+// 32-row blocks, the tiled padding beyond them is not written), from the x chunks already in LDS,
+// so the W4A8 linear reads its activation once for both the quantizer and the low-rank branch.
+template <bool QUANT>
 __global__ void __launch_bounds__(LR_WAVES * 64) lowrank_down_kernel(const uint16_t* __restrict__ x,
                                                                      int64_t ld_x,
                                                                      const uint16_t* __restrict__ down_t,
                                                                      int M, int K, int R,
-                                                                     uint16_t* __restrict__ u) {
+                                                                     uint16_t* __restrict__ u,
+                                                                     uint8_t* __restrict__ codes,
+                                                                     uint8_t* __restrict__ scales) {
   __shared__ __attribute__((aligned(16))) uint8_t smem[LR_WAVES * LR_STG * LR_STAGE];
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
@@ -1307,6 +1349,30 @@ __global__ void __launch_bounds__(LR_WAVES * 64) lowrank_down_kernel(const uint1
       if (k0 + 16 * j + 8 * h >= K) {  // past K (K % 32 == 0, so only whole pieces)
         fx[j] = v4i{0, 0, 0, 0};
         fd[j] = v4i{0, 0, 0, 0};
+      }
+    }
+    if constexpr (QUANT) {
+      if (blockIdx.y == 0) {  // one rank block quantizes (uniform)
+        // this lane's group: row r32, elements 32h .. 32h + 31 of the chunk = pieces 4h .. 4h + 3
+        uint32_t w[16];
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+          const v4i d = *(const v4i*)(sx + r32 * 128 + (((4 * h + q) ^ swz) << 4));
+          w[4 * q] = (uint32_t)d[0];
+          w[4 * q + 1] = (uint32_t)d[1];
+          w[4 * q + 2] = (uint32_t)d[2];
+          w[4 * q + 3] = (uint32_t)d[3];
+        }
+        uint32_t cw[8], sbyte;
+        quant_fp8_group32(w, cw, sbyte);
+        const int kg = k0 + 32 * h;  // first element of the group
+        if (kg < K) {
+          const int64_t r = mb + r32, kb = kg >> 7, nkc = K >> 7;
+          const int g16 = (kg & 127) >> 4;  // first 16-element piece of the group in its tile
+          *(uint4*)(codes + tiled_fp8_off(r, kb, g16, nkc)) = make_uint4(cw[0], cw[1], cw[2], cw[3]);
+          *(uint4*)(codes + tiled_fp8_off(r, kb, g16 + 1, nkc)) = make_uint4(cw[4], cw[5], cw[6], cw[7]);
+          scales[tiled_scale_off(r, kb, nkc) + ((kg & 127) >> 5)] = (uint8_t)sbyte;
+        }
       }
     }
     issue(c + 3, (c + 3) & 3);  // into the stage of chunk c - 1, read last iteration
@@ -1441,7 +1507,17 @@ hipError_t launch_lowrank_down(const uint16_t* x, int64_t ld_x, const uint16_t* 
                                int K, int R, uint16_t* u, hipStream_t s) {
   if (M == 0) return hipSuccess;
   dim3 grid((M + 31) / 32, (R + 31) / 32);
-  lowrank_down_kernel<<<grid, LR_WAVES * 64, 0, s>>>(x, ld_x, down_t, M, K, R, u);
+  lowrank_down_kernel<false><<<grid, LR_WAVES * 64, 0, s>>>(x, ld_x, down_t, M, K, R, u, nullptr, nullptr);
+  return hipGetLastError();
+}
+
+hipError_t launch_quant8_lowrank_down(const uint16_t* x, int64_t ld_x, const uint16_t* down_t, int M,
+                                      int K, int R, uint16_t* u, uint8_t* codes, uint8_t* scales,
+                                      hipStream_t s) {
+  if (M == 0) return hipSuccess;
+  if (K % 128) return hipErrorInvalidValue;  // the tiled layout
+  dim3 grid((M + 31) / 32, (R + 31) / 32);
+  lowrank_down_kernel<true><<<grid, LR_WAVES * 64, 0, s>>>(x, ld_x, down_t, M, K, R, u, codes, scales);
   return hipGetLastError();
 }
 

@@ -59,5 +59,10 @@ hipError_t launch_gemm_nv(const GemmParams& p, hipStream_t s);
 // u[m, r] = bf16_rne(sum_k x[m, k] * down_t[r, k])
 hipError_t launch_lowrank_down(const uint16_t* x, int64_t ld_x, const uint16_t* down_t, int M,
                                int K, int R, uint16_t* u, hipStream_t s);
+// The same, also quantizing x to MXFP8 in the tiled layout (K % 128 == 0) in the same pass:
+// codes and scales of the rows of the 32-row blocks (the tiled padding rows beyond are not written).
+hipError_t launch_quant8_lowrank_down(const uint16_t* x, int64_t ld_x, const uint16_t* down_t, int M,
+                                      int K, int R, uint16_t* u, uint8_t* codes, uint8_t* scales,
+                                      hipStream_t s);
 
 }  // namespace mxk

@@ -246,8 +246,12 @@ def test_w8a8_lowrank_and_gelu_epilogue(mx):
     assert np.all(err <= 1.13 * tol_y + 4e-6 * np.abs(h_ref) + 1e-7)
 
 
-def test_lowrank_zero_down_is_plain_w4a8(mx):
-    M, K, N, R = 96, 512, 256, 32
+@pytest.mark.parametrize("M,K,N,R", [(96, 512, 256, 32), (97, 640, 128, 16), (300, 1024, 384, 64),
+                                     (33, 384, 256, 48)])
+def test_lowrank_zero_down_is_plain_w4a8(mx, M, K, N, R):
+    """With L_down = 0 the branch adds exact zeros, so the output equals plain W4A8 bit for bit:
+    this also checks that the pass quantizing the activation together with the low-rank input
+    (K % 128 == 0) writes the same codes as the standalone quantizer."""
     a = to_dev_bf16(activation_bits(M, K, seed_base=13500))
     wq = _quant_w(mx, weight_bits(N, K, seed=13600))
     lr = mx.LowRank(torch.zeros((R, K), dtype=torch.bfloat16, device="cuda"),
