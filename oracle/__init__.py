@@ -70,6 +70,9 @@ def lib():
         L.mxr_absmax_bf16.restype = ctypes.c_double
         L.mxr_norm_modulate.argtypes = [_P, _I, _I, _I, ctypes.c_double, _P, _P, _P, _P, _P]
         L.mxr_norm_modulate.restype = None
+        L.mxr_attention_mx.argtypes = [_P, _P, _P, _P, _P, _P, _I, _I, _I, _I, ctypes.c_int,
+                                       ctypes.c_double, _P, _I, _P, _P, _P]
+        L.mxr_attention_mx.restype = None
         _lib = L
     return _lib
 
@@ -298,3 +301,32 @@ def norm_modulate(x_bits, eps: float, gamma=None, beta=None, scale=None, shift=N
     h = np.empty((rows, cols), dtype=np.float64)
     lib().mxr_norm_modulate(px, rows, cols, cols, float(eps), *[p for _, p in vecs], h.ctypes.data)
     return h
+
+
+# ---- microscaled attention -------------------------------------------------------------------
+def attention_mx(qc, qs, kc, ks, vtc, vts, BH: int, S: int, D: int, kvb: int, softmax_scale: float,
+                 qrows=None):
+    """(out, bound, absacc) [nq, D] in fp64 for the listed query rows (all rows if None); see
+    mxr_attention_mx.  q/k codes [BH*S, D/2] + scales [BH*S, D/32]; V^T codes [BH, D, Sp] E4M3 +
+    scales [BH, D, Sp/32], Sp = S rounded up to kvb."""
+    assert D <= 1024 and kvb <= 256 and kvb % 32 == 0
+    Sp = (S + kvb - 1) // kvb * kvb
+    arrs = [_c(a, np.uint8) for a in (qc, qs, kc, ks, vtc, vts)]
+    assert arrs[4][0].size == BH * D * Sp and arrs[5][0].size == BH * D * (Sp // 32)
+    rows = np.arange(BH * S, dtype=np.int64) if qrows is None else np.asarray(qrows, dtype=np.int64)
+    rows, pr = _c(rows, np.int64)
+    nq = rows.size
+    out = np.empty((nq, D)); bnd = np.empty((nq, D)); ab = np.empty((nq, D))
+    lib().mxr_attention_mx(*[p for _, p in arrs], BH, S, D, Sp, kvb, float(softmax_scale), pr, nq,
+                           out.ctypes.data, bnd.ctypes.data, ab.ctypes.data)
+    return out, bnd, ab
+
+
+def quantize_vt_mx8(v_bits, BH: int, S: int, D: int, kvb: int):
+    """V [BH, S, D] BF16 bits -> (codes [BH, D, Sp], scales [BH, D, Sp/32]): Q_MX8 of V transposed
+    along the key axis, keys padded with zeros to Sp = S rounded up to kvb."""
+    Sp = (S + kvb - 1) // kvb * kvb
+    vt = np.zeros((BH, D, Sp), dtype=np.uint16)
+    vt[:, :, :S] = np.asarray(v_bits, dtype=np.uint16).reshape(BH, S, D).transpose(0, 2, 1)
+    c, s = quantize_mx_bf16(vt.reshape(BH * D, Sp), E4M3)
+    return c.reshape(BH, D, Sp), s.reshape(BH, D, Sp // 32)

@@ -482,3 +482,93 @@ void mxr_norm_modulate(const uint16_t* x, int64_t rows, int64_t cols, int64_t ld
         }
     }
 }
+
+/* ------------------------------------------------------------------------------------------ */
+/* Microscaled attention                                                                      */
+/* ------------------------------------------------------------------------------------------ */
+/* "intel-ai/Wan2.2-I2V-A14B-Lightning-Diffusers-MXFP4-AutoRound", attention backends and
+ * Performance Profile: attention takes the larger share of the DiT's kernel time, and one of the
+ * backends runs it as microscaled FP4 attention; "Wan2.2-Animate-14B-Diffusers-MXFP4-AutoRound"
+ * notes that backend's lower fidelity.  The pages do not give its algorithm.  This is the reading
+ * used here: blocked attention with an online softmax, in the formats of the linear layer.
+ *  - Q and K rows (length D) are MXFP4 along D (the activation quantizer); V is MXFP8 (E4M3)
+ *    along the key axis: Q_MX8 of V transposed, keys padded with zeros to whole blocks.
+ *  - Per block of kvb keys: s_j = c * (q . k_j), c = softmax_scale * log2(e), keys past S
+ *    masked; m' = max(m, max_j s_j); alpha = 2^(m - m'); p_j = 2^(s_j - m');
+ *    l = alpha l + sum_j p_j; p^ = Q_MX8(p) in groups of 32 keys; o = alpha o + sum_j p^_j v^_j.
+ *  - out = o / l.
+ * fp64 throughout.  Only the query rows listed in qrows (indices into the BH*S rows) are
+ * computed.  bound accumulates like o with the worst case of |p^_j - p_j| between two
+ * implementations whose p differ by rounding noise: 2^(floor(log2 p_j) - 2) (a rounding step of
+ * p, or the block scale moving across a power of two) plus the subnormal quantum 2^(e - 9), times
+ * |v^_jd|; absacc accumulates sum_j p^_j |v^_jd|.  Both are divided by l like o. */
+void mxr_attention_mx(const uint8_t* qc, const uint8_t* qs, const uint8_t* kc, const uint8_t* ks,
+                      const uint8_t* vc, const uint8_t* vs, int64_t BH, int64_t S, int64_t D,
+                      int64_t Sp, int kvb, double softmax_scale, const int64_t* qrows, int64_t nq,
+                      double* out, double* bound, double* absacc) {
+    (void)BH;
+    const double c = softmax_scale / log(2.0);
+#pragma omp parallel for schedule(dynamic)
+    for (int64_t t = 0; t < nq; ++t) {
+        const int64_t row = qrows[t], bh = row / S;
+        double q[1024], o[1024], bnd[1024], ab[1024], s[256], p[256], ph[256], step[256];
+        for (int64_t d = 0; d < D; ++d) {
+            q[d] = mxr_e2m1_value((qc[row * (D / 2) + d / 2] >> (4 * (d & 1))) & 15) *
+                   mxr_e8m0_value(qs[row * (D / 32) + d / 32]);
+            o[d] = bnd[d] = ab[d] = 0.0;
+        }
+        double m = -INFINITY, l = 0.0;
+        for (int64_t b0 = 0; b0 < Sp; b0 += kvb) {
+            double mb = -INFINITY;
+            for (int j = 0; j < kvb; ++j) {
+                const int64_t key = b0 + j;
+                if (key >= S) { s[j] = -INFINITY; continue; }
+                const int64_t krow = bh * S + key;
+                double dot = 0.0;
+                for (int64_t d = 0; d < D; ++d)
+                    dot += q[d] * mxr_e2m1_value((kc[krow * (D / 2) + d / 2] >> (4 * (d & 1))) & 15) *
+                           mxr_e8m0_value(ks[krow * (D / 32) + d / 32]);
+                s[j] = c * dot;
+                if (s[j] > mb) mb = s[j];
+            }
+            const double mn = mb > m ? mb : m;
+            const double alpha = (m == -INFINITY) ? 0.0 : exp2(m - mn);
+            double psum = 0.0;
+            for (int j = 0; j < kvb; ++j) {
+                p[j] = (s[j] == -INFINITY) ? 0.0 : exp2(s[j] - mn);
+                psum += p[j];
+            }
+            l = l * alpha + psum;
+            for (int g = 0; g < kvb / 32; ++g) {
+                unsigned char codes[32], sc;
+                mxr_mx_block(p + 32 * g, 32, MXR_E4M3, codes, &sc);
+                const double e = mxr_e8m0_value(sc);
+                for (int j = 0; j < 32; ++j) {
+                    const double pj = p[32 * g + j];
+                    ph[32 * g + j] = mxr_e4m3_value(codes[j]) * e;
+                    step[32 * g + j] = pj > 0.0 ? ldexp(1.0, ilogb(pj) - 2) + e * ldexp(1.0, -9) : 0.0;
+                }
+            }
+            for (int64_t d = 0; d < D; ++d) {
+                double acc = 0.0, accb = 0.0, acca = 0.0;
+                for (int j = 0; j < kvb; ++j) {
+                    const int64_t key = b0 + j;
+                    const double v = mxr_e4m3_value(vc[(bh * D + d) * Sp + key]) *
+                                     mxr_e8m0_value(vs[(bh * D + d) * (Sp / 32) + key / 32]);
+                    acc += ph[j] * v;
+                    accb += step[j] * fabs(v);
+                    acca += ph[j] * fabs(v);
+                }
+                o[d] = o[d] * alpha + acc;
+                bnd[d] = bnd[d] * alpha + accb;
+                ab[d] = ab[d] * alpha + acca;
+            }
+            m = mn;
+        }
+        for (int64_t d = 0; d < D; ++d) {
+            out[t * D + d] = o[d] / l;
+            bound[t * D + d] = bnd[d] / l;
+            absacc[t * D + d] = ab[d] / l;
+        }
+    }
+}

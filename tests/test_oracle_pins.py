@@ -531,3 +531,74 @@ def test_norm_modulate_identities():
     hc = O.norm_modulate(const, 1e-6, beta=b, scale=s, shift=t)
     np.testing.assert_array_equal(hc[0], b.astype(np.float64) * (1.0 + s.astype(np.float64))
                                   + t.astype(np.float64))
+
+
+# ---------------------------------------------------------------------------------------------
+# microscaled attention
+# ---------------------------------------------------------------------------------------------
+def _attn_inputs(BH, S, D, kvb, seed, same_keys=False):
+    q = synth.bits16(synth.to_bf16(synth.normal_f32(seed, (BH * S, D), 1.0)))
+    kf = synth.normal_f32(seed + 1, (BH * S, D), 1.0)
+    if same_keys:
+        kf = np.tile(kf[:1], (BH * S, 1))
+    k = synth.bits16(synth.to_bf16(kf))
+    v = synth.bits16(synth.to_bf16(synth.normal_f32(seed + 2, (BH * S, D), 1.0)))
+    qc, qs = O.quantize_mx_bf16(q, O.E2M1)
+    kc, ks = O.quantize_mx_bf16(k, O.E2M1)
+    vtc, vts = O.quantize_vt_mx8(v, BH, S, D, kvb)
+    return qc, qs, kc, ks, vtc, vts
+
+
+def _vt_dequant(vtc, vts, BH, S, D):
+    Sp = vtc.shape[2]
+    vt = O.dequantize_mx(vtc.reshape(BH * D, Sp), vts.reshape(BH * D, Sp // 32), Sp, O.E4M3)
+    return vt.reshape(BH, D, Sp)[:, :, :S].transpose(0, 2, 1)  # [BH, S, D]
+
+
+def test_attention_single_key_and_identical_keys_are_exact():
+    BH, D, kvb = 2, 128, 64
+    # one key: p = 1 exactly, so out = v^ of that key
+    qc, qs, kc, ks, vtc, vts = _attn_inputs(BH, 1, D, kvb, 71)
+    out, bnd, _ = O.attention_mx(qc, qs, kc, ks, vtc, vts, BH, 1, D, kvb, D ** -0.5)
+    np.testing.assert_array_equal(out, _vt_dequant(vtc, vts, BH, 1, D).reshape(BH, D))
+    # identical keys: every s is equal, every p is 1 (quantized exactly), out = mean of v^
+    S = 100
+    qc, qs, kc, ks, vtc, vts = _attn_inputs(1, S, D, kvb, 72, same_keys=True)
+    out, _, _ = O.attention_mx(qc, qs, kc, ks, vtc, vts, 1, S, D, kvb, D ** -0.5, qrows=[0, 57, 99])
+    mean = _vt_dequant(vtc, vts, 1, S, D)[0].mean(axis=0)
+    np.testing.assert_allclose(out, np.broadcast_to(mean, (3, D)), rtol=1e-14, atol=1e-15)
+
+
+@pytest.mark.parametrize("S,kvb", [(130, 64), (77, 32), (64, 64)])
+def test_attention_matches_softmax_attention_within_p_quantization(S, kvb):
+    """torch's float64 softmax attention on the dequantized Q, K, V is an independent reference;
+    the oracle differs from it only by the E4M3 rounding of p (at most 1/8 of p, saturation at
+    the block maximum included), so |out - ref| <= sum_j p_j |v_j| / (8 l)."""
+    BH, D = 2, 128
+    qc, qs, kc, ks, vtc, vts = _attn_inputs(BH, S, D, kvb, 73 + S)
+    out, bnd, ab = O.attention_mx(qc, qs, kc, ks, vtc, vts, BH, S, D, kvb, D ** -0.5)
+    qd = O.dequantize_mx(qc, qs, D).reshape(BH, S, D)
+    kd = O.dequantize_mx(kc, ks, D).reshape(BH, S, D)
+    vd = _vt_dequant(vtc, vts, BH, S, D)
+    sc = torch.from_numpy(qd) @ torch.from_numpy(kd).transpose(1, 2) * D ** -0.5
+    p = torch.softmax(sc, dim=-1)
+    ref = (p @ torch.from_numpy(np.ascontiguousarray(vd))).numpy().reshape(BH * S, D)
+    tol = (p @ torch.from_numpy(np.abs(np.ascontiguousarray(vd)))).numpy().reshape(BH * S, D) / 8 + 1e-12
+    assert np.all(np.abs(out - ref) <= tol)
+    assert np.all(bnd >= 0) and np.all(ab > 0)
+    # the oracle's own p-rounding bound also covers the distance to the unquantized attention
+    assert np.all(np.abs(out - ref) <= 4 * bnd + 1e-12)
+
+
+def test_vt_quantizer_pads_and_round_trips():
+    BH, S, D, kvb = 2, 70, 128, 64
+    v = synth.bits16(synth.to_bf16(synth.normal_f32(79, (BH * S, D), 1.0)))
+    vtc, vts = O.quantize_vt_mx8(v, BH, S, D, kvb)
+    assert vtc.shape == (BH, D, 128) and vts.shape == (BH, D, 4)
+    assert np.all(vtc[:, :, S:] == 0) and np.all(vts[:, :, 3] == 0)  # keys 96..127 are all padding
+    vd = _vt_dequant(vtc, vts, BH, S, D)
+    x = O.bf16_values(v).reshape(BH, S, D)
+    # per element: half an E4M3 step (1/16 relative), 1/8 at a saturated block maximum, and half
+    # the subnormal quantum 2^(e - 9) of its 32-key block
+    e = np.repeat(vts.astype(np.float64) - 127, 32, axis=2)[:, :, :S].transpose(0, 2, 1)
+    assert np.all(np.abs(vd - x) <= np.abs(x) / 8 + 2.0 ** (e - 10))
