@@ -10,7 +10,7 @@ way and reported beside it.  The CPU baseline times the oracle on a bounded row 
   python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME] [--no-cpu]
 
 Other workloads (``--workload``) bench the variant paths: the FFN pair, W4A8 SVDQuant, the MXFP8
-W8A8 reference layer, NVFP4.
+W8A8 reference layer, NVFP4, the fused LayerNorm + quantizer and microscaled attention.
 """
 from __future__ import annotations
 
@@ -282,6 +282,43 @@ def bench_variant(args, torch, mx, synth):
             "frac_of_peak": v / peak, "peak_tflops": peak, "kernels": kernels}
 
 
+def bench_attention(args, torch, mx, synth):
+    """Microscaled attention at the Wan2.2-A14B 720p self-attention shape, in the projections'
+    layout: one step quantizes Q and K to MXFP4 and V^T to MXFP8, then runs the attention kernel.
+    FLOPs 4 S^2 D H (half on FP4 x FP4 MFMA, half on FP8 x FP8); the peak quoted is that mix's,
+    1 / (0.5 / 10.1 + 0.5 / 5.0) PFLOP/s."""
+    import numpy as np
+    wl = synth.WORKLOADS[args.workload]
+    S, H, D = wl.M, wl.extra["heads"], mx.ATTN_HEAD_DIM
+    to_dev = lambda x: torch.from_numpy(synth.bits16(synth.to_bf16(x)).view(np.int16)).view(torch.bfloat16).cuda()
+    q, k, v = (to_dev(x) for x in wl.qkv())
+    vv = v.view(S, H, D).transpose(0, 1)
+    qg, kg = mx.quantize(q, "mxfp4"), mx.quantize(k, "mxfp4")
+    vt = mx.quantize_vt(vv)
+    o = torch.empty((S, H * D), dtype=torch.bfloat16, device="cuda")
+    attn = lambda: mx.attention(qg, kg, vt, H, layout="shd", out=o)
+    step = lambda: (mx.quantize(q, "mxfp4", out=qg), mx.quantize(k, "mxfp4", out=kg),
+                    mx.quantize_vt(vv, out=vt), attn())
+    flops = 4.0 * S * S * D * H
+    peak = 1.0 / (0.5 / PEAK_TFLOPS["mxfp4"] + 0.5 / PEAK_TFLOPS["mxfp8"])
+    kernels = {}
+    for _ in range(args.warmup):
+        step()
+    ms = time_events(step, args.steps, torch)
+    kernels["attention_ms"] = time_events(attn, args.steps, torch)
+    kernels["attention_tflops"] = flops / (kernels["attention_ms"] * 1e-3) / 1e12
+    kernels["quant_qk_ms"] = time_events(lambda: (mx.quantize(q, "mxfp4", out=qg), mx.quantize(k, "mxfp4", out=kg)),
+                                         args.steps, torch)
+    kernels["quant_vt_ms"] = time_events(lambda: mx.quantize_vt(vv, out=vt), args.steps, torch)
+    val = flops / (ms * 1e-3) / 1e12
+    return {"metric": f"{wl.name} TFLOPS (Q/K/V quantization + attention)", "value": val,
+            "unit": "TFLOP/s", "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,
+            "ms_per_step": ms, "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
+            "dtype": "mxfp4 QK, mxfp8 PV", "data": "synthetic",
+            "config": {"workload": wl.name, "S": S, "heads": H, "head_dim": D},
+            "frac_of_peak": val / peak, "peak_tflops": peak, "kernels": kernels}
+
+
 COPY_BYTES = 1 << 30
 COPY_KERNEL_HINT = "copy"  # substring of the device copy kernel's name in the counter CSV
 
@@ -392,6 +429,8 @@ def main():
     if args.workload == "wan_a14b_attn_75600x5120x5120" or synth.WORKLOADS[args.workload].fmt == "mxfp4" \
             and not synth.WORKLOADS[args.workload].N2:
         res = bench_mx_linear(args, torch, mx, synth)
+    elif synth.WORKLOADS[args.workload].fmt == "attn":
+        res = bench_attention(args, torch, mx, synth)
     else:
         res = bench_variant(args, torch, mx, synth)
     print(json.dumps(res), flush=True)

@@ -80,8 +80,11 @@ def lib():
         F = ctypes.c_float
         L.mx_norm.argtypes = [P, I64, I64, I64, F, P, P, P, P, P, I64, P]
         L.mx_norm_quantize.argtypes = [P, I64, I64, I64, F, P, P, P, P, I32, I32, P, P, P]
+        L.mx_quantize_vt.argtypes = [P, I64, I64, I64, I64, I64, P, P, P]
+        L.mx_attention.argtypes = [P, P, P, P, I64, I64, P, P, I64, I64, I64, F, I32, P, I64, I64, P]
         for f in ("mx_quantize", "mx_dequantize", "mx_absmax", "mx_linear", "mx_linear_q",
-                  "mx_tiled_bytes", "mx_relayout", "mx_norm", "mx_norm_quantize"):
+                  "mx_tiled_bytes", "mx_relayout", "mx_norm", "mx_norm_quantize",
+                  "mx_quantize_vt", "mx_attention"):
             getattr(L, f).restype = ctypes.c_int
         if L.mx_abi_version() != 2:
             raise MxError("libmxfp.so ABI version mismatch")
@@ -228,6 +231,73 @@ def norm_quantize(x: torch.Tensor, eps: float = 1e-6, gamma=None, beta=None, sca
                                   _vec(shift, cols, "shift"), fmt, q.layout, _ptr(q.codes),
                                   _ptr(q.scales), _stream()))
     return q
+
+
+ATTN_HEAD_DIM = 128
+ATTN_KVB = 64
+
+
+def quantize_vt(v: torch.Tensor, out=None):
+    """MXFP8 of V transposed along the key axis, the V operand of attention(): v is a 3-D BF16
+    [BH, S, D] GPU tensor with unit last stride (any head and row strides, e.g. a transposed view
+    of an [S, H, D] projection).  Returns (codes [BH, D, Sp] uint8, scales [BH, D, Sp/32] uint8),
+    Sp = S rounded up to 64 (written into ``out`` = (codes, scales) when given)."""
+    _need_cuda(v, "v", torch.bfloat16)
+    if v.dim() != 3 or v.stride(2) != 1:
+        raise MxError("v must be 3-D [BH, S, D] with unit last stride")
+    BH, S, D = v.shape
+    Sp = (S + ATTN_KVB - 1) // ATTN_KVB * ATTN_KVB
+    if out is not None:
+        codes, scales = out
+        if tuple(codes.shape) != (BH, D, Sp) or tuple(scales.shape) != (BH, D, Sp // 32) or \
+                codes.dtype != torch.uint8 or scales.dtype != torch.uint8 or \
+                not codes.is_contiguous() or not scales.is_contiguous():
+            raise MxError("out must be contiguous uint8 (codes [BH, D, Sp], scales [BH, D, Sp/32])")
+    else:
+        codes = torch.empty((BH, D, Sp), dtype=torch.uint8, device=v.device)
+        scales = torch.empty((BH, D, Sp // 32), dtype=torch.uint8, device=v.device)
+    _check(lib().mx_quantize_vt(_ptr(v), BH, S, D, v.stride(1), v.stride(0), _ptr(codes), _ptr(scales),
+                                _stream()))
+    return codes, scales
+
+
+def attention(q: QMatrix, k: QMatrix, vt, heads: int, softmax_scale: Optional[float] = None,
+              layout: str = "bhsd", out_dtype=torch.bfloat16, out: Optional[torch.Tensor] = None):
+    """Microscaled attention (head dimension 128): q and k are row-major MXFP4 QMatrix of the
+    queries and keys, vt = quantize_vt(v).  layout "bhsd": q/k rows are heads * S rows of 128
+    (head-major), out [heads, S, 128]; layout "shd": q/k are S x (heads * 128) (one batch of a
+    projection), out [S, heads * 128].  softmax_scale defaults to 1/sqrt(128)."""
+    for t, name in ((q, "q"), (k, "k")):
+        if t.fmt != MXFP4 or t.layout != ROW_MAJOR:
+            raise MxError(f"{name} must be a row-major MXFP4 QMatrix")
+    if (q.rows, q.cols) != (k.rows, k.cols):
+        raise MxError("q and k shapes differ")
+    D = ATTN_HEAD_DIM
+    if layout == "bhsd":
+        if q.cols != D or q.rows % heads:
+            raise MxError("bhsd: q must be (heads * S) x 128")
+        S = q.rows // heads
+        ld, hs, shape = D, S * D, (heads, S, D)
+    elif layout == "shd":
+        if q.cols != heads * D:
+            raise MxError("shd: q must be S x (heads * 128)")
+        S = q.rows
+        ld, hs, shape = heads * D, D, (S, heads * D)
+    else:
+        raise MxError(f"unknown attention layout {layout!r}")
+    vc, vs = vt
+    Sp = (S + ATTN_KVB - 1) // ATTN_KVB * ATTN_KVB
+    if tuple(vc.shape) != (heads, D, Sp) or tuple(vs.shape) != (heads, D, Sp // 32):
+        raise MxError("vt does not match q's heads and sequence length")
+    o = out if out is not None else torch.empty(shape, dtype=out_dtype, device=q.codes.device)
+    if tuple(o.shape) != shape or not o.is_contiguous() or o.dtype not in (torch.bfloat16, torch.float32):
+        raise MxError(f"out must be a contiguous bfloat16 / float32 tensor of shape {shape}")
+    ld_o, hs_o = (D, S * D) if layout == "bhsd" else (heads * D, D)
+    scale = float(softmax_scale) if softmax_scale is not None else D ** -0.5
+    _check(lib().mx_attention(_ptr(q.codes), _ptr(q.scales), _ptr(k.codes), _ptr(k.scales), ld, hs,
+                              _ptr(vc), _ptr(vs), heads, S, D, scale,
+                              1 if o.dtype == torch.float32 else 0, _ptr(o), ld_o, hs_o, _stream()))
+    return o
 
 
 def relayout(q: QMatrix, layout=None) -> QMatrix:

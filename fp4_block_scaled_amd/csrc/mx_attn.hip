@@ -1,0 +1,288 @@
+// Microscaled attention for gfx950: the FP4 attention backend named by the MXFP4 Wan2.2 model
+// cards (intel-ai/Wan2.2-I2V-A14B-Lightning-Diffusers-MXFP4-AutoRound, attention backends and
+// Performance Profile), in the formats of the linear layer.  Q and K rows are MXFP4 along the
+// head dimension (the activation quantizer's row-major output); V is MXFP8 along the key axis,
+// stored transposed; the probabilities of each block are quantized to MXFP8 per 32 keys before
+// they multiply V.  Both products run on V_MFMA_SCALE_F32_32X32X64_F8F6F4, so every MX scale is
+// applied by the matrix core.
+//
+// Per block of 64 keys, with c = softmax_scale * log2(e):
+//   s_j = c (q . k_j) (keys past S masked to -inf), m' = max(m, max_j s_j), alpha = 2^(m - m'),
+//   p_j = 2^(s_j - m'), l = alpha l + sum_j p_j, o = alpha o + sum_j Q_MX8(p)_j v_j;
+// the output is o / l.  The running maximum is exact (no deferred rescaling), so the quantized
+// probabilities are the ones that definition gives; o is rescaled only when some query's maximum
+// moved (alpha == 1 otherwise, and multiplying by it changes nothing).
+#include "mx_common.h"
+#include "mx_internal.h"
+
+namespace mxk {
+
+constexpr int AT_D = 128;    // head dimension
+constexpr int AT_KVB = 64;   // keys per block
+constexpr int AT_WAVES = 4;  // waves per workgroup, 32 queries each
+
+typedef short s16x2a __attribute__((ext_vector_type(2)));
+
+// value of lane ^ 32 (the other half of the wave)
+__device__ __forceinline__ uint32_t xor32(uint32_t v) {
+  return (uint32_t)__builtin_amdgcn_ds_bpermute((lane_id() ^ 32) << 2, (int)v);
+}
+__device__ __forceinline__ float xor32f(float v) { return __uint_as_float(xor32(__float_as_uint(v))); }
+
+// ---------------------------------------------------------------------------------------------
+// V^T MXFP8 quantizer
+// ---------------------------------------------------------------------------------------------
+// One workgroup per (64 keys, 128 head-dim columns, head): the BF16 tile is staged in LDS as
+// loaded (key rows), then thread (d, g) gathers key group g of column d and quantizes it with the
+// MXFP8 group routine of the activation quantizer.  Keys past S are zero.
+constexpr int VT_PITCH = 136;  // BF16 elements per LDS key row (272 bytes, 16-byte aligned)
+
+__global__ __launch_bounds__(256) void quant_vt_kernel(const uint16_t* __restrict__ v, int S, int D,
+                                                       int64_t ld, int64_t hs, int Sp,
+                                                       uint8_t* __restrict__ codes,
+                                                       uint8_t* __restrict__ scales) {
+  __shared__ __attribute__((aligned(16))) uint16_t tile[AT_KVB * VT_PITCH];
+  const int kb0 = blockIdx.x * AT_KVB, d0 = blockIdx.y * 128;
+  const int64_t bh = blockIdx.z;
+  const int dn = min(128, D - d0);  // a multiple of 32
+  const uint16_t* vb = v + bh * hs + d0;
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const int c = threadIdx.x + 256 * i;  // 16-byte chunk: key row c / 16, columns 8 (c % 16)..
+    const int r = c >> 4, cc = c & 15;
+    uint4 x = {0u, 0u, 0u, 0u};
+    if (kb0 + r < S && 8 * cc < dn) x = *(const uint4*)(vb + (int64_t)(kb0 + r) * ld + 8 * cc);
+    *(uint4*)(tile + r * VT_PITCH + 8 * cc) = x;
+  }
+  __syncthreads();
+  const int d = threadIdx.x & 127, g = threadIdx.x >> 7;
+  if (d >= dn) return;
+  uint32_t w[16];
+#pragma unroll
+  for (int i = 0; i < 16; ++i)
+    w[i] = (uint32_t)tile[(32 * g + 2 * i) * VT_PITCH + d] |
+           (uint32_t)tile[(32 * g + 2 * i + 1) * VT_PITCH + d] << 16;
+  uint32_t out[8], sb;
+  quant_fp8_group32(w, out, sb);
+  const int64_t row = bh * D + d0 + d;
+  uint4* dst = (uint4*)(codes + row * Sp + kb0 + 32 * g);
+  dst[0] = uint4{out[0], out[1], out[2], out[3]};
+  dst[1] = uint4{out[4], out[5], out[6], out[7]};
+  scales[row * (Sp / 32) + kb0 / 32 + g] = (uint8_t)sb;
+}
+
+hipError_t launch_quant_vt(const uint16_t* v, int64_t BH, int64_t S, int64_t D, int64_t ld, int64_t hs,
+                           uint8_t* codes, uint8_t* scales, hipStream_t s) {
+  const int64_t Sp = (S + AT_KVB - 1) / AT_KVB * AT_KVB;
+  dim3 grid((unsigned)(Sp / AT_KVB), (unsigned)((D + 127) / 128), (unsigned)BH);
+  hipLaunchKernelGGL(quant_vt_kernel, grid, dim3(256), 0, s, v, (int)S, (int)D, ld, hs, (int)Sp, codes, scales);
+  return hipGetLastError();
+}
+
+// ---------------------------------------------------------------------------------------------
+// attention
+// ---------------------------------------------------------------------------------------------
+// Operand placement (see the GEMM kernels for the scaled MFMA's lane layout):
+//  - scores: first operand K (32 keys), second Q (32 queries), K dimension the head dimension
+//    (128 = two MFMAs, step s taking 32-element blocks s and 2 + s).  A lane holds query l % 32
+//    and, of each 32-key tile, keys 8 (e / 4) + 4 h + e % 4 (h = l / 32, e = 0..15);
+//  - PV: first operand V^T (32 head-dim rows), second the quantized probabilities (32 queries),
+//    K dimension the 64 keys of the block (scale block b = keys 32 b..32 b + 31).  The FP8 operand
+//    lane of half h must hold keys 16 h..16 h + 15 of each scale block: each lane has four runs
+//    of 4 keys per tile (one dword of codes each) and trades two of them with lane ^ 32;
+//  - the output tile has the scores' layout with head-dim rows in place of keys.
+struct AttnFrags {
+  v4i k[2][2];     // [key tile][MFMA step] FP4 codes of K
+  uint32_t ks[2];  // K scale dword of each key tile, shifted for the lane's half
+  v8i v[4];        // [head-dim tile] E4M3 codes of V^T
+  uint32_t vs[4];  // V^T scale byte of scale block h
+};
+
+__device__ __forceinline__ void attn_load_k(AttnFrags& f, const uint8_t* kc, const uint8_t* ks,
+                                            int64_t crow, int64_t srow, int kb0, int S, int r32, int h) {
+#pragma unroll
+  for (int t = 0; t < 2; ++t) {
+    const int key = min(kb0 + 32 * t + r32, S - 1);  // rows past S are read but masked
+    const uint8_t* row = kc + key * crow;
+    f.k[t][0] = *(const v4i*)(row + 32 * h);
+    f.k[t][1] = *(const v4i*)(row + 32 * h + 16);
+    f.ks[t] = *(const uint32_t*)(ks + key * srow) >> (16 * h);
+  }
+}
+
+__device__ __forceinline__ void attn_load_v(AttnFrags& f, const uint8_t* vc, const uint8_t* vs, int Sp,
+                                            int kb0, int r32, int h) {
+#pragma unroll
+  for (int dt = 0; dt < 4; ++dt) {
+    const int64_t d = 32 * dt + r32;
+    const uint8_t* row = vc + d * Sp + kb0 + 16 * h;
+    const uint4 a = *(const uint4*)row, b = *(const uint4*)(row + 32);
+    f.v[dt] = v8i{(int)a.x, (int)a.y, (int)a.z, (int)a.w, (int)b.x, (int)b.y, (int)b.z, (int)b.w};
+    f.vs[dt] = vs[d * (Sp / 32) + kb0 / 32 + h];
+  }
+}
+
+// Q_MX8 of one lane's 16 probabilities of a 32-key group whose (group-wide) maximum is amax >= 0:
+// scale byte floor(log2 amax) - 8 (clamped to -127), magnitudes clamped to 448 * 2^e, then the
+// scaled conversion, round to nearest even.  d[j] packs keys 4j..4j+3 of the lane's elements.
+__device__ __forceinline__ void quant_p8(const v16f& p, float amax, uint32_t (&d)[4], uint32_t& sb) {
+  int e = (int)(__float_as_uint(amax) >> 23) - 127 - 8;
+  if (e < -127) e = -127;
+  const float scale = __uint_as_float(e >= -126 ? (uint32_t)(127 + e) << 23 : 0x00400000u);
+  const float lim = __uint_as_float((uint32_t)(e + 135) << 23 | 0x600000u);  // 448 * 2^e
+#pragma unroll
+  for (int j = 0; j < 4; ++j) {
+    s16x2a r = __builtin_amdgcn_cvt_scalef32_pk_fp8_f32(s16x2a{0, 0}, fminf(p[4 * j], lim),
+                                                        fminf(p[4 * j + 1], lim), scale, false);
+    r = __builtin_amdgcn_cvt_scalef32_pk_fp8_f32(r, fminf(p[4 * j + 2], lim), fminf(p[4 * j + 3], lim),
+                                                 scale, true);
+    __builtin_memcpy(&d[j], &r, 4);
+  }
+  sb = (uint32_t)(e + 127);
+}
+
+template <bool OUTF32>
+__global__ __launch_bounds__(256, 2) void attn_mx_kernel(
+    const uint8_t* __restrict__ qc, const uint8_t* __restrict__ qs, const uint8_t* __restrict__ kc,
+    const uint8_t* __restrict__ ks, const uint8_t* __restrict__ vc, const uint8_t* __restrict__ vs,
+    int S, int Sp, int64_t ld, int64_t hs, float cexp, void* __restrict__ out, int64_t ld_o,
+    int64_t hs_o) {
+  const int lane = lane_id(), r32 = lane & 31, h = lane >> 5;
+  const int64_t bh = blockIdx.y;
+  const int q = blockIdx.x * (32 * AT_WAVES) + (threadIdx.x >> 6) * 32 + r32;
+  const int64_t crow = ld / 2, srow = ld / 32;  // bytes per row of codes / scales
+  const uint8_t* qcb = qc + bh * (hs / 2);
+  const uint8_t* qsb = qs + bh * (hs / 32);
+  const uint8_t* kcb = kc + bh * (hs / 2);
+  const uint8_t* ksb = ks + bh * (hs / 32);
+  const uint8_t* vcb = vc + bh * AT_D * (int64_t)Sp;
+  const uint8_t* vsb = vs + bh * AT_D * (int64_t)(Sp / 32);
+
+  const int qr = min(q, S - 1);
+  const v4i qf0 = *(const v4i*)(qcb + qr * crow + 32 * h);
+  const v4i qf1 = *(const v4i*)(qcb + qr * crow + 32 * h + 16);
+  const uint32_t qsc = *(const uint32_t*)(qsb + qr * srow) >> (16 * h);
+
+  AttnFrags f;
+  attn_load_k(f, kcb, ksb, crow, srow, 0, S, r32, h);
+  attn_load_v(f, vcb, vsb, Sp, 0, r32, h);
+
+  v16f o[4];
+#pragma unroll
+  for (int dt = 0; dt < 4; ++dt)
+#pragma unroll
+    for (int e = 0; e < 16; ++e) o[dt][e] = 0.0f;
+  float m = -__builtin_inff(), l = 0.0f;
+
+  for (int kb0 = 0; kb0 < Sp; kb0 += AT_KVB) {
+    v16f sc[2];
+#pragma unroll
+    for (int t = 0; t < 2; ++t) {
+      v16f z;
+#pragma unroll
+      for (int e = 0; e < 16; ++e) z[e] = 0.0f;
+      z = mfma_scale_32x32x64_f4f4(f.k[t][0], qf0, z, 4, 4, 0, (int)f.ks[t], 0, (int)qsc);
+      sc[t] = mfma_scale_32x32x64_f4f4(f.k[t][1], qf1, z, 4, 4, 1, (int)f.ks[t], 1, (int)qsc);
+    }
+    const int nk = kb0 + AT_KVB;
+    if (nk < Sp) attn_load_k(f, kcb, ksb, crow, srow, nk, S, r32, h);
+
+    // scores, running maximum, probabilities
+    const bool full = kb0 + AT_KVB <= S;
+    float mb = -__builtin_inff();
+#pragma unroll
+    for (int t = 0; t < 2; ++t)
+#pragma unroll
+      for (int e = 0; e < 16; ++e) {
+        float s = sc[t][e] * cexp;
+        if (!full && kb0 + 32 * t + 8 * (e >> 2) + 4 * h + (e & 3) >= S) s = -__builtin_inff();
+        sc[t][e] = s;
+        mb = fmaxf(mb, s);
+      }
+    mb = fmaxf(mb, xor32f(mb));
+    const float mn = fmaxf(m, mb);  // finite: every block holds a key < S
+    const float alpha = __builtin_amdgcn_exp2f(m - mn);
+    float ps = 0.0f, amax[2] = {0.0f, 0.0f};
+#pragma unroll
+    for (int t = 0; t < 2; ++t)
+#pragma unroll
+      for (int e = 0; e < 16; ++e) {
+        const float p = __builtin_amdgcn_exp2f(sc[t][e] - mn);
+        sc[t][e] = p;
+        ps += p;
+        amax[t] = fmaxf(amax[t], p);
+      }
+    l = l * alpha + ps;
+    m = mn;
+
+    // Q_MX8 of the probabilities, then the PV operand: half 0 takes keys 0..15 of each tile,
+    // half 1 keys 16..31
+    v8i pf;
+    uint32_t psb[2];
+#pragma unroll
+    for (int t = 0; t < 2; ++t) {
+      const float gmax = fmaxf(amax[t], xor32f(amax[t]));
+      uint32_t dw[4];
+      quant_p8(sc[t], gmax, dw, psb[t]);
+      const uint32_t r0 = xor32(h ? dw[0] : dw[2]);
+      const uint32_t r1 = xor32(h ? dw[1] : dw[3]);
+      pf[4 * t + 0] = (int)(h ? r0 : dw[0]);
+      pf[4 * t + 1] = (int)(h ? dw[2] : r0);
+      pf[4 * t + 2] = (int)(h ? r1 : dw[1]);
+      pf[4 * t + 3] = (int)(h ? dw[3] : r1);
+    }
+    const uint32_t psc = h ? psb[1] : psb[0];
+
+    if (__builtin_amdgcn_ballot_w64(alpha != 1.0f)) {
+#pragma unroll
+      for (int dt = 0; dt < 4; ++dt)
+#pragma unroll
+        for (int e = 0; e < 16; ++e) o[dt][e] *= alpha;
+    }
+#pragma unroll
+    for (int dt = 0; dt < 4; ++dt)
+      o[dt] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(f.v[dt], pf, o[dt], 0, 0, 0, (int)f.vs[dt],
+                                                              0, (int)psc);
+    if (nk < Sp) attn_load_v(f, vcb, vsb, Sp, nk, r32, h);
+  }
+
+  l += xor32f(l);
+  const float inv = 1.0f / l;
+  if (q >= S) return;
+  if (OUTF32) {
+    float* orow = (float*)out + bh * hs_o + (int64_t)q * ld_o;
+#pragma unroll
+    for (int dt = 0; dt < 4; ++dt)
+#pragma unroll
+      for (int j = 0; j < 4; ++j)
+        *(float4*)(orow + 32 * dt + 8 * j + 4 * h) =
+            float4{o[dt][4 * j] * inv, o[dt][4 * j + 1] * inv, o[dt][4 * j + 2] * inv, o[dt][4 * j + 3] * inv};
+  } else {
+    uint16_t* orow = (uint16_t*)out + bh * hs_o + (int64_t)q * ld_o;
+#pragma unroll
+    for (int dt = 0; dt < 4; ++dt)
+#pragma unroll
+      for (int j = 0; j < 4; ++j)
+        *(uint2*)(orow + 32 * dt + 8 * j + 4 * h) =
+            uint2{pack_bf16x2(o[dt][4 * j] * inv, o[dt][4 * j + 1] * inv),
+                  pack_bf16x2(o[dt][4 * j + 2] * inv, o[dt][4 * j + 3] * inv)};
+  }
+}
+
+hipError_t launch_attn_mx(const uint8_t* qc, const uint8_t* qs, const uint8_t* kc, const uint8_t* ks,
+                          int64_t ld, int64_t hs, const uint8_t* vc, const uint8_t* vs, int64_t BH,
+                          int64_t S, float softmax_scale, bool out_f32, void* out, int64_t ld_o,
+                          int64_t hs_o, hipStream_t s) {
+  const int64_t Sp = (S + AT_KVB - 1) / AT_KVB * AT_KVB;
+  const float cexp = (float)((double)softmax_scale * 1.4426950408889634);  // softmax_scale * log2(e)
+  dim3 grid((unsigned)((S + 32 * AT_WAVES - 1) / (32 * AT_WAVES)), (unsigned)BH);
+  if (out_f32)
+    hipLaunchKernelGGL(attn_mx_kernel<true>, grid, dim3(64 * AT_WAVES), 0, s, qc, qs, kc, ks, vc, vs,
+                       (int)S, (int)Sp, ld, hs, cexp, out, ld_o, hs_o);
+  else
+    hipLaunchKernelGGL(attn_mx_kernel<false>, grid, dim3(64 * AT_WAVES), 0, s, qc, qs, kc, ks, vc, vs,
+                       (int)S, (int)Sp, ld, hs, cexp, out, ld_o, hs_o);
+  return hipGetLastError();
+}
+
+}  // namespace mxk

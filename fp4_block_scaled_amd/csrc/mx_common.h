@@ -194,6 +194,45 @@ __device__ v16f mfma_scale_32x32x64_f4f8(v4i a, v8i b, v16f c, int fmt_a, int fm
     __asm("llvm.amdgcn.mfma.scale.f32.32x32x64.f8f6f4.v4i32.v8i32");
 
 // ---------------------------------------------------------------------------------------------
+// one lane's 32-element MXFP8 group
+// ---------------------------------------------------------------------------------------------
+typedef __bf16 bf2x __attribute__((ext_vector_type(2)));
+typedef short s16x2 __attribute__((ext_vector_type(2)));
+
+// One lane's 32-element MXFP8 group (16 BF16 pairs): the same rule and instruction sequence as
+// the standalone MX quantizer (amax, scale byte floor(log2 amax) - 8 clamped to [-127, 127],
+// magnitudes clamped to 448 * 2^e because the conversion overflows to NaN instead of saturating,
+// then V_CVT_SCALEF32_PK_FP8_BF16), with the amax taken within the lane.  NaN/Inf in the group:
+// codes 0, scale byte 0xFF.
+__device__ __forceinline__ void quant_fp8_group32(const uint32_t (&w)[16], uint32_t (&out)[8], uint32_t& sbyte) {
+  uint32_t amax = 0;
+#pragma unroll
+  for (int i = 0; i < 16; ++i) amax = max(amax, max(w[i] & 0x7FFFu, (w[i] >> 16) & 0x7FFFu));
+  const bool bad = amax >= 0x7F80u;
+  int e = (int)(amax >> 7) - 127 - 8;
+  if (e < -127) e = -127;
+  const float scale = __uint_as_float(e >= -126 ? (uint32_t)(127 + e) << 23 : 0x00400000u);
+  const uint32_t lim = (uint32_t)((e + 135) << 7 | 0x60);  // BF16 bits of 448 * 2^e
+#pragma unroll
+  for (int q = 0; q < 8; ++q) {
+    bf2x b[2];
+#pragma unroll
+    for (int k = 0; k < 2; ++k) {
+      const uint32_t v = w[2 * q + k];
+      const uint32_t lo = min(v & 0x7FFFu, lim), hi = min((v >> 16) & 0x7FFFu, lim);
+      const uint32_t c = lo | (hi << 16) | (v & 0x80008000u);
+      __builtin_memcpy(&b[k], &c, 4);
+    }
+    s16x2 r = __builtin_amdgcn_cvt_scalef32_pk_fp8_bf16(s16x2{0, 0}, b[0], scale, false);
+    r = __builtin_amdgcn_cvt_scalef32_pk_fp8_bf16(r, b[1], scale, true);
+    uint32_t d;
+    __builtin_memcpy(&d, &r, 4);
+    out[q] = bad ? 0u : d;
+  }
+  sbyte = bad ? 0xFFu : (uint32_t)(e + 127);
+}
+
+// ---------------------------------------------------------------------------------------------
 // cross-lane helpers
 // ---------------------------------------------------------------------------------------------
 // max with the lane xor 1 / xor 2 inside each quad (DPP quad_perm)

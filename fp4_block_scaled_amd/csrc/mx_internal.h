@@ -65,4 +65,17 @@ hipError_t launch_quant8_lowrank_down(const uint16_t* x, int64_t ld_x, const uin
                                       int K, int R, uint16_t* u, uint8_t* codes, uint8_t* scales,
                                       hipStream_t s);
 
+// V [BH, S, D] BF16 (element (b, s, d) at v[b * hs + s * ld + d], D % 32 == 0) -> MXFP8 of V
+// transposed: codes [BH, D, Sp] E4M3 and scales [BH, D, Sp / 32], Sp = S rounded up to 64, keys
+// past S zero.
+hipError_t launch_quant_vt(const uint16_t* v, int64_t BH, int64_t S, int64_t D, int64_t ld, int64_t hs,
+                           uint8_t* codes, uint8_t* scales, hipStream_t s);
+// Microscaled attention, head dimension 128: Q/K MXFP4 row-major codes and scales of rows
+// (b, s) at b * hs + s * ld elements; V^T as launch_quant_vt writes it; out [BH, S, 128] BF16 or
+// FP32 at b * hs_o + s * ld_o elements.
+hipError_t launch_attn_mx(const uint8_t* qc, const uint8_t* qs, const uint8_t* kc, const uint8_t* ks,
+                          int64_t ld, int64_t hs, const uint8_t* vc, const uint8_t* vs, int64_t BH,
+                          int64_t S, float softmax_scale, bool out_f32, void* out, int64_t ld_o,
+                          int64_t hs_o, hipStream_t s);
+
 }  // namespace mxk

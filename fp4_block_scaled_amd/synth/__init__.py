@@ -25,6 +25,7 @@ _lib = None
 # tensor ids inside a config's seed space
 T_A, T_W, T_BIAS, T_OUTLIER, T_LDOWN, T_LUP, T_W2, T_B2 = 1, 2, 3, 4, 5, 6, 7, 8
 T_MSCALE, T_MSHIFT = 9, 10  # modulation vectors of the norm in front of a linear
+T_Q, T_K, T_V = 11, 12, 13   # attention inputs
 
 
 def _load():
@@ -107,7 +108,7 @@ class Workload:
     M: int
     K: int
     N: int
-    fmt: str = "mxfp4"     # weight/activation format: mxfp4 | w4a8 | w8a8 | nvfp4 | norm
+    fmt: str = "mxfp4"     # weight/activation format: mxfp4 | w4a8 | w8a8 | nvfp4 | norm | attn
     a_sigma: float = 1.0
     outlier_frac: float = 0.01
     outlier_factor: float = 20.0
@@ -152,6 +153,22 @@ class Workload:
         return (normal_f32(self.seed_base + T_MSCALE, (self.K,), 0.1),
                 normal_f32(self.seed_base + T_MSHIFT, (self.K,), 0.1))
 
+    def qkv(self, S: int | None = None):
+        """F32 (q, k, v) of self-attention, each S x K (K = heads * head_dim, one batch of the
+        projections): N(0, a_sigma); q and k have round(outlier_frac * K) channels scaled by
+        outlier_factor (the channel spread of the normalized, rotated queries and keys)."""
+        S = self.M if S is None else S
+        out = []
+        for t in (T_Q, T_K, T_V):
+            x = normal_f32(self.seed_base + t, (S, self.K), self.a_sigma)
+            count = int(round(self.outlier_frac * self.K)) if t != T_V else 0
+            if count and S:
+                idx = outlier_channels(self.seed_base + T_OUTLIER + t, self.K, count)
+                _load().mxs_scale_columns_f32(x.ctypes.data, S, self.K, idx.ctypes.data, count,
+                                              float(self.outlier_factor))
+            out.append(x)
+        return tuple(out)
+
 
 WORKLOADS = {
     # smallest MXFP4 W4A4 instance
@@ -182,6 +199,10 @@ WORKLOADS = {
     "wan_a14b_norm_quant_75600x5120": Workload(
         "wan_a14b_norm_quant_75600x5120", 2, 75600, 5120, 5120, "norm",
         outlier_frac=0.005, outlier_factor=30.0),
+    # Wan2.2-A14B self-attention at 720p: 75600 tokens, 40 heads of 128 (N unused)
+    "wan_a14b_attn_mx_75600x40x128": Workload(
+        "wan_a14b_attn_mx_75600x40x128", 6, 75600, 5120, 5120, "attn",
+        outlier_frac=0.02, outlier_factor=3.0, extra={"heads": 40}),
     # NVFP4 at the A14B FFN shape with a static activation global scale (amax 40)
     "wan_a14b_nvfp4_75600x5120x13824": Workload(
         "wan_a14b_nvfp4_75600x5120x13824", 5, 75600, 5120, 13824, "nvfp4",

@@ -205,6 +205,50 @@ mx_status mx_norm(const uint16_t* x, int64_t rows, int64_t cols, int64_t ld_x, f
                   const float* gamma, const float* beta, const float* scale, const float* shift,
                   uint16_t* y, int64_t ld_y, void* stream);
 
+/* Microscaled attention: head dimension and keys per block. */
+#define MX_ATTN_HEAD_DIM 128
+#define MX_ATTN_KVB 64
+
+/*
+ * mx_quantize_vt - the V operand of mx_attention.  The FP4 attention backend of the MXFP4 Wan2.2
+ * model cards ("intel-ai/Wan2.2-I2V-A14B-Lightning-Diffusers-MXFP4-AutoRound", attention backends
+ * and Performance Profile) is read as attention in the formats of the linear layer; V's
+ * 32-element MXFP8 (E4M3) groups run along the key axis, the axis its product with the
+ * probabilities sums over, so V is stored transposed.  Input v: device BF16, BH heads of an
+ * S x D matrix, element (b, s, d) at v[b * hs_v + s * ld_v + d] (a [BH, S, D] tensor has
+ * ld_v = D, hs_v = S * D; one batch of a [S, H * D] projection has ld_v = H * D, hs_v = D).
+ * Output: codes [BH, D, Sp] E4M3 bytes and scales [BH, D, Sp / 32] E8M0, Sp = S rounded up to
+ * MX_ATTN_KVB, keys past S quantized as zeros; each group is quantized as mx_quantize quantizes
+ * an MXFP8 row group (bit for bit the same rule).  Requires D % 32 == 0, BH <= 65535,
+ * S <= 2^30, v 16-byte aligned with ld_v and hs_v multiples of 8, codes 16-byte aligned.
+ * Caller owns every buffer.
+ */
+mx_status mx_quantize_vt(const uint16_t* v, int64_t BH, int64_t S, int64_t D, int64_t ld_v,
+                         int64_t hs_v, uint8_t* codes, uint8_t* scales, void* stream);
+
+/*
+ * mx_attention - softmax(softmax_scale * Q K^T) V per head, with Q and K in MXFP4 and V and the
+ * probabilities in MXFP8 (same pages as mx_quantize_vt).  Per block of MX_ATTN_KVB keys, with
+ * c = softmax_scale * log2(e): s = c (q . k) (keys past S masked), m' = max(m, block max),
+ * alpha = 2^(m - m'), p = 2^(s - m'), l = alpha l + sum p, o = alpha o + Q_MX8(p) . V (p
+ * quantized to MXFP8 in groups of 32 consecutive keys); out = o / l.  Scores and o accumulate in
+ * FP32 on the scaled matrix cores.
+ *  q_codes/q_scales, k_codes/k_scales: row-major MXFP4 (mx_quantize's output) of BH heads of
+ *        S x MX_ATTN_HEAD_DIM, row (b, s) at element offset b * hs_qk + s * ld_qk: codes byte
+ *        (b * hs_qk + s * ld_qk) / 2, scale byte (b * hs_qk + s * ld_qk) / 32.  ld_qk and hs_qk
+ *        multiples of 128; codes 16-byte and scales 4-byte aligned.
+ *  vt_codes/vt_scales: mx_quantize_vt's output for the same BH, S, D (16-byte aligned).
+ *  out: device BF16 (MX_OUT_BF16, the RNE of the FP32 result) or FP32, element (b, s, d) at
+ *        b * hs_o + s * ld_o + d; 16-byte aligned, ld_o and hs_o multiples of 8.
+ * Requires D == MX_ATTN_HEAD_DIM, BH <= 65535, 0 <= S <= 2^30, softmax_scale finite and > 0.
+ * S == 0 does nothing.  Caller owns every buffer; nothing is allocated.
+ */
+mx_status mx_attention(const uint8_t* q_codes, const uint8_t* q_scales, const uint8_t* k_codes,
+                       const uint8_t* k_scales, int64_t ld_qk, int64_t hs_qk,
+                       const uint8_t* vt_codes, const uint8_t* vt_scales, int64_t BH, int64_t S,
+                       int64_t D, float softmax_scale, int32_t out_dtype, void* out, int64_t ld_o,
+                       int64_t hs_o, void* stream);
+
 /* Bytes of workspace mx_linear needs for an M x K activation in act_fmt (codes + scales of the
  * quantized activation -- in the tiled layout for the MX formats when K % 128 == 0 -- plus the
  * low-rank intermediate when rank > 0). */

@@ -215,6 +215,37 @@ def test_norm_validation(mx):
     assert nn(rows=0, x=0, y=0) == 0
 
 
+def test_attention_validation(mx):
+    L = mx.lib()
+    P = ctypes.c_void_p
+
+    def vt(v=FAKE, BH=2, S=100, D=128, ld=128, hs=12800, codes=FAKE, scales=FAKE):
+        return L.mx_quantize_vt(P(v) if v else None, BH, S, D, ld, hs, P(codes) if codes else None,
+                                P(scales) if scales else None, None)
+
+    def at(q=FAKE, k=FAKE, ld=128, hs=12800, v=FAKE, BH=2, S=100, D=128, scale=0.088, dt=0,
+           out=FAKE, ldo=128, hso=12800):
+        return L.mx_attention(P(q) if q else None, P(FAKE), P(k) if k else None, P(FAKE), ld, hs,
+                              P(v) if v else None, P(FAKE), BH, S, D, scale, dt,
+                              P(out) if out else None, ldo, hso, None)
+
+    assert vt(D=100, ld=104) == 2 and vt(D=0) == 2
+    assert vt(BH=70000) == 2 and vt(S=-1) == 2
+    assert vt(ld=64) == 3 and vt(hs=12804) == 3
+    assert vt(v=0) == 1 and vt(codes=0) == 1
+    assert vt(v=FAKE + 8) == 3 and vt(codes=FAKE + 4) == 3
+    assert vt(S=0, v=0, codes=0, scales=0) == 0
+    assert at(D=64) == 4
+    assert at(scale=0.0) == 2 and at(scale=float("nan")) == 2
+    assert at(dt=7) == 4
+    assert at(ld=192) == 3 and at(hs=64) == 3
+    assert at(ldo=100) == 3
+    assert at(q=0) == 1 and at(out=0) == 1
+    assert at(k=FAKE + 8) == 3 and at(out=FAKE + 8) == 3
+    assert at(S=0, q=0, k=0, v=0, out=0) == 0
+    assert at(BH=70000) == 2
+
+
 def test_relayout_validation(mx):
     L = mx.lib()
     rm, ti = _qm(mx, 16, 128, mx.MXFP4), _qm(mx, 16, 128, mx.MXFP4, layout=1)

@@ -1,0 +1,185 @@
+"""GPU parity of microscaled attention (MXFP4 Q/K, MXFP8 V and probabilities) and of the V^T
+MXFP8 quantizer, against the oracle.
+
+The V^T quantizer and the Q/K quantizer are compared bit for bit.  The attention output is
+compared element by element with the oracle's fp64 result on the oracle's own quantized
+operands, within
+
+    bound + (2e-3 + nblk * 2^-23) * absacc + 1e-6
+
+absacc = sum_j p^_j |v_jd| / l is the sum of |products| of the probabilities-times-V product,
+a block-scaled GEMM, so the GEMM tolerance 2e-3 * sum |a w| applies to it; nblk * 2^-23
+covers the fp32 rescale-and-add of o and l once per key block (nblk blocks) and the fp32
+scores and exponentials (the FP4 score products are exact); 1e-6 absorbs results near zero
+and probabilities below fp32's normal range.  bound is the oracle's worst case for
+probabilities that quantize to a neighbouring E4M3 value (the GPU's p is the fp32 evaluation
+of the same expression, so a p within rounding noise of an E4M3 rounding boundary, or of a
+power of two that moves the group scale, may land on the other side).
+
+Flips are rare (a relative noise of ~1e-7 against E4M3 steps of 2^-4..2^-3), so nearly every
+element must also be within (2^-12 + nblk * 2^-23) * absacc + 1e-6 without the bound: 2^-12
+is twice the accumulation error of the FP8 x FP8 scaled MFMA over one 64-key block as measured
+through the W8A8 GEMM on a softmax block's probabilities (8.8e-5 of sum |p^ v^|; the matrix
+core does not accumulate a block's products exactly in fp32).
+"""
+import numpy as np
+import pytest
+import torch
+
+import oracle as O
+from fp4_block_scaled_amd import synth
+from _util import dev_bits16, sample_rows, to_dev_bf16
+
+pytestmark = pytest.mark.gpu
+
+D = 128
+KVB = 64
+
+
+@pytest.fixture(scope="module")
+def mx():
+    import fp4_block_scaled_amd as m
+    assert torch.cuda.is_available()
+    m.lib()
+    return m
+
+
+def _bits(seed, shape, sigma):
+    return synth.bits16(synth.to_bf16(synth.normal_f32(seed, shape, sigma)))
+
+
+def _tol(bnd, ab, S, with_bound=True):
+    nblk = (S + KVB - 1) // KVB
+    if with_bound:
+        return bnd + (2e-3 + nblk * 2.0 ** -23) * ab + 1e-6
+    return (2.0 ** -12 + nblk * 2.0 ** -23) * ab + 1e-6
+
+
+def _compare(o_gpu, ref, bnd, ab, S, what, extra=0.0, flip_frac=0.02):
+    err = np.abs(o_gpu.astype(np.float64) - ref)
+    tol = _tol(bnd, ab, S) + extra
+    bad = err > tol
+    assert not bad.any(), (f"{what}: {bad.sum()} of {bad.size} outside tolerance, first "
+                           f"{np.argwhere(bad)[:4].tolist()}, max err/tol {np.max(err / tol):.3g}")
+    tight = err > _tol(bnd, ab, S, with_bound=False) + extra
+    frac = float(np.mean(tight))
+    print(f"{what}: max err/tol {np.max(err / tol):.3g}, beyond the no-flip tolerance: {frac:.2e}")
+    assert frac <= flip_frac
+
+
+def _oracle_operands(q_bits, k_bits, v_bits, BH, S):
+    qc, qs = O.quantize_mx_bf16(q_bits)
+    kc, ks = O.quantize_mx_bf16(k_bits)
+    vtc, vts = O.quantize_vt_mx8(v_bits, BH, S, D, KVB)
+    return qc, qs, kc, ks, vtc, vts
+
+
+@pytest.mark.parametrize("BH,S,D_", [(2, 100, 128), (3, 64, 64), (1, 1, 32), (2, 257, 256), (1, 1000, 96)])
+def test_quantize_vt_bit_exact(mx, BH, S, D_):
+    v_bits = _bits(31000 + S, (BH, S, D_), 1.0)
+    v_bits[0, 0, :4] = 0  # a zero run inside a group
+    codes, scales = mx.quantize_vt(to_dev_bf16(v_bits))
+    torch.cuda.synchronize()
+    rc, rs = O.quantize_vt_mx8(v_bits, BH, S, D_, KVB)
+    np.testing.assert_array_equal(scales.cpu().numpy(), rs)
+    np.testing.assert_array_equal(codes.cpu().numpy(), rc)
+
+
+def test_quantize_vt_strided_view_and_extremes(mx):
+    """A transposed view of an [S, H, D] projection (head stride D, row stride H * D), with
+    large, tiny and zero values in it."""
+    S, H = 150, 3
+    x = synth.normal_f32(31500, (S, H * D), 1.0)
+    x[:7, :40] *= 3000.0
+    x[20:60, 128:200] *= 1e-30
+    x[100:140, 256:300] = 0.0
+    v_bits = synth.bits16(synth.to_bf16(x))
+    v = to_dev_bf16(v_bits).view(S, H, D).transpose(0, 1)
+    codes, scales = mx.quantize_vt(v)
+    torch.cuda.synchronize()
+    ref_in = np.ascontiguousarray(v_bits.reshape(S, H, D).transpose(1, 0, 2))
+    rc, rs = O.quantize_vt_mx8(ref_in, H, S, D, KVB)
+    np.testing.assert_array_equal(scales.cpu().numpy(), rs)
+    np.testing.assert_array_equal(codes.cpu().numpy(), rc)
+
+
+@pytest.mark.parametrize("BH,S,sigma,scale", [
+    (2, 200, 1.0, D ** -0.5),   # ragged key block and query block
+    (1, 64, 1.0, D ** -0.5),    # one whole key block
+    (3, 1, 1.0, D ** -0.5),     # a single key: out = v^ exactly
+    (1, 129, 3.0, D ** -0.5),   # sharp softmax (scores spread over ~100 in log2 units)
+    (2, 384, 1.5, 0.2),
+    (1, 1000, 1.0, D ** -0.5),  # 16 key blocks
+])
+def test_attention_vs_oracle(mx, BH, S, sigma, scale):
+    q_bits = _bits(32000 + S, (BH * S, D), sigma)
+    k_bits = _bits(32100 + S, (BH * S, D), sigma)
+    v_bits = _bits(32200 + S, (BH * S, D), 1.0)
+    qc, qs, kc, ks, vtc, vts = _oracle_operands(q_bits, k_bits, v_bits, BH, S)
+    qg = mx.quantize(to_dev_bf16(q_bits), "mxfp4")
+    kg = mx.quantize(to_dev_bf16(k_bits), "mxfp4")
+    vt = mx.quantize_vt(to_dev_bf16(v_bits).view(BH, S, D))
+    o = mx.attention(qg, kg, vt, heads=BH, softmax_scale=scale, out_dtype=torch.float32)
+    torch.cuda.synchronize()
+    assert np.array_equal(qg.codes.cpu().numpy(), qc) and np.array_equal(kg.scales.cpu().numpy(), ks)
+    ref, bnd, ab = O.attention_mx(qc, qs, kc, ks, vtc, vts, BH, S, D, KVB, scale)
+    _compare(o.cpu().numpy().reshape(BH * S, D), ref, bnd, ab, S, f"attention BH={BH} S={S}")
+
+
+def test_single_key_is_v_exactly(mx):
+    """With one key every probability is 1 (quantized exactly), so out = v^ for every query."""
+    BH, S = 2, 1
+    q_bits = _bits(33000, (BH * S, D), 2.0)
+    k_bits = _bits(33001, (BH * S, D), 2.0)
+    v_bits = _bits(33002, (BH * S, D), 1.0)
+    vt = mx.quantize_vt(to_dev_bf16(v_bits).view(BH, S, D))
+    o = mx.attention(mx.quantize(to_dev_bf16(q_bits), "mxfp4"), mx.quantize(to_dev_bf16(k_bits), "mxfp4"),
+                     vt, heads=BH, out_dtype=torch.float32)
+    torch.cuda.synchronize()
+    vtc, vts = O.quantize_vt_mx8(v_bits, BH, S, D, KVB)
+    vhat = np.vectorize(O.e4m3_value)(vtc[:, :, 0]) * np.vectorize(O.e8m0_value)(vts[:, :, 0])
+    np.testing.assert_array_equal(o.cpu().numpy().reshape(BH, D).astype(np.float64), vhat)
+
+
+def test_attention_bf16_out_and_shd_layout(mx):
+    """Heads interleaved in the row ([S, H * 128], one batch of the projections) and BF16 out:
+    the BF16 result is the RNE of a value within the F32 tolerance."""
+    S, H, scale = 150, 3, D ** -0.5
+    q_bits = _bits(34000, (S, H * D), 1.2)
+    k_bits = _bits(34001, (S, H * D), 1.2)
+    v_bits = _bits(34002, (S, H * D), 1.0)
+    heads = lambda b: np.ascontiguousarray(b.reshape(S, H, D).transpose(1, 0, 2)).reshape(H * S, D)
+    qc, qs, kc, ks, vtc, vts = _oracle_operands(heads(q_bits), heads(k_bits), heads(v_bits), H, S)
+    vt = mx.quantize_vt(to_dev_bf16(v_bits).view(S, H, D).transpose(0, 1))
+    o = mx.attention(mx.quantize(to_dev_bf16(q_bits), "mxfp4"), mx.quantize(to_dev_bf16(k_bits), "mxfp4"),
+                     vt, heads=H, layout="shd")
+    torch.cuda.synchronize()
+    assert np.array_equal(vt[0].cpu().numpy(), vtc)
+    ref, bnd, ab = O.attention_mx(qc, qs, kc, ks, vtc, vts, H, S, D, KVB, scale)
+    got = O.bf16_values(dev_bits16(o)).reshape(S, H, D).transpose(1, 0, 2).reshape(H * S, D)
+    _compare(got, ref, bnd, ab, S, "attention shd bf16", extra=2.0 ** -8 * np.abs(ref))
+
+
+def test_full_size_wan_a14b_attention(mx):
+    """75600 tokens x 40 heads of 128 in the projections' layout with BF16 out, as the benchmark
+    runs it; sampled queries of three heads (including the last, partial query block, whose
+    last key block holds 16 keys) against the oracle, and the V^T codes of those heads bit for
+    bit."""
+    wl = synth.WORKLOADS["wan_a14b_attn_mx_75600x40x128"]
+    S, H = wl.M, wl.extra["heads"]
+    q, k, v = wl.qkv()
+    bits = [synth.bits16(synth.to_bf16(x)) for x in (q, k, v)]
+    del q, k, v
+    qd, kd, vd = (to_dev_bf16(b) for b in bits)
+    qg, kg = mx.quantize(qd, "mxfp4"), mx.quantize(kd, "mxfp4")
+    vt = mx.quantize_vt(vd.view(S, H, D).transpose(0, 1))
+    o = mx.attention(qg, kg, vt, heads=H, layout="shd")
+    torch.cuda.synchronize()
+    rows = np.unique(np.concatenate([sample_rows(S, 24), [0, S - 80, S - 1]]))
+    for h in (0, 17, H - 1):
+        hb = [np.ascontiguousarray(b[:, h * D:(h + 1) * D]) for b in bits]
+        qc, qs, kc, ks, vtc, vts = _oracle_operands(hb[0], hb[1], hb[2], 1, S)
+        assert np.array_equal(vt[0][h].cpu().numpy(), vtc[0]) and np.array_equal(vt[1][h].cpu().numpy(), vts[0])
+        ref, bnd, ab = O.attention_mx(qc, qs, kc, ks, vtc, vts, 1, S, D, KVB, D ** -0.5, qrows=rows)
+        got = O.bf16_values(dev_bits16(o[torch.from_numpy(rows).cuda(), h * D:(h + 1) * D]))
+        _compare(got, ref, bnd, ab, S, f"full-size head {h}", extra=2.0 ** -8 * np.abs(ref), flip_frac=0.05)
