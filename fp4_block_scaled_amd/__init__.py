@@ -240,8 +240,9 @@ ATTN_KVB = 64
 def quantize_vt(v: torch.Tensor, out=None):
     """MXFP8 of V transposed along the key axis, the V operand of attention(): v is a 3-D BF16
     [BH, S, D] GPU tensor with unit last stride (any head and row strides, e.g. a transposed view
-    of an [S, H, D] projection).  Returns (codes [BH, D, Sp] uint8, scales [BH, D, Sp/32] uint8),
-    Sp = S rounded up to 64 (written into ``out`` = (codes, scales) when given)."""
+    of an [S, H, D] projection).  Returns (codes [BH, Sp/64, D, 64] uint8, scales
+    [BH, Sp/64, D, 2] uint8): V^T in blocks of 64 keys, Sp = S rounded up to 64 (written into
+    ``out`` = (codes, scales) when given)."""
     _need_cuda(v, "v", torch.bfloat16)
     if v.dim() != 3 or v.stride(2) != 1:
         raise MxError("v must be 3-D [BH, S, D] with unit last stride")
@@ -249,13 +250,13 @@ def quantize_vt(v: torch.Tensor, out=None):
     Sp = (S + ATTN_KVB - 1) // ATTN_KVB * ATTN_KVB
     if out is not None:
         codes, scales = out
-        if tuple(codes.shape) != (BH, D, Sp) or tuple(scales.shape) != (BH, D, Sp // 32) or \
+        if tuple(codes.shape) != (BH, Sp // 64, D, 64) or tuple(scales.shape) != (BH, Sp // 64, D, 2) or \
                 codes.dtype != torch.uint8 or scales.dtype != torch.uint8 or \
                 not codes.is_contiguous() or not scales.is_contiguous():
-            raise MxError("out must be contiguous uint8 (codes [BH, D, Sp], scales [BH, D, Sp/32])")
+            raise MxError("out must be contiguous uint8 (codes [BH, Sp/64, D, 64], scales [BH, Sp/64, D, 2])")
     else:
-        codes = torch.empty((BH, D, Sp), dtype=torch.uint8, device=v.device)
-        scales = torch.empty((BH, D, Sp // 32), dtype=torch.uint8, device=v.device)
+        codes = torch.empty((BH, Sp // 64, D, 64), dtype=torch.uint8, device=v.device)
+        scales = torch.empty((BH, Sp // 64, D, 2), dtype=torch.uint8, device=v.device)
     _check(lib().mx_quantize_vt(_ptr(v), BH, S, D, v.stride(1), v.stride(0), _ptr(codes), _ptr(scales),
                                 _stream()))
     return codes, scales
@@ -287,7 +288,7 @@ def attention(q: QMatrix, k: QMatrix, vt, heads: int, softmax_scale: Optional[fl
         raise MxError(f"unknown attention layout {layout!r}")
     vc, vs = vt
     Sp = (S + ATTN_KVB - 1) // ATTN_KVB * ATTN_KVB
-    if tuple(vc.shape) != (heads, D, Sp) or tuple(vs.shape) != (heads, D, Sp // 32):
+    if tuple(vc.shape) != (heads, Sp // 64, D, 64) or tuple(vs.shape) != (heads, Sp // 64, D, 2):
         raise MxError("vt does not match q's heads and sequence length")
     o = out if out is not None else torch.empty(shape, dtype=out_dtype, device=q.codes.device)
     if tuple(o.shape) != shape or not o.is_contiguous() or o.dtype not in (torch.bfloat16, torch.float32):

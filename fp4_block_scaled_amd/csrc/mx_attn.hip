@@ -32,9 +32,11 @@ __device__ __forceinline__ float xor32f(float v) { return __uint_as_float(xor32(
 // ---------------------------------------------------------------------------------------------
 // V^T MXFP8 quantizer
 // ---------------------------------------------------------------------------------------------
-// One workgroup per (64 keys, 128 head-dim columns, head): the BF16 tile is staged in LDS as
-// loaded (key rows), then thread (d, g) gathers key group g of column d and quantizes it with the
-// MXFP8 group routine of the activation quantizer.  Keys past S are zero.
+// Output in key blocks of 64: codes [BH, Sp / 64, D, 64] and scales [BH, Sp / 64, D, 2], so that
+// one block of V^T (the 64 keys x D codes and 2 x D scales the attention kernel stages at a time)
+// is contiguous.  One workgroup per (64 keys, 128 head-dim columns, head): the BF16 tile is
+// staged in LDS as loaded (key rows), then thread (d, g) gathers key group g of column d and
+// quantizes it with the MXFP8 group routine of the activation quantizer.  Keys past S are zero.
 constexpr int VT_PITCH = 136;  // BF16 elements per LDS key row (272 bytes, 16-byte aligned)
 
 __global__ __launch_bounds__(256) void quant_vt_kernel(const uint16_t* __restrict__ v, int S, int D,
@@ -64,11 +66,11 @@ __global__ __launch_bounds__(256) void quant_vt_kernel(const uint16_t* __restric
            (uint32_t)tile[(32 * g + 2 * i + 1) * VT_PITCH + d] << 16;
   uint32_t out[8], sb;
   quant_fp8_group32(w, out, sb);
-  const int64_t row = bh * D + d0 + d;
-  uint4* dst = (uint4*)(codes + row * Sp + kb0 + 32 * g);
+  const int64_t row = (bh * (Sp / AT_KVB) + blockIdx.x) * D + d0 + d;  // [BH, Sp / 64, D] rows
+  uint4* dst = (uint4*)(codes + row * AT_KVB + 32 * g);
   dst[0] = uint4{out[0], out[1], out[2], out[3]};
   dst[1] = uint4{out[4], out[5], out[6], out[7]};
-  scales[row * (Sp / 32) + kb0 / 32 + g] = (uint8_t)sb;
+  scales[row * 2 + g] = (uint8_t)sb;
 }
 
 hipError_t launch_quant_vt(const uint16_t* v, int64_t BH, int64_t S, int64_t D, int64_t ld, int64_t hs,
@@ -84,47 +86,37 @@ hipError_t launch_quant_vt(const uint16_t* v, int64_t BH, int64_t S, int64_t D, 
 // ---------------------------------------------------------------------------------------------
 // Operand placement (see the GEMM kernels for the scaled MFMA's lane layout):
 //  - scores: first operand K (32 keys), second Q (32 queries), K dimension the head dimension
-//    (128 = two MFMAs, step s taking 32-element blocks s and 2 + s).  A lane holds query l % 32
-//    and, of each 32-key tile, keys 8 (e / 4) + 4 h + e % 4 (h = l / 32, e = 0..15);
+//    (128 = two MFMAs, step s taking 32-element blocks 2h + s in the lanes of half h).  A lane
+//    holds query l % 32 and, of each 32-key tile, keys 8 (e / 4) + 4 h + e % 4 (h = l / 32,
+//    e = 0..15);
 //  - PV: first operand V^T (32 head-dim rows), second the quantized probabilities (32 queries),
 //    K dimension the 64 keys of the block (scale block b = keys 32 b..32 b + 31).  The FP8 operand
 //    lane of half h must hold keys 16 h..16 h + 15 of each scale block: each lane has four runs
 //    of 4 keys per tile (one dword of codes each) and trades two of them with lane ^ 32;
 //  - the output tile has the scores' layout with head-dim rows in place of keys.
-struct AttnFrags {
-  v4i k[2][2];     // [key tile][MFMA step] FP4 codes of K
-  uint32_t ks[2];  // K scale dword of each key tile, shifted for the lane's half
-  v8i v[4];        // [head-dim tile] E4M3 codes of V^T
-  uint32_t vs[4];  // V^T scale byte of scale block h
-};
+//
+// A workgroup of 4 waves takes 128 queries of one head and walks the keys in blocks of 64
+// through a 3-stage LDS ring: block b + 2 is fetched by direct-to-LDS buffer loads while block b
+// is used, and each wave waits (vmcnt) only for its own loads of block b + 1 before the barrier
+// that publishes it.  Stage: K codes (64 rows of 64 bytes), V^T codes (128 rows of 64 bytes),
+// K scales (64 dwords), V^T scales (128 x 2 bytes).  Code rows hold their four 16-byte pieces
+// XOR-swizzled by (row >> 2) & 3, so the 16 rows that a quarter wave reads at one piece index
+// fall in distinct bank groups.
+constexpr int AT_STAGES = 3;
+constexpr int AT_KC = 64 * 64, AT_VC = AT_D * 64, AT_KS = 64 * 4, AT_VS = AT_D * 2;
+constexpr int AT_STAGE = AT_KC + AT_VC + AT_KS + AT_VS;
 
-__device__ __forceinline__ void attn_load_k(AttnFrags& f, const uint8_t* kc, const uint8_t* ks,
-                                            int64_t crow, int64_t srow, int kb0, int S, int r32, int h) {
-#pragma unroll
-  for (int t = 0; t < 2; ++t) {
-    const int key = min(kb0 + 32 * t + r32, S - 1);  // rows past S are read but masked
-    const uint8_t* row = kc + key * crow;
-    f.k[t][0] = *(const v4i*)(row + 32 * h);
-    f.k[t][1] = *(const v4i*)(row + 32 * h + 16);
-    f.ks[t] = *(const uint32_t*)(ks + key * srow) >> (16 * h);
-  }
+template <int N>
+__device__ __forceinline__ void at_wait_vmcnt() {
+  __builtin_amdgcn_s_waitcnt((N & 15) | (7 << 4) | (15 << 8) | ((N >> 4) << 14));
 }
-
-__device__ __forceinline__ void attn_load_v(AttnFrags& f, const uint8_t* vc, const uint8_t* vs, int Sp,
-                                            int kb0, int r32, int h) {
-#pragma unroll
-  for (int dt = 0; dt < 4; ++dt) {
-    const int64_t d = 32 * dt + r32;
-    const uint8_t* row = vc + d * Sp + kb0 + 16 * h;
-    const uint4 a = *(const uint4*)row, b = *(const uint4*)(row + 32);
-    f.v[dt] = v8i{(int)a.x, (int)a.y, (int)a.z, (int)a.w, (int)b.x, (int)b.y, (int)b.z, (int)b.w};
-    f.vs[dt] = vs[d * (Sp / 32) + kb0 / 32 + h];
-  }
-}
+__device__ __forceinline__ void at_barrier() { asm volatile("s_barrier" ::: "memory"); }
+__device__ __forceinline__ int at_swz(int row, int piece) { return row * 64 + 16 * (piece ^ ((row >> 2) & 3)); }
 
 // Q_MX8 of one lane's 16 probabilities of a 32-key group whose (group-wide) maximum is amax >= 0:
-// scale byte floor(log2 amax) - 8 (clamped to -127), magnitudes clamped to 448 * 2^e, then the
-// scaled conversion, round to nearest even.  d[j] packs keys 4j..4j+3 of the lane's elements.
+// scale byte floor(log2 amax) - 8 (clamped to -127), magnitudes clamped to 448 * 2^e (the
+// conversion gives NaN past the largest E4M3 value), then the scaled conversion, round to
+// nearest even.  d[j] packs keys 4j..4j+3 of the lane's elements.
 __device__ __forceinline__ void quant_p8(const v16f& p, float amax, uint32_t (&d)[4], uint32_t& sb) {
   int e = (int)(__float_as_uint(amax) >> 23) - 127 - 8;
   if (e < -127) e = -127;
@@ -142,30 +134,54 @@ __device__ __forceinline__ void quant_p8(const v16f& p, float amax, uint32_t (&d
 }
 
 template <bool OUTF32>
-__global__ __launch_bounds__(256, 2) void attn_mx_kernel(
+__global__ __launch_bounds__(64 * AT_WAVES, 2) void attn_mx_kernel(
     const uint8_t* __restrict__ qc, const uint8_t* __restrict__ qs, const uint8_t* __restrict__ kc,
     const uint8_t* __restrict__ ks, const uint8_t* __restrict__ vc, const uint8_t* __restrict__ vs,
-    int S, int Sp, int64_t ld, int64_t hs, float cexp, void* __restrict__ out, int64_t ld_o,
+    int S, int nblk, int64_t ld, int64_t hs, float cexp, void* __restrict__ out, int64_t ld_o,
     int64_t hs_o) {
+  __shared__ __attribute__((aligned(16))) uint8_t smem[AT_STAGES * AT_STAGE];
   const int lane = lane_id(), r32 = lane & 31, h = lane >> 5;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int64_t bh = blockIdx.y;
-  const int q = blockIdx.x * (32 * AT_WAVES) + (threadIdx.x >> 6) * 32 + r32;
+  const int q = blockIdx.x * (32 * AT_WAVES) + wave * 32 + r32;
   const int64_t crow = ld / 2, srow = ld / 32;  // bytes per row of codes / scales
-  const uint8_t* qcb = qc + bh * (hs / 2);
-  const uint8_t* qsb = qs + bh * (hs / 32);
-  const uint8_t* kcb = kc + bh * (hs / 2);
-  const uint8_t* ksb = ks + bh * (hs / 32);
-  const uint8_t* vcb = vc + bh * AT_D * (int64_t)Sp;
-  const uint8_t* vsb = vs + bh * AT_D * (int64_t)(Sp / 32);
 
   const int qr = min(q, S - 1);
-  const v4i qf0 = *(const v4i*)(qcb + qr * crow + 32 * h);
-  const v4i qf1 = *(const v4i*)(qcb + qr * crow + 32 * h + 16);
-  const uint32_t qsc = *(const uint32_t*)(qsb + qr * srow) >> (16 * h);
+  const uint8_t* qrow = qc + bh * (hs / 2) + qr * crow;
+  const v4i qf0 = *(const v4i*)(qrow + 32 * h);
+  const v4i qf1 = *(const v4i*)(qrow + 32 * h + 16);
+  const uint32_t qsc = *(const uint32_t*)(qs + bh * (hs / 32) + qr * srow) >> (16 * h);
+  wait_vmem_all();  // from here on the only vector-memory loads in flight are the ring's
 
-  AttnFrags f;
-  attn_load_k(f, kcb, ksb, crow, srow, 0, S, r32, h);
-  attn_load_v(f, vcb, vsb, Sp, 0, r32, h);
+  // ring fill: per block, wave w loads K rows 16w..16w+15 and V^T rows 32w..32w+31 (1 KB per
+  // instruction, lane i -> 16-byte slot i), wave 0 the K scales and wave 1 the V^T scales
+  const v4i rk = make_rsrc_sgpr(kc + bh * (hs / 2), (uint32_t)((S - 1) * crow + 64));
+  const v4i rks = make_rsrc_sgpr(ks + bh * (hs / 32), (uint32_t)((S - 1) * srow + 4));
+  const v4i rv = make_rsrc_sgpr(vc + bh * (int64_t)nblk * AT_VC, (uint32_t)nblk * AT_VC);
+  const v4i rvs = make_rsrc_sgpr(vs + bh * (int64_t)nblk * AT_VS, (uint32_t)nblk * AT_VS);
+  const uint32_t lds0 = lds_addr_of(smem);
+  const int krow = 16 * wave + (lane >> 2);
+  const int kpiece = (lane & 3) ^ ((krow >> 2) & 3);
+  const int vrow0 = 32 * wave + (lane >> 2), vrow1 = vrow0 + 16;
+  const uint32_t voff0 = (uint32_t)(vrow0 * 64 + 16 * ((lane & 3) ^ ((vrow0 >> 2) & 3)));
+  const uint32_t voff1 = (uint32_t)(vrow1 * 64 + 16 * ((lane & 3) ^ ((vrow1 >> 2) & 3)));
+  auto issue = [&](int b, int stage) {
+    const uint32_t sb = lds0 + (uint32_t)(stage * AT_STAGE);
+    const int key = min(b * AT_KVB + krow, S - 1);  // rows past S are fetched but masked
+    dma_lds16(rk, sb + (uint32_t)(wave * 1024), (uint32_t)(key * crow + 16 * kpiece), 0u);
+    dma_lds16(rv, sb + (uint32_t)(AT_KC + wave * 2048), voff0, (uint32_t)(b * AT_VC));
+    dma_lds16(rv, sb + (uint32_t)(AT_KC + wave * 2048 + 1024), voff1, (uint32_t)(b * AT_VC));
+    if (wave == 0) {
+      const int key2 = min(b * AT_KVB + lane, S - 1);
+      dma_lds4(rks, sb + (uint32_t)(AT_KC + AT_VC), (uint32_t)(key2 * srow), 0u);
+    } else if (wave == 1) {
+      dma_lds4(rvs, sb + (uint32_t)(AT_KC + AT_VC + AT_KS), (uint32_t)(4 * lane), (uint32_t)(b * AT_VS));
+    }
+  };
+  // this wave's loads of one block are complete when at most one block's worth is in flight
+  auto wait_block = [&]() {
+    if (wave < 2) at_wait_vmcnt<4>(); else at_wait_vmcnt<3>();
+  };
 
   v16f o[4];
 #pragma unroll
@@ -174,35 +190,70 @@ __global__ __launch_bounds__(256, 2) void attn_mx_kernel(
     for (int e = 0; e < 16; ++e) o[dt][e] = 0.0f;
   float m = -__builtin_inff(), l = 0.0f;
 
-  for (int kb0 = 0; kb0 < Sp; kb0 += AT_KVB) {
+  issue(0, 0);
+  issue(min(1, nblk - 1), 1);
+  wait_block();
+  at_barrier();
+
+  for (int b = 0; b < nblk; ++b) {
+    const int cur = b % AT_STAGES;
+    // the last iterations refetch the last block into stages nobody reads again: every iteration
+    // issues the same loads, so the wait below counts the same for all of them
+    issue(min(b + 2, nblk - 1), (b + 2) % AT_STAGES);
+    const uint8_t* st = smem + cur * AT_STAGE;
+
+    // scores
     v16f sc[2];
 #pragma unroll
     for (int t = 0; t < 2; ++t) {
+      const int row = 32 * t + r32;
+      const v4i k0 = *(const v4i*)(st + at_swz(row, 2 * h));
+      const v4i k1 = *(const v4i*)(st + at_swz(row, 2 * h + 1));
+      const int ksc = (int)(*(const uint32_t*)(st + AT_KC + AT_VC + 4 * row) >> (16 * h));
       v16f z;
 #pragma unroll
       for (int e = 0; e < 16; ++e) z[e] = 0.0f;
-      z = mfma_scale_32x32x64_f4f4(f.k[t][0], qf0, z, 4, 4, 0, (int)f.ks[t], 0, (int)qsc);
-      sc[t] = mfma_scale_32x32x64_f4f4(f.k[t][1], qf1, z, 4, 4, 1, (int)f.ks[t], 1, (int)qsc);
+      z = mfma_scale_32x32x64_f4f4(k0, qf0, z, 4, 4, 0, ksc, 0, (int)qsc);
+      sc[t] = mfma_scale_32x32x64_f4f4(k1, qf1, z, 4, 4, 1, ksc, 1, (int)qsc);
     }
-    const int nk = kb0 + AT_KVB;
-    if (nk < Sp) attn_load_k(f, kcb, ksb, crow, srow, nk, S, r32, h);
+    // V^T fragments (read early: the softmax below covers their latency)
+    v8i vf[4];
+    int vsc[4];
+#pragma unroll
+    for (int dt = 0; dt < 4; ++dt) {
+      const int row = 32 * dt + r32;
+      const uint4 a = *(const uint4*)(st + AT_KC + at_swz(row, h));
+      const uint4 c = *(const uint4*)(st + AT_KC + at_swz(row, 2 + h));
+      vf[dt] = v8i{(int)a.x, (int)a.y, (int)a.z, (int)a.w, (int)c.x, (int)c.y, (int)c.z, (int)c.w};
+      vsc[dt] = st[AT_KC + AT_VC + AT_KS + 2 * row + h];
+    }
 
-    // scores, running maximum, probabilities
-    const bool full = kb0 + AT_KVB <= S;
-    float mb = -__builtin_inff();
+    // s = c * acc (rounded: the maximal key's p must be exactly 2^0 = 1, as the definition has
+    // it; p slightly below 1 would move its group's scale down a power of two), keys past S
+    // masked; the per-tile maxima of s give each 32-key group's largest p directly
 #pragma unroll
     for (int t = 0; t < 2; ++t)
 #pragma unroll
-      for (int e = 0; e < 16; ++e) {
-        float s = sc[t][e] * cexp;
-        if (!full && kb0 + 32 * t + 8 * (e >> 2) + 4 * h + (e & 3) >= S) s = -__builtin_inff();
-        sc[t][e] = s;
-        mb = fmaxf(mb, s);
-      }
-    mb = fmaxf(mb, xor32f(mb));
-    const float mn = fmaxf(m, mb);  // finite: every block holds a key < S
+      for (int e = 0; e < 16; ++e) sc[t][e] *= cexp;
+    if ((b + 1) * AT_KVB > S) {
+#pragma unroll
+      for (int t = 0; t < 2; ++t)
+#pragma unroll
+        for (int e = 0; e < 16; ++e)
+          if (b * AT_KVB + 32 * t + 8 * (e >> 2) + 4 * h + (e & 3) >= S) sc[t][e] = -__builtin_inff();
+    }
+    float mt[2];
+#pragma unroll
+    for (int t = 0; t < 2; ++t) {
+      float x = sc[t][0];
+#pragma unroll
+      for (int e = 1; e < 16; ++e) x = fmaxf(x, sc[t][e]);
+      mt[t] = fmaxf(x, xor32f(x));
+    }
+    const float mn = fmaxf(m, fmaxf(mt[0], mt[1]));  // finite: every block holds a key < S
     const float alpha = __builtin_amdgcn_exp2f(m - mn);
-    float ps = 0.0f, amax[2] = {0.0f, 0.0f};
+    m = mn;
+    float ps = 0.0f;
 #pragma unroll
     for (int t = 0; t < 2; ++t)
 #pragma unroll
@@ -210,10 +261,8 @@ __global__ __launch_bounds__(256, 2) void attn_mx_kernel(
         const float p = __builtin_amdgcn_exp2f(sc[t][e] - mn);
         sc[t][e] = p;
         ps += p;
-        amax[t] = fmaxf(amax[t], p);
       }
     l = l * alpha + ps;
-    m = mn;
 
     // Q_MX8 of the probabilities, then the PV operand: half 0 takes keys 0..15 of each tile,
     // half 1 keys 16..31
@@ -221,7 +270,7 @@ __global__ __launch_bounds__(256, 2) void attn_mx_kernel(
     uint32_t psb[2];
 #pragma unroll
     for (int t = 0; t < 2; ++t) {
-      const float gmax = fmaxf(amax[t], xor32f(amax[t]));
+      const float gmax = __builtin_amdgcn_exp2f(mt[t] - mn);  // = max of the group's p
       uint32_t dw[4];
       quant_p8(sc[t], gmax, dw, psb[t]);
       const uint32_t r0 = xor32(h ? dw[0] : dw[2]);
@@ -231,7 +280,7 @@ __global__ __launch_bounds__(256, 2) void attn_mx_kernel(
       pf[4 * t + 2] = (int)(h ? r1 : dw[1]);
       pf[4 * t + 3] = (int)(h ? dw[3] : r1);
     }
-    const uint32_t psc = h ? psb[1] : psb[0];
+    const int psc = (int)(h ? psb[1] : psb[0]);
 
     if (__builtin_amdgcn_ballot_w64(alpha != 1.0f)) {
 #pragma unroll
@@ -241,10 +290,12 @@ __global__ __launch_bounds__(256, 2) void attn_mx_kernel(
     }
 #pragma unroll
     for (int dt = 0; dt < 4; ++dt)
-      o[dt] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(f.v[dt], pf, o[dt], 0, 0, 0, (int)f.vs[dt],
-                                                              0, (int)psc);
-    if (nk < Sp) attn_load_v(f, vcb, vsb, Sp, nk, r32, h);
+      o[dt] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(vf[dt], pf, o[dt], 0, 0, 0, vsc[dt], 0, psc);
+
+    wait_block();  // block b + 1 is in this wave's part of the ring
+    at_barrier();
   }
+  wait_vmem_all();  // the refetches of the last iterations land before the workgroup ends
 
   l += xor32f(l);
   const float inv = 1.0f / l;
@@ -273,15 +324,15 @@ hipError_t launch_attn_mx(const uint8_t* qc, const uint8_t* qs, const uint8_t* k
                           int64_t ld, int64_t hs, const uint8_t* vc, const uint8_t* vs, int64_t BH,
                           int64_t S, float softmax_scale, bool out_f32, void* out, int64_t ld_o,
                           int64_t hs_o, hipStream_t s) {
-  const int64_t Sp = (S + AT_KVB - 1) / AT_KVB * AT_KVB;
+  const int nblk = (int)((S + AT_KVB - 1) / AT_KVB);
   const float cexp = (float)((double)softmax_scale * 1.4426950408889634);  // softmax_scale * log2(e)
   dim3 grid((unsigned)((S + 32 * AT_WAVES - 1) / (32 * AT_WAVES)), (unsigned)BH);
   if (out_f32)
     hipLaunchKernelGGL(attn_mx_kernel<true>, grid, dim3(64 * AT_WAVES), 0, s, qc, qs, kc, ks, vc, vs,
-                       (int)S, (int)Sp, ld, hs, cexp, out, ld_o, hs_o);
+                       (int)S, nblk, ld, hs, cexp, out, ld_o, hs_o);
   else
     hipLaunchKernelGGL(attn_mx_kernel<false>, grid, dim3(64 * AT_WAVES), 0, s, qc, qs, kc, ks, vc, vs,
-                       (int)S, (int)Sp, ld, hs, cexp, out, ld_o, hs_o);
+                       (int)S, nblk, ld, hs, cexp, out, ld_o, hs_o);
   return hipGetLastError();
 }
 

@@ -66,8 +66,8 @@ hipError_t launch_quant8_lowrank_down(const uint16_t* x, int64_t ld_x, const uin
                                       hipStream_t s);
 
 // V [BH, S, D] BF16 (element (b, s, d) at v[b * hs + s * ld + d], D % 32 == 0) -> MXFP8 of V
-// transposed: codes [BH, D, Sp] E4M3 and scales [BH, D, Sp / 32], Sp = S rounded up to 64, keys
-// past S zero.
+// transposed, in key blocks of 64: codes [BH, Sp / 64, D, 64] E4M3 and scales [BH, Sp / 64, D, 2],
+// Sp = S rounded up to 64, keys past S zero.
 hipError_t launch_quant_vt(const uint16_t* v, int64_t BH, int64_t S, int64_t D, int64_t ld, int64_t hs,
                            uint8_t* codes, uint8_t* scales, hipStream_t s);
 // Microscaled attention, head dimension 128: Q/K MXFP4 row-major codes and scales of rows

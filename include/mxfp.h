@@ -217,10 +217,13 @@ mx_status mx_norm(const uint16_t* x, int64_t rows, int64_t cols, int64_t ld_x, f
  * probabilities sums over, so V is stored transposed.  Input v: device BF16, BH heads of an
  * S x D matrix, element (b, s, d) at v[b * hs_v + s * ld_v + d] (a [BH, S, D] tensor has
  * ld_v = D, hs_v = S * D; one batch of a [S, H * D] projection has ld_v = H * D, hs_v = D).
- * Output: codes [BH, D, Sp] E4M3 bytes and scales [BH, D, Sp / 32] E8M0, Sp = S rounded up to
- * MX_ATTN_KVB, keys past S quantized as zeros; each group is quantized as mx_quantize quantizes
- * an MXFP8 row group (bit for bit the same rule).  Requires D % 32 == 0, BH <= 65535,
- * S <= 2^30, v 16-byte aligned with ld_v and hs_v multiples of 8, codes 16-byte aligned.
+ * Output, in blocks of MX_ATTN_KVB keys (Sp = S rounded up to MX_ATTN_KVB, keys past S quantized
+ * as zeros): codes [BH, Sp / 64, D, 64] E4M3 bytes -- code (b, s, d) at
+ * ((b * Sp / 64 + s / 64) * D + d) * 64 + s % 64 -- and scales [BH, Sp / 64, D, 2] E8M0, the
+ * scale of keys 32 g..32 g + 31 of block s / 64 at ((b * Sp / 64 + s / 64) * D + d) * 2 + g % 2.
+ * Each 32-key group is quantized as mx_quantize quantizes an MXFP8 row group (bit for bit the
+ * same rule).  Requires D % 32 == 0, BH <= 65535, S <= 2^24, v 16-byte aligned with ld_v and
+ * hs_v multiples of 8, codes 16-byte aligned.
  * Caller owns every buffer.
  */
 mx_status mx_quantize_vt(const uint16_t* v, int64_t BH, int64_t S, int64_t D, int64_t ld_v,
@@ -237,10 +240,12 @@ mx_status mx_quantize_vt(const uint16_t* v, int64_t BH, int64_t S, int64_t D, in
  *        S x MX_ATTN_HEAD_DIM, row (b, s) at element offset b * hs_qk + s * ld_qk: codes byte
  *        (b * hs_qk + s * ld_qk) / 2, scale byte (b * hs_qk + s * ld_qk) / 32.  ld_qk and hs_qk
  *        multiples of 128; codes 16-byte and scales 4-byte aligned.
- *  vt_codes/vt_scales: mx_quantize_vt's output for the same BH, S, D (16-byte aligned).
+ *  vt_codes/vt_scales: mx_quantize_vt's output for the same BH, S, D (codes 16-byte, scales
+ *        4-byte aligned).
  *  out: device BF16 (MX_OUT_BF16, the RNE of the FP32 result) or FP32, element (b, s, d) at
  *        b * hs_o + s * ld_o + d; 16-byte aligned, ld_o and hs_o multiples of 8.
- * Requires D == MX_ATTN_HEAD_DIM, BH <= 65535, 0 <= S <= 2^30, softmax_scale finite and > 0.
+ * Requires D == MX_ATTN_HEAD_DIM, BH <= 65535, 0 <= S <= 2^24 with (S + 64) * ld_qk / 2 < 2^32,
+ * softmax_scale finite and > 0.
  * S == 0 does nothing.  Caller owns every buffer; nothing is allocated.
  */
 mx_status mx_attention(const uint8_t* q_codes, const uint8_t* q_scales, const uint8_t* k_codes,

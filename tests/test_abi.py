@@ -244,6 +244,8 @@ def test_attention_validation(mx):
     assert at(k=FAKE + 8) == 3 and at(out=FAKE + 8) == 3
     assert at(S=0, q=0, k=0, v=0, out=0) == 0
     assert at(BH=70000) == 2
+    assert at(S=1 << 24, ld=512, hs=0) == 2      # K offsets must stay 32-bit
+    assert vt(S=(1 << 24) + 1) == 2
 
 
 def test_relayout_validation(mx):

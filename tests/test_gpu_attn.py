@@ -67,6 +67,15 @@ def _compare(o_gpu, ref, bnd, ab, S, what, extra=0.0, flip_frac=0.02):
     assert frac <= flip_frac
 
 
+def _blocked(vtc, vts):
+    """The oracle's V^T MXFP8 ([BH, D, Sp] codes, [BH, D, Sp/32] scales) in the library's
+    key-block-major layout ([BH, Sp/64, D, 64], [BH, Sp/64, D, 2])."""
+    BH, D_, Sp = vtc.shape
+    nb = Sp // KVB
+    return (np.ascontiguousarray(vtc.reshape(BH, D_, nb, KVB).transpose(0, 2, 1, 3)),
+            np.ascontiguousarray(vts.reshape(BH, D_, nb, 2).transpose(0, 2, 1, 3)))
+
+
 def _oracle_operands(q_bits, k_bits, v_bits, BH, S):
     qc, qs = O.quantize_mx_bf16(q_bits)
     kc, ks = O.quantize_mx_bf16(k_bits)
@@ -80,7 +89,7 @@ def test_quantize_vt_bit_exact(mx, BH, S, D_):
     v_bits[0, 0, :4] = 0  # a zero run inside a group
     codes, scales = mx.quantize_vt(to_dev_bf16(v_bits))
     torch.cuda.synchronize()
-    rc, rs = O.quantize_vt_mx8(v_bits, BH, S, D_, KVB)
+    rc, rs = _blocked(*O.quantize_vt_mx8(v_bits, BH, S, D_, KVB))
     np.testing.assert_array_equal(scales.cpu().numpy(), rs)
     np.testing.assert_array_equal(codes.cpu().numpy(), rc)
 
@@ -98,7 +107,7 @@ def test_quantize_vt_strided_view_and_extremes(mx):
     codes, scales = mx.quantize_vt(v)
     torch.cuda.synchronize()
     ref_in = np.ascontiguousarray(v_bits.reshape(S, H, D).transpose(1, 0, 2))
-    rc, rs = O.quantize_vt_mx8(ref_in, H, S, D, KVB)
+    rc, rs = _blocked(*O.quantize_vt_mx8(ref_in, H, S, D, KVB))
     np.testing.assert_array_equal(scales.cpu().numpy(), rs)
     np.testing.assert_array_equal(codes.cpu().numpy(), rc)
 
@@ -154,7 +163,7 @@ def test_attention_bf16_out_and_shd_layout(mx):
     o = mx.attention(mx.quantize(to_dev_bf16(q_bits), "mxfp4"), mx.quantize(to_dev_bf16(k_bits), "mxfp4"),
                      vt, heads=H, layout="shd")
     torch.cuda.synchronize()
-    assert np.array_equal(vt[0].cpu().numpy(), vtc)
+    assert np.array_equal(vt[0].cpu().numpy(), _blocked(vtc, vts)[0])
     ref, bnd, ab = O.attention_mx(qc, qs, kc, ks, vtc, vts, H, S, D, KVB, scale)
     got = O.bf16_values(dev_bits16(o)).reshape(S, H, D).transpose(1, 0, 2).reshape(H * S, D)
     _compare(got, ref, bnd, ab, S, "attention shd bf16", extra=2.0 ** -8 * np.abs(ref))
@@ -179,7 +188,8 @@ def test_full_size_wan_a14b_attention(mx):
     for h in (0, 17, H - 1):
         hb = [np.ascontiguousarray(b[:, h * D:(h + 1) * D]) for b in bits]
         qc, qs, kc, ks, vtc, vts = _oracle_operands(hb[0], hb[1], hb[2], 1, S)
-        assert np.array_equal(vt[0][h].cpu().numpy(), vtc[0]) and np.array_equal(vt[1][h].cpu().numpy(), vts[0])
+        bc, bs = _blocked(vtc, vts)
+        assert np.array_equal(vt[0][h].cpu().numpy(), bc[0]) and np.array_equal(vt[1][h].cpu().numpy(), bs[0])
         ref, bnd, ab = O.attention_mx(qc, qs, kc, ks, vtc, vts, 1, S, D, KVB, D ** -0.5, qrows=rows)
         got = O.bf16_values(dev_bits16(o[torch.from_numpy(rows).cuda(), h * D:(h + 1) * D]))
         _compare(got, ref, bnd, ab, S, f"full-size head {h}", extra=2.0 ** -8 * np.abs(ref), flip_frac=0.05)
