@@ -195,11 +195,13 @@ __global__ __launch_bounds__(64 * AT_WAVES, 2) void attn_mx_kernel(
   wait_block();
   at_barrier();
 
-  for (int b = 0; b < nblk; ++b) {
-    const int cur = b % AT_STAGES;
+  // One key block; the ring stage is a compile-time constant (the loop below is unrolled by the
+  // ring depth), so every LDS address is a fixed offset from loop-invariant registers.
+  auto step = [&](int b, auto stage_c) {
+    constexpr int cur = decltype(stage_c)::value;
     // the last iterations refetch the last block into stages nobody reads again: every iteration
     // issues the same loads, so the wait below counts the same for all of them
-    issue(min(b + 2, nblk - 1), (b + 2) % AT_STAGES);
+    issue(min(b + 2, nblk - 1), (cur + 2) % AT_STAGES);
     const uint8_t* st = smem + cur * AT_STAGE;
 
     // scores
@@ -228,13 +230,12 @@ __global__ __launch_bounds__(64 * AT_WAVES, 2) void attn_mx_kernel(
       vsc[dt] = st[AT_KC + AT_VC + AT_KS + 2 * row + h];
     }
 
-    // s = c * acc (rounded: the maximal key's p must be exactly 2^0 = 1, as the definition has
-    // it; p slightly below 1 would move its group's scale down a power of two), keys past S
-    // masked; the per-tile maxima of s give each 32-key group's largest p directly
-#pragma unroll
-    for (int t = 0; t < 2; ++t)
-#pragma unroll
-      for (int e = 0; e < 16; ++e) sc[t][e] *= cexp;
+    // Keys past S are masked.  The running reference m' is c * max(acc) rounded toward -inf
+    // (from the exact residual of the product), and p = 2^(c * acc - m') is evaluated with one
+    // fused multiply-add: the maximal key's exponent is then >= 0 and tiny, its p rounds to 1
+    // (or 1 + 2^-23) and quantizes to exactly 1 as in the definition, while a p slightly below
+    // 1 would move its group's scale down a power of two.  The per-tile maxima of acc give each
+    // 32-key group's largest p by the same expression.
     if ((b + 1) * AT_KVB > S) {
 #pragma unroll
       for (int t = 0; t < 2; ++t)
@@ -250,7 +251,12 @@ __global__ __launch_bounds__(64 * AT_WAVES, 2) void attn_mx_kernel(
       for (int e = 1; e < 16; ++e) x = fmaxf(x, sc[t][e]);
       mt[t] = fmaxf(x, xor32f(x));
     }
-    const float mn = fmaxf(m, fmaxf(mt[0], mt[1]));  // finite: every block holds a key < S
+    const float amx = fmaxf(mt[0], mt[1]);  // finite: every block holds a key < S
+    float mb = amx * cexp;
+    if (__builtin_fmaf(amx, cexp, -mb) < 0.0f)  // mb was rounded up: step one ulp toward -inf
+      mb = mb > 0.0f ? __uint_as_float(__float_as_uint(mb) - 1u)
+                     : (mb < 0.0f ? __uint_as_float(__float_as_uint(mb) + 1u) : -__FLT_DENORM_MIN__);
+    const float mn = fmaxf(m, mb);
     const float alpha = __builtin_amdgcn_exp2f(m - mn);
     m = mn;
     float ps = 0.0f;
@@ -258,7 +264,9 @@ __global__ __launch_bounds__(64 * AT_WAVES, 2) void attn_mx_kernel(
     for (int t = 0; t < 2; ++t)
 #pragma unroll
       for (int e = 0; e < 16; ++e) {
-        const float p = __builtin_amdgcn_exp2f(sc[t][e] - mn);
+        // p <= 1 as in the definition (the maximal key's 2^(tiny >= 0) becomes exactly 1); the
+        // clamp to [0, 1] is the exponential's output clamp modifier
+        const float p = __builtin_amdgcn_fmed3f(__builtin_amdgcn_exp2f(__builtin_fmaf(sc[t][e], cexp, -mn)), 0.0f, 1.0f);
         sc[t][e] = p;
         ps += p;
       }
@@ -270,7 +278,8 @@ __global__ __launch_bounds__(64 * AT_WAVES, 2) void attn_mx_kernel(
     uint32_t psb[2];
 #pragma unroll
     for (int t = 0; t < 2; ++t) {
-      const float gmax = __builtin_amdgcn_exp2f(mt[t] - mn);  // = max of the group's p
+      const float gmax =  // = max of the group's p
+          __builtin_amdgcn_fmed3f(__builtin_amdgcn_exp2f(__builtin_fmaf(mt[t], cexp, -mn)), 0.0f, 1.0f);
       uint32_t dw[4];
       quant_p8(sc[t], gmax, dw, psb[t]);
       const uint32_t r0 = xor32(h ? dw[0] : dw[2]);
@@ -294,7 +303,13 @@ __global__ __launch_bounds__(64 * AT_WAVES, 2) void attn_mx_kernel(
 
     wait_block();  // block b + 1 is in this wave's part of the ring
     at_barrier();
+  };
+  for (int b = 0; b < nblk; b += AT_STAGES) {
+    step(b, std::integral_constant<int, 0>{});
+    if (b + 1 < nblk) step(b + 1, std::integral_constant<int, 1>{});
+    if (b + 2 < nblk) step(b + 2, std::integral_constant<int, 2>{});
   }
+  static_assert(AT_STAGES == 3, "the block loop is unrolled by the ring depth");
   wait_vmem_all();  // the refetches of the last iterations land before the workgroup ends
 
   l += xor32f(l);
