@@ -268,3 +268,37 @@ def test_binding_fails_loudly_without_native_library(mx, monkeypatch, tmp_path):
     monkeypatch.setattr(mx, "LIB_PATH", str(tmp_path / "missing.so"))
     with pytest.raises(mx.MxError):
         mx.lib()
+
+
+def test_attention_binding_checks_arguments_before_any_call(mx):
+    """The binding's shape and format checks run on the host, before the library is called."""
+    import torch
+    D = mx.ATTN_HEAD_DIM
+
+    def qm(rows, cols, fmt=None, layout=None):
+        fmt = mx.MXFP4 if fmt is None else fmt
+        return mx.QMatrix(torch.zeros((rows, cols // 2), dtype=torch.uint8),
+                          torch.zeros((rows, cols // 32), dtype=torch.uint8), fmt, rows, cols, 1.0,
+                          mx.ROW_MAJOR if layout is None else layout)
+
+    def vt(heads, S):
+        nb = (S + 63) // 64
+        return (torch.zeros((heads, nb, D, 64), dtype=torch.uint8), torch.zeros((heads, nb, D, 2), dtype=torch.uint8))
+
+    q = qm(2 * 100, D)
+    with pytest.raises(mx.MxError):
+        mx.attention(qm(200, D, fmt=mx.MXFP8), q, vt(2, 100), 2)          # Q must be MXFP4
+    with pytest.raises(mx.MxError):
+        mx.attention(q, qm(200, D, layout=mx.TILED), vt(2, 100), 2)       # row-major only
+    with pytest.raises(mx.MxError):
+        mx.attention(q, qm(202, D), vt(2, 100), 2)                        # q and k shapes differ
+    with pytest.raises(mx.MxError):
+        mx.attention(qm(200, 2 * D), qm(200, 2 * D), vt(2, 100), 2)       # bhsd needs 128 columns
+    with pytest.raises(mx.MxError):
+        mx.attention(q, q, vt(2, 164), 2)                                 # V^T of another length
+    with pytest.raises(mx.MxError):
+        mx.attention(qm(100, 3 * D), qm(100, 3 * D), vt(3, 100), 2, layout="shd")  # heads * 128 columns
+    with pytest.raises(mx.MxError):
+        mx.attention(q, q, vt(2, 100), 2, layout="sbhd")                  # unknown layout
+    with pytest.raises(mx.MxError):
+        mx.quantize_vt(torch.zeros((2, 100, D), dtype=torch.bfloat16))    # a host tensor
