@@ -92,7 +92,8 @@ hipError_t launch_quant_vt(const uint16_t* v, int64_t BH, int64_t S, int64_t D, 
 //  - PV: first operand V^T (32 head-dim rows), second the quantized probabilities (32 queries),
 //    K dimension the 64 keys of the block (scale block b = keys 32 b..32 b + 31).  The FP8 operand
 //    lane of half h must hold keys 16 h..16 h + 15 of each scale block: each lane has four runs
-//    of 4 keys per tile (one dword of codes each) and trades two of them with lane ^ 32;
+//    of 4 keys per tile (one dword of codes each) and trades two of them with lane ^ 32
+//    (V_PERMLANE32_SWAP);
 //  - the output tile has the scores' layout with head-dim rows in place of keys.
 //
 // A workgroup of 4 waves takes 128 queries of one head and walks the keys in blocks of 64
@@ -273,7 +274,9 @@ __global__ __launch_bounds__(64 * AT_WAVES, 2) void attn_mx_kernel(
     l = l * alpha + ps;
 
     // Q_MX8 of the probabilities, then the PV operand: half 0 takes keys 0..15 of each tile,
-    // half 1 keys 16..31
+    // half 1 keys 16..31.  Dword j of a lane holds keys 8j + 4h..8j + 4h + 3; V_PERMLANE32_SWAP
+    // trades the upper half's dword 0 (1) for the lower half's dword 2 (3), which leaves both
+    // halves with their 16 keys in order as dwords 0, 2, 1, 3.
     v8i pf;
     uint32_t psb[2];
 #pragma unroll
@@ -282,12 +285,12 @@ __global__ __launch_bounds__(64 * AT_WAVES, 2) void attn_mx_kernel(
           __builtin_amdgcn_fmed3f(__builtin_amdgcn_exp2f(__builtin_fmaf(mt[t], cexp, -mn)), 0.0f, 1.0f);
       uint32_t dw[4];
       quant_p8(sc[t], gmax, dw, psb[t]);
-      const uint32_t r0 = xor32(h ? dw[0] : dw[2]);
-      const uint32_t r1 = xor32(h ? dw[1] : dw[3]);
-      pf[4 * t + 0] = (int)(h ? r0 : dw[0]);
-      pf[4 * t + 1] = (int)(h ? dw[2] : r0);
-      pf[4 * t + 2] = (int)(h ? r1 : dw[1]);
-      pf[4 * t + 3] = (int)(h ? dw[3] : r1);
+      const auto s02 = __builtin_amdgcn_permlane32_swap(dw[0], dw[2], false, false);
+      const auto s13 = __builtin_amdgcn_permlane32_swap(dw[1], dw[3], false, false);
+      pf[4 * t + 0] = (int)s02[0];
+      pf[4 * t + 1] = (int)s02[1];
+      pf[4 * t + 2] = (int)s13[0];
+      pf[4 * t + 3] = (int)s13[1];
     }
     const int psc = (int)(h ? psb[1] : psb[0]);
 
