@@ -23,11 +23,18 @@ constexpr int AT_WAVES = 4;  // waves per workgroup, 32 queries each
 
 typedef short s16x2a __attribute__((ext_vector_type(2)));
 
-// value of lane ^ 32 (the other half of the wave)
-__device__ __forceinline__ uint32_t xor32(uint32_t v) {
-  return (uint32_t)__builtin_amdgcn_ds_bpermute((lane_id() ^ 32) << 2, (int)v);
+// Combine a value with the one in lane ^ 32 (the other half of the wave): V_PERMLANE32_SWAP of a
+// register with itself leaves one copy holding the lower half's values in every lane and the
+// other the upper half's, in some order per lane; max and + are commutative, so every lane gets
+// the same result.
+__device__ __forceinline__ float halves_max(float v) {
+  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+  return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
 }
-__device__ __forceinline__ float xor32f(float v) { return __uint_as_float(xor32(__float_as_uint(v))); }
+__device__ __forceinline__ float halves_sum(float v) {
+  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+  return __uint_as_float(r[0]) + __uint_as_float(r[1]);
+}
 
 // ---------------------------------------------------------------------------------------------
 // V^T MXFP8 quantizer
@@ -250,7 +257,7 @@ __global__ __launch_bounds__(64 * AT_WAVES, 2) void attn_mx_kernel(
       float x = sc[t][0];
 #pragma unroll
       for (int e = 1; e < 16; ++e) x = fmaxf(x, sc[t][e]);
-      mt[t] = fmaxf(x, xor32f(x));
+      mt[t] = halves_max(x);
     }
     const float amx = fmaxf(mt[0], mt[1]);  // finite: every block holds a key < S
     float mb = amx * cexp;
@@ -315,7 +322,7 @@ __global__ __launch_bounds__(64 * AT_WAVES, 2) void attn_mx_kernel(
   static_assert(AT_STAGES == 3, "the block loop is unrolled by the ring depth");
   wait_vmem_all();  // the refetches of the last iterations land before the workgroup ends
 
-  l += xor32f(l);
+  l = halves_sum(l);
   const float inv = 1.0f / l;
   if (q >= S) return;
   if (OUTF32) {
