@@ -203,6 +203,10 @@ WORKLOADS = {
     "wan_a14b_attn_mx_75600x40x128": Workload(
         "wan_a14b_attn_mx_75600x40x128", 6, 75600, 5120, 5120, "attn",
         outlier_frac=0.02, outlier_factor=3.0, extra={"heads": 40}),
+    # Wan2.2-TI2V-5B self-attention: 4290 tokens, 24 heads of 128 (N unused)
+    "wan_ti2v5b_attn_mx_4290x24x128": Workload(
+        "wan_ti2v5b_attn_mx_4290x24x128", 7, 4290, 3072, 3072, "attn",
+        outlier_frac=0.02, outlier_factor=3.0, extra={"heads": 24}),
     # NVFP4 at the A14B FFN shape with a static activation global scale (amax 40)
     "wan_a14b_nvfp4_75600x5120x13824": Workload(
         "wan_a14b_nvfp4_75600x5120x13824", 5, 75600, 5120, 13824, "nvfp4",

@@ -169,12 +169,13 @@ def test_attention_bf16_out_and_shd_layout(mx):
     _compare(got, ref, bnd, ab, S, "attention shd bf16", extra=2.0 ** -8 * np.abs(ref))
 
 
-def test_full_size_wan_a14b_attention(mx):
-    """75600 tokens x 40 heads of 128 in the projections' layout with BF16 out, as the benchmark
-    runs it; sampled queries of three heads (including the last, partial query block, whose
-    last key block holds 16 keys) against the oracle, and the V^T codes of those heads bit for
-    bit."""
-    wl = synth.WORKLOADS["wan_a14b_attn_mx_75600x40x128"]
+@pytest.mark.parametrize("name", ["wan_a14b_attn_mx_75600x40x128", "wan_ti2v5b_attn_mx_4290x24x128"])
+def test_full_size_wan_attention(mx, name):
+    """Full Wan2.2 self-attention shapes (A14B at 720p: 75600 tokens x 40 heads, as the benchmark
+    runs it; TI2V-5B: 4290 tokens x 24 heads), in the projections' layout with BF16 out: sampled
+    queries of three heads (including the last, partial query block; the last key block holds
+    16 / 2 keys) against the oracle, and the V^T codes of those heads bit for bit."""
+    wl = synth.WORKLOADS[name]
     S, H = wl.M, wl.extra["heads"]
     q, k, v = wl.qkv()
     bits = [synth.bits16(synth.to_bf16(x)) for x in (q, k, v)]
@@ -185,7 +186,7 @@ def test_full_size_wan_a14b_attention(mx):
     o = mx.attention(qg, kg, vt, heads=H, layout="shd")
     torch.cuda.synchronize()
     rows = np.unique(np.concatenate([sample_rows(S, 24), [0, S - 80, S - 1]]))
-    for h in (0, 17, H - 1):
+    for h in (0, H // 2 - 3, H - 1):
         hb = [np.ascontiguousarray(b[:, h * D:(h + 1) * D]) for b in bits]
         qc, qs, kc, ks, vtc, vts = _oracle_operands(hb[0], hb[1], hb[2], 1, S)
         bc, bs = _blocked(vtc, vts)
