@@ -99,10 +99,25 @@ def cpu_baseline_mx(wl, a_bits, w_codes, w_scales, b_bits, rows: int):
     dt = time.perf_counter() - t0
     flops = 2.0 * rows * wl.K * wl.N
     threads = int(os.environ.get("OMP_NUM_THREADS", os.cpu_count() or 1))
-    return {"value": flops / dt / 1e12, "unit": "TFLOP/s", "cores": threads, "kind": "oracle",
-            "sample": f"{rows} rows (first and last {rows // 2}) of the {wl.M}x{wl.K}x{wl.N} linear: "
-                      f"oracle MXFP4 quantization + dequantization + fp64 GEMM, {dt:.2f} s; "
-                      f"CPU: {cpu_info()}"}
+    res = {"value": flops / dt / 1e12, "unit": "TFLOP/s", "cores": threads, "kind": "oracle",
+           "sample": f"{rows} rows (first and last {rows // 2}) of the {wl.M}x{wl.K}x{wl.N} linear: "
+                     f"oracle MXFP4 quantization + dequantization + fp64 GEMM, {dt:.2f} s; "
+                     f"CPU: {cpu_info()}"}
+    # the same on one thread (OpenMP of the oracle and the BLAS under numpy), on 1024 rows
+    try:
+        from threadpoolctl import threadpool_limits
+        r1 = min(rows, 1024)
+        s1 = np.ascontiguousarray(sample[np.r_[0:r1 // 2, rows - r1 // 2:rows]])
+        with threadpool_limits(limits=1):
+            t0 = time.perf_counter()
+            ac, as_ = O.quantize_mx_bf16(s1, O.E2M1)
+            O.gemm(O.dequantize_mx(ac, as_, wl.K, O.E2M1), wdeq, bias)
+            d1 = time.perf_counter() - t0
+        res["single_thread"] = {"value": 2.0 * r1 * wl.K * wl.N / d1 / 1e12, "unit": "TFLOP/s",
+                                "rows": r1, "seconds": d1}
+    except ImportError:
+        pass
+    return res
 
 
 def bench_mx_linear(args, torch, mx, synth):
