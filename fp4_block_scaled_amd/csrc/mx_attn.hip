@@ -23,10 +23,10 @@ constexpr int AT_WAVES = 4;  // waves per workgroup, 32 queries each
 
 typedef short s16x2a __attribute__((ext_vector_type(2)));
 
-// Combine a value with the one in lane ^ 32 (the other half of the wave): V_PERMLANE32_SWAP of a
-// register with itself leaves one copy holding the lower half's values in every lane and the
-// other the upper half's, in some order per lane; max and + are commutative, so every lane gets
-// the same result.
+// Combine a value with the one in lane ^ 32 (the other half of the wave).  V_PERMLANE32_SWAP
+// exchanges the upper 32 lanes of its first register with the lower 32 lanes of its second; of a
+// register with itself, the first result then holds the lower half's value in every lane and the
+// second the upper half's, so both halves compute the same max or sum of the same two operands.
 __device__ __forceinline__ float halves_max(float v) {
   const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v), false, false);
   return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
@@ -240,10 +240,10 @@ __global__ __launch_bounds__(64 * AT_WAVES, 2) void attn_mx_kernel(
 
     // Keys past S are masked.  The running reference m' is c * max(acc) rounded toward -inf
     // (from the exact residual of the product), and p = 2^(c * acc - m') is evaluated with one
-    // fused multiply-add: the maximal key's exponent is then >= 0 and tiny, its p rounds to 1
-    // (or 1 + 2^-23) and quantizes to exactly 1 as in the definition, while a p slightly below
-    // 1 would move its group's scale down a power of two.  The per-tile maxima of acc give each
-    // 32-key group's largest p by the same expression.
+    // fused multiply-add and clamped to [0, 1]: the maximal key's exponent is >= 0 and tiny, so
+    // its p is exactly 1 as in the definition (a p slightly below 1 would move its group's scale
+    // down a power of two).  The per-tile maxima of acc give each 32-key group's largest p by
+    // the same expression.
     if ((b + 1) * AT_KVB > S) {
 #pragma unroll
       for (int t = 0; t < 2; ++t)
@@ -272,8 +272,7 @@ __global__ __launch_bounds__(64 * AT_WAVES, 2) void attn_mx_kernel(
     for (int t = 0; t < 2; ++t)
 #pragma unroll
       for (int e = 0; e < 16; ++e) {
-        // p <= 1 as in the definition (the maximal key's 2^(tiny >= 0) becomes exactly 1); the
-        // clamp to [0, 1] is the exponential's output clamp modifier
+        // the clamp to [0, 1] is the exponential's output clamp modifier
         const float p = __builtin_amdgcn_fmed3f(__builtin_amdgcn_exp2f(__builtin_fmaf(sc[t][e], cexp, -mn)), 0.0f, 1.0f);
         sc[t][e] = p;
         ps += p;
