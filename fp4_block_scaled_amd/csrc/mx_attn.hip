@@ -27,9 +27,16 @@ typedef short s16x2a __attribute__((ext_vector_type(2)));
 // exchanges the upper 32 lanes of its first register with the lower 32 lanes of its second; of a
 // register with itself, the first result then holds the lower half's value in every lane and the
 // second the upper half's, so both halves compute the same max or sum of the same two operands.
+// max of three floats without the NaN-quieting moves the compiler adds before a library max in
+// IEEE mode (the values here are finite scores or -inf, never NaN)
+__device__ __forceinline__ float max3_raw(float a, float b, float c) {
+  float r;
+  asm("v_max3_f32 %0, %1, %2, %3" : "=v"(r) : "v"(a), "v"(b), "v"(c));
+  return r;
+}
 __device__ __forceinline__ float halves_max(float v) {
   const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v), false, false);
-  return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
+  return max3_raw(__uint_as_float(r[0]), __uint_as_float(r[1]), __uint_as_float(r[1]));
 }
 __device__ __forceinline__ float halves_sum(float v) {
   const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v), false, false);
@@ -130,10 +137,14 @@ __device__ __forceinline__ void quant_p8(const v16f& p, float amax, uint32_t (&d
   if (e < -127) e = -127;
   const float scale = __uint_as_float(e >= -126 ? (uint32_t)(127 + e) << 23 : 0x00400000u);
   const float lim = __uint_as_float((uint32_t)(e + 135) << 23 | 0x600000u);  // 448 * 2^e
+  // both 16-bit halves of each result are written, so the first conversion's pass-through
+  // operand (tied to its destination) is the first clamped input, which dies there: no zeroing
 #pragma unroll
   for (int j = 0; j < 4; ++j) {
-    s16x2a r = __builtin_amdgcn_cvt_scalef32_pk_fp8_f32(s16x2a{0, 0}, fminf(p[4 * j], lim),
-                                                        fminf(p[4 * j + 1], lim), scale, false);
+    const float a0 = fminf(p[4 * j], lim);
+    s16x2a init;
+    __builtin_memcpy(&init, &a0, 4);
+    s16x2a r = __builtin_amdgcn_cvt_scalef32_pk_fp8_f32(init, a0, fminf(p[4 * j + 1], lim), scale, false);
     r = __builtin_amdgcn_cvt_scalef32_pk_fp8_f32(r, fminf(p[4 * j + 2], lim), fminf(p[4 * j + 3], lim),
                                                  scale, true);
     __builtin_memcpy(&d[j], &r, 4);
@@ -238,12 +249,12 @@ __global__ __launch_bounds__(64 * AT_WAVES, 2) void attn_mx_kernel(
       vsc[dt] = st[AT_KC + AT_VC + AT_KS + 2 * row + h];
     }
 
-    // Keys past S are masked.  The running reference m' is c * max(acc) rounded toward -inf
-    // (from the exact residual of the product), and p = 2^(c * acc - m') is evaluated with one
-    // fused multiply-add and clamped to [0, 1]: the maximal key's exponent is >= 0 and tiny, so
-    // its p is exactly 1 as in the definition (a p slightly below 1 would move its group's scale
-    // down a power of two).  The per-tile maxima of acc give each 32-key group's largest p by
-    // the same expression.
+    // Keys past S are masked.  The running reference m' sits just below c * max(acc), and
+    // p = 2^(c * acc - m') is evaluated with one fused multiply-add and clamped to [0, 1]: the
+    // maximal key's exponent is >= 0 and tiny, so its p is exactly 1 as in the definition (a p
+    // slightly below 1 would move its group's scale down a power of two).  Every p of a row
+    // carries the same factor 2^(c * max - m'), which cancels in o / l.  The per-tile maxima of
+    // acc give each 32-key group's largest p by the same expression.
     if ((b + 1) * AT_KVB > S) {
 #pragma unroll
       for (int t = 0; t < 2; ++t)
@@ -254,16 +265,17 @@ __global__ __launch_bounds__(64 * AT_WAVES, 2) void attn_mx_kernel(
     float mt[2];
 #pragma unroll
     for (int t = 0; t < 2; ++t) {
-      float x = sc[t][0];
+      float x = max3_raw(sc[t][0], sc[t][1], sc[t][2]);
 #pragma unroll
-      for (int e = 1; e < 16; ++e) x = fmaxf(x, sc[t][e]);
-      mt[t] = halves_max(x);
+      for (int e = 3; e < 15; e += 2) x = max3_raw(x, sc[t][e], sc[t][e + 1]);
+      mt[t] = halves_max(max3_raw(x, sc[t][15], sc[t][15]));
     }
-    const float amx = fmaxf(mt[0], mt[1]);  // finite: every block holds a key < S
-    float mb = amx * cexp;
-    if (__builtin_fmaf(amx, cexp, -mb) < 0.0f)  // mb was rounded up: step one ulp toward -inf
-      mb = mb > 0.0f ? __uint_as_float(__float_as_uint(mb) - 1u)
-                     : (mb < 0.0f ? __uint_as_float(__float_as_uint(mb) + 1u) : -__FLT_DENORM_MIN__);
+    const float amx = max3_raw(mt[0], mt[1], mt[1]);  // finite: every block holds a key < S
+    // mb = fp32(c * amx) lowered by |mb| 2^-23 (at least one ulp): strictly below the exact
+    // c * amx for any normal mb, so the maximal key's exponent is >= 0 (a subnormal mb means
+    // |c * amx| < 2^-126, where 2^exponent rounds to 1 anyway)
+    const float mb0 = amx * cexp;
+    const float mb = __builtin_fmaf(-__builtin_fabsf(mb0), 0x1p-23f, mb0);
     const float mn = fmaxf(m, mb);
     const float alpha = __builtin_amdgcn_exp2f(m - mn);
     m = mn;
