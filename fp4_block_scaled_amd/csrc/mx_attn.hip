@@ -276,10 +276,10 @@ __global__ __launch_bounds__(64 * AT_WAVES, 2) void attn_mx_kernel(
     // |c * amx| < 2^-126, where 2^exponent rounds to 1 anyway)
     const float mb0 = amx * cexp;
     const float mb = __builtin_fmaf(-__builtin_fabsf(mb0), 0x1p-23f, mb0);
-    const float mn = fmaxf(m, mb);
+    const float mn = max3_raw(m, mb, mb);
     const float alpha = __builtin_amdgcn_exp2f(m - mn);
     m = mn;
-    float ps = 0.0f;
+    float ps;
 #pragma unroll
     for (int t = 0; t < 2; ++t)
 #pragma unroll
@@ -287,7 +287,7 @@ __global__ __launch_bounds__(64 * AT_WAVES, 2) void attn_mx_kernel(
         // the clamp to [0, 1] is the exponential's output clamp modifier
         const float p = __builtin_amdgcn_fmed3f(__builtin_amdgcn_exp2f(__builtin_fmaf(sc[t][e], cexp, -mn)), 0.0f, 1.0f);
         sc[t][e] = p;
-        ps += p;
+        ps = (t == 0 && e == 0) ? p : ps + p;
       }
     l = l * alpha + ps;
 
