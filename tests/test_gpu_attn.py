@@ -194,3 +194,30 @@ def test_full_size_wan_attention(mx, name):
         ref, bnd, ab = O.attention_mx(qc, qs, kc, ks, vtc, vts, 1, S, D, KVB, D ** -0.5, qrows=rows)
         got = O.bf16_values(dev_bits16(o[torch.from_numpy(rows).cuda(), h * D:(h + 1) * D]))
         _compare(got, ref, bnd, ab, S, f"full-size head {h}", extra=2.0 ** -8 * np.abs(ref), flip_frac=0.05)
+
+
+def test_head_and_row_strides_through_the_c_abi(mx):
+    """Heads spaced apart in memory (a head stride beyond S rows) for Q/K and the output, called
+    through the C ABI directly: bit-identical to the dense call."""
+    import ctypes
+    BH, S, pad = 3, 150, 26
+    q_bits = _bits(35000, (BH, S, D), 1.0)
+    k_bits = _bits(35001, (BH, S, D), 1.0)
+    v_bits = _bits(35002, (BH, S, D), 1.0)
+    dense = mx.attention(mx.quantize(to_dev_bf16(q_bits.reshape(BH * S, D)), "mxfp4"),
+                         mx.quantize(to_dev_bf16(k_bits.reshape(BH * S, D)), "mxfp4"),
+                         mx.quantize_vt(to_dev_bf16(v_bits)), BH, out_dtype=torch.float32)
+    padded = lambda b: np.concatenate([b, np.zeros((BH, pad, D), np.uint16)], axis=1).reshape(BH * (S + pad), D)
+    qp = mx.quantize(to_dev_bf16(padded(q_bits)), "mxfp4")
+    kp = mx.quantize(to_dev_bf16(padded(k_bits)), "mxfp4")
+    vt = mx.quantize_vt(to_dev_bf16(v_bits))
+    out = torch.full((BH, S + pad, D), float("nan"), dtype=torch.float32, device="cuda")
+    hs = (S + pad) * D
+    st = mx.lib().mx_attention(qp.codes.data_ptr(), qp.scales.data_ptr(), kp.codes.data_ptr(),
+                               kp.scales.data_ptr(), D, hs, vt[0].data_ptr(), vt[1].data_ptr(), BH, S, D,
+                               ctypes.c_float(D ** -0.5), 1, out.data_ptr(), D, hs,
+                               ctypes.c_void_p(torch.cuda.current_stream().cuda_stream))
+    torch.cuda.synchronize()
+    assert st == 0
+    assert torch.equal(out[:, :S], dense)
+    assert torch.isnan(out[:, S:]).all()  # rows past S untouched
