@@ -184,15 +184,19 @@ __global__ __launch_bounds__(64 * AT_WAVES, 2) void attn_mx_kernel(
   const int vrow0 = 32 * wave + (lane >> 2), vrow1 = vrow0 + 16;
   const uint32_t voff0 = (uint32_t)(vrow0 * 64 + 16 * ((lane & 3) ^ ((vrow0 >> 2) & 3)));
   const uint32_t voff1 = (uint32_t)(vrow1 * 64 + 16 * ((lane & 3) ^ ((vrow1 >> 2) & 3)));
+  // K byte offsets: row min(64 b + krow, S - 1) (rows past S are fetched but masked) as a
+  // block offset plus loop-invariant per-lane parts, all below 2^32 (checked by the caller)
+  const uint32_t koff = (uint32_t)(krow * crow + 16 * kpiece), kmax = (uint32_t)((S - 1) * crow + 16 * kpiece);
+  const uint32_t ksoff = (uint32_t)(lane * srow), ksmax = (uint32_t)((S - 1) * srow);
   auto issue = [&](int b, int stage) {
     const uint32_t sb = lds0 + (uint32_t)(stage * AT_STAGE);
-    const int key = min(b * AT_KVB + krow, S - 1);  // rows past S are fetched but masked
-    dma_lds16(rk, sb + (uint32_t)(wave * 1024), (uint32_t)(key * crow + 16 * kpiece), 0u);
+    const uint32_t kblk = (uint32_t)b * (uint32_t)(AT_KVB * crow);
+    dma_lds16(rk, sb + (uint32_t)(wave * 1024), min(kblk + koff, kmax), 0u);
     dma_lds16(rv, sb + (uint32_t)(AT_KC + wave * 2048), voff0, (uint32_t)(b * AT_VC));
     dma_lds16(rv, sb + (uint32_t)(AT_KC + wave * 2048 + 1024), voff1, (uint32_t)(b * AT_VC));
     if (wave == 0) {
-      const int key2 = min(b * AT_KVB + lane, S - 1);
-      dma_lds4(rks, sb + (uint32_t)(AT_KC + AT_VC), (uint32_t)(key2 * srow), 0u);
+      const uint32_t sblk = (uint32_t)b * (uint32_t)(AT_KVB * srow);
+      dma_lds4(rks, sb + (uint32_t)(AT_KC + AT_VC), min(sblk + ksoff, ksmax), 0u);
     } else if (wave == 1) {
       dma_lds4(rvs, sb + (uint32_t)(AT_KC + AT_VC + AT_KS), (uint32_t)(4 * lane), (uint32_t)(b * AT_VS));
     }
