@@ -119,6 +119,9 @@ def test_quantize_vt_strided_view_and_extremes(mx):
     (1, 129, 3.0, D ** -0.5),   # sharp softmax (scores spread over ~100 in log2 units)
     (2, 384, 1.5, 0.2),
     (1, 1000, 1.0, D ** -0.5),  # 16 key blocks
+    (1, 63, 1.0, D ** -0.5),    # one key short of a block
+    (1, 65, 1.0, D ** -0.5),    # one key past a block
+    (2, 128, 2.0, D ** -0.5),   # exactly one query block per head
 ])
 def test_attention_vs_oracle(mx, BH, S, sigma, scale):
     q_bits = _bits(32000 + S, (BH * S, D), sigma)
