@@ -84,6 +84,30 @@ def time_events(fn, iters: int, torch, warmup: int = 3):
     return start.elapsed_time(end) / iters
 
 
+MAX_SCLK_MHZ = 2400.0  # the clock the published peaks assume
+
+
+def sample_sclk(fn, launches: int, torch):
+    """Shader clock (MHz) that rocm-smi reports while `launches` calls of fn run back to back (the
+    calls are queued first, the clock is read while they execute); None if it cannot be read."""
+    import re
+    import shutil
+    import subprocess
+    if not shutil.which("rocm-smi"):
+        return None
+    torch.cuda.synchronize()
+    for _ in range(launches):
+        fn()
+    time.sleep(0.5)
+    try:
+        r = subprocess.run(["rocm-smi", "--showclocks"], capture_output=True, text=True, timeout=20)
+        m = re.search(r"sclk clock level: \d+: \((\d+)Mhz\)", r.stdout)
+    except (OSError, subprocess.SubprocessError):
+        m = None
+    torch.cuda.synchronize()
+    return float(m.group(1)) if m else None
+
+
 def cpu_baseline_mx(wl, a_bits, w_codes, w_scales, b_bits, rows: int):
     """The oracle (as it stands) on a sample of rows: quantize + dequantize + fp64 GEMM."""
     import numpy as np
@@ -152,6 +176,9 @@ def bench_mx_linear(args, torch, mx, synth):
     ms_quant = time_events(quant, args.steps, torch)
     ms_gemm = time_events(gemm, args.steps, torch)
 
+    # the shader clock during about 1.5 s of back-to-back GEMMs (the published peak assumes 2.4 GHz)
+    sclk = sample_sclk(gemm, max(100, int(1500.0 / ms_gemm)), torch)
+
     flops = 2.0 * M * N * K
     quant_bytes = M * K * 2 + M * K // 2 + M * K // 32
     gemm_bytes = M * K // 2 + M * K // 32 + N * K // 2 + N * K // 32 + M * N * 2 + (N * 2 if b is not None else 0)
@@ -177,7 +204,10 @@ def bench_mx_linear(args, torch, mx, synth):
                      "unit": "TFLOP/s", "frac": achieved / PEAK_TFLOPS["mxfp4"],
                      "traffic": traffic,
                      "kernel": "gemm_mx_ring_kernel<256,128> (MXFP4 x MXFP4, tiled operands, bias, BF16 out)",
-                     "algorithmic_flops_per_launch": flops, "ms_per_launch": ms_gemm},
+                     "algorithmic_flops_per_launch": flops, "ms_per_launch": ms_gemm,
+                     "sclk_mhz_sampled": sclk,
+                     "frac_at_sampled_clock": (achieved / (PEAK_TFLOPS["mxfp4"] * sclk / MAX_SCLK_MHZ)
+                                               if sclk else None)},
         "kernels": {
             "quantizer": {"ms": ms_quant, "GB/s": quant_bytes / (ms_quant * 1e-3) / 1e9,
                           "frac_hbm": quant_bytes / (ms_quant * 1e-3) / 1e9 / HBM_GBPS,
