@@ -70,7 +70,7 @@ def lib():
         L.mxr_absmax_bf16.restype = ctypes.c_double
         L.mxr_norm_modulate.argtypes = [_P, _I, _I, _I, ctypes.c_double, _P, _P, _P, _P, _P]
         L.mxr_norm_modulate.restype = None
-        L.mxr_attention_mx.argtypes = [_P, _P, _P, _P, _P, _P, _I, _I, _I, _I, ctypes.c_int,
+        L.mxr_attention_mx.argtypes = [_P, _P, _P, _P, _P, _P, _I, _I, _I, _I, _I, ctypes.c_int,
                                        ctypes.c_double, _P, _I, _P, _P, _P]
         L.mxr_attention_mx.restype = None
         _lib = L
@@ -305,19 +305,21 @@ def norm_modulate(x_bits, eps: float, gamma=None, beta=None, scale=None, shift=N
 
 # ---- microscaled attention -------------------------------------------------------------------
 def attention_mx(qc, qs, kc, ks, vtc, vts, BH: int, S: int, D: int, kvb: int, softmax_scale: float,
-                 qrows=None):
+                 qrows=None, S_kv=None):
     """(out, bound, absacc) [nq, D] in fp64 for the listed query rows (all rows if None); see
-    mxr_attention_mx.  q/k codes [BH*S, D/2] + scales [BH*S, D/32]; V^T codes [BH, D, Sp] E4M3 +
-    scales [BH, D, Sp/32], Sp = S rounded up to kvb."""
+    mxr_attention_mx.  q codes [BH*S, D/2] + scales [BH*S, D/32]; k codes [BH*S_kv, D/2] + scales;
+    V^T codes [BH, D, Sp] E4M3 + scales [BH, D, Sp/32], Sp = S_kv rounded up to kvb.  S_kv
+    defaults to S (self-attention)."""
     assert D <= 1024 and kvb <= 256 and kvb % 32 == 0
-    Sp = (S + kvb - 1) // kvb * kvb
+    Skv = S if S_kv is None else S_kv
+    Sp = (Skv + kvb - 1) // kvb * kvb
     arrs = [_c(a, np.uint8) for a in (qc, qs, kc, ks, vtc, vts)]
-    assert arrs[4][0].size == BH * D * Sp and arrs[5][0].size == BH * D * (Sp // 32)
+    assert arrs[2][0].size == BH * Skv * (D // 2) and arrs[4][0].size == BH * D * Sp and arrs[5][0].size == BH * D * (Sp // 32)
     rows = np.arange(BH * S, dtype=np.int64) if qrows is None else np.asarray(qrows, dtype=np.int64)
     rows, pr = _c(rows, np.int64)
     nq = rows.size
     out = np.empty((nq, D)); bnd = np.empty((nq, D)); ab = np.empty((nq, D))
-    lib().mxr_attention_mx(*[p for _, p in arrs], BH, S, D, Sp, kvb, float(softmax_scale), pr, nq,
+    lib().mxr_attention_mx(*[p for _, p in arrs], BH, S, Skv, D, Sp, kvb, float(softmax_scale), pr, nq,
                            out.ctypes.data, bnd.ctypes.data, ab.ctypes.data)
     return out, bnd, ab
 

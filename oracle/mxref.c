@@ -497,15 +497,18 @@ void mxr_norm_modulate(const uint16_t* x, int64_t rows, int64_t cols, int64_t ld
  *    masked; m' = max(m, max_j s_j); alpha = 2^(m - m'); p_j = 2^(s_j - m');
  *    l = alpha l + sum_j p_j; p^ = Q_MX8(p) in groups of 32 keys; o = alpha o + sum_j p^_j v^_j.
  *  - out = o / l.
- * fp64 throughout.  Only the query rows listed in qrows (indices into the BH*S rows) are
+ * fp64 throughout.  Queries and keys may come from sequences of different lengths: S query rows
+ * and Skv key / value rows per head (self-attention has Skv = S; the DiT's second attention
+ * layer, attn2 in the MXFP4 card's Quantization Details, takes its keys and values from the
+ * conditioning context).  Only the query rows listed in qrows (indices into the BH*S rows) are
  * computed.  bound accumulates like o with the worst case of |p^_j - p_j| between two
  * implementations whose p differ by rounding noise: 2^(floor(log2 p_j) - 2) (a rounding step of
  * p, or the block scale moving across a power of two) plus the subnormal quantum 2^(e - 9), times
  * |v^_jd|; absacc accumulates sum_j p^_j |v^_jd|.  Both are divided by l like o. */
 void mxr_attention_mx(const uint8_t* qc, const uint8_t* qs, const uint8_t* kc, const uint8_t* ks,
-                      const uint8_t* vc, const uint8_t* vs, int64_t BH, int64_t S, int64_t D,
-                      int64_t Sp, int kvb, double softmax_scale, const int64_t* qrows, int64_t nq,
-                      double* out, double* bound, double* absacc) {
+                      const uint8_t* vc, const uint8_t* vs, int64_t BH, int64_t S, int64_t Skv,
+                      int64_t D, int64_t Sp, int kvb, double softmax_scale, const int64_t* qrows,
+                      int64_t nq, double* out, double* bound, double* absacc) {
     (void)BH;
     const double c = softmax_scale / log(2.0);
 #pragma omp parallel for schedule(dynamic)
@@ -522,8 +525,8 @@ void mxr_attention_mx(const uint8_t* qc, const uint8_t* qs, const uint8_t* kc, c
             double mb = -INFINITY;
             for (int j = 0; j < kvb; ++j) {
                 const int64_t key = b0 + j;
-                if (key >= S) { s[j] = -INFINITY; continue; }
-                const int64_t krow = bh * S + key;
+                if (key >= Skv) { s[j] = -INFINITY; continue; }
+                const int64_t krow = bh * Skv + key;
                 double dot = 0.0;
                 for (int64_t d = 0; d < D; ++d)
                     dot += q[d] * mxr_e2m1_value((kc[krow * (D / 2) + d / 2] >> (4 * (d & 1))) & 15) *

@@ -602,3 +602,39 @@ def test_vt_quantizer_pads_and_round_trips():
     # the subnormal quantum 2^(e - 9) of its 32-key block
     e = np.repeat(vts.astype(np.float64) - 127, 32, axis=2)[:, :, :S].transpose(0, 2, 1)
     assert np.all(np.abs(vd - x) <= np.abs(x) / 8 + 2.0 ** (e - 10))
+
+
+def _cross_inputs(BH, Sq, Skv, D, kvb, seed):
+    q = synth.bits16(synth.to_bf16(synth.normal_f32(seed, (BH * Sq, D), 1.0)))
+    k = synth.bits16(synth.to_bf16(synth.normal_f32(seed + 1, (BH * Skv, D), 1.0)))
+    v = synth.bits16(synth.to_bf16(synth.normal_f32(seed + 2, (BH * Skv, D), 1.0)))
+    qc, qs = O.quantize_mx_bf16(q, O.E2M1)
+    kc, ks = O.quantize_mx_bf16(k, O.E2M1)
+    vtc, vts = O.quantize_vt_mx8(v, BH, Skv, D, kvb)
+    return qc, qs, kc, ks, vtc, vts
+
+
+def test_cross_attention_single_key_is_exact():
+    """Queries and keys of different lengths: with one key every query's output is that key's v^."""
+    BH, Sq, D, kvb = 2, 5, 128, 64
+    qc, qs, kc, ks, vtc, vts = _cross_inputs(BH, Sq, 1, D, kvb, 81)
+    out, _, _ = O.attention_mx(qc, qs, kc, ks, vtc, vts, BH, Sq, D, kvb, D ** -0.5, S_kv=1)
+    vhat = _vt_dequant(vtc, vts, BH, 1, D).reshape(BH, 1, D)
+    np.testing.assert_array_equal(out.reshape(BH, Sq, D), np.broadcast_to(vhat, (BH, Sq, D)))
+
+
+@pytest.mark.parametrize("Sq,Skv,kvb", [(40, 130, 64), (130, 40, 64), (7, 77, 32)])
+def test_cross_attention_matches_softmax_attention_within_p_quantization(Sq, Skv, kvb):
+    """As the self-attention pin, with Sq query rows and Skv key / value rows per head."""
+    BH, D = 2, 128
+    qc, qs, kc, ks, vtc, vts = _cross_inputs(BH, Sq, Skv, D, kvb, 90 + Sq + Skv)
+    out, bnd, ab = O.attention_mx(qc, qs, kc, ks, vtc, vts, BH, Sq, D, kvb, D ** -0.5, S_kv=Skv)
+    qd = O.dequantize_mx(qc, qs, D).reshape(BH, Sq, D)
+    kd = O.dequantize_mx(kc, ks, D).reshape(BH, Skv, D)
+    vd = _vt_dequant(vtc, vts, BH, Skv, D)
+    sc = torch.from_numpy(qd) @ torch.from_numpy(kd).transpose(1, 2) * D ** -0.5
+    p = torch.softmax(sc, dim=-1)
+    ref = (p @ torch.from_numpy(np.ascontiguousarray(vd))).numpy().reshape(BH * Sq, D)
+    tol = (p @ torch.from_numpy(np.abs(np.ascontiguousarray(vd)))).numpy().reshape(BH * Sq, D) / 8 + 1e-12
+    assert np.all(np.abs(out - ref) <= tol)
+    assert np.all(np.abs(out - ref) <= 4 * bnd + 1e-12)
