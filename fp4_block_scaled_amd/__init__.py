@@ -81,7 +81,8 @@ def lib():
         L.mx_norm.argtypes = [P, I64, I64, I64, F, P, P, P, P, P, I64, P]
         L.mx_norm_quantize.argtypes = [P, I64, I64, I64, F, P, P, P, P, I32, I32, P, P, P]
         L.mx_quantize_vt.argtypes = [P, I64, I64, I64, I64, I64, P, P, P]
-        L.mx_attention.argtypes = [P, P, P, P, I64, I64, P, P, I64, I64, I64, F, I32, P, I64, I64, P]
+        L.mx_attention.argtypes = [P, P, I64, I64, P, P, I64, I64, P, P, I64, I64, I64, I64, F, I32, P,
+                                   I64, I64, P]
         for f in ("mx_quantize", "mx_dequantize", "mx_absmax", "mx_linear", "mx_linear_q",
                   "mx_tiled_bytes", "mx_relayout", "mx_norm", "mx_norm_quantize",
                   "mx_quantize_vt", "mx_attention"):
@@ -265,38 +266,42 @@ def quantize_vt(v: torch.Tensor, out=None):
 def attention(q: QMatrix, k: QMatrix, vt, heads: int, softmax_scale: Optional[float] = None,
               layout: str = "bhsd", out_dtype=torch.bfloat16, out: Optional[torch.Tensor] = None):
     """Microscaled attention (head dimension 128): q and k are row-major MXFP4 QMatrix of the
-    queries and keys, vt = quantize_vt(v).  layout "bhsd": q/k rows are heads * S rows of 128
-    (head-major), out [heads, S, 128]; layout "shd": q/k are S x (heads * 128) (one batch of a
-    projection), out [S, heads * 128].  softmax_scale defaults to 1/sqrt(128)."""
+    queries (S_q per head) and keys (S_kv per head, which may differ: cross-attention), and
+    vt = quantize_vt(v) of the S_kv values.  layout "bhsd": q/k rows are heads * S rows of 128
+    (head-major), out [heads, S_q, 128]; layout "shd": q/k are S x (heads * 128) (one batch of a
+    projection), out [S_q, heads * 128].  softmax_scale defaults to 1/sqrt(128)."""
     for t, name in ((q, "q"), (k, "k")):
         if t.fmt != MXFP4 or t.layout != ROW_MAJOR:
             raise MxError(f"{name} must be a row-major MXFP4 QMatrix")
-    if (q.rows, q.cols) != (k.rows, k.cols):
-        raise MxError("q and k shapes differ")
+    if q.cols != k.cols:
+        raise MxError("q and k widths differ")
     D = ATTN_HEAD_DIM
     if layout == "bhsd":
-        if q.cols != D or q.rows % heads:
-            raise MxError("bhsd: q must be (heads * S) x 128")
-        S = q.rows // heads
-        ld, hs, shape = D, S * D, (heads, S, D)
+        if q.cols != D or q.rows % heads or k.rows % heads:
+            raise MxError("bhsd: q and k must be (heads * S) x 128")
+        Sq, Skv = q.rows // heads, k.rows // heads
+        ld_q, hs_q, ld_k, hs_k = D, Sq * D, D, Skv * D
+        shape = (heads, Sq, D)
     elif layout == "shd":
         if q.cols != heads * D:
-            raise MxError("shd: q must be S x (heads * 128)")
-        S = q.rows
-        ld, hs, shape = heads * D, D, (S, heads * D)
+            raise MxError("shd: q and k must be S x (heads * 128)")
+        Sq, Skv = q.rows, k.rows
+        ld_q = ld_k = heads * D
+        hs_q = hs_k = D
+        shape = (Sq, heads * D)
     else:
         raise MxError(f"unknown attention layout {layout!r}")
     vc, vs = vt
-    Sp = (S + ATTN_KVB - 1) // ATTN_KVB * ATTN_KVB
-    if tuple(vc.shape) != (heads, Sp // 64, D, 64) or tuple(vs.shape) != (heads, Sp // 64, D, 2):
-        raise MxError("vt does not match q's heads and sequence length")
+    nb = (Skv + ATTN_KVB - 1) // ATTN_KVB
+    if tuple(vc.shape) != (heads, nb, D, 64) or tuple(vs.shape) != (heads, nb, D, 2):
+        raise MxError("vt does not match k's heads and sequence length")
     o = out if out is not None else torch.empty(shape, dtype=out_dtype, device=q.codes.device)
     if tuple(o.shape) != shape or not o.is_contiguous() or o.dtype not in (torch.bfloat16, torch.float32):
         raise MxError(f"out must be a contiguous bfloat16 / float32 tensor of shape {shape}")
-    ld_o, hs_o = (D, S * D) if layout == "bhsd" else (heads * D, D)
+    ld_o, hs_o = (D, Sq * D) if layout == "bhsd" else (heads * D, D)
     scale = float(softmax_scale) if softmax_scale is not None else D ** -0.5
-    _check(lib().mx_attention(_ptr(q.codes), _ptr(q.scales), _ptr(k.codes), _ptr(k.scales), ld, hs,
-                              _ptr(vc), _ptr(vs), heads, S, D, scale,
+    _check(lib().mx_attention(_ptr(q.codes), _ptr(q.scales), ld_q, hs_q, _ptr(k.codes), _ptr(k.scales),
+                              ld_k, hs_k, _ptr(vc), _ptr(vs), heads, Sq, Skv, D, scale,
                               1 if o.dtype == torch.float32 else 0, _ptr(o), ld_o, hs_o, _stream()))
     return o
 

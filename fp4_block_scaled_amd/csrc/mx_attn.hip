@@ -6,8 +6,10 @@
 // they multiply V.  Both products run on V_MFMA_SCALE_F32_32X32X64_F8F6F4, so every MX scale is
 // applied by the matrix core.
 //
+// Queries and keys may come from sequences of different lengths (Sq query rows, Skv key / value
+// rows per head: self-attention, or the cross-attention of the DiT's second attention layer).
 // Per block of 64 keys, with c = softmax_scale * log2(e):
-//   s_j = c (q . k_j) (keys past S masked to -inf), m' = max(m, max_j s_j), alpha = 2^(m - m'),
+//   s_j = c (q . k_j) (keys past Skv masked to -inf), m' = max(m, max_j s_j), alpha = 2^(m - m'),
 //   p_j = 2^(s_j - m'), l = alpha l + sum_j p_j, o = alpha o + sum_j Q_MX8(p)_j v_j;
 // the output is o / l.  The running maximum is exact (no deferred rescaling), so the quantized
 // probabilities are the ones that definition gives; o is rescaled only when some query's maximum
@@ -156,26 +158,26 @@ template <bool OUTF32>
 __global__ __launch_bounds__(64 * AT_WAVES, 2) void attn_mx_kernel(
     const uint8_t* __restrict__ qc, const uint8_t* __restrict__ qs, const uint8_t* __restrict__ kc,
     const uint8_t* __restrict__ ks, const uint8_t* __restrict__ vc, const uint8_t* __restrict__ vs,
-    int S, int nblk, int64_t ld, int64_t hs, float cexp, void* __restrict__ out, int64_t ld_o,
-    int64_t hs_o) {
+    int Sq, int Skv, int nblk, int64_t ld_q, int64_t hs_q, int64_t ld_k, int64_t hs_k, float cexp,
+    void* __restrict__ out, int64_t ld_o, int64_t hs_o) {
   __shared__ __attribute__((aligned(16))) uint8_t smem[AT_STAGES * AT_STAGE];
   const int lane = lane_id(), r32 = lane & 31, h = lane >> 5;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int64_t bh = blockIdx.y;
   const int q = blockIdx.x * (32 * AT_WAVES) + wave * 32 + r32;
-  const int64_t crow = ld / 2, srow = ld / 32;  // bytes per row of codes / scales
+  const int64_t crow = ld_k / 2, srow = ld_k / 32;  // bytes per key row of codes / scales
 
-  const int qr = min(q, S - 1);
-  const uint8_t* qrow = qc + bh * (hs / 2) + qr * crow;
+  const int qr = min(q, Sq - 1);
+  const uint8_t* qrow = qc + bh * (hs_q / 2) + qr * (ld_q / 2);
   const v4i qf0 = *(const v4i*)(qrow + 32 * h);
   const v4i qf1 = *(const v4i*)(qrow + 32 * h + 16);
-  const uint32_t qsc = *(const uint32_t*)(qs + bh * (hs / 32) + qr * srow) >> (16 * h);
+  const uint32_t qsc = *(const uint32_t*)(qs + bh * (hs_q / 32) + qr * (ld_q / 32)) >> (16 * h);
   wait_vmem_all();  // from here on the only vector-memory loads in flight are the ring's
 
   // ring fill: per block, wave w loads K rows 16w..16w+15 and V^T rows 32w..32w+31 (1 KB per
   // instruction, lane i -> 16-byte slot i), wave 0 the K scales and wave 1 the V^T scales
-  const v4i rk = make_rsrc_sgpr(kc + bh * (hs / 2), (uint32_t)((S - 1) * crow + 64));
-  const v4i rks = make_rsrc_sgpr(ks + bh * (hs / 32), (uint32_t)((S - 1) * srow + 4));
+  const v4i rk = make_rsrc_sgpr(kc + bh * (hs_k / 2), (uint32_t)((Skv - 1) * crow + 64));
+  const v4i rks = make_rsrc_sgpr(ks + bh * (hs_k / 32), (uint32_t)((Skv - 1) * srow + 4));
   const v4i rv = make_rsrc_sgpr(vc + bh * (int64_t)nblk * AT_VC, (uint32_t)nblk * AT_VC);
   const v4i rvs = make_rsrc_sgpr(vs + bh * (int64_t)nblk * AT_VS, (uint32_t)nblk * AT_VS);
   const uint32_t lds0 = lds_addr_of(smem);
@@ -184,10 +186,10 @@ __global__ __launch_bounds__(64 * AT_WAVES, 2) void attn_mx_kernel(
   const int vrow0 = 32 * wave + (lane >> 2), vrow1 = vrow0 + 16;
   const uint32_t voff0 = (uint32_t)(vrow0 * 64 + 16 * ((lane & 3) ^ ((vrow0 >> 2) & 3)));
   const uint32_t voff1 = (uint32_t)(vrow1 * 64 + 16 * ((lane & 3) ^ ((vrow1 >> 2) & 3)));
-  // K byte offsets: row min(64 b + krow, S - 1) (rows past S are fetched but masked) as a
+  // K byte offsets: row min(64 b + krow, Skv - 1) (rows past Skv are fetched but masked) as a
   // block offset plus loop-invariant per-lane parts, all below 2^32 (checked by the caller)
-  const uint32_t koff = (uint32_t)(krow * crow + 16 * kpiece), kmax = (uint32_t)((S - 1) * crow + 16 * kpiece);
-  const uint32_t ksoff = (uint32_t)(lane * srow), ksmax = (uint32_t)((S - 1) * srow);
+  const uint32_t koff = (uint32_t)(krow * crow + 16 * kpiece), kmax = (uint32_t)((Skv - 1) * crow + 16 * kpiece);
+  const uint32_t ksoff = (uint32_t)(lane * srow), ksmax = (uint32_t)((Skv - 1) * srow);
   auto issue = [&](int b, int stage) {
     const uint32_t sb = lds0 + (uint32_t)(stage * AT_STAGE);
     const uint32_t kblk = (uint32_t)b * (uint32_t)(AT_KVB * crow);
@@ -259,12 +261,12 @@ __global__ __launch_bounds__(64 * AT_WAVES, 2) void attn_mx_kernel(
     // slightly below 1 would move its group's scale down a power of two).  Every p of a row
     // carries the same factor 2^(c * max - m'), which cancels in o / l.  The per-tile maxima of
     // acc give each 32-key group's largest p by the same expression.
-    if ((b + 1) * AT_KVB > S) {
+    if ((b + 1) * AT_KVB > Skv) {
 #pragma unroll
       for (int t = 0; t < 2; ++t)
 #pragma unroll
         for (int e = 0; e < 16; ++e)
-          if (b * AT_KVB + 32 * t + 8 * (e >> 2) + 4 * h + (e & 3) >= S) sc[t][e] = -__builtin_inff();
+          if (b * AT_KVB + 32 * t + 8 * (e >> 2) + 4 * h + (e & 3) >= Skv) sc[t][e] = -__builtin_inff();
     }
     float mt[2];
 #pragma unroll
@@ -274,7 +276,7 @@ __global__ __launch_bounds__(64 * AT_WAVES, 2) void attn_mx_kernel(
       for (int e = 3; e < 15; e += 2) x = max3_raw(x, sc[t][e], sc[t][e + 1]);
       mt[t] = halves_max(max3_raw(x, sc[t][15], sc[t][15]));
     }
-    const float amx = max3_raw(mt[0], mt[1], mt[1]);  // finite: every block holds a key < S
+    const float amx = max3_raw(mt[0], mt[1], mt[1]);  // finite: every block holds a key < Skv
     // mb = fp32(c * amx) lowered by |mb| 2^-23 (at least one ulp): strictly below the exact
     // c * amx for any normal mb, so the maximal key's exponent is >= 0 (a subnormal mb means
     // |c * amx| < 2^-126, where 2^exponent rounds to 1 anyway)
@@ -339,7 +341,7 @@ __global__ __launch_bounds__(64 * AT_WAVES, 2) void attn_mx_kernel(
 
   l = halves_sum(l);
   const float inv = 1.0f / l;
-  if (q >= S) return;
+  if (q >= Sq) return;
   if (OUTF32) {
     float* orow = (float*)out + bh * hs_o + (int64_t)q * ld_o;
 #pragma unroll
@@ -360,19 +362,19 @@ __global__ __launch_bounds__(64 * AT_WAVES, 2) void attn_mx_kernel(
   }
 }
 
-hipError_t launch_attn_mx(const uint8_t* qc, const uint8_t* qs, const uint8_t* kc, const uint8_t* ks,
-                          int64_t ld, int64_t hs, const uint8_t* vc, const uint8_t* vs, int64_t BH,
-                          int64_t S, float softmax_scale, bool out_f32, void* out, int64_t ld_o,
-                          int64_t hs_o, hipStream_t s) {
-  const int nblk = (int)((S + AT_KVB - 1) / AT_KVB);
+hipError_t launch_attn_mx(const uint8_t* qc, const uint8_t* qs, int64_t ld_q, int64_t hs_q, const uint8_t* kc,
+                          const uint8_t* ks, int64_t ld_k, int64_t hs_k, const uint8_t* vc, const uint8_t* vs,
+                          int64_t BH, int64_t Sq, int64_t Skv, float softmax_scale, bool out_f32, void* out,
+                          int64_t ld_o, int64_t hs_o, hipStream_t s) {
+  const int nblk = (int)((Skv + AT_KVB - 1) / AT_KVB);
   const float cexp = (float)((double)softmax_scale * 1.4426950408889634);  // softmax_scale * log2(e)
-  dim3 grid((unsigned)((S + 32 * AT_WAVES - 1) / (32 * AT_WAVES)), (unsigned)BH);
+  dim3 grid((unsigned)((Sq + 32 * AT_WAVES - 1) / (32 * AT_WAVES)), (unsigned)BH);
   if (out_f32)
-    hipLaunchKernelGGL(attn_mx_kernel<true>, grid, dim3(64 * AT_WAVES), 0, s, qc, qs, kc, ks, vc, vs,
-                       (int)S, nblk, ld, hs, cexp, out, ld_o, hs_o);
+    hipLaunchKernelGGL(attn_mx_kernel<true>, grid, dim3(64 * AT_WAVES), 0, s, qc, qs, kc, ks, vc, vs, (int)Sq,
+                       (int)Skv, nblk, ld_q, hs_q, ld_k, hs_k, cexp, out, ld_o, hs_o);
   else
-    hipLaunchKernelGGL(attn_mx_kernel<false>, grid, dim3(64 * AT_WAVES), 0, s, qc, qs, kc, ks, vc, vs,
-                       (int)S, nblk, ld, hs, cexp, out, ld_o, hs_o);
+    hipLaunchKernelGGL(attn_mx_kernel<false>, grid, dim3(64 * AT_WAVES), 0, s, qc, qs, kc, ks, vc, vs, (int)Sq,
+                       (int)Skv, nblk, ld_q, hs_q, ld_k, hs_k, cexp, out, ld_o, hs_o);
   return hipGetLastError();
 }
 

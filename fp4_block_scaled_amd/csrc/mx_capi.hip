@@ -257,28 +257,30 @@ mx_status mx_quantize_vt(const uint16_t* v, int64_t BH, int64_t S, int64_t D, in
                     "mx_quantize_vt launch");
 }
 
-mx_status mx_attention(const uint8_t* q_codes, const uint8_t* q_scales, const uint8_t* k_codes,
-                       const uint8_t* k_scales, int64_t ld_qk, int64_t hs_qk,
-                       const uint8_t* vt_codes, const uint8_t* vt_scales, int64_t BH, int64_t S,
-                       int64_t D, float softmax_scale, int32_t out_dtype, void* out, int64_t ld_o,
-                       int64_t hs_o, void* stream) {
+mx_status mx_attention(const uint8_t* q_codes, const uint8_t* q_scales, int64_t ld_q, int64_t hs_q,
+                       const uint8_t* k_codes, const uint8_t* k_scales, int64_t ld_k, int64_t hs_k,
+                       const uint8_t* vt_codes, const uint8_t* vt_scales, int64_t BH, int64_t S_q,
+                       int64_t S_kv, int64_t D, float softmax_scale, int32_t out_dtype, void* out,
+                       int64_t ld_o, int64_t hs_o, void* stream) {
   g_err[0] = 0;
   if (D != MX_ATTN_HEAD_DIM) return fail(MX_ERR_UNSUPPORTED, "head dimension %lld (only %d)", (long long)D, MX_ATTN_HEAD_DIM);
-  if (BH < 0 || BH > 65535 || S < 0 || S > (1 << 24)) return fail(MX_ERR_SHAPE, "need 0 <= BH <= 65535 and 0 <= S <= 2^24");
+  if (BH < 0 || BH > 65535 || S_q < 0 || S_q > (1 << 24) || S_kv < 0 || S_kv > (1 << 24))
+    return fail(MX_ERR_SHAPE, "need 0 <= BH <= 65535 and 0 <= S_q, S_kv <= 2^24");
   if (!(softmax_scale > 0.0f) || !isfinite(softmax_scale)) return fail(MX_ERR_SHAPE, "softmax_scale must be finite and > 0");
   if (out_dtype != MX_OUT_BF16 && out_dtype != MX_OUT_F32) return fail(MX_ERR_UNSUPPORTED, "unknown out_dtype %d", out_dtype);
-  if (ld_qk < D || ld_qk % 128 || hs_qk < 0 || hs_qk % 128)
-    return fail(MX_ERR_ALIGN, "need ld_qk >= 128 and ld_qk, hs_qk multiples of 128");
+  if (ld_q < D || ld_q % 128 || hs_q < 0 || hs_q % 128 || ld_k < D || ld_k % 128 || hs_k < 0 || hs_k % 128)
+    return fail(MX_ERR_ALIGN, "need ld_q, ld_k >= 128 and ld_q, hs_q, ld_k, hs_k multiples of 128");
   if (ld_o < D || ld_o % 8 || hs_o < 0 || hs_o % 8) return fail(MX_ERR_ALIGN, "need ld_o >= 128 and ld_o, hs_o multiples of 8");
-  if ((S + 64) * (ld_qk / 2) >= (int64_t)1 << 32) return fail(MX_ERR_SHAPE, "(S + 64) * ld_qk / 2 must stay below 2^32");
-  if (BH == 0 || S == 0) return MX_OK;
+  if ((S_kv + 64) * (ld_k / 2) >= (int64_t)1 << 32) return fail(MX_ERR_SHAPE, "(S_kv + 64) * ld_k / 2 must stay below 2^32");
+  if (BH == 0 || S_q == 0) return MX_OK;
+  if (S_kv == 0) return fail(MX_ERR_SHAPE, "attention over zero keys is undefined (S_kv == 0, S_q > 0)");
   if (!q_codes || !q_scales || !k_codes || !k_scales || !vt_codes || !vt_scales || !out)
     return fail(MX_ERR_NULL, "operands and out must be non-NULL");
   if (!aligned(q_codes, 16) || !aligned(k_codes, 16) || !aligned(vt_codes, 16) || !aligned(out, 16) ||
       !aligned(q_scales, 4) || !aligned(k_scales, 4) || !aligned(vt_scales, 4))
     return fail(MX_ERR_ALIGN, "codes and out need 16-byte, scales 4-byte alignment");
-  return hip_status(mxk::launch_attn_mx(q_codes, q_scales, k_codes, k_scales, ld_qk, hs_qk, vt_codes,
-                                        vt_scales, BH, S, softmax_scale, out_dtype == MX_OUT_F32, out,
+  return hip_status(mxk::launch_attn_mx(q_codes, q_scales, ld_q, hs_q, k_codes, k_scales, ld_k, hs_k, vt_codes,
+                                        vt_scales, BH, S_q, S_kv, softmax_scale, out_dtype == MX_OUT_F32, out,
                                         ld_o, hs_o, (hipStream_t)stream),
                     "mx_attention launch");
 }

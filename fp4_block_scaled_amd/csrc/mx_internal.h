@@ -70,12 +70,12 @@ hipError_t launch_quant8_lowrank_down(const uint16_t* x, int64_t ld_x, const uin
 // Sp = S rounded up to 64, keys past S zero.
 hipError_t launch_quant_vt(const uint16_t* v, int64_t BH, int64_t S, int64_t D, int64_t ld, int64_t hs,
                            uint8_t* codes, uint8_t* scales, hipStream_t s);
-// Microscaled attention, head dimension 128: Q/K MXFP4 row-major codes and scales of rows
-// (b, s) at b * hs + s * ld elements; V^T as launch_quant_vt writes it; out [BH, S, 128] BF16 or
-// FP32 at b * hs_o + s * ld_o elements.
-hipError_t launch_attn_mx(const uint8_t* qc, const uint8_t* qs, const uint8_t* kc, const uint8_t* ks,
-                          int64_t ld, int64_t hs, const uint8_t* vc, const uint8_t* vs, int64_t BH,
-                          int64_t S, float softmax_scale, bool out_f32, void* out, int64_t ld_o,
-                          int64_t hs_o, hipStream_t s);
+// Microscaled attention, head dimension 128: Q MXFP4 row-major codes and scales of rows (b, s)
+// at b * hs_q + s * ld_q elements (s < Sq), K likewise with ld_k, hs_k (s < Skv); V^T as
+// launch_quant_vt writes it for Skv keys; out [BH, Sq, 128] BF16 or FP32 at b * hs_o + s * ld_o.
+hipError_t launch_attn_mx(const uint8_t* qc, const uint8_t* qs, int64_t ld_q, int64_t hs_q, const uint8_t* kc,
+                          const uint8_t* ks, int64_t ld_k, int64_t hs_k, const uint8_t* vc, const uint8_t* vs,
+                          int64_t BH, int64_t Sq, int64_t Skv, float softmax_scale, bool out_f32, void* out,
+                          int64_t ld_o, int64_t hs_o, hipStream_t s);
 
 }  // namespace mxk

@@ -231,31 +231,35 @@ mx_status mx_quantize_vt(const uint16_t* v, int64_t BH, int64_t S, int64_t D, in
 
 /*
  * mx_attention - softmax(softmax_scale * Q K^T) V per head, with Q and K in MXFP4 and V and the
- * probabilities in MXFP8 (same pages as mx_quantize_vt).  Per block of MX_ATTN_KVB keys, with
- * c = softmax_scale * log2(e): s = c (q . k) (keys past S masked), m' = max(m, block max),
- * alpha = 2^(m - m'), p = 2^(s - m'), l = alpha l + sum p, o = alpha o + Q_MX8(p) . V (p
+ * probabilities in MXFP8 (same pages as mx_quantize_vt).  Queries and keys may come from
+ * sequences of different lengths: S_q query rows and S_kv key / value rows per head (the DiT's
+ * first attention layer has S_kv = S_q; its second, attn2 in the MXFP4 card's Quantization
+ * Details, takes keys and values from the conditioning context).  Per block of MX_ATTN_KVB keys,
+ * with c = softmax_scale * log2(e): s = c (q . k) (keys past S_kv masked), m' = max(m, block
+ * max), alpha = 2^(m - m'), p = 2^(s - m'), l = alpha l + sum p, o = alpha o + Q_MX8(p) . V (p
  * quantized to MXFP8 in groups of 32 consecutive keys); out = o / l.  Scores and o accumulate in
  * FP32 on the scaled matrix cores.  Accuracy against the exact (fp64) evaluation of that
  * definition: within 2e-3 * sum p^ |v^| / l per element, plus the effect of probabilities whose
  * fp32 evaluation rounds to a neighbouring E4M3 value; the matrix core accumulates a block's FP8
  * products to about 1e-4 of their absolute sum rather than exactly in binary32.
- *  q_codes/q_scales, k_codes/k_scales: row-major MXFP4 (mx_quantize's output) of BH heads of
- *        S x MX_ATTN_HEAD_DIM, row (b, s) at element offset b * hs_qk + s * ld_qk: codes byte
- *        (b * hs_qk + s * ld_qk) / 2, scale byte (b * hs_qk + s * ld_qk) / 32.  ld_qk and hs_qk
+ *  q_codes/q_scales: row-major MXFP4 (mx_quantize's output) of BH heads of S_q x
+ *        MX_ATTN_HEAD_DIM, row (b, s) at element offset b * hs_q + s * ld_q: codes byte
+ *        (b * hs_q + s * ld_q) / 2, scale byte (b * hs_q + s * ld_q) / 32.
+ *  k_codes/k_scales: the same for S_kv key rows with ld_k, hs_k.  ld_q, hs_q, ld_k, hs_k are
  *        multiples of 128; codes 16-byte and scales 4-byte aligned.
- *  vt_codes/vt_scales: mx_quantize_vt's output for the same BH, S, D (codes 16-byte, scales
- *        4-byte aligned).
+ *  vt_codes/vt_scales: mx_quantize_vt's output for BH, S_kv, D (codes 16-byte, scales 4-byte
+ *        aligned).
  *  out: device BF16 (MX_OUT_BF16, the RNE of the FP32 result) or FP32, element (b, s, d) at
- *        b * hs_o + s * ld_o + d; 16-byte aligned, ld_o and hs_o multiples of 8.
- * Requires D == MX_ATTN_HEAD_DIM, BH <= 65535, 0 <= S <= 2^24 with (S + 64) * ld_qk / 2 < 2^32,
- * softmax_scale finite and > 0.
- * S == 0 does nothing.  Caller owns every buffer; nothing is allocated.
+ *        b * hs_o + s * ld_o + d (s < S_q); 16-byte aligned, ld_o and hs_o multiples of 8.
+ * Requires D == MX_ATTN_HEAD_DIM, BH <= 65535, 0 <= S_q, S_kv <= 2^24 with
+ * (S_kv + 64) * ld_k / 2 < 2^32, softmax_scale finite and > 0; S_kv == 0 with S_q > 0 is an
+ * error (MX_ERR_SHAPE).  S_q == 0 does nothing.  Caller owns every buffer; nothing is allocated.
  */
-mx_status mx_attention(const uint8_t* q_codes, const uint8_t* q_scales, const uint8_t* k_codes,
-                       const uint8_t* k_scales, int64_t ld_qk, int64_t hs_qk,
-                       const uint8_t* vt_codes, const uint8_t* vt_scales, int64_t BH, int64_t S,
-                       int64_t D, float softmax_scale, int32_t out_dtype, void* out, int64_t ld_o,
-                       int64_t hs_o, void* stream);
+mx_status mx_attention(const uint8_t* q_codes, const uint8_t* q_scales, int64_t ld_q, int64_t hs_q,
+                       const uint8_t* k_codes, const uint8_t* k_scales, int64_t ld_k, int64_t hs_k,
+                       const uint8_t* vt_codes, const uint8_t* vt_scales, int64_t BH, int64_t S_q,
+                       int64_t S_kv, int64_t D, float softmax_scale, int32_t out_dtype, void* out,
+                       int64_t ld_o, int64_t hs_o, void* stream);
 
 /* Bytes of workspace mx_linear needs for an M x K activation in act_fmt (codes + scales of the
  * quantized activation -- in the tiled layout for the MX formats when K % 128 == 0 -- plus the

@@ -224,9 +224,10 @@ def test_attention_validation(mx):
                                 P(scales) if scales else None, None)
 
     def at(q=FAKE, k=FAKE, ld=128, hs=12800, v=FAKE, BH=2, S=100, D=128, scale=0.088, dt=0,
-           out=FAKE, ldo=128, hso=12800):
-        return L.mx_attention(P(q) if q else None, P(FAKE), P(k) if k else None, P(FAKE), ld, hs,
-                              P(v) if v else None, P(FAKE), BH, S, D, scale, dt,
+           out=FAKE, ldo=128, hso=12800, Skv=None, ldk=None, hsk=None):
+        return L.mx_attention(P(q) if q else None, P(FAKE), ld, hs, P(k) if k else None, P(FAKE),
+                              ld if ldk is None else ldk, hs if hsk is None else hsk,
+                              P(v) if v else None, P(FAKE), BH, S, S if Skv is None else Skv, D, scale, dt,
                               P(out) if out else None, ldo, hso, None)
 
     assert vt(D=100, ld=104) == 2 and vt(D=0) == 2
@@ -246,6 +247,10 @@ def test_attention_validation(mx):
     assert at(BH=70000) == 2
     assert at(S=1 << 24, ld=512, hs=0) == 2      # K offsets must stay 32-bit
     assert vt(S=(1 << 24) + 1) == 2
+    assert at(Skv=0) == 2                        # queries but no keys
+    assert at(S=0, Skv=0, q=0, k=0, v=0, out=0) == 0
+    assert at(Skv=-1) == 2 and at(Skv=(1 << 24) + 1) == 2
+    assert at(ldk=192) == 3 and at(hsk=64) == 3
 
 
 def test_relayout_validation(mx):
@@ -291,11 +296,15 @@ def test_attention_binding_checks_arguments_before_any_call(mx):
     with pytest.raises(mx.MxError):
         mx.attention(q, qm(200, D, layout=mx.TILED), vt(2, 100), 2)       # row-major only
     with pytest.raises(mx.MxError):
-        mx.attention(q, qm(202, D), vt(2, 100), 2)                        # q and k shapes differ
+        mx.attention(q, qm(201, D), vt(2, 100), 2)                        # k rows not heads * S_kv
+    with pytest.raises(mx.MxError):
+        mx.attention(q, qm(200, 2 * D), vt(2, 100), 2)                    # q and k widths differ
     with pytest.raises(mx.MxError):
         mx.attention(qm(200, 2 * D), qm(200, 2 * D), vt(2, 100), 2)       # bhsd needs 128 columns
     with pytest.raises(mx.MxError):
         mx.attention(q, q, vt(2, 164), 2)                                 # V^T of another length
+    with pytest.raises(mx.MxError):
+        mx.attention(q, qm(2 * 200, D), vt(2, 100), 2)                    # V^T not of the keys' length
     with pytest.raises(mx.MxError):
         mx.attention(qm(100, 3 * D), qm(100, 3 * D), vt(3, 100), 2, layout="shd")  # heads * 128 columns
     with pytest.raises(mx.MxError):

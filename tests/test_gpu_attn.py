@@ -216,11 +216,59 @@ def test_head_and_row_strides_through_the_c_abi(mx):
     vt = mx.quantize_vt(to_dev_bf16(v_bits))
     out = torch.full((BH, S + pad, D), float("nan"), dtype=torch.float32, device="cuda")
     hs = (S + pad) * D
-    st = mx.lib().mx_attention(qp.codes.data_ptr(), qp.scales.data_ptr(), kp.codes.data_ptr(),
-                               kp.scales.data_ptr(), D, hs, vt[0].data_ptr(), vt[1].data_ptr(), BH, S, D,
-                               ctypes.c_float(D ** -0.5), 1, out.data_ptr(), D, hs,
+    st = mx.lib().mx_attention(qp.codes.data_ptr(), qp.scales.data_ptr(), D, hs, kp.codes.data_ptr(),
+                               kp.scales.data_ptr(), D, hs, vt[0].data_ptr(), vt[1].data_ptr(), BH, S, S,
+                               D, ctypes.c_float(D ** -0.5), 1, out.data_ptr(), D, hs,
                                ctypes.c_void_p(torch.cuda.current_stream().cuda_stream))
     torch.cuda.synchronize()
     assert st == 0
     assert torch.equal(out[:, :S], dense)
     assert torch.isnan(out[:, S:]).all()  # rows past S untouched
+
+
+@pytest.mark.parametrize("BH,Sq,Skv,sigma", [
+    (2, 300, 77, 1.0),    # more queries than keys, ragged key block
+    (1, 64, 512, 1.0),    # eight key blocks for one query block
+    (3, 10, 1, 1.0),      # a single key: out = v^
+    (2, 129, 200, 2.0),   # sharper softmax
+])
+def test_cross_attention_vs_oracle(mx, BH, Sq, Skv, sigma):
+    """Queries and keys / values of different lengths (the second attention layer of the DiT
+    attends to the conditioning context)."""
+    q_bits = _bits(36000 + Sq, (BH * Sq, D), sigma)
+    k_bits = _bits(36100 + Skv, (BH * Skv, D), sigma)
+    v_bits = _bits(36200 + Skv, (BH * Skv, D), 1.0)
+    qc, qs = O.quantize_mx_bf16(q_bits)
+    kc, ks = O.quantize_mx_bf16(k_bits)
+    vtc, vts = O.quantize_vt_mx8(v_bits, BH, Skv, D, KVB)
+    o = mx.attention(mx.quantize(to_dev_bf16(q_bits), "mxfp4"), mx.quantize(to_dev_bf16(k_bits), "mxfp4"),
+                     mx.quantize_vt(to_dev_bf16(v_bits).view(BH, Skv, D)), BH, out_dtype=torch.float32)
+    torch.cuda.synchronize()
+    ref, bnd, ab = O.attention_mx(qc, qs, kc, ks, vtc, vts, BH, Sq, D, KVB, D ** -0.5, S_kv=Skv)
+    _compare(o.cpu().numpy().reshape(BH * Sq, D), ref, bnd, ab, Skv, f"cross-attention {Sq}x{Skv}")
+
+
+@pytest.mark.parametrize("name", ["wan_a14b_attn_mx_75600x40x128", "wan_ti2v5b_attn_mx_4290x24x128"])
+def test_full_size_wan_cross_attention(mx, name):
+    """The workload's queries against 512 context tokens (keys and values N(0,1), seeded), in the
+    projections' layout with BF16 out: sampled queries of three heads against the oracle."""
+    wl = synth.WORKLOADS[name]
+    Sq, H, Skv = wl.M, wl.extra["heads"], 512
+    q_bits = synth.bits16(synth.to_bf16(wl.qkv(Sq)[0]))
+    k_bits = _bits(wl.seed_base + 21, (Skv, H * D), 1.0)
+    v_bits = _bits(wl.seed_base + 22, (Skv, H * D), 1.0)
+    vt = mx.quantize_vt(to_dev_bf16(v_bits).view(Skv, H, D).transpose(0, 1))
+    o = mx.attention(mx.quantize(to_dev_bf16(q_bits), "mxfp4"), mx.quantize(to_dev_bf16(k_bits), "mxfp4"),
+                     vt, heads=H, layout="shd")
+    torch.cuda.synchronize()
+    rows = np.unique(np.concatenate([sample_rows(Sq, 24), [0, Sq - 1]]))
+    for h in (0, H // 2 - 3, H - 1):
+        hq = np.ascontiguousarray(q_bits[:, h * D:(h + 1) * D])
+        hk = np.ascontiguousarray(k_bits[:, h * D:(h + 1) * D])
+        hv = np.ascontiguousarray(v_bits[:, h * D:(h + 1) * D])
+        qc, qs = O.quantize_mx_bf16(hq)
+        kc, ks = O.quantize_mx_bf16(hk)
+        vtc, vts = O.quantize_vt_mx8(hv, 1, Skv, D, KVB)
+        ref, bnd, ab = O.attention_mx(qc, qs, kc, ks, vtc, vts, 1, Sq, D, KVB, D ** -0.5, qrows=rows, S_kv=Skv)
+        got = O.bf16_values(dev_bits16(o[torch.from_numpy(rows).cuda(), h * D:(h + 1) * D]))
+        _compare(got, ref, bnd, ab, Skv, f"full-size cross head {h}", extra=2.0 ** -8 * np.abs(ref), flip_frac=0.05)
