@@ -1,4 +1,5 @@
-"""CPU oracle for the microscaled-FP4 linear layer (ctypes wrapper over ``mxref.c``).
+"""CPU oracle for the microscaled-FP4 linear layer and the microscaled attention (ctypes wrapper
+over ``mxref.c``).
 
 TEST INFRASTRUCTURE ONLY.  Imported by the tests, by ``__graft_entry__.smoke()`` and by the
 benchmark's CPU-baseline leg; never by the product package.  It shares no code with the HIP

@@ -1,5 +1,5 @@
 /*
- * CPU ORACLE for the microscaled-FP4 linear layer.  TEST INFRASTRUCTURE ONLY: nothing in the
+ * CPU ORACLE for the microscaled-FP4 linear layer and the microscaled attention.  TEST INFRASTRUCTURE ONLY: nothing in the
  * product library links, includes or calls this file; only the tests, the smoke check and the
  * CPU-baseline leg of the benchmark do.  It shares no code, header or table with the HIP path.
  *
@@ -19,10 +19,12 @@
  *  - "Wan2.2-I2V-A14B-Lightning-Diffusers-MXFP4-AutoRound", Quantization Details, list of layers
  *    kept at higher precision (norm, modulation table): the LayerNorm + modulation that produces
  *    a quantized linear's input (mxr_norm_modulate).
+ *  - "Wan2.2-I2V-A14B-Lightning-Diffusers-MXFP4-AutoRound", attention backends and Performance
+ *    Profile, and "Wan2.2-Animate-14B-Diffusers-MXFP4-AutoRound" on the FP4 attention backend:
+ *    microscaled attention in the formats of the linear layer (mxr_attention_mx).
  * The pages name these formats but do not define them bit by bit; the element and scale
  * encodings follow the OCP Microscaling (MX) v1.0 specification that the "MX" names refer to.
- * Every reading taken where the pages are silent is listed in the design notes; each function
- * below states the one it uses.
+ * Where the pages are silent, each function below states the reading it takes.
  *
  * Parity status: every function here is pinned by a CPU test against values the pages fix, a
  * hand-derived worked example, a brute-force search or a library routine, except the NVFP4 path
