@@ -356,12 +356,29 @@ def bench_attention(args, torch, mx, synth):
                                          args.steps, torch)
     kernels["quant_vt_ms"] = time_events(lambda: mx.quantize_vt(vv, out=vt), args.steps, torch)
     val = flops / (ms * 1e-3) / 1e12
+    cpu = None
+    if not args.no_cpu:
+        # the oracle on 64 query rows of head 0 against all S keys (its quantization of that
+        # head's Q, K and V^T included), as TFLOP/s of the same 4 S D work per query row
+        import oracle as O
+        hb = [synth.bits16(x[:, :D].contiguous().cpu()) for x in (q, k, v)]  # head 0's columns
+        rows = np.concatenate([np.arange(32), np.arange(S - 32, S)])
+        t0 = time.perf_counter()
+        qc, qs = O.quantize_mx_bf16(hb[0])
+        kc, ks = O.quantize_mx_bf16(hb[1])
+        vtc, vts = O.quantize_vt_mx8(hb[2], 1, S, D, mx.ATTN_KVB)
+        O.attention_mx(qc, qs, kc, ks, vtc, vts, 1, S, D, mx.ATTN_KVB, D ** -0.5, qrows=rows)
+        dt = time.perf_counter() - t0
+        cpu = {"value": 4.0 * S * D * rows.size / dt / 1e12, "unit": "TFLOP/s",
+               "cores": int(os.environ.get("OMP_NUM_THREADS", os.cpu_count() or 1)), "kind": "oracle",
+               "sample": f"64 query rows (first and last 32) of head 0 against all {S} keys, with that "
+                         f"head's quantization: {dt:.2f} s; CPU: {cpu_info()}"}
     return {"metric": f"{wl.name} TFLOPS (Q/K/V quantization + attention)", "value": val,
             "unit": "TFLOP/s", "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,
             "ms_per_step": ms, "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
             "dtype": "mxfp4 QK, mxfp8 PV", "data": "synthetic",
             "config": {"workload": wl.name, "S": S, "heads": H, "head_dim": D},
-            "frac_of_peak": val / peak, "peak_tflops": peak, "kernels": kernels}
+            "frac_of_peak": val / peak, "peak_tflops": peak, "kernels": kernels, "cpu_baseline": cpu}
 
 
 COPY_BYTES = 1 << 30
