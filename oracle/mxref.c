@@ -27,9 +27,12 @@
  * Where the pages are silent, each function below states the reading it takes.
  *
  * Parity status: every function here is pinned by a CPU test against values the pages fix, a
- * hand-derived worked example, a brute-force search or a library routine, except the NVFP4 path
- * with a global scale other than 1 (see mxr_quantize_nv), whose rounding is pinned only by the
- * brute-force comparison on small inputs.
+ * hand-derived worked example, a brute-force search, exact rational arithmetic or a library
+ * routine (the tests of the oracle name the pin of each function).  The NVFP4 global scale
+ * other than 1 is pinned by hand-derived blocks, an exact rational brute force of the quantizer,
+ * the decode as an exact product and a rational brute-force GEMM; the attention's probability
+ * quantization, its 32-key grouping, its flip bound and its absolute accumulator are pinned by a
+ * constructed case whose scores are exact.
  */
 #include <math.h>
 #include <stdint.h>

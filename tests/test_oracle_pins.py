@@ -157,7 +157,8 @@ def test_mxfp8_worked_blocks(b):
 @pytest.mark.parametrize("b", _golden("nvfp4_worked_blocks.json")["blocks"], ids=lambda b: b["name"])
 def test_nvfp4_worked_blocks(b):
     bits = _block_bits(b)[None, :]
-    codes, scales = O.quantize_nv_bf16(bits, 1.0)
+    sg = b.get("global_scale", _golden("nvfp4_worked_blocks.json")["global_scale"])
+    codes, scales = O.quantize_nv_bf16(bits, sg)
     assert int(scales[0, 0]) == b["scale"]
     np.testing.assert_array_equal(_unpack(codes[0], 16), b["codes"])
     if "packed" in b:
@@ -638,3 +639,300 @@ def test_cross_attention_matches_softmax_attention_within_p_quantization(Sq, Skv
     tol = (p @ torch.from_numpy(np.abs(np.ascontiguousarray(vd)))).numpy().reshape(BH * Sq, D) / 8 + 1e-12
     assert np.all(np.abs(out - ref) <= tol)
     assert np.all(np.abs(out - ref) <= 4 * bnd + 1e-12)
+
+
+# ---------------------------------------------------------------------------------------------
+# NVFP4 decode with a global scale other than 1 (NVFP4 model card, Model Details: one FP32
+# global scale per tensor; value = code * block scale * global scale, decode direction)
+# ---------------------------------------------------------------------------------------------
+_E4M3_ALL_F = [None if (b & 0x7F) == 0x7F else
+               Fraction(float(torch.tensor([b], dtype=torch.uint8).view(torch.float8_e4m3fn).to(torch.float64)[0]))
+               for b in range(256)]
+
+
+def _e2m1_f(code):
+    """E2M1 code -> Fraction, from the golden grid (sign bit 3)."""
+    v = _E2M1_F[code & 7]
+    return -v if code & 8 else v
+
+
+@pytest.mark.parametrize("sg", [40.0 / 2688.0, 3.0 / 7.0, 1e-3])
+def test_nvfp4_dequantize_is_exact_product_with_global_scale(sg):
+    """dequantize_nv(quantize_nv(x, sg), sg) is code * sb * sg as an exact rational (the three
+    factors carry 2, 4 and 24 significant bits, so fp64 holds the product exactly).  Reading the
+    global scale the other way (/sg) or dropping it fails."""
+    sg32 = float(np.float32(sg))
+    bits = _blocks_for_nv(48, 101)
+    codes, scales = O.quantize_nv_bf16(bits, sg32)
+    deq = O.dequantize_nv(codes, scales, sg32, 16)
+    cod = _unpack(codes, 16)
+    g = Fraction(sg32)
+    for r in range(bits.shape[0]):
+        sb = _E4M3_ALL_F[int(scales[r, 0])]
+        for i in range(16):
+            assert Fraction(float(deq[r, i])) == _e2m1_f(int(cod[r, i])) * sb * g, (r, i)
+    # the quantizer fits that decode: where the block scale amax / (6 sg) is a normal,
+    # unsaturated E4M3 value, the block maximum decodes within the E4M3 half step (1/16) of
+    # amax, code 6 times sb times sg
+    x = O.bf16_values(bits)
+    amax = np.abs(x).max(axis=1)
+    dmax = np.abs(deq).max(axis=1)
+    ratio = amax / (6.0 * sg32)
+    ok = (ratio >= 2.0 ** -6) & (ratio <= 448.0)
+    assert ok.sum() >= 3
+    assert np.all(np.abs(dmax[ok] - amax[ok]) <= amax[ok] / 16 * (1 + 1e-12))
+
+
+def test_nvfp4_gemm_matches_rational_bruteforce():
+    """A 3 x 5 x 64 NVFP4 linear with activation and weight global scales other than 1 and an
+    FP16 bias, against exact rational arithmetic on the decoded operands."""
+    M, N, K = 3, 5, 64
+    sg_a, sg_w = float(np.float32(40.0 / 2688.0)), float(np.float32(0.0123))
+    a_bits = synth.bits16(synth.to_bf16(synth.activation_f32(111, M, K, 1.0, 0.05, 30.0)))
+    w_bits = synth.bits16(synth.to_bf16(synth.normal_f32(112, (N, K), 0.01)))
+    b_bits = synth.bits16(synth.to_f16(synth.normal_f32(113, (N,), 0.01)))
+    ac, as_ = O.quantize_nv_bf16(a_bits, sg_a)
+    wc, ws = O.quantize_nv_bf16(w_bits, sg_w)
+    y, t = O.linear_ref_nv(ac, as_, sg_a, wc, ws, sg_w, K, b_bits)
+    acod, wcod = _unpack(ac, K), _unpack(wc, K)
+    bias = torch.from_numpy(b_bits.view(np.int16)).view(torch.float16).to(torch.float64).numpy()
+    for m in range(M):
+        for n in range(N):
+            s = Fraction(0)
+            sa = Fraction(0)
+            for k in range(K):
+                av = _e2m1_f(int(acod[m, k])) * _E4M3_ALL_F[int(as_[m, k // 16])] * Fraction(sg_a)
+                wv = _e2m1_f(int(wcod[n, k])) * _E4M3_ALL_F[int(ws[n, k // 16])] * Fraction(sg_w)
+                s += av * wv
+                sa += abs(av * wv)
+            exact = s + Fraction(float(bias[n]))
+            # fp64 summation of K products: within K ulps of the absolute sum
+            assert abs(Fraction(float(y[m, n])) - exact) <= Fraction(K * 2.0 ** -52) * (sa + abs(Fraction(float(bias[n]))))
+            assert abs(Fraction(float(t[m, n])) - sa) <= Fraction(K * 2.0 ** -52) * sa
+    assert np.any(t > 0)
+
+
+def test_absmax_matches_numpy():
+    """mxr_absmax_bf16 against numpy's max of |x| on torch's BF16 decoding, with negative,
+    subnormal and extreme values."""
+    rng = np.random.default_rng(7)
+    x = rng.standard_normal((37, 129)).astype(np.float32)
+    x[3, 5] = -3.0e38
+    x[7, 9] = 1e-40  # BF16 subnormal
+    bits = synth.bits16(synth.to_bf16(x))
+    ref = float(np.abs(torch.from_numpy(bits.view(np.int16)).view(torch.bfloat16).to(torch.float64).numpy()).max())
+    assert O.absmax_bf16(bits) == ref
+    sub = bits[:, 60:]  # without the large negative value
+    ref2 = float(np.abs(torch.from_numpy(np.ascontiguousarray(sub).view(np.int16)).view(torch.bfloat16)
+                        .to(torch.float64).numpy()).max())
+    assert O.absmax_bf16(np.ascontiguousarray(sub)) == ref2
+    # the maximum at each corner of the matrix (first / last row and column)
+    for r, c in ((0, 0), (0, 128), (36, 0), (36, 128)):
+        xc = np.ascontiguousarray(bits[:, 60:].copy())
+        xc[r % xc.shape[0], c % xc.shape[1]] = 0xC700  # -32768
+        assert O.absmax_bf16(xc) == 32768.0, (r, c)
+    assert O.absmax_bf16(np.zeros((2, 3), dtype=np.uint16)) == 0.0
+    assert O.absmax_bf16(np.full((1, 4), 0x8001, dtype=np.uint16)) == 2.0 ** -133  # -min subnormal
+
+
+# ---------------------------------------------------------------------------------------------
+# microscaled attention: the probabilities' MXFP8 quantization, seen through a constructed case
+# ---------------------------------------------------------------------------------------------
+def _encode_exact(v):
+    """(E2M1 code, E8M0 byte) whose decoded value is exactly v, by search over the grid."""
+    fv = Fraction(v)
+    for sb in range(0, 255):
+        sc = Fraction(2) ** (sb - 127)
+        for c in range(16):
+            if _e2m1_f(c) * sc == fv and (c != 8 or v == 0):
+                return c, sb
+    raise AssertionError(f"{v} is not an E2M1 value times a power of two")
+
+
+_SINGLE = sorted({sg * m * 2.0 ** e for sg in (1, -1) for m in (1, 3) for e in range(-6, 7)} | {0.0})
+
+
+def _split3(v):
+    """v as a sum of at most three values each exactly an E2M1 value times a power of two."""
+    import itertools
+    for n in (1, 2, 3):
+        for t in itertools.combinations_with_replacement(_SINGLE, n):
+            if sum(Fraction(x) for x in t) == Fraction(v):
+                return list(t) + [0.0] * (3 - n)
+    raise AssertionError(v)
+
+
+# scores (softmax_scale = ln 2, so c = softmax_scale * log2(e) = 1 and s = q . k) of 128 key
+# slots in two blocks of 64: group 0 holds the block maximum 0; group 1 sits 2^20 below it;
+# block 1 raises the running maximum to 2; keys 120..127 are past S_kv (masked).
+_ATT_S = np.full(128, -48.0)
+_ATT_S[[0, 1, 2, 3, 4, 5, 6, 7, 8, 9, 10, 11]] = [0, -0.5, -1.5, -3, -8, -16, -17, -18, -24, -0.75, -0.25, -19]
+_ATT_S[[32, 33, 34, 35, 36, 37]] = [-20, -20.5, -24, -36, -38, -21.5]
+_ATT_S[[64, 65, 66, 67, 96, 97, 98]] = [2, 1, -12, -0.5, -3, -4, -6]
+_ATT_SKV = 120
+
+
+def _attn_constructed():
+    D, Skv = 128, _ATT_SKV
+    qc = np.zeros((1, D // 2), dtype=np.uint8)
+    qs = np.full((1, D // 32), 127, dtype=np.uint8)
+    qc[0, [0, 16, 32]] = 2             # q[0] = q[32] = q[64] = 1.0 (E2M1 code 2), others 0
+    kc = np.zeros((Skv, D // 2), dtype=np.uint8)
+    ks = np.full((Skv, D // 32), 127, dtype=np.uint8)
+    for j in range(Skv):
+        # k_j[0] + k_j[32] + k_j[64] = s_j, each term in its own 32-element scale block
+        for b, t in enumerate(_split3(float(_ATT_S[j]))):
+            c, sb = _encode_exact(t)
+            kc[j, 16 * b] = c
+            ks[j, b] = sb
+    # V one-hot: v^[key j, column d] = 1 for d == j (E4M3 1.0 = 0x38, unit scales)
+    Sp = 128
+    vtc = np.zeros((1, D, Sp), dtype=np.uint8)
+    for d in range(Skv):
+        vtc[0, d, d] = 0x38
+    vts = np.full((1, D, Sp // 32), 127, dtype=np.uint8)
+    return qc, qs, kc, ks, vtc, vts
+
+
+def _e4m3_torch(x):
+    """E4M3 rounding (RNE, subnormals kept) by torch's float8_e4m3fn conversion, from float32."""
+    t = torch.tensor(np.asarray(x, dtype=np.float32))
+    return t.to(torch.float8_e4m3fn).to(torch.float64).numpy()
+
+
+def test_attention_probability_quantization_constructed():
+    """out * l exposes the quantized probabilities p^ key by key: they must equal an independent
+    per-32-key MXFP8 quantization (E8M0 exponent floor(log2 max p) - 8 per group, torch's E4M3
+    rounding), o / l must divide by the unquantized l = sum p, absacc must be sum p^ |v^| / l
+    exactly, and the flip bound must cover one E4M3 step of p^ without exceeding p / 4 plus the
+    group's subnormal quantum.  A scale taken per 64 keys instead of per 32 zeroes group 1 (its
+    probabilities lie 2^20 below the block maximum) and fails."""
+    D, Skv = 128, _ATT_SKV
+    qc, qs, kc, ks, vtc, vts = _attn_constructed()
+    out, bnd, ab = O.attention_mx(qc, qs, kc, ks, vtc, vts, 1, 1, D, 64, math.log(2.0), S_kv=Skv)
+    out, bnd, ab = out[0], bnd[0], ab[0]
+    s = _ATT_S[:Skv]
+    # independent evaluation: per block of 64 keys, p = 2^(s - block-running max), quantized per
+    # 32-key group; the block-0 terms are rescaled by 2^(m0 - m1) when block 1 raises the max
+    m0 = s[:64].max()
+    m1 = max(m0, s[64:].max())
+    p = np.concatenate([np.exp2(s[:64] - m0), np.exp2(s[64:] - m1)])
+    resc = np.concatenate([np.full(64, 2.0 ** (m0 - m1)), np.ones(Skv - 64)])
+    p_hat = np.zeros(Skv)
+    step_lo = np.zeros(Skv)
+    sub_q = np.zeros(Skv)
+    for g0 in range(0, Skv, 32):
+        grp = slice(g0, min(g0 + 32, Skv))
+        _, ex = np.frexp(p[grp].max())
+        e = (ex - 1) - 8
+        p_hat[grp] = _e4m3_torch(p[grp] * 2.0 ** -e) * 2.0 ** e
+        # one E4M3 step at each p^ (normal: 2^(floor(log2 p) - 3); subnormal: 2^(e - 9))
+        _, pe = np.frexp(p[grp])
+        step_lo[grp] = np.where(p[grp] * 2.0 ** -e >= 2.0 ** -6, np.ldexp(1.0, pe - 1 - 3), 2.0 ** (e - 9))
+        sub_q[grp] = 2.0 ** (e - 9)
+    l = math.fsum(p * resc)
+    ref = p_hat * resc / l
+    np.testing.assert_allclose(out[:Skv], ref, rtol=4e-16, atol=0)
+    assert np.all(out[Skv:] == 0) and np.all(bnd[Skv:] == 0) and np.all(ab[Skv:] == 0)
+    # group 1 is quantized on its own scale: its keys survive (a per-64 scale would zero them)
+    assert np.all(out[[32, 33, 34, 35]] > 0) and out[36] == 0.0  # key 36: 2^-10 of its scale, tie to 0
+    # keys whose p^ rounds to zero still count in l
+    assert out[11] == 0.0 and out[7] == 0.0 and p[11] > 0
+    np.testing.assert_array_equal(ab, np.abs(out))
+    pos = p > 0
+    hi = (p / 4 + sub_q) * resc / l
+    lo = step_lo * resc / l
+    assert np.all(bnd[:Skv][pos] <= hi[pos] * (1 + 1e-15))
+    assert np.all(bnd[:Skv][pos] >= lo[pos] * (1 - 1e-15))
+
+
+# ---------------------------------------------------------------------------------------------
+# storage decoders, the MX dequantizer and the fp32 / fp64 quantizer entry points
+# ---------------------------------------------------------------------------------------------
+def test_bf16_and_f16_decoders_match_torch_on_every_pattern():
+    """mxr_bf16_value and mxr_f16_value on all 65536 patterns against torch's conversions."""
+    allb = np.arange(65536, dtype=np.uint32).astype(np.uint16)
+    tb = torch.from_numpy(allb.view(np.int16))
+    ref_b = tb.view(torch.bfloat16).to(torch.float64).numpy()
+    ref_h = tb.view(torch.float16).to(torch.float64).numpy()
+    got_b = np.array([O.bf16_value(int(b)) for b in allb])
+    got_h = O.f16_values(allb)
+    for got, ref in ((got_b, ref_b), (got_h, ref_h)):
+        nan = np.isnan(ref)
+        assert np.array_equal(np.isnan(got), nan)
+        np.testing.assert_array_equal(got[~nan], ref[~nan])
+        np.testing.assert_array_equal(np.signbit(got[~nan]), np.signbit(ref[~nan]))
+    # the vectorised decoder used by the tests agrees with the C one
+    with np.errstate(invalid="ignore"):  # signalling NaN patterns
+        vec = O.bf16_values(allb)
+    np.testing.assert_array_equal(np.isnan(vec), np.isnan(ref_b))
+    np.testing.assert_array_equal(vec[~np.isnan(ref_b)], ref_b[~np.isnan(ref_b)])
+
+
+@pytest.mark.parametrize("elem", [O.E2M1, O.E4M3])
+def test_dequantize_mx_is_code_times_power_of_two(elem):
+    """mxr_dequantize_mx: value(code) * 2^(byte - 127), NaN for byte 0xFF, from the golden E2M1
+    grid / torch's E4M3 decoding (nibble 2j low, 2j + 1 high)."""
+    rng = np.random.default_rng(5)
+    rows, cols = 9, 256
+    scales = rng.integers(0, 255, size=(rows, cols // 32)).astype(np.uint8)
+    scales[3, 2] = 0xFF
+    if elem == O.E2M1:
+        codes = rng.integers(0, 256, size=(rows, cols // 2), dtype=np.uint8)
+        c = _unpack(codes, cols)
+        grid = np.concatenate([E2M1_GRID, -E2M1_GRID])
+        val = grid[c]
+    else:
+        codes = rng.integers(0, 256, size=(rows, cols), dtype=np.uint8)
+        codes[(codes & 0x7F) == 0x7F] = 0x40
+        val = torch.from_numpy(codes).view(torch.float8_e4m3fn).to(torch.float64).numpy()
+    ref = val * np.ldexp(1.0, np.repeat(scales.astype(np.int64) - 127, 32, axis=1))
+    ref[np.repeat(scales == 0xFF, 32, axis=1)] = np.nan
+    got = O.dequantize_mx(codes, scales, cols, elem)
+    np.testing.assert_array_equal(np.isnan(got), np.isnan(ref))
+    ok = ~np.isnan(ref)
+    np.testing.assert_array_equal(got[ok], ref[ok])
+    np.testing.assert_array_equal(np.signbit(got[ok]), np.signbit(ref[ok]))
+
+
+def _mx_blocks_brute(x, emax, grid, sign_shift):
+    """Independent MX quantization of [rows, cols] fp64 values: per 32 columns, exponent from
+    frexp of the block maximum, argmin-distance grid search with ties to the even index."""
+    rows, cols = x.shape
+    xb = x.reshape(rows, cols // 32, 32)
+    amax = np.abs(xb).max(axis=2, keepdims=True)
+    _, ex = np.frexp(amax)
+    e = np.clip(np.where(amax == 0, -127, ex - 1 - emax), -127, 127)
+    q = np.ldexp(np.abs(xb), -e).reshape(-1)
+    idx = _nearest_even(q, grid).reshape(xb.shape)
+    codes = idx | (np.signbit(xb).astype(np.int64) << sign_shift)
+    return codes.reshape(rows, cols).astype(np.uint8), (e[..., 0] + 127).astype(np.uint8)
+
+
+@pytest.mark.parametrize("elem", [O.E2M1, O.E4M3])
+def test_quantize_mx_f32_and_f64_entry_points(elem):
+    """mxr_quantize_mx_f32 (the re-quantization of an fp32 intermediate) and mxr_quantize_mx_f64
+    on values that are not BF16-representable, against the independent block brute force; on
+    BF16-representable values all three entry points agree."""
+    rng = np.random.default_rng(9)
+    x32 = (rng.standard_normal((12, 128)) * np.exp(rng.uniform(-6, 6, (12, 1)))).astype(np.float32)
+    x32[2, :32] = 0.0
+    x32[4, 40] = -0.0
+    emax, grid, sh = (2, E2M1_GRID, 3) if elem == O.E2M1 else (8, E4M3_GRID, 7)
+    ref_c, ref_s = _mx_blocks_brute(x32.astype(np.float64), emax, grid, sh)
+    for fn, arg in ((O.quantize_mx_f32, x32), (O.quantize_mx_f64, x32.astype(np.float64))):
+        c, s = fn(arg, elem)
+        np.testing.assert_array_equal(s, ref_s)
+        np.testing.assert_array_equal(_unpack(c, 128) if elem == O.E2M1 else c, ref_c)
+    bits = synth.bits16(synth.to_bf16(x32))
+    cb, sb = O.quantize_mx_bf16(bits, elem)
+    c32, s32 = O.quantize_mx_f32(O.bf16_values(bits).astype(np.float32), elem)
+    np.testing.assert_array_equal(cb, c32)
+    np.testing.assert_array_equal(sb, s32)
+
+
+def test_bf16_rne_array_matches_torch():
+    rng = np.random.default_rng(3)
+    f = np.concatenate([rng.standard_normal(4000), rng.standard_normal(200) * 1e-39]).astype(np.float32)
+    ref = torch.from_numpy(f).to(torch.bfloat16).view(torch.int16).numpy().view(np.uint16)
+    np.testing.assert_array_equal(O.bf16_rne_array(f.astype(np.float64)), ref)
