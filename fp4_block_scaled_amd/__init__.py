@@ -355,13 +355,67 @@ def _alloc_out(M: int, N: int, epi: int, out_dtype, device):
         return empty_qmatrix(M, N, MXFP4, device)
     if epi == EPI_BIAS_GELU_QUANT_MXFP4_TILED:
         return empty_qmatrix(M, N, MXFP4, device, layout=TILED)
+    if out_dtype not in (torch.bfloat16, torch.float32):
+        raise MxError(f"out_dtype must be torch.bfloat16 or torch.float32, got {out_dtype}")
     return torch.empty((M, N), dtype=out_dtype, device=device)
 
 
-def _out_args(out, epi, out_dtype):
+def _check_out(out, M: int, N: int, epi: int):
+    """Shape, dtype and layout of a caller-supplied output (before any launch)."""
+    if epi in (EPI_BIAS_GELU_QUANT_MXFP4, EPI_BIAS_GELU_QUANT_MXFP4_TILED):
+        if not isinstance(out, QMatrix):
+            raise MxError("the re-quantizing epilogues write a QMatrix")
+        layout = TILED if epi == EPI_BIAS_GELU_QUANT_MXFP4_TILED else ROW_MAJOR
+        if out.fmt != MXFP4 or out.layout != layout or out.rows != M or out.cols != N:
+            raise MxError(f"out must be an MXFP4 {M} x {N} QMatrix in the "
+                          f"{'tiled' if layout == TILED else 'row-major'} layout")
+        for t, name in ((out.codes, "out.codes"), (out.scales, "out.scales")):
+            _need_cuda(t, name, torch.uint8)
+            if not t.is_contiguous():
+                raise MxError(f"{name} must be contiguous")
+        if layout == TILED:
+            cb, sb = tiled_bytes(M, N, MXFP4)
+        else:
+            cb, sb = M * (N // 2), M * (N // 32)
+        if out.codes.numel() < cb or out.scales.numel() < sb:
+            raise MxError(f"out holds {out.codes.numel()} code / {out.scales.numel()} scale bytes, "
+                          f"{cb} / {sb} needed")
+        return
+    if not isinstance(out, torch.Tensor):
+        raise MxError("out must be a tensor")
+    _need_cuda(out, "out")
+    if out.dtype not in (torch.bfloat16, torch.float32):
+        raise MxError(f"out must be bfloat16 or float32, got {out.dtype}")
+    if out.dim() != 2 or tuple(out.shape) != (M, N) or (M and out.stride(1) != 1) or \
+            (M > 1 and out.stride(0) < N):
+        raise MxError(f"out must be a {M} x {N} matrix with unit column stride, got "
+                      f"{tuple(out.shape)} / strides {tuple(out.stride())}")
+
+
+def _check_bias(bias, N: int):
+    if bias is None:
+        return
+    _need_cuda(bias, "bias", torch.float16)
+    if bias.dim() != 1 or bias.shape[0] != N or not bias.is_contiguous():
+        raise MxError(f"bias must be a contiguous float16 vector of length {N}")
+
+
+def _check_lowrank(lr: LowRank, K: int, N: int):
+    d, u = lr.down_t, lr.up_t
+    for t, name in ((d, "down_t"), (u, "up_t")):
+        _need_cuda(t, f"lowrank.{name}", torch.bfloat16)
+        if t.dim() != 2 or not t.is_contiguous():
+            raise MxError(f"lowrank.{name} must be a contiguous 2-D tensor")
+    r = d.shape[0]
+    if tuple(d.shape) != (r, K) or tuple(u.shape) != (N, r):
+        raise MxError(f"lowrank factors must be down_t [rank, K={K}] and up_t [N={N}, rank], got "
+                      f"{tuple(d.shape)} and {tuple(u.shape)}")
+
+
+def _out_args(out, epi):
     if epi in (EPI_BIAS_GELU_QUANT_MXFP4, EPI_BIAS_GELU_QUANT_MXFP4_TILED):
         return _ptr(out.codes), out.cols, _ptr(out.scales), OUT_BF16
-    od = OUT_F32 if out_dtype == torch.float32 else OUT_BF16
+    od = OUT_F32 if out.dtype == torch.float32 else OUT_BF16
     return _ptr(out), (_ld(out) if out.shape[0] else out.shape[1]), None, od
 
 
@@ -377,20 +431,27 @@ def linear(a: torch.Tensor, w: QMatrix, bias: Optional[torch.Tensor] = None, act
     _need_cuda(a, "a", torch.bfloat16)
     if a.dim() != 2 or a.stride(1) != 1:
         raise MxError("a must be 2-D with unit column stride")
-    if bias is not None:
-        _need_cuda(bias, "bias", torch.float16)
     M, K = a.shape
+    N = w.rows
+    _check_bias(bias, N)
     if out is None:
-        out = _alloc_out(M, w.rows, epi, out_dtype, a.device)
+        out = _alloc_out(M, N, epi, out_dtype, a.device)
+    _check_out(out, M, N, epi)
     rank = lowrank.rank if lowrank is not None else 0
+    if lowrank is not None:
+        _check_lowrank(lowrank, K, N)
     need = linear_workspace_bytes(M, K, act_fmt, rank) if M else 0
     if workspace is None:
         workspace = torch.empty(max(need, 1), dtype=torch.uint8, device=a.device)
+    else:
+        _need_cuda(workspace, "workspace", torch.uint8)
+        if not workspace.is_contiguous():
+            raise MxError("workspace must be contiguous")
     wc = w._c()
     lr = None
     if lowrank is not None:
         lr = ctypes.byref(_LowRank(lowrank.down_t.data_ptr(), lowrank.up_t.data_ptr(), rank))
-    optr, ld, sptr, od = _out_args(out, epi, out_dtype)
+    optr, ld, sptr, od = _out_args(out, epi)
     _check(lib().mx_linear(_ptr(a), M, K, _ld(a) if M else K, act_fmt, act_global_scale, ctypes.byref(wc),
                            _ptr(bias), lr, epi, od, optr, ld, sptr, _ptr(workspace),
                            workspace.numel(), _stream()))
@@ -401,12 +462,12 @@ def linear_q(a: QMatrix, w: QMatrix, bias: Optional[torch.Tensor] = None, epilog
              out_dtype=torch.bfloat16, out=None):
     """The same GEMM and epilogues on a pre-quantized activation QMatrix [M, K]."""
     epi = _epi(epilogue)
-    if bias is not None:
-        _need_cuda(bias, "bias", torch.float16)
+    _check_bias(bias, w.rows)
     if out is None:
         out = _alloc_out(a.rows, w.rows, epi, out_dtype, a.codes.device)
+    _check_out(out, a.rows, w.rows, epi)
     ac, wc = a._c(), w._c()
-    optr, ld, sptr, od = _out_args(out, epi, out_dtype)
+    optr, ld, sptr, od = _out_args(out, epi)
     _check(lib().mx_linear_q(ctypes.byref(ac), ctypes.byref(wc), _ptr(bias), epi, od, optr, ld,
                              sptr, _stream()))
     return out

@@ -142,6 +142,54 @@ def test_validation_failure_writes_nothing(mx):
     assert torch.all(out == 3.0)
 
 
+def test_binding_rejects_bad_out_bias_and_lowrank(mx):
+    """linear / linear_q check out (shape, dtype, layout), bias (length, dtype, contiguity) and
+    the low-rank factors (dtype, shapes, contiguity) on the host and raise before any launch: the
+    sentinel output stays untouched."""
+    M, K, N = 64, 256, 128
+    a = to_dev_bf16(activation_bits(M, K, seed_base=13000))
+    wq = _quant_w(mx, weight_bits(N, K, seed=13100))
+    aq = mx.quantize(a, "mxfp4")
+    sentinel = torch.full((M, N), 7.0, dtype=torch.float32, device="cuda")
+    bias = torch.zeros(N, dtype=torch.float16, device="cuda")
+    down = torch.zeros((32, K), dtype=torch.bfloat16, device="cuda")
+    up = torch.zeros((N, 32), dtype=torch.bfloat16, device="cuda")
+    bad_calls = [
+        lambda: mx.linear(a, wq, out=torch.empty((M, N - 8), dtype=torch.float32, device="cuda")),
+        lambda: mx.linear(a, wq, out=torch.empty((M + 1, N), dtype=torch.float32, device="cuda")),
+        lambda: mx.linear(a, wq, out=torch.empty((M, N), dtype=torch.float16, device="cuda")),
+        lambda: mx.linear(a, wq, out=torch.empty((N, M), dtype=torch.float32, device="cuda").t()),
+        lambda: mx.linear(a, wq, out=torch.empty((M, N), dtype=torch.float32)),
+        lambda: mx.linear(a, wq, bias=torch.zeros(N - 1, dtype=torch.float16, device="cuda"), out=sentinel),
+        lambda: mx.linear(a, wq, bias=torch.zeros(N, dtype=torch.float32, device="cuda"), out=sentinel),
+        lambda: mx.linear(a, wq, bias=torch.zeros(2 * N, dtype=torch.float16, device="cuda")[::2], out=sentinel),
+        lambda: mx.linear(a, wq, lowrank=mx.LowRank(down[:, : K - 32], up), out=sentinel),
+        lambda: mx.linear(a, wq, lowrank=mx.LowRank(down, up[: N - 1]), out=sentinel),
+        lambda: mx.linear(a, wq, lowrank=mx.LowRank(down, torch.zeros((N, 16), dtype=torch.bfloat16,
+                                                                       device="cuda")), out=sentinel),
+        lambda: mx.linear(a, wq, lowrank=mx.LowRank(down.float(), up), out=sentinel),
+        lambda: mx.linear(a, wq, lowrank=mx.LowRank(down, torch.zeros((32, N), dtype=torch.bfloat16,
+                                                                       device="cuda").t()), out=sentinel),
+        lambda: mx.linear(a, wq, epilogue="bias_gelu_quant_mxfp4", out=sentinel),
+        lambda: mx.linear(a, wq, epilogue="bias_gelu_quant_mxfp4_tiled", out=mx.empty_qmatrix(M, N, "mxfp4")),
+        lambda: mx.linear(a, wq, epilogue="bias_gelu_quant_mxfp4", out=mx.empty_qmatrix(M, N // 2, "mxfp4")),
+        lambda: mx.linear(a, wq, out_dtype=torch.float16),
+        lambda: mx.linear_q(aq, wq, out=torch.empty((M, N // 2), dtype=torch.float32, device="cuda")),
+        lambda: mx.linear_q(aq, wq, bias=torch.zeros(N + 1, dtype=torch.float16, device="cuda"), out=sentinel),
+    ]
+    for i, call in enumerate(bad_calls):
+        with pytest.raises(mx.MxError):
+            call()
+    torch.cuda.synchronize()
+    assert torch.all(sentinel == 7.0)
+    # the output type follows the tensor passed as out, whatever out_dtype says
+    y32 = torch.empty((M, N), dtype=torch.float32, device="cuda")
+    mx.linear(a, wq, bias, out=y32)
+    y16 = mx.linear(a, wq, bias)
+    torch.cuda.synchronize()
+    np.testing.assert_array_equal(dev_bits16(y16), bf16_rne_of_f32(y32.cpu().numpy()))
+
+
 @pytest.mark.parametrize("act", ["mxfp4", "mxfp8"])
 @pytest.mark.parametrize("M,K,N", [(300, 1024, 640), (260, 384, 200), (513, 768, 1024)])
 def test_tiled_operands_give_identical_results(mx, M, K, N, act):
@@ -197,6 +245,15 @@ def _lowrank_case(mx, M, K, N, R, act, bias, w_fmt="mxfp4"):
 def test_lowrank_branch_vs_oracle(mx, act, R):
     y, y_ref, abs_sum, extra = _lowrank_case(mx, 200, 768, 320, R, act, bias=(R == 32))
     assert_within(y.cpu().numpy(), y_ref, abs_sum, extra, what=f"low-rank {act} R={R}")
+
+
+@pytest.mark.parametrize("act", ["mxfp8", "mxfp4"])
+@pytest.mark.parametrize("M,K,N,R", [(150, 288, 192, 32), (97, 352, 100, 16), (70, 160, 64, 48)])
+def test_lowrank_branch_k_not_multiple_of_128(mx, act, M, K, N, R):
+    """K % 128 != 0: the register-staged GEMM with its low-rank pass, and the low-rank down
+    projection's partial last 64-element chunk."""
+    y, y_ref, abs_sum, extra = _lowrank_case(mx, M, K, N, R, act, bias=(R != 16))
+    assert_within(y.cpu().numpy(), y_ref, abs_sum, extra, what=f"low-rank {act} {M}x{K}x{N} R={R}")
 
 
 # ---------------------------------------------------------------------------------------------
@@ -374,7 +431,10 @@ def test_nvfp4_linear_vs_oracle(mx, M, K, N):
 # ---------------------------------------------------------------------------------------------
 # full workload sizes, in the launch configuration the benchmark times (sampled rows)
 # ---------------------------------------------------------------------------------------------
-def _full_mx(mx, wl_name, act, nsample=192, w_fmt="mxfp4"):
+FULL_SAMPLE = 1024  # seeded rows per full-size case, plus the first 32 and the last 96 (the M-tail)
+
+
+def _full_mx(mx, wl_name, act, nsample=FULL_SAMPLE, w_fmt="mxfp4"):
     wl = synth.WORKLOADS[wl_name]
     a_bits = synth.bits16(synth.to_bf16(wl.activation()))
     w_bits = synth.bits16(synth.to_bf16(wl.weight()))
@@ -413,10 +473,12 @@ def test_full_size_w8a8(mx):
     print(f"max err/tol {r:.3f}")
 
 
-def test_full_size_w4a8_with_lowrank_branch(mx):
-    """The W4A8 SVDQuant workload as the benchmark runs it: MXFP8 activations, prepared MXFP4
-    weight, rank-32 low-rank branch (no bias), sampled rows against the oracle."""
-    wl = synth.WORKLOADS["wan_ti2v5b_w4a8_4290x3072x3072"]
+@pytest.mark.parametrize("name", ["wan_ti2v5b_w4a8_4290x3072x3072", "wan_ti2v5b_w4a8_4290x3072x14336"])
+def test_full_size_w4a8_with_lowrank_branch(mx, name):
+    """The W4A8 SVDQuant workloads as the benchmark runs them (N = 3072 and 14336): MXFP8
+    activations, prepared MXFP4 weight, rank-32 low-rank branch (no bias), sampled rows against
+    the oracle."""
+    wl = synth.WORKLOADS[name]
     a_bits = synth.bits16(synth.to_bf16(wl.activation()))
     w_bits = synth.bits16(synth.to_bf16(wl.weight()))
     down = synth.bits16(synth.to_bf16(wl.lora_down()))
@@ -425,14 +487,14 @@ def test_full_size_w4a8_with_lowrank_branch(mx):
     lr = mx.LowRank(to_dev_bf16(np.ascontiguousarray(down.T)), to_dev_bf16(np.ascontiguousarray(up.T)))
     y = mx.linear(to_dev_bf16(a_bits), wq, None, act_fmt="mxfp8", lowrank=lr, out_dtype=torch.float32)
     torch.cuda.synchronize()
-    rows = sample_rows(wl.M, 256)
+    rows = sample_rows(wl.M, FULL_SAMPLE)
     ys = y[torch.from_numpy(rows).cuda()].cpu().numpy()
     ac, as_ = O.quantize_mx_bf16(a_bits[rows], O.E4M3)
     wc, ws = O.quantize_mx_bf16(w_bits)
     y_ref, abs_sum = O.linear_ref_mx(ac, as_, O.E4M3, wc, ws, wl.K, None)
     u_bits, lr_ref, lr_abs = O.lowrank(np.ascontiguousarray(a_bits[rows]), down, up)
     flip = (2.0 ** -8) * (np.abs(O.bf16_values(u_bits)) @ np.abs(O.bf16_values(up)))
-    assert_within(ys, y_ref + lr_ref, abs_sum, 2e-3 * lr_abs + flip, what="W4A8 + low-rank, full size")
+    assert_within(ys, y_ref + lr_ref, abs_sum, 2e-3 * lr_abs + flip, what=f"W4A8 + low-rank, {name}")
 
 
 def test_full_size_ffn_pair(mx):
@@ -446,7 +508,7 @@ def test_full_size_ffn_pair(mx):
     b_bits, b2_bits = f16_bits(wl.bias()), f16_bits(wl.bias2())
     a = to_dev_bf16(a_bits)
     wq, w2q = mx.relayout(_quant_w(mx, w_bits)), mx.relayout(_quant_w(mx, w2_bits))
-    rows = sample_rows(wl.M, 96)
+    rows = sample_rows(wl.M, FULL_SAMPLE)
     idx = torch.from_numpy(rows).cuda()
     h32 = mx.linear(a, wq, to_dev_f16(b_bits), epilogue="bias_gelu", out_dtype=torch.float32)
     torch.cuda.synchronize()
@@ -490,7 +552,7 @@ def test_full_size_nvfp4(mx):
     y = mx.linear(to_dev_bf16(a_bits), wq, to_dev_f16(b_bits), act_fmt="nvfp4",
                   act_global_scale=sg_a, out_dtype=torch.float32)
     torch.cuda.synchronize()
-    rows = sample_rows(wl.M, 96)
+    rows = sample_rows(wl.M, FULL_SAMPLE)
     ys = y[torch.from_numpy(rows).cuda()].cpu().numpy()
     del y
     assert sg_a == O.nv_global_scale(wl.act_amax_static)
