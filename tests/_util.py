@@ -101,3 +101,17 @@ def tile_mx(codes: np.ndarray, scales: np.ndarray, rows: int, cols: int, fp8: bo
             sb = ((r // 64) * nkc + kb) * 256 + (r % 64) * 4
             out_s[sb: sb + 4] = s[r, 4 * kb: 4 * kb + 4]
     return out_c, out_s
+
+
+def split_exact(v: float, nterms: int = 3):
+    """v as a sum of at most `nterms` values each of the form +-2^a or +-1.5 * 2^a (a in
+    [-6, 6]): values that MXFP4 holds exactly when each sits alone in its 32-element block
+    (an E2M1 code 4 or 6 times a power-of-two scale).  Padded with zeros."""
+    import itertools
+    from fractions import Fraction
+    single = sorted({s * m * 2.0 ** e for s in (1, -1) for m in (1, 1.5) for e in range(-6, 7)})
+    for n in range(1, nterms + 1):
+        for t in itertools.combinations_with_replacement(single, n):
+            if sum(Fraction(x) for x in t) == Fraction(v):
+                return list(t) + [0.0] * (nterms - n)
+    raise ValueError(f"{v} needs more than {nterms} terms")

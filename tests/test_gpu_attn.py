@@ -28,7 +28,7 @@ import torch
 
 import oracle as O
 from fp4_block_scaled_amd import synth
-from _util import dev_bits16, sample_rows, to_dev_bf16
+from _util import bf16_rne_of_f32, dev_bits16, sample_rows, split_exact, to_dev_bf16
 
 pytestmark = pytest.mark.gpu
 
@@ -138,6 +138,57 @@ def test_attention_vs_oracle(mx, BH, S, sigma, scale):
     _compare(o.cpu().numpy().reshape(BH * S, D), ref, bnd, ab, S, f"attention BH={BH} S={S}")
 
 
+# Scores of 128 key slots (two blocks of 64): groups 1 and 3 sit 2^24 and more below their
+# block's maximum, and their V values are 2^24 larger than those of groups 0 and 2, so their
+# products carry most of the output.  Keys 120..127 are past S_kv (masked).
+_GS = np.full(128, -6.0)
+_GS[:16] = [0, -0.5, -1, -1.5, -2, -3, -4, -6, -8, -0.25, -0.75, -2.5, -3.5, -5, -7, -10]
+_GS[32:48] = [-24, -24.5, -25, -26, -27, -28, -30, -32, -36, -24.25, -25.5, -29, -33, -40, -26.5, -27.5]
+_GS[48:64] = -31.0
+_GS[64:80] = [-0.5, -1, -1.5, -2, -3, -0.25, -0.75, -4, -5, -6, -2.5, -3.5, -7, -9, -12, -16]
+_GS[96:120] = -27.0
+_GS[96:104] = [-26, -25, -30, -24.5, -33, -28, -24.75, -36]
+
+
+def test_probability_groups_of_32_keys(mx):
+    """The probabilities are quantized to MXFP8 in groups of 32 keys, each group with its own
+    scale.  Scores are exact (Q and K hold +-2^a or +-1.5 * 2^a alone in their 32-element blocks,
+    softmax_scale = ln 2 so that c = 1), groups 1 and 3 lie 2^24 and more below their 64-key
+    block's maximum with V 2^24 larger and of one sign: a scale per 64 keys (or one shared by the
+    wrong groups) would zero those probabilities and remove most of the output.  F32 out against
+    the oracle; and the oracle without groups 1 and 3 lies outside the tolerance everywhere, so
+    the test can fail."""
+    BH, Sq, Skv = 1, 40, 120
+    q = np.zeros((Sq, D), dtype=np.float32)
+    q[:, [0, 32, 64]] = 1.0
+    k = np.zeros((Skv, D), dtype=np.float32)
+    for j in range(Skv):
+        k[j, [0, 32, 64]] = split_exact(float(_GS[j]))
+    v = synth.normal_f32(37000, (Skv, D), 1.0)
+    far = np.zeros(Skv, dtype=bool)
+    far[32:64] = far[96:] = True
+    v[far] = np.abs(v[far]) * 2.0 ** 24  # one sign: the far products add up
+    q_bits, k_bits, v_bits = (synth.bits16(synth.to_bf16(x)) for x in (q, k, v))
+    # c = softmax_scale * log2(e) is exactly 1 on both sides: the oracle divides ln 2 by ln 2
+    # in fp64, the kernel rounds fp32(ln 2) * log2(e) to binary32, which is 1.0
+    scale = float(np.log(2.0))
+    qc, qs = O.quantize_mx_bf16(q_bits)
+    kc, ks = O.quantize_mx_bf16(k_bits)
+    # the scores are exact: the quantized Q and K hold the values given above
+    assert np.array_equal(O.dequantize_mx(kc, ks, D)[:, [0, 32, 64]].sum(axis=1), _GS[:Skv])
+    vtc, vts = O.quantize_vt_mx8(v_bits, BH, Skv, D, KVB)
+    o = mx.attention(mx.quantize(to_dev_bf16(q_bits), "mxfp4"), mx.quantize(to_dev_bf16(k_bits), "mxfp4"),
+                     mx.quantize_vt(to_dev_bf16(v_bits).view(BH, Skv, D)), BH, softmax_scale=scale,
+                     out_dtype=torch.float32)
+    torch.cuda.synchronize()
+    ref, bnd, ab = O.attention_mx(qc, qs, kc, ks, vtc, vts, BH, Sq, D, KVB, scale, S_kv=Skv)
+    _compare(o.cpu().numpy().reshape(Sq, D), ref, bnd, ab, Skv, "32-key probability groups", flip_frac=0.05)
+    vtc_near = vtc.copy()
+    vtc_near[:, :, far.nonzero()[0]] = 0  # the far groups' products removed
+    ablated, _, _ = O.attention_mx(qc, qs, kc, ks, vtc_near, vts, BH, Sq, D, KVB, scale, S_kv=Skv)
+    assert np.all(np.abs(ablated - ref) > _tol(bnd, ab, Skv))
+
+
 def test_single_key_is_v_exactly(mx):
     """With one key every probability is 1 (quantized exactly), so out = v^ for every query."""
     BH, S = 2, 1
@@ -175,9 +226,10 @@ def test_attention_bf16_out_and_shd_layout(mx):
 @pytest.mark.parametrize("name", ["wan_a14b_attn_mx_75600x40x128", "wan_ti2v5b_attn_mx_4290x24x128"])
 def test_full_size_wan_attention(mx, name):
     """Full Wan2.2 self-attention shapes (A14B at 720p: 75600 tokens x 40 heads, as the benchmark
-    runs it; TI2V-5B: 4290 tokens x 24 heads), in the projections' layout with BF16 out: sampled
-    queries of three heads (including the last, partial query block; the last key block holds
-    16 / 2 keys) against the oracle, and the V^T codes of those heads bit for bit."""
+    runs it; TI2V-5B: 4290 tokens x 24 heads), in the projections' layout: sampled queries of
+    three heads (including the last, partial query block; the last key block holds 16 / 2 keys)
+    in F32 against the oracle, the BF16 output as the RNE of the F32 one, and the V^T codes of
+    those heads bit for bit."""
     wl = synth.WORKLOADS[name]
     S, H = wl.M, wl.extra["heads"]
     q, k, v = wl.qkv()
@@ -186,7 +238,8 @@ def test_full_size_wan_attention(mx, name):
     qd, kd, vd = (to_dev_bf16(b) for b in bits)
     qg, kg = mx.quantize(qd, "mxfp4"), mx.quantize(kd, "mxfp4")
     vt = mx.quantize_vt(vd.view(S, H, D).transpose(0, 1))
-    o = mx.attention(qg, kg, vt, heads=H, layout="shd")
+    o = mx.attention(qg, kg, vt, heads=H, layout="shd", out_dtype=torch.float32)
+    o16 = mx.attention(qg, kg, vt, heads=H, layout="shd")
     torch.cuda.synchronize()
     rows = np.unique(np.concatenate([sample_rows(S, 24), [0, S - 80, S - 1]]))
     for h in (0, H // 2 - 3, H - 1):
@@ -195,8 +248,11 @@ def test_full_size_wan_attention(mx, name):
         bc, bs = _blocked(vtc, vts)
         assert np.array_equal(vt[0][h].cpu().numpy(), bc[0]) and np.array_equal(vt[1][h].cpu().numpy(), bs[0])
         ref, bnd, ab = O.attention_mx(qc, qs, kc, ks, vtc, vts, 1, S, D, KVB, D ** -0.5, qrows=rows)
-        got = O.bf16_values(dev_bits16(o[torch.from_numpy(rows).cuda(), h * D:(h + 1) * D]))
-        _compare(got, ref, bnd, ab, S, f"full-size head {h}", extra=2.0 ** -8 * np.abs(ref), flip_frac=0.05)
+        idx = torch.from_numpy(rows).cuda()
+        got = o[idx, h * D:(h + 1) * D].cpu().numpy()
+        _compare(got, ref, bnd, ab, S, f"full-size head {h}", flip_frac=0.05)
+        # the BF16 output is the RNE of the F32 one
+        np.testing.assert_array_equal(dev_bits16(o16[idx, h * D:(h + 1) * D]), bf16_rne_of_f32(got))
 
 
 def test_head_and_row_strides_through_the_c_abi(mx):
@@ -251,7 +307,7 @@ def test_cross_attention_vs_oracle(mx, BH, Sq, Skv, sigma):
 @pytest.mark.parametrize("name", ["wan_a14b_attn_mx_75600x40x128", "wan_ti2v5b_attn_mx_4290x24x128"])
 def test_full_size_wan_cross_attention(mx, name):
     """The workload's queries against 512 context tokens (keys and values N(0,1), seeded), in the
-    projections' layout with BF16 out: sampled queries of three heads against the oracle."""
+    projections' layout with F32 out: sampled queries of three heads against the oracle."""
     wl = synth.WORKLOADS[name]
     Sq, H, Skv = wl.M, wl.extra["heads"], 512
     q_bits = synth.bits16(synth.to_bf16(wl.qkv(Sq)[0]))
@@ -259,7 +315,7 @@ def test_full_size_wan_cross_attention(mx, name):
     v_bits = _bits(wl.seed_base + 22, (Skv, H * D), 1.0)
     vt = mx.quantize_vt(to_dev_bf16(v_bits).view(Skv, H, D).transpose(0, 1))
     o = mx.attention(mx.quantize(to_dev_bf16(q_bits), "mxfp4"), mx.quantize(to_dev_bf16(k_bits), "mxfp4"),
-                     vt, heads=H, layout="shd")
+                     vt, heads=H, layout="shd", out_dtype=torch.float32)
     torch.cuda.synchronize()
     rows = np.unique(np.concatenate([sample_rows(Sq, 24), [0, Sq - 1]]))
     for h in (0, H // 2 - 3, H - 1):
@@ -270,5 +326,5 @@ def test_full_size_wan_cross_attention(mx, name):
         kc, ks = O.quantize_mx_bf16(hk)
         vtc, vts = O.quantize_vt_mx8(hv, 1, Skv, D, KVB)
         ref, bnd, ab = O.attention_mx(qc, qs, kc, ks, vtc, vts, 1, Sq, D, KVB, D ** -0.5, qrows=rows, S_kv=Skv)
-        got = O.bf16_values(dev_bits16(o[torch.from_numpy(rows).cuda(), h * D:(h + 1) * D]))
-        _compare(got, ref, bnd, ab, Skv, f"full-size cross head {h}", extra=2.0 ** -8 * np.abs(ref), flip_frac=0.05)
+        got = o[torch.from_numpy(rows).cuda(), h * D:(h + 1) * D].cpu().numpy()
+        _compare(got, ref, bnd, ab, Skv, f"full-size cross head {h}", flip_frac=0.05)

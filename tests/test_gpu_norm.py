@@ -91,13 +91,25 @@ def test_norm_quantize_vs_oracle(mx, fmt, elem):
     rows, cols = 200, 5120
     x_bits = activation_bits(rows, cols, seed_base=23000, factor=30.0)
     host, dev = _vecs(cols, 23100, ("scale", "shift"))
-    q = mx.norm_quantize(to_dev_bf16(x_bits), EPS, fmt=fmt, layout="row_major", **dev)
+    x = to_dev_bf16(x_bits)
+    q = mx.norm_quantize(x, EPS, fmt=fmt, layout="row_major", **dev)
+    y = mx.norm(x, EPS, **dev)
     torch.cuda.synchronize()
-    rc, rs = O.quantize_mx_bf16(O.bf16_rne_array(O.norm_modulate(x_bits, EPS, **host)), elem)
-    srate = float(np.mean(q.scales.cpu().numpy() != rs))
-    crate = float(np.mean(q.codes.cpu().numpy() != rc))
-    print(f"{fmt}: scale-byte mismatch rate {srate:.2e}, code-byte mismatch rate {crate:.2e}")
-    assert srate < 1e-3 and crate < 1e-2
+    h_ref = O.bf16_rne_array(O.norm_modulate(x_bits, EPS, **host))
+    rc, rs = O.quantize_mx_bf16(h_ref, elem)
+    gs = q.scales.cpu().numpy()
+    gc = q.codes.cpu().numpy().reshape(rows, cols // 32, -1)
+    # A code or scale byte of a 32-element group can only differ from the oracle's where the
+    # GPU's fp32 statistics round some BF16 element of h of that group to the other neighbour
+    # (the fused codes are exactly the quantizer's codes of the GPU's own BF16 h, tested below
+    # at full size): the groups with a mismatch are a subset of the groups with an h flip.
+    hflip = (dev_bits16(y) != h_ref).reshape(rows, cols // 32, 32).any(axis=2)
+    bad = (gs != rs) | (gc != rc.reshape(rows, cols // 32, -1)).any(axis=2)
+    hrate = float(np.mean(dev_bits16(y) != h_ref))
+    print(f"{fmt}: BF16 h flips {hrate:.2e}, groups with a code or scale mismatch {int(bad.sum())} "
+          f"of {bad.size}, groups with an h flip {int(hflip.sum())}")
+    assert not (bad & ~hflip).any()
+    assert hrate < 1e-4  # measured about 2e-5: fp32 statistics against fp64
 
 
 def test_constant_rows_are_bit_exact_and_tiled_padding_is_zero(mx):

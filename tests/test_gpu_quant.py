@@ -80,10 +80,15 @@ def test_mx_worked_blocks_on_gpu(mx, name, fmt, elem):
 
 
 def test_nv_worked_blocks_on_gpu(mx):
-    for b in json.load(open(os.path.join(GOLDEN, "nvfp4_worked_blocks.json")))["blocks"]:
-        bits = synth.bits16(torch.tensor(b["x"], dtype=torch.float64).to(torch.float32)
-                            .to(torch.bfloat16))
-        c, s = _gpu_quant(mx, bits[None, :], "nvfp4", 1.0)
+    g = json.load(open(os.path.join(GOLDEN, "nvfp4_worked_blocks.json")))
+    for b in g["blocks"]:
+        if "bits" in b:
+            bits = np.asarray(b["bits"], dtype=np.uint16)
+        else:
+            bits = synth.bits16(torch.tensor(b["x"], dtype=torch.float64).to(torch.float32)
+                                .to(torch.bfloat16))
+        sg = b.get("global_scale", g["global_scale"])
+        c, s = _gpu_quant(mx, bits[None, :], "nvfp4", sg)
         assert int(s[0, 0]) == b["scale"], b["name"]
         np.testing.assert_array_equal(unpack_fp4(c[0], 16), b["codes"], err_msg=b["name"])
 
