@@ -37,12 +37,20 @@ def _run(cmd, verbose):
     subprocess.run(cmd, check=True)
 
 
-def build_synth(verbose: bool = False) -> str:
+SYNTH_SAN_PATH = os.path.join(PKG, "synth", "libmxsynth_san.so")
+
+
+def build_synth(verbose: bool = False, sanitize: bool = False) -> str:
+    """The input generator; sanitize=True builds libmxsynth_san.so with AddressSanitizer and
+    UndefinedBehaviorSanitizer (selected by MXSYNTH_LIB, with libasan preloaded)."""
     src = os.path.join(PKG, "synth", "synth.c")
-    _run(["gcc", "-std=c11", "-O2", "-fopenmp", "-ffp-contract=off", "-Wall", "-shared", "-fPIC",
-          src, "-o", SYNTH_PATH + ".tmp", "-lm"], verbose)
-    os.replace(SYNTH_PATH + ".tmp", SYNTH_PATH)
-    return SYNTH_PATH
+    out = SYNTH_SAN_PATH if sanitize else SYNTH_PATH
+    san = ["-fsanitize=address,undefined", "-fno-sanitize-recover=undefined",
+           "-fno-omit-frame-pointer", "-g"] if sanitize else []
+    _run(["gcc", "-std=c11", "-O1" if sanitize else "-O2", "-fopenmp", "-ffp-contract=off", "-Wall",
+          "-shared", "-fPIC", *san, src, "-o", out + ".tmp", "-lm"], verbose)
+    os.replace(out + ".tmp", out)
+    return out
 
 
 def build_hip(verbose: bool = False, jobs: int = 8) -> str:

@@ -19,7 +19,8 @@ from dataclasses import dataclass, field
 import numpy as np
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
-_LIB_PATH = os.path.join(_HERE, "libmxsynth.so")
+# MXSYNTH_LIB selects another build of synth.c (the sanitizer build)
+_LIB_PATH = os.environ.get("MXSYNTH_LIB") or os.path.join(_HERE, "libmxsynth.so")
 _lib = None
 
 # tensor ids inside a config's seed space

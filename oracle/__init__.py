@@ -15,7 +15,8 @@ import os
 import numpy as np
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
-LIB_PATH = os.path.join(_HERE, "libmxref.so")
+# MXREF_LIB selects another build of mxref.c (the sanitizer build of oracle/build.py)
+LIB_PATH = os.environ.get("MXREF_LIB") or os.path.join(_HERE, "libmxref.so")
 E2M1, E4M3 = 0, 1
 
 _lib = None

@@ -8,11 +8,19 @@ import subprocess
 HERE = os.path.dirname(os.path.abspath(__file__))
 
 
-def build(verbose: bool = False) -> str:
+SANITIZE_FLAGS = ["-fsanitize=address,undefined", "-fno-sanitize-recover=undefined",
+                  "-fno-omit-frame-pointer", "-g"]
+SAN_LIB_PATH = os.path.join(HERE, "libmxref_san.so")
+
+
+def build(verbose: bool = False, sanitize: bool = False) -> str:
+    """Build libmxref.so; with sanitize=True, libmxref_san.so instrumented with AddressSanitizer
+    and UndefinedBehaviorSanitizer (loaded by setting MXREF_LIB, with libasan preloaded)."""
     src = os.path.join(HERE, "mxref.c")
-    out = os.path.join(HERE, "libmxref.so")
-    cmd = ["gcc", "-std=c11", "-O2", "-fopenmp", "-ffp-contract=off", "-fno-fast-math",
-           "-Wall", "-Wextra", "-shared", "-fPIC", src, "-o", out + ".tmp", "-lm"]
+    out = SAN_LIB_PATH if sanitize else os.path.join(HERE, "libmxref.so")
+    cmd = ["gcc", "-std=c11", "-O1" if sanitize else "-O2", "-fopenmp", "-ffp-contract=off",
+           "-fno-fast-math", "-Wall", "-Wextra", "-shared", "-fPIC",
+           *(SANITIZE_FLAGS if sanitize else []), src, "-o", out + ".tmp", "-lm"]
     if verbose:
         print(" ".join(cmd), flush=True)
     subprocess.run(cmd, check=True)
