@@ -158,7 +158,11 @@ mx_status mx_tiled_bytes(int64_t rows, int64_t cols, int32_t fmt, size_t* code_b
 mx_status mx_relayout(const mx_qmatrix* src, const mx_qmatrix* dst, void* stream);
 
 /*
- * mx_dequantize - BF16 values of a quantized matrix: y = code * 2^(scale - 127) for MX (exact),
+ * mx_dequantize - the values a quantized matrix stands for.  The MXFP4 model cards
+ * ("intel-ai/Wan2.2-I2V-A14B-Lightning-Diffusers-MXFP4-AutoRound", Quantization Details) store
+ * FP4 E2M1 codes with one E8M0 (power-of-two) scale per 32 elements; the NVFP4 card
+ * ("Wan2.2-T2V-A14B-Diffusers-NVFP4-AutoRound", Model Details) adds an FP8 E4M3 scale per 16
+ * and an FP32 global scale per tensor.  BF16 values: y = code * 2^(scale - 127) for MX (exact),
  * y = bf16_rne(code * sb * global_scale) for NVFP4 (one rounding of the exact product).  A NaN
  * scale byte gives NaN.  y: device BF16, rows x cols with leading dimension ld_y >= cols.
  * Row-major matrices only (mx_relayout converts a tiled one).
@@ -261,15 +265,25 @@ mx_status mx_attention(const uint8_t* q_codes, const uint8_t* q_scales, int64_t 
                        int64_t S_kv, int64_t D, float softmax_scale, int32_t out_dtype, void* out,
                        int64_t ld_o, int64_t hs_o, void* stream);
 
-/* Bytes of workspace mx_linear needs for an M x K activation in act_fmt (codes + scales of the
- * quantized activation -- in the tiled layout for the MX formats when K % 128 == 0 -- plus the
- * low-rank intermediate when rank > 0). */
+/* Bytes of workspace mx_linear needs for an M x K activation in act_fmt: the activation is
+ * quantized dynamically on every call ("intel-ai/Wan2.2-I2V-A14B-Lightning-Diffusers-MXFP4-AutoRound",
+ * Quantization Details: act_dynamic, activations quantized to MXFP4 at run time), so its codes
+ * and scales are staged here -- in the tiled layout for the MX formats when K % 128 == 0 -- plus
+ * the BF16 M x rank input of the low-rank branch when rank > 0 ("Wan2.2 W4A8 SVDQuant - NVIDIA
+ * (CUDA) artifacts", introduction).  Host-side arithmetic only; 0 for M <= 0. */
 size_t mx_linear_workspace_bytes(int64_t M, int64_t K, int32_t act_fmt, int32_t rank);
 
 /*
  * mx_linear - the quantized linear layer on a BF16 activation a (M x K, leading dimension ld_a):
  * quantize a dynamically to act_fmt (act_global_scale is the static NVFP4 activation global
- * scale), then y = dequant(a) . dequant(w)^T in fp32 accumulation, then the epilogue.
+ * scale), then y = dequant(a) . dequant(w)^T in fp32 accumulation, then the epilogue.  Sources:
+ * the W4A4 layer of "intel-ai/Wan2.2-I2V-A14B-Lightning-Diffusers-MXFP4-AutoRound" (Model
+ * Summary: an MXFP4 W4A4 linear kernel with a block-scaled matrix multiply; Quantization Details:
+ * dynamic MXFP4 activations, MXFP4 weights, F16 biases); the NVFP4 variant of
+ * "Wan2.2-T2V-A14B-Diffusers-NVFP4-AutoRound" (Model Details: real FP4 GEMMs, not an activation
+ * quantize-dequantize emulation, dynamic block scales under a static activation global scale);
+ * the W4A8 variant and its rank-32 BF16 branch of "Wan2.2 W4A8 SVDQuant - NVIDIA (CUDA)
+ * artifacts" (introduction).
  * Supported (act_fmt, w->fmt): (MXFP4, MXFP4) W4A4; (MXFP8, MXFP4) W4A8; (MXFP8, MXFP8) W8A8
  * (K % 128 == 0); (NVFP4, NVFP4).
  *  bias: device FP16 [N] or NULL.
@@ -300,8 +314,13 @@ mx_status mx_linear(const uint16_t* a, int64_t M, int64_t K, int64_t ld_a, int32
 
 /*
  * mx_linear_q - the same GEMM and epilogues on an already quantized activation a (M x K), e.g.
- * the MXFP4 output of a MX_EPI_BIAS_GELU_QUANT_MXFP4 call feeding the next linear.  No
- * workspace and no low-rank branch.  a and w may each be row-major or tiled (MX formats).
+ * the MXFP4 output of a MX_EPI_BIAS_GELU_QUANT_MXFP4 call feeding the next linear.  The
+ * quantized linears of "intel-ai/Wan2.2-I2V-A14B-Lightning-Diffusers-MXFP4-AutoRound"
+ * (Quantization Details, coverage list) include both layers of each block's feed-forward network,
+ * ffn.net.0.proj and ffn.net.2; the second consumes the first's GELU output, which this library
+ * re-quantizes in the first GEMM's epilogue (the pages do not say where that quantization
+ * happens).  No workspace and no low-rank branch.  a and w may each be row-major or tiled (MX
+ * formats).
  */
 mx_status mx_linear_q(const mx_qmatrix* a, const mx_qmatrix* w, const uint16_t* bias,
                       int32_t epilogue, int32_t out_dtype, void* out, int64_t ld_out,
