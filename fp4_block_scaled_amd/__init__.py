@@ -7,8 +7,9 @@ library is missing or no GPU is present the calls raise.
 The C ABI is declared in ``include/mxfp.h``; the functions here carry the same names:
 ``quantize``, ``dequantize``, ``absmax``, ``nvfp4_global_scale``, ``relayout``, ``tiled_bytes``,
 ``linear`` (dynamic
-activation quantization + block-scaled GEMM + epilogue), ``linear_q`` (pre-quantized
-activation) and ``linear_workspace_bytes``.
+activation quantization + block-scaled GEMM + epilogue), ``linear_noalloc`` (the same with the
+library's static workspace), ``linear_q`` (pre-quantized activation) and
+``linear_workspace_bytes``.
 """
 from __future__ import annotations
 
@@ -23,6 +24,7 @@ _HERE = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(_HERE, "libmxfp.so")
 
 MXFP4, MXFP8, NVFP4 = 0, 1, 2
+NOALLOC_SCRATCH_BYTES = 64 << 20  # MX_NOALLOC_SCRATCH_BYTES of include/mxfp.h
 ROW_MAJOR, TILED = 0, 1
 EPI_BIAS, EPI_BIAS_GELU, EPI_BIAS_GELU_QUANT_MXFP4, EPI_BIAS_GELU_QUANT_MXFP4_TILED = 0, 1, 2, 3
 OUT_BF16, OUT_F32 = 0, 1
@@ -77,13 +79,15 @@ def lib():
                                 ctypes.POINTER(_LowRank), I32, I32, P, I64, P, P, ctypes.c_size_t, P]
         L.mx_linear_q.argtypes = [ctypes.POINTER(_QMatrix), ctypes.POINTER(_QMatrix), P, I32, I32,
                                   P, I64, P, P]
+        L.mx_linear_noalloc.argtypes = [P, I64, I64, I64, I32, ctypes.c_float, ctypes.POINTER(_QMatrix),
+                                        P, ctypes.POINTER(_LowRank), I32, I32, P, I64, P, P]
         F = ctypes.c_float
         L.mx_norm.argtypes = [P, I64, I64, I64, F, P, P, P, P, P, I64, P]
         L.mx_norm_quantize.argtypes = [P, I64, I64, I64, F, P, P, P, P, I32, I32, P, P, P]
         L.mx_quantize_vt.argtypes = [P, I64, I64, I64, I64, I64, P, P, P]
         L.mx_attention.argtypes = [P, P, I64, I64, P, P, I64, I64, P, P, I64, I64, I64, I64, F, I32, P,
                                    I64, I64, P]
-        for f in ("mx_quantize", "mx_dequantize", "mx_absmax", "mx_linear", "mx_linear_q",
+        for f in ("mx_quantize", "mx_dequantize", "mx_absmax", "mx_linear", "mx_linear_q", "mx_linear_noalloc",
                   "mx_tiled_bytes", "mx_relayout", "mx_norm", "mx_norm_quantize",
                   "mx_quantize_vt", "mx_attention"):
             getattr(L, f).restype = ctypes.c_int
@@ -455,6 +459,34 @@ def linear(a: torch.Tensor, w: QMatrix, bias: Optional[torch.Tensor] = None, act
     _check(lib().mx_linear(_ptr(a), M, K, _ld(a) if M else K, act_fmt, act_global_scale, ctypes.byref(wc),
                            _ptr(bias), lr, epi, od, optr, ld, sptr, _ptr(workspace),
                            workspace.numel(), _stream()))
+    return out
+
+
+def linear_noalloc(a: torch.Tensor, w: QMatrix, bias: Optional[torch.Tensor] = None, act_fmt="mxfp4",
+                   act_global_scale: float = 1.0, lowrank: Optional[LowRank] = None, epilogue="bias",
+                   out_dtype=torch.bfloat16, out=None):
+    """linear() through mx_linear_noalloc: the library's static per-GPU workspace instead of a
+    caller one (for callers that cannot allocate; pass ``out`` to allocate nothing at all).  The
+    workspace must fit NOALLOC_SCRATCH_BYTES; calls that overlap on one GPU race on it."""
+    act_fmt, epi = _fmt(act_fmt), _epi(epilogue)
+    _need_cuda(a, "a", torch.bfloat16)
+    if a.dim() != 2 or a.stride(1) != 1:
+        raise MxError("a must be 2-D with unit column stride")
+    M, K = a.shape
+    N = w.rows
+    _check_bias(bias, N)
+    if out is None:
+        out = _alloc_out(M, N, epi, out_dtype, a.device)
+    _check_out(out, M, N, epi)
+    rank = lowrank.rank if lowrank is not None else 0
+    lr = None
+    if lowrank is not None:
+        _check_lowrank(lowrank, K, N)
+        lr = ctypes.byref(_LowRank(lowrank.down_t.data_ptr(), lowrank.up_t.data_ptr(), rank))
+    wc = w._c()
+    optr, ld, sptr, od = _out_args(out, epi)
+    _check(lib().mx_linear_noalloc(_ptr(a), M, K, _ld(a) if M else K, act_fmt, act_global_scale,
+                                   ctypes.byref(wc), _ptr(bias), lr, epi, od, optr, ld, sptr, _stream()))
     return out
 
 

@@ -5,6 +5,8 @@
 #include <stdio.h>
 #include <string.h>
 
+#include <mutex>
+
 #include "mx_internal.h"
 #include "mxfp.h"
 
@@ -388,12 +390,15 @@ static mx_status run_gemm(const uint8_t* a_codes, const uint8_t* a_scales, float
   return hip_status(e, "GEMM launch");
 }
 
-mx_status mx_linear(const uint16_t* a, int64_t M, int64_t K, int64_t ld_a, int32_t act_fmt,
-                    float act_global_scale, const mx_qmatrix* w, const uint16_t* bias,
-                    const mx_lowrank* lr, int32_t epilogue, int32_t out_dtype, void* out,
-                    int64_t ld_out, uint8_t* out_scales, void* workspace, size_t workspace_bytes,
-                    void* stream) {
-  g_err[0] = 0;
+}  // extern "C"
+
+namespace {
+
+// Arguments of mx_linear besides the workspace (shared with mx_linear_noalloc).
+mx_status check_linear(const uint16_t* a, int64_t M, int64_t K, int64_t ld_a, int32_t act_fmt,
+                       float act_global_scale, const mx_qmatrix* w, const uint16_t* bias,
+                       const mx_lowrank* lr, int32_t epilogue, int32_t out_dtype, void* out,
+                       int64_t ld_out, uint8_t* out_scales) {
   mx_status st = check_gemm_tail(act_fmt, M, K, w, bias, epilogue, out_dtype, out, ld_out, out_scales);
   if (st != MX_OK) return st;
   if (!a && M != 0) return fail(MX_ERR_NULL, "a is NULL");
@@ -402,20 +407,22 @@ mx_status mx_linear(const uint16_t* a, int64_t M, int64_t K, int64_t ld_a, int32
     return fail(MX_ERR_ALIGN, "a needs 16-byte alignment and ld_a %% 8 == 0");
   if (act_fmt == MX_FMT_NVFP4 && !finite_pos(act_global_scale))
     return fail(MX_ERR_SHAPE, "NVFP4 activation global scale must be finite and > 0");
-  const int32_t rank = lr ? lr->rank : 0;
   if (lr) {
     if (act_fmt == MX_FMT_NVFP4) return fail(MX_ERR_UNSUPPORTED, "low-rank branch needs an MX format");
     if (!lr->down || !lr->up) return fail(MX_ERR_NULL, "lr->down / lr->up is NULL");
-    if (rank < 1 || rank > 64 || rank % 16) return fail(MX_ERR_SHAPE, "rank must be 16, 32, 48 or 64");
+    if (lr->rank < 1 || lr->rank > 64 || lr->rank % 16) return fail(MX_ERR_SHAPE, "rank must be 16, 32, 48 or 64");
     if (!aligned(lr->down, 16) || !aligned(lr->up, 16)) return fail(MX_ERR_ALIGN, "low-rank factors need 16-byte alignment");
   }
-  if (M == 0) return MX_OK;
-  const size_t need = mx_linear_workspace_bytes(M, K, act_fmt, rank);
-  if (!workspace || workspace_bytes < need)
-    return fail(MX_ERR_WORKSPACE, "workspace of %zu bytes needed, %zu given", need, workspace_bytes);
-  if (!aligned(workspace, 256)) return fail(MX_ERR_ALIGN, "workspace needs 256-byte alignment");
+  return MX_OK;
+}
 
-  hipStream_t s = (hipStream_t)stream;
+// The launches of mx_linear on a checked argument set and a workspace of
+// mx_linear_workspace_bytes bytes (256-byte aligned).
+mx_status run_linear(const uint16_t* a, int64_t M, int64_t K, int64_t ld_a, int32_t act_fmt,
+                     float act_global_scale, const mx_qmatrix* w, const uint16_t* bias,
+                     const mx_lowrank* lr, int32_t epilogue, int32_t out_dtype, void* out,
+                     int64_t ld_out, uint8_t* out_scales, void* workspace, hipStream_t s) {
+  const int32_t rank = lr ? lr->rank : 0;
   Workspace ws = carve(workspace, M, K, act_fmt, rank);
   hipError_t e;
   const bool tiled = act_tiled(act_fmt, K);
@@ -440,6 +447,77 @@ mx_status mx_linear(const uint16_t* a, int64_t M, int64_t K, int64_t ld_a, int32
   }
   return run_gemm(ws.codes, ws.scales, act_global_scale, act_fmt, tiled, M, K, w, bias, ws.u, lr,
                   epilogue, out_dtype, out, ld_out, out_scales, s);
+}
+
+// ---------------------------------------------------------------------------------------------
+// The statically allocated workspace of mx_linear_noalloc: one copy per GPU, held until the
+// process ends.  In host code `scratch` names a host-side stand-in, not device memory: its
+// device address is taken once per device with hipGetSymbolAddress (with that device current)
+// and only that address is used.
+// ---------------------------------------------------------------------------------------------
+static __device__ __align__(256) uint8_t scratch[MX_NOALLOC_SCRATCH_BYTES];
+
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mutex;
+void* g_scratch_ptr[kMaxDevices];  // device address of `scratch` on each device, once taken
+
+mx_status scratch_address(void** ptr) {
+  int dev = -1;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return hip_status(e, "hipGetDevice");
+  if (dev < 0 || dev >= kMaxDevices) return fail(MX_ERR_HIP, "device index %d out of range", dev);
+  std::lock_guard<std::mutex> lock(g_scratch_mutex);
+  if (!g_scratch_ptr[dev]) {
+    void* p = nullptr;
+    e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    if (e != hipSuccess) return hip_status(e, "hipGetSymbolAddress(scratch)");
+    if (!p || !aligned(p, 256)) return fail(MX_ERR_HIP, "scratch symbol has no usable device address");
+    g_scratch_ptr[dev] = p;
+  }
+  *ptr = g_scratch_ptr[dev];
+  return MX_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+mx_status mx_linear(const uint16_t* a, int64_t M, int64_t K, int64_t ld_a, int32_t act_fmt,
+                    float act_global_scale, const mx_qmatrix* w, const uint16_t* bias,
+                    const mx_lowrank* lr, int32_t epilogue, int32_t out_dtype, void* out,
+                    int64_t ld_out, uint8_t* out_scales, void* workspace, size_t workspace_bytes,
+                    void* stream) {
+  g_err[0] = 0;
+  mx_status st = check_linear(a, M, K, ld_a, act_fmt, act_global_scale, w, bias, lr, epilogue, out_dtype,
+                              out, ld_out, out_scales);
+  if (st != MX_OK) return st;
+  if (M == 0) return MX_OK;
+  const size_t need = mx_linear_workspace_bytes(M, K, act_fmt, lr ? lr->rank : 0);
+  if (!workspace || workspace_bytes < need)
+    return fail(MX_ERR_WORKSPACE, "workspace of %zu bytes needed, %zu given", need, workspace_bytes);
+  if (!aligned(workspace, 256)) return fail(MX_ERR_ALIGN, "workspace needs 256-byte alignment");
+  return run_linear(a, M, K, ld_a, act_fmt, act_global_scale, w, bias, lr, epilogue, out_dtype, out,
+                    ld_out, out_scales, workspace, (hipStream_t)stream);
+}
+
+mx_status mx_linear_noalloc(const uint16_t* a, int64_t M, int64_t K, int64_t ld_a, int32_t act_fmt,
+                            float act_global_scale, const mx_qmatrix* w, const uint16_t* bias,
+                            const mx_lowrank* lr, int32_t epilogue, int32_t out_dtype, void* out,
+                            int64_t ld_out, uint8_t* out_scales, void* stream) {
+  g_err[0] = 0;
+  mx_status st = check_linear(a, M, K, ld_a, act_fmt, act_global_scale, w, bias, lr, epilogue, out_dtype,
+                              out, ld_out, out_scales);
+  if (st != MX_OK) return st;
+  if (M == 0) return MX_OK;
+  const size_t need = mx_linear_workspace_bytes(M, K, act_fmt, lr ? lr->rank : 0);
+  if (need > (size_t)MX_NOALLOC_SCRATCH_BYTES)
+    return fail(MX_ERR_WORKSPACE, "workspace of %zu bytes needed, the static scratch holds %zu", need,
+                (size_t)MX_NOALLOC_SCRATCH_BYTES);
+  void* ws = nullptr;
+  st = scratch_address(&ws);
+  if (st != MX_OK) return st;
+  return run_linear(a, M, K, ld_a, act_fmt, act_global_scale, w, bias, lr, epilogue, out_dtype, out,
+                    ld_out, out_scales, ws, (hipStream_t)stream);
 }
 
 mx_status mx_linear_q(const mx_qmatrix* a, const mx_qmatrix* w, const uint16_t* bias,

@@ -23,7 +23,8 @@
  *
  * Conventions for every call:
  *  - Pointers marked "device" are HIP device (or host-coherent) addresses owned by the caller;
- *    the library allocates nothing, frees nothing and keeps no pointer after the call returns.
+ *    the library allocates nothing, frees nothing and keeps no pointer after the call returns
+ *    (mx_linear_noalloc's workspace is a static device array of the library, see there).
  *  - BF16 and FP16 values are passed as uint16_t bit patterns.
  *  - The canonical layout (MX_LAYOUT_ROW_MAJOR) is row-major and unshuffled.  FP4 codes:
  *    [rows, cols/2] bytes, element 2j in the low nibble of byte j.  FP8 codes: [rows, cols]
@@ -50,7 +51,8 @@
  *    written.  MX_ERR_HIP reports a launch failure.  mx_last_error() gives a message for the
  *    calling thread's last failing call.  M = 0 (rows = 0) is a valid no-op.
  *  - Results are deterministic: no atomics, no split-K; the same inputs give the same bytes.
- *  - Calls are thread-safe; the library holds no state besides the per-thread error message.
+ *  - Calls are thread-safe; the library holds no state besides the per-thread error message
+ *    and mx_linear_noalloc's per-GPU static workspace (whose concurrent use races, see there).
  */
 #ifndef MXFP_H
 #define MXFP_H
@@ -311,6 +313,31 @@ mx_status mx_linear(const uint16_t* a, int64_t M, int64_t K, int64_t ld_a, int32
                     const mx_lowrank* lr, int32_t epilogue, int32_t out_dtype, void* out,
                     int64_t ld_out, uint8_t* out_scales, void* workspace, size_t workspace_bytes,
                     void* stream);
+
+/* Bytes of the static device workspace of mx_linear_noalloc (64 MiB per GPU). */
+#define MX_NOALLOC_SCRATCH_BYTES (64u << 20)
+
+/*
+ * mx_linear_noalloc - mx_linear for callers that cannot allocate device memory: code under HIP
+ * graph capture, tight serving loops, harnesses that forbid allocation.  Same arguments, same
+ * kernels and bit-identical results as mx_linear, without the workspace arguments: the
+ * workspace is a statically allocated device array of MX_NOALLOC_SCRATCH_BYTES inside the
+ * library, one per GPU, held from the first call on that GPU until the process ends.  It calls
+ * no allocating routine.
+ *  - Limit: mx_linear_workspace_bytes(M, K, act_fmt, rank) <= MX_NOALLOC_SCRATCH_BYTES, else
+ *    MX_ERR_WORKSPACE before anything is launched (MXFP4 at K = 5120: M up to 24576 rows;
+ *    larger activations are split along M by the caller, rows being independent).
+ *  - The array of the calling thread's current device is used; `stream` must belong to that
+ *    device.  The first call on a device looks the array's device address up once
+ *    (hipGetSymbolAddress); a failure there is MX_ERR_HIP.
+ *  - Every call on one GPU shares that GPU's array, which keeps the last call's contents (no
+ *    call relies on it starting at zero).  Calls whose executions overlap on one GPU (several
+ *    streams, or several host threads) race on it: serialise them, e.g. on one stream.
+ */
+mx_status mx_linear_noalloc(const uint16_t* a, int64_t M, int64_t K, int64_t ld_a, int32_t act_fmt,
+                            float act_global_scale, const mx_qmatrix* w, const uint16_t* bias,
+                            const mx_lowrank* lr, int32_t epilogue, int32_t out_dtype, void* out,
+                            int64_t ld_out, uint8_t* out_scales, void* stream);
 
 /*
  * mx_linear_q - the same GEMM and epilogues on an already quantized activation a (M x K), e.g.

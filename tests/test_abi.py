@@ -168,6 +168,34 @@ def test_linear_validation(mx):
     assert call(M=0, ws=0) == 0                      # empty activation: no-op
 
 
+def test_linear_noalloc_validation(mx):
+    """mx_linear_noalloc checks mx_linear's arguments, then its static workspace limit, before
+    any HIP call: an activation whose workspace exceeds MX_NOALLOC_SCRATCH_BYTES is
+    MX_ERR_WORKSPACE."""
+    L = mx.lib()
+    P = ctypes.c_void_p
+    byref = ctypes.byref
+    K = 5120
+    w = _qm(mx, 64, K, mx.MXFP4)
+
+    def call(M, a=FAKE, w_=w, epi=0, ldo=64):
+        return L.mx_linear_noalloc(P(a) if a else None, M, K, K, mx.MXFP4, 1.0, byref(w_) if w_ else None,
+                                   None, None, epi, 0, P(FAKE), ldo, None, None)
+
+    hdr = open(HEADER).read()
+    assert re.search(r"#define MX_NOALLOC_SCRATCH_BYTES \(64u << 20\)", hdr)
+    assert mx.NOALLOC_SCRATCH_BYTES == 64 << 20
+    assert mx.linear_workspace_bytes(24576, K, "mxfp4") <= mx.NOALLOC_SCRATCH_BYTES
+    assert mx.linear_workspace_bytes(24577, K, "mxfp4") > mx.NOALLOC_SCRATCH_BYTES
+    assert call(24577) == 5
+    assert "static scratch" in L.mx_last_error().decode()
+    assert call(10**6) == 5
+    assert call(16, w_=None) == 1
+    assert call(16, a=0) == 1
+    assert call(16, ldo=32) == 2
+    assert call(0) == 0  # empty activation: no-op, no device touched
+
+
 def test_linear_q_validation(mx):
     L = mx.lib()
     P = ctypes.c_void_p
