@@ -9,14 +9,17 @@
 // vectors and reduce a 32-wide re-quantization group with a single cross-lane exchange.
 //
 // Two MX kernels share those conventions:
-//  - the ring kernel (K % 128 == 0, every configuration of the model): 256 x 128 (W4A4) or
-//    128 x 128 (W4A8) output tiles, two workgroups per compute unit, a 3-deep LDS ring of
+//  - the ring kernel (K % 128 == 0, every configuration of the model): an LDS ring of
 //    128-element K chunks filled by direct-to-LDS buffer loads, operands row-major or in the
-//    tiled layout whose 1 KB / 256 B tiles are exactly the LDS images the ring holds;
+//    tiled layout whose 1 KB / 256 B tiles are exactly the LDS images the ring holds.  W4A4 on
+//    a grid of at least 256 tiles runs 256 x 256 tiles, one workgroup of 8 waves per compute
+//    unit in a ping-pong schedule (one wave per SIMD multiplies while the other loads); smaller
+//    W4A4 grids and the low-rank branch run 256 x 128 tiles, W4A8 128 x 128 and W8A8 128 x 256,
+//    two workgroups (one for W8A8) per compute unit;
 //  - the register-staged kernel for any other K (a multiple of 32): 256-element chunks
 //    double-buffered through registers, partial last chunk zero-filled.
 // Sums over k are order-free, so each kernel pairs K blocks into MFMA steps in whatever order
-// makes the per-lane scale bytes one shifted or op_sel-selected dword (see each kernel).
+// makes the per-lane scale bytes one op_sel-selected register (see each kernel).
 //
 // NVFP4 (NVFP4 model card, Model Details) has E4M3 scales per 16 elements that the scaled MFMA
 // cannot apply, and code * scale needs up to 6 significant bits, more than FP8 holds; it is
@@ -30,6 +33,15 @@
 namespace mxk {
 
 constexpr int KC = 256;  // K elements per staged chunk
+
+// Band heights (tile rows) of the XCD-ordered tile walks: the ring kernels (8) and the
+// ping-pong W4A4 kernel (4: its 32 tiles per XCD span 4 rows of A and 8 columns of W).
+#ifndef MX_RING_GM
+#define MX_RING_GM 8
+#endif
+#ifndef MX_PP_GM
+#define MX_PP_GM 4
+#endif
 
 // tanh-form GELU, 0.5 y (1 + tanh(u)) with u = sqrt(2/pi) (y + 0.044715 y^3), evaluated as the
 // equal y / (1 + exp(-2u)): no cancellation for large negative y, and one hardware exp2 and one
@@ -503,36 +515,45 @@ __global__ void __launch_bounds__(256, 1) gemm_mx_kernel(GemmParams p) {
 // ---------------------------------------------------------------------------------------------
 // MX GEMM, ring-staged (K a multiple of 128)
 // ---------------------------------------------------------------------------------------------
-// Two workgroups per compute unit, each with a BM x BN output tile (4 waves, 2 x 2, BM/2 x BN/2
-// each) and a 3-deep LDS ring of 128-element K chunks.  Chunk kc + 2 is fetched by direct-to-LDS
-// buffer loads while chunk kc is multiplied, so two chunks of load latency are hidden; the second
-// workgroup on the CU fills the MFMA pipe while one waits at its barrier or runs its epilogue.
+// A BM x BN output tile per workgroup, its waves in 2 (m) x NWAVES/2 (n), each wave
+// BM/2 x 32 FN, and an LDS ring of 128-element K chunks:
+//  - two workgroups per compute unit (tiles up to 256 x 128 with 4 waves, or 256 x 256 with 8
+//    waves in step) and a 3-deep ring: chunk kc + 2 is fetched by direct-to-LDS buffer loads
+//    while chunk kc is multiplied, so two chunks of load latency are hidden, and the second
+//    workgroup fills the MFMA pipe while one waits at its barrier or runs its epilogue;
+//  - the ping-pong W4A4 tile (PP, 256 x 256, one workgroup of 8 waves per compute unit, a 4-deep
+//    ring): waves 0-3 and 4-7 alternate between MFMA and memory phases (see the main loop).
+//  Measured at 75600 x 5120 x 5120 against the 256 x 128 two-workgroup tile: 0.974 against
+//  1.00 ms, with 1.74 against 2.70 GB of L2 fills (the larger tile moves fewer bytes per MFMA,
+//  and the shader clock under the power limit rises from about 1.57 to 1.81 GHz).
 //
 // K ordering inside a 128-element chunk (four 32-element blocks): MFMA step s (0, 1) takes blocks
 // s and 2 + s as its scale blocks 0 and 1.  An FP4 lane of half h holds block 2h + s whole (16
 // bytes); an FP8 lane of half h holds elements 16h..16h+15 of both blocks.  The E8M0 bytes of a
-// row's chunk are one dword (blocks 0..3); shifted right by 16h, op_sel s picks block 2h + s.
+// row's chunk are one dword (blocks 0..3); a lane of half h reads its bytes 2h, 2h + 1 and
+// op_sel s picks block 2h + s.
 //
 // LDS rows (64 bytes for FP4 codes, 128 for FP8) hold 16-byte pieces XOR-swizzled by the row so
 // that a quarter wave of 16-byte fragment reads (16 consecutive rows, one piece index) covers
 // all 64 banks: piece ^ ((row >> 2) & 3) for 64-byte rows, piece ^ ((row >> 1) & 7) for 128-byte
 // rows.  A load instruction fills 1 KB of consecutive LDS (16 or 8 rows), lane i slot i, so each
 // lane fetches the global piece that the swizzle puts in its slot.
-template <int BM, int BN, bool AFP8, bool WFP8 = false>
+template <int BM, int BN, bool AFP8, bool WFP8 = false, bool PP = false>
 struct RingTile {
   static_assert((BM == 128 || BM == 256) && (BN == 128 || BN == 256), "tile sizes");
   static_assert(!WFP8 || AFP8, "E4M3 weights are paired with E4M3 activations");
+  static_assert(!PP || (BM == 256 && BN == 256 && !AFP8), "ping-pong: 256 x 256 W4A4 tiles");
 #ifndef MX_RING_W256
 #define MX_RING_W256 8
 #endif
   // 2 (m) x NWAVES/2 (n) waves; a 256-wide tile has 8 waves of 128 x 64 or 4 of 128 x 128
-  static constexpr int NWAVES = BN == 256 ? MX_RING_W256 : 4;
+  static constexpr int NWAVES = PP ? 8 : BN == 256 ? MX_RING_W256 : 4;
   static constexpr int KCR = 128;
   static constexpr int WROWB = WFP8 ? 128 : 64, AROWB = AFP8 ? 128 : 64;  // bytes per row and chunk
   static constexpr int W_BYTES = BN * WROWB, A_BYTES = BM * AROWB;
   static constexpr int WS_BYTES = BN * 4, AS_BYTES = BM * 4;
   static constexpr int STAGE = W_BYTES + A_BYTES + WS_BYTES + AS_BYTES;
-  static constexpr int NSTAGE = 3;
+  static constexpr int NSTAGE = PP ? 4 : 3;
   static constexpr int LDS = NSTAGE * STAGE > BM * BN * 2 ? NSTAGE * STAGE : BM * BN * 2;
   static constexpr int WGS = 2 * LDS <= 160 * 1024 ? 2 : 1;  // workgroups per compute unit
   static constexpr int FN = BN / (NWAVES / 2) / 32, FM = BM / 64;  // 32x32 blocks per wave
@@ -616,10 +637,13 @@ __device__ __forceinline__ void epilogue_ring_staged(const GemmParams& p, v16f (
   }
 }
 
-template <int BM, int BN, bool AFP8, bool WFP8, int EPI, bool OUTF32, bool LR>
-__global__ void __launch_bounds__((RingTile<BM, BN, AFP8, WFP8>::NWAVES * 64), (RingTile<BM, BN, AFP8, WFP8>::WGS))
+template <int BM, int BN, bool AFP8, bool WFP8, int EPI, bool OUTF32, bool LR, bool PP = false>
+__global__ void __launch_bounds__((RingTile<BM, BN, AFP8, WFP8, PP>::NWAVES * 64), (RingTile<BM, BN, AFP8, WFP8, PP>::WGS))
 gemm_mx_ring_kernel(GemmParams p) {
-  using T = RingTile<BM, BN, AFP8, WFP8>;
+  using T = RingTile<BM, BN, AFP8, WFP8, PP>;
+  // Ping-pong: an operand constrained to an AGPR lets the register allocator place the MFMA
+  // accumulators in AGPRs (about 1 % faster at 75600 x 5120 x 5120 than in VGPRs)
+  if constexpr (PP) asm volatile("; accumulators in AGPRs" ::"a"(0.0f));
   typedef typename std::conditional<AFP8, v8i, v4i>::type AV;
   typedef typename std::conditional<WFP8, v8i, v4i>::type WV;
   __shared__ __attribute__((aligned(16))) uint8_t smem[T::LDS];
@@ -630,7 +654,7 @@ gemm_mx_ring_kernel(GemmParams p) {
   const int wn0 = (wave >> 1) * (32 * T::FN), wm0 = (wave & 1) * (BM / 2);
   const int tiles_n = (p.N + BN - 1) / BN, tiles_m = (p.M + BM - 1) / BM;
   int tm, tn;
-  tile_coords_gm<8>(blockIdx.x, tiles_m, tiles_n, tm, tn);
+  tile_coords_gm<PP ? MX_PP_GM : MX_RING_GM>(blockIdx.x, tiles_m, tiles_n, tm, tn);
   const int m0 = tm * BM, n0 = tn * BN;
   const int nkc = p.K / T::KCR;
   const uint32_t w_row = WFP8 ? (uint32_t)p.K : ((uint32_t)p.K >> 1), a_row = AFP8 ? (uint32_t)p.K : ((uint32_t)p.K >> 1);
@@ -719,7 +743,6 @@ gemm_mx_ring_kernel(GemmParams p) {
 
   // fragment addresses inside a stage (step 0; step 1 is piece ^ 1)
   const int wrow = wn0 + r32, arow = wm0 + r32;  // + 32 i: the XOR term is unchanged
-  const uint32_t shift = 16u * (uint32_t)h;
 
   // The fragments of a chunk (both MFMA steps) and its scale dwords, read from stage `stg`.
   struct Frags {
@@ -744,10 +767,12 @@ gemm_mx_ring_kernel(GemmParams p) {
     const uint8_t* sA = sW + T::W_BYTES;
     const uint8_t* sWS = sA + T::A_BYTES;
     const uint8_t* sAS = sWS + T::WS_BYTES;
+    // the two E8M0 bytes of this lane's half (blocks 2h, 2h + 1 of the chunk): a 16-bit read at
+    // byte 2h of the row's scale dword, op_sel picking the step's byte
 #pragma unroll
-    for (int i = 0; i < T::FN; ++i) f.wsc[i] = *(const uint32_t*)(sWS + (wrow + 32 * i) * 4) >> shift;
+    for (int i = 0; i < T::FN; ++i) f.wsc[i] = *(const uint16_t*)(sWS + (wrow + 32 * i) * 4 + 2 * h);
 #pragma unroll
-    for (int j = 0; j < T::FM; ++j) f.asc[j] = *(const uint32_t*)(sAS + (arow + 32 * j) * 4) >> shift;
+    for (int j = 0; j < T::FM; ++j) f.asc[j] = *(const uint16_t*)(sAS + (arow + 32 * j) * 4 + 2 * h);
 #pragma unroll
     for (int s = 0; s < 2; ++s) {
 #pragma unroll
@@ -806,6 +831,66 @@ gemm_mx_ring_kernel(GemmParams p) {
     return true;
   }(), "every load has an MFMA slot");
 
+  if constexpr (PP) {
+    // Ping-pong: waves 0-3 (group 0) and 4-7 (group 1) put one wave of each group on every SIMD.
+    // The groups alternate between an MFMA phase (the 16 MFMAs of one chunk on fragments already
+    // in registers) and a memory phase (this wave's share of chunk c + 3's direct-to-LDS loads,
+    // then the fragment reads of chunk c), with a workgroup barrier between phases, so the matrix
+    // core of each SIMD is fed by one wave while the other waits on LDS and memory.
+    //   phase 2c:     group 0 memory(c),     group 1 MFMA(c - 1)
+    //   phase 2c + 1: group 0 MFMA(c),       group 1 memory(c)
+    // Chunk c + 3 goes into the stage of chunk c - 1, whose last reads were in phases 2c - 2 and
+    // 2c - 1.  A memory phase ends by waiting for this wave's loads of chunk c + 1 (chunks c + 2
+    // and c + 3 may fly); the barrier after it publishes them before chunk c + 1 is read (phase
+    // 2c + 2 at the earliest).
+    static_assert(T::NSTAGE == 4, "ping-pong ring depth");
+    const bool g0 = wave < T::NWAVES / 2;
+    issue(0, 0);
+    issue(1, 1);
+    issue(2, 2);
+    wait_vmcnt<2 * T::NDMA>();  // chunk 0 landed
+    barrier_only();
+    Frags f;
+    auto memory = [&](int c) {
+      issue(c + 3, (c + 3) & 3);  // past the last chunk: empty loads (zero-range descriptors)
+      read_chunk(c & 3, f);
+      wait_vmcnt<2 * T::NDMA>();  // chunk c + 1 landed
+      wait_lds_all();
+    };
+    auto mfma = [&]() {
+      static_for<2>([&](auto sc) {
+        constexpr int S = decltype(sc)::value;
+        static_for<T::FN>([&](auto i) {
+          static_for<T::FM>([&](auto j) {
+            acc[i][j] = mfma_scale_32x32x64_f4f4(f.wf[S][i], f.af[S][j], acc[i][j], 4, 4, S, (int)f.wsc[i], S,
+                                                 (int)f.asc[j]);
+          });
+        });
+      });
+    };
+    // One loop per group (the group is uniform per wave): each wave passes 2 nkc + 1 barriers.
+    if (g0) {
+      for (int c = 0; c < nkc; ++c) {
+        memory(c);
+        barrier_only();
+        __builtin_amdgcn_sched_barrier(0);
+        mfma();
+        __builtin_amdgcn_sched_barrier(0);
+        barrier_only();
+      }
+      barrier_only();  // phase 2 nkc: group 1's last MFMA phase
+    } else {
+      barrier_only();  // phase 0: group 0 reads chunk 0
+      for (int c = 0; c < nkc; ++c) {
+        memory(c);
+        barrier_only();
+        __builtin_amdgcn_sched_barrier(0);
+        mfma();
+        __builtin_amdgcn_sched_barrier(0);
+        barrier_only();
+      }
+    }
+  } else {
   // Software pipeline over chunks.  Iteration kc: step-0 MFMAs of chunk kc (its fragments were
   // read last iteration) while chunk kc + 2 starts loading into the stage of chunk kc - 1; then
   // the barrier that publishes chunk kc + 1 -- its wait overlaps the MFMAs already in the pipe --
@@ -835,6 +920,7 @@ gemm_mx_ring_kernel(GemmParams p) {
     __builtin_amdgcn_sched_barrier(0);
     cur = nxt;
     st = st1;
+  }
   }
 
   if constexpr (LR && LR_EARLY) {  // slices 0-1 (rank 32) were loaded before the loop
@@ -1057,7 +1143,7 @@ __global__ void __launch_bounds__(256, 256 / BN) gemm_nv_ring_kernel(GemmParams 
   const int wn0 = (wave >> 1) * (BN / 2), wm0 = (wave & 1) * (BM / 2);
   const int tiles_n = (p.N + BN - 1) / BN, tiles_m = (p.M + BM - 1) / BM;
   int tm, tn;
-  tile_coords_gm<8>(blockIdx.x, tiles_m, tiles_n, tm, tn);
+  tile_coords_gm<MX_RING_GM>(blockIdx.x, tiles_m, tiles_n, tm, tn);
   const int m0 = tm * BM, n0 = tn * BN;
   const int nkc = p.K / T::KCN;
   const uint32_t row_b = (uint32_t)p.K >> 1, s_row = (uint32_t)p.K >> 4;
@@ -1373,9 +1459,15 @@ __global__ void __launch_bounds__(LR_WAVES * 64) lowrank_down_kernel(const uint1
 // ---------------------------------------------------------------------------------------------
 // launchers
 // ---------------------------------------------------------------------------------------------
+// PP: the ping-pong schedule of the 256 x 256 W4A4 tile (MX_RING_PP=0 turns it off).
+#ifndef MX_RING_PP
+#define MX_RING_PP 1
+#endif
 template <int BM, int BN, bool AFP8, bool WFP8, int EPI, bool OUTF32, bool LR>
 static void run_ring(const GemmParams& p, int grid, hipStream_t s) {
-  gemm_mx_ring_kernel<BM, BN, AFP8, WFP8, EPI, OUTF32, LR><<<grid, RingTile<BM, BN, AFP8, WFP8>::NWAVES * 64, 0, s>>>(p);
+  constexpr bool PP = MX_RING_PP && BM == 256 && BN == 256 && !AFP8 && !WFP8 && !LR;
+  gemm_mx_ring_kernel<BM, BN, AFP8, WFP8, EPI, OUTF32, LR, PP>
+      <<<grid, RingTile<BM, BN, AFP8, WFP8, PP>::NWAVES * 64, 0, s>>>(p);
 }
 
 // Every (epilogue, output type, low-rank) combination of the ring kernel.
@@ -1400,12 +1492,26 @@ static void run_ring_e(const GemmParams& p, int grid, hipStream_t s) {
 
 // K % 128 == 0: the ring kernel (row-major or tiled operands); otherwise the register-staged
 // kernel, which reads row-major operands (the tiled layout implies K % 128 == 0).
+// The ping-pong tile needs one 256 x 256 tile per compute unit of the MI355X (256) to pay: with
+// fewer tiles the 256 x 128 two-workgroup tile spreads the work over more compute units.
+constexpr int PP_MIN_TILES = 256;
+
 template <int BM, int BN, bool AFP8>
 static hipError_t run_mx(const GemmParams& p, hipStream_t s) {
   if (p.K % 128 == 0) {
 #ifndef MX_RING_BN
 #define MX_RING_BN 128
 #endif
+    // W4A4 without a low-rank branch on a large grid: the 256 x 256 ping-pong tile (one workgroup
+    // of 8 waves per compute unit); otherwise 256 x MX_RING_BN (W4A4) or 128 x 128 (W4A8), two
+    // workgroups per compute unit
+    if constexpr (!AFP8 && MX_RING_PP) {
+      const int tiles_pp = ((p.M + 255) / 256) * ((p.N + 255) / 256);
+      if (p.R == 0 && tiles_pp >= PP_MIN_TILES) {
+        run_ring_e<256, 256, false, false, false>(p, tiles_pp, s);
+        return hipGetLastError();
+      }
+    }
     constexpr int RBN = AFP8 ? 128 : MX_RING_BN;
     const int tiles = ((p.M + BM - 1) / BM) * ((p.N + RBN - 1) / RBN);
     if (p.R > 0) run_ring_e<BM, RBN, AFP8, false, true>(p, tiles, s);

@@ -428,6 +428,47 @@ def test_nvfp4_linear_vs_oracle(mx, M, K, N):
     assert_within(y.cpu().numpy(), y_ref, abs_sum, what="NVFP4 linear")
 
 
+@pytest.mark.parametrize("epi", ["bias", "bias_gelu", "bias_gelu_quant_mxfp4", "bias_gelu_quant_mxfp4_tiled"])
+def test_pingpong_tile_ragged(mx, epi):
+    """A grid of 17 x 17 256 x 256 tiles (at least one per compute unit) takes the ping-pong
+    W4A4 kernel: ragged M and N, 6 K chunks, every epilogue, against the oracle on sampled rows
+    (the BF16 output as the RNE of the F32 one; the re-quantized codes as Q_MX of the GPU's own
+    GELU output)."""
+    M, K, N = 4177, 768, 4224  # N % 128 == 0 (tiled re-quantized output), N % 256 != 0
+    assert ((M + 255) // 256) * ((N + 255) // 256) >= 256
+    a_bits = activation_bits(M, K, seed_base=17000)
+    w_bits = weight_bits(N, K, seed=17100)
+    b_bits = f16_bits(synth.normal_f32(17200, (N,), 0.01))
+    a, bias = to_dev_bf16(a_bits), to_dev_f16(b_bits)
+    wq = mx.quantize(to_dev_bf16(w_bits), "mxfp4", layout="tiled")
+    rows = sample_rows(M, 400)
+    idx = torch.from_numpy(rows).cuda()
+    ac, as_ = O.quantize_mx_bf16(a_bits[rows])
+    wc, ws = O.quantize_mx_bf16(w_bits)
+    y_ref, abs_sum = O.linear_ref_mx(ac, as_, O.E2M1, wc, ws, K, b_bits)
+    if epi in ("bias", "bias_gelu"):
+        y32 = mx.linear(a, wq, bias, epilogue=epi, out_dtype=torch.float32)
+        y16 = mx.linear(a, wq, bias, epilogue=epi)
+        torch.cuda.synchronize()
+        ys = y32[idx].cpu().numpy()
+        np.testing.assert_array_equal(dev_bits16(y16[idx]), bf16_rne_of_f32(ys))
+        if epi == "bias":
+            assert_within(ys, y_ref, abs_sum, what="ping-pong tile")
+        else:
+            tol = 2e-3 * abs_sum + 2.0 ** -23 * np.abs(y_ref)
+            h_ref = O.gelu_tanh(y_ref)
+            assert np.all(np.abs(ys - h_ref) <= 1.13 * tol + 4e-6 * np.abs(h_ref) + 1e-7)
+    else:
+        h32 = mx.linear(a, wq, bias, epilogue="bias_gelu", out_dtype=torch.float32)
+        hq = mx.linear(a, wq, bias, epilogue=epi)
+        if epi.endswith("tiled"):
+            hq = mx.relayout(hq)
+        torch.cuda.synchronize()
+        c_self, s_self = O.quantize_mx_f32(h32[idx].cpu().numpy())
+        np.testing.assert_array_equal(hq.scales[idx].cpu().numpy(), s_self)
+        np.testing.assert_array_equal(hq.codes[idx].cpu().numpy(), c_self)
+
+
 # ---------------------------------------------------------------------------------------------
 # full workload sizes, in the launch configuration the benchmark times (sampled rows)
 # ---------------------------------------------------------------------------------------------
@@ -495,6 +536,32 @@ def test_full_size_w4a8_with_lowrank_branch(mx, name):
     u_bits, lr_ref, lr_abs = O.lowrank(np.ascontiguousarray(a_bits[rows]), down, up)
     flip = (2.0 ** -8) * (np.abs(O.bf16_values(u_bits)) @ np.abs(O.bf16_values(up)))
     assert_within(ys, y_ref + lr_ref, abs_sum, 2e-3 * lr_abs + flip, what=f"W4A8 + low-rank, {name}")
+
+
+def test_full_size_w4a4_with_lowrank_branch(mx):
+    """W4A4 SVDQuant (MXFP4 activations + rank-32 BF16 branch, the W4A8 page's experimental
+    activation format) at the A14B attention-projection shape 75600 x 5120 x 5120, factors
+    N(0, 0.02) from the workload's seed space, FP16 bias; sampled rows against the oracle."""
+    wl = synth.WORKLOADS["wan_a14b_attn_75600x5120x5120"]
+    R = 32
+    a_bits = synth.bits16(synth.to_bf16(wl.activation()))
+    w_bits = synth.bits16(synth.to_bf16(wl.weight()))
+    b_bits = f16_bits(wl.bias())
+    down = synth.bits16(synth.to_bf16(synth.normal_f32(wl.seed_base + synth.T_LDOWN, (wl.K, R), 0.02)))
+    up = synth.bits16(synth.to_bf16(synth.normal_f32(wl.seed_base + synth.T_LUP, (R, wl.N), 0.02)))
+    wq = mx.relayout(_quant_w(mx, w_bits))
+    lr = mx.LowRank(to_dev_bf16(np.ascontiguousarray(down.T)), to_dev_bf16(np.ascontiguousarray(up.T)))
+    y = mx.linear(to_dev_bf16(a_bits), wq, to_dev_f16(b_bits), lowrank=lr, out_dtype=torch.float32)
+    torch.cuda.synchronize()
+    rows = sample_rows(wl.M, FULL_SAMPLE)
+    ys = y[torch.from_numpy(rows).cuda()].cpu().numpy()
+    del y
+    ac, as_ = O.quantize_mx_bf16(a_bits[rows])
+    wc, ws = O.quantize_mx_bf16(w_bits)
+    y_ref, abs_sum = O.linear_ref_mx(ac, as_, O.E2M1, wc, ws, wl.K, b_bits)
+    u_bits, lr_ref, lr_abs = O.lowrank(np.ascontiguousarray(a_bits[rows]), down, up)
+    flip = (2.0 ** -8) * (np.abs(O.bf16_values(u_bits)) @ np.abs(O.bf16_values(up)))
+    assert_within(ys, y_ref + lr_ref, abs_sum, 2e-3 * lr_abs + flip, what="W4A4 + low-rank, full size")
 
 
 def test_full_size_ffn_pair(mx):
