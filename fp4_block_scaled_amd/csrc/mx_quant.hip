@@ -404,18 +404,34 @@ __device__ __forceinline__ NvThresholds nv_thresholds(double D, bool zero) {
   return th;
 }
 
+// Positive binary32 q rounded to its nearest value with BITS significant bits (ties away; q is
+// never a tie where this is used).
+template <int BITS>
+__device__ __forceinline__ float round_sig(float q) {
+  constexpr uint32_t drop = 24 - BITS;
+  return __uint_as_float((__float_as_uint(q) + (1u << (drop - 1))) & ~((1u << drop) - 1u));
+}
+
 // One thread per 16-element group (two 16-byte loads), NV_U groups per thread and step, all
 // loaded before any is coded.  Every rounding below is exact; the fast paths are binary32
 // brackets:
 //  - Block scale sb = E4M3_rne_sat(amax / (6 sg)).  amax * (1/(6 sg)) in binary32 (product and
 //    reciprocal each within an ulp) is within 2^-22 of the exact quotient, so nudging it by 2^-20
 //    down and up brackets the quotient strictly; since RNE is monotone, equal E4M3 codes for the
-//    two ends are the exact code.  Otherwise the fp64 quotient decides (one rounding: an 8-bit by
-//    26-bit quotient never lands on a false E4M3 midpoint).
+//    two ends are the exact code.  Different codes are neighbours, and the quotient lies within
+//    about 2^-19 of the E4M3 midpoint between them, which has at most 5 significant bits: rounding
+//    the bracket's end to 5 bits recovers it exactly, and the sign of amax - (6 m) sg, one fused
+//    multiply-add (6 m is exact, the fma rounds once, and the difference is far above the
+//    underflow range for the 6 sg allowed here), says on which side the quotient lies; on the
+//    midpoint itself the even code wins.  A global scale outside that range takes the fp64
+//    quotient (one rounding: an 8-bit by 26-bit quotient never lands on a false E4M3 midpoint).
 //  - Elements: code = RNE(x / D), D = sb * sg, by the hardware FP32 -> E2M1 conversion of the two
-//    nudged products x * (1/D) * (1 -+ 2^-20).  Equal codes are the exact code; a group where any
-//    element's codes differ (within about 2^-20 of a midpoint, exact ties included), or where D
-//    or 6 sg is outside the normal binary32 range, is coded against exact thresholds instead.
+//    nudged products x * (1/D) * (1 -+ 2^-20).  Equal codes are the exact code.  An element whose
+//    two codes differ sits within about 2^-19 of an E2M1 midpoint (at most 3 significant bits);
+//    that midpoint m is recovered by rounding, and the sign of |x| - (m sb) sg (m sb exact, one
+//    fma) picks the code, the even one on a tie.  Only those elements are visited, one at a time
+//    per lane.  A block whose D lies outside [2^-70, 2^100] (an all-zero block, say) is coded
+//    against exact fp64-derived thresholds instead.
 constexpr int NV_U = 2;
 
 // IDX: the group-index type, 32-bit when the group count allows (cheaper division)
@@ -429,7 +445,7 @@ __global__ void __launch_bounds__(256) quant_nv_kernel(const uint16_t* __restric
   const double six_sg = 6.0 * (double)sg;
   constexpr float kLo = 1.0f - 0x1p-20f, kHi = 1.0f + 0x1p-20f;
   const float c6 = 6.0f * sg;
-  const bool scale_fast = c6 >= 0x1p-125f && c6 <= 0x1p125f;
+  const bool scale_fast = c6 >= 0x1p-80f && c6 <= 0x1p100f;
   const float inv6 = __builtin_amdgcn_rcpf(c6);
   const float inv6_lo = inv6 * kLo, inv6_hi = inv6 * kHi;
   for (IDX base = (IDX)blockIdx.x * 256 * NV_U; base < total; base += (IDX)gridDim.x * 256 * NV_U) {
@@ -461,32 +477,60 @@ __global__ void __launch_bounds__(256) quant_nv_kernel(const uint16_t* __restric
       const uint32_t amax = max((uint32_t)m2.x, (uint32_t)m2.y);
       const bool bad = amax >= 0x7F80u;
       const float af = bf16_to_f32(amax);
-      uint32_t sbyte = e4m3_code(af * inv6_lo);
-      if (!scale_fast || sbyte != e4m3_code(af * inv6_hi)) sbyte = e4m3_code_f64((double)af / six_sg);
-      const float sb = e4m3_value(sbyte);
+      uint32_t sbyte;
+      if (scale_fast) {
+        const float ql = af * inv6_lo;
+        sbyte = e4m3_code(ql);
+        if (!bad && sbyte != e4m3_code(af * inv6_hi)) {
+          const float e = __builtin_fmaf(-(round_sig<5>(ql) * 6.0f), sg, af);
+          sbyte += (e > 0.0f || (e == 0.0f && (sbyte & 1u))) ? 1u : 0u;
+        }
+      } else {
+        sbyte = e4m3_code_f64((double)af / six_sg);
+      }
+      // sbyte <= 126: a positive finite E4M3 value (normal ones: exponent field + 120 as the
+      // binary32 exponent, the 3 mantissa bits on top of binary32's)
+      const float sb = sbyte >= 8u ? __uint_as_float((sbyte << 20) + (120u << 23)) : (float)sbyte * 0x1p-9f;
       const float d32 = sb * sg;
       uint32_t out0 = 0, out1 = 0;
-      bool exact = !(d32 >= 0x1p-125f && d32 <= 0x1p125f);
-      if (!exact) {
+      if (d32 >= 0x1p-70f && d32 <= 0x1p100f) {
         const float inv = __builtin_amdgcn_rcpf(d32);
         const float il = inv * kLo, ih = inv * kHi;
-        uint32_t lo0 = 0, hi0 = 0, lo1 = 0, hi1 = 0;
+        uint32_t hi0 = 0, hi1 = 0;
         static_for<4>([&](auto q) {
           constexpr int Q = decltype(q)::value;
           const float a0 = bf16_to_f32(w[Q] & 0xFFFFu), a1 = __uint_as_float(w[Q] & 0xFFFF0000u);
           const float b0 = bf16_to_f32(w[4 + Q] & 0xFFFFu), b1 = __uint_as_float(w[4 + Q] & 0xFFFF0000u);
-          lo0 = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(lo0, a0 * il, a1 * il, 1.0f, Q);
+          out0 = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(out0, a0 * il, a1 * il, 1.0f, Q);
           hi0 = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(hi0, a0 * ih, a1 * ih, 1.0f, Q);
-          lo1 = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(lo1, b0 * il, b1 * il, 1.0f, Q);
+          out1 = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(out1, b0 * il, b1 * il, 1.0f, Q);
           hi1 = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(hi1, b0 * ih, b1 * ih, 1.0f, Q);
         });
-        exact = (lo0 != hi0) | (lo1 != hi1);
-        out0 = lo0;
-        out1 = lo1;
-      }
-      if (exact) {
+        // elements near a midpoint: nibbles where the two brackets disagree (out* holds the
+        // lower magnitude, the upper one is one step above)
+        uint32_t d0 = bad ? 0u : out0 ^ hi0, d1 = bad ? 0u : out1 ^ hi1;
+        while (d0 | d1) {
+          const bool first = d0 != 0u;
+          const uint32_t nib = (uint32_t)__builtin_ctz(first ? d0 : d1) >> 2;
+          const uint32_t el = nib + (first ? 0u : 8u);  // element index in the group
+          const uint32_t wa = (el & 2u) ? ((el & 8u) ? w[5] : w[1]) : ((el & 8u) ? w[4] : w[0]);
+          const uint32_t wb = (el & 2u) ? ((el & 8u) ? w[7] : w[3]) : ((el & 8u) ? w[6] : w[2]);
+          const uint32_t word = (el & 4u) ? wb : wa;
+          const float a = __uint_as_float(((el & 1u) ? word >> 16 : word) << 17 >> 1);
+          const float e = __builtin_fmaf(-(round_sig<3>(a * il) * sb), sg, a);
+          const uint32_t lo = ((first ? out0 : out1) >> (4 * nib)) & 7u;
+          const uint32_t up = (e > 0.0f || (e == 0.0f && (lo & 1u))) ? 1u << (4 * nib) : 0u;
+          const uint32_t clr = ~(0xFu << (4 * nib));
+          if (first) {
+            out0 += up;
+            d0 &= clr;
+          } else {
+            out1 += up;
+            d1 &= clr;
+          }
+        }
+      } else {
         const NvThresholds th = nv_thresholds((double)sb * (double)sg, sbyte == 0);
-        out0 = out1 = 0;
 #pragma unroll
         for (int i = 0; i < 16; ++i) {
           const uint32_t b = (w[i >> 1] >> ((i & 1) * 16)) & 0xFFFFu;

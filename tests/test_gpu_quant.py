@@ -119,6 +119,29 @@ def test_nv_quantizer_exhaustive_bf16(mx):
         np.testing.assert_array_equal(c, ref_c, err_msg=f"anchor {a:#06x}")
 
 
+@pytest.mark.parametrize("sg", [1.0, 0.75, 2.0 ** -10, 3.0 / 7.0, 40.0 / 2688.0])
+def test_nv_quantizer_ties_and_near_ties(mx, sg):
+    """Blocks built on the rounding midpoints: elements m * 2^k * sg with m an E2M1 midpoint or
+    grid value, and a block maximum placed on or next to an E4M3 midpoint.  At a power-of-two or
+    short global scale these are exact ties (the even code wins); at 3/7 and 40/2688 the BF16
+    rounding leaves them within a few units in the last place of a midpoint on either side."""
+    sg = float(np.float32(sg))
+    rng = np.random.default_rng(4100)
+    mids = np.array([0.25, 0.75, 1.25, 1.75, 2.5, 3.5, 5.0, 6.0, 0.5, 1.0, 3.0, 4.0])
+    n = 8192
+    blk = rng.choice(mids, (n, 16)) * np.where(rng.integers(0, 2, (n, 16)) == 1, -1.0, 1.0)
+    # block maximum 6 * s with s on an E4M3 value (exact block scale) or midpoint (a scale tie)
+    e4m3_mid = np.array([1.0625, 1.1875, 1.3125, 1.4375, 1.5625, 1.6875, 1.8125, 1.9375])
+    smax = np.where(rng.integers(0, 2, n) == 1, rng.choice(e4m3_mid, n), 1.0)
+    blk[:, 0] = 6.0 * smax
+    x = (blk * np.exp2(rng.integers(-8, 9, (n, 1))) * sg).astype(np.float32)
+    bits = synth.bits16(synth.to_bf16(x)).reshape(-1, 256)
+    ref_c, ref_s = O.quantize_nv_bf16(bits, sg)
+    c, s = _gpu_quant(mx, bits, "nvfp4", sg)
+    np.testing.assert_array_equal(s, ref_s)
+    np.testing.assert_array_equal(c, ref_c)
+
+
 @pytest.mark.parametrize("rows,cols,ld", [(1, 16, 16), (3, 96, 104), (257, 528, 536), (1000, 3072, 3072)])
 def test_nv_quantizer_shapes_and_strides(mx, rows, cols, ld):
     sg = float(np.float32(40.0 / 2688.0))
