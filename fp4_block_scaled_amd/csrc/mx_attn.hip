@@ -14,6 +14,8 @@
 // the output is o / l.  The running maximum is exact (no deferred rescaling), so the quantized
 // probabilities are the ones that definition gives; o is rescaled only when some query's maximum
 // moved (alpha == 1 otherwise, and multiplying by it changes nothing).
+#include <algorithm>
+
 #include "mx_common.h"
 #include "mx_internal.h"
 
@@ -50,50 +52,61 @@ __device__ __forceinline__ float halves_sum(float v) {
 // ---------------------------------------------------------------------------------------------
 // Output in key blocks of 64: codes [BH, Sp / 64, D, 64] and scales [BH, Sp / 64, D, 2], so that
 // one block of V^T (the 64 keys x D codes and 2 x D scales the attention kernel stages at a time)
-// is contiguous.  One workgroup per (64 keys, 128 head-dim columns, head): the BF16 tile is
-// staged in LDS as loaded (key rows), then thread (d, g) gathers key group g of column d and
-// quantizes it with the MXFP8 group routine of the activation quantizer.  Keys past S are zero.
+// is contiguous.  A workgroup takes one unit (64 keys, 128 head-dim columns, one head) at a
+// time: the BF16 tile is staged in LDS as loaded (key rows), then thread (d, g) gathers key group
+// g of column d and quantizes it with the MXFP8 group routine of the activation quantizer.  Keys
+// past S are zero.  Units are numbered heads first, then column tiles, then key blocks: with the
+// heads of a token interleaved in memory ([B, S, H, D] activations), the workgroups in flight at
+// once read whole contiguous token rows rather than one 256-byte piece of each (measured 2.5 %
+// faster than key blocks first at 75600 x 40 x 128).  The grid walks the units with a stride of
+// its size; the unit index is uniform in the workgroup, so every thread reaches the same barriers.
 constexpr int VT_PITCH = 136;  // BF16 elements per LDS key row (272 bytes, 16-byte aligned)
 
-__global__ __launch_bounds__(256) void quant_vt_kernel(const uint16_t* __restrict__ v, int S, int D,
-                                                       int64_t ld, int64_t hs, int Sp,
+__global__ __launch_bounds__(256) void quant_vt_kernel(const uint16_t* __restrict__ v, int64_t BH, int64_t S,
+                                                       int64_t D, int64_t ld, int64_t hs, int64_t Sp,
                                                        uint8_t* __restrict__ codes,
                                                        uint8_t* __restrict__ scales) {
   __shared__ __attribute__((aligned(16))) uint16_t tile[AT_KVB * VT_PITCH];
-  const int kb0 = blockIdx.x * AT_KVB, d0 = blockIdx.y * 128;
-  const int64_t bh = blockIdx.z;
-  const int dn = min(128, D - d0);  // a multiple of 32
-  const uint16_t* vb = v + bh * hs + d0;
-#pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    const int c = threadIdx.x + 256 * i;  // 16-byte chunk: key row c / 16, columns 8 (c % 16)..
-    const int r = c >> 4, cc = c & 15;
-    uint4 x = {0u, 0u, 0u, 0u};
-    if (kb0 + r < S && 8 * cc < dn) x = *(const uint4*)(vb + (int64_t)(kb0 + r) * ld + 8 * cc);
-    *(uint4*)(tile + r * VT_PITCH + 8 * cc) = x;
-  }
-  __syncthreads();
+  const int64_t nkb = Sp / AT_KVB, ny = (D + 127) >> 7, units = nkb * ny * BH;
   const int d = threadIdx.x & 127, g = threadIdx.x >> 7;
-  if (d >= dn) return;
-  uint32_t w[16];
+  for (int64_t u = blockIdx.x; u < units; u += gridDim.x) {
+    const int64_t rest = u / BH, bh = u - rest * BH;
+    const int64_t kb = rest / ny, d0 = (rest - kb * ny) * 128, kb0 = kb * AT_KVB;
+    const int dn = (int)min((int64_t)128, D - d0);  // a multiple of 32
+    const uint16_t* vb = v + bh * hs + d0;
+    __syncthreads();  // the previous unit's gathers are done with the tile
 #pragma unroll
-  for (int i = 0; i < 16; ++i)
-    w[i] = (uint32_t)tile[(32 * g + 2 * i) * VT_PITCH + d] |
-           (uint32_t)tile[(32 * g + 2 * i + 1) * VT_PITCH + d] << 16;
-  uint32_t out[8], sb;
-  quant_fp8_group32(w, out, sb);
-  const int64_t row = (bh * (Sp / AT_KVB) + blockIdx.x) * D + d0 + d;  // [BH, Sp / 64, D] rows
-  uint4* dst = (uint4*)(codes + row * AT_KVB + 32 * g);
-  dst[0] = uint4{out[0], out[1], out[2], out[3]};
-  dst[1] = uint4{out[4], out[5], out[6], out[7]};
-  scales[row * 2 + g] = (uint8_t)sb;
+    for (int i = 0; i < 4; ++i) {
+      const int c = threadIdx.x + 256 * i;  // 16-byte chunk: key row c / 16, columns 8 (c % 16)..
+      const int r = c >> 4, cc = c & 15;
+      uint4 x = make_uint4(0u, 0u, 0u, 0u);
+      if (kb0 + r < S && 8 * cc < dn) x = *(const uint4*)(vb + (kb0 + r) * ld + 8 * cc);
+      *(uint4*)(tile + r * VT_PITCH + 8 * cc) = x;
+    }
+    __syncthreads();
+    if (d >= dn) continue;
+    uint32_t w[16];
+#pragma unroll
+    for (int i = 0; i < 16; ++i)
+      w[i] = (uint32_t)tile[(32 * g + 2 * i) * VT_PITCH + d] |
+             (uint32_t)tile[(32 * g + 2 * i + 1) * VT_PITCH + d] << 16;
+    uint32_t out[8], sb;
+    quant_fp8_group32(w, out, sb);
+    const int64_t row = (bh * nkb + kb) * D + d0 + d;  // [BH, Sp / 64, D] rows
+    uint4* dst = (uint4*)(codes + row * AT_KVB + 32 * g);
+    dst[0] = uint4{out[0], out[1], out[2], out[3]};
+    dst[1] = uint4{out[4], out[5], out[6], out[7]};
+    scales[row * 2 + g] = (uint8_t)sb;
+  }
 }
 
 hipError_t launch_quant_vt(const uint16_t* v, int64_t BH, int64_t S, int64_t D, int64_t ld, int64_t hs,
                            uint8_t* codes, uint8_t* scales, hipStream_t s) {
   const int64_t Sp = (S + AT_KVB - 1) / AT_KVB * AT_KVB;
-  dim3 grid((unsigned)(Sp / AT_KVB), (unsigned)((D + 127) / 128), (unsigned)BH);
-  hipLaunchKernelGGL(quant_vt_kernel, grid, dim3(256), 0, s, v, (int)S, (int)D, ld, hs, (int)Sp, codes, scales);
+  const int64_t units = (Sp / AT_KVB) * ((D + 127) / 128) * BH;
+  if (units == 0) return hipSuccess;
+  const unsigned grid = (unsigned)std::min<int64_t>(units, 1 << 20);
+  hipLaunchKernelGGL(quant_vt_kernel, dim3(grid), dim3(256), 0, s, v, BH, S, D, ld, hs, Sp, codes, scales);
   return hipGetLastError();
 }
 
