@@ -21,7 +21,8 @@ from typing import Optional
 import torch  # loaded first: its HIP runtime is the one the native library binds to
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
-LIB_PATH = os.path.join(_HERE, "libmxfp.so")
+# MXFP_LIB selects another build of the same library (a variant built with compile-time knobs)
+LIB_PATH = os.environ.get("MXFP_LIB") or os.path.join(_HERE, "libmxfp.so")
 
 MXFP4, MXFP8, NVFP4 = 0, 1, 2
 NOALLOC_SCRATCH_BYTES = 64 << 20  # MX_NOALLOC_SCRATCH_BYTES of include/mxfp.h

@@ -53,18 +53,30 @@ def build_synth(verbose: bool = False, sanitize: bool = False) -> str:
     return out
 
 
-def build_hip(verbose: bool = False, jobs: int = 8) -> str:
+VARIANT_DIR = os.path.join(PKG, "variants")
+
+
+def build_hip(verbose: bool = False, jobs: int = 8, defines=(), variant: str = "") -> str:
+    """Compile every HIP source and link libmxfp.so.  With `variant`, the sources are compiled
+    with the extra `defines` (compile-time knobs such as MX_RING_PP=0) into
+    fp4_block_scaled_amd/variants/libmxfp_<variant>.so instead, which a process loads when the
+    environment variable MXFP_LIB names it."""
     srcs = sorted(glob.glob(os.path.join(CSRC, "*.hip")))
     if not srcs:
         raise RuntimeError("no HIP sources under " + CSRC)
-    objdir = os.path.join(ROOT, "_build")
+    if variant and not variant.replace("_", "").isalnum():
+        raise ValueError("variant names are letters, digits and underscores")
+    objdir = os.path.join(ROOT, "_build", variant) if variant else os.path.join(ROOT, "_build")
+    out = os.path.join(VARIANT_DIR, f"libmxfp_{variant}.so") if variant else LIB_PATH
     os.makedirs(objdir, exist_ok=True)
+    os.makedirs(os.path.dirname(out), exist_ok=True)
     inc = ["-I", os.path.join(ROOT, "include"), "-I", CSRC]
+    dflags = [f"-D{d}" for d in defines]
     procs, objs = [], []
     for s in srcs:
         o = os.path.join(objdir, os.path.basename(s) + ".o")
         objs.append(o)
-        cmd = [HIPCC, *HIP_FLAGS, *inc, "-c", s, "-o", o]
+        cmd = [HIPCC, *HIP_FLAGS, *dflags, *inc, "-c", s, "-o", o]
         if verbose:
             print(" ".join(cmd), flush=True)
         procs.append((s, subprocess.Popen(cmd)))
@@ -75,10 +87,9 @@ def build_hip(verbose: bool = False, jobs: int = 8) -> str:
     for s0, p0 in procs:
         if p0.wait():
             raise RuntimeError(f"hipcc failed on {s0}")
-    _run([HIPCC, f"--offload-arch={ARCH}", "-shared", "-fPIC", *objs, "-o", LIB_PATH + ".tmp"],
-         verbose)
-    os.replace(LIB_PATH + ".tmp", LIB_PATH)
-    return LIB_PATH
+    _run([HIPCC, f"--offload-arch={ARCH}", "-shared", "-fPIC", *objs, "-o", out + ".tmp"], verbose)
+    os.replace(out + ".tmp", out)
+    return out
 
 
 def build(verbose: bool = False) -> None:
@@ -87,4 +98,12 @@ def build(verbose: bool = False) -> None:
 
 
 if __name__ == "__main__":
-    build(verbose=True)
+    import argparse
+    ap = argparse.ArgumentParser(description="build the native libraries")
+    ap.add_argument("--variant", default="", help="build variants/libmxfp_<VARIANT>.so with -D knobs")
+    ap.add_argument("-D", dest="defines", action="append", default=[], metavar="KNOB=VALUE")
+    a = ap.parse_args()
+    if a.variant:
+        print(build_hip(verbose=True, defines=a.defines, variant=a.variant))
+    else:
+        build(verbose=True)

@@ -23,8 +23,9 @@
 //
 // NVFP4 (NVFP4 model card, Model Details) has E4M3 scales per 16 elements that the scaled MFMA
 // cannot apply, and code * scale needs up to 6 significant bits, more than FP8 holds; it is
-// dequantized exactly to BF16 after staging and run on V_MFMA_F32_32X32X16_BF16, with the
-// product of the two FP32 global scales applied in the epilogue.
+// dequantized exactly after staging, to FP16 in the ring kernel (V_MFMA_F32_32X32X16_F16) and to
+// BF16 in the register-staged one (V_MFMA_F32_32X32X16_BF16), with the product of the two FP32
+// global scales applied in the epilogue.
 #include "mx_common.h"
 #include "mx_internal.h"
 

@@ -339,3 +339,23 @@ def test_attention_binding_checks_arguments_before_any_call(mx):
         mx.attention(q, q, vt(2, 100), 2, layout="sbhd")                  # unknown layout
     with pytest.raises(mx.MxError):
         mx.quantize_vt(torch.zeros((2, 100, D), dtype=torch.bfloat16))    # a host tensor
+
+
+def test_variant_library_selection():
+    """MXFP_LIB points the binding at another build of the library (a compile-time-knob
+    variant); unset, it loads the in-tree libmxfp.so.  Variant names are checked before any
+    compiler runs."""
+    import sys
+    code = "import fp4_block_scaled_amd as m; print(m.LIB_PATH)"
+    env = dict(os.environ)
+    env.pop("MXFP_LIB", None)
+    default = subprocess.run([sys.executable, "-c", code], cwd=ROOT, env=env, capture_output=True,
+                             text=True, check=True).stdout.strip()
+    assert default == os.path.join(ROOT, "fp4_block_scaled_amd", "libmxfp.so")
+    env["MXFP_LIB"] = "/nonexistent/libmxfp_variant.so"
+    chosen = subprocess.run([sys.executable, "-c", code], cwd=ROOT, env=env, capture_output=True,
+                            text=True, check=True).stdout.strip()
+    assert chosen == "/nonexistent/libmxfp_variant.so"
+    from fp4_block_scaled_amd import build
+    with pytest.raises(ValueError):
+        build.build_hip(defines=["MX_RING_PP=0"], variant="../escape")
