@@ -29,30 +29,36 @@ METRIC = "W4A4 MXFP4 linear TFLOPS (quant+GEMM) at Wan-A14B shapes; % MXFP4 MFMA
 PEAK_TFLOPS = {"mxfp4": 10100.0, "mxfp8": 5000.0, "bf16": 2500.0}
 HBM_GBPS = 8000.0
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic.json")
-KERNEL_SOURCES = [os.path.join(ROOT, "fp4_block_scaled_amd", "csrc", f)
-                  for f in ("mx_gemm.hip", "mx_quant.hip", "mx_common.h")]
+CSRC = os.path.join(ROOT, "fp4_block_scaled_amd", "csrc")
 
 
-def kernel_source_hash() -> str:
+def kernel_sources(kernel: str):
+    """The source files a kernel is built from (its own file and the shared headers)."""
+    own = ("mx_gemm.hip" if "gemm_" in kernel else
+           "mx_attn.hip" if ("attn_" in kernel or "quant_vt" in kernel) else "mx_quant.hip")
+    return [os.path.join(CSRC, f) for f in (own, "mx_common.h", "mx_internal.h")]
+
+
+def kernel_source_hash(kernel: str) -> str:
     h = hashlib.sha256()
-    for f in KERNEL_SOURCES:
+    for f in kernel_sources(kernel):
         with open(f, "rb") as fh:
             h.update(fh.read())
     return h.hexdigest()[:16]
 
 
 def measured_traffic(workload: str, kernel: str):
-    """HBM bytes per launch from the committed rocprofv3 counter runs, if they were taken on
-    the current kernel sources; else None."""
+    """HBM bytes per launch of the kernel whose name contains `kernel`, from the committed
+    rocprofv3 counter runs, if they were taken on the current kernel sources; else None."""
     try:
         with open(TRAFFIC_FILE) as f:
             t = json.load(f)
     except (OSError, ValueError):
         return None
-    e = t.get(workload, {}).get(kernel)
-    if not e or e.get("source_hash") != kernel_source_hash():
+    hits = [(name, e) for name, e in t.get(workload, {}).items() if kernel in name]
+    if len(hits) != 1 or hits[0][1].get("source_hash") != kernel_source_hash(hits[0][0]):
         return None
-    return e.get("bytes_per_launch")
+    return hits[0][1].get("bytes_per_launch")
 
 
 def cpu_info():
@@ -84,28 +90,56 @@ def time_events(fn, iters: int, torch, warmup: int = 3):
     return start.elapsed_time(end) / iters
 
 
-MAX_SCLK_MHZ = 2400.0  # the clock the published peaks assume
+def launch_stats(fn, iters: int, torch, warmup: int = 3):
+    """Per-launch milliseconds of fn(): one HIP event pair around each of `iters` launches on the
+    current stream (after `warmup` untimed ones); median, min, mean and max."""
+    import statistics
+    s = torch.cuda.current_stream()
+    for _ in range(warmup):
+        fn()
+    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(iters)]
+    torch.cuda.synchronize()
+    for e0, e1 in ev:
+        e0.record(s)
+        fn()
+        e1.record(s)
+    torch.cuda.synchronize()
+    ms = [e0.elapsed_time(e1) for e0, e1 in ev]
+    return {"median": statistics.median(ms), "min": min(ms), "mean": sum(ms) / len(ms), "max": max(ms),
+            "launches": iters}
+
+
+GEMM_KERNEL = "gemm_mx_ring_kernel<256,256,ping-pong> (MXFP4 x MXFP4, tiled operands, bias, BF16 out)"
 
 
 def sample_sclk(fn, launches: int, torch):
     """Shader clock (MHz) that rocm-smi reports while `launches` calls of fn run back to back (the
-    calls are queued first, the clock is read while they execute); None if it cannot be read."""
+    calls are queued first, the reading is taken while they execute); None if it cannot be read."""
+    import json
     import re
     import shutil
     import subprocess
-    if not shutil.which("rocm-smi"):
+    # under a profiler (a preloaded rocprofiler library) the rocm-smi child would inherit the
+    # preload and initialise the GPU before its interpreter starts: skip the reading there
+    if not shutil.which("rocm-smi") or "rocprof" in os.environ.get("LD_PRELOAD", ""):
         return None
     torch.cuda.synchronize()
     for _ in range(launches):
         fn()
     time.sleep(0.5)
+    sclk = None
     try:
-        r = subprocess.run(["rocm-smi", "--showclocks"], capture_output=True, text=True, timeout=20)
-        m = re.search(r"sclk clock level: \d+: \((\d+)Mhz\)", r.stdout)
-    except (OSError, subprocess.SubprocessError):
-        m = None
+        r = subprocess.run(["rocm-smi", "--showclocks", "--json"], capture_output=True, text=True,
+                           timeout=20)
+        for card in json.loads(r.stdout).values():
+            for key, val in (card.items() if isinstance(card, dict) else ()):
+                m = re.search(r"(\d+)\s*mhz", str(val), re.IGNORECASE)
+                if sclk is None and key.lower().startswith("sclk clock speed") and m:
+                    sclk = float(m.group(1))
+    except (OSError, subprocess.SubprocessError, ValueError):
+        pass
     torch.cuda.synchronize()
-    return float(m.group(1)) if m else None
+    return sclk
 
 
 def cpu_baseline_mx(wl, a_bits, w_codes, w_scales, b_bits, rows: int):
@@ -144,6 +178,28 @@ def cpu_baseline_mx(wl, a_bits, w_codes, w_scales, b_bits, rows: int):
     return res
 
 
+def smallest_instance_latency(torch, mx, synth, iters: int = 200, warmup: int = 50):
+    """The smallest MXFP4 instance (256x512x512, bias, BF16 out): per-launch latency of the whole
+    linear (quantizer + GEMM) and of each kernel, in microseconds.  Launch-bound: no roofline
+    fraction applies."""
+    import numpy as np
+    wl = synth.WORKLOADS["mxfp4_256x512x512"]
+    to_dev = lambda bits, dt: torch.from_numpy(bits.view(np.int16)).view(dt).cuda()
+    a = to_dev(synth.bits16(synth.to_bf16(wl.activation())), torch.bfloat16)
+    wq = mx.quantize(to_dev(synth.bits16(synth.to_bf16(wl.weight())), torch.bfloat16), "mxfp4", layout="tiled")
+    bias = to_dev(synth.bits16(synth.to_f16(wl.bias())), torch.float16)
+    out = torch.empty((wl.M, wl.N), dtype=torch.bfloat16, device="cuda")
+    ws = torch.empty(mx.linear_workspace_bytes(wl.M, wl.K, "mxfp4"), dtype=torch.uint8, device="cuda")
+    aq = mx.empty_qmatrix(wl.M, wl.K, "mxfp4", layout="tiled")
+    res = {"workload": wl.name, "M": wl.M, "K": wl.K, "N": wl.N}
+    for name, fn in (("linear", lambda: mx.linear(a, wq, bias, out=out, workspace=ws)),
+                     ("quantizer", lambda: mx.quantize(a, "mxfp4", out=aq)),
+                     ("gemm", lambda: mx.linear_q(aq, wq, bias, out=out))):
+        st = launch_stats(fn, iters, torch, warmup)
+        res[name + "_us"] = {k: (v * 1e3 if k != "launches" else v) for k, v in st.items()}
+    return res
+
+
 def bench_mx_linear(args, torch, mx, synth):
     import numpy as np
     wl = synth.WORKLOADS[args.workload]
@@ -175,6 +231,9 @@ def bench_mx_linear(args, torch, mx, synth):
     quant()
     ms_quant = time_events(quant, args.steps, torch)
     ms_gemm = time_events(gemm, args.steps, torch)
+    # per-launch distributions (one event pair per launch, outside the timed region above)
+    dist = {"step": launch_stats(step, args.steps, torch, 1), "quantizer": launch_stats(quant, args.steps, torch, 1),
+            "gemm": launch_stats(gemm, args.steps, torch, 1)}
 
     # the shader clock during about 1.5 s of back-to-back GEMMs (the published peak assumes 2.4 GHz)
     sclk = sample_sclk(gemm, max(100, int(1500.0 / ms_gemm)), torch)
@@ -183,7 +242,7 @@ def bench_mx_linear(args, torch, mx, synth):
     quant_bytes = M * K * 2 + M * K // 2 + M * K // 32
     gemm_bytes = M * K // 2 + M * K // 32 + N * K // 2 + N * K // 32 + M * N * 2 + (N * 2 if b is not None else 0)
     achieved = flops / (ms_gemm * 1e-3) / 1e12
-    traffic = measured_traffic(args.workload, "gemm")
+    traffic = measured_traffic(args.workload, "gemm_mx_ring_kernel<256, 256")
     res = {
         "metric": METRIC,
         "value": flops / (ms_step * 1e-3) / 1e12,
@@ -203,22 +262,25 @@ def bench_mx_linear(args, torch, mx, synth):
         "roofline": {"bound": "mfma", "achieved": achieved, "peak": PEAK_TFLOPS["mxfp4"],
                      "unit": "TFLOP/s", "frac": achieved / PEAK_TFLOPS["mxfp4"],
                      "traffic": traffic,
-                     "kernel": "gemm_mx_ring_kernel<256,128> (MXFP4 x MXFP4, tiled operands, bias, BF16 out)",
+                     "kernel": GEMM_KERNEL,
                      "algorithmic_flops_per_launch": flops, "ms_per_launch": ms_gemm,
-                     "sclk_mhz_sampled": sclk,
-                     "frac_at_sampled_clock": (achieved / (PEAK_TFLOPS["mxfp4"] * sclk / MAX_SCLK_MHZ)
-                                               if sclk else None)},
+                     "ms_per_launch_median": dist["gemm"]["median"], "ms_per_launch_min": dist["gemm"]["min"],
+                     "sclk_mhz_sampled": sclk},
         "kernels": {
             "quantizer": {"ms": ms_quant, "GB/s": quant_bytes / (ms_quant * 1e-3) / 1e9,
                           "frac_hbm": quant_bytes / (ms_quant * 1e-3) / 1e9 / HBM_GBPS,
                           "algorithmic_bytes": quant_bytes,
-                          "traffic": measured_traffic(args.workload, "quant")},
+                          "traffic": measured_traffic(args.workload, "quant_mx_tiled_kernel<0>")},
             "gemm": {"ms": ms_gemm, "TFLOP/s": achieved, "algorithmic_bytes": gemm_bytes},
             "step_frac_of_mxfp4_peak": flops / (ms_step * 1e-3) / 1e12 / PEAK_TFLOPS["mxfp4"],
             "wall_ms_per_step": wall_ms,
+            "per_launch_ms": dist,
+            "step_tflops_at_median": flops / (dist["step"]["median"] * 1e-3) / 1e12,
         },
         "setup_s": setup_s,
     }
+    if wl.name == "wan_a14b_attn_75600x5120x5120":
+        res["smallest_instance"] = smallest_instance_latency(torch, mx, synth)
     if not args.no_cpu:
         wrm = mx.relayout(wq)  # the oracle reads the canonical layout
         res["cpu_baseline"] = cpu_baseline_mx(wl, a_bits, wrm.codes.cpu().numpy(),
@@ -305,6 +367,7 @@ def bench_variant(args, torch, mx, synth):
         for _ in range(args.warmup):
             step()
         ms = time_events(step, args.steps, torch)
+        kernels["step_per_launch_ms"] = launch_stats(step, args.steps, torch, 1)
         byts = M * K * 2 + M * K // 2 + M * K // 32 + 2 * K * 4
         v = byts / (ms * 1e-3) / 1e9
         kernels["speedup_vs_unfused"] = kernels["unfused_ms"] / ms
@@ -319,6 +382,7 @@ def bench_variant(args, torch, mx, synth):
     for _ in range(args.warmup):
         step()
     ms = time_events(step, args.steps, torch)
+    kernels["step_per_launch_ms"] = launch_stats(step, args.steps, torch, 1)
     v = flops / (ms * 1e-3) / 1e12
     return {"metric": f"{wl.name} TFLOPS (quant+GEMM)", "value": v, "unit": "TFLOP/s", "n_gpus": 1,
             "steps": args.steps, "warmup": args.warmup, "ms_per_step": ms, "higher_is_better": True,
@@ -351,6 +415,7 @@ def bench_attention(args, torch, mx, synth):
         step()
     ms = time_events(step, args.steps, torch)
     kernels["attention_ms"] = time_events(attn, args.steps, torch)
+    kernels["attention_per_launch_ms"] = launch_stats(attn, min(args.steps, 10), torch, 1)
     kernels["attention_tflops"] = flops / (kernels["attention_ms"] * 1e-3) / 1e12
     kernels["quant_qk_ms"] = time_events(lambda: (mx.quantize(q, "mxfp4", out=qg), mx.quantize(k, "mxfp4", out=kg)),
                                          args.steps, torch)
@@ -415,6 +480,9 @@ def _counter_means(csv_path: str, counter: str):
 
 
 def ingest_counters(args, fetch_csv: str, write_csv: str, out_md: str):
+    """Every kernel of the counter runs except the calibration copy: HBM bytes per launch (the
+    counters scaled by the copy calibration) into profiles/traffic.json under the workload, keyed
+    by kernel name, and a table appended to out_md."""
     fetch = _counter_means(fetch_csv, "FETCH_SIZE")
     write = _counter_means(write_csv, "WRITE_SIZE")
 
@@ -427,25 +495,25 @@ def ingest_counters(args, fetch_csv: str, write_csv: str, out_md: str):
     kc_f, kc_w = find(fetch, COPY_KERNEL_HINT), find(write, COPY_KERNEL_HINT)
     f_scale = COPY_BYTES / (fetch[kc_f][0] * 1024.0)
     w_scale = COPY_BYTES / (write[kc_w][0] * 1024.0)
-    entries = {"gemm": ("gemm_mx_ring_kernel",), "quant": ("quant_mx_tiled_kernel",)}
     try:
         with open(TRAFFIC_FILE) as f:
             table = json.load(f)
     except (OSError, ValueError):
         table = {}
-    wl = table.setdefault(args.workload, {})
+    wl = table[args.workload] = {}
     lines = [f"# HBM traffic per launch, workload {args.workload}", "",
              f"Copy calibration: {kc_f}: FETCH_SIZE {fetch[kc_f][0]:.0f} KiB, "
              f"WRITE_SIZE {write[kc_w][0]:.0f} KiB per launch for a {COPY_BYTES} B copy; "
              f"scale factors {f_scale:.4f} (fetch), {w_scale:.4f} (write).", "",
              "| kernel | dispatches | FETCH_SIZE KiB | WRITE_SIZE KiB | HBM read B | HBM write B |",
              "|---|---|---|---|---|---|"]
-    for key, subs in entries.items():
-        kf, kw = find(fetch, *subs), find(write, *subs)
-        rd, wr = fetch[kf][0] * 1024.0 * f_scale, write[kw][0] * 1024.0 * w_scale
-        wl[key] = {"bytes_per_launch": rd + wr, "read_bytes": rd, "write_bytes": wr,
-                   "source_hash": kernel_source_hash(), "kernel": kf}
-        lines.append(f"| {kf[:90]} | {fetch[kf][1]} | {fetch[kf][0]:.0f} | {write[kw][0]:.0f} | "
+    for kf in sorted(fetch):
+        if COPY_KERNEL_HINT in kf or kf not in write or kf.startswith("void at::"):
+            continue  # the calibration copy and torch's own fill kernel
+        rd, wr = fetch[kf][0] * 1024.0 * f_scale, write[kf][0] * 1024.0 * w_scale
+        wl[kf] = {"bytes_per_launch": rd + wr, "read_bytes": rd, "write_bytes": wr,
+                  "source_hash": kernel_source_hash(kf)}
+        lines.append(f"| {kf[:110]} | {fetch[kf][1]} | {fetch[kf][0]:.0f} | {write[kf][0]:.0f} | "
                      f"{rd:.4g} | {wr:.4g} |")
     with open(TRAFFIC_FILE, "w") as f:
         json.dump(table, f, indent=1, sort_keys=True)
