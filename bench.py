@@ -192,11 +192,31 @@ def smallest_instance_latency(torch, mx, synth, iters: int = 200, warmup: int = 
     ws = torch.empty(mx.linear_workspace_bytes(wl.M, wl.K, "mxfp4"), dtype=torch.uint8, device="cuda")
     aq = mx.empty_qmatrix(wl.M, wl.K, "mxfp4", layout="tiled")
     res = {"workload": wl.name, "M": wl.M, "K": wl.K, "N": wl.N}
-    for name, fn in (("linear", lambda: mx.linear(a, wq, bias, out=out, workspace=ws)),
+    linear = lambda: mx.linear(a, wq, bias, out=out, workspace=ws)
+    for name, fn in (("linear", linear),
                      ("quantizer", lambda: mx.quantize(a, "mxfp4", out=aq)),
                      ("gemm", lambda: mx.linear_q(aq, wq, bias, out=out))):
         st = launch_stats(fn, iters, torch, warmup)
         res[name + "_us"] = {k: (v * 1e3 if k != "launches" else v) for k, v in st.items()}
+    # the same call replayed from a captured HIP graph (the path allocates nothing when out and
+    # workspace are given), alone and as 16 calls in one graph
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        for _ in range(3):
+            linear()
+    torch.cuda.current_stream().wait_stream(side)
+    torch.cuda.synchronize()
+    g1, g16 = torch.cuda.CUDAGraph(), torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g1):
+        linear()
+    with torch.cuda.graph(g16):
+        for _ in range(16):
+            linear()
+    st = launch_stats(g1.replay, iters, torch, warmup)
+    res["linear_graph_us"] = {k: (v * 1e3 if k != "launches" else v) for k, v in st.items()}
+    st = launch_stats(g16.replay, max(1, iters // 16), torch, max(1, warmup // 16))
+    res["linear_graph16_us_per_call"] = {k: (v * 1e3 / 16 if k != "launches" else v) for k, v in st.items()}
     return res
 
 
