@@ -175,6 +175,14 @@ def cpu_baseline_mx(wl, a_bits, w_codes, w_scales, b_bits, rows: int):
                                 "rows": r1, "seconds": d1}
     except ImportError:
         pass
+    # the oracle's quantizer alone on the full activation (all threads), as GB/s of the same
+    # algorithmic bytes the GPU quantizer is measured on
+    t0 = time.perf_counter()
+    O.quantize_mx_bf16(a_bits, O.E2M1)
+    dq = time.perf_counter() - t0
+    qbytes = wl.M * wl.K * 2 + wl.M * wl.K // 2 + wl.M * wl.K // 32
+    res["quantizer"] = {"value": qbytes / dq / 1e9, "unit": "GB/s", "seconds": dq,
+                        "sample": f"the full {wl.M}x{wl.K} activation"}
     return res
 
 
@@ -285,7 +293,9 @@ def bench_mx_linear(args, torch, mx, synth):
                      "kernel": GEMM_KERNEL,
                      "algorithmic_flops_per_launch": flops, "ms_per_launch": ms_gemm,
                      "ms_per_launch_median": dist["gemm"]["median"], "ms_per_launch_min": dist["gemm"]["min"],
-                     "sclk_mhz_sampled": sclk},
+                     "sclk_mhz_sampled": sclk,
+                     # context only: the achieved rate against the peak scaled to that clock
+                     "frac_at_sampled_clock": (achieved / (PEAK_TFLOPS["mxfp4"] * sclk / 2400.0)) if sclk else None},
         "kernels": {
             "quantizer": {"ms": ms_quant, "GB/s": quant_bytes / (ms_quant * 1e-3) / 1e9,
                           "frac_hbm": quant_bytes / (ms_quant * 1e-3) / 1e9 / HBM_GBPS,
