@@ -37,12 +37,15 @@ typedef short i16x2 __attribute__((ext_vector_type(2)));
 template <int ELEM>  // 0: E2M1 (emax 2), 1: E4M3 (emax 8)
 __device__ __forceinline__ void quant_mx8(const uint4 v, uint32_t& lo, uint32_t& hi, uint32_t& sbyte) {
   uint32_t w[4] = {v.x, v.y, v.z, v.w};
-  uint32_t amax = 0;
+  u16x2 m2 = {0, 0};  // per-half maxima of the magnitudes (packed 16-bit max)
 #pragma unroll
   for (int i = 0; i < 4; ++i) {
-    uint32_t l = w[i] & 0x7FFFu, h = (w[i] >> 16) & 0x7FFFu;
-    amax = max(amax, max(l, h));
+    u16x2 mag;
+    const uint32_t wm = w[i] & 0x7FFF7FFFu;
+    __builtin_memcpy(&mag, &wm, 4);
+    m2 = __builtin_elementwise_max(m2, mag);
   }
+  uint32_t amax = max((uint32_t)m2.x, (uint32_t)m2.y);
   amax = max(amax, quad_xor1(amax));
   amax = max(amax, quad_xor2(amax));
   const bool bad = amax >= 0x7F80u;  // NaN or Inf in the group
@@ -164,7 +167,7 @@ __global__ void __launch_bounds__(256) quant_mx_tiled_kernel(const uint16_t* __r
 // quantizer then codes that BF16 tensor exactly as the standalone quantizer would (same group
 // routine).  OUT 0 writes the BF16 h instead (the unfused producer).  Padding rows of a tiled
 // output get zero codes and zero scale bytes.
-constexpr int NORM_ROWS = 4, NORM_WAVES = 8, NORM_RPL = NORM_ROWS / 4;  // rows per lane
+constexpr int NORM_ROWS = 4, NORM_WAVES = 8;  // rows per step (one per 16 lanes), waves
 
 template <int ELEM, int OUT, int CPW>  // OUT 0: BF16 h, 1: codes row-major, 2: codes tiled
 __global__ void __launch_bounds__(NORM_WAVES * 64, 2) norm_quant_kernel(const uint16_t* __restrict__ x, int64_t rows,
@@ -196,97 +199,91 @@ __global__ void __launch_bounds__(NORM_WAVES * 64, 2) norm_quant_kernel(const ui
   const int g4 = cs >> 2, part = cs & 3;
   const float inv_n = 1.0f / (float)cols;
   const int64_t nrb = (OUT == 2 ? tiled_rows(rows) : rows + NORM_ROWS - 1) / NORM_ROWS;
-  // the rows of step rb (zero past the matrix); the next step's are loaded before this one is
-  // reduced, so their latency overlaps this step's work
-  auto fetch = [&](int64_t rb, uint4 (&dst)[CPW][NORM_RPL]) {
+  // this lane's columns of each chunk (loop-invariant), whether they exist, and the byte offset
+  // of its 16-byte piece from the step's first row (past the end of the buffer for a missing
+  // column: the bounds-checked buffer load then reads zero)
+  int64_t colv[CPW];
+  bool colok[CPW];
+  uint32_t loff[CPW];
 #pragma unroll
-    for (int c = 0; c < CPW; ++c) {
-      const int64_t col = (int64_t)(wave * CPW + c) * 128 + cs * 8;
+  for (int c = 0; c < CPW; ++c) {
+    colv[c] = (int64_t)(wave * CPW + c) * 128 + cs * 8;
+    colok[c] = colv[c] < cols;
+    loff[c] = colok[c] ? (uint32_t)((rsub * ld + colv[c]) * 2) : 0x80000000u;
+  }
+  // the rows of step rb through a buffer descriptor that ends after the last valid element of
+  // the step's last valid row, so rows past the matrix (and steps past the last) read zero with
+  // no per-lane test; the next step's are loaded as soon as the current step's are unpacked, so
+  // their latency overlaps this step's work
+  auto fetch = [&](int64_t rb, uint4 (&dst)[CPW]) {
+    const int64_t r0 = rb * NORM_ROWS;
+    const int64_t vr = rb < nrb ? min((int64_t)NORM_ROWS, rows - r0) : 0;
+    const auto rs = make_rsrc(vr > 0 ? x + r0 * ld : x, vr > 0 ? (uint32_t)(((vr - 1) * ld + cols) * 2) : 0u);
 #pragma unroll
-      for (int i = 0; i < NORM_RPL; ++i) {
-        const int64_t r = rb * NORM_ROWS + rsub + 4 * i;
-        dst[c][i] = rb < nrb && r < rows && col < cols ? load_stream16(x + r * ld + col) : make_uint4(0, 0, 0, 0);
-      }
-    }
+    for (int c = 0; c < CPW; ++c) dst[c] = load16(rs, loff[c]);
   };
-  uint4 vn[CPW][NORM_RPL];
+  uint4 vn[CPW];
   fetch(blockIdx.x, vn);
   for (int64_t rb = blockIdx.x; rb < nrb; rb += gridDim.x) {
-    const int64_t r0 = rb * NORM_ROWS;
-    uint4 v[CPW][NORM_RPL];
-#pragma unroll
-    for (int c = 0; c < CPW; ++c)
-#pragma unroll
-      for (int i = 0; i < NORM_RPL; ++i) v[c][i] = vn[c][i];
-    fetch(rb + gridDim.x, vn);
-    // pass 1: row sums (columns past cols read as zero)
-    float acc[NORM_RPL];
-#pragma unroll
-    for (int i = 0; i < NORM_RPL; ++i) acc[i] = 0.0f;
-#pragma unroll
-    for (int c = 0; c < CPW; ++c)
-#pragma unroll
-      for (int i = 0; i < NORM_RPL; ++i) {
-        const uint32_t w[4] = {v[c][i].x, v[c][i].y, v[c][i].z, v[c][i].w};
-#pragma unroll
-        for (int e = 0; e < 4; ++e) acc[i] += bf16_to_f32(w[e] & 0xFFFFu) + __uint_as_float(w[e] & 0xFFFF0000u);
-      }
-#pragma unroll
-    for (int i = 0; i < NORM_RPL; ++i)
-#pragma unroll
-      for (int m = 1; m < 16; m <<= 1) acc[i] += __shfl_xor(acc[i], m);
-    if (cs == 0)
-#pragma unroll
-      for (int i = 0; i < NORM_RPL; ++i) psum[wave * NORM_ROWS + rsub + 4 * i] = acc[i];
-    __syncthreads();
-    float mean[NORM_RPL];
-#pragma unroll
-    for (int i = 0; i < NORM_RPL; ++i) {
-      float t = 0.0f;
-      for (int w = 0; w < nw; ++w) t += psum[w * NORM_ROWS + rsub + 4 * i];
-      mean[i] = t * inv_n;
-    }
-    // pass 2: sums of squared deviations over the valid columns
-#pragma unroll
-    for (int i = 0; i < NORM_RPL; ++i) acc[i] = 0.0f;
+    const int64_t r = rb * NORM_ROWS + rsub;
+    // unpack once: the three passes read the same fp32 values
+    float xv[CPW][8];
 #pragma unroll
     for (int c = 0; c < CPW; ++c) {
-      const bool valid = (int64_t)(wave * CPW + c) * 128 + cs * 8 < cols;
+      const uint32_t w[4] = {vn[c].x, vn[c].y, vn[c].z, vn[c].w};
 #pragma unroll
-      for (int i = 0; i < NORM_RPL; ++i) {
-        const uint32_t w[4] = {v[c][i].x, v[c][i].y, v[c][i].z, v[c][i].w};
-        float q = 0.0f;
-#pragma unroll
-        for (int e = 0; e < 4; ++e) {
-          const float d0 = bf16_to_f32(w[e] & 0xFFFFu) - mean[i];
-          const float d1 = __uint_as_float(w[e] & 0xFFFF0000u) - mean[i];
-          q += d0 * d0 + d1 * d1;
-        }
-        acc[i] += valid ? q : 0.0f;
+      for (int e = 0; e < 4; ++e) {
+        xv[c][2 * e] = __uint_as_float(w[e] << 16);
+        xv[c][2 * e + 1] = __uint_as_float(w[e] & 0xFFFF0000u);
       }
     }
+    fetch(rb + gridDim.x, vn);
+    // pass 1: row sums (columns past cols read as zero)
+    float acc = 0.0f;
 #pragma unroll
-    for (int i = 0; i < NORM_RPL; ++i)
+    for (int c = 0; c < CPW; ++c)
 #pragma unroll
-      for (int m = 1; m < 16; m <<= 1) acc[i] += __shfl_xor(acc[i], m);
-    if (cs == 0)
+      for (int e = 0; e < 4; ++e) acc += xv[c][2 * e] + xv[c][2 * e + 1];
 #pragma unroll
-      for (int i = 0; i < NORM_RPL; ++i) psq[wave * NORM_ROWS + rsub + 4 * i] = acc[i];
+    for (int m = 1; m < 16; m <<= 1) acc += __shfl_xor(acc, m);
+    if (cs == 0) psum[wave * NORM_ROWS + rsub] = acc;
     __syncthreads();
-    float rstd[NORM_RPL];
-#pragma unroll
-    for (int i = 0; i < NORM_RPL; ++i) {
+    float mean;
+    {
       float t = 0.0f;
-      for (int w = 0; w < nw; ++w) t += psq[w * NORM_ROWS + rsub + 4 * i];
-      rstd[i] = __builtin_amdgcn_rsqf(t * inv_n + eps);
+      for (int w = 0; w < nw; ++w) t += psum[w * NORM_ROWS + rsub];
+      mean = t * inv_n;
+    }
+    // pass 2: sums of squared deviations over the valid columns
+    acc = 0.0f;
+#pragma unroll
+    for (int c = 0; c < CPW; ++c) {
+      float q = 0.0f;
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        const float d0 = xv[c][2 * e] - mean;
+        const float d1 = xv[c][2 * e + 1] - mean;
+        q += d0 * d0 + d1 * d1;
+      }
+      acc += colok[c] ? q : 0.0f;
+    }
+#pragma unroll
+    for (int m = 1; m < 16; m <<= 1) acc += __shfl_xor(acc, m);
+    if (cs == 0) psq[wave * NORM_ROWS + rsub] = acc;
+    __syncthreads();
+    float rstd;
+    {
+      float t = 0.0f;
+      for (int w = 0; w < nw; ++w) t += psq[w * NORM_ROWS + rsub];
+      rstd = __builtin_amdgcn_rsqf(t * inv_n + eps);
     }
     // pass 3: h, BF16, then the output
 #pragma unroll
     for (int c = 0; c < CPW; ++c) {
       const int64_t kb = wave * CPW + c;
       if (kb >= nkc) break;  // uniform across the wave
-      const int64_t col = kb * 128 + cs * 8;
-      const bool valid = col < cols;
+      const int64_t col = colv[c];
+      const bool valid = colok[c];
       float a[8], b[8];
       if (valid) {
         *(float4*)&a[0] = *(const float4*)&A[col];
@@ -297,33 +294,28 @@ __global__ void __launch_bounds__(NORM_WAVES * 64, 2) norm_quant_kernel(const ui
 #pragma unroll
         for (int e = 0; e < 8; ++e) a[e] = b[e] = 0.0f;
       }
+      uint32_t hb[4];
 #pragma unroll
-      for (int i = 0; i < NORM_RPL; ++i) {
-        const int64_t r = r0 + rsub + 4 * i;
-        const uint32_t w[4] = {v[c][i].x, v[c][i].y, v[c][i].z, v[c][i].w};
-        uint32_t hb[4];
-#pragma unroll
-        for (int e = 0; e < 4; ++e) {
-          const float h0 = (bf16_to_f32(w[e] & 0xFFFFu) - mean[i]) * rstd[i] * a[2 * e] + b[2 * e];
-          const float h1 = (__uint_as_float(w[e] & 0xFFFF0000u) - mean[i]) * rstd[i] * a[2 * e + 1] + b[2 * e + 1];
-          hb[e] = pack_bf16x2(h0, h1);
-        }
-        if constexpr (OUT == 0) {
-          if (r < rows && valid) *(uint4*)(y + r * ld_y + col) = make_uint4(hb[0], hb[1], hb[2], hb[3]);
+      for (int e = 0; e < 4; ++e) {
+        const float h0 = (xv[c][2 * e] - mean) * rstd * a[2 * e] + b[2 * e];
+        const float h1 = (xv[c][2 * e + 1] - mean) * rstd * a[2 * e + 1] + b[2 * e + 1];
+        hb[e] = pack_bf16x2(h0, h1);
+      }
+      if constexpr (OUT == 0) {
+        if (r < rows && valid) *(uint4*)(y + r * ld_y + col) = make_uint4(hb[0], hb[1], hb[2], hb[3]);
+      } else {
+        uint32_t lo, hi, sbyte;
+        quant_mx8<ELEM>(make_uint4(hb[0], hb[1], hb[2], hb[3]), lo, hi, sbyte);
+        if constexpr (OUT == 2) {
+          if (r >= rows) lo = hi = sbyte = 0;  // padding rows of the tiled layout
+          if (ELEM == 0) *(uint32_t*)(codes + tiled_fp4_off(r, kb, g4, nkc) + part * 4) = lo;
+          else *(uint2*)(codes + tiled_fp8_off(r, kb, 2 * g4 + (part >> 1), nkc) + (part & 1) * 8) = make_uint2(lo, hi);
+          if (part == 0) scales[tiled_scale_off(r, kb, nkc) + g4] = (uint8_t)sbyte;
         } else {
-          uint32_t lo, hi, sbyte;
-          quant_mx8<ELEM>(make_uint4(hb[0], hb[1], hb[2], hb[3]), lo, hi, sbyte);
-          if constexpr (OUT == 2) {
-            if (r >= rows) lo = hi = sbyte = 0;  // padding rows of the tiled layout
-            if (ELEM == 0) *(uint32_t*)(codes + tiled_fp4_off(r, kb, g4, nkc) + part * 4) = lo;
-            else *(uint2*)(codes + tiled_fp8_off(r, kb, 2 * g4 + (part >> 1), nkc) + (part & 1) * 8) = make_uint2(lo, hi);
-            if (part == 0) scales[tiled_scale_off(r, kb, nkc) + g4] = (uint8_t)sbyte;
-          } else {
-            if (r < rows && valid) {
-              if (ELEM == 0) *(uint32_t*)(codes + r * (cols >> 1) + (col >> 1)) = lo;
-              else *(uint2*)(codes + r * cols + col) = make_uint2(lo, hi);
-              if (part == 0) scales[r * (cols >> 5) + (col >> 5)] = (uint8_t)sbyte;
-            }
+          if (r < rows && valid) {
+            if (ELEM == 0) *(uint32_t*)(codes + r * (cols >> 1) + (col >> 1)) = lo;
+            else *(uint2*)(codes + r * cols + col) = make_uint2(lo, hi);
+            if (part == 0) scales[r * (cols >> 5) + (col >> 5)] = (uint8_t)sbyte;
           }
         }
       }
@@ -704,6 +696,8 @@ hipError_t launch_norm_quant(const uint16_t* x, int64_t rows, int64_t cols, int6
   if (rows == 0) return hipSuccess;
   const int64_t nkc = (cols + 127) / 128;
   if (nkc > NORM_WAVES * 8) return hipErrorInvalidValue;
+  // a step's four rows are addressed with 32-bit buffer offsets below 2^31
+  if ((NORM_ROWS * ld + cols) * 2 >= ((int64_t)1 << 31)) return hipErrorInvalidValue;
   const int cpw = (int)((nkc + NORM_WAVES - 1) / NORM_WAVES);
   const int nw = (int)((nkc + cpw - 1) / cpw);
   const int threads = nw * 64;
