@@ -629,3 +629,40 @@ def test_full_size_nvfp4(mx):
     wc, ws = O.quantize_nv_bf16(w_bits, sg_w)
     y_ref, abs_sum = O.linear_ref_nv(ac, as_, sg_a, wc, ws, sg_w, wl.K, b_bits)
     assert_within(ys, y_ref, abs_sum, what="NVFP4, full size")
+
+
+@pytest.mark.parametrize("act,M,K,N", [(a, 300, 512, 256) for a in ("mxfp4", "mxfp8", "nvfp4")] +
+                         [(a, 600, 1024, 512) for a in ("mxfp4", "mxfp8", "nvfp4")] +
+                         [("mxfp4", 4096, 256, 4096)])  # 256 tiles of 256 x 256: the ping-pong kernel
+def test_nan_and_inf_activations_make_their_rows_nan(mx, act, M, K, N):
+    """A NaN or an infinity in an activation block quantizes to the NaN scale (0xFF for E8M0,
+    0x7F for E4M3) with zero codes; the block then decodes to NaN, so every output of that row is
+    NaN, in the oracle's dequantize-then-GEMM and on the GPU.  The other rows are unaffected."""
+    a_bits = activation_bits(M, K, seed_base=16000 + M, factor=30.0)
+    a_bits[3, 40] = 0x7FC0     # NaN
+    a_bits[100, K - 1] = 0x7F80  # +Inf
+    a_bits[M - 1, 0] = 0xFF80    # -Inf, in the last row
+    bad = np.zeros(M, dtype=bool)
+    bad[[3, 100, M - 1]] = True
+    w_bits = weight_bits(N, K, seed=16100, sigma=0.02)
+    b_bits = f16_bits(synth.normal_f32(16200, (N,), 0.01))
+    if act == "nvfp4":
+        sg_a = O.nv_global_scale(40.0)
+        wq = mx.quantize_weight_nvfp4(to_dev_bf16(w_bits))
+        y = mx.linear(to_dev_bf16(a_bits), wq, to_dev_f16(b_bits), act_fmt="nvfp4",
+                      act_global_scale=sg_a, out_dtype=torch.float32)
+        ac, as_ = O.quantize_nv_bf16(a_bits, sg_a)
+        wc, ws = O.quantize_nv_bf16(w_bits, wq.global_scale)
+        y_ref, abs_sum = O.linear_ref_nv(ac, as_, sg_a, wc, ws, wq.global_scale, K, b_bits)
+    else:
+        wq = mx.quantize(to_dev_bf16(w_bits), "mxfp4")
+        y = mx.linear(to_dev_bf16(a_bits), wq, to_dev_f16(b_bits), act_fmt=act, out_dtype=torch.float32)
+        elem = O.E4M3 if act == "mxfp8" else O.E2M1
+        ac, as_ = O.quantize_mx_bf16(a_bits, elem)
+        wc, ws = O.quantize_mx_bf16(w_bits, O.E2M1)
+        y_ref, abs_sum = O.linear_ref_mx(ac, as_, elem, wc, ws, K, b_bits)
+    torch.cuda.synchronize()
+    yg = y.cpu().numpy()
+    assert np.isnan(y_ref[bad]).all() and np.isfinite(y_ref[~bad]).all()
+    assert np.isnan(yg[bad]).all(), f"{act}: rows with a NaN scale are not all NaN on the GPU"
+    assert_within(yg[~bad], y_ref[~bad], abs_sum[~bad], what=f"{act} linear, finite rows")
