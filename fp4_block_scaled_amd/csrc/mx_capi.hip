@@ -358,11 +358,11 @@ size_t mx_linear_workspace_bytes(int64_t M, int64_t K, int32_t act_fmt, int32_t 
   return b;
 }
 
-static mx_status run_gemm(const uint8_t* a_codes, const uint8_t* a_scales, float a_gscale,
-                          int32_t act_fmt, bool a_is_tiled, int64_t M, int64_t K, const mx_qmatrix* w,
-                          const uint16_t* bias, const uint16_t* lr_u, const mx_lowrank* lr,
-                          int32_t epilogue, int32_t out_dtype, void* out, int64_t ld_out,
-                          uint8_t* out_scales, hipStream_t s) {
+static mxk::GemmParams gemm_params(const uint8_t* a_codes, const uint8_t* a_scales, float a_gscale,
+                                   bool a_is_tiled, int64_t M, int64_t K, const mx_qmatrix* w,
+                                   const uint16_t* bias, const uint16_t* lr_u, const mx_lowrank* lr,
+                                   int32_t epilogue, int32_t out_dtype, void* out, int64_t ld_out,
+                                   uint8_t* out_scales) {
   mxk::GemmParams p;
   p.a_codes = a_codes;
   p.a_scales = a_scales;
@@ -385,6 +385,16 @@ static mx_status run_gemm(const uint8_t* a_codes, const uint8_t* a_scales, float
   p.out_f32 = out_dtype == MX_OUT_F32 ? 1 : 0;
   p.a_tiled = a_is_tiled ? 1 : 0;
   p.w_tiled = w->layout == MX_LAYOUT_TILED ? 1 : 0;
+  return p;
+}
+
+static mx_status run_gemm(const uint8_t* a_codes, const uint8_t* a_scales, float a_gscale,
+                          int32_t act_fmt, bool a_is_tiled, int64_t M, int64_t K, const mx_qmatrix* w,
+                          const uint16_t* bias, const uint16_t* lr_u, const mx_lowrank* lr,
+                          int32_t epilogue, int32_t out_dtype, void* out, int64_t ld_out,
+                          uint8_t* out_scales, hipStream_t s) {
+  const mxk::GemmParams p = gemm_params(a_codes, a_scales, a_gscale, a_is_tiled, M, K, w, bias, lr_u, lr,
+                                        epilogue, out_dtype, out, ld_out, out_scales);
   hipError_t e = w->fmt == MX_FMT_NVFP4 ? mxk::launch_gemm_nv(p, s)
                                          : mxk::launch_gemm_mx(p, act_fmt == MX_FMT_MXFP8, w->fmt == MX_FMT_MXFP8, s);
   return hip_status(e, "GEMM launch");
@@ -423,6 +433,13 @@ mx_status run_linear(const uint16_t* a, int64_t M, int64_t K, int64_t ld_a, int3
                      const mx_lowrank* lr, int32_t epilogue, int32_t out_dtype, void* out,
                      int64_t ld_out, uint8_t* out_scales, void* workspace, hipStream_t s) {
   const int32_t rank = lr ? lr->rank : 0;
+  if (act_fmt == MX_FMT_MXFP4 && w->fmt == MX_FMT_MXFP4 && rank == 0 && M > 0) {
+    // a small grid: quantization and GEMM in one launch (same output bits)
+    const mxk::GemmParams p = gemm_params(nullptr, nullptr, 1.0f, false, M, K, w, bias, nullptr, nullptr,
+                                          epilogue, out_dtype, out, ld_out, out_scales);
+    if (mxk::linear_fused_small_ok(p))
+      return hip_status(mxk::launch_linear_fused_small(p, a, ld_a, s), "small linear launch");
+  }
   Workspace ws = carve(workspace, M, K, act_fmt, rank);
   hipError_t e;
   const bool tiled = act_tiled(act_fmt, K);

@@ -232,6 +232,38 @@ __device__ __forceinline__ void quant_fp8_group32(const uint32_t (&w)[16], uint3
   sbyte = bad ? 0xFFu : (uint32_t)(e + 127);
 }
 
+// One lane's 32-element MXFP4 group (16 BF16 pairs), amax within the lane: the standalone MX
+// quantizer's rule and instruction (scale byte floor(log2 amax) - 2 clamped to [-127, 127], then
+// V_CVT_SCALEF32_PK_FP4_BF16).  out[d] byte j codes elements 8d + 2j and 8d + 2j + 1 (low
+// nibble first), the FP4 operand layout.  NaN/Inf in the group: codes 0, scale byte 0xFF.
+__device__ __forceinline__ void quant_fp4_group32(const uint32_t (&w)[16], uint32_t (&out)[4], uint32_t& sbyte) {
+  typedef uint16_t u16x2g __attribute__((ext_vector_type(2)));
+  u16x2g m2 = {0, 0};
+#pragma unroll
+  for (int i = 0; i < 16; ++i) {
+    u16x2g mag;
+    const uint32_t wm = w[i] & 0x7FFF7FFFu;
+    __builtin_memcpy(&mag, &wm, 4);
+    m2 = __builtin_elementwise_max(m2, mag);
+  }
+  const uint32_t amax = max((uint32_t)m2.x, (uint32_t)m2.y);
+  const bool bad = amax >= 0x7F80u;
+  int e = (int)(amax >> 7) - 127 - 2;
+  if (e < -127) e = -127;
+  const float scale = __uint_as_float(e >= -126 ? (uint32_t)(127 + e) << 23 : 0x00400000u);
+#pragma unroll
+  for (int d = 0; d < 4; ++d) {
+    bf2x b[4];
+    __builtin_memcpy(b, &w[4 * d], 16);
+    uint32_t r = __builtin_amdgcn_cvt_scalef32_pk_fp4_bf16(0u, b[0], scale, 0);
+    r = __builtin_amdgcn_cvt_scalef32_pk_fp4_bf16(r, b[1], scale, 1);
+    r = __builtin_amdgcn_cvt_scalef32_pk_fp4_bf16(r, b[2], scale, 2);
+    r = __builtin_amdgcn_cvt_scalef32_pk_fp4_bf16(r, b[3], scale, 3);
+    out[d] = bad ? 0u : r;
+  }
+  sbyte = bad ? 0xFFu : (uint32_t)(e + 127);
+}
+
 // ---------------------------------------------------------------------------------------------
 // cross-lane helpers
 // ---------------------------------------------------------------------------------------------

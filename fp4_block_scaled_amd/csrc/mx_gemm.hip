@@ -1541,6 +1541,107 @@ static hipError_t run_w8a8(const GemmParams& p, hipStream_t s) {
   return hipGetLastError();
 }
 
+// ---------------------------------------------------------------------------------------------
+// Small W4A4 linears in one launch: quantize A and multiply
+// ---------------------------------------------------------------------------------------------
+// When the grid of the ring kernels would be a handful of tiles, the two launches (quantizer,
+// GEMM) and their load latencies are most of the time.  A workgroup of 4 waves takes a 64 x 64
+// output tile: it loads its 64 weight rows (codes and scales) and quantizes its 64 activation
+// rows, each lane one 32-element group with the standalone quantizer's rule, into LDS; then each
+// wave multiplies one 32 x 32 block over the whole K and runs the common epilogue.  The MFMA of
+// chunk c, step s pairs blocks 4c + s (lanes 0-31) and 4c + 2 + s (lanes 32-63), in the ring
+// kernels' order, with one accumulator chained through K from zero, so the output bits equal
+// those of the quantizer + ring GEMM pair.  K % 128 == 0, K <= FS_KMAX (the LDS holds the tile's
+// codes for the whole K, within the 64 KB of dynamic LDS a launch gets by default); A rows past M
+// and W rows past N read as zero.
+constexpr int FS_KMAX = 896;
+constexpr int FS_MAX_TILES = 8;  // ring tiles (256 x 128) up to which the one-launch path is taken
+
+bool linear_fused_small_ok(const GemmParams& p) {
+  const int64_t ring_tiles = (int64_t)((p.M + 255) / 256) * ((p.N + 127) / 128);
+  return p.R == 0 && (p.epi == EPI_BIAS || p.epi == EPI_GELU) && p.K % 128 == 0 && p.K <= FS_KMAX &&
+         p.M > 0 && ring_tiles <= FS_MAX_TILES;
+}
+
+__global__ void __launch_bounds__(256) linear_fused_small_kernel(GemmParams p, const uint16_t* __restrict__ a,
+                                                                 int64_t ld_a) {
+  extern __shared__ __attribute__((aligned(16))) uint8_t fs_lds[];
+  const int K = p.K, kbs = K / 32;      // 32-element blocks per row
+  const int pitch = K / 2 + 16;         // code bytes per LDS row (+16: rows fall in different banks)
+  uint8_t* sW = fs_lds;                 // [64][pitch] weight codes
+  uint8_t* sA = sW + 64 * pitch;        // [64][pitch] activation codes
+  uint8_t* sWs = sA + 64 * pitch;       // [64][kbs] weight scale bytes
+  uint8_t* sAs = sWs + 64 * kbs;        // [64][kbs] activation scale bytes
+  const int tiles_n = (p.N + 63) / 64;
+  const int m0 = (blockIdx.x / tiles_n) * 64, n0 = (blockIdx.x % tiles_n) * 64;
+  const int64_t nkc = K >> 7;
+  for (int i = threadIdx.x; i < 64 * kbs; i += 256) {
+    const int r = i / kbs, kb = i - r * kbs;
+    // weight block: 16 code bytes and one scale byte (row-major or tiled operand layout)
+    const int n = n0 + r;
+    uint4 wc = make_uint4(0u, 0u, 0u, 0u);
+    uint32_t wsb = 0u;
+    if (n < p.N) {
+      if (p.w_tiled) {
+        wc = *(const uint4*)(p.w_codes + tiled_fp4_off(n, kb >> 2, kb & 3, nkc));
+        wsb = p.w_scales[tiled_scale_off(n, kb >> 2, nkc) + (kb & 3)];
+      } else {
+        wc = *(const uint4*)(p.w_codes + (int64_t)n * (K / 2) + kb * 16);
+        wsb = p.w_scales[(int64_t)n * kbs + kb];
+      }
+    }
+    *(uint4*)(sW + r * pitch + kb * 16) = wc;
+    sWs[r * kbs + kb] = (uint8_t)wsb;
+    // activation group: 32 BF16 values, quantized in this lane
+    const int m = m0 + r;
+    uint32_t w[16];
+    if (m < p.M) {
+      const uint16_t* src = a + (int64_t)m * ld_a + kb * 32;
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        const uint4 v = *(const uint4*)(src + 8 * q);
+        w[4 * q] = v.x, w[4 * q + 1] = v.y, w[4 * q + 2] = v.z, w[4 * q + 3] = v.w;
+      }
+    } else {
+#pragma unroll
+      for (int q = 0; q < 16; ++q) w[q] = 0u;
+    }
+    uint32_t ac[4], asb;
+    quant_fp4_group32(w, ac, asb);
+    *(uint4*)(sA + r * pitch + kb * 16) = make_uint4(ac[0], ac[1], ac[2], ac[3]);
+    sAs[r * kbs + kb] = (uint8_t)asb;
+  }
+  __syncthreads();
+  const int lane = lane_id(), r32 = lane & 31, h = lane >> 5;
+  const int wave = threadIdx.x >> 6;
+  const int wn = 32 * (wave & 1), wm = 32 * (wave >> 1);
+  const uint8_t* wrow = sW + (wn + r32) * pitch;
+  const uint8_t* arow = sA + (wm + r32) * pitch;
+  const uint8_t* wsrow = sWs + (wn + r32) * kbs;
+  const uint8_t* asrow = sAs + (wm + r32) * kbs;
+  v16f acc;
+#pragma unroll
+  for (int e = 0; e < 16; ++e) acc[e] = 0.0f;
+  for (int c = 0; c < K / 128; ++c) {
+#pragma unroll
+    for (int st = 0; st < 2; ++st) {
+      const int kb = 4 * c + 2 * h + st;
+      const v4i wf = *(const v4i*)(wrow + kb * 16);
+      const v4i af = *(const v4i*)(arow + kb * 16);
+      acc = mfma_scale_32x32x64_f4f4(wf, af, acc, 4, 4, 0, (int)wsrow[kb], 0, (int)asrow[kb]);
+    }
+  }
+  epilogue_block(p, acc, n0 + wn, m0 + wm);
+}
+
+hipError_t launch_linear_fused_small(const GemmParams& p, const uint16_t* a, int64_t ld_a, hipStream_t s) {
+  if (!linear_fused_small_ok(p)) return hipErrorInvalidValue;
+  const int tiles = ((p.M + 63) / 64) * ((p.N + 63) / 64);
+  const size_t lds = (size_t)2 * 64 * (p.K / 2 + 16) + (size_t)2 * 64 * (p.K / 32);
+  hipLaunchKernelGGL(linear_fused_small_kernel, dim3(tiles), dim3(256), lds, s, p, a, ld_a);
+  return hipGetLastError();
+}
+
 hipError_t launch_gemm_mx(const GemmParams& p, bool act_fp8, bool w_fp8, hipStream_t s) {
   if (p.M == 0) return hipSuccess;
   if (w_fp8) return p.K % 128 == 0 && act_fp8 ? run_w8a8(p, s) : hipErrorInvalidValue;

@@ -56,6 +56,12 @@ struct GemmParams {
 // (W8A8, with act_fp8 and K % 128 == 0 only); otherwise E2M1.
 hipError_t launch_gemm_mx(const GemmParams& p, bool act_fp8, bool w_fp8, hipStream_t s);
 hipError_t launch_gemm_nv(const GemmParams& p, hipStream_t s);
+// MXFP4 x MXFP4 linear on a small grid in one launch, from the BF16 activation a (row m at
+// a + m * ld_a): quantization and GEMM, output bits equal to launch_quant_mx* + launch_gemm_mx.
+// linear_fused_small_ok says when it applies (no low-rank branch, bias/GELU epilogue,
+// K % 128 == 0, K <= 896, at most 8 tiles of 256 x 128).
+bool linear_fused_small_ok(const GemmParams& p);
+hipError_t launch_linear_fused_small(const GemmParams& p, const uint16_t* a, int64_t ld_a, hipStream_t s);
 // u[m, r] = bf16_rne(sum_k x[m, k] * down_t[r, k])
 hipError_t launch_lowrank_down(const uint16_t* x, int64_t ld_x, const uint16_t* down_t, int M,
                                int K, int R, uint16_t* u, hipStream_t s);

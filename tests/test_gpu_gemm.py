@@ -666,3 +666,27 @@ def test_nan_and_inf_activations_make_their_rows_nan(mx, act, M, K, N):
     assert np.isnan(y_ref[bad]).all() and np.isfinite(y_ref[~bad]).all()
     assert np.isnan(yg[bad]).all(), f"{act}: rows with a NaN scale are not all NaN on the GPU"
     assert_within(yg[~bad], y_ref[~bad], abs_sum[~bad], what=f"{act} linear, finite rows")
+
+
+@pytest.mark.parametrize("M,K,N", [(256, 512, 512), (1, 128, 64), (77, 384, 200), (300, 896, 96),
+                                   (512, 256, 512), (2048, 128, 128), (130, 640, 1024)])
+@pytest.mark.parametrize("layout", ["row_major", "tiled"])
+def test_small_linear_one_launch_equals_quantizer_plus_gemm(mx, M, K, N, layout):
+    """Small W4A4 grids run quantization and GEMM in one launch; its output bits equal those of
+    the quantizer followed by the GEMM on the same codes (same MFMA pairing and order), for the
+    bias and GELU epilogues, BF16 and F32 outputs, with and without bias, ragged M and N."""
+    a = to_dev_bf16(activation_bits(M, K, seed_base=17000 + M + K))
+    w = mx.quantize(to_dev_bf16(weight_bits(N, K, seed=17100 + N)), "mxfp4")
+    if layout == "tiled":
+        w = mx.relayout(w)
+    bias = to_dev_f16(f16_bits(synth.normal_f32(17200 + N, (N,), 0.01)))
+    aq = mx.quantize(a, "mxfp4")
+    for b in (bias, None):
+        for epi in ("bias", "bias_gelu"):
+            for od in (torch.float32, torch.bfloat16):
+                one = mx.linear(a, w, b, epilogue=epi, out_dtype=od)
+                two = mx.linear_q(aq, w, b, epilogue=epi, out_dtype=od)
+                torch.cuda.synchronize()
+                assert torch.equal(one.view(torch.int16), two.view(torch.int16)), (epi, od, b is None)
+    y, y_ref, abs_sum, _ = _mx_case(mx, M, K, N, seed=M + 3 * K)
+    assert_within(y.cpu().numpy(), y_ref, abs_sum, what="small linear")
