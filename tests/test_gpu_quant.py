@@ -93,7 +93,9 @@ def test_nv_worked_blocks_on_gpu(mx):
         np.testing.assert_array_equal(unpack_fp4(c[0], 16), b["codes"], err_msg=b["name"])
 
 
-@pytest.mark.parametrize("sg", [1.0, 40.0 / 2688.0, 0.5, 3.0 / 7.0, 1e-3, 0.0625 / 2688.0])
+# 1e-24: block scales whose D = sb * sg falls below the fused test's range (exact thresholds);
+# 1e-30: a global scale outside the block-scale bracket's range (fp64 quotient); 1e20: large
+@pytest.mark.parametrize("sg", [1.0, 40.0 / 2688.0, 0.5, 3.0 / 7.0, 1e-3, 0.0625 / 2688.0, 1e-24, 1e-30, 1e20])
 def test_nv_quantizer_vs_oracle(mx, sg):
     sg = float(np.float32(sg))
     x = synth.activation_f32(4321, 512, 1024, 1.0, 0.01, 30.0)
