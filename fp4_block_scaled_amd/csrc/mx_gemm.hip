@@ -543,7 +543,8 @@ template <int BM, int BN, bool AFP8, bool WFP8 = false, bool PP = false>
 struct RingTile {
   static_assert((BM == 128 || BM == 256) && (BN == 128 || BN == 256), "tile sizes");
   static_assert(!WFP8 || AFP8, "E4M3 weights are paired with E4M3 activations");
-  static_assert(!PP || (BM == 256 && BN == 256 && !AFP8), "ping-pong: 256 x 256 W4A4 tiles");
+  static_assert(!PP || (BM == 256 && BN == 256 && !AFP8) || (BM == 128 && BN == 256 && AFP8 && WFP8),
+                "ping-pong: 256 x 256 W4A4 or 128 x 256 W8A8 tiles");
 #ifndef MX_RING_W256
 #define MX_RING_W256 8
 #endif
@@ -554,7 +555,8 @@ struct RingTile {
   static constexpr int W_BYTES = BN * WROWB, A_BYTES = BM * AROWB;
   static constexpr int WS_BYTES = BN * 4, AS_BYTES = BM * 4;
   static constexpr int STAGE = W_BYTES + A_BYTES + WS_BYTES + AS_BYTES;
-  static constexpr int NSTAGE = PP ? 4 : 3;
+  // ping-pong: 4 stages for W4A4; W8A8 stages are 49.5 KB, so 3 (chunk c + 2 loads in phase c)
+  static constexpr int NSTAGE = PP && !WFP8 ? 4 : 3;
   static constexpr int LDS = NSTAGE * STAGE > BM * BN * 2 ? NSTAGE * STAGE : BM * BN * 2;
   static constexpr int WGS = 2 * LDS <= 160 * 1024 ? 2 : 1;  // workgroups per compute unit
   static constexpr int FN = BN / (NWAVES / 2) / 32, FM = BM / 64;  // 32x32 blocks per wave
@@ -840,22 +842,21 @@ gemm_mx_ring_kernel(GemmParams p) {
     // core of each SIMD is fed by one wave while the other waits on LDS and memory.
     //   phase 2c:     group 0 memory(c),     group 1 MFMA(c - 1)
     //   phase 2c + 1: group 0 MFMA(c),       group 1 memory(c)
-    // Chunk c + 3 goes into the stage of chunk c - 1, whose last reads were in phases 2c - 2 and
-    // 2c - 1.  A memory phase ends by waiting for this wave's loads of chunk c + 1 (chunks c + 2
-    // and c + 3 may fly); the barrier after it publishes them before chunk c + 1 is read (phase
-    // 2c + 2 at the earliest).
-    static_assert(T::NSTAGE == 4, "ping-pong ring depth");
+    // Chunk c + D (D = stages - 1: 3 for W4A4, 2 for W8A8) goes into the stage of chunk c - 1,
+    // whose last reads were in phases 2c - 2 and 2c - 1.  A memory phase ends by waiting for this
+    // wave's loads of chunk c + 1 (the later ones may fly); the barrier after it publishes them
+    // before chunk c + 1 is read (phase 2c + 2 at the earliest).
+    static_assert(T::NSTAGE == 3 || T::NSTAGE == 4, "ping-pong ring depth");
+    constexpr int D = T::NSTAGE - 1;  // a memory phase issues chunk c + D
     const bool g0 = wave < T::NWAVES / 2;
-    issue(0, 0);
-    issue(1, 1);
-    issue(2, 2);
-    wait_vmcnt<2 * T::NDMA>();  // chunk 0 landed
+    static_for<D>([&](auto q) { issue(decltype(q)::value, decltype(q)::value); });
+    wait_vmcnt<(D - 1) * T::NDMA>();  // chunk 0 landed
     barrier_only();
     Frags f;
     auto memory = [&](int c) {
-      issue(c + 3, (c + 3) & 3);  // past the last chunk: empty loads (zero-range descriptors)
-      read_chunk(c & 3, f);
-      wait_vmcnt<2 * T::NDMA>();  // chunk c + 1 landed
+      issue(c + D, (c + D) % T::NSTAGE);  // past the last chunk: empty loads (zero-range descriptors)
+      read_chunk(c % T::NSTAGE, f);
+      wait_vmcnt<(D - 1) * T::NDMA>();  // chunk c + 1 landed
       wait_lds_all();
     };
     auto mfma = [&]() {
@@ -863,8 +864,12 @@ gemm_mx_ring_kernel(GemmParams p) {
         constexpr int S = decltype(sc)::value;
         static_for<T::FN>([&](auto i) {
           static_for<T::FM>([&](auto j) {
-            acc[i][j] = mfma_scale_32x32x64_f4f4(f.wf[S][i], f.af[S][j], acc[i][j], 4, 4, S, (int)f.wsc[i], S,
-                                                 (int)f.asc[j]);
+            if constexpr (WFP8)
+              acc[i][j] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(f.wf[S][i], f.af[S][j], acc[i][j], 0, 0, S,
+                                                                          (int)f.wsc[i], S, (int)f.asc[j]);
+            else
+              acc[i][j] = mfma_scale_32x32x64_f4f4(f.wf[S][i], f.af[S][j], acc[i][j], 4, 4, S, (int)f.wsc[i], S,
+                                                   (int)f.asc[j]);
           });
         });
       });
@@ -1460,13 +1465,18 @@ __global__ void __launch_bounds__(LR_WAVES * 64) lowrank_down_kernel(const uint1
 // ---------------------------------------------------------------------------------------------
 // launchers
 // ---------------------------------------------------------------------------------------------
-// PP: the ping-pong schedule of the 256 x 256 W4A4 tile (MX_RING_PP=0 turns it off).
+// PP: the ping-pong schedule of the 256 x 256 W4A4 tile (MX_RING_PP=0 turns it off) and of the
+// 128 x 256 W8A8 tile (MX_W8_PP).
 #ifndef MX_RING_PP
 #define MX_RING_PP 1
 #endif
+#ifndef MX_W8_PP
+#define MX_W8_PP 0
+#endif
 template <int BM, int BN, bool AFP8, bool WFP8, int EPI, bool OUTF32, bool LR>
 static void run_ring(const GemmParams& p, int grid, hipStream_t s) {
-  constexpr bool PP = MX_RING_PP && BM == 256 && BN == 256 && !AFP8 && !WFP8 && !LR;
+  constexpr bool PP = (MX_RING_PP && BM == 256 && BN == 256 && !AFP8 && !WFP8 && !LR) ||
+                      (MX_W8_PP && BM == 128 && BN == 256 && AFP8 && WFP8 && !LR);
   gemm_mx_ring_kernel<BM, BN, AFP8, WFP8, EPI, OUTF32, LR, PP>
       <<<grid, RingTile<BM, BN, AFP8, WFP8, PP>::NWAVES * 64, 0, s>>>(p);
 }
