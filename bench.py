@@ -39,11 +39,20 @@ def kernel_sources(kernel: str):
     return [os.path.join(CSRC, f) for f in (own, "mx_common.h", "mx_internal.h")]
 
 
+def _code_only(text: str) -> str:
+    """C++ source without comments and with whitespace collapsed: edits to comments or layout
+    leave the hash alone (string literals in these files hold no comment markers)."""
+    import re
+    text = re.sub(r"/\*.*?\*/", " ", text, flags=re.S)
+    text = re.sub(r"//[^\n]*", " ", text)
+    return " ".join(text.split())
+
+
 def kernel_source_hash(kernel: str) -> str:
     h = hashlib.sha256()
     for f in kernel_sources(kernel):
-        with open(f, "rb") as fh:
-            h.update(fh.read())
+        with open(f, encoding="utf-8") as fh:
+            h.update(_code_only(fh.read()).encode())
     return h.hexdigest()[:16]
 
 

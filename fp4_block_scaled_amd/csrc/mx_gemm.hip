@@ -8,7 +8,7 @@
 // of one output row m, 4 consecutive n at a time, in each lane: the epilogue can store them as
 // vectors and reduce a 32-wide re-quantization group with a single cross-lane exchange.
 //
-// Two MX kernels share those conventions:
+// The MX kernels share those conventions:
 //  - the ring kernel (K % 128 == 0, every configuration of the model): an LDS ring of
 //    128-element K chunks filled by direct-to-LDS buffer loads, operands row-major or in the
 //    tiled layout whose 1 KB / 256 B tiles are exactly the LDS images the ring holds.  W4A4 on
@@ -17,7 +17,9 @@
 //    W4A4 grids and the low-rank branch run 256 x 128 tiles, W4A8 128 x 128 and W8A8 128 x 256,
 //    two workgroups (one for W8A8) per compute unit;
 //  - the register-staged kernel for any other K (a multiple of 32): 256-element chunks
-//    double-buffered through registers, partial last chunk zero-filled.
+//    double-buffered through registers, partial last chunk zero-filled;
+//  - for W4A4 linears on a grid of a few tiles, one kernel that quantizes the BF16 activation
+//    into LDS and multiplies (linear_fused_small_kernel), with the ring kernels' MFMA order.
 // Sums over k are order-free, so each kernel pairs K blocks into MFMA steps in whatever order
 // makes the per-lane scale bytes one op_sel-selected register (see each kernel).
 //
