@@ -359,3 +359,25 @@ def test_variant_library_selection():
     from fp4_block_scaled_amd import build
     with pytest.raises(ValueError):
         build.build_hip(defines=["MX_RING_PP=0"], variant="../escape")
+
+
+def _build_c_caller(out_dir):
+    """Compile tests/c/linear_from_c.c with the C compiler against include/mxfp.h and link it to
+    the in-tree library: the header is plain C and the boundary needs no C++ or Python."""
+    exe = os.path.join(out_dir, "linear_from_c")
+    pkg = os.path.join(ROOT, "fp4_block_scaled_amd")
+    cmd = ["gcc", "-std=c11", "-Wall", "-Wextra", "-Werror", "-O2", "-D__HIP_PLATFORM_AMD__",
+           "-I/opt/rocm/include", "-I" + os.path.join(ROOT, "include"),
+           os.path.join(ROOT, "tests", "c", "linear_from_c.c"), "-o", exe,
+           "-L" + pkg, "-lmxfp", "-L/opt/rocm/lib", "-lamdhip64",
+           "-Wl,-rpath," + pkg, "-Wl,-rpath,/opt/rocm/lib"]
+    subprocess.run(cmd, check=True, capture_output=True, text=True)
+    return exe
+
+
+def test_c_caller_compiles_and_links(tmp_path):
+    exe = _build_c_caller(str(tmp_path))
+    out = subprocess.run(["nm", "-u", exe], capture_output=True, text=True, check=True).stdout
+    for name in ("mx_quantize", "mx_linear", "mx_linear_workspace_bytes", "mx_tiled_bytes",
+                 "mx_abi_version", "mx_status_string", "mx_last_error"):
+        assert name in out, name
