@@ -422,6 +422,8 @@ mx_status check_linear(const uint16_t* a, int64_t M, int64_t K, int64_t ld_a, in
     if (!lr->down || !lr->up) return fail(MX_ERR_NULL, "lr->down / lr->up is NULL");
     if (lr->rank < 1 || lr->rank > 64 || lr->rank % 16) return fail(MX_ERR_SHAPE, "rank must be 16, 32, 48 or 64");
     if (!aligned(lr->down, 16) || !aligned(lr->up, 16)) return fail(MX_ERR_ALIGN, "low-rank factors need 16-byte alignment");
+    if (31 * ld_a + K >= ((int64_t)1 << 30))
+      return fail(MX_ERR_SHAPE, "with a low-rank branch, 31 * ld_a + K must be below 2^30");
   }
   return MX_OK;
 }

@@ -290,7 +290,8 @@ size_t mx_linear_workspace_bytes(int64_t M, int64_t K, int32_t act_fmt, int32_t 
  * (K % 128 == 0); (NVFP4, NVFP4).
  *  bias: device FP16 [N] or NULL.
  *  lr:   low-rank branch or NULL (MX formats only); y += bf16_rne(a . lr->down) . lr->up,
- *        added before the bias.
+ *        added before the bias.  With a branch, 31 * ld_a + K must be below 2^30 (a 32-row
+ *        block of a spans less than 2 GiB), else MX_ERR_SHAPE.
  *  epilogue MX_EPI_BIAS / MX_EPI_BIAS_GELU: out is BF16 (out_dtype MX_OUT_BF16) or FP32
  *        (MX_OUT_F32), M x N with leading dimension ld_out elements.  The BF16 result is the
  *        RNE of the FP32 result.

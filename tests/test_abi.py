@@ -162,6 +162,10 @@ def test_linear_validation(mx):
     assert call(lr=byref(lr_bad)) == 2
     lr_nv = mx._LowRank(FAKE, FAKE, 32)
     assert call(act=mx.NVFP4, w_=_qm(mx, 64, 128, mx.NVFP4), lr=byref(lr_nv)) == 4
+    lr_ok = mx._LowRank(FAKE, FAKE, 32)
+    big = (1 << 30) // 31 + 8                        # a 32-row block of a would span >= 2 GiB
+    assert call(lr=byref(lr_ok), lda=big - big % 8) == 2
+    assert call(lr=byref(lr_ok), lda=(1 << 25), M=0, ws=0) == 0  # 31 * 2^25 + 128 < 2^30
     assert call(K=160, lda=160, w_=_qm(mx, 64, 160, mx.MXFP4, layout=1)) == 2  # tiled needs K % 128
     assert call(act=mx.NVFP4, w_=_qm(mx, 64, 128, mx.NVFP4, layout=1)) == 4     # tiled NVFP4
     assert call(w_=_qm(mx, 64, 128, mx.MXFP4, layout=3)) == 4                   # unknown layout
