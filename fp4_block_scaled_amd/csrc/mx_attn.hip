@@ -144,25 +144,28 @@ __device__ __forceinline__ void at_barrier() { asm volatile("s_barrier" ::: "mem
 __device__ __forceinline__ int at_swz(int row, int piece) { return row * 64 + 16 * (piece ^ ((row >> 2) & 3)); }
 
 // Q_MX8 of one lane's 16 probabilities of a 32-key group whose (group-wide) maximum is amax >= 0:
-// scale byte floor(log2 amax) - 8 (clamped to -127), magnitudes clamped to 448 * 2^e (the
-// conversion gives NaN past the largest E4M3 value), then the scaled conversion, round to
-// nearest even.  d[j] packs keys 4j..4j+3 of the lane's elements.
+// scale byte floor(log2 amax) - 8 (clamped to -127), magnitudes saturated at 448 * 2^e, then the
+// scaled conversion, round to nearest even.  d[j] packs keys 4j..4j+3 of the lane's elements.
+// Saturation: every p lies in [0, 512 * 2^e), and the conversion turns the ones that round past
+// 448 * 2^e (E4M3 has no infinity) into the NaN byte 0x7F, which is rewritten to 0x7E, the code
+// of 448: three integer operations per four codes instead of a clamp on every input.
 __device__ __forceinline__ void quant_p8(const v16f& p, float amax, uint32_t (&d)[4], uint32_t& sb) {
   int e = (int)(__float_as_uint(amax) >> 23) - 127 - 8;
   if (e < -127) e = -127;
   const float scale = __uint_as_float(e >= -126 ? (uint32_t)(127 + e) << 23 : 0x00400000u);
-  const float lim = __uint_as_float((uint32_t)(e + 135) << 23 | 0x600000u);  // 448 * 2^e
   // both 16-bit halves of each result are written, so the first conversion's pass-through
-  // operand (tied to its destination) is the first clamped input, which dies there: no zeroing
+  // operand (tied to its destination) is the first input, which dies there: no zeroing
 #pragma unroll
   for (int j = 0; j < 4; ++j) {
-    const float a0 = fminf(p[4 * j], lim);
+    const float a0 = p[4 * j];
     s16x2a init;
     __builtin_memcpy(&init, &a0, 4);
-    s16x2a r = __builtin_amdgcn_cvt_scalef32_pk_fp8_f32(init, a0, fminf(p[4 * j + 1], lim), scale, false);
-    r = __builtin_amdgcn_cvt_scalef32_pk_fp8_f32(r, fminf(p[4 * j + 2], lim), fminf(p[4 * j + 3], lim),
-                                                 scale, true);
-    __builtin_memcpy(&d[j], &r, 4);
+    s16x2a r = __builtin_amdgcn_cvt_scalef32_pk_fp8_f32(init, a0, p[4 * j + 1], scale, false);
+    r = __builtin_amdgcn_cvt_scalef32_pk_fp8_f32(r, p[4 * j + 2], p[4 * j + 3], scale, true);
+    uint32_t v;
+    __builtin_memcpy(&v, &r, 4);
+    // codes are at most 0x7F, so adding 1 to every byte carries into bit 7 exactly for 0x7F
+    d[j] = v ^ (((v + 0x01010101u) >> 7) & 0x01010101u);
   }
   sb = (uint32_t)(e + 127);
 }

@@ -189,6 +189,51 @@ def test_probability_groups_of_32_keys(mx):
     assert np.all(np.abs(ablated - ref) > _tol(bnd, ab, Skv))
 
 
+# Scores of one 64-key block for the exact probability test: group 0 holds the row maximum
+# (p = 1, scale 2^-8, so nothing there can pass 448 * 2^-8); group 1's largest p is 2^-1/16
+# = 0.9576, scale 2^-9, so p / 2^-9 = 490.3 and 469.5 (keys 32, 33) lie past the largest E4M3
+# value and must saturate to 448, 449.6 (key 34) rounds to 448, and 430.5, 394.8, 362.0 round to
+# 416, 384, 352; none lies near a rounding boundary.
+_SAT = np.full(64, -8.0)
+_SAT[:12] = [0, -0.0625, -0.125, -0.1875, -0.25, -0.375, -0.5, -1, -1.5, -2, -3, -6]
+_SAT[32:44] = [-0.0625, -0.125, -0.1875, -0.25, -0.375, -0.5, -1, -1.5, -2, -3, -6, -12]
+
+
+def test_probability_codes_exact_with_saturation(mx):
+    """The GPU's quantized probabilities read off exactly: exact scores (Q and K hold +-2^a or
+    +-1.5 * 2^a alone in their blocks, softmax_scale = ln 2 so that c = 1) and V one-hot (key j
+    carries 1 in head-dim column j, exact in MXFP8), so out[d] = p^_d / l, and key 0 (p = 1,
+    code 256 * 2^-8, exact) gives p^_d = out[d] / out[0].  Expected codes: p = 2^s in fp64, the
+    group scale floor(log2 max p) - 8, p / 2^scale saturated at 448 and rounded by torch's E4M3
+    cast.  Two keys of group 1 pass the largest E4M3 value, so a conversion without saturation
+    (E4M3 has no infinity: it gives NaN there) fails."""
+    BH, Sq, Skv = 1, 32, 64
+    q = np.zeros((Sq, D), dtype=np.float32)
+    q[:, [0, 32, 64]] = 1.0
+    k = np.zeros((Skv, D), dtype=np.float32)
+    for j in range(Skv):
+        k[j, [0, 32, 64]] = split_exact(float(_SAT[j]))
+    v = np.zeros((Skv, D), dtype=np.float32)
+    v[np.arange(Skv), np.arange(Skv)] = 1.0
+    q_bits, k_bits, v_bits = (synth.bits16(synth.to_bf16(x)) for x in (q, k, v))
+    o = mx.attention(mx.quantize(to_dev_bf16(q_bits), "mxfp4"), mx.quantize(to_dev_bf16(k_bits), "mxfp4"),
+                     mx.quantize_vt(to_dev_bf16(v_bits).view(BH, Skv, D)), BH,
+                     softmax_scale=float(np.log(2.0)), out_dtype=torch.float32)
+    torch.cuda.synchronize()
+    o = o.cpu().numpy().reshape(Sq, D).astype(np.float64)
+    assert np.all(o[:, Skv:] == 0.0)
+    got = o[:, :Skv] / o[:, :1]
+    p = 2.0 ** _SAT
+    want = np.empty(Skv)
+    for g in range(2):
+        grp = p[32 * g:32 * g + 32]
+        e = np.floor(np.log2(grp.max())) - 8
+        qv = np.minimum(grp / 2.0 ** e, 448.0)
+        want[32 * g:32 * g + 32] = torch.from_numpy(qv).float().to(torch.float8_e4m3fn).double().numpy() * 2.0 ** e
+    assert (p[32:34] / 2.0 ** -9 > 464).all()  # the saturating keys are there
+    np.testing.assert_allclose(got, np.broadcast_to(want, got.shape), rtol=2.0 ** -20, atol=0)
+
+
 def test_single_key_is_v_exactly(mx):
     """With one key every probability is 1 (quantized exactly), so out = v^ for every query."""
     BH, S = 2, 1
