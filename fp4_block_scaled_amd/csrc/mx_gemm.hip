@@ -1567,6 +1567,7 @@ static hipError_t run_w8a8(const GemmParams& p, hipStream_t s) {
 // codes for the whole K, within the 64 KB of dynamic LDS a launch gets by default); A rows past M
 // and W rows past N read as zero.
 constexpr int FS_KMAX = 896;
+constexpr int FS_IT = 64 * (FS_KMAX / 32) / 256;  // 32-element blocks per thread at K = FS_KMAX
 constexpr int FS_MAX_TILES = 8;  // ring tiles (256 x 128) up to which the one-launch path is taken
 
 bool linear_fused_small_ok(const GemmParams& p) {
@@ -1587,36 +1588,45 @@ __global__ void __launch_bounds__(256) linear_fused_small_kernel(GemmParams p, c
   const int tiles_n = (p.N + 63) / 64;
   const int m0 = (blockIdx.x / tiles_n) * 64, n0 = (blockIdx.x % tiles_n) * 64;
   const int64_t nkc = K >> 7;
-  for (int i = threadIdx.x; i < 64 * kbs; i += 256) {
-    const int r = i / kbs, kb = i - r * kbs;
-    // weight block: 16 code bytes and one scale byte (row-major or tiled operand layout)
-    const int n = n0 + r;
-    uint4 wc = make_uint4(0u, 0u, 0u, 0u);
-    uint32_t wsb = 0u;
-    if (n < p.N) {
-      if (p.w_tiled) {
-        wc = *(const uint4*)(p.w_codes + tiled_fp4_off(n, kb >> 2, kb & 3, nkc));
-        wsb = p.w_scales[tiled_scale_off(n, kb >> 2, nkc) + (kb & 3)];
-      } else {
-        wc = *(const uint4*)(p.w_codes + (int64_t)n * (K / 2) + kb * 16);
-        wsb = p.w_scales[(int64_t)n * kbs + kb];
-      }
-    }
-    *(uint4*)(sW + r * pitch + kb * 16) = wc;
-    sWs[r * kbs + kb] = (uint8_t)wsb;
-    // activation group: 32 BF16 values, quantized in this lane
-    const int m = m0 + r;
-    uint32_t w[16];
-    if (m < p.M) {
-      const uint16_t* src = a + (int64_t)m * ld_a + kb * 32;
+  // Thread t takes blocks i = t + 256 j (row i / kbs, 32-element block i % kbs), j < nit: 64 kbs
+  // is a multiple of 256 (K % 128 == 0), so every thread has exactly nit of them.  All their
+  // loads are issued first (rows past M or N read the last valid row and are zeroed after), so
+  // the workgroup waits for memory once rather than once per block.
+  const int nit = 64 * kbs / 256;  // <= FS_IT
+  uint4 wcv[FS_IT], av[FS_IT][4];
+  uint32_t wsv[FS_IT];
 #pragma unroll
-      for (int q = 0; q < 4; ++q) {
-        const uint4 v = *(const uint4*)(src + 8 * q);
-        w[4 * q] = v.x, w[4 * q + 1] = v.y, w[4 * q + 2] = v.z, w[4 * q + 3] = v.w;
-      }
+  for (int j = 0; j < FS_IT; ++j) {
+    if (j >= nit) break;  // uniform
+    const int i = threadIdx.x + 256 * j, r = i / kbs, kb = i - r * kbs;
+    const int n = min(n0 + r, p.N - 1), m = min(m0 + r, p.M - 1);
+    if (p.w_tiled) {
+      wcv[j] = *(const uint4*)(p.w_codes + tiled_fp4_off(n, kb >> 2, kb & 3, nkc));
+      wsv[j] = p.w_scales[tiled_scale_off(n, kb >> 2, nkc) + (kb & 3)];
     } else {
+      wcv[j] = *(const uint4*)(p.w_codes + (int64_t)n * (K / 2) + kb * 16);
+      wsv[j] = p.w_scales[(int64_t)n * kbs + kb];
+    }
+    const uint16_t* src = a + (int64_t)m * ld_a + kb * 32;
 #pragma unroll
-      for (int q = 0; q < 16; ++q) w[q] = 0u;
+    for (int q = 0; q < 4; ++q) av[j][q] = *(const uint4*)(src + 8 * q);
+  }
+#pragma unroll
+  for (int j = 0; j < FS_IT; ++j) {
+    if (j >= nit) break;
+    const int i = threadIdx.x + 256 * j, r = i / kbs, kb = i - r * kbs;
+    // weight block: 16 code bytes and one scale byte (row-major or tiled operand layout)
+    const bool nin = n0 + r < p.N, min_ = m0 + r < p.M;
+    *(uint4*)(sW + r * pitch + kb * 16) = nin ? wcv[j] : make_uint4(0u, 0u, 0u, 0u);
+    sWs[r * kbs + kb] = (uint8_t)(nin ? wsv[j] : 0u);
+    // activation group: 32 BF16 values, quantized in this lane
+    uint32_t w[16];
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+      w[4 * q] = min_ ? av[j][q].x : 0u;
+      w[4 * q + 1] = min_ ? av[j][q].y : 0u;
+      w[4 * q + 2] = min_ ? av[j][q].z : 0u;
+      w[4 * q + 3] = min_ ? av[j][q].w : 0u;
     }
     uint32_t ac[4], asb;
     quant_fp4_group32(w, ac, asb);
