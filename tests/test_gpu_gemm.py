@@ -256,6 +256,45 @@ def test_lowrank_branch_k_not_multiple_of_128(mx, act, M, K, N, R):
     assert_within(y.cpu().numpy(), y_ref, abs_sum, extra, what=f"low-rank {act} {M}x{K}x{N} R={R}")
 
 
+@pytest.mark.parametrize("act,w_fmt,M,K,N,R", [
+    ("mxfp4", "mxfp4", 256, 512, 512, 0),    # the one-launch small linear
+    ("mxfp4", "mxfp4", 600, 1024, 640, 0),   # quantizer + GEMM
+    ("mxfp8", "mxfp4", 300, 1024, 384, 32),  # MXFP8 quantizer fused with the low-rank down projection
+    ("mxfp4", "mxfp4", 200, 768, 320, 16),   # quantizer, then the low-rank down projection
+    ("mxfp8", "mxfp4", 77, 352, 200, 32),    # K % 128 != 0: row-major operands
+    ("nvfp4", "nvfp4", 257, 288, 96, 0),
+    ("mxfp8", "mxfp8", 130, 512, 256, 0),
+])
+def test_strided_activation_equals_contiguous(mx, act, w_fmt, M, K, N, R):
+    """An activation view with ld_a = K + 64 whose 64 padding columns hold BF16 NaN gives the same
+    F32 output, bit for bit, as its contiguous copy: every kernel on the path (quantizers, the
+    one-launch small linear, the fused MXFP8 quantizer + low-rank projection) steps rows by ld_a
+    and reads no element past K (a NaN read would turn its group's scale and outputs to NaN)."""
+    a_bits = activation_bits(M, K, seed_base=16000 + M, factor=20.0)
+    w_bits = weight_bits(N, K, seed=16100)
+    b = to_dev_f16(f16_bits(synth.normal_f32(16200, (N,), 0.01)))
+    wide = np.full((M, K + 64), 0x7FC0, dtype=np.uint16)
+    wide[:, :K] = a_bits
+    a_wide = to_dev_bf16(wide)
+    a_view, a_cont = a_wide[:, :K], to_dev_bf16(a_bits)
+    assert a_view.stride(0) == K + 64
+    kw = {}
+    if w_fmt == "nvfp4":
+        wq = mx.quantize_weight_nvfp4(to_dev_bf16(w_bits))
+        kw["act_global_scale"] = O.nv_global_scale(40.0)
+    else:
+        wq = mx.quantize(to_dev_bf16(w_bits), w_fmt)
+    if R:
+        down = synth.bits16(synth.to_bf16(synth.normal_f32(16300, (R, K), 0.02)))
+        up = synth.bits16(synth.to_bf16(synth.normal_f32(16400, (N, R), 0.02)))
+        kw["lowrank"] = mx.LowRank(to_dev_bf16(down), to_dev_bf16(up))
+    y_view = mx.linear(a_view, wq, b, act_fmt=act, out_dtype=torch.float32, **kw)
+    y_cont = mx.linear(a_cont, wq, b, act_fmt=act, out_dtype=torch.float32, **kw)
+    torch.cuda.synchronize()
+    assert torch.isfinite(y_cont).all()
+    assert torch.equal(y_view, y_cont)
+
+
 # ---------------------------------------------------------------------------------------------
 # W8A8 (MXFP8 weights and activations), the MXFP8 reference layer
 # ---------------------------------------------------------------------------------------------
