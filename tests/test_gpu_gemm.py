@@ -295,6 +295,39 @@ def test_strided_activation_equals_contiguous(mx, act, w_fmt, M, K, N, R):
     assert torch.equal(y_view, y_cont)
 
 
+@pytest.mark.parametrize("pad", [40, 4])  # ld_out % 8 == 0: staged BF16 epilogue; % 8 == 4: direct
+@pytest.mark.parametrize("odt", [torch.bfloat16, torch.float32])
+@pytest.mark.parametrize("act,w_fmt,M,K,N,R,epi", [
+    ("mxfp4", "mxfp4", 256, 512, 512, 0, "bias"),          # the one-launch small linear
+    ("mxfp4", "mxfp4", 600, 1024, 640, 0, "bias_gelu"),    # 256 x 128 ring tiles
+    ("mxfp4", "mxfp4", 4096, 512, 4096, 0, "bias"),        # ping-pong 256 x 256 tiles
+    ("mxfp8", "mxfp4", 300, 1024, 384, 32, "bias"),
+    ("nvfp4", "nvfp4", 257, 288, 96, 0, "bias"),
+    ("mxfp8", "mxfp8", 130, 512, 256, 0, "bias_gelu"),
+])
+def test_strided_output_equals_contiguous(mx, act, w_fmt, M, K, N, R, epi, odt, pad):
+    """An output view with ld_out = N + pad receives the same bits as a contiguous output, and
+    the pad columns of every row keep their sentinel (no write past N)."""
+    a = to_dev_bf16(activation_bits(M, K, seed_base=17000 + M, factor=20.0))
+    w_bits = weight_bits(N, K, seed=17100)
+    b = to_dev_f16(f16_bits(synth.normal_f32(17200, (N,), 0.01)))
+    kw = {"act_fmt": act, "epilogue": epi, "out_dtype": odt}
+    if w_fmt == "nvfp4":
+        wq = mx.quantize_weight_nvfp4(to_dev_bf16(w_bits))
+        kw["act_global_scale"] = O.nv_global_scale(40.0)
+    else:
+        wq = mx.quantize(to_dev_bf16(w_bits), w_fmt, layout="tiled")
+    if R:
+        kw["lowrank"] = mx.LowRank(to_dev_bf16(synth.bits16(synth.to_bf16(synth.normal_f32(17300, (R, K), 0.02)))),
+                                   to_dev_bf16(synth.bits16(synth.to_bf16(synth.normal_f32(17400, (N, R), 0.02)))))
+    y = mx.linear(a, wq, b, **kw)
+    wide = torch.full((M, N + pad), -7.5, dtype=odt, device="cuda")
+    mx.linear(a, wq, b, out=wide[:, :N], **kw)
+    torch.cuda.synchronize()
+    assert torch.equal(wide[:, :N], y)
+    assert bool((wide[:, N:] == -7.5).all())
+
+
 # ---------------------------------------------------------------------------------------------
 # W8A8 (MXFP8 weights and activations), the MXFP8 reference layer
 # ---------------------------------------------------------------------------------------------
