@@ -500,6 +500,48 @@ def test_nvfp4_linear_vs_oracle(mx, M, K, N):
     assert_within(y.cpu().numpy(), y_ref, abs_sum, what="NVFP4 linear")
 
 
+def test_activation_past_2_31_elements(mx):
+    """An activation of 262181 x 8192 BF16 values (2.15e9 elements, 4.3 GB: past 2^31 elements and
+    2^32 bytes; seeded on the device, the sampled rows copied back for the oracle).  The row-major
+    MXFP4, MXFP8 and NVFP4 quantizers' codes and scales, and the F32 output of the linear (tiled
+    quantizer, ping-pong GEMM), are checked against the oracle on rows at the start, on both sides
+    of element 2^31 (row 262144 starts at byte 2^32) and at the end; the absolute maximum against
+    torch's."""
+    M, K, N = 262181, 8192, 256
+    assert M * K > 2 ** 31 and 262144 * K == 2 ** 31
+    g = torch.Generator(device="cuda").manual_seed(18000)
+    a = torch.randn((M, K), generator=g, device="cuda", dtype=torch.bfloat16)
+    rows = np.array([0, 1, 2, 262142, 262143, 262144, 262145, 262150, M - 2, M - 1])
+    idx = torch.from_numpy(rows).cuda()
+    a_rows = synth.bits16(a[idx].cpu())
+    w_bits = weight_bits(N, K, seed=18100)
+    b_bits = f16_bits(synth.normal_f32(18200, (N,), 0.01))
+    wq = mx.quantize(to_dev_bf16(w_bits), "mxfp4", layout="tiled")
+    q = mx.quantize(a, "mxfp4")
+    y = mx.linear(a, wq, to_dev_f16(b_bits), out_dtype=torch.float32)
+    torch.cuda.synchronize()
+    ac, as_ = O.quantize_mx_bf16(a_rows)
+    np.testing.assert_array_equal(q.codes[idx].cpu().numpy(), ac)
+    np.testing.assert_array_equal(q.scales[idx].cpu().numpy(), as_)
+    wc, ws = O.quantize_mx_bf16(w_bits)
+    y_ref, abs_sum = O.linear_ref_mx(ac, as_, O.E2M1, wc, ws, K, b_bits)
+    assert_within(y[idx].cpu().numpy(), y_ref, abs_sum, what="activation past 2^31 elements")
+    del q, y
+    # the MXFP8 and NVFP4 quantizers and the absolute maximum on the same activation
+    q8 = mx.quantize(a, "mxfp8")
+    c8, s8 = O.quantize_mx_bf16(a_rows, O.E4M3)
+    np.testing.assert_array_equal(q8.codes[idx].cpu().numpy(), c8)
+    np.testing.assert_array_equal(q8.scales[idx].cpu().numpy(), s8)
+    del q8
+    sg = O.nv_global_scale(40.0)
+    qn = mx.quantize(a, "nvfp4", global_scale=sg)
+    cn, sn = O.quantize_nv_bf16(a_rows, sg)
+    np.testing.assert_array_equal(qn.codes[idx].cpu().numpy(), cn)
+    np.testing.assert_array_equal(qn.scales[idx].cpu().numpy(), sn)
+    del qn
+    assert float(mx.absmax(a)) == float(a.abs().max().float())
+
+
 @pytest.mark.parametrize("epi", ["bias", "bias_gelu", "bias_gelu_quant_mxfp4", "bias_gelu_quant_mxfp4_tiled"])
 def test_pingpong_tile_ragged(mx, epi):
     """A grid of 17 x 17 256 x 256 tiles (at least one per compute unit) takes the ping-pong
