@@ -542,6 +542,34 @@ def test_activation_past_2_31_elements(mx):
     assert float(mx.absmax(a)) == float(a.abs().max().float())
 
 
+@pytest.mark.parametrize("odt", [torch.bfloat16, torch.float32])
+def test_output_past_2_31_elements(mx, odt):
+    """A 262181 x 8192 output (2.15e9 elements; row 262144 starts at element 2^31) from K = 256:
+    the BF16 output (staged epilogue) and the F32 output (direct epilogue, 8.6 GB) against the
+    oracle on rows at the start, on both sides of the boundary and at the end."""
+    M, K, N = 262181, 256, 8192
+    assert M * N > 2 ** 31 and 262144 * N == 2 ** 31
+    g = torch.Generator(device="cuda").manual_seed(18300)
+    a = torch.randn((M, K), generator=g, device="cuda", dtype=torch.bfloat16)
+    rows = np.array([0, 1, 262142, 262143, 262144, 262145, M - 2, M - 1])
+    idx = torch.from_numpy(rows).cuda()
+    a_rows = synth.bits16(a[idx].cpu())
+    w_bits = weight_bits(N, K, seed=18400)
+    b_bits = f16_bits(synth.normal_f32(18500, (N,), 0.01))
+    wq = mx.quantize(to_dev_bf16(w_bits), "mxfp4", layout="tiled")
+    y = mx.linear(a, wq, to_dev_f16(b_bits), out_dtype=odt)
+    torch.cuda.synchronize()
+    got = y[idx].float().cpu().numpy()
+    del y
+    ac, as_ = O.quantize_mx_bf16(a_rows)
+    wc, ws = O.quantize_mx_bf16(w_bits)
+    y_ref, abs_sum = O.linear_ref_mx(ac, as_, O.E2M1, wc, ws, K, b_bits)
+    if odt == torch.float32:
+        assert_within(got, y_ref, abs_sum, what="output past 2^31 elements")
+    else:  # BF16: one rounding of a value within the tolerance
+        assert np.all(np.abs(got - y_ref) <= 2e-3 * abs_sum + 2.0 ** -8 * np.abs(y_ref) + 1e-30)
+
+
 @pytest.mark.parametrize("epi", ["bias", "bias_gelu", "bias_gelu_quant_mxfp4", "bias_gelu_quant_mxfp4_tiled"])
 def test_pingpong_tile_ragged(mx, epi):
     """A grid of 17 x 17 256 x 256 tiles (at least one per compute unit) takes the ping-pong
